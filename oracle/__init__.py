@@ -1,0 +1,202 @@
+"""ctypes wrapper of the plain C oracle (kvc_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and by
+bench.py's CPU-baseline leg, never by the product library.  See kvc_oracle.c
+for the page passages each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvc_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liborc.so")
+
+ORC_OK, ORC_ERR_ARG, ORC_ERR_NONFINITE, ORC_ERR_CAPACITY, ORC_ERR_CORRUPT = 0, -1, -2, -3, -4
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile liborc.so: gcc, -O2, no FP contraction, no fast-math."""
+    hdr = os.path.join(_HERE, "kvc_oracle.h")
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(hdr))
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        lib.orc_half_to_float.restype = ctypes.c_float
+        lib.orc_half_to_float.argtypes = [ctypes.c_uint16]
+        lib.orc_float_to_half.restype = ctypes.c_uint16
+        lib.orc_float_to_half.argtypes = [ctypes.c_float]
+        lib.orc_quantize.restype = ctypes.c_int
+        lib.orc_quantize.argtypes = [I32, I32, I64, P, P, P, P]
+        lib.orc_cdf.restype = ctypes.c_int
+        lib.orc_cdf.argtypes = [I32, I32, I64, I32, I32, P, P]
+        lib.orc_encode_stream.restype = I64
+        lib.orc_encode_stream.argtypes = [P, I32, I32, P, P, I64]
+        lib.orc_decode_stream.restype = ctypes.c_int
+        lib.orc_decode_stream.argtypes = [P, I64, I32, I32, P, P]
+        lib.orc_encode.restype = I64
+        lib.orc_encode.argtypes = [I32, I32, I64, I32, I32, P, P, P, P, P, I64]
+        lib.orc_decode.restype = ctypes.c_int
+        lib.orc_decode.argtypes = [I32, I32, I64, I32, I32, P, P, P, P, P]
+        lib.orc_dequantize.restype = ctypes.c_int
+        lib.orc_dequantize.argtypes = [I32, I32, I64, P, P, P, P, I32]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    if not a.flags.c_contiguous:
+        raise ValueError("array must be C-contiguous")
+    return a.ctypes.data
+
+
+class OracleError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} returned {code}")
+        self.code = code
+
+
+# ----------------------------------------------------------------- scalars
+
+def half_to_float(h: int) -> float:
+    return float(_load().orc_half_to_float(int(h) & 0xFFFF))
+
+
+def float_to_half(f: float) -> int:
+    return int(_load().orc_float_to_half(float(np.float32(f))))
+
+
+# ----------------------------------------------------------------- sizes
+
+def n_chunks(T: int, Tc: int) -> int:
+    return (T + Tc - 1) // Tc
+
+
+def chunk_tokens(T: int, Tc: int, j: int) -> int:
+    return min(Tc, T - j * Tc)
+
+
+# ----------------------------------------------------------------- steps
+
+def quantize(kv: np.ndarray, bins: np.ndarray):
+    """kv: uint16 fp16 bits [L][2][T][C]; bins int32 [L][2] -> (sym u8, max1 u16 [L][2][T])."""
+    L, two, T, C = kv.shape
+    assert two == 2
+    bins = np.ascontiguousarray(bins, dtype=np.int32)
+    kv = np.ascontiguousarray(kv, dtype=np.uint16)
+    sym = np.empty(kv.shape, dtype=np.uint8)
+    max1 = np.empty((L, 2, T), dtype=np.uint16)
+    rc = _load().orc_quantize(L, C, T, _ptr(bins), _ptr(kv), _ptr(sym), _ptr(max1))
+    if rc != ORC_OK:
+        raise OracleError("orc_quantize", rc)
+    return sym, max1
+
+
+def cdf(sym: np.ndarray, Tc: int, A: int) -> np.ndarray:
+    """sym u8 [L][2][T][C] -> cdf u16 [NC][L][2][C][A]."""
+    L, _, T, C = sym.shape
+    sym = np.ascontiguousarray(sym, dtype=np.uint8)
+    out = np.empty((n_chunks(T, Tc), L, 2, C, A), dtype=np.uint16)
+    rc = _load().orc_cdf(L, C, T, Tc, A, _ptr(sym), _ptr(out))
+    if rc != ORC_OK:
+        raise OracleError("orc_cdf", rc)
+    return out
+
+
+def encode_stream(q: np.ndarray, cdf_rows: np.ndarray) -> bytes:
+    """q u8 [C]; cdf_rows u16 [C][A] -> stream bytes."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    cdf_rows = np.ascontiguousarray(cdf_rows, dtype=np.uint16)
+    C, A = cdf_rows.shape
+    assert q.shape == (C,)
+    cap = 2 * C + 8
+    buf = np.empty(cap, dtype=np.uint8)
+    n = _load().orc_encode_stream(_ptr(q), C, A, _ptr(cdf_rows), _ptr(buf), cap)
+    if n < 0:
+        raise OracleError("orc_encode_stream", n)
+    return buf[:n].tobytes()
+
+
+def decode_stream(data: bytes, cdf_rows: np.ndarray):
+    """-> (symbols u8 [C], corrupt flag)."""
+    cdf_rows = np.ascontiguousarray(cdf_rows, dtype=np.uint16)
+    C, A = cdf_rows.shape
+    src = np.frombuffer(bytes(data) + b"\0", dtype=np.uint8)  # +1: never a zero-size buffer
+    q = np.empty(C, dtype=np.uint8)
+    bad = _load().orc_decode_stream(_ptr(src), len(data), C, A, _ptr(cdf_rows), _ptr(q))
+    return q, bool(bad)
+
+
+def encode(sym: np.ndarray, cdf_tab: np.ndarray, Tc: int, A: int, payload_cap: int | None = None):
+    """-> (stream_len u16 [n_streams], slab_off u64 [n_slabs+1], payload u8)."""
+    L, _, T, C = sym.shape
+    NC = n_chunks(T, Tc)
+    n_streams = 2 * L * T
+    n_slabs = NC * L * 2
+    if payload_cap is None:
+        payload_cap = n_streams * (2 * C + 1)
+    stream_len = np.zeros(n_streams, dtype=np.uint16)
+    slab_off = np.zeros(n_slabs + 1, dtype=np.uint64)
+    payload = np.zeros(max(payload_cap, 1), dtype=np.uint8)
+    n = _load().orc_encode(L, C, T, Tc, A, _ptr(np.ascontiguousarray(sym)),
+                           _ptr(np.ascontiguousarray(cdf_tab)), _ptr(stream_len), _ptr(slab_off),
+                           _ptr(payload), payload_cap)
+    if n < 0:
+        raise OracleError("orc_encode", n)
+    return stream_len, slab_off, payload[:n].copy()
+
+
+def decode(payload: np.ndarray, slab_off: np.ndarray, stream_len: np.ndarray, cdf_tab: np.ndarray,
+           L: int, C: int, T: int, Tc: int, A: int):
+    """-> (sym u8 [L][2][T][C], corrupt flag)."""
+    sym = np.empty((L, 2, T, C), dtype=np.uint8)
+    pay = np.concatenate([np.ascontiguousarray(payload, dtype=np.uint8), np.zeros(1, np.uint8)])
+    rc = _load().orc_decode(L, C, T, Tc, A, _ptr(pay), _ptr(np.ascontiguousarray(slab_off)),
+                            _ptr(np.ascontiguousarray(stream_len)),
+                            _ptr(np.ascontiguousarray(cdf_tab)), _ptr(sym))
+    if rc not in (ORC_OK, ORC_ERR_CORRUPT):
+        raise OracleError("orc_decode", rc)
+    return sym, rc == ORC_ERR_CORRUPT
+
+
+def dequantize(sym: np.ndarray, max1: np.ndarray, bins: np.ndarray, fp32: bool = True) -> np.ndarray:
+    """-> float32 [L][2][T][C] or uint16 fp16 bits."""
+    L, _, T, C = sym.shape
+    out = np.empty(sym.shape, dtype=np.float32 if fp32 else np.uint16)
+    rc = _load().orc_dequantize(L, C, T, _ptr(np.ascontiguousarray(bins, dtype=np.int32)),
+                                _ptr(np.ascontiguousarray(sym)), _ptr(np.ascontiguousarray(max1)),
+                                _ptr(out), 1 if fp32 else 0)
+    if rc != ORC_OK:
+        raise OracleError("orc_dequantize", rc)
+    return out
+
+
+def codec(kv: np.ndarray, bins: np.ndarray, Tc: int):
+    """The whole hot path on the CPU: dict of every intermediate and output."""
+    A = int(np.max(bins))
+    sym, max1 = quantize(kv, bins)
+    cdf_tab = cdf(sym, Tc, A)
+    stream_len, slab_off, payload = encode(sym, cdf_tab, Tc, A)
+    L, _, T, C = kv.shape
+    dsym, bad = decode(payload, slab_off, stream_len, cdf_tab, L, C, T, Tc, A)
+    out16 = dequantize(dsym, max1, bins, fp32=False)
+    return dict(A=A, sym=sym, max1=max1, cdf=cdf_tab, stream_len=stream_len, slab_off=slab_off,
+                payload=payload, dec_sym=dsym, corrupt=bad, out_f16=out16)
