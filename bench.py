@@ -1,0 +1,179 @@
+#!/usr/bin/env python3
+"""Throughput of the KV codec hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic fp16 KV already in
+HBM: quantize + CDF (kvc_quantize), range coding + packing (kvc_encode), and
+decode with fused dequantization to fp16 (kvc_decode).  `value` is fp16
+input bytes per second of whole steps (GB/s).  Per-stage times come from HIP
+events recorded on the stream the kernels run on.  The roofline object is
+for the decode kernel (one launch per kvc_decode call).  The CPU baseline is
+the plain single-threaded oracle on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV codec encode/decode GB/s (fp16 in) + bits/elem + % HBM roofline, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_CONFIG = "c2"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from committed counter runs, if they were taken on
+    the current kernel source (profiles/traffic.json records its hash)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}/{workload}")
+    except Exception:
+        return None
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in rec.get("sources", []):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return rec.get("bytes_per_launch") if h.hexdigest() == rec.get("source_sha256") else None
+
+
+def cpu_baseline(cfg, kv_np):
+    """The oracle, as it stands, over a bounded sample: whole slabs of the
+    workload (all of it when it is small), single-threaded."""
+    import numpy as np
+
+    import oracle
+    L, T, C, Tc = cfg.n_layers, cfg.n_tokens, cfg.n_channels, cfg.chunk_tokens
+    bins = cfg.bins()
+    n_tok = min(T, Tc)  # the first chunk of every layer
+    sub = np.ascontiguousarray(kv_np[:, :, :n_tok])
+    budget_s, n_el, spent, passes = 10.0, 0, 0.0, 0
+    while spent < budget_s and passes < 8:
+        t0 = time.perf_counter()
+        r = oracle.codec(sub, bins, Tc)
+        spent += time.perf_counter() - t0
+        n_el += sub.size
+        passes += 1
+        assert not r["corrupt"]
+    gbps = 2 * n_el / spent / 1e9
+    sample = (f"{passes} pass(es) of the whole hot path (quantize, CDF, encode, pack, decode, "
+              f"dequantize) over tokens [0, {n_tok}) of all {L} layers = {sub.size} elements, "
+              f"{spent:.1f} s")
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this codec is measured on one GPU; --gpus must be 1 "
+                                   "(sharding across GPUs is described in DESIGN.md, not run)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import entropy_coding_02_amd as kvc
+    import kvgen
+
+    cfg = kvgen.CONFIGS[args.config]
+    L, T, C, Tc = cfg.n_layers, cfg.n_tokens, cfg.n_channels, cfg.chunk_tokens
+    kv_np, _ = kvgen.generate(cfg)
+    torch.cuda.set_device(0)
+    kvt = torch.from_numpy(kv_np.view(np.int16)).cuda()
+    d = kvc.Desc(L, C, T, cfg.bins(), Tc)
+    buf = kvc.alloc(d, out_dtype=kvc.KVC_F16)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        kvc.kvc_quantize(d, kvt, buf.sym, buf.max1, buf.cdf, buf.dev_status, stream)
+        if ev:
+            ev[1].record(stream)
+        kvc.kvc_encode(d, buf.sym, buf.cdf, buf.scratch, buf.stream_len, buf.slab_off, buf.payload,
+                       buf.dev_status, stream)
+        if ev:
+            ev[2].record(stream)
+        kvc.kvc_decode(d, buf.payload, buf.slab_off, buf.stream_len, buf.cdf, buf.max1, None, buf.out,
+                       kvc.KVC_F16, buf.dev_status, stream)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert int(buf.dev_status.item()) == 0, "device status flags set"
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    q_ms = statistics.median(e[0].elapsed_time(e[1]) for e in evs)
+    e_ms = statistics.median(e[1].elapsed_time(e[2]) for e in evs)
+    d_ms = statistics.median(e[2].elapsed_time(e[3]) for e in evs)
+    d_avg = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    in_bytes = cfg.input_bytes
+    n_el = cfg.n_elements
+    payload = int(buf.slab_off[d.n_slabs].item())
+    side = d.cdf_bytes + 2 * (L * 2 * T) + 2 * d.n_streams + 8 * (d.n_slabs + 1)
+    # decode kernel, algorithmic bytes per launch: payload + CDFs + max1 + stream lengths
+    # + slab offsets in, fp16 out
+    dec_bytes = payload + side + 2 * n_el
+    achieved = dec_bytes / (d_avg * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(in_bytes / (ms_step * 1e-3) / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+u32",
+        "data": "synthetic",
+        "config": {"workload": cfg.workload, "layers": L, "channels": C, "tokens": T,
+                   "chunk_tokens": Tc, "bins": [list(s) for s in cfg.layer_bins],
+                   "input": "fp16 [L][2][T][C]", "output": "fp16"},
+        "encode_GBps": round(in_bytes / ((q_ms + e_ms) * 1e-3) / 1e9, 3),
+        "decode_GBps": round(in_bytes / (d_ms * 1e-3) / 1e9, 3),
+        "stage_ms": {"quantize_cdf": round(q_ms, 4), "encode_pack": round(e_ms, 4),
+                     "decode_dequant": round(d_ms, 4)},
+        "payload_bits_per_elem": round(8 * payload / n_el, 4),
+        "total_bits_per_elem": round(8 * (payload + side) / n_el, 4),
+        "roofline": {"kernel": "k_decode", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_for("k_decode", cfg.workload),
+                     "algorithmic_bytes_per_launch": dec_bytes},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, kv_np)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

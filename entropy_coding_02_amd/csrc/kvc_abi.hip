@@ -1,0 +1,209 @@
+// kvc_abi.hip - the extern "C" entry points of libkvc.so: argument checks on
+// the host, then asynchronous launches on the caller's stream.
+#include <string.h>
+
+#include "kvc_common.h"
+#include "kvc_kernels.h"
+
+namespace {
+
+struct Geometry {
+    KParams p;
+    int64_t slot_area;   // bytes of encoder stream slots
+    int64_t scratch;     // total encoder scratch bytes
+};
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Validate the descriptor and derive every size; KVC_OK or KVC_ERR_ARG.
+int make_geometry(const kvc_desc *d, Geometry &g)
+{
+    if (!d || !d->bins) return KVC_ERR_ARG;
+    if (d->n_layers < 1 || d->n_layers > KVC_MAX_LAYERS) return KVC_ERR_ARG;
+    if (d->n_channels < 1 || d->n_channels > 16384) return KVC_ERR_ARG;
+    if (d->n_tokens < 0 || d->n_tokens > ((int64_t)1 << 40)) return KVC_ERR_ARG;
+    if (d->chunk_tokens < 1 || d->chunk_tokens > 65535 || d->reserved != 0) return KVC_ERR_ARG;
+    memset(&g, 0, sizeof(g));
+    KParams &p = g.p;
+    int A = 0;
+    for (int i = 0; i < 2 * d->n_layers; ++i) {
+        int b = d->bins[i];
+        if (b < 4 || b > 256 || (b & 1)) return KVC_ERR_ARG;
+        p.maxq[i] = (uint8_t)(b / 2 - 1);
+        A = b > A ? b : A;
+    }
+    p.L = d->n_layers;
+    p.C = d->n_channels;
+    p.A = A;
+    p.Tc = d->chunk_tokens;
+    p.T = d->n_tokens;
+    int64_t NC = (p.T + p.Tc - 1) / p.Tc;
+    if (NC > INT32_MAX) return KVC_ERR_ARG;
+    p.NC = (int32_t)NC;
+    p.last_nj = NC ? (int32_t)(p.T - (NC - 1) * p.Tc) : 0;
+    p.n_rows = 2 * (int64_t)p.L * p.T;
+    p.n_streams = p.n_rows;
+    p.n_slabs = NC * 2 * p.L;
+    p.slot_bytes = round_up(2 * (int64_t)p.C + 16, 16);
+    g.slot_area = p.n_streams * p.slot_bytes;
+    g.scratch = g.slot_area + 8 * p.n_slabs;
+    // launch-size limits (1-D grids of 32-bit block counts)
+    if (p.n_slabs * ((p.Tc + 255) / 256) >= ((int64_t)1 << 31)) return KVC_ERR_ARG;
+    if (p.n_slabs * ((p.C + 63) / 64) >= ((int64_t)1 << 31)) return KVC_ERR_ARG;
+    return KVC_OK;
+}
+
+bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int kvc_version(void) { return KVC_VERSION; }
+
+const char *kvc_status_string(int status)
+{
+    switch (status) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_ARG: return "invalid argument";
+    case KVC_ERR_CAPACITY: return "buffer too small";
+    case KVC_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int32_t kvc_alphabet(const kvc_desc *desc)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    return rc == KVC_OK ? g.p.A : rc;
+}
+
+int64_t kvc_n_chunks(const kvc_desc *desc)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    return rc == KVC_OK ? (int64_t)g.p.NC : rc;
+}
+
+int64_t kvc_n_slabs(const kvc_desc *desc)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    return rc == KVC_OK ? g.p.n_slabs : rc;
+}
+
+int64_t kvc_n_streams(const kvc_desc *desc)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    return rc == KVC_OK ? g.p.n_streams : rc;
+}
+
+int64_t kvc_cdf_bytes(const kvc_desc *desc)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    return rc == KVC_OK ? g.p.n_slabs * g.p.C * g.p.A * 2 : rc;
+}
+
+int64_t kvc_scratch_bytes(const kvc_desc *desc)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    return rc == KVC_OK ? g.scratch : rc;
+}
+
+int64_t kvc_max_payload_bytes(const kvc_desc *desc)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    return rc == KVC_OK ? g.p.n_streams * (2 * (int64_t)g.p.C + 1) : rc;
+}
+
+int kvc_quantize(const kvc_desc *desc, const uint16_t *kv, uint8_t *sym, uint16_t *max1,
+                 uint16_t *cdf, int32_t *dev_status, void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    if (g.p.n_rows == 0) return KVC_OK;
+    if (!kv || !sym || !max1 || !aligned(kv, 4) || !aligned(sym, 4) || !aligned(max1, 2) ||
+        (cdf && !aligned(cdf, 4)) || (dev_status && !aligned(dev_status, 4)))
+        return KVC_ERR_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    const bool vec8 = (g.p.C % 8 == 0) && aligned(kv, 16) && aligned(sym, 8);
+    hipError_t e = launch_quantize_rows(kv, sym, max1, g.p, dev_status, vec8, s);
+    if (e == hipSuccess && cdf) e = launch_cdf(sym, cdf, g.p, s);
+    return launch_status(e);
+}
+
+int kvc_cdf(const kvc_desc *desc, const uint8_t *sym, uint16_t *cdf, void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    if (g.p.n_rows == 0) return KVC_OK;
+    if (!sym || !cdf || !aligned(sym, 4) || !aligned(cdf, 4)) return KVC_ERR_ARG;
+    return launch_status(launch_cdf(sym, cdf, g.p, (hipStream_t)stream));
+}
+
+int kvc_encode(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf, void *scratch,
+               int64_t scratch_bytes, uint16_t *stream_len, uint64_t *slab_off, uint8_t *payload,
+               int64_t payload_cap, int32_t *dev_status, void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    if (!slab_off || !aligned(slab_off, 8) || payload_cap < 0) return KVC_ERR_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    if (g.p.n_rows == 0) return launch_status(launch_zero_u64(slab_off, s));
+    if (!sym || !cdf || !scratch || !stream_len || (!payload && payload_cap > 0) ||
+        !aligned(sym, 4) || !aligned(cdf, 4) || !aligned(scratch, 16) || !aligned(stream_len, 2) ||
+        (dev_status && !aligned(dev_status, 4)))
+        return KVC_ERR_ARG;
+    if (scratch_bytes < g.scratch) return KVC_ERR_CAPACITY;
+    uint8_t *slots = (uint8_t *)scratch;
+    uint64_t *slab_total = (uint64_t *)(slots + g.slot_area);
+    const bool vec16 = (g.p.C % 16 == 0) && aligned(sym, 16);
+    return launch_status(launch_encode(sym, cdf, slots, slab_total, stream_len, slab_off, payload,
+                                       payload_cap, g.p, dev_status, vec16, s));
+}
+
+int kvc_decode(const kvc_desc *desc, const uint8_t *payload, int64_t payload_bytes,
+               const uint64_t *slab_off, const uint16_t *stream_len, const uint16_t *cdf,
+               const uint16_t *max1, uint8_t *sym_out, void *out, int32_t out_dtype,
+               int32_t *dev_status, void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    if (out && out_dtype != KVC_F16 && out_dtype != KVC_F32) return KVC_ERR_ARG;
+    if (g.p.n_rows == 0) return KVC_OK;
+    if (!slab_off || !stream_len || !cdf || payload_bytes < 0 || (!payload && payload_bytes > 0) ||
+        (!out && !sym_out) || (out && !max1) || !aligned(payload, 4) || !aligned(slab_off, 8) ||
+        !aligned(stream_len, 2) || !aligned(cdf, 4) || (dev_status && !aligned(dev_status, 4)))
+        return KVC_ERR_ARG;
+    const bool vec = (g.p.C % 16 == 0) && (!sym_out || aligned(sym_out, 16)) &&
+                     (!out || aligned(out, 16));
+    return launch_status(launch_decode(payload, payload_bytes, slab_off, stream_len, cdf, max1,
+                                       sym_out, out, out_dtype, g.p, dev_status, vec,
+                                       (hipStream_t)stream));
+}
+
+int kvc_dequantize(const kvc_desc *desc, const uint8_t *sym, const uint16_t *max1, void *out,
+                   int32_t out_dtype, void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    if (out_dtype != KVC_F16 && out_dtype != KVC_F32) return KVC_ERR_ARG;
+    if (g.p.n_rows == 0) return KVC_OK;
+    if (!sym || !max1 || !out || !aligned(out, 4)) return KVC_ERR_ARG;
+    return launch_status(
+        launch_dequantize(sym, max1, out, out_dtype, g.p, false, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,254 @@
+// lane_coder.h - one range-coder stream per GPU lane.
+//
+// The CacheGen write-up (LMCache, "1.2 Core challenges and solutions", design
+// point 3, and "2.1 Core components": ac_enc / ac_dec) codes the quantized
+// symbols with GPU-parallel arithmetic coding; the stream unit here is one
+// (chunk, layer, K|V, token) row of C channel symbols.  The coder is a 32-bit
+// range coder over 16-bit cumulative frequencies with byte renormalisation:
+//
+//   r = range >> 16;  low += r * cdf_s;  range = r * f_s;  scale by 256 while range < 2^24
+//   finish: round low up to a multiple of 2^24; the stream is the number
+//   written in base 256 with its (always zero) first byte and its trailing
+//   zero bytes removed.  A decoder reads zeros past the end.
+//
+// The byte sequence is fully fixed by those rules; how a lane buffers bytes
+// and resolves carries is free, and this file does it without a byte loop:
+//   * the renormalisation shift count is clz(range) & 24 (0, 8 or 16 bits),
+//     applied to a 96-bit shift register {pb (64 bits), lo (32 bits)};
+//   * pb holds k <= 7 pending bytes; a carry out of lo is added to pb, and
+//     integer addition ripples it through pending 0xFF bytes by itself.  A
+//     carry that runs past all k pending bytes sets bit 8k of pb: it belongs
+//     to bytes already written, and is added to them (a rare path);
+//   * when k reaches 6, the 4 oldest pending bytes go out as one aligned
+//     big-endian dword, so at least 2 bytes always stay pending.
+// All arithmetic is 32/64-bit integer; this header is compiled both for the
+// GPU kernels and, in the tests, for the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define KVC_HD __host__ __device__ __forceinline__
+
+KVC_HD uint32_t kvc_bswap32(uint32_t v) { return __builtin_bswap32(v); }
+
+// Shift count (bits) that brings range back to >= 2^24; range must be >= 2^8.
+KVC_HD uint32_t kvc_renorm_bits(uint32_t range) { return (uint32_t)__builtin_clz(range) & 24u; }
+
+// ----------------------------------------------------------------- encoder
+
+struct EncState {
+    uint32_t lo;     // low 32 bits of the coding interval's lower end
+    uint32_t range;  // interval width, >= 2^24 between symbols
+    uint64_t pb;     // k pending bytes (newest lowest) + carry indicator at bit 8k
+    uint32_t k;      // pending byte count
+    uint32_t w;      // dwords already written to the stream slot
+};
+
+// A stream slot: dword-addressable memory owned by one lane.
+struct SlotOut {
+    uint32_t *p;
+    KVC_HD uint32_t load(uint32_t i) const { return p[i]; }
+    KVC_HD void store(uint32_t i, uint32_t v) const { p[i] = v; }
+};
+
+KVC_HD void enc_init(EncState &e)
+{
+    e.lo = 0;
+    e.range = 0xFFFFFFFFu;
+    e.pb = 0;
+    e.k = 0;
+    e.w = 0;
+}
+
+// Add one to the big-endian number held in dwords [0, w) of the slot.
+template <class Out>
+__host__ __device__ __noinline__ void enc_carry_into_written(const Out &out, uint32_t w)
+{
+    for (int32_t i = (int32_t)w - 1; i >= 0; --i) {
+        uint32_t v = kvc_bswap32(out.load((uint32_t)i)) + 1u;
+        out.store((uint32_t)i, kvc_bswap32(v));
+        if (v != 0) break;
+    }
+}
+
+// Code one symbol with cumulative frequency st and frequency fr (1 <= fr,
+// st + fr <= 65536).
+template <class Out>
+KVC_HD void enc_put(EncState &e, uint32_t st, uint32_t fr, const Out &out)
+{
+    uint32_t r = e.range >> 16;
+    uint32_t add = r * st;
+    uint32_t lo2 = e.lo + add;
+    e.pb += (lo2 < add) ? 1u : 0u;
+    e.range = r * fr;
+    uint32_t n = kvc_renorm_bits(e.range);
+    e.range <<= n;
+    uint64_t wide = (uint64_t)lo2 << n;
+    e.pb = (e.pb << n) | (wide >> 32);
+    e.lo = (uint32_t)wide;
+    e.k += n >> 3;
+    if (e.k >= 6) {
+        uint32_t sh = 8u * (e.k - 4u);
+        uint32_t word = (uint32_t)(e.pb >> sh);
+        if ((e.pb >> (sh + 32u)) != 0) enc_carry_into_written(out, e.w);
+        out.store(e.w, kvc_bswap32(word));
+        e.w += 1;
+        e.pb &= ((uint64_t)1 << sh) - 1u;
+        e.k -= 4;
+    }
+}
+
+// Flush and write the tail; returns the stream length in bytes (trailing
+// zero bytes removed).  At most 4*w + 8 bytes of the slot are touched.
+template <class Out>
+KVC_HD uint32_t enc_finish(EncState &e, const Out &out)
+{
+    uint32_t lo2 = e.lo + 0xFFFFFFu;
+    e.pb += (lo2 < 0xFFFFFFu) ? 1u : 0u;
+    uint32_t top = lo2 >> 24;  // the byte kept after rounding up to a multiple of 2^24
+    uint32_t kb = 8u * e.k;
+    if ((e.pb >> kb) != 0) {
+        enc_carry_into_written(out, e.w);
+        e.pb &= ((uint64_t)1 << kb) - 1u;
+    }
+    uint64_t tail = (e.pb << 8) | top;  // k + 1 bytes, oldest first
+    uint32_t nt = e.k + 1u;
+    while (nt > 0 && (tail & 0xFFu) == 0) {
+        tail >>= 8;
+        nt -= 1;
+    }
+    if (nt > 0) {
+        uint64_t t = tail << (64u - 8u * nt);  // left-align
+        out.store(e.w, kvc_bswap32((uint32_t)(t >> 32)));
+        if (nt > 4) out.store(e.w + 1u, kvc_bswap32((uint32_t)t));
+        return 4u * e.w + nt;
+    }
+    // the tail is all zero: the stream ends inside the written dwords
+    for (int32_t i = (int32_t)e.w - 1; i >= 0; --i) {
+        uint32_t v = kvc_bswap32(out.load((uint32_t)i));
+        if (v != 0) return 4u * (uint32_t)i + 4u - ((uint32_t)__builtin_ctz(v) >> 3);
+    }
+    return 0;
+}
+
+// ----------------------------------------------------------------- decoder
+
+// Reads one stream [pos, end) of a byte buffer of `cap` bytes as big-endian
+// dwords; bytes at or past `end` read as zero and are never loaded, and no
+// load touches bytes at or past `cap`.  `base` must be 4-byte aligned.
+struct StreamIn {
+    const uint8_t *base;
+    uint64_t a;    // aligned address of the dword held in `cur`
+    uint64_t end;  // stream end (exclusive)
+    uint64_t cap;  // buffer size
+    uint32_t sh;   // (start & 3) * 8
+    uint32_t cur;  // big-endian dword at a, masked to the stream
+
+    KVC_HD uint32_t load_be(uint64_t addr) const
+    {
+        if (addr >= end) return 0u;
+        uint32_t v;
+        if (addr + 4u <= cap) {
+            v = kvc_bswap32(*(const uint32_t *)(base + addr));
+        } else {
+            v = 0;
+            for (uint32_t i = 0; i < 4; ++i)
+                v |= (addr + i < cap ? (uint32_t)base[addr + i] : 0u) << (24u - 8u * i);
+        }
+        uint64_t keep = end - addr;
+        if (keep < 4u) v &= ~(0xFFFFFFFFu >> (8u * (uint32_t)keep));
+        return v;
+    }
+    KVC_HD void init(const uint8_t *b, uint64_t start, uint64_t len, uint64_t capacity)
+    {
+        base = b;
+        end = start + len;
+        cap = capacity;
+        a = start & ~(uint64_t)3;
+        sh = (uint32_t)(start & 3u) * 8u;
+        cur = load_be(a);
+        if (start > a) cur &= 0xFFFFFFFFu >> sh;  // bytes before the stream are not ours
+    }
+    // The next 4 stream bytes as a big-endian dword.
+    KVC_HD uint32_t next()
+    {
+        uint32_t nxt = load_be(a + 4u);
+        uint32_t v = sh ? (cur << sh) | (nxt >> (32u - sh)) : cur;
+        cur = nxt;
+        a += 4u;
+        return v;
+    }
+};
+
+struct DecState {
+    uint32_t code;
+    uint32_t range;
+    uint64_t bb;  // upcoming stream bits, most significant first
+    uint32_t nb;  // valid bits in bb
+};
+
+KVC_HD void dec_init(DecState &d, StreamIn &in)
+{
+    d.code = in.next();
+    d.bb = (uint64_t)in.next() << 32;
+    d.nb = 32;
+    d.range = 0xFFFFFFFFu;
+}
+
+// After the symbol with cumulative frequency st and frequency fr was found
+// for r = range >> 16: narrow the interval and refill.  Returns 1 if the
+// stream is inconsistent with the CDF (code outside the new interval).
+KVC_HD uint32_t dec_advance(DecState &d, uint32_t r, uint32_t st, uint32_t fr, StreamIn &in)
+{
+    d.code -= r * st;
+    d.range = r * fr;
+    uint32_t bad = d.code >= d.range ? 1u : 0u;
+    uint32_t n = kvc_renorm_bits(d.range);
+    d.range <<= n;
+    uint64_t t = (((uint64_t)d.code << 32) | (d.bb >> 32)) << n;
+    d.code = (uint32_t)(t >> 32);
+    d.bb <<= n;
+    d.nb -= n;
+    if (d.nb < 16u) {
+        d.bb |= (uint64_t)in.next() << (32u - d.nb);
+        d.nb += 32u;
+    }
+    return bad;
+}
+
+// ------------------------------------------------- per-symbol table lookups
+
+// Code symbol s with CDF row `row` of A entries (cdf_A = 65536 implicit).
+// Out-of-alphabet symbols are clamped and non-increasing rows get frequency
+// 1, so malformed input cannot make a lane write past its slot.
+template <class Out>
+KVC_HD void enc_symbol(EncState &e, const uint16_t *row, uint32_t A, uint32_t s, const Out &out)
+{
+    s = s < A ? s : A - 1u;
+    uint32_t st = row[s];
+    uint32_t nx = (s + 1u < A) ? (uint32_t)row[s + 1u] : 65536u;
+    uint32_t fr = nx > st ? nx - st : 1u;
+    enc_put(e, st, fr, out);
+}
+
+// Largest k in [0, A) with r * row[k] <= code, by binary lifting from
+// step0 = the largest power of two <= A - 1; then the interval update.
+// Returns the symbol; *bad |= 1 when the stream left its interval.
+KVC_HD uint32_t dec_symbol(DecState &d, const uint16_t *row, uint32_t A, uint32_t step0,
+                           StreamIn &in, uint32_t *bad)
+{
+    const uint32_t r = d.range >> 16;
+    uint32_t s = 0;
+    for (uint32_t step = step0; step > 0; step >>= 1) {
+        uint32_t k = s + step;
+        if (k < A && r * (uint32_t)row[k] <= d.code) s = k;
+    }
+    const uint32_t st = row[s];
+    const uint32_t nx = (s + 1u < A) ? (uint32_t)row[s + 1u] : 65536u;
+    const uint32_t fr = nx > st ? nx - st : 1u;
+    *bad |= dec_advance(d, r, st, fr, in);
+    return s;
+}
+
+KVC_HD uint32_t dec_step0(uint32_t A) { return 1u << (31 - __builtin_clz(A - 1u)); }

@@ -1,0 +1,179 @@
+/*
+ * kvc.h - C ABI of libkvc.so, a CacheGen-style KV-cache codec for AMD
+ * MI355X (gfx950), written as HIP kernels.
+ *
+ * The method is the one the page "CacheGen technical deep dive: efficient
+ * compression and streaming of the KV cache" (an LMCache write-up of the
+ * SIGCOMM'24 CacheGen paper) describes, cited below as [CG]:
+ *   - layer-wise adaptive group quantization of fp16 K/V ([CG] 1.2 point 2,
+ *     2.2 CacheGenConfig, 2.3 step 1),
+ *   - per-(layer, channel) symbol statistics turned into CDFs ([CG] 1.2 point 3,
+ *     2.3 step 2),
+ *   - parallel arithmetic coding of independent streams in 256-token chunks
+ *     ([CG] 2.1, 2.3 step 3),
+ *   - parallel decode and dequantization ([CG] 2.4 steps 1-2).
+ *
+ * Data layout in device memory (row-major):
+ *   kv, out      [L][2][T][C]      fp16 (out: fp16 or fp32), (layer, K|V, token, channel)
+ *                                   i.e. the kv_shape (layers, 2, tokens, kv_heads, head_dim)
+ *                                   of [CG] 3.2 with C = kv_heads * head_dim
+ *   sym          [L][2][T][C]      uint8 symbols, in [0, bins-2]
+ *   max1         [L][2][T]         fp16 bits: max |x| of each (layer, K|V, token) row
+ *   cdf          [NC][L][2][C][A]  uint16 cumulative frequencies out of 65536;
+ *                                   cdf[0] = 0, cdf[A] = 65536 is implicit
+ *   stream_len   [n_streams]       uint16 byte length of each stream
+ *   slab_off     [n_slabs + 1]     uint64 payload offset of each slab's first stream
+ *   payload      bytes of all streams back to back
+ * with A = max bins, NC = ceil(T / chunk_tokens) chunks, a slab = (chunk j,
+ * layer l, K|V), slabs in (j, l, kv) order, n_slabs = 2*L*NC, and one stream
+ * per (chunk, layer, K|V, token) in that order, n_streams = 2*L*T.  Stream
+ * (j, l, kv, t) codes the C symbols of token j*chunk_tokens + t of (l, kv),
+ * channel 0 first, with the CDF rows of slab (j, l, kv).
+ *
+ * Conventions:
+ *   - The caller allocates every buffer.  The library allocates no memory and
+ *     keeps no state between calls; calls are re-entrant.
+ *   - Every compute call is asynchronous on `stream` (a hipStream_t; NULL is
+ *     the default stream).  Outputs are valid once the stream is synchronised.
+ *   - Errors the host can see return a negative kvc_status at once and launch
+ *     nothing.  Errors found on the device are OR-ed as KVC_DEV_* bits into
+ *     *dev_status (a device int32 the caller zeroes), which may be NULL.
+ *   - Pointers to device buffers must be 4-byte aligned (16-byte alignment
+ *     enables the vectorised paths); `desc->bins` is a host pointer.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_VERSION 1
+
+enum kvc_status {
+    KVC_OK = 0,
+    KVC_ERR_ARG = -1,      /* null/misaligned pointer, bad bins, size out of range */
+    KVC_ERR_CAPACITY = -2, /* a caller buffer is smaller than the call needs */
+    KVC_ERR_HIP = -3       /* a HIP launch failed */
+};
+
+/* device-side findings, OR-ed into *dev_status */
+#define KVC_DEV_NONFINITE 1        /* a row max was Inf or NaN (kvc_quantize) */
+#define KVC_DEV_CORRUPT 2          /* a stream left its coding interval (kvc_decode) */
+#define KVC_DEV_PAYLOAD_OVERFLOW 4 /* the packed payload did not fit (kvc_encode) */
+
+enum kvc_dtype { KVC_F16 = 0, KVC_F32 = 1 };
+
+typedef struct kvc_desc {
+    int32_t n_layers;     /* L, 1..256 */
+    int32_t n_channels;   /* C = kv_heads * head_dim, 1..16384 */
+    int64_t n_tokens;     /* T >= 0 */
+    int32_t chunk_tokens; /* tokens per chunk, 1..65535 ([CG] 2.3 step 3 uses 256) */
+    int32_t reserved;     /* must be 0 */
+    const int32_t *bins;  /* HOST [L][2] (K, V) bin counts, even, 4..256 ([CG] 2.2) */
+} kvc_desc;
+
+/* Library version (KVC_VERSION). */
+int kvc_version(void);
+
+/* Static text for a kvc_status value. */
+const char *kvc_status_string(int status);
+
+/* Sizes.  Each returns a negative kvc_status if the descriptor is invalid.
+ *   kvc_alphabet          A = max over layers and K|V of bins ([CG] 2.3 step 2
+ *                         sizes the CDF by the largest bins value)
+ *   kvc_scratch_bytes     device scratch kvc_encode needs (per-stream slots of
+ *                         round_up(2C+16, 16) bytes, plus 8 bytes per slab)
+ *   kvc_max_payload_bytes an upper bound of the payload: n_streams * (2C+1) */
+int32_t kvc_alphabet(const kvc_desc *desc);
+int64_t kvc_n_chunks(const kvc_desc *desc);
+int64_t kvc_n_slabs(const kvc_desc *desc);
+int64_t kvc_n_streams(const kvc_desc *desc);
+int64_t kvc_cdf_bytes(const kvc_desc *desc);
+int64_t kvc_scratch_bytes(const kvc_desc *desc);
+int64_t kvc_max_payload_bytes(const kvc_desc *desc);
+
+/*
+ * Group quantization, [CG] 2.3 step 1 (and 2.2 for the per-layer bins).
+ * For each (layer l, K|V, token) row x of C channels, with MAX = bins/2 - 1:
+ *   max1 = max_c |x_c|                       (exact, stored as fp16)
+ *   factor = MAX / max1                      (one IEEE fp32 division; 0 if max1 = 0)
+ *   sym_c = round_half_even(fp32(x_c * factor) + MAX)   in [0, 2*MAX]
+ * every fp32 operation rounded on its own (no fused multiply-add).
+ *   kv    [L][2][T][C] fp16 (device, read)
+ *   sym   [L][2][T][C] uint8 (device, written)
+ *   max1  [L][2][T] fp16 bits (device, written)
+ *   cdf   NULL, or [NC][L][2][C][A] uint16 (device, written): when given, the
+ *         CDFs of kvc_cdf are produced in the same pass
+ * A row holding Inf or NaN sets KVC_DEV_NONFINITE; its outputs are unspecified.
+ */
+int kvc_quantize(const kvc_desc *desc, const uint16_t *kv, uint8_t *sym, uint16_t *max1,
+                 uint16_t *cdf, int32_t *dev_status, void *stream);
+
+/*
+ * Symbol statistics to CDFs, [CG] 2.3 step 2, per 256-token chunk (step 3).
+ * For chunk j with N_j tokens, layer, K|V and channel c: n_s = count of
+ * symbol s in the chunk's column, C_k = n_0 + .. + n_{k-1}, K = 65536 - A,
+ *   cdf_k = k + floor(C_k * K / N_j),  k = 0..A-1     (every frequency >= 1)
+ *   sym  [L][2][T][C] uint8 (device, read; values >= A are counted as A-1)
+ *   cdf  [NC][L][2][C][A] uint16 (device, written)
+ */
+int kvc_cdf(const kvc_desc *desc, const uint8_t *sym, uint16_t *cdf, void *stream);
+
+/*
+ * Range coding of every stream and packing, [CG] 2.1 (ac_enc) and 1.2 point 3.
+ * Per stream: r = range >> 16; low += r*cdf_s; range = r*f_s; renormalise by
+ * bytes while range < 2^24; at the end round low up to a multiple of 2^24;
+ * the stream is that number in base 256 without its zero first byte and
+ * without trailing zero bytes.  Then stream_len, the slab offsets (exclusive
+ * scan) and the payload (streams back to back in stream order) are written.
+ *   sym         [L][2][T][C] uint8 (device, read)
+ *   cdf         [NC][L][2][C][A] uint16 (device, read)
+ *   scratch     device scratch of scratch_bytes >= kvc_scratch_bytes (else KVC_ERR_CAPACITY)
+ *   stream_len  [n_streams] uint16 (device, written)
+ *   slab_off    [n_slabs + 1] uint64 (device, written; slab_off[n_slabs] = payload size)
+ *   payload     payload_cap bytes (device, written); if the payload is larger,
+ *               KVC_DEV_PAYLOAD_OVERFLOW is set and only bytes below the cap are written
+ */
+int kvc_encode(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf, void *scratch,
+               int64_t scratch_bytes, uint16_t *stream_len, uint64_t *slab_off, uint8_t *payload,
+               int64_t payload_cap, int32_t *dev_status, void *stream);
+
+/*
+ * Parallel decode with fused dequantization, [CG] 2.4 steps 1-2.
+ * Per stream: code = first 4 bytes (big-endian), range = 2^32-1; per channel
+ * r = range >> 16, s = the largest k with r*cdf_k <= code, code -= r*cdf_s,
+ * range = r*f_s, refill bytes while range < 2^24 (bytes past the stream read
+ * as 0).  Then y = fp32(fp32(s - MAX) / MAX) * max1, rounded to out_dtype.
+ *   payload        payload_bytes bytes (device, read; never read past payload_bytes)
+ *   slab_off       [n_slabs + 1] uint64 (device, read)
+ *   stream_len     [n_streams] uint16 (device, read)
+ *   cdf            [NC][L][2][C][A] uint16 (device, read)
+ *   max1           [L][2][T] fp16 bits (device, read; may be NULL when out is NULL)
+ *   sym_out        NULL, or [L][2][T][C] uint8 (device, written): decoded symbols
+ *   out            NULL, or [L][2][T][C] of out_dtype (device, written)
+ * A stream inconsistent with its CDFs sets KVC_DEV_CORRUPT; C symbols are
+ * still written for it.
+ */
+int kvc_decode(const kvc_desc *desc, const uint8_t *payload, int64_t payload_bytes,
+               const uint64_t *slab_off, const uint16_t *stream_len, const uint16_t *cdf,
+               const uint16_t *max1, uint8_t *sym_out, void *out, int32_t out_dtype,
+               int32_t *dev_status, void *stream);
+
+/*
+ * Dequantization on its own, [CG] 2.4 step 2, in the page's order:
+ *   y = fp32(fp32(sym - MAX) / MAX) * max1, then rounded to out_dtype.
+ *   sym   [L][2][T][C] uint8 (device, read)
+ *   max1  [L][2][T] fp16 bits (device, read)
+ *   out   [L][2][T][C] of out_dtype (device, written)
+ */
+int kvc_dequantize(const kvc_desc *desc, const uint8_t *sym, const uint16_t *max1, void *out,
+                   int32_t out_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVC_H */

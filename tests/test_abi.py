@@ -1,0 +1,81 @@
+"""libkvc.so loads and exports every entry point include/kvc.h declares, and
+its host-side size queries and argument checks behave (no GPU needed: these
+calls return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import entropy_coding_02_amd as kvc
+import kvgen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "kvc.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvc.LIB_PATH):
+        from entropy_coding_02_amd import build
+        build.build()
+    return kvc.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(kvc.EXPORTED)
+    assert kvc.kvc_version() == 1
+
+
+def test_sizes_match_layout(lib):
+    for name, cfg in kvgen.CONFIGS.items():
+        d = kvc.Desc(cfg.n_layers, cfg.n_channels, cfg.n_tokens, cfg.bins(), cfg.chunk_tokens)
+        NC = -(-cfg.n_tokens // cfg.chunk_tokens)
+        A = int(cfg.bins().max())
+        assert d.alphabet == A
+        assert d.n_chunks == NC
+        assert d.n_slabs == NC * 2 * cfg.n_layers
+        assert d.n_streams == 2 * cfg.n_layers * cfg.n_tokens
+        assert d.cdf_bytes == NC * 2 * cfg.n_layers * cfg.n_channels * A * 2
+        slot = (2 * cfg.n_channels + 16 + 15) // 16 * 16
+        assert d.scratch_bytes == d.n_streams * slot + 8 * d.n_slabs
+        assert d.max_payload_bytes == d.n_streams * (2 * cfg.n_channels + 1)
+    # the write-up's validation shape: 256 tokens = one chunk, 16,384 streams
+    c2 = kvgen.CONFIGS["c2"]
+    d = kvc.Desc(c2.n_layers, c2.n_channels, c2.n_tokens, c2.bins())
+    assert d.n_chunks == 1 and d.n_streams == 16384 and d.cdf_bytes == 4194304
+
+
+@pytest.mark.parametrize("bad", [
+    dict(bins=[[3, 16]]), dict(bins=[[2, 16]]), dict(bins=[[258, 16]]), dict(bins=[[31, 16]]),
+    dict(n_channels=0), dict(n_channels=16385), dict(chunk_tokens=0), dict(chunk_tokens=65536),
+    dict(n_tokens=-1),
+])
+def test_invalid_descriptors_rejected(lib, bad):
+    args = dict(n_layers=1, n_channels=16, n_tokens=64, bins=[[32, 16]], chunk_tokens=256)
+    args.update(bad)
+    d = kvc.Desc(args["n_layers"], args["n_channels"], args["n_tokens"], args["bins"], args["chunk_tokens"])
+    assert lib.kvc_alphabet(d.ref) == kvc.KVC_ERR_ARG
+    assert lib.kvc_scratch_bytes(d.ref) == kvc.KVC_ERR_ARG
+    # compute entry points reject before touching the GPU
+    assert lib.kvc_quantize(d.ref, 16, 16, 16, None, None, None) == kvc.KVC_ERR_ARG
+
+
+def test_null_and_misaligned_pointers_rejected(lib):
+    d = kvc.Desc(1, 16, 64, [[32, 16]])
+    assert lib.kvc_quantize(d.ref, None, 64, 64, None, None, None) == kvc.KVC_ERR_ARG
+    assert lib.kvc_quantize(d.ref, 66, 64, 64, None, None, None) == kvc.KVC_ERR_ARG  # kv % 4 != 0
+    assert lib.kvc_encode(d.ref, 64, 64, 64, 1, 64, 64, 64, 100, None, None) == kvc.KVC_ERR_CAPACITY
+    assert lib.kvc_decode(d.ref, 64, 10, 64, 64, 64, 64, None, 64, 7, None, None) == kvc.KVC_ERR_ARG
+    assert lib.kvc_dequantize(d.ref, 64, 64, 64, 9, None) == kvc.KVC_ERR_ARG
+    assert lib.kvc_status_string(kvc.KVC_ERR_CAPACITY) == b"buffer too small"

@@ -1,0 +1,124 @@
+"""The GPU lane coder (entropy_coding_02_amd/csrc/lane_coder.h) compiled for
+the host and compared with the oracle stream by stream: byte-identical
+encodes (including carries into bytes already written and the trailing-zero
+trim reaching back into them) and identical decodes from streams placed at
+every byte alignment, up against the exact end of the buffer."""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from test_oracle_coder import _straddling_sequence, cdf_from_counts
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "hostsim", "hostsim.hip")
+LIB = os.path.join(HERE, "hostsim", "libhostsim.so")
+HDR = os.path.join(os.path.dirname(HERE), "entropy_coding_02_amd", "csrc", "lane_coder.h")
+
+
+@pytest.fixture(scope="module")
+def hs():
+    newest = max(os.path.getmtime(SRC), os.path.getmtime(HDR))
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < newest:
+        tmp = LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["/opt/rocm/bin/hipcc", "-std=c++17", "-O2", "--offload-arch=gfx950",
+                               "-fPIC", "-shared", "-o", tmp, SRC])
+        os.replace(tmp, LIB)
+    lib = ctypes.CDLL(LIB)
+    P = ctypes.c_void_p
+    lib.hostsim_encode_stream.restype = ctypes.c_int64
+    lib.hostsim_encode_stream.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P]
+    lib.hostsim_decode_stream.restype = ctypes.c_int
+    lib.hostsim_decode_stream.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int32, ctypes.c_int32, P, P]
+    return lib
+
+
+def h_encode(lib, q, rows):
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+    C, A = rows.shape
+    slot = np.full((2 * C + 16 + 15) // 16 * 16, 0xAB, dtype=np.uint8)
+    n = lib.hostsim_encode_stream(q.ctypes.data, C, A, rows.ctypes.data, slot.ctypes.data)
+    return slot[:n].tobytes()
+
+
+def h_decode(lib, buf, off, length, rows, cap=None):
+    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+    C, A = rows.shape
+    q = np.empty(C, dtype=np.uint8)
+    cap = buf.size if cap is None else cap
+    bad = lib.hostsim_decode_stream(buf.ctypes.data, cap, off, length, C, A, rows.ctypes.data,
+                                    q.ctypes.data)
+    return q, bool(bad)
+
+
+def check(lib, q, rows):
+    want = oracle.encode_stream(np.asarray(q, np.uint8), rows)
+    got = h_encode(lib, q, rows)
+    assert got == want, (len(got), len(want))
+    return want
+
+
+def test_random_and_skewed_streams(hs):
+    rng = np.random.default_rng(31)
+    for trial in range(800):
+        A = int(rng.choice([2, 4, 6, 16, 32, 64, 256]))
+        C = int(rng.integers(1, 300))
+        rows = np.array([cdf_from_counts((rng.integers(0, 3, A) * rng.integers(1, 40000, A)).tolist())
+                         for _ in range(C)], dtype=np.uint16)
+        q = rng.integers(0, A, C)
+        check(hs, q, rows)
+
+
+def test_forced_carries_through_written_bytes(hs):
+    """Straddling sequences: runs of 0xFF long enough that the carry reaches
+    dwords the lane has already written."""
+    rng = np.random.default_rng(77)
+    for trial in range(600):
+        A = int(rng.choice([2, 4, 16, 32, 64]))
+        C = int(rng.integers(20, 200))
+        rows = np.array([cdf_from_counts((rng.integers(0, 4, A) * rng.integers(1, 30000, A) + 1).tolist())
+                         for _ in range(C)], dtype=np.uint16)
+        q = _straddling_sequence(rows, rng, int(rng.integers(1, C)), resolve_up=bool(trial % 2))
+        check(hs, q, rows)
+
+
+def test_zero_tail_trim_reaches_written_dwords(hs):
+    rows = np.tile(cdf_from_counts([10, 1, 1, 1]), (400, 1))
+    for n_tail in range(0, 40):
+        q = np.zeros(400, np.uint8)
+        q[: 400 - n_tail - 1] = np.random.default_rng(n_tail).integers(0, 4, 400 - n_tail - 1)
+        check(hs, q, rows)  # the final all-zero symbols give trailing zero bytes
+    check(hs, np.zeros(400, np.uint8), rows)  # empty stream
+
+
+def test_decode_every_alignment_up_to_buffer_end(hs):
+    rng = np.random.default_rng(5)
+    A, C = 32, 96
+    rows = np.array([cdf_from_counts(rng.integers(0, 60, A).tolist()) for _ in range(C)], dtype=np.uint16)
+    streams, syms = [], []
+    for i in range(40):
+        q = rng.integers(0, A, C).astype(np.uint8)
+        syms.append(q)
+        streams.append(check(hs, q, rows))
+    for lead in range(8):  # stream start at every byte alignment
+        buf = np.frombuffer(bytes(lead) + b"".join(streams), dtype=np.uint8).copy()
+        off = lead
+        for q, s in zip(syms, streams):
+            for cap in (buf.size, off + len(s)):  # padded buffer, or the stream ends the buffer
+                got, bad = h_decode(hs, buf, off, len(s), rows, cap=cap)
+                assert not bad and np.array_equal(got, q)
+            off += len(s)
+
+
+def test_corrupt_streams_match_oracle_flag(hs):
+    rows = np.tile(cdf_from_counts([5, 20, 5, 1]), (64, 1))
+    for data in (b"\xff" * 16, b"\xfe\xff\xff\xff\x00", bytes(range(200, 256))):
+        buf = np.frombuffer(data, np.uint8).copy()
+        q_o, bad_o = oracle.decode_stream(data, rows)
+        q_h, bad_h = h_decode(hs, buf, 0, len(data), rows)
+        assert bad_o == bad_h and np.array_equal(q_o, q_h)
