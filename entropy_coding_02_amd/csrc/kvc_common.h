@@ -8,6 +8,11 @@
 
 #define KVC_MAX_LAYERS 256
 
+// Pointers into LDS.  Typed with the LDS address space so the compiler emits
+// ds_* instructions (32-bit addresses, own wait counter) rather than flat ones.
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
 // Everything a kernel needs to know about the problem, passed by value.
 // Slab s = (chunk j, layer l, K|V kv) with lk = 2*l + kv; j = s / (2L).
 struct KParams {

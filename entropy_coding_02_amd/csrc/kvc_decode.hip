@@ -13,12 +13,13 @@
 #include "kvc_common.h"
 #include "kvc_kernels.h"
 #include "lane_coder.h"
+#include "pair_tile.h"
 
 namespace {
 
 enum { ODT_F16 = 0, ODT_F32 = 1, ODT_NONE = 2 };
 
-template <bool VEC, int ODT>
+template <bool VEC, int ODT, int NSTEP>
 __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payload,
                                                 int64_t payload_bytes,
                                                 const uint64_t *__restrict__ slab_off,
@@ -26,17 +27,27 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
                                                 const uint16_t *__restrict__ cdf,
                                                 const uint16_t *__restrict__ max1,
                                                 uint8_t *__restrict__ sym_out, void *__restrict__ out,
-                                                KParams p, int32_t *status)
+                                                KParams p, int32_t *status, int CT)
 {
-    __shared__ float lut[256];
+    // LDS: lut[256] f32 | ring[256][17] u32 | rows16 [CT][P2] u16 | pairs [CT][A] u32
+    extern __shared__ uint32_t lds[];
     __shared__ uint32_t s_red[4];
+    constexpr uint32_t P2 = 1u << NSTEP;  // search row length: A padded to a power of two
+    const int C = p.C, A = p.A;
+    float *lut = (float *)lds;
+    lds_u32 *const ring = (lds_u32 *)(lds + 256) + threadIdx.x * 17u;
+    const int n16 = (CT * (int)P2 + 1) / 2;
+    lds_u32 *const tile = (lds_u32 *)(lds + 256 + 256 * 17);
+    lds_u16 *const r16 = (lds_u16 *)tile;
+    lds_u32 *const pr = tile + n16;
+
     const int bps = (p.Tc + 255) / 256;
     const int64_t slab = blockIdx.x / bps;
     const int tb = (int)(blockIdx.x - slab * bps);
     const int t = tb * 256 + (int)threadIdx.x;
     const SlabGeom g = slab_geom(p, slab);
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int C = p.C, A = p.A;
+    const bool active = t < g.nj;
 
     // bytes of the slab's streams before this block (only when chunk_tokens > 256)
     uint32_t pre = 0;
@@ -48,7 +59,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
     pre = s_red[0] + s_red[1] + s_red[2] + s_red[3];
     __syncthreads();
     // exclusive scan of this block's lengths
-    const uint32_t len = t < g.nj ? stream_len[g.sid0 + t] : 0u;
+    const uint32_t len = active ? stream_len[g.sid0 + t] : 0u;
     uint32_t incl = len;
     for (int off = 1; off < 64; off <<= 1) {
         uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
@@ -59,75 +70,88 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
         const int M = p.maxq[g.lk];
         lut[threadIdx.x] = (float)((int)threadIdx.x - M) / (float)M;
     }
+    // padding of the search rows (never rewritten by the tile stores)
+    if (P2 > (uint32_t)A)
+        for (int e = threadIdx.x; e < CT * (int)P2; e += 256)
+            if ((uint32_t)(e & (P2 - 1)) >= (uint32_t)A) r16[e] = 0xFFFFu;
     __syncthreads();
     uint32_t wbase = 0;
     for (int i = 0; i < wid; ++i) wbase += s_red[i];
-    if (t >= g.nj) return;  // no barriers below
 
-    const int64_t row = g.row0 + t;
-    const uint64_t off = slab_off[slab] + pre + wbase + incl - len;
-    StreamIn in;
-    in.init(payload, off, len, (uint64_t)payload_bytes);
+    const int64_t row = g.row0 + (active ? t : 0);
+    const uint64_t off = active ? slab_off[slab] + pre + wbase + incl - len : 0;
+    RingIn<lds_u32 *> in;
+    in.init(payload, off, len, (uint64_t)payload_bytes, ring);
     DecState d;
     dec_init(d, in);
-    const uint16_t *rows = cdf + slab * C * A;
     const float m = (ODT != ODT_NONE) ? kvc_h2f(max1[row]) : 0.0f;
-    const uint32_t step0 = dec_step0((uint32_t)A);
     uint32_t bad = 0;
-    uint8_t *so = sym_out ? sym_out + row * C : nullptr;
+    uint8_t *so = (sym_out && active) ? sym_out + row * C : nullptr;
+    const uint16_t *srows = cdf + slab * C * A;
+    const int ntiles = (C + CT - 1) / CT;
 
-    auto decode1 = [&](int c) -> uint32_t {
-        return dec_symbol(d, rows + c * A, (uint32_t)A, step0, in, &bad);
-    };
-
-    if constexpr (VEC) {
-        // C % 16 == 0: 16 symbols per round, written with 16-byte stores
-        for (int c0 = 0; c0 < C; c0 += 16) {
-            uint32_t sw[4] = {0, 0, 0, 0};
-            uint32_t hw[8];
-            float fw[16];
+    for (int it = 0; it < ntiles; ++it) {
+        const int c0 = it * CT, c1 = min(C, c0 + CT);
+        // stage this tile's rows: all waves are done with the previous one
+        __syncthreads();
+        {
+            PairTile pt;
+            pt.load(srows, c0, CT, C, A);
+            pt.store(pr, CT, A, r16, (int)P2);
+        }
+        __syncthreads();
+        if (!active) continue;
+        if constexpr (VEC) {
+            // C % 16 == 0 and CT % 16 == 0: groups of 8 symbols, 16-byte fp16 stores
+#pragma unroll 1
+            for (int cg = c0; cg < c1; cg += 8) {
+                in.group();
+                uint32_t sw[2] = {0, 0};
+                uint32_t hw[4];
+                float fw[8];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                uint32_t s = decode1(c0 + i);
-                sw[i >> 2] |= s << (8 * (i & 3));
-                if constexpr (ODT != ODT_NONE) {
-                    float y = lut[s] * m;
-                    if constexpr (ODT == ODT_F16) {
-                        if (i & 1)
-                            hw[i >> 1] |= kvc_f2h(y) << 16;
-                        else
-                            hw[i >> 1] = kvc_f2h(y);
-                    } else {
-                        fw[i] = y;
+                for (int i = 0; i < 8; ++i) {
+                    const int cl = cg - c0 + i;
+                    const uint32_t s = dec_symbol<NSTEP>(d, r16 + cl * P2, pr + cl * A, (uint32_t)A, in, &bad);
+                    sw[i >> 2] |= s << (8 * (i & 3));
+                    if constexpr (ODT != ODT_NONE) {
+                        const float y = lut[s] * m;
+                        if constexpr (ODT == ODT_F16) {
+                            if (i & 1)
+                                hw[i >> 1] |= kvc_f2h(y) << 16;
+                            else
+                                hw[i >> 1] = kvc_f2h(y);
+                        } else {
+                            fw[i] = y;
+                        }
                     }
                 }
+                if (so) *(uint2 *)(so + cg) = make_uint2(sw[0], sw[1]);
+                if constexpr (ODT == ODT_F16) {
+                    *(uint4 *)((uint16_t *)out + row * C + cg) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                } else if constexpr (ODT == ODT_F32) {
+                    float4 *o = (float4 *)((float *)out + row * C + cg);
+                    o[0] = make_float4(fw[0], fw[1], fw[2], fw[3]);
+                    o[1] = make_float4(fw[4], fw[5], fw[6], fw[7]);
+                }
             }
-            if (so) *(uint4 *)(so + c0) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
-            if constexpr (ODT == ODT_F16) {
-                uint4 *o = (uint4 *)((uint16_t *)out + row * C + c0);
-                o[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-                o[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-            } else if constexpr (ODT == ODT_F32) {
-                float4 *o = (float4 *)((float *)out + row * C + c0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    o[i] = make_float4(fw[4 * i], fw[4 * i + 1], fw[4 * i + 2], fw[4 * i + 3]);
-            }
-        }
-    } else {
-        for (int c = 0; c < C; ++c) {
-            uint32_t s = decode1(c);
-            if (so) so[c] = (uint8_t)s;
-            if constexpr (ODT != ODT_NONE) {
-                float y = lut[s] * m;
-                if constexpr (ODT == ODT_F16)
-                    ((uint16_t *)out)[row * C + c] = (uint16_t)kvc_f2h(y);
-                else
-                    ((float *)out)[row * C + c] = y;
+        } else {
+            for (int c = c0; c < c1; ++c) {
+                if ((c & 7) == 0) in.group();
+                const int cl = c - c0;
+                const uint32_t s = dec_symbol<NSTEP>(d, r16 + cl * P2, pr + cl * A, (uint32_t)A, in, &bad);
+                if (so) so[c] = (uint8_t)s;
+                if constexpr (ODT != ODT_NONE) {
+                    const float y = lut[s] * m;
+                    if constexpr (ODT == ODT_F16)
+                        ((uint16_t *)out)[row * C + c] = (uint16_t)kvc_f2h(y);
+                    else
+                        ((float *)out)[row * C + c] = y;
+                }
             }
         }
     }
-    if (bad) kvc_flag(status, KVC_DEV_CORRUPT);
+    if (active && bad) kvc_flag(status, KVC_DEV_CORRUPT);
 }
 
 // Dequantization alone: one wavefront per row; each wave keeps the table of
@@ -164,6 +188,23 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ sym
 
 }  // namespace
 
+// Channels per LDS tile: search rows of P2 entries, CT * P2 = 1024, at least 16
+// (12.8 KB of LDS per block at A = 32, so 8 blocks fit on a CU).
+static int dec_tile_channels(int A)
+{
+    int P2 = 1;
+    while (P2 < A) P2 <<= 1;
+    return P2 <= 64 ? 1024 / P2 : 16;
+}
+
+static size_t dec_lds_bytes(int A, int CT)
+{
+    int P2 = 1;
+    while (P2 < A) P2 <<= 1;
+    const size_t n16 = ((size_t)CT * P2 + 1) / 2;
+    return sizeof(uint32_t) * (256 + 256 * 17 + n16 + (size_t)CT * A);
+}
+
 hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const uint64_t *slab_off,
                          const uint16_t *stream_len, const uint16_t *cdf, const uint16_t *max1,
                          uint8_t *sym_out, void *out, int out_dtype, const KParams &p,
@@ -173,18 +214,33 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
     const int64_t bps = (p.Tc + 255) / 256;
     dim3 grid((unsigned)(bps * p.n_slabs)), block(256);
     const int odt = out ? out_dtype : ODT_NONE;
-#define KVC_DEC(V, O)                                                                            \
-    hipLaunchKernelGGL((k_decode<V, O>), grid, block, 0, stream, payload, payload_bytes, slab_off, \
-                       stream_len, cdf, max1, sym_out, out, p, status)
-    if (vec) {
-        if (odt == ODT_F16) KVC_DEC(true, ODT_F16);
-        else if (odt == ODT_F32) KVC_DEC(true, ODT_F32);
-        else KVC_DEC(true, ODT_NONE);
-    } else {
-        if (odt == ODT_F16) KVC_DEC(false, ODT_F16);
-        else if (odt == ODT_F32) KVC_DEC(false, ODT_F32);
-        else KVC_DEC(false, ODT_NONE);
+    const int CT = dec_tile_channels(p.A);
+    const size_t lds = dec_lds_bytes(p.A, CT);
+    vec = vec && (CT % 16 == 0);
+    const int nstep = (int)cdf_nstep((uint32_t)p.A);
+#define KVC_DEC(V, O, N)                                                                             \
+    hipLaunchKernelGGL((k_decode<V, O, N>), grid, block, lds, stream, payload, payload_bytes,        \
+                       slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
+#define KVC_DEC_N(V, O)                                                                              \
+    switch (nstep) {                                                                                 \
+    case 2: KVC_DEC(V, O, 2); break;                                                                 \
+    case 3: KVC_DEC(V, O, 3); break;                                                                 \
+    case 4: KVC_DEC(V, O, 4); break;                                                                 \
+    case 5: KVC_DEC(V, O, 5); break;                                                                 \
+    case 6: KVC_DEC(V, O, 6); break;                                                                 \
+    case 7: KVC_DEC(V, O, 7); break;                                                                 \
+    default: KVC_DEC(V, O, 8); break;                                                                \
     }
+    if (vec) {
+        if (odt == ODT_F16) KVC_DEC_N(true, ODT_F16)
+        else if (odt == ODT_F32) KVC_DEC_N(true, ODT_F32)
+        else KVC_DEC_N(true, ODT_NONE)
+    } else {
+        if (odt == ODT_F16) KVC_DEC_N(false, ODT_F16)
+        else if (odt == ODT_F32) KVC_DEC_N(false, ODT_F32)
+        else KVC_DEC_N(false, ODT_NONE)
+    }
+#undef KVC_DEC_N
 #undef KVC_DEC
     return hipGetLastError();
 }

@@ -13,39 +13,71 @@
 #include "kvc_common.h"
 #include "kvc_kernels.h"
 #include "lane_coder.h"
+#include "pair_tile.h"
 
 namespace {
 
+// One lane per stream, 256 tokens of one slab per block.  The slab's CDF is
+// walked in tiles of CT channels (CT * A = 2048 pairs, 8 KB), double-buffered
+// in LDS: while a tile is coded, the next one is in flight in registers.
+// All lanes of a wave read the same tile row at the same step, so a pair
+// lookup is a broadcast or a distinct bank.
 template <bool VEC16>
 __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
                                                 const uint16_t *__restrict__ cdf,
                                                 uint8_t *__restrict__ slots,
-                                                uint16_t *__restrict__ stream_len, KParams p)
+                                                uint16_t *__restrict__ stream_len, KParams p, int CT)
 {
+    extern __shared__ uint32_t lds[];
     const int bps = (p.Tc + 255) / 256;
     const int64_t slab = blockIdx.x / bps;
     const int t = (int)(blockIdx.x - slab * bps) * 256 + (int)threadIdx.x;
     const SlabGeom g = slab_geom(p, slab);
-    if (t >= g.nj) return;  // this kernel has no barriers
     const int C = p.C, A = p.A;
+    const bool active = t < g.nj;
     const int64_t sid = g.sid0 + t;
-    const uint8_t *q = sym + (g.row0 + t) * C;
+    const uint8_t *q = sym + (g.row0 + (active ? t : 0)) * C;
     const uint16_t *rows = cdf + slab * C * A;
-    SlotOut out{(uint32_t *)(slots + sid * p.slot_bytes)};
+    lds_u32 *const tiles = (lds_u32 *)lds;
+    const int ntiles = (C + CT - 1) / CT;
+
+    PairTile pt;
+    pt.load(rows, 0, CT, C, A);
+    pt.store(tiles, CT, A);
+    __syncthreads();
+
+    SlotOut out{(uint32_t *)(slots + (active ? sid : 0) * p.slot_bytes)};
     EncState e;
     enc_init(e);
-    auto code = [&](int c, uint32_t s) { enc_symbol(e, rows + c * A, (uint32_t)A, s, out); };
-    if constexpr (VEC16) {
-        for (int c0 = 0; c0 < C; c0 += 16) {
-            uint4 v = *(const uint4 *)(q + c0);
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int it = 0; it < ntiles; ++it) {
+        const int c0 = it * CT, c1 = min(C, c0 + CT);
+        if (it + 1 < ntiles) pt.load(rows, c0 + CT, CT, C, A);
+        const lds_u32 *tile = tiles + (it & 1) * CT * A;
+        if (active) {
+            if constexpr (VEC16) {
+                for (int cg = c0; cg < c1; cg += 16) {
+                    const uint4 v = *(const uint4 *)(q + cg);
+                    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+                    const lds_u32 *trow = tile + (cg - c0) * A;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) code(c0 + i, (w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+                    for (int i = 0; i < 16; ++i) {
+                        uint32_t s = (wv[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+                        s = s < (uint32_t)A ? s : (uint32_t)(A - 1);
+                        enc_pair(e, trow[i * A + s], out);
+                    }
+                }
+            } else {
+                for (int c = c0; c < c1; ++c) {
+                    uint32_t s = q[c];
+                    s = s < (uint32_t)A ? s : (uint32_t)(A - 1);
+                    enc_pair(e, tile[(c - c0) * A + s], out);
+                }
+            }
         }
-    } else {
-        for (int c = 0; c < C; ++c) code(c, q[c]);
+        if (it + 1 < ntiles) pt.store(tiles + ((it + 1) & 1) * CT * A, CT, A);
+        __syncthreads();
     }
-    stream_len[sid] = (uint16_t)enc_finish(e, out);
+    if (active) stream_len[sid] = (uint16_t)enc_finish(e, out);
 }
 
 __global__ __launch_bounds__(256) void k_slab_sum(const uint16_t *__restrict__ stream_len,
@@ -150,6 +182,9 @@ __global__ void k_zero_u64(uint64_t *dst) { *dst = 0; }
 
 }  // namespace
 
+// Channels per LDS tile: 2048 pairs (8 KB) per buffer; at least 16 channels.
+static int enc_tile_channels(int A) { return A <= 128 ? 2048 / A : 16; }
+
 hipError_t launch_zero_u64(uint64_t *dst, hipStream_t stream)
 {
     hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(1), 0, stream, dst);
@@ -164,10 +199,12 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
     if (p.n_slabs == 0) return launch_zero_u64(slab_off, stream);
     const int64_t bps = (p.Tc + 255) / 256;
     dim3 grid((unsigned)(bps * p.n_slabs));
-    if (vec16)
-        hipLaunchKernelGGL(k_encode<true>, grid, dim3(256), 0, stream, sym, cdf, slots, stream_len, p);
+    const int CT = enc_tile_channels(p.A);
+    const size_t lds = 2 * (size_t)CT * p.A * sizeof(uint32_t);
+    if (vec16 && CT % 16 == 0)
+        hipLaunchKernelGGL(k_encode<true>, grid, dim3(256), lds, stream, sym, cdf, slots, stream_len, p, CT);
     else
-        hipLaunchKernelGGL(k_encode<false>, grid, dim3(256), 0, stream, sym, cdf, slots, stream_len, p);
+        hipLaunchKernelGGL(k_encode<false>, grid, dim3(256), lds, stream, sym, cdf, slots, stream_len, p, CT);
     hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
                        slab_total, p);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, slab_total, slab_off, p.n_slabs,

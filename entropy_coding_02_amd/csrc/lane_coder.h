@@ -134,49 +134,86 @@ KVC_HD uint32_t enc_finish(EncState &e, const Out &out)
 
 // ----------------------------------------------------------------- decoder
 
-// Reads one stream [pos, end) of a byte buffer of `cap` bytes as big-endian
-// dwords; bytes at or past `end` read as zero and are never loaded, and no
-// load touches bytes at or past `cap`.  `base` must be 4-byte aligned.
-struct StreamIn {
-    const uint8_t *base;
-    uint64_t a;    // aligned address of the dword held in `cur`
-    uint64_t end;  // stream end (exclusive)
-    uint64_t cap;  // buffer size
-    uint32_t sh;   // (start & 3) * 8
-    uint32_t cur;  // big-endian dword at a, masked to the stream
+// Byte feed of one stream through a 64-byte per-lane ring in LDS.
+//
+// The stream [start, start+len) of a buffer of `cap` bytes (a multiple of 4,
+// at least 4) is read as aligned dwords from a0 = start & ~3.  Every group of
+// 8 symbols the lane takes in 16 fetched bytes (if it had asked for them) and,
+// while at most 48 bytes are unread, asks for the next 16 with four clamped
+// dword loads whose results are only used one group later.  8 symbols use at
+// most 16 bytes, so with 64 ring bytes the reader never catches up with the
+// writer.  The reader keeps one ring dword ahead in a register; bytes at or
+// past the stream end read as zero.
+template <class Ring>
+struct RingIn {
+    const uint8_t *p;  // base + a0
+    Ring ring;         // this lane's 16 ring dwords (dword i of the stream at ring[i & 15])
+    uint32_t end;      // stream end, from p
+    uint32_t lim;      // largest offset from p at which a dword may be loaded
+    uint32_t sh;       // (start & 3) * 8
+    uint32_t pf;       // bytes fetched into the ring (multiple of 16)
+    uint32_t rd;       // offset of the next dword to read from the ring
+    uint32_t cur;      // big-endian dword being consumed, masked
+    uint32_t nxt;      // big-endian dword after it, masked
+    uint32_t st[4];    // raw dwords in flight for [pf, pf + 16)
+    uint32_t want;     // st[] holds a pending fetch
 
-    KVC_HD uint32_t load_be(uint64_t addr) const
+    KVC_HD uint32_t load(uint32_t off) const { return *(const uint32_t *)(p + (off < lim ? off : lim)); }
+    KVC_HD uint32_t be(uint32_t rawv, uint32_t off) const
     {
-        if (addr >= end) return 0u;
-        uint32_t v;
-        if (addr + 4u <= cap) {
-            v = kvc_bswap32(*(const uint32_t *)(base + addr));
-        } else {
-            v = 0;
-            for (uint32_t i = 0; i < 4; ++i)
-                v |= (addr + i < cap ? (uint32_t)base[addr + i] : 0u) << (24u - 8u * i);
-        }
-        uint64_t keep = end - addr;
-        if (keep < 4u) v &= ~(0xFFFFFFFFu >> (8u * (uint32_t)keep));
-        return v;
+        const uint32_t v = kvc_bswap32(rawv);
+        const uint32_t keep = end > off ? end - off : 0u;
+        return keep >= 4u ? v : (keep == 0u ? 0u : v & ~(0xFFFFFFFFu >> (8u * keep)));
     }
-    KVC_HD void init(const uint8_t *b, uint64_t start, uint64_t len, uint64_t capacity)
+    KVC_HD void issue()
     {
-        base = b;
-        end = start + len;
-        cap = capacity;
-        a = start & ~(uint64_t)3;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st[j] = load(pf + 4u * (uint32_t)j);
+        want = 1;
+    }
+    KVC_HD void commit()
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ring[((pf >> 2) + (uint32_t)j) & 15u] = st[j];
+        pf += 16u;
+        want = 0;
+    }
+    KVC_HD void init(const uint8_t *b, uint64_t start, uint64_t len, uint64_t capacity, Ring r)
+    {
+        uint64_t a0 = start & ~(uint64_t)3;
         sh = (uint32_t)(start & 3u) * 8u;
-        cur = load_be(a);
-        if (start > a) cur &= 0xFFFFFFFFu >> sh;  // bytes before the stream are not ours
+        end = (uint32_t)(start - a0 + len);
+        if (a0 + 4u > capacity) {  // only an empty stream at the very end of the buffer
+            a0 = capacity - 4u;
+            end = 0;
+        }
+        p = b + a0;
+        const uint64_t room = capacity - 4u - a0;
+        lim = room > 0xFFFFFFFCull ? 0xFFFFFFFCu : (uint32_t)room;
+        ring = r;
+        pf = 0;
+        issue();
+        commit();
+        issue();
+        commit();  // 32 bytes in the ring
+        issue();   // the next 16 in flight
+        cur = be(ring[0], 0);
+        nxt = be(ring[1], 4);
+        rd = 8;
+    }
+    // Once per group of 8 symbols.
+    KVC_HD void group()
+    {
+        if (want) commit();
+        if (pf - rd <= 48u) issue();
     }
     // The next 4 stream bytes as a big-endian dword.
     KVC_HD uint32_t next()
     {
-        uint32_t nxt = load_be(a + 4u);
-        uint32_t v = sh ? (cur << sh) | (nxt >> (32u - sh)) : cur;
+        const uint32_t v = sh ? (cur << sh) | (nxt >> (32u - sh)) : cur;
         cur = nxt;
-        a += 4u;
+        nxt = be(ring[(rd >> 2) & 15u], rd);
+        rd += 4u;
         return v;
     }
 };
@@ -188,7 +225,8 @@ struct DecState {
     uint32_t nb;  // valid bits in bb
 };
 
-KVC_HD void dec_init(DecState &d, StreamIn &in)
+template <class In>
+KVC_HD void dec_init(DecState &d, In &in)
 {
     d.code = in.next();
     d.bb = (uint64_t)in.next() << 32;
@@ -199,7 +237,8 @@ KVC_HD void dec_init(DecState &d, StreamIn &in)
 // After the symbol with cumulative frequency st and frequency fr was found
 // for r = range >> 16: narrow the interval and refill.  Returns 1 if the
 // stream is inconsistent with the CDF (code outside the new interval).
-KVC_HD uint32_t dec_advance(DecState &d, uint32_t r, uint32_t st, uint32_t fr, StreamIn &in)
+template <class In>
+KVC_HD uint32_t dec_advance(DecState &d, uint32_t r, uint32_t st, uint32_t fr, In &in)
 {
     d.code -= r * st;
     d.range = r * fr;
@@ -219,36 +258,57 @@ KVC_HD uint32_t dec_advance(DecState &d, uint32_t r, uint32_t st, uint32_t fr, S
 
 // ------------------------------------------------- per-symbol table lookups
 
-// Code symbol s with CDF row `row` of A entries (cdf_A = 65536 implicit).
-// Out-of-alphabet symbols are clamped and non-increasing rows get frequency
-// 1, so malformed input cannot make a lane write past its slot.
-template <class Out>
-KVC_HD void enc_symbol(EncState &e, const uint16_t *row, uint32_t A, uint32_t s, const Out &out)
+// The (start, frequency) pair of symbol s of a CDF row with A entries
+// (cdf_A = 65536 implicit), packed as start | frequency << 16.  A
+// non-increasing row gets frequency 1, so malformed tables cannot stall or
+// overrun the coder.
+KVC_HD uint32_t cdf_pair(uint32_t st, uint32_t nx)
 {
-    s = s < A ? s : A - 1u;
-    uint32_t st = row[s];
-    uint32_t nx = (s + 1u < A) ? (uint32_t)row[s + 1u] : 65536u;
     uint32_t fr = nx > st ? nx - st : 1u;
-    enc_put(e, st, fr, out);
+    return st | (fr << 16);
 }
 
-// Largest k in [0, A) with r * row[k] <= code, by binary lifting from
-// step0 = the largest power of two <= A - 1; then the interval update.
-// Returns the symbol; *bad |= 1 when the stream left its interval.
-KVC_HD uint32_t dec_symbol(DecState &d, const uint16_t *row, uint32_t A, uint32_t step0,
-                           StreamIn &in, uint32_t *bad)
+// Code symbol s whose packed pair is p.
+template <class Out>
+KVC_HD void enc_pair(EncState &e, uint32_t p, const Out &out)
+{
+    enc_put(e, p & 0xFFFFu, p >> 16, out);
+}
+
+// Largest k in [0, A) with r * row[k] <= code, where `row` holds the A
+// cumulative frequencies padded with 0xFFFF up to 2^NSTEP entries: binary
+// lifting over the padded row, then a clamp to A - 1 (a padding entry can
+// only be chosen when every real entry qualifies, and then A - 1 is right).
+template <int NSTEP, class Row>
+KVC_HD uint32_t cdf_search(const Row &row, uint32_t A, uint32_t r, uint32_t code)
+{
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = NSTEP - 1; i >= 0; --i) {
+        const uint32_t k = s + (1u << i);
+        if (r * (uint32_t)row[k] <= code) s = k;
+    }
+    return s < A - 1u ? s : A - 1u;
+}
+
+// Decode one symbol: search `row` (padded cumulative frequencies), take its
+// packed pair from `pairs`, narrow the interval.  *bad |= 1 when the stream
+// left its interval.
+template <int NSTEP, class Row, class Pairs, class In>
+KVC_HD uint32_t dec_symbol(DecState &d, const Row &row, const Pairs &pairs, uint32_t A, In &in,
+                           uint32_t *bad)
 {
     const uint32_t r = d.range >> 16;
-    uint32_t s = 0;
-    for (uint32_t step = step0; step > 0; step >>= 1) {
-        uint32_t k = s + step;
-        if (k < A && r * (uint32_t)row[k] <= d.code) s = k;
-    }
-    const uint32_t st = row[s];
-    const uint32_t nx = (s + 1u < A) ? (uint32_t)row[s + 1u] : 65536u;
-    const uint32_t fr = nx > st ? nx - st : 1u;
-    *bad |= dec_advance(d, r, st, fr, in);
+    const uint32_t s = cdf_search<NSTEP>(row, A, r, d.code);
+    const uint32_t p = pairs[s];
+    *bad |= dec_advance(d, r, p & 0xFFFFu, p >> 16, in);
     return s;
 }
 
-KVC_HD uint32_t dec_step0(uint32_t A) { return 1u << (31 - __builtin_clz(A - 1u)); }
+// Binary-lifting steps for an alphabet of A symbols: log2 of the next power of two.
+KVC_HD uint32_t cdf_nstep(uint32_t A)
+{
+    uint32_t n = 0;
+    while ((1u << n) < A) ++n;
+    return n;
+}

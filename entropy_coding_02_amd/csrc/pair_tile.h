@@ -1,0 +1,55 @@
+// pair_tile.h - staging of CDF rows into LDS as packed (start, frequency)
+// pairs, shared by the encoder and the decoder kernels.
+#pragma once
+
+#include "kvc_common.h"
+#include "lane_coder.h"
+
+// Stage CDF rows [c0, c0+CT) of a slab as packed (start, frequency) pairs.
+// Thread i handles the entry pairs (2j, 2j+1) with index i, i+256, ...: one
+// 4-byte load of cdf[2j], cdf[2j+1] plus cdf[2j+2] for the second frequency
+// (A is even, so rows and pairs are 4-byte aligned).
+struct PairTile {
+    static constexpr int kMaxPer = 8;  // CT * A / 2 / 256 <= 8 for CT * A <= 4096
+    uint32_t w[kMaxPer], n2[kMaxPer];
+
+    __device__ void load(const uint16_t *rows, int c0, int CT, int C, int A)
+    {
+        const int npairs = CT * (A >> 1);
+#pragma unroll
+        for (int i = 0; i < kMaxPer; ++i) {
+            const int e = (int)threadIdx.x + i * 256;
+            w[i] = 0;
+            n2[i] = 65536u;
+            if (e < npairs) {
+                const int cl = e / (A >> 1), k = (e - cl * (A >> 1)) * 2;
+                if (c0 + cl < C) {
+                    const uint16_t *row = rows + (int64_t)(c0 + cl) * A;
+                    w[i] = *(const uint32_t *)(row + k);
+                    if (k + 2 < A) n2[i] = row[k + 2];
+                }
+            }
+        }
+    }
+    // Also writes the starts as rows of P2 uint16 (for the decoder's search).
+    template <class D32, class D16 = lds_u16 *>
+    __device__ void store(D32 dst, int CT, int A, D16 dst16 = nullptr, int P2 = 0) const
+    {
+        const int npairs = CT * (A >> 1);
+#pragma unroll
+        for (int i = 0; i < kMaxPer; ++i) {
+            const int e = (int)threadIdx.x + i * 256;
+            if (e < npairs) {
+                const uint32_t st0 = w[i] & 0xFFFFu, st1 = w[i] >> 16;
+                dst[2 * e] = cdf_pair(st0, st1);
+                dst[2 * e + 1] = cdf_pair(st1, n2[i]);
+                if (dst16) {
+                    const int cl = e / (A >> 1), k = (e - cl * (A >> 1)) * 2;
+                    dst16[cl * P2 + k] = (uint16_t)w[i];
+                    dst16[cl * P2 + k + 1] = (uint16_t)(w[i] >> 16);
+                }
+            }
+        }
+    }
+};
+

@@ -30,8 +30,12 @@ def run_gpu(kv_np: np.ndarray, bins: np.ndarray, Tc: int, fused: bool = True,
     total = int(slab_off[-1])
     buf.dev_status.zero_()
     if exact_payload:
-        pay = buf.payload[:total].clone() if total else torch.empty(0, dtype=torch.uint8, device="cuda")
-        kvc.decode(buf, out_dtype=out_dtype, payload=pay if total else buf.payload, payload_bytes=total)
+        # the smallest buffer the decoder accepts: the packed size rounded up to whole dwords,
+        # the padding filled with junk it must not use
+        nb = max(4, (total + 3) // 4 * 4)
+        pay = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
+        pay[:total] = buf.payload[:total]
+        kvc.decode(buf, out_dtype=out_dtype, payload=pay, payload_bytes=nb)
     else:
         kvc.decode(buf, out_dtype=out_dtype)
     torch.cuda.synchronize()

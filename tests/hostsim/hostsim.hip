@@ -2,6 +2,7 @@
 // compiled for the host, so CPU tests can compare it with the oracle stream
 // by stream before any kernel runs.  Test infrastructure only.
 #include <stdint.h>
+#include <vector>
 
 #include "../../entropy_coding_02_amd/csrc/lane_coder.h"
 
@@ -14,21 +15,46 @@ int64_t hostsim_encode_stream(const uint8_t *q, int32_t C, int32_t A, const uint
     EncState e;
     enc_init(e);
     SlotOut out{(uint32_t *)slot};
-    for (int32_t c = 0; c < C; ++c) enc_symbol(e, cdf_rows + (int64_t)c * A, (uint32_t)A, q[c], out);
+    for (int32_t c = 0; c < C; ++c) {
+        const uint16_t *row = cdf_rows + (int64_t)c * A;
+        uint32_t s = q[c] < (uint32_t)A ? q[c] : (uint32_t)A - 1u;
+        uint32_t nx = s + 1 < (uint32_t)A ? row[s + 1] : 65536u;
+        enc_pair(e, cdf_pair(row[s], nx), out);
+    }
     return enc_finish(e, out);
 }
 
-// Decode the stream at [off, off+len) of a buffer of `cap` bytes; returns the corrupt flag.
+// Decode the stream at [off, off+len) of a buffer of `cap` bytes (a multiple
+// of 4, at least 4); returns the corrupt flag.
 int hostsim_decode_stream(const uint8_t *buf, int64_t cap, int64_t off, int64_t len, int32_t C,
                           int32_t A, const uint16_t *cdf_rows, uint8_t *q)
 {
-    StreamIn in;
-    in.init(buf, (uint64_t)off, (uint64_t)len, (uint64_t)cap);
+    uint32_t ring[16];
+    RingIn<uint32_t *> in;
+    in.init(buf, (uint64_t)off, (uint64_t)len, (uint64_t)cap, ring);
     DecState d;
     dec_init(d, in);
-    uint32_t bad = 0, step0 = dec_step0((uint32_t)A);
-    for (int32_t c = 0; c < C; ++c)
-        q[c] = (uint8_t)dec_symbol(d, cdf_rows + (int64_t)c * A, (uint32_t)A, step0, in, &bad);
+    uint32_t bad = 0, nstep = cdf_nstep((uint32_t)A), P2 = 1u << nstep;
+    std::vector<uint16_t> padded(P2);
+    std::vector<uint32_t> pairs(A);
+    for (int32_t c = 0; c < C; ++c) {
+        if ((c & 7) == 0) in.group();
+        const uint16_t *row = cdf_rows + (int64_t)c * A;
+        for (uint32_t k = 0; k < P2; ++k) padded[k] = k < (uint32_t)A ? row[k] : 0xFFFFu;
+        for (int32_t k = 0; k < A; ++k) pairs[k] = cdf_pair(row[k], k + 1 < A ? row[k + 1] : 65536u);
+        uint32_t sym;
+        switch (nstep) {
+        case 1: sym = dec_symbol<1>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
+        case 2: sym = dec_symbol<2>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
+        case 3: sym = dec_symbol<3>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
+        case 4: sym = dec_symbol<4>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
+        case 5: sym = dec_symbol<5>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
+        case 6: sym = dec_symbol<6>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
+        case 7: sym = dec_symbol<7>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
+        default: sym = dec_symbol<8>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
+        }
+        q[c] = (uint8_t)sym;
+    }
     return (int)bad;
 }
 

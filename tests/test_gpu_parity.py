@@ -140,9 +140,9 @@ def test_corrupt_payload_flagged_and_bounded():
     kvc.encode(buf, torch.from_numpy(kv.view(np.int16)).cuda())
     torch.cuda.synchronize()
     total = int(buf.slab_off[d.n_slabs].item())
-    bad = torch.full((total,), 0xFF, dtype=torch.uint8, device="cuda")
+    bad = torch.full(((total + 3) // 4 * 4,), 0xFF, dtype=torch.uint8, device="cuda")
     buf.dev_status.zero_()
-    kvc.decode(buf, payload=bad, payload_bytes=total)
+    kvc.decode(buf, payload=bad)
     torch.cuda.synchronize()
     assert int(buf.dev_status.item()) & kvc.KVC_DEV_CORRUPT
     # the oracle agrees on the symbols it decodes from the same bytes
