@@ -35,7 +35,59 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also launch one elementwise kernel that reads and writes 256 MiB "
+                         "(the reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --calibrate-copy run into profiles/traffic.json")
     return ap.parse_args()
+
+
+DECODE_SOURCES = ["entropy_coding_02_amd/csrc/kvc_decode.hip", "entropy_coding_02_amd/csrc/lane_coder.h",
+                  "entropy_coding_02_amd/csrc/pair_tile.h", "entropy_coding_02_amd/csrc/kvc_common.h"]
+COPY_BYTES = 256 << 20
+
+
+def sources_sha256(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of k_decode, scaled by what the
+    same counters read for the COPY_BYTES copy kernel, into profiles/traffic.json."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r["Kernel_Name"]
+            low = name.lower()
+            key = ("copy" if ("elementwise" in low and "add" in low) else
+                   ("k_decode" if "k_decode" in name else None))
+            if key:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sorted(v)[len(v) // 2] for k, v in vals.items()}  # median dispatch
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    rf, rw = COPY_BYTES / f["copy"], COPY_BYTES / w["copy"]
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    db = json.load(open(path)) if os.path.exists(path) else {}
+    db[f"k_decode/{workload}"] = {
+        "bytes_per_launch": round(f["k_decode"] * rf + w["k_decode"] * rw),
+        "fetch_bytes_raw": f["k_decode"], "write_bytes_raw": w["k_decode"],
+        "copy_scale_fetch": rf, "copy_scale_write": rw,
+        "sources": DECODE_SOURCES, "source_sha256": sources_sha256(DECODE_SOURCES),
+    }
+    json.dump(db, open(path, "w"), indent=1, sort_keys=True)
+    print(json.dumps(db[f"k_decode/{workload}"]))
 
 
 def traffic_for(kernel: str, workload: str):
@@ -84,6 +136,10 @@ def cpu_baseline(cfg, kv_np):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        import kvgen
+        summarize_pmc(*args.summarize_pmc, kvgen.CONFIGS[args.config].workload)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this codec is measured on one GPU; --gpus must be 1 "
                                    "(sharding across GPUs is described in DESIGN.md, not run)"}))
@@ -118,6 +174,13 @@ def main():
         if ev:
             ev[3].record(stream)
 
+    if args.calibrate_copy:
+        # one kernel that reads COPY_BYTES and writes COPY_BYTES
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.add(src, 1, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -45,7 +45,8 @@ int make_geometry(const kvc_desc *d, Geometry &g)
     p.n_streams = p.n_rows;
     p.n_slabs = NC * 2 * p.L;
     p.slot_bytes = round_up(2 * (int64_t)p.C + 16, 16);
-    g.slot_area = p.n_streams * p.slot_bytes;
+    // encoder slots: one per lane of every 256-lane block (slab x ceil(Tc/256))
+    g.slot_area = p.n_slabs * ((p.Tc + 255) / 256) * 256 * p.slot_bytes;
     g.scratch = g.slot_area + 8 * p.n_slabs;
     // launch-size limits (1-D grids of 32-bit block counts)
     if (p.n_slabs * ((p.Tc + 255) / 256) >= ((int64_t)1 << 31)) return KVC_ERR_ARG;

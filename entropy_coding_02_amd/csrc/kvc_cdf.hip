@@ -56,11 +56,72 @@ __global__ __launch_bounds__(256) void k_cdf(const uint8_t *__restrict__ sym,
     }
 }
 
+// Wide variant for C % 4 == 0 and A <= 64: a block covers 256 channels of a
+// slab (4 consecutive channels per lane, so a wave reads 256 contiguous
+// symbol bytes of a token with one dword load per lane); wave w takes the
+// tokens t = w (mod 4).  Counters are 16-bit halves of LDS words, word
+// (c, s) at c*W + (c >> 2) + s/2 with W = A/2 + 1: at each of a lane's four
+// steps the lanes' channels are 4 apart, and the (c >> 2) skew makes the word
+// stride between lanes odd, so equal symbols fall in distinct banks.  Each
+// thread then turns one channel's counts into its CDF row.
+__global__ __launch_bounds__(256) void k_cdf_wide(const uint8_t *__restrict__ sym,
+                                                  uint16_t *__restrict__ cdf, KParams p)
+{
+    extern __shared__ uint32_t hist[];
+    const int A = p.A, W = A / 2 + 1, C = p.C;
+    const int ntile = (C + 255) / 256;
+    const int64_t slab = blockIdx.x / ntile;
+    const SlabGeom g = slab_geom(p, slab);
+    const int c0 = (int)(blockIdx.x - slab * ntile) * 256;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int nwords = 256 * W + 64;
+    for (int i = threadIdx.x; i < nwords; i += 256) hist[i] = 0;
+    __syncthreads();
+    const int cq = c0 + 4 * lane;  // this lane's first channel
+    if (cq < C) {
+        const uint8_t *col = sym + g.row0 * C + cq;
+        const int cl = 4 * lane;
+        for (int t = wid; t < g.nj; t += 4) {
+            const uint32_t v = *(const uint32_t *)(col + (int64_t)t * C);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                uint32_t s = (v >> (8 * k)) & 0xFFu;
+                s = s < (uint32_t)A ? s : (uint32_t)(A - 1);
+                const int c = cl + k;
+                atomicAdd(&hist[c * W + (c >> 2) + (int)(s >> 1)], 1u << (16 * (s & 1u)));
+            }
+        }
+    }
+    __syncthreads();
+    const int c = c0 + (int)threadIdx.x;
+    if (c < C) {
+        const int cl = (int)threadIdx.x;
+        const uint32_t *h = hist + cl * W + (cl >> 2);
+        const uint32_t K = 65536u - (uint32_t)A, N = (uint32_t)g.nj;
+        uint16_t *dst = cdf + (slab * C + c) * A;
+        uint32_t Ck = 0;
+        for (int k = 0; k < A; k += 2) {
+            const uint32_t w = h[k >> 1];
+            const uint32_t lo = (uint32_t)k + (Ck * K) / N;
+            Ck += w & 0xFFFFu;
+            const uint32_t hi = (uint32_t)(k + 1) + (Ck * K) / N;
+            Ck += w >> 16;
+            *(uint32_t *)(dst + k) = lo | (hi << 16);  // A even, rows 4-byte aligned
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_cdf(const uint8_t *sym, uint16_t *cdf, const KParams &p, hipStream_t stream)
 {
     if (p.n_slabs == 0) return hipSuccess;
+    if (p.C % 4 == 0 && p.A <= 64 && ((uintptr_t)sym & 3) == 0 && ((uintptr_t)cdf & 3) == 0) {
+        const size_t lds = sizeof(uint32_t) * (256 * (size_t)(p.A / 2 + 1) + 64);
+        dim3 grid((unsigned)(((p.C + 255) / 256) * p.n_slabs));
+        hipLaunchKernelGGL(k_cdf_wide, grid, dim3(256), lds, stream, sym, cdf, p);
+        return hipGetLastError();
+    }
     const int CT = p.A <= 128 ? 64 : 32;
     const size_t lds = (size_t)CT * (p.A + 1) * sizeof(uint32_t);
     dim3 grid((unsigned)(((p.C + CT - 1) / CT) * p.n_slabs));

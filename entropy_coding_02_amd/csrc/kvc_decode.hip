@@ -102,37 +102,49 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
         __syncthreads();
         if (!active) continue;
         if constexpr (VEC) {
-            // C % 16 == 0 and CT % 16 == 0: groups of 8 symbols, 16-byte fp16 stores
-#pragma unroll 1
-            for (int cg = c0; cg < c1; cg += 8) {
-                in.group();
-                uint32_t sw[2] = {0, 0};
-                uint32_t hw[4];
+            // C % 16 == 0 and CT % 16 == 0: groups of 8 symbols; the fp16 output of
+            // up to 32 channels (64 bytes of the row) is collected in registers and
+            // written with back-to-back 16-byte stores, so whole 64-byte pieces of
+            // a line reach L2 together instead of 16-byte fragments.
+            for (int cb = c0; cb < c1; cb += 32) {
+                const int nb = min(32, c1 - cb);  // 16 or 32
+                uint32_t hw[16];
                 float fw[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int cl = cg - c0 + i;
-                    const uint32_t s = dec_symbol<NSTEP>(d, r16 + cl * P2, pr + cl * A, (uint32_t)A, in, &bad);
-                    sw[i >> 2] |= s << (8 * (i & 3));
-                    if constexpr (ODT != ODT_NONE) {
-                        const float y = lut[s] * m;
-                        if constexpr (ODT == ODT_F16) {
-                            if (i & 1)
-                                hw[i >> 1] |= kvc_f2h(y) << 16;
-                            else
-                                hw[i >> 1] = kvc_f2h(y);
-                        } else {
-                            fw[i] = y;
+                for (int gi = 0; gi < 4; ++gi) {
+                    if (gi * 8 >= nb) break;
+                    const int cg = cb + gi * 8;
+                    in.group();
+                    uint32_t sw[2] = {0, 0};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int cl = cg - c0 + i;
+                        const uint32_t s = dec_symbol<NSTEP>(d, r16 + cl * P2, pr + cl * A, (uint32_t)A, in, &bad);
+                        sw[i >> 2] |= s << (8 * (i & 3));
+                        if constexpr (ODT != ODT_NONE) {
+                            const float y = lut[s] * m;
+                            if constexpr (ODT == ODT_F16) {
+                                if (i & 1)
+                                    hw[gi * 4 + (i >> 1)] |= kvc_f2h(y) << 16;
+                                else
+                                    hw[gi * 4 + (i >> 1)] = kvc_f2h(y);
+                            } else {
+                                fw[i] = y;
+                            }
                         }
                     }
+                    if (so) *(uint2 *)(so + cg) = make_uint2(sw[0], sw[1]);
+                    if constexpr (ODT == ODT_F32) {
+                        float4 *o = (float4 *)((float *)out + row * C + cg);
+                        o[0] = make_float4(fw[0], fw[1], fw[2], fw[3]);
+                        o[1] = make_float4(fw[4], fw[5], fw[6], fw[7]);
+                    }
                 }
-                if (so) *(uint2 *)(so + cg) = make_uint2(sw[0], sw[1]);
                 if constexpr (ODT == ODT_F16) {
-                    *(uint4 *)((uint16_t *)out + row * C + cg) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-                } else if constexpr (ODT == ODT_F32) {
-                    float4 *o = (float4 *)((float *)out + row * C + cg);
-                    o[0] = make_float4(fw[0], fw[1], fw[2], fw[3]);
-                    o[1] = make_float4(fw[4], fw[5], fw[6], fw[7]);
+                    uint4 *o = (uint4 *)((uint16_t *)out + row * C + cb);
+#pragma unroll
+                    for (int gi = 0; gi < 4; ++gi)
+                        if (gi * 8 < nb) o[gi] = make_uint4(hw[4 * gi], hw[4 * gi + 1], hw[4 * gi + 2], hw[4 * gi + 3]);
                 }
             }
         } else {

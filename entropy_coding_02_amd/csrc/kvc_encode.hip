@@ -17,65 +17,90 @@
 
 namespace {
 
-// One lane per stream, 256 tokens of one slab per block.  The slab's CDF is
-// walked in tiles of CT channels (CT * A = 2048 pairs, 8 KB), double-buffered
-// in LDS: while a tile is coded, the next one is in flight in registers.
-// All lanes of a wave read the same tile row at the same step, so a pair
-// lookup is a broadcast or a distinct bank.
+// One lane per stream, 256 tokens of one slab per block.  The slab is walked
+// in tiles of CT channels: at each tile boundary the block stages the tile's
+// CDF rows as packed (start, frequency) pairs and, when C % 16 == 0, the
+// tile's symbols of its 256 tokens (coalesced 16-byte loads) in LDS.  The
+// coding loop then reads only LDS: 16 symbols per ds_read_b128, pair lookups
+// in batches of 8.  All lanes of a wave read the same pair row at the same
+// step (broadcast or distinct banks); the symbol rows have a 16-byte-padded
+// stride that spreads lanes over all banks.  Without global loads in the
+// loop, the lanes' byte stores never make it wait.
 template <bool VEC16>
 __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
                                                 const uint16_t *__restrict__ cdf,
                                                 uint8_t *__restrict__ slots,
                                                 uint16_t *__restrict__ stream_len, KParams p, int CT)
 {
+    // LDS: pairs [CT][A] u32 | symbols [256][CT + 16] u8 (VEC16 only)
     extern __shared__ uint32_t lds[];
     const int bps = (p.Tc + 255) / 256;
     const int64_t slab = blockIdx.x / bps;
-    const int t = (int)(blockIdx.x - slab * bps) * 256 + (int)threadIdx.x;
+    const int tb = (int)(blockIdx.x - slab * bps);
+    const int t = tb * 256 + (int)threadIdx.x;
     const SlabGeom g = slab_geom(p, slab);
     const int C = p.C, A = p.A;
     const bool active = t < g.nj;
     const int64_t sid = g.sid0 + t;
     const uint8_t *q = sym + (g.row0 + (active ? t : 0)) * C;
     const uint16_t *rows = cdf + slab * C * A;
-    lds_u32 *const tiles = (lds_u32 *)lds;
+    lds_u32 *const pairs = (lds_u32 *)lds;
+    const int sstride = CT + 16;
+    lds_u8 *const stile = (lds_u8 *)(pairs + CT * A);
     const int ntiles = (C + CT - 1) / CT;
 
-    PairTile pt;
-    pt.load(rows, 0, CT, C, A);
-    pt.store(tiles, CT, A);
-    __syncthreads();
-
-    SlotOut out{(uint32_t *)(slots + (active ? sid : 0) * p.slot_bytes)};
+    // slot dword k of this lane: block region + (k * 256 + lane) dwords
+    SlotOut out{(uint32_t *)(slots + (int64_t)blockIdx.x * p.slot_bytes * 256) + threadIdx.x, 256u};
     EncState e;
     enc_init(e);
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
-        if (it + 1 < ntiles) pt.load(rows, c0 + CT, CT, C, A);
-        const lds_u32 *tile = tiles + (it & 1) * CT * A;
-        if (active) {
-            if constexpr (VEC16) {
-                for (int cg = c0; cg < c1; cg += 16) {
-                    const uint4 v = *(const uint4 *)(q + cg);
-                    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-                    const lds_u32 *trow = tile + (cg - c0) * A;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        uint32_t s = (wv[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-                        s = s < (uint32_t)A ? s : (uint32_t)(A - 1);
-                        enc_pair(e, trow[i * A + s], out);
-                    }
-                }
-            } else {
-                for (int c = c0; c < c1; ++c) {
-                    uint32_t s = q[c];
-                    s = s < (uint32_t)A ? s : (uint32_t)(A - 1);
-                    enc_pair(e, tile[(c - c0) * A + s], out);
+        __syncthreads();  // every wave is done with the previous tile
+        {
+            PairTile pt;
+            pt.load(rows, c0, CT, C, A);
+            pt.store(pairs, CT, A);
+        }
+        if constexpr (VEC16) {
+            const int per_row = CT / 16;
+            for (int ch = threadIdx.x; ch < 256 * per_row; ch += 256) {
+                const int r = ch / per_row, part = ch - r * per_row;
+                const int tok = tb * 256 + r, cc = c0 + part * 16;
+                if (tok < g.nj && cc < C) {
+                    const u32x4 v = *(const u32x4 *)(sym + (g.row0 + tok) * C + cc);
+                    *(lds_u32x4 *)(stile + r * sstride + part * 16) = v;
                 }
             }
         }
-        if (it + 1 < ntiles) pt.store(tiles + ((it + 1) & 1) * CT * A, CT, A);
         __syncthreads();
+        if (!active) continue;
+        if constexpr (VEC16) {
+            const lds_u8 *my = stile + threadIdx.x * sstride;
+            for (int cg = c0; cg < c1; cg += 16) {
+                const u32x4 v = *(const lds_u32x4 *)(my + (cg - c0));
+                const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+                const lds_u32 *trow = pairs + (cg - c0) * A;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t pv[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int k = h * 8 + i;
+                        uint32_t s = (wv[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+                        s = s < (uint32_t)A ? s : (uint32_t)(A - 1);
+                        pv[i] = trow[k * A + s];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) enc_pair(e, pv[i], out);
+                }
+            }
+        } else {
+            for (int c = c0; c < c1; ++c) {
+                uint32_t s = q[c];
+                s = s < (uint32_t)A ? s : (uint32_t)(A - 1);
+                enc_pair(e, pairs[(c - c0) * A + s], out);
+            }
+        }
     }
     if (active) stream_len[sid] = (uint16_t)enc_finish(e, out);
 }
@@ -133,47 +158,72 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *__restrict__ slab
     }
 }
 
+// Per encoder block (256 streams of a slab): the streams' payload offsets
+// (slab offset + the lengths before them), then rounds of 64 bytes per
+// stream: the block stages dwords [16r, 16r+16) of every lane's interleaved
+// slot in LDS (loads coalesced across lanes), and each wave copies its 64
+// streams' 64-byte pieces to their places in the payload, a stream at a time
+// with one byte per lane.
 __global__ __launch_bounds__(256) void k_pack(const uint8_t *__restrict__ slots,
                                               const uint16_t *__restrict__ stream_len,
                                               const uint64_t *__restrict__ slab_off,
                                               uint8_t *__restrict__ payload, int64_t payload_cap,
                                               KParams p)
 {
+    __shared__ uint32_t stage[256 * 17];
     __shared__ uint32_t s_len[256];
-    __shared__ uint32_t s_off[256];
-    __shared__ uint32_t s_wave[4];
-    const SlabGeom g = slab_geom(p, blockIdx.x);
+    __shared__ uint32_t s_red[4];
+    __shared__ uint32_t s_max[4];
+    const int bps = (p.Tc + 255) / 256;
+    const int64_t slab = blockIdx.x / bps;
+    const int tb = (int)(blockIdx.x - slab * bps);
+    const SlabGeom g = slab_geom(p, slab);
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    uint64_t base = slab_off[blockIdx.x];
-    for (int t0 = 0; t0 < g.nj; t0 += 256) {
-        const int t = t0 + (int)threadIdx.x;
-        uint32_t len = t < g.nj ? stream_len[g.sid0 + t] : 0u;
-        // block exclusive scan of len
-        uint32_t incl = len;
-        for (int off = 1; off < 64; off <<= 1) {
-            uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
-            if (lane >= off) incl += o;
+    const int t = tb * 256 + (int)threadIdx.x;
+    const bool active = t < g.nj;
+
+    uint32_t pre = 0;
+    const int n_before = min(tb * 256, g.nj);
+    for (int i = threadIdx.x; i < n_before; i += 256) pre += stream_len[g.sid0 + i];
+    pre = wave_sum_u32(pre);
+    if (lane == 0) s_red[wid] = pre;
+    __syncthreads();
+    pre = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    __syncthreads();
+    const uint32_t len = active ? stream_len[g.sid0 + t] : 0u;
+    uint32_t incl = len;
+    for (int off = 1; off < 64; off <<= 1) {
+        uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    const uint32_t mx = wave_max_u32(len);
+    if (lane == 63) s_red[wid] = incl;
+    if (lane == 0) s_max[wid] = mx;
+    s_len[threadIdx.x] = len;
+    __syncthreads();
+    uint32_t wbase = 0;
+    for (int i = 0; i < wid; ++i) wbase += s_red[i];
+    const uint64_t my_off = slab_off[slab] + pre + wbase + incl - len;
+    const uint32_t maxlen = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+    const uint32_t *region = (const uint32_t *)(slots + (int64_t)blockIdx.x * p.slot_bytes * 256);
+
+    for (uint32_t r0 = 0; r0 < maxlen; r0 += 64) {
+        // stage dwords [r0/4, r0/4 + 16) of every lane's slot
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t k = r0 / 4 + (uint32_t)j;
+            stage[threadIdx.x * 17 + j] = (4u * k < len) ? region[(int64_t)k * 256 + threadIdx.x] : 0u;
         }
-        if (lane == 63) s_wave[wid] = incl;
         __syncthreads();
-        uint32_t wbase = 0;
-        for (int i = 0; i < wid; ++i) wbase += s_wave[i];
-        s_len[threadIdx.x] = len;
-        s_off[threadIdx.x] = wbase + incl - len;
-        const uint32_t round_total = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
-        __syncthreads();
-        // wave wid copies the streams of its own 64 lanes, one after another
+        // wave wid copies bytes [r0, r0+64) of streams wid*64 .. wid*64+63
         for (int k = 0; k < 64; ++k) {
             const int idx = wid * 64 + k;
-            const int tk = t0 + idx;
-            if (tk >= g.nj) break;
             const uint32_t n = s_len[idx];
-            const uint8_t *src = slots + (g.sid0 + tk) * p.slot_bytes;
-            const uint64_t dst = base + s_off[idx];
-            for (uint32_t i = lane; i < n; i += 64)
-                if (dst + i < (uint64_t)payload_cap) payload[dst + i] = src[i];
+            const uint32_t b = r0 + (uint32_t)lane;
+            const uint64_t o = __shfl(my_off, k, 64) + b;
+            if (b < n && o < (uint64_t)payload_cap)
+                payload[o] = (uint8_t)(stage[idx * 17 + lane / 4] >> (8 * (lane & 3)));
         }
-        base += round_total;
         __syncthreads();
     }
 }
@@ -182,8 +232,13 @@ __global__ void k_zero_u64(uint64_t *dst) { *dst = 0; }
 
 }  // namespace
 
-// Channels per LDS tile: 2048 pairs (8 KB) per buffer; at least 16 channels.
-static int enc_tile_channels(int A) { return A <= 128 ? 2048 / A : 16; }
+// Channels per tile: 1024 pairs (4 KB), between 16 and 64 channels (a
+// multiple of 16, so symbol tiles are whole 16-byte pieces).
+static int enc_tile_channels(int A)
+{
+    const int ct = 1024 / A;
+    return ct < 16 ? 16 : (ct > 64 ? 64 : ct);
+}
 
 hipError_t launch_zero_u64(uint64_t *dst, hipStream_t stream)
 {
@@ -200,16 +255,18 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
     const int64_t bps = (p.Tc + 255) / 256;
     dim3 grid((unsigned)(bps * p.n_slabs));
     const int CT = enc_tile_channels(p.A);
-    const size_t lds = 2 * (size_t)CT * p.A * sizeof(uint32_t);
-    if (vec16 && CT % 16 == 0)
-        hipLaunchKernelGGL(k_encode<true>, grid, dim3(256), lds, stream, sym, cdf, slots, stream_len, p, CT);
+    const size_t lds_pairs = (size_t)CT * p.A * sizeof(uint32_t);
+    if (vec16)
+        hipLaunchKernelGGL(k_encode<true>, grid, dim3(256), lds_pairs + 256 * (size_t)(CT + 16), stream,
+                           sym, cdf, slots, stream_len, p, CT);
     else
-        hipLaunchKernelGGL(k_encode<false>, grid, dim3(256), lds, stream, sym, cdf, slots, stream_len, p, CT);
+        hipLaunchKernelGGL(k_encode<false>, grid, dim3(256), lds_pairs, stream, sym, cdf, slots,
+                           stream_len, p, CT);
     hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
                        slab_total, p);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, slab_total, slab_off, p.n_slabs,
                        payload_cap, status);
-    hipLaunchKernelGGL(k_pack, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, slots, stream_len,
+    hipLaunchKernelGGL(k_pack, grid, dim3(256), 0, stream, slots, stream_len,
                        slab_off, payload, payload_cap, p);
     return hipGetLastError();
 }

@@ -36,17 +36,30 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restric
         const uint16_t *x = kv + row * C;
         uint8_t *q = sym + row * C;
         uint32_t mx = 0;
+        // rows of up to 1024 channels stay in registers (two 16-byte pieces per lane)
+        constexpr int KREG = VEC == 8 ? 2 : 1;
+        u32x4 reg[KREG];
         if constexpr (VEC == 8) {
-            for (int c = lane * 8; c < C; c += 64 * 8) {
-                uint4 v = *(const uint4 *)(x + c);
-                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < KREG; ++k) {
+                const int c = (lane + 64 * k) * 8;
+                reg[k] = c < C ? *(const u32x4 *)(x + c) : u32x4{0, 0, 0, 0};
+            }
+            for (int c = (lane + 64 * KREG) * 8; c < C; c += 64 * 8) {
+                const u32x4 v = *(const u32x4 *)(x + c);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    uint32_t a = w[i] & 0x7FFF7FFFu;
-                    uint32_t lo = a & 0xFFFFu, hi = a >> 16;
-                    mx = max(mx, max(lo, hi));
+                    const uint32_t a = v[i] & 0x7FFF7FFFu;
+                    mx = max(mx, max(a & 0xFFFFu, a >> 16));
                 }
             }
+#pragma unroll
+            for (int k = 0; k < KREG; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t a = reg[k][i] & 0x7FFF7FFFu;
+                    mx = max(mx, max(a & 0xFFFFu, a >> 16));
+                }
         } else {
             for (int c = lane; c < C; c += 64) mx = max(mx, (uint32_t)(x[c] & 0x7FFFu));
         }
@@ -58,18 +71,22 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restric
         if (mx >= 0x7C00u && lane == 0) kvc_flag(status, KVC_DEV_NONFINITE);
         if (lane == 0) max1[row] = (uint16_t)mx;
         if constexpr (VEC == 8) {
-            for (int c = lane * 8; c < C; c += 64 * 8) {
-                uint4 v = *(const uint4 *)(x + c);
-                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            auto put = [&](int c, const u32x4 &v) {
                 uint32_t b[2] = {0, 0};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    uint32_t q0 = quant1(w[i] & 0xFFFFu, factor, M);
-                    uint32_t q1 = quant1(w[i] >> 16, factor, M);
+                    const uint32_t q0 = quant1(v[i] & 0xFFFFu, factor, M);
+                    const uint32_t q1 = quant1(v[i] >> 16, factor, M);
                     b[i >> 1] |= (q0 | (q1 << 8)) << ((i & 1) * 16);
                 }
                 *(uint2 *)(q + c) = make_uint2(b[0], b[1]);
+            };
+#pragma unroll
+            for (int k = 0; k < KREG; ++k) {
+                const int c = (lane + 64 * k) * 8;
+                if (c < C) put(c, reg[k]);
             }
+            for (int c = (lane + 64 * KREG) * 8; c < C; c += 64 * 8) put(c, *(const u32x4 *)(x + c));
         } else {
             for (int c = lane; c < C; c += 64) q[c] = (uint8_t)quant1(x[c], factor, M);
         }

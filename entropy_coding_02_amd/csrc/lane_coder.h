@@ -45,11 +45,15 @@ struct EncState {
     uint32_t w;      // dwords already written to the stream slot
 };
 
-// A stream slot: dword-addressable memory owned by one lane.
+// A stream slot: dword-addressable memory owned by one lane; dword i of the
+// stream is at p[i * stride] (the kernels interleave the slots of a block's
+// lanes, stride = lanes per block, so lanes writing their k-th dwords at
+// about the same time fill the same cache lines).
 struct SlotOut {
     uint32_t *p;
-    KVC_HD uint32_t load(uint32_t i) const { return p[i]; }
-    KVC_HD void store(uint32_t i, uint32_t v) const { p[i] = v; }
+    uint32_t stride;
+    KVC_HD uint32_t load(uint32_t i) const { return p[(uint64_t)i * stride]; }
+    KVC_HD void store(uint32_t i, uint32_t v) const { p[(uint64_t)i * stride] = v; }
 };
 
 KVC_HD void enc_init(EncState &e)

@@ -48,7 +48,8 @@ def test_sizes_match_layout(lib):
         assert d.n_streams == 2 * cfg.n_layers * cfg.n_tokens
         assert d.cdf_bytes == NC * 2 * cfg.n_layers * cfg.n_channels * A * 2
         slot = (2 * cfg.n_channels + 16 + 15) // 16 * 16
-        assert d.scratch_bytes == d.n_streams * slot + 8 * d.n_slabs
+        lanes = d.n_slabs * -(-cfg.chunk_tokens // 256) * 256
+        assert d.scratch_bytes == lanes * slot + 8 * d.n_slabs
         assert d.max_payload_bytes == d.n_streams * (2 * cfg.n_channels + 1)
     # the write-up's validation shape: 256 tokens = one chunk, 16,384 streams
     c2 = kvgen.CONFIGS["c2"]
