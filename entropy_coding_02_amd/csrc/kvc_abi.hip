@@ -163,6 +163,7 @@ int kvc_encode(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf, vo
     if (g.p.n_rows == 0) return launch_status(launch_zero_u64(slab_off, s));
     if (!sym || !cdf || !scratch || !stream_len || (!payload && payload_cap > 0) ||
         !aligned(sym, 4) || !aligned(cdf, 4) || !aligned(scratch, 16) || !aligned(stream_len, 2) ||
+        !aligned(payload, 4) ||
         (dev_status && !aligned(dev_status, 4)))
         return KVC_ERR_ARG;
     if (scratch_bytes < g.scratch) return KVC_ERR_CAPACITY;

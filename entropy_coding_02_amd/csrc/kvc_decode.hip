@@ -19,7 +19,7 @@ namespace {
 
 enum { ODT_F16 = 0, ODT_F32 = 1, ODT_NONE = 2 };
 
-template <bool VEC, int ODT, int NSTEP>
+template <bool VEC, int ODT, int NSTEP, int PER>
 __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payload,
                                                 int64_t payload_bytes,
                                                 const uint64_t *__restrict__ slab_off,
@@ -89,17 +89,20 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
     uint8_t *so = (sym_out && active) ? sym_out + row * C : nullptr;
     const uint16_t *srows = cdf + slab * C * A;
     const int ntiles = (C + CT - 1) / CT;
+    auto decode1 = [&](int cl) -> uint32_t {
+        return dec_symbol<NSTEP>(d, r16 + cl * P2, pr + cl * A, (uint32_t)A, &bad);
+    };
 
+    // the tile's rows arrive in registers while the previous tile is decoded,
+    // and go into LDS between two barriers
+    PairTile<PER> pt;
+    pt.load(srows, 0, CT, C, A);
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
-        // stage this tile's rows: all waves are done with the previous one
+        __syncthreads();  // all waves are done with the previous tile
+        pt.store(pr, CT, A, r16, (int)P2);
         __syncthreads();
-        {
-            PairTile pt;
-            pt.load(srows, c0, CT, C, A);
-            pt.store(pr, CT, A, r16, (int)P2);
-        }
-        __syncthreads();
+        if (it + 1 < ntiles) pt.load(srows, c0 + CT, CT, C, A);
         if (!active) continue;
         if constexpr (VEC) {
             // C % 16 == 0 and CT % 16 == 0: groups of 8 symbols; the fp16 output of
@@ -118,8 +121,8 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
                     uint32_t sw[2] = {0, 0};
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const int cl = cg - c0 + i;
-                        const uint32_t s = dec_symbol<NSTEP>(d, r16 + cl * P2, pr + cl * A, (uint32_t)A, in, &bad);
+                        if ((i & 1) == 0) dec_refill(d, in);
+                        const uint32_t s = decode1(cg - c0 + i);
                         sw[i >> 2] |= s << (8 * (i & 3));
                         if constexpr (ODT != ODT_NONE) {
                             const float y = lut[s] * m;
@@ -150,8 +153,8 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
         } else {
             for (int c = c0; c < c1; ++c) {
                 if ((c & 7) == 0) in.group();
-                const int cl = c - c0;
-                const uint32_t s = dec_symbol<NSTEP>(d, r16 + cl * P2, pr + cl * A, (uint32_t)A, in, &bad);
+                if ((c & 1) == 0) dec_refill(d, in);
+                const uint32_t s = decode1(c - c0);
                 if (so) so[c] = (uint8_t)s;
                 if constexpr (ODT != ODT_NONE) {
                     const float y = lut[s] * m;
@@ -230,9 +233,14 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
     const size_t lds = dec_lds_bytes(p.A, CT);
     vec = vec && (CT % 16 == 0);
     const int nstep = (int)cdf_nstep((uint32_t)p.A);
+    const int per = (CT * (p.A / 2) + 255) / 256;  // pairs staged per thread
 #define KVC_DEC(V, O, N)                                                                             \
-    hipLaunchKernelGGL((k_decode<V, O, N>), grid, block, lds, stream, payload, payload_bytes,        \
-                       slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
+    if (per <= 2)                                                                                    \
+        hipLaunchKernelGGL((k_decode<V, O, N, 2>), grid, block, lds, stream, payload, payload_bytes, \
+                           slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT);            \
+    else                                                                                             \
+        hipLaunchKernelGGL((k_decode<V, O, N, 8>), grid, block, lds, stream, payload, payload_bytes, \
+                           slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
 #define KVC_DEC_N(V, O)                                                                              \
     switch (nstep) {                                                                                 \
     case 2: KVC_DEC(V, O, 2); break;                                                                 \

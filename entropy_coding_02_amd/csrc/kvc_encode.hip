@@ -26,7 +26,7 @@ namespace {
 // step (broadcast or distinct banks); the symbol rows have a 16-byte-padded
 // stride that spreads lanes over all banks.  Without global loads in the
 // loop, the lanes' byte stores never make it wait.
-template <bool VEC16>
+template <bool VEC16, int PER>
 __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
                                                 const uint16_t *__restrict__ cdf,
                                                 uint8_t *__restrict__ slots,
@@ -53,26 +53,45 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
     SlotOut out{(uint32_t *)(slots + (int64_t)blockIdx.x * p.slot_bytes * 256) + threadIdx.x, 256u};
     EncState e;
     enc_init(e);
+    // A tile's pairs and symbols arrive in registers while the previous tile
+    // is coded, and go into LDS between two barriers.  Symbol pieces: 16 bytes
+    // of a token row; CT <= 64 gives at most 4 per thread.
+    PairTile<PER> pt;
+    u32x4 sv[4];
+    const int per_row = CT / 16;
+    auto load_syms = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ch = (int)threadIdx.x + 256 * i;
+            const int r = ch / per_row, part = ch - r * per_row;
+            const int tok = tb * 256 + r, cc = c0 + part * 16;
+            sv[i] = (ch < 256 * per_row && tok < g.nj && cc < C)
+                        ? *(const u32x4 *)(sym + (g.row0 + tok) * C + cc)
+                        : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto store_syms = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ch = (int)threadIdx.x + 256 * i;
+            if (ch < 256 * per_row) {
+                const int r = ch / per_row, part = ch - r * per_row;
+                *(lds_u32x4 *)(stile + r * sstride + part * 16) = sv[i];
+            }
+        }
+    };
+    pt.load(rows, 0, CT, C, A);
+    if constexpr (VEC16) load_syms(0);
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
         __syncthreads();  // every wave is done with the previous tile
-        {
-            PairTile pt;
-            pt.load(rows, c0, CT, C, A);
-            pt.store(pairs, CT, A);
-        }
-        if constexpr (VEC16) {
-            const int per_row = CT / 16;
-            for (int ch = threadIdx.x; ch < 256 * per_row; ch += 256) {
-                const int r = ch / per_row, part = ch - r * per_row;
-                const int tok = tb * 256 + r, cc = c0 + part * 16;
-                if (tok < g.nj && cc < C) {
-                    const u32x4 v = *(const u32x4 *)(sym + (g.row0 + tok) * C + cc);
-                    *(lds_u32x4 *)(stile + r * sstride + part * 16) = v;
-                }
-            }
-        }
+        pt.store(pairs, CT, A);
+        if constexpr (VEC16) store_syms();
         __syncthreads();
+        if (it + 1 < ntiles) {
+            pt.load(rows, c0 + CT, CT, C, A);
+            if constexpr (VEC16) load_syms(c0 + CT);
+        }
         if (!active) continue;
         if constexpr (VEC16) {
             const lds_u8 *my = stile + threadIdx.x * sstride;
@@ -158,22 +177,21 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *__restrict__ slab
     }
 }
 
-// Per encoder block (256 streams of a slab): the streams' payload offsets
-// (slab offset + the lengths before them), then rounds of 64 bytes per
-// stream: the block stages dwords [16r, 16r+16) of every lane's interleaved
-// slot in LDS (loads coalesced across lanes), and each wave copies its 64
-// streams' 64-byte pieces to their places in the payload, a stream at a time
-// with one byte per lane.
+// Per encoder block (256 streams of a slab), one lane per stream: the
+// stream's payload offset o (slab offset + the lengths before it), then its
+// bytes go out as whole aligned dwords wherever a destination dword lies
+// inside [o, o + len), each the funnel shift of two consecutive slot dwords
+// (slot loads are coalesced: lanes read their k-th dwords together); the up
+// to 3 + 3 bytes at either end, which share a dword with the neighbouring
+// streams, are written one byte at a time.  Nothing is written at or past
+// payload_cap.
 __global__ __launch_bounds__(256) void k_pack(const uint8_t *__restrict__ slots,
                                               const uint16_t *__restrict__ stream_len,
                                               const uint64_t *__restrict__ slab_off,
                                               uint8_t *__restrict__ payload, int64_t payload_cap,
                                               KParams p)
 {
-    __shared__ uint32_t stage[256 * 17];
-    __shared__ uint32_t s_len[256];
     __shared__ uint32_t s_red[4];
-    __shared__ uint32_t s_max[4];
     const int bps = (p.Tc + 255) / 256;
     const int64_t slab = blockIdx.x / bps;
     const int tb = (int)(blockIdx.x - slab * bps);
@@ -196,35 +214,44 @@ __global__ __launch_bounds__(256) void k_pack(const uint8_t *__restrict__ slots,
         uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
         if (lane >= off) incl += o;
     }
-    const uint32_t mx = wave_max_u32(len);
     if (lane == 63) s_red[wid] = incl;
-    if (lane == 0) s_max[wid] = mx;
-    s_len[threadIdx.x] = len;
     __syncthreads();
     uint32_t wbase = 0;
     for (int i = 0; i < wid; ++i) wbase += s_red[i];
-    const uint64_t my_off = slab_off[slab] + pre + wbase + incl - len;
-    const uint32_t maxlen = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
-    const uint32_t *region = (const uint32_t *)(slots + (int64_t)blockIdx.x * p.slot_bytes * 256);
-
-    for (uint32_t r0 = 0; r0 < maxlen; r0 += 64) {
-        // stage dwords [r0/4, r0/4 + 16) of every lane's slot
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const uint32_t k = r0 / 4 + (uint32_t)j;
-            stage[threadIdx.x * 17 + j] = (4u * k < len) ? region[(int64_t)k * 256 + threadIdx.x] : 0u;
+    if (!active || len == 0) return;  // no barriers below
+    const uint64_t o = slab_off[slab] + pre + wbase + incl - len;
+    const uint64_t e = o + len;
+    const uint32_t *src = (const uint32_t *)(slots + (int64_t)blockIdx.x * p.slot_bytes * 256) + threadIdx.x;
+    const uint64_t cap = (uint64_t)payload_cap;
+    // byte i of the stream is byte (i & 3) of slot dword i >> 2 (bytes in memory order)
+    auto byte_at = [&](uint32_t i) -> uint32_t { return (src[(i >> 2) * 256u] >> (8u * (i & 3u))) & 0xFFu; };
+    const uint64_t d0 = (o + 3u) & ~(uint64_t)3;  // first whole destination dword
+    const uint64_t d1 = e & ~(uint64_t)3;         // end of the whole destination dwords
+    if (d0 >= d1) {
+        for (uint32_t i = 0; i < len; ++i)
+            if (o + i < cap) payload[o + i] = (uint8_t)byte_at(i);
+        return;
+    }
+    for (uint64_t b = o; b < d0; ++b)
+        if (b < cap) payload[b] = (uint8_t)byte_at((uint32_t)(b - o));
+    for (uint64_t b = d1; b < e; ++b)
+        if (b < cap) payload[b] = (uint8_t)byte_at((uint32_t)(b - o));
+    // whole dwords: destination dword at b takes stream bytes [b - o, b - o + 4)
+    const uint32_t i0 = (uint32_t)(d0 - o);  // 0..3
+    const uint32_t sh = 8u * (i0 & 3u);
+    uint32_t k = i0 >> 2;  // 0
+    uint32_t lo = src[(uint64_t)k * 256u];
+    for (uint64_t b = d0; b < d1; b += 4) {
+        const uint32_t hi = (b - o + 4u <= len) || sh ? src[(uint64_t)(k + 1) * 256u] : 0u;
+        const uint32_t v = sh ? (lo >> sh) | (hi << (32u - sh)) : lo;
+        if (b + 4u <= cap) {
+            *(uint32_t *)(payload + b) = v;
+        } else {
+            for (uint32_t j = 0; j < 4; ++j)
+                if (b + j < cap) payload[b + j] = (uint8_t)(v >> (8u * j));
         }
-        __syncthreads();
-        // wave wid copies bytes [r0, r0+64) of streams wid*64 .. wid*64+63
-        for (int k = 0; k < 64; ++k) {
-            const int idx = wid * 64 + k;
-            const uint32_t n = s_len[idx];
-            const uint32_t b = r0 + (uint32_t)lane;
-            const uint64_t o = __shfl(my_off, k, 64) + b;
-            if (b < n && o < (uint64_t)payload_cap)
-                payload[o] = (uint8_t)(stage[idx * 17 + lane / 4] >> (8 * (lane & 3)));
-        }
-        __syncthreads();
+        lo = hi;
+        ++k;
     }
 }
 
@@ -256,12 +283,18 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
     dim3 grid((unsigned)(bps * p.n_slabs));
     const int CT = enc_tile_channels(p.A);
     const size_t lds_pairs = (size_t)CT * p.A * sizeof(uint32_t);
-    if (vec16)
-        hipLaunchKernelGGL(k_encode<true>, grid, dim3(256), lds_pairs + 256 * (size_t)(CT + 16), stream,
-                           sym, cdf, slots, stream_len, p, CT);
-    else
-        hipLaunchKernelGGL(k_encode<false>, grid, dim3(256), lds_pairs, stream, sym, cdf, slots,
-                           stream_len, p, CT);
+    const int per = (CT * (p.A / 2) + 255) / 256;  // pairs staged per thread
+#define KVC_ENC(V, P, L)                                                                             \
+    hipLaunchKernelGGL((k_encode<V, P>), grid, dim3(256), L, stream, sym, cdf, slots, stream_len, p, CT)
+    const size_t lds_syms = lds_pairs + 256 * (size_t)(CT + 16);
+    if (vec16) {
+        if (per <= 2) KVC_ENC(true, 2, lds_syms);
+        else KVC_ENC(true, 8, lds_syms);
+    } else {
+        if (per <= 2) KVC_ENC(false, 2, lds_pairs);
+        else KVC_ENC(false, 8, lds_pairs);
+    }
+#undef KVC_ENC
     hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
                        slab_total, p);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, slab_total, slab_off, p.n_slabs,

@@ -138,86 +138,94 @@ KVC_HD uint32_t enc_finish(EncState &e, const Out &out)
 
 // ----------------------------------------------------------------- decoder
 
-// Byte feed of one stream through a 64-byte per-lane ring in LDS.
+// Byte feed of one stream through a 16-dword per-lane ring in LDS.
 //
 // The stream [start, start+len) of a buffer of `cap` bytes (a multiple of 4,
-// at least 4) is read as aligned dwords from a0 = start & ~3.  Every group of
-// 8 symbols the lane takes in 16 fetched bytes (if it had asked for them) and,
-// while at most 48 bytes are unread, asks for the next 16 with four clamped
-// dword loads whose results are only used one group later.  8 symbols use at
-// most 16 bytes, so with 64 ring bytes the reader never catches up with the
-// writer.  The reader keeps one ring dword ahead in a register; bytes at or
-// past the stream end read as zero.
+// at least 4) is fetched as aligned raw dwords from a0 = start & ~3.  Stream
+// dword j (bytes start+4j .. start+4j+3) is funnel-shifted out of raw dwords
+// j and j+1, byte-swapped to big-endian and masked past the end of the stream
+// when it enters the ring, so a reader refill is one LDS read.  Every group
+// of 8 symbols (at most 16 bytes = 4 stream dwords) the lane commits the 4
+// raw dwords it asked for one group earlier (writing 4 stream dwords) and,
+// while at most 8 stream dwords are unread, asks for the next 4 raw dwords
+// with clamped loads.  That keeps at least 5 unread dwords at every group
+// start and never overwrites an unread one.  The reader keeps one ring dword
+// ahead in a register.
 template <class Ring>
 struct RingIn {
     const uint8_t *p;  // base + a0
-    Ring ring;         // this lane's 16 ring dwords (dword i of the stream at ring[i & 15])
-    uint32_t end;      // stream end, from p
-    uint32_t lim;      // largest offset from p at which a dword may be loaded
+    Ring ring;         // this lane's 16 ring dwords (stream dword j at ring[j & 15])
+    uint32_t len;      // stream length in bytes
+    uint32_t lim;      // largest offset from p at which a raw dword may be loaded
     uint32_t sh;       // (start & 3) * 8
-    uint32_t pf;       // bytes fetched into the ring (multiple of 16)
-    uint32_t rd;       // offset of the next dword to read from the ring
-    uint32_t cur;      // big-endian dword being consumed, masked
-    uint32_t nxt;      // big-endian dword after it, masked
-    uint32_t st[4];    // raw dwords in flight for [pf, pf + 16)
+    uint32_t w;        // stream dwords in the ring: [0, w)
+    uint32_t rd;       // next stream dword to read from the ring
+    uint32_t nxt;      // stream dword rd - 1, read ahead
+    uint32_t last;     // raw dword w: the low part of stream dword w
+    uint32_t st[4];    // raw dwords w+1 .. w+4 in flight
     uint32_t want;     // st[] holds a pending fetch
 
     KVC_HD uint32_t load(uint32_t off) const { return *(const uint32_t *)(p + (off < lim ? off : lim)); }
-    KVC_HD uint32_t be(uint32_t rawv, uint32_t off) const
+    // stream dword j from raw dwords j (lo) and j + 1 (hi), big-endian, masked
+    KVC_HD uint32_t make(uint32_t lo, uint32_t hi, uint32_t j) const
     {
-        const uint32_t v = kvc_bswap32(rawv);
-        const uint32_t keep = end > off ? end - off : 0u;
+        const uint32_t v = kvc_bswap32(sh ? (lo >> sh) | (hi << (32u - sh)) : lo);
+        const uint32_t keep = len > 4u * j ? len - 4u * j : 0u;
         return keep >= 4u ? v : (keep == 0u ? 0u : v & ~(0xFFFFFFFFu >> (8u * keep)));
     }
     KVC_HD void issue()
     {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) st[j] = load(pf + 4u * (uint32_t)j);
+        for (int k = 0; k < 4; ++k) st[k] = load(4u * (w + 1u + (uint32_t)k));
         want = 1;
     }
     KVC_HD void commit()
     {
+        uint32_t lo = last;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ring[((pf >> 2) + (uint32_t)j) & 15u] = st[j];
-        pf += 16u;
+        for (int k = 0; k < 4; ++k) {
+            ring[(w + (uint32_t)k) & 15u] = make(lo, st[k], w + (uint32_t)k);
+            lo = st[k];
+        }
+        last = lo;
+        w += 4u;
         want = 0;
     }
-    KVC_HD void init(const uint8_t *b, uint64_t start, uint64_t len, uint64_t capacity, Ring r)
+    KVC_HD void init(const uint8_t *b, uint64_t start, uint64_t length, uint64_t capacity, Ring r)
     {
         uint64_t a0 = start & ~(uint64_t)3;
         sh = (uint32_t)(start & 3u) * 8u;
-        end = (uint32_t)(start - a0 + len);
+        len = (uint32_t)length;
         if (a0 + 4u > capacity) {  // only an empty stream at the very end of the buffer
             a0 = capacity - 4u;
-            end = 0;
+            len = 0;
         }
         p = b + a0;
         const uint64_t room = capacity - 4u - a0;
         lim = room > 0xFFFFFFFCull ? 0xFFFFFFFCu : (uint32_t)room;
         ring = r;
-        pf = 0;
+        w = 0;
+        last = load(0);
         issue();
         commit();
         issue();
-        commit();  // 32 bytes in the ring
-        issue();   // the next 16 in flight
-        cur = be(ring[0], 0);
-        nxt = be(ring[1], 4);
-        rd = 8;
+        commit();  // stream dwords 0..7 in the ring
+        issue();   // raw dwords 9..12 in flight
+        nxt = ring[0];
+        rd = 1;
     }
     // Once per group of 8 symbols.
     KVC_HD void group()
     {
         if (want) commit();
-        if (pf - rd <= 48u) issue();
+        if (w - rd <= 8u) issue();
     }
     // The next 4 stream bytes as a big-endian dword.
     KVC_HD uint32_t next()
     {
-        const uint32_t v = sh ? (cur << sh) | (nxt >> (32u - sh)) : cur;
-        cur = nxt;
-        nxt = be(ring[(rd >> 2) & 15u], rd);
-        rd += 4u;
+        const uint32_t v = nxt;
+        nxt = ring[rd & 15u];
+        rd += 1u;
         return v;
     }
 };
@@ -239,10 +247,11 @@ KVC_HD void dec_init(DecState &d, In &in)
 }
 
 // After the symbol with cumulative frequency st and frequency fr was found
-// for r = range >> 16: narrow the interval and refill.  Returns 1 if the
-// stream is inconsistent with the CDF (code outside the new interval).
-template <class In>
-KVC_HD uint32_t dec_advance(DecState &d, uint32_t r, uint32_t st, uint32_t fr, In &in)
+// for r = range >> 16: narrow the interval and renormalise, taking the new
+// bits from bb.  Returns 1 if the stream is inconsistent with the CDF (code
+// outside the new interval).  A symbol consumes at most 16 bits (range >=
+// 2^8 after narrowing), so bb must hold at least 16 valid bits.
+KVC_HD uint32_t dec_advance(DecState &d, uint32_t r, uint32_t st, uint32_t fr)
 {
     d.code -= r * st;
     d.range = r * fr;
@@ -253,11 +262,17 @@ KVC_HD uint32_t dec_advance(DecState &d, uint32_t r, uint32_t st, uint32_t fr, I
     d.code = (uint32_t)(t >> 32);
     d.bb <<= n;
     d.nb -= n;
-    if (d.nb < 16u) {
+    return bad;
+}
+
+// Top bb up to at least 32 valid bits: enough for the next two symbols.
+template <class In>
+KVC_HD void dec_refill(DecState &d, In &in)
+{
+    if (d.nb < 32u) {
         d.bb |= (uint64_t)in.next() << (32u - d.nb);
         d.nb += 32u;
     }
-    return bad;
 }
 
 // ------------------------------------------------- per-symbol table lookups
@@ -297,15 +312,16 @@ KVC_HD uint32_t cdf_search(const Row &row, uint32_t A, uint32_t r, uint32_t code
 
 // Decode one symbol: search `row` (padded cumulative frequencies), take its
 // packed pair from `pairs`, narrow the interval.  *bad |= 1 when the stream
-// left its interval.
-template <int NSTEP, class Row, class Pairs, class In>
-KVC_HD uint32_t dec_symbol(DecState &d, const Row &row, const Pairs &pairs, uint32_t A, In &in,
+// left its interval.  The caller refills bb (dec_refill) before every second
+// symbol.
+template <int NSTEP, class Row, class Pairs>
+KVC_HD uint32_t dec_symbol(DecState &d, const Row &row, const Pairs &pairs, uint32_t A,
                            uint32_t *bad)
 {
     const uint32_t r = d.range >> 16;
     const uint32_t s = cdf_search<NSTEP>(row, A, r, d.code);
     const uint32_t p = pairs[s];
-    *bad |= dec_advance(d, r, p & 0xFFFFu, p >> 16, in);
+    *bad |= dec_advance(d, r, p & 0xFFFFu, p >> 16);
     return s;
 }
 

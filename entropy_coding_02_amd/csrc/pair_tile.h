@@ -9,8 +9,8 @@
 // Thread i handles the entry pairs (2j, 2j+1) with index i, i+256, ...: one
 // 4-byte load of cdf[2j], cdf[2j+1] plus cdf[2j+2] for the second frequency
 // (A is even, so rows and pairs are 4-byte aligned).
+template <int kMaxPer>  // pairs per thread: CT * A / 2 / 256 rounded up
 struct PairTile {
-    static constexpr int kMaxPer = 8;  // CT * A / 2 / 256 <= 8 for CT * A <= 4096
     uint32_t w[kMaxPer], n2[kMaxPer];
 
     __device__ void load(const uint16_t *rows, int c0, int CT, int C, int A)

@@ -39,19 +39,20 @@ int hostsim_decode_stream(const uint8_t *buf, int64_t cap, int64_t off, int64_t 
     std::vector<uint32_t> pairs(A);
     for (int32_t c = 0; c < C; ++c) {
         if ((c & 7) == 0) in.group();
+        if ((c & 1) == 0) dec_refill(d, in);
         const uint16_t *row = cdf_rows + (int64_t)c * A;
         for (uint32_t k = 0; k < P2; ++k) padded[k] = k < (uint32_t)A ? row[k] : 0xFFFFu;
         for (int32_t k = 0; k < A; ++k) pairs[k] = cdf_pair(row[k], k + 1 < A ? row[k + 1] : 65536u);
         uint32_t sym;
         switch (nstep) {
-        case 1: sym = dec_symbol<1>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
-        case 2: sym = dec_symbol<2>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
-        case 3: sym = dec_symbol<3>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
-        case 4: sym = dec_symbol<4>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
-        case 5: sym = dec_symbol<5>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
-        case 6: sym = dec_symbol<6>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
-        case 7: sym = dec_symbol<7>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
-        default: sym = dec_symbol<8>(d, padded.data(), pairs.data(), (uint32_t)A, in, &bad); break;
+        case 1: sym = dec_symbol<1>(d, padded.data(), pairs.data(), (uint32_t)A, &bad); break;
+        case 2: sym = dec_symbol<2>(d, padded.data(), pairs.data(), (uint32_t)A, &bad); break;
+        case 3: sym = dec_symbol<3>(d, padded.data(), pairs.data(), (uint32_t)A, &bad); break;
+        case 4: sym = dec_symbol<4>(d, padded.data(), pairs.data(), (uint32_t)A, &bad); break;
+        case 5: sym = dec_symbol<5>(d, padded.data(), pairs.data(), (uint32_t)A, &bad); break;
+        case 6: sym = dec_symbol<6>(d, padded.data(), pairs.data(), (uint32_t)A, &bad); break;
+        case 7: sym = dec_symbol<7>(d, padded.data(), pairs.data(), (uint32_t)A, &bad); break;
+        default: sym = dec_symbol<8>(d, padded.data(), pairs.data(), (uint32_t)A, &bad); break;
         }
         q[c] = (uint8_t)sym;
     }

@@ -53,6 +53,7 @@ def h_decode(lib, buf, off, length, rows, cap=None):
     cap = buf.size if cap is None else cap
     bad = lib.hostsim_decode_stream(buf.ctypes.data, cap, off, length, C, A, rows.ctypes.data,
                                     q.ctypes.data)
+    assert bad >= 0
     return q, bool(bad)
 
 
@@ -123,9 +124,11 @@ def test_decode_every_alignment_up_to_buffer_end(hs):
 
 
 def test_corrupt_streams_match_oracle_flag(hs):
-    rows = np.tile(cdf_from_counts([5, 20, 5, 1]), (64, 1))
-    for data in (b"\xff" * 16, b"\xfe\xff\xff\xff\x00", bytes(range(200, 256))):
-        buf = np.frombuffer(data + bytes((-len(data)) % 4), np.uint8).copy()
-        q_o, bad_o = oracle.decode_stream(data, rows)
-        q_h, bad_h = h_decode(hs, buf, 0, len(data), rows)
-        assert bad_o == bad_h and np.array_equal(q_o, q_h)
+    for rows in (np.tile(cdf_from_counts([5, 20, 5, 1]), (64, 1)),
+                 np.tile(np.array([0] + list(range(65504, 65535)), np.uint16), (64, 1))):  # f=1 tail
+        A = rows.shape[1]
+        for data in (b"\xff" * 16, b"\xfe\xff\xff\xff\x00", bytes(range(200, 256)), b"\xff\xfe" * 9):
+            buf = np.frombuffer(data + bytes((-len(data)) % 4), np.uint8).copy()
+            q_o, bad_o = oracle.decode_stream(data, rows)
+            q_h, bad_h = h_decode(hs, buf, 0, len(data), rows)
+            assert bad_o == bad_h and np.array_equal(q_o, q_h)
