@@ -49,7 +49,7 @@ int make_geometry(const kvc_desc *d, Geometry &g)
     g.slot_area = p.n_slabs * ((p.Tc + 255) / 256) * 256 * p.slot_bytes;
     g.scratch = g.slot_area + 8 * p.n_slabs;
     // launch-size limits (1-D grids of 32-bit block counts)
-    if (p.n_slabs * ((p.Tc + 255) / 256) >= ((int64_t)1 << 31)) return KVC_ERR_ARG;
+    if (p.n_slabs * ((p.Tc + 255) / 256) >= ((int64_t)1 << 29)) return KVC_ERR_ARG;  // x4 for k_pack
     if (p.n_slabs * ((p.C + 63) / 64) >= ((int64_t)1 << 31)) return KVC_ERR_ARG;
     return KVC_OK;
 }

@@ -8,8 +8,8 @@
 //              scratch slot as aligned dwords; the length to stream_len.
 // k_slab_sum:  per-slab sum of the stream lengths.
 // k_scan:      exclusive scan of the slab sums -> slab_off (one block).
-// k_pack:      per slab, an exclusive scan of its stream lengths, then each
-//              wave copies streams from their slots to the payload.
+// k_pack:      per 64 streams, their payload offsets, then the wave copies
+//              them from their slots to the payload through an LDS window.
 #include "kvc_common.h"
 #include "kvc_kernels.h"
 #include "lane_coder.h"
@@ -177,81 +177,105 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *__restrict__ slab
     }
 }
 
-// Per encoder block (256 streams of a slab), one lane per stream: the
-// stream's payload offset o (slab offset + the lengths before it), then its
-// bytes go out as whole aligned dwords wherever a destination dword lies
-// inside [o, o + len), each the funnel shift of two consecutive slot dwords
-// (slot loads are coalesced: lanes read their k-th dwords together); the up
-// to 3 + 3 bytes at either end, which share a dword with the neighbouring
-// streams, are written one byte at a time.  Nothing is written at or past
-// payload_cap.
-__global__ __launch_bounds__(256) void k_pack(const uint8_t *__restrict__ slots,
-                                              const uint16_t *__restrict__ stream_len,
-                                              const uint64_t *__restrict__ slab_off,
-                                              uint8_t *__restrict__ payload, int64_t payload_cap,
-                                              KParams p)
+// One wavefront per 64 consecutive streams of an encoder block (so 4 blocks
+// of 64 lanes per encoder block).  Lane i first finds stream i's payload
+// offset o (slab offset + the lengths before it).  The wave then walks its
+// streams' destination dwords in rounds of 64: it stages slot dwords
+// [64r - 1, 64r + 64) of all 64 streams in LDS (coalesced loads: the slots
+// are interleaved, lane i's k-th dword next to lane i + 1's), and writes the
+// streams one after the other, lane j taking destination dword 64r + j of
+// the stream: the funnel shift of two staged dwords, stored as one dword
+// when the destination dword lies inside [o, o + len) and byte by byte at
+// the stream's two ends, whose dwords it shares with its neighbours.  One
+// store instruction thus covers 256 contiguous bytes.  Nothing is written at
+// or past payload_cap.
+constexpr int PACK_W = 64;  // destination dwords per stream and round
+
+__global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
+                                             const uint16_t *__restrict__ stream_len,
+                                             const uint64_t *__restrict__ slab_off,
+                                             uint8_t *__restrict__ payload, int64_t payload_cap,
+                                             KParams p)
 {
-    __shared__ uint32_t s_red[4];
+    __shared__ uint32_t win[64 * (PACK_W + 1)];  // [stream][PACK_W + 1] staged slot dwords
     const int bps = (p.Tc + 255) / 256;
-    const int64_t slab = blockIdx.x / bps;
-    const int tb = (int)(blockIdx.x - slab * bps);
+    const int64_t eb = blockIdx.x >> 2;  // encoder block
+    const int wq = (int)(blockIdx.x & 3u);
+    const int64_t slab = eb / bps;
+    const int tb = (int)(eb - slab * bps);
     const SlabGeom g = slab_geom(p, slab);
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int t = tb * 256 + (int)threadIdx.x;
+    const int lane = (int)threadIdx.x;
+    const int t0 = tb * 256 + wq * 64;
+    if (t0 >= g.nj) return;  // the whole wave is past the slab's streams
+    const int t = t0 + lane;
     const bool active = t < g.nj;
 
-    uint32_t pre = 0;
-    const int n_before = min(tb * 256, g.nj);
-    for (int i = threadIdx.x; i < n_before; i += 256) pre += stream_len[g.sid0 + i];
+    uint32_t pre = 0;  // bytes of the slab's streams before this wave's
+    for (int i = lane; i < t0; i += 64) pre += stream_len[g.sid0 + i];
     pre = wave_sum_u32(pre);
-    if (lane == 0) s_red[wid] = pre;
-    __syncthreads();
-    pre = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-    __syncthreads();
     const uint32_t len = active ? stream_len[g.sid0 + t] : 0u;
     uint32_t incl = len;
     for (int off = 1; off < 64; off <<= 1) {
-        uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
-        if (lane >= off) incl += o;
+        uint32_t v = (uint32_t)__shfl_up((int)incl, off, 64);
+        if (lane >= off) incl += v;
     }
-    if (lane == 63) s_red[wid] = incl;
-    __syncthreads();
-    uint32_t wbase = 0;
-    for (int i = 0; i < wid; ++i) wbase += s_red[i];
-    if (!active || len == 0) return;  // no barriers below
-    const uint64_t o = slab_off[slab] + pre + wbase + incl - len;
-    const uint64_t e = o + len;
-    const uint32_t *src = (const uint32_t *)(slots + (int64_t)blockIdx.x * p.slot_bytes * 256) + threadIdx.x;
+    const uint64_t o = slab_off[slab] + pre + incl - len;
+    // destination dwords the stream touches, and its slot dwords
+    const uint32_t nd = len ? (uint32_t)(((o + len + 3u) >> 2) - (o >> 2)) : 0u;
+    const int ndw = (int)((len + 3u) >> 2);
+    const uint32_t rounds = (wave_max_u32(nd) + PACK_W - 1) / PACK_W;
+    // slot dword k of stream wq * 64 + i is dword k * 256 + wq * 64 + i of the block's slots
+    const uint32_t *srcw = (const uint32_t *)(slots + eb * p.slot_bytes * 256) + wq * 64;
+    const int slot_dw = (int)(p.slot_bytes / 4);
+    const int ndw_max = (int)wave_max_u32((uint32_t)ndw);
+    const uint32_t olo = (uint32_t)o, ohi = (uint32_t)(o >> 32);
     const uint64_t cap = (uint64_t)payload_cap;
-    // byte i of the stream is byte (i & 3) of slot dword i >> 2 (bytes in memory order)
-    auto byte_at = [&](uint32_t i) -> uint32_t { return (src[(i >> 2) * 256u] >> (8u * (i & 3u))) & 0xFFu; };
-    const uint64_t d0 = (o + 3u) & ~(uint64_t)3;  // first whole destination dword
-    const uint64_t d1 = e & ~(uint64_t)3;         // end of the whole destination dwords
-    if (d0 >= d1) {
-        for (uint32_t i = 0; i < len; ++i)
-            if (o + i < cap) payload[o + i] = (uint8_t)byte_at(i);
-        return;
-    }
-    for (uint64_t b = o; b < d0; ++b)
-        if (b < cap) payload[b] = (uint8_t)byte_at((uint32_t)(b - o));
-    for (uint64_t b = d1; b < e; ++b)
-        if (b < cap) payload[b] = (uint8_t)byte_at((uint32_t)(b - o));
-    // whole dwords: destination dword at b takes stream bytes [b - o, b - o + 4)
-    const uint32_t i0 = (uint32_t)(d0 - o);  // 0..3
-    const uint32_t sh = 8u * (i0 & 3u);
-    uint32_t k = i0 >> 2;  // 0
-    uint32_t lo = src[(uint64_t)k * 256u];
-    for (uint64_t b = d0; b < d1; b += 4) {
-        const uint32_t hi = (b - o + 4u <= len) || sh ? src[(uint64_t)(k + 1) * 256u] : 0u;
-        const uint32_t v = sh ? (lo >> sh) | (hi << (32u - sh)) : lo;
-        if (b + 4u <= cap) {
-            *(uint32_t *)(payload + b) = v;
-        } else {
-            for (uint32_t j = 0; j < 4; ++j)
-                if (b + j < cap) payload[b + j] = (uint8_t)(v >> (8u * j));
+    // staging: lane l loads 16 bytes = dword k of streams 4m .. 4m + 3 (m = l & 15) for
+    // k = k0 + 4q + (l >> 4), q = 0 .. 16, so one wave-wide load covers 4 slot rows
+    const int sg = lane >> 4, sm = lane & 15;
+
+    for (uint32_t r = 0; r < rounds; ++r) {
+        // win[i][u] = slot dword 64r - 1 + u of stream i (u = 0 .. 64; 0 before the stream)
+        const int k0 = (int)r * PACK_W - 1;
+        u32x4 v4[(PACK_W + 4) / 4];
+#pragma unroll
+        for (int q = 0; q < (PACK_W + 4) / 4; ++q) {
+            const int k = k0 + 4 * q + sg;
+            v4[q] = (k >= 0 && k < ndw_max && k < slot_dw) ? *(const u32x4 *)(srcw + (int64_t)k * 256 + 4 * sm)
+                                                            : u32x4{0, 0, 0, 0};
         }
-        lo = hi;
-        ++k;
+#pragma unroll
+        for (int q = 0; q < (PACK_W + 4) / 4; ++q) {
+            const int u = 4 * q + sg;
+            if (u <= PACK_W) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) win[(4 * sm + e) * (PACK_W + 1) + u] = v4[q][e];
+            }
+        }
+        __syncthreads();
+        for (int i = 0; i < 64; ++i) {
+            const uint32_t nd_i = (uint32_t)__builtin_amdgcn_readlane((int)nd, i);
+            if (r * PACK_W >= nd_i) continue;
+            const uint32_t j = r * PACK_W + (uint32_t)lane;
+            if (j >= nd_i) continue;
+            const uint64_t o_i = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ohi, i) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readlane((int)olo, i);
+            const uint32_t len_i = (uint32_t)__builtin_amdgcn_readlane((int)len, i);
+            const uint32_t lo = win[i * (PACK_W + 1) + lane], hi = win[i * (PACK_W + 1) + lane + 1];
+            const uint32_t a = (uint32_t)o_i & 3u;
+            // destination dword (o_i >> 2) + j holds stream bytes [4j - a, 4j - a + 4)
+            const uint32_t v = a ? (lo >> (32u - 8u * a)) | (hi << (8u * a)) : hi;
+            const uint64_t b = ((o_i >> 2) + j) * 4u;
+            if (b >= o_i && b + 4u <= o_i + len_i && b + 4u <= cap) {
+                *(uint32_t *)(payload + b) = v;
+            } else {
+                for (uint32_t q = 0; q < 4; ++q) {
+                    const uint64_t bq = b + q;
+                    if (bq >= o_i && bq < o_i + len_i && bq < cap) payload[bq] = (uint8_t)(v >> (8u * q));
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -299,7 +323,7 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
                        slab_total, p);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, slab_total, slab_off, p.n_slabs,
                        payload_cap, status);
-    hipLaunchKernelGGL(k_pack, grid, dim3(256), 0, stream, slots, stream_len,
+    hipLaunchKernelGGL(k_pack, dim3(grid.x * 4), dim3(64), 0, stream, slots, stream_len,
                        slab_off, payload, payload_cap, p);
     return hipGetLastError();
 }

@@ -40,6 +40,9 @@
  *     *dev_status (a device int32 the caller zeroes), which may be NULL.
  *   - Pointers to device buffers must be 4-byte aligned (16-byte alignment
  *     enables the vectorised paths); `desc->bins` is a host pointer.
+ *   - A descriptor is rejected (KVC_ERR_ARG) when its 1-D launches would not
+ *     fit 32-bit grids: 2^29 or more blocks of 256 streams (n_slabs times
+ *     ceil(chunk_tokens / 256)), or 2^31 or more blocks of 64 channels.
  */
 #ifndef KVC_H
 #define KVC_H
