@@ -184,7 +184,7 @@ int kvc_decode(const kvc_desc *desc, const uint8_t *payload, int64_t payload_byt
     if (rc != KVC_OK) return rc;
     if (out && out_dtype != KVC_F16 && out_dtype != KVC_F32) return KVC_ERR_ARG;
     if (g.p.n_rows == 0) return KVC_OK;
-    if (!slab_off || !stream_len || !cdf || !payload || payload_bytes < 4 || payload_bytes % 4 != 0 ||
+    if (!slab_off || !stream_len || !cdf || !payload || payload_bytes < 16 || payload_bytes % 4 != 0 ||
         (!out && !sym_out) || (out && !max1) || !aligned(payload, 4) || !aligned(slab_off, 8) ||
         !aligned(stream_len, 2) || !aligned(cdf, 4) || (dev_status && !aligned(dev_status, 4)))
         return KVC_ERR_ARG;

@@ -15,11 +15,22 @@
 #include "lane_coder.h"
 #include "pair_tile.h"
 
+// Launches of at most this many waves use the two-level table search for
+// 64-entry rows.
+#ifndef KVC_DEC_BLOCKS_MAX_WAVES
+#define KVC_DEC_BLOCKS_MAX_WAVES 2048
+#endif
+
 namespace {
 
-enum { ODT_F16 = 0, ODT_F32 = 1, ODT_NONE = 2 };
+enum { ODT_F16 = 0, ODT_F32 = 1 };
+// what k_decode writes: a compile-time set, so every store in the symbol loop
+// is unconditional and the loads of the byte feed never wait for them
+enum { OUT_F16 = 1, OUT_F32 = 2, OUT_SYM = 4 };
 
-template <bool VEC, int ODT, int NSTEP, int PER>
+// BLK: the two-level table search (two dependent LDS reads per symbol
+// instead of NSTEP, a few more VALU operations).
+template <bool VEC, int OUT, int NSTEP, bool BLK>
 __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payload,
                                                 int64_t payload_bytes,
                                                 const uint64_t *__restrict__ slab_off,
@@ -84,18 +95,34 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
     in.init(payload, off, len, (uint64_t)payload_bytes, ring);
     DecState d;
     dec_init(d, in);
-    const float m = (ODT != ODT_NONE) ? kvc_h2f(max1[row]) : 0.0f;
+    constexpr int ODT = (OUT & OUT_F16) ? ODT_F16 : (OUT & OUT_F32) ? ODT_F32 : -1;
+    constexpr int PER = NSTEP >= 7 ? 8 : 2;  // pairs staged per thread: CT * A / 2 / 256
+    const float m = (ODT >= 0) ? kvc_h2f(max1[row]) : 0.0f;
     uint32_t bad = 0;
-    uint8_t *so = (sym_out && active) ? sym_out + row * C : nullptr;
+    uint8_t *so = (OUT & OUT_SYM) ? sym_out + row * C : nullptr;
     const uint16_t *srows = cdf + slab * C * A;
     const int ntiles = (C + CT - 1) / CT;
     auto decode1 = [&](int cl) -> uint32_t {
-        return dec_symbol<NSTEP>(d, r16 + cl * P2, pr + cl * A, (uint32_t)A, &bad);
+        if constexpr (BLK) {
+            const lds_u16 *rowp = r16 + cl * P2;
+            auto piece = [&](uint32_t b) -> kvc_u32x4 { return *(const lds_u32x4 *)(rowp + 8u * b); };
+            return dec_symbol_blocks<NSTEP>(d, rowp, piece, pr + cl * A, (uint32_t)A, &bad);
+        } else {
+            return dec_symbol<NSTEP>(d, r16 + cl * P2, pr + cl * A, (uint32_t)A, &bad);
+        }
     };
 
     // the tile's rows arrive in registers while the previous tile is decoded,
     // and go into LDS between two barriers
     PairTile<PER> pt;
+    // fp16 output of a 32-channel block (VEC path)
+    uint32_t hw[16];
+    auto put_f16 = [&](int cb, int nb) {
+        uint4 *o = (uint4 *)((uint16_t *)out + row * C + cb);
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+            if (gi * 8 < nb) o[gi] = make_uint4(hw[4 * gi], hw[4 * gi + 1], hw[4 * gi + 2], hw[4 * gi + 3]);
+    };
     pt.load(srows, 0, CT, C, A);
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
@@ -111,7 +138,6 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
             // a line reach L2 together instead of 16-byte fragments.
             for (int cb = c0; cb < c1; cb += 32) {
                 const int nb = min(32, c1 - cb);  // 16 or 32
-                uint32_t hw[16];
                 float fw[8];
 #pragma unroll
                 for (int gi = 0; gi < 4; ++gi) {
@@ -124,7 +150,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
                         if ((i & 1) == 0) dec_refill(d, in);
                         const uint32_t s = decode1(cg - c0 + i);
                         sw[i >> 2] |= s << (8 * (i & 3));
-                        if constexpr (ODT != ODT_NONE) {
+                        if constexpr (ODT >= 0) {
                             const float y = lut[s] * m;
                             if constexpr (ODT == ODT_F16) {
                                 if (i & 1)
@@ -136,27 +162,22 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
                             }
                         }
                     }
-                    if (so) *(uint2 *)(so + cg) = make_uint2(sw[0], sw[1]);
+                    if constexpr ((OUT & OUT_SYM) != 0) *(uint2 *)(so + cg) = make_uint2(sw[0], sw[1]);
                     if constexpr (ODT == ODT_F32) {
                         float4 *o = (float4 *)((float *)out + row * C + cg);
                         o[0] = make_float4(fw[0], fw[1], fw[2], fw[3]);
                         o[1] = make_float4(fw[4], fw[5], fw[6], fw[7]);
                     }
                 }
-                if constexpr (ODT == ODT_F16) {
-                    uint4 *o = (uint4 *)((uint16_t *)out + row * C + cb);
-#pragma unroll
-                    for (int gi = 0; gi < 4; ++gi)
-                        if (gi * 8 < nb) o[gi] = make_uint4(hw[4 * gi], hw[4 * gi + 1], hw[4 * gi + 2], hw[4 * gi + 3]);
-                }
+                if constexpr (ODT == ODT_F16) put_f16(cb, nb);
             }
         } else {
             for (int c = c0; c < c1; ++c) {
                 if ((c & 7) == 0) in.group();
                 if ((c & 1) == 0) dec_refill(d, in);
                 const uint32_t s = decode1(c - c0);
-                if (so) so[c] = (uint8_t)s;
-                if constexpr (ODT != ODT_NONE) {
+                if constexpr ((OUT & OUT_SYM) != 0) so[c] = (uint8_t)s;
+                if constexpr (ODT >= 0) {
                     const float y = lut[s] * m;
                     if constexpr (ODT == ODT_F16)
                         ((uint16_t *)out)[row * C + c] = (uint16_t)kvc_f2h(y);
@@ -166,6 +187,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
             }
         }
     }
+
     if (active && bad) kvc_flag(status, KVC_DEV_CORRUPT);
 }
 
@@ -228,38 +250,44 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
     if (p.n_slabs == 0) return hipSuccess;
     const int64_t bps = (p.Tc + 255) / 256;
     dim3 grid((unsigned)(bps * p.n_slabs)), block(256);
-    const int odt = out ? out_dtype : ODT_NONE;
+    const int mode = (out ? (out_dtype == KVC_F16 ? OUT_F16 : OUT_F32) : 0) | (sym_out ? OUT_SYM : 0);
     const int CT = dec_tile_channels(p.A);
     const size_t lds = dec_lds_bytes(p.A, CT);
     vec = vec && (CT % 16 == 0);
     const int nstep = (int)cdf_nstep((uint32_t)p.A);
-    const int per = (CT * (p.A / 2) + 255) / 256;  // pairs staged per thread
-#define KVC_DEC(V, O, N)                                                                             \
-    if (per <= 2)                                                                                    \
-        hipLaunchKernelGGL((k_decode<V, O, N, 2>), grid, block, lds, stream, payload, payload_bytes, \
-                           slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT);            \
-    else                                                                                             \
-        hipLaunchKernelGGL((k_decode<V, O, N, 8>), grid, block, lds, stream, payload, payload_bytes, \
-                           slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
+    // The two-level search: measured faster for rows of up to 32 entries at any
+    // launch size (most so where few waves cannot hide LDS latency), slower
+    // for 64-entry rows unless the launch is that small.
+    const bool blk = (nstep >= 3 && nstep <= 5) ||
+                     (nstep == 6 && (int64_t)grid.x * 4 <= KVC_DEC_BLOCKS_MAX_WAVES);
+#define KVC_DEC(V, O, N, B)                                                                          \
+    hipLaunchKernelGGL((k_decode<V, O, N, B>), grid, block, lds, stream, payload, payload_bytes,     \
+                       slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
 #define KVC_DEC_N(V, O)                                                                              \
     switch (nstep) {                                                                                 \
-    case 2: KVC_DEC(V, O, 2); break;                                                                 \
-    case 3: KVC_DEC(V, O, 3); break;                                                                 \
-    case 4: KVC_DEC(V, O, 4); break;                                                                 \
-    case 5: KVC_DEC(V, O, 5); break;                                                                 \
-    case 6: KVC_DEC(V, O, 6); break;                                                                 \
-    case 7: KVC_DEC(V, O, 7); break;                                                                 \
-    default: KVC_DEC(V, O, 8); break;                                                                \
+    case 2: KVC_DEC(V, O, 2, false); break;                                                          \
+    case 3: if (blk) KVC_DEC(V, O, 3, true); else KVC_DEC(V, O, 3, false); break;                    \
+    case 4: if (blk) KVC_DEC(V, O, 4, true); else KVC_DEC(V, O, 4, false); break;                    \
+    case 5: if (blk) KVC_DEC(V, O, 5, true); else KVC_DEC(V, O, 5, false); break;                    \
+    case 6: if (blk) KVC_DEC(V, O, 6, true); else KVC_DEC(V, O, 6, false); break;                    \
+    case 7: KVC_DEC(V, O, 7, false); break;                                                          \
+    default: KVC_DEC(V, O, 8, false); break;                                                         \
+    }
+#define KVC_DEC_M(V)                                                                                 \
+    switch (mode) {                                                                                  \
+    case OUT_F16: KVC_DEC_N(V, OUT_F16) break;                                                       \
+    case OUT_F32: KVC_DEC_N(V, OUT_F32) break;                                                       \
+    case OUT_SYM: KVC_DEC_N(V, OUT_SYM) break;                                                       \
+    case OUT_F16 | OUT_SYM: KVC_DEC_N(V, OUT_F16 | OUT_SYM) break;                                   \
+    case OUT_F32 | OUT_SYM: KVC_DEC_N(V, OUT_F32 | OUT_SYM) break;                                   \
+    default: break; /* nothing to write: rejected by kvc_decode */                                  \
     }
     if (vec) {
-        if (odt == ODT_F16) KVC_DEC_N(true, ODT_F16)
-        else if (odt == ODT_F32) KVC_DEC_N(true, ODT_F32)
-        else KVC_DEC_N(true, ODT_NONE)
+        KVC_DEC_M(true)
     } else {
-        if (odt == ODT_F16) KVC_DEC_N(false, ODT_F16)
-        else if (odt == ODT_F32) KVC_DEC_N(false, ODT_F32)
-        else KVC_DEC_N(false, ODT_NONE)
+        KVC_DEC_M(false)
     }
+#undef KVC_DEC_M
 #undef KVC_DEC_N
 #undef KVC_DEC
     return hipGetLastError();

@@ -30,6 +30,8 @@
 
 #define KVC_HD __host__ __device__ __forceinline__
 
+typedef uint32_t kvc_u32x4 __attribute__((ext_vector_type(4)));
+
 KVC_HD uint32_t kvc_bswap32(uint32_t v) { return __builtin_bswap32(v); }
 
 // Shift count (bits) that brings range back to >= 2^24; range must be >= 2^8.
@@ -138,60 +140,96 @@ KVC_HD uint32_t enc_finish(EncState &e, const Out &out)
 
 // ----------------------------------------------------------------- decoder
 
+// Funnel shift: bits [sh, sh + 32) of the 64-bit value hi:lo (sh < 32).
+KVC_HD uint32_t kvc_alignbit(uint32_t hi, uint32_t lo, uint32_t sh)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_alignbit(hi, lo, sh);
+#else
+    return sh ? (lo >> sh) | (hi << (32u - sh)) : lo;
+#endif
+}
+
+// True if `c` holds on every active lane of the wavefront (on the host: c).
+KVC_HD bool kvc_all(bool c)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __all(c);
+#else
+    return c;
+#endif
+}
+
 // Byte feed of one stream through a 16-dword per-lane ring in LDS.
 //
 // The stream [start, start+len) of a buffer of `cap` bytes (a multiple of 4,
-// at least 4) is fetched as aligned raw dwords from a0 = start & ~3.  Stream
-// dword j (bytes start+4j .. start+4j+3) is funnel-shifted out of raw dwords
-// j and j+1, byte-swapped to big-endian and masked past the end of the stream
-// when it enters the ring, so a reader refill is one LDS read.  Every group
-// of 8 symbols (at most 16 bytes = 4 stream dwords) the lane commits the 4
-// raw dwords it asked for one group earlier (writing 4 stream dwords) and,
-// while at most 8 stream dwords are unread, asks for the next 4 raw dwords
-// with clamped loads.  That keeps at least 5 unread dwords at every group
-// start and never overwrites an unread one.  The reader keeps one ring dword
-// ahead in a register.
+// at least 16) is fetched as aligned raw dwords from a0 = start & ~3.
+// Stream dword j (bytes start+4j .. start+4j+3) is funnel-shifted out of raw
+// dwords j and j+1, byte-swapped to big-endian and, past the end of the
+// stream, masked to zero when it enters the ring, so a reader refill is one
+// LDS read.  Every group of 8 symbols (at most 16 bytes = 4 stream dwords)
+// the lane commits the 4 raw dwords it asked for one group earlier, if any,
+// and, while at most 8 stream dwords are unread, asks for the next 4 with
+// one 16-byte load.  That keeps at least 5 unread dwords at every group
+// start and never overwrites an unread one.  Near the end of the buffer the 16-byte
+// piece is moved back to end at `cap`, and the commit shifts its dwords into
+// place (dwords it cannot supply lie past the buffer, so past the stream,
+// and are masked).  The reader keeps one ring dword ahead in a register.
 template <class Ring>
 struct RingIn {
     const uint8_t *p;  // base + a0
     Ring ring;         // this lane's 16 ring dwords (stream dword j at ring[j & 15])
     uint32_t len;      // stream length in bytes
-    uint32_t lim;      // largest offset from p at which a raw dword may be loaded
+    int32_t lim16;     // largest offset from p at which a 16-byte piece may be loaded (>= -12)
     uint32_t sh;       // (start & 3) * 8
-    uint32_t w;        // stream dwords in the ring: [0, w)
+    uint32_t w;        // stream dwords in the ring: [0, w), a multiple of 4
     uint32_t rd;       // next stream dword to read from the ring
     uint32_t nxt;      // stream dword rd - 1, read ahead
     uint32_t last;     // raw dword w: the low part of stream dword w
-    uint32_t st[4];    // raw dwords w+1 .. w+4 in flight
-    uint32_t want;     // st[] holds a pending fetch
+    kvc_u32x4 st;      // the piece in flight: raw dwords w+1 .. w+4, moved back by `back` bytes
+    uint32_t back;     // how far the piece was moved back (0 unless near the buffer end)
+    uint32_t want;     // a piece is in flight
 
-    KVC_HD uint32_t load(uint32_t off) const { return *(const uint32_t *)(p + (off < lim ? off : lim)); }
-    // stream dword j from raw dwords j (lo) and j + 1 (hi), big-endian, masked
-    KVC_HD uint32_t make(uint32_t lo, uint32_t hi, uint32_t j) const
-    {
-        const uint32_t v = kvc_bswap32(sh ? (lo >> sh) | (hi << (32u - sh)) : lo);
-        const uint32_t keep = len > 4u * j ? len - 4u * j : 0u;
-        return keep >= 4u ? v : (keep == 0u ? 0u : v & ~(0xFFFFFFFFu >> (8u * keep)));
-    }
     KVC_HD void issue()
     {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) st[k] = load(4u * (w + 1u + (uint32_t)k));
-        want = 1;
+        const int32_t off = 4 * (int32_t)(w + 1u);
+        const int32_t at = off < lim16 ? off : lim16;
+        __builtin_memcpy(&st, p + at, 16);
+        back = (uint32_t)(off - at);
     }
     KVC_HD void commit()
     {
-        uint32_t lo = last;
+        kvc_u32x4 r = st;
+        if (!kvc_all(back == 0u)) {
+            // raw dword w+1+k is piece dword k + back/4 (none when that is >= 4)
+            const uint32_t d = back >> 2;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            ring[(w + (uint32_t)k) & 15u] = make(lo, st[k], w + (uint32_t)k);
-            lo = st[k];
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t i = (uint32_t)k + d;
+                r[k] = i == 1u ? st[1] : i == 2u ? st[2] : i == 3u ? st[3] : (i == 0u ? st[0] : 0u);
+            }
         }
-        last = lo;
+        uint32_t v[4];
+        v[0] = kvc_bswap32(kvc_alignbit(r[0], last, sh));
+        v[1] = kvc_bswap32(kvc_alignbit(r[1], r[0], sh));
+        v[2] = kvc_bswap32(kvc_alignbit(r[2], r[1], sh));
+        v[3] = kvc_bswap32(kvc_alignbit(r[3], r[2], sh));
+        if (!kvc_all(4u * w + 16u <= len)) {
+            // bytes at or past len read as zero
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t pos = 4u * (w + (uint32_t)k);
+                const uint32_t keep = len > pos ? len - pos : 0u;
+                v[k] = keep >= 4u ? v[k] : (keep == 0u ? 0u : v[k] & ~(0xFFFFFFFFu >> (8u * keep)));
+            }
+        }
+        const uint32_t b = w & 12u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ring[b + (uint32_t)k] = v[k];
+        last = r[3];
         w += 4u;
-        want = 0;
     }
-    KVC_HD void init(const uint8_t *b, uint64_t start, uint64_t length, uint64_t capacity, Ring r)
+    KVC_HD void init(const uint8_t *base, uint64_t start, uint64_t length, uint64_t capacity, Ring rg)
     {
         uint64_t a0 = start & ~(uint64_t)3;
         sh = (uint32_t)(start & 3u) * 8u;
@@ -200,17 +238,18 @@ struct RingIn {
             a0 = capacity - 4u;
             len = 0;
         }
-        p = b + a0;
-        const uint64_t room = capacity - 4u - a0;
-        lim = room > 0xFFFFFFFCull ? 0xFFFFFFFCu : (uint32_t)room;
-        ring = r;
+        p = base + a0;
+        const uint64_t room = capacity - 16u;  // the last piece starts here
+        lim16 = a0 > room ? -(int32_t)(a0 - room) : (room - a0 > 0x7FFFFFF0u ? 0x7FFFFFF0 : (int32_t)(room - a0));
+        ring = rg;
         w = 0;
-        last = load(0);
+        last = *(const uint32_t *)p;
         issue();
         commit();
         issue();
         commit();  // stream dwords 0..7 in the ring
         issue();   // raw dwords 9..12 in flight
+        want = 1;
         nxt = ring[0];
         rd = 1;
     }
@@ -218,7 +257,8 @@ struct RingIn {
     KVC_HD void group()
     {
         if (want) commit();
-        if (w - rd <= 8u) issue();
+        want = w - rd <= 8u ? 1u : 0u;
+        if (want) issue();
     }
     // The next 4 stream bytes as a big-endian dword.
     KVC_HD uint32_t next()
@@ -310,6 +350,30 @@ KVC_HD uint32_t cdf_search(const Row &row, uint32_t A, uint32_t r, uint32_t code
     return s < A - 1u ? s : A - 1u;
 }
 
+// Two-level form of cdf_search for rows padded to 2^NSTEP = 8 * NB entries
+// (NSTEP 3 .. 6): b = how many block heads row[8], row[16], .. qualify, then
+// n = how many of row[8b + 1 .. 8b + 7] qualify, those 8 entries read as one
+// 16-byte piece (piece(b) returns entries 8b .. 8b + 7, two per dword, the
+// lower index in the low half).  On a non-decreasing padded row the
+// qualifying entries form a prefix, so 8b + n is the k binary lifting finds;
+// the count needs two dependent table reads instead of NSTEP.
+template <int NSTEP, class Row, class Piece>
+KVC_HD uint32_t cdf_search_blocks(const Row &row, const Piece &piece, uint32_t A, uint32_t r,
+                                  uint32_t code)
+{
+    static_assert(NSTEP >= 3 && NSTEP <= 6, "rows of 8 to 64 entries");
+    constexpr int NB = 1 << (NSTEP - 3);
+    uint32_t b = 0;
+#pragma unroll
+    for (int i = 1; i < NB; ++i) b += r * (uint32_t)row[8 * i] <= code ? 1u : 0u;
+    const kvc_u32x4 v = piece(b);
+    uint32_t n = 0;
+#pragma unroll
+    for (int i = 1; i < 8; ++i) n += r * ((v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) <= code ? 1u : 0u;
+    const uint32_t s = 8u * b + n;
+    return s < A - 1u ? s : A - 1u;
+}
+
 // Decode one symbol: search `row` (padded cumulative frequencies), take its
 // packed pair from `pairs`, narrow the interval.  *bad |= 1 when the stream
 // left its interval.  The caller refills bb (dec_refill) before every second
@@ -320,6 +384,18 @@ KVC_HD uint32_t dec_symbol(DecState &d, const Row &row, const Pairs &pairs, uint
 {
     const uint32_t r = d.range >> 16;
     const uint32_t s = cdf_search<NSTEP>(row, A, r, d.code);
+    const uint32_t p = pairs[s];
+    *bad |= dec_advance(d, r, p & 0xFFFFu, p >> 16);
+    return s;
+}
+
+// dec_symbol with the two-level search (cdf_search_blocks).
+template <int NSTEP, class Row, class Piece, class Pairs>
+KVC_HD uint32_t dec_symbol_blocks(DecState &d, const Row &row, const Piece &piece, const Pairs &pairs,
+                                  uint32_t A, uint32_t *bad)
+{
+    const uint32_t r = d.range >> 16;
+    const uint32_t s = cdf_search_blocks<NSTEP>(row, piece, A, r, d.code);
     const uint32_t p = pairs[s];
     *bad |= dec_advance(d, r, p & 0xFFFFu, p >> 16);
     return s;

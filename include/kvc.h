@@ -153,8 +153,8 @@ int kvc_encode(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf, vo
  * range = r*f_s, refill bytes while range < 2^24 (bytes past the stream read
  * as 0).  Then y = fp32(fp32(s - MAX) / MAX) * max1, rounded to out_dtype.
  *   payload        payload_bytes bytes (device, read; never read at or past payload_bytes).
- *                  payload_bytes must be a multiple of 4 and at least 4 (the decoder
- *                  reads whole aligned dwords); it may exceed the packed size.
+ *                  payload_bytes must be a multiple of 4 and at least 16 (the decoder
+ *                  reads aligned dwords in 16-byte pieces); it may exceed the packed size.
  *   slab_off       [n_slabs + 1] uint64 (device, read)
  *   stream_len     [n_streams] uint16 (device, read)
  *   cdf            [NC][L][2][C][A] uint16 (device, read)

@@ -30,9 +30,9 @@ def run_gpu(kv_np: np.ndarray, bins: np.ndarray, Tc: int, fused: bool = True,
     total = int(slab_off[-1])
     buf.dev_status.zero_()
     if exact_payload:
-        # the smallest buffer the decoder accepts: the packed size rounded up to whole dwords,
-        # the padding filled with junk it must not use
-        nb = max(4, (total + 3) // 4 * 4)
+        # the smallest buffer the decoder accepts: the packed size rounded up to whole dwords
+        # (at least 16 bytes), the padding filled with junk it must not use
+        nb = max(16, (total + 3) // 4 * 4)
         pay = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
         pay[:total] = buf.payload[:total]
         kvc.decode(buf, out_dtype=out_dtype, payload=pay, payload_bytes=nb)

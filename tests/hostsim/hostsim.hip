@@ -2,6 +2,7 @@
 // compiled for the host, so CPU tests can compare it with the oracle stream
 // by stream before any kernel runs.  Test infrastructure only.
 #include <stdint.h>
+#include <string.h>
 #include <vector>
 
 #include "../../entropy_coding_02_amd/csrc/lane_coder.h"
@@ -26,8 +27,10 @@ int64_t hostsim_encode_stream(const uint8_t *q, int32_t C, int32_t A, const uint
 
 // Decode the stream at [off, off+len) of a buffer of `cap` bytes (a multiple
 // of 4, at least 4); returns the corrupt flag.
+// search 0: binary lifting; 1: the two-level search where the padded row has
+// 8 to 64 entries (binary lifting otherwise).
 int hostsim_decode_stream(const uint8_t *buf, int64_t cap, int64_t off, int64_t len, int32_t C,
-                          int32_t A, const uint16_t *cdf_rows, uint8_t *q)
+                          int32_t A, const uint16_t *cdf_rows, uint8_t *q, int32_t search)
 {
     uint32_t ring[16];
     RingIn<uint32_t *> in;
@@ -43,7 +46,22 @@ int hostsim_decode_stream(const uint8_t *buf, int64_t cap, int64_t off, int64_t 
         const uint16_t *row = cdf_rows + (int64_t)c * A;
         for (uint32_t k = 0; k < P2; ++k) padded[k] = k < (uint32_t)A ? row[k] : 0xFFFFu;
         for (int32_t k = 0; k < A; ++k) pairs[k] = cdf_pair(row[k], k + 1 < A ? row[k + 1] : 65536u);
+        auto piece = [&](uint32_t b) {
+            kvc_u32x4 v;
+            memcpy(&v, padded.data() + 8 * b, 16);
+            return v;
+        };
         uint32_t sym;
+        if (search == 1 && nstep >= 3 && nstep <= 6) {
+            switch (nstep) {
+            case 3: sym = dec_symbol_blocks<3>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
+            case 4: sym = dec_symbol_blocks<4>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
+            case 5: sym = dec_symbol_blocks<5>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
+            default: sym = dec_symbol_blocks<6>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
+            }
+            q[c] = (uint8_t)sym;
+            continue;
+        }
         switch (nstep) {
         case 1: sym = dec_symbol<1>(d, padded.data(), pairs.data(), (uint32_t)A, &bad); break;
         case 2: sym = dec_symbol<2>(d, padded.data(), pairs.data(), (uint32_t)A, &bad); break;

@@ -78,8 +78,8 @@ def test_null_and_misaligned_pointers_rejected(lib):
     assert lib.kvc_quantize(d.ref, 66, 64, 64, None, None, None) == kvc.KVC_ERR_ARG  # kv % 4 != 0
     assert lib.kvc_encode(d.ref, 64, 64, 64, 1, 64, 64, 64, 100, None, None) == kvc.KVC_ERR_CAPACITY
     assert lib.kvc_decode(d.ref, 64, 16, 64, 64, 64, 64, None, 64, 7, None, None) == kvc.KVC_ERR_ARG
-    # payload_bytes must be a whole number of dwords, at least one
-    for nb in (0, 2, 10):
+    # payload_bytes must be a whole number of dwords, at least four
+    for nb in (0, 2, 4, 10, 12, 18):
         assert lib.kvc_decode(d.ref, 64, nb, 64, 64, 64, 64, None, 64, 0, None, None) == kvc.KVC_ERR_ARG
     assert lib.kvc_dequantize(d.ref, 64, 64, 64, 9, None) == kvc.KVC_ERR_ARG
     assert lib.kvc_status_string(kvc.KVC_ERR_CAPACITY) == b"buffer too small"

@@ -2,7 +2,8 @@
 the host and compared with the oracle stream by stream: byte-identical
 encodes (including carries into bytes already written and the trailing-zero
 trim reaching back into them) and identical decodes from streams placed at
-every byte alignment, up against the exact end of the buffer."""
+every byte alignment, up against the exact end of the buffer (the decoder's
+buffers are whole dwords, at least 16 bytes)."""
 import ctypes
 import os
 import subprocess
@@ -33,7 +34,7 @@ def hs():
     lib.hostsim_encode_stream.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P]
     lib.hostsim_decode_stream.restype = ctypes.c_int
     lib.hostsim_decode_stream.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                          ctypes.c_int32, ctypes.c_int32, P, P]
+                                          ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32]
     return lib
 
 
@@ -46,13 +47,13 @@ def h_encode(lib, q, rows):
     return slot[:n].tobytes()
 
 
-def h_decode(lib, buf, off, length, rows, cap=None):
+def h_decode(lib, buf, off, length, rows, cap=None, search=0):
     rows = np.ascontiguousarray(rows, dtype=np.uint16)
     C, A = rows.shape
     q = np.empty(C, dtype=np.uint8)
     cap = buf.size if cap is None else cap
     bad = lib.hostsim_decode_stream(buf.ctypes.data, cap, off, length, C, A, rows.ctypes.data,
-                                    q.ctypes.data)
+                                    q.ctypes.data, search)
     assert bad >= 0
     return q, bool(bad)
 
@@ -65,14 +66,20 @@ def check(lib, q, rows):
 
 
 def test_random_and_skewed_streams(hs):
+    """Encodes byte-identical to the oracle; decodes (both table searches) give
+    the symbols back."""
     rng = np.random.default_rng(31)
     for trial in range(800):
-        A = int(rng.choice([2, 4, 6, 16, 32, 64, 256]))
+        A = int(rng.choice([2, 4, 6, 8, 12, 16, 32, 40, 64, 256]))
         C = int(rng.integers(1, 300))
         rows = np.array([cdf_from_counts((rng.integers(0, 3, A) * rng.integers(1, 40000, A)).tolist())
                          for _ in range(C)], dtype=np.uint16)
-        q = rng.integers(0, A, C)
-        check(hs, q, rows)
+        q = rng.integers(0, A, C).astype(np.uint8)
+        data = check(hs, q, rows)
+        buf = np.frombuffer(data + bytes(max(16, (len(data) + 4) // 4 * 4) - len(data)), np.uint8).copy()
+        for search in (0, 1):
+            got, bad = h_decode(hs, buf, 0, len(data), rows, search=search)
+            assert not bad and np.array_equal(got, q), (trial, search)
 
 
 def test_forced_carries_through_written_bytes(hs):
@@ -97,7 +104,8 @@ def test_zero_tail_trim_reaches_written_dwords(hs):
     check(hs, np.zeros(400, np.uint8), rows)  # empty stream
 
 
-def test_decode_every_alignment_up_to_buffer_end(hs):
+@pytest.mark.parametrize("search", [0, 1])
+def test_decode_every_alignment_up_to_buffer_end(hs, search):
     """Streams at every byte alignment; the buffer ends right after the last
     stream (rounded up to whole dwords, the padding filled with junk that
     must be masked off), so the reader's clamped loads are exercised."""
@@ -117,18 +125,19 @@ def test_decode_every_alignment_up_to_buffer_end(hs):
         buf = np.frombuffer(body + b"\xa5" * pad, dtype=np.uint8).copy()
         off = lead
         for q, s in zip(syms, streams):
-            got, bad = h_decode(hs, buf, off, len(s), rows)
+            got, bad = h_decode(hs, buf, off, len(s), rows, search=search)
             if q is not None:
                 assert not bad and np.array_equal(got, q)
             off += len(s)
 
 
-def test_corrupt_streams_match_oracle_flag(hs):
+@pytest.mark.parametrize("search", [0, 1])
+def test_corrupt_streams_match_oracle_flag(hs, search):
     for rows in (np.tile(cdf_from_counts([5, 20, 5, 1]), (64, 1)),
                  np.tile(np.array([0] + list(range(65504, 65535)), np.uint16), (64, 1))):  # f=1 tail
         A = rows.shape[1]
         for data in (b"\xff" * 16, b"\xfe\xff\xff\xff\x00", bytes(range(200, 256)), b"\xff\xfe" * 9):
-            buf = np.frombuffer(data + bytes((-len(data)) % 4), np.uint8).copy()
+            buf = np.frombuffer(data + bytes(max(16 - len(data), (-len(data)) % 4)), np.uint8).copy()
             q_o, bad_o = oracle.decode_stream(data, rows)
-            q_h, bad_h = h_decode(hs, buf, 0, len(data), rows)
+            q_h, bad_h = h_decode(hs, buf, 0, len(data), rows, search=search)
             assert bad_o == bad_h and np.array_equal(q_o, q_h)
