@@ -41,6 +41,8 @@ int make_geometry(const kvc_desc *d, Geometry &g)
     if (NC > INT32_MAX) return KVC_ERR_ARG;
     p.NC = (int32_t)NC;
     p.last_nj = NC ? (int32_t)(p.T - (NC - 1) * p.Tc) : 0;
+    p.rn_full = 1.0 / (double)p.Tc;
+    p.rn_last = p.last_nj ? 1.0 / (double)p.last_nj : 0.0;
     p.n_rows = 2 * (int64_t)p.L * p.T;
     p.n_streams = p.n_rows;
     p.n_slabs = NC * 2 * p.L;
@@ -136,6 +138,8 @@ int kvc_quantize(const kvc_desc *desc, const uint16_t *kv, uint8_t *sym, uint16_
         return KVC_ERR_ARG;
     hipStream_t s = (hipStream_t)stream;
     const bool vec8 = (g.p.C % 8 == 0) && aligned(kv, 16) && aligned(sym, 8);
+    if (cdf && vec8 && aligned(cdf, 16) && quant_cdf_fused_ok(g.p))
+        return launch_status(launch_quant_cdf(kv, sym, max1, cdf, g.p, dev_status, s));
     hipError_t e = launch_quantize_rows(kv, sym, max1, g.p, dev_status, vec8, s);
     if (e == hipSuccess && cdf) e = launch_cdf(sym, cdf, g.p, s);
     return launch_status(e);

@@ -6,7 +6,7 @@
 // channels in different banks, so the atomics of a wave (one channel per
 // lane, all counting the modal symbols) do not collide.  Each thread then
 // turns its channel's row into cdf_k = k + floor(C_k * (65536 - A) / N_j)
-// in place, and the block writes the tile's [CT][A] uint16 rows, which are
+// in place (kvc_cdf_entry), and the block writes the tile's [CT][A] uint16 rows, which are
 // contiguous in the output, with coalesced stores.
 #include "kvc_common.h"
 #include "kvc_kernels.h"
@@ -39,11 +39,11 @@ __global__ __launch_bounds__(256) void k_cdf(const uint8_t *__restrict__ sym,
     __syncthreads();
     if (tg == 0 && c < C) {
         uint32_t *h = hist + cl * stride;
-        const uint32_t K = 65536u - (uint32_t)A, N = (uint32_t)g.nj;
+        const uint32_t K = 65536u - (uint32_t)A;
         uint32_t Ck = 0;
         for (int k = 0; k < A; ++k) {
             uint32_t n = h[k];
-            h[k] = (uint32_t)k + (Ck * K) / N;  // Ck * K < 2^32 since Ck <= N <= 65535
+            h[k] = kvc_cdf_entry((uint32_t)k, Ck, K, g.rn);
             Ck += n;
         }
     }
@@ -97,14 +97,14 @@ __global__ __launch_bounds__(256) void k_cdf_wide(const uint8_t *__restrict__ sy
     if (c < C) {
         const int cl = (int)threadIdx.x;
         const uint32_t *h = hist + cl * W + (cl >> 2);
-        const uint32_t K = 65536u - (uint32_t)A, N = (uint32_t)g.nj;
+        const uint32_t K = 65536u - (uint32_t)A;
         uint16_t *dst = cdf + (slab * C + c) * A;
         uint32_t Ck = 0;
         for (int k = 0; k < A; k += 2) {
             const uint32_t w = h[k >> 1];
-            const uint32_t lo = (uint32_t)k + (Ck * K) / N;
+            const uint32_t lo = kvc_cdf_entry((uint32_t)k, Ck, K, g.rn);
             Ck += w & 0xFFFFu;
-            const uint32_t hi = (uint32_t)(k + 1) + (Ck * K) / N;
+            const uint32_t hi = kvc_cdf_entry((uint32_t)(k + 1), Ck, K, g.rn);
             Ck += w >> 16;
             *(uint32_t *)(dst + k) = lo | (hi << 16);  // A even, rows 4-byte aligned
         }

@@ -27,6 +27,8 @@ struct KParams {
     int32_t L, C, A, Tc;
     int32_t NC;         // chunks
     int32_t last_nj;    // tokens of the last chunk
+    double rn_full;     // 1 / Tc, rounded to double
+    double rn_last;     // 1 / last_nj, rounded to double (0 if there are no tokens)
     uint8_t maxq[2 * KVC_MAX_LAYERS];  // MAX = bins/2 - 1 per (l, kv)
 };
 
@@ -35,6 +37,7 @@ struct SlabGeom {
     int64_t sid0;    // stream id of the slab's first token
     int32_t nj;      // tokens in the slab
     int32_t lk;      // 2*l + kv
+    double rn;       // 1 / nj, rounded to double
 };
 
 __device__ __forceinline__ SlabGeom slab_geom(const KParams &p, int64_t s)
@@ -44,9 +47,23 @@ __device__ __forceinline__ SlabGeom slab_geom(const KParams &p, int64_t s)
     int64_t j = s / twoL;
     g.lk = (int32_t)(s - j * twoL);
     g.nj = (j == p.NC - 1) ? p.last_nj : p.Tc;
+    g.rn = (j == p.NC - 1) ? p.rn_last : p.rn_full;
     g.row0 = (int64_t)g.lk * p.T + j * p.Tc;
     g.sid0 = j * twoL * p.Tc + (int64_t)g.lk * g.nj;
     return g;
+}
+
+// CDF entry k of a row whose counts below k sum to Ck, over N tokens, with
+// K = 65536 - A:  k + floor(Ck * K / N), rn = 1/N rounded to double.
+// Exact: x = Ck * K < 2^32 and N < 2^16, so x * rn is x/N within a relative
+// 2^-52 (under 2^-36 absolutely).  If x/N is an integer m the biased
+// product lands in (m, m + 2^-17); otherwise x/N is at least 1/N >= 2^-16
+// away from both neighbouring integers, and the product plus 2^-18 stays
+// strictly between them.  The integer part is the floor.
+__device__ __forceinline__ uint32_t kvc_cdf_entry(uint32_t k, uint32_t Ck, uint32_t K, double rn)
+{
+    const double q = (double)(Ck * K) * rn;
+    return k + (uint32_t)(q + 0x1p-18);
 }
 
 __device__ __forceinline__ float kvc_h2f(uint32_t bits)

@@ -8,6 +8,11 @@
 hipError_t launch_quantize_rows(const uint16_t *kv, uint8_t *sym, uint16_t *max1, const KParams &p,
                                 int32_t *status, bool vec8, hipStream_t stream);
 
+// Fused quantize + histogram + CDF (one kernel), where the shape allows it.
+bool quant_cdf_fused_ok(const KParams &p);
+hipError_t launch_quant_cdf(const uint16_t *kv, uint8_t *sym, uint16_t *max1, uint16_t *cdf,
+                            const KParams &p, int32_t *status, hipStream_t stream);
+
 hipError_t launch_cdf(const uint8_t *sym, uint16_t *cdf, const KParams &p, hipStream_t stream);
 
 hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots,

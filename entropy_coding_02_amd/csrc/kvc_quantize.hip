@@ -1,4 +1,5 @@
-// kvc_quantize.hip - group max-abs quantization ([CG] 2.3 step 1).
+// kvc_quantize.hip - group max-abs quantization ([CG] 2.3 step 1), alone or
+// fused with the histograms and CDFs of steps 2-3.
 //
 // One wavefront per (layer, K|V, token) row.  For finite fp16, |x| orders
 // like its bit pattern with the sign cleared, so the row max is an integer
@@ -93,7 +94,129 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restric
     }
 }
 
+// Quantization, histograms and CDFs in one pass: one block of 1024 threads
+// per slab (chunk, layer, K|V), for C % 8 == 0 and C <= 512 * KREG.  Each
+// wave takes whole token rows: the row (8 channels per 16-byte piece, KREG
+// pieces per lane) stays in registers for the integer max, the quantizer
+// and the symbol stores, and every symbol is counted at once in an LDS
+// histogram of packed 16-bit counters.  Counter pair (channel c, symbols
+// 2h, 2h+1) is word h * C + (c & 7) * (C / 8) + (c >> 3): at each step the
+// lanes of a wave hold channels 8 apart, which this layout puts in
+// consecutive words, so their atomics hit distinct banks whatever the
+// symbols.  After the last row each thread turns one channel's counts into
+// its CDF row (kvc_cdf_entry) and writes it with 16-byte stores.  The input
+// is read once; no pass re-reads the symbols.
+template <int KREG>
+__global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__ kv,
+                                                    uint8_t *__restrict__ sym,
+                                                    uint16_t *__restrict__ max1,
+                                                    uint16_t *__restrict__ cdf, KParams p,
+                                                    int32_t *status)
+{
+    extern __shared__ uint32_t hist[];
+    const int64_t slab = blockIdx.x;
+    const SlabGeom g = slab_geom(p, slab);
+    const int C = p.C, A = p.A, C8 = C / 8;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int nwords = (A / 2) * C;
+    for (int i = threadIdx.x; i < nwords; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    const float M = (float)p.maxq[g.lk];
+    const uint32_t amax = (uint32_t)A - 1u;
+    for (int t = wid; t < g.nj; t += nw) {
+        const int64_t row = g.row0 + t;
+        const uint16_t *x = kv + row * C;
+        u32x4 reg[KREG];
+        uint32_t mx = 0;
+#pragma unroll
+        for (int k = 0; k < KREG; ++k) {
+            const int pi = lane + 64 * k;
+            reg[k] = pi < C8 ? *(const u32x4 *)(x + 8 * pi) : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t a = reg[k][i] & 0x7FFF7FFFu;
+                mx = max(mx, max(a & 0xFFFFu, a >> 16));
+            }
+        }
+        mx = wave_max_u32(mx);
+        const float m = kvc_h2f(mx);
+        const float factor = (mx != 0) ? M / m : 0.0f;
+        if (mx >= 0x7C00u && lane == 0) kvc_flag(status, KVC_DEV_NONFINITE);
+        if (lane == 0) max1[row] = (uint16_t)mx;
+#pragma unroll
+        for (int k = 0; k < KREG; ++k) {
+            const int pi = lane + 64 * k;
+            if (pi >= C8) continue;
+            uint32_t b[2] = {0, 0};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t h = (reg[k][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                const uint32_t q = quant1(h, factor, M);
+                b[i >> 2] |= q << (8 * (i & 3));
+                const uint32_t s = q < amax ? q : amax;  // only non-finite rows exceed A - 1
+                atomicAdd(&hist[(int)(s >> 1) * C + i * C8 + pi], 1u << (16u * (s & 1u)));
+            }
+            *(uint2 *)(sym + row * C + 8 * pi) = make_uint2(b[0], b[1]);
+        }
+    }
+    __syncthreads();
+    const uint32_t K = 65536u - (uint32_t)A;
+    for (int c = threadIdx.x; c < C; c += blockDim.x) {
+        const uint32_t *h = hist + (c & 7) * C8 + (c >> 3);
+        uint32_t *dst = (uint32_t *)(cdf + (slab * C + c) * A);
+        uint32_t Ck = 0;
+        for (int k = 0; k < A; k += 8) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t cnt = h[(k / 2 + e) * C];
+                const uint32_t lo = kvc_cdf_entry((uint32_t)(k + 2 * e), Ck, K, g.rn);
+                Ck += cnt & 0xFFFFu;
+                const uint32_t hi = kvc_cdf_entry((uint32_t)(k + 2 * e + 1), Ck, K, g.rn);
+                Ck += cnt >> 16;
+                w[e] = lo | (hi << 16);
+            }
+            *(u32x4 *)(dst + k / 2) = u32x4{w[0], w[1], w[2], w[3]};  // A % 8 == 0
+        }
+    }
+}
+
 }  // namespace
+
+// Dynamic LDS of the fused pass, or 0 when the shape does not qualify
+// (C % 8, C <= 1024, A % 8, histogram within the device's LDS per block).
+static size_t quant_cdf_lds(const KParams &p)
+{
+    if (p.C % 8 != 0 || p.C > 1024 || p.A % 8 != 0) return 0;
+    const size_t bytes = sizeof(uint32_t) * (size_t)(p.A / 2) * (size_t)p.C;
+    int dev = 0, lim = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return 0;
+    return bytes <= (size_t)lim ? bytes : 0;
+}
+
+bool quant_cdf_fused_ok(const KParams &p) { return quant_cdf_lds(p) != 0; }
+
+hipError_t launch_quant_cdf(const uint16_t *kv, uint8_t *sym, uint16_t *max1, uint16_t *cdf,
+                            const KParams &p, int32_t *status, hipStream_t stream)
+{
+    if (p.n_slabs == 0) return hipSuccess;
+    const size_t lds = quant_cdf_lds(p);
+    if (lds == 0) return hipErrorInvalidValue;
+    const void *fn = p.C <= 512 ? (const void *)k_quant_cdf<1> : (const void *)k_quant_cdf<2>;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    if (p.C <= 512)
+        hipLaunchKernelGGL(k_quant_cdf<1>, dim3((unsigned)p.n_slabs), dim3(1024), lds, stream, kv, sym,
+                           max1, cdf, p, status);
+    else
+        hipLaunchKernelGGL(k_quant_cdf<2>, dim3((unsigned)p.n_slabs), dim3(1024), lds, stream, kv, sym,
+                           max1, cdf, p, status);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_rows(const uint16_t *kv, uint8_t *sym, uint16_t *max1, const KParams &p,
                                 int32_t *status, bool vec8, hipStream_t stream)
