@@ -44,8 +44,15 @@ def parse():
     return ap.parse_args()
 
 
-DECODE_SOURCES = ["entropy_coding_02_amd/csrc/kvc_decode.hip", "entropy_coding_02_amd/csrc/lane_coder.h",
-                  "entropy_coding_02_amd/csrc/pair_tile.h", "entropy_coding_02_amd/csrc/kvc_common.h"]
+CSRC = "entropy_coding_02_amd/csrc/"
+COMMON = [CSRC + "kvc_common.h"]
+# the sources each kernel is built from (a traffic record is used only while they are unchanged)
+KERNEL_SOURCES = {
+    "k_decode": [CSRC + "kvc_decode.hip", CSRC + "lane_coder.h", CSRC + "pair_tile.h"] + COMMON,
+    "k_encode": [CSRC + "kvc_encode.hip", CSRC + "lane_coder.h", CSRC + "pair_tile.h"] + COMMON,
+    "k_pack": [CSRC + "kvc_encode.hip"] + COMMON,
+    "k_quant_cdf": [CSRC + "kvc_quantize.hip"] + COMMON,
+}
 COPY_BYTES = 256 << 20
 
 
@@ -57,9 +64,18 @@ def sources_sha256(files):
     return h.hexdigest()
 
 
+def kernel_key(name: str):
+    low = name.lower()
+    if "elementwise" in low and "add" in low:
+        return "copy"
+    base = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0].split("<")[0]
+    return base.strip() if base.strip() in KERNEL_SOURCES else None
+
+
 def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of k_decode, scaled by what the
-    same counters read for the COPY_BYTES copy kernel, into profiles/traffic.json."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each hot kernel, scaled by
+    what the same counters read for the COPY_BYTES copy kernel, into
+    profiles/traffic.json."""
     import csv
 
     def per_kernel(path, counter):
@@ -67,10 +83,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
         for r in csv.DictReader(open(path)):
             if r.get("Counter_Name") != counter:
                 continue
-            name = r["Kernel_Name"]
-            low = name.lower()
-            key = ("copy" if ("elementwise" in low and "add" in low) else
-                   ("k_decode" if "k_decode" in name else None))
+            key = kernel_key(r["Kernel_Name"])
             if key:
                 vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
         return {k: sorted(v)[len(v) // 2] for k, v in vals.items()}  # median dispatch
@@ -80,20 +93,20 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
     rf, rw = COPY_BYTES / f["copy"], COPY_BYTES / w["copy"]
     path = os.path.join(ROOT, "profiles", "traffic.json")
     db = json.load(open(path)) if os.path.exists(path) else {}
-    db[f"k_decode/{workload}"] = {
-        "bytes_per_launch": round(f["k_decode"] * rf + w["k_decode"] * rw),
-        "fetch_bytes_raw": f["k_decode"], "write_bytes_raw": w["k_decode"],
-        "copy_scale_fetch": rf, "copy_scale_write": rw,
-        "sources": DECODE_SOURCES, "source_sha256": sources_sha256(DECODE_SOURCES),
-    }
+    for k in sorted(set(f) & set(w) - {"copy"}):
+        db[f"{k}/{workload}"] = {
+            "bytes_per_launch": round(f[k] * rf + w[k] * rw),
+            "fetch_bytes_raw": f[k], "write_bytes_raw": w[k],
+            "copy_scale_fetch": rf, "copy_scale_write": rw,
+            "sources": KERNEL_SOURCES[k], "source_sha256": sources_sha256(KERNEL_SOURCES[k]),
+        }
+        print(k, json.dumps(db[f"{k}/{workload}"]))
     json.dump(db, open(path, "w"), indent=1, sort_keys=True)
-    print(json.dumps(db[f"k_decode/{workload}"]))
 
 
 def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from committed counter runs, if they were taken on
     the current kernel source (profiles/traffic.json records its hash)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -103,10 +116,8 @@ def traffic_for(kernel: str, workload: str):
         return None
     if not rec:
         return None
-    h = hashlib.sha256()
-    for f in rec.get("sources", []):
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    return rec.get("bytes_per_launch") if h.hexdigest() == rec.get("source_sha256") else None
+    ok = sources_sha256(rec.get("sources", [])) == rec.get("source_sha256")
+    return rec.get("bytes_per_launch") if ok else None
 
 
 def cpu_baseline(cfg, kv_np):
@@ -200,11 +211,25 @@ def main():
     d_avg = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
     in_bytes = cfg.input_bytes
     n_el = cfg.n_elements
+    A = d.alphabet
     payload = int(buf.slab_off[d.n_slabs].item())
-    side = d.cdf_bytes + 2 * (L * 2 * T) + 2 * d.n_streams + 8 * (d.n_slabs + 1)
-    # decode kernel, algorithmic bytes per launch: payload + CDFs + max1 + stream lengths
-    # + slab offsets in, fp16 out
-    dec_bytes = payload + side + 2 * n_el
+    cdf_b, max1_b, len_b, off_b = d.cdf_bytes, 2 * (L * 2 * T), 2 * d.n_streams, 8 * (d.n_slabs + 1)
+    side = cdf_b + max1_b + len_b + off_b
+    # algorithmic bytes per call of each stage (what it must read and write at least)
+    alg = {
+        # fp16 in; symbols, max1 and CDFs out
+        "quantize_cdf": 2 * n_el + n_el + max1_b + cdf_b,
+        # symbols and CDFs in; payload, stream lengths and slab offsets out
+        "encode_pack": n_el + cdf_b + payload + len_b + off_b,
+        # payload, CDFs, max1, stream lengths, slab offsets in; fp16 out
+        "decode_dequant": payload + side + 2 * n_el,
+    }
+    ms = {"quantize_cdf": q_ms, "encode_pack": e_ms, "decode_dequant": d_ms}
+    stages = {k: {"ms": round(ms[k], 4), "algorithmic_bytes": alg[k],
+                  "GBps": round(alg[k] / (ms[k] * 1e-3) / 1e9, 1),
+                  "frac_hbm": round(alg[k] / (ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)} for k in alg}
+    # the decode stage is one launch of k_decode: its duration is the stage's
+    dec_bytes = alg["decode_dequant"]
     achieved = dec_bytes / (d_avg * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -220,12 +245,12 @@ def main():
         "dtype": "f32+u32",
         "data": "synthetic",
         "config": {"workload": cfg.workload, "layers": L, "channels": C, "tokens": T,
-                   "chunk_tokens": Tc, "bins": [list(s) for s in cfg.layer_bins],
+                   "chunk_tokens": Tc, "bins": [list(s) for s in cfg.layer_bins], "alphabet": A,
                    "input": "fp16 [L][2][T][C]", "output": "fp16"},
         "encode_GBps": round(in_bytes / ((q_ms + e_ms) * 1e-3) / 1e9, 3),
         "decode_GBps": round(in_bytes / (d_ms * 1e-3) / 1e9, 3),
-        "stage_ms": {"quantize_cdf": round(q_ms, 4), "encode_pack": round(e_ms, 4),
-                     "decode_dequant": round(d_ms, 4)},
+        "stage_ms": {k: round(v, 4) for k, v in ms.items()},
+        "stages": stages,
         "payload_bits_per_elem": round(8 * payload / n_el, 4),
         "total_bits_per_elem": round(8 * (payload + side) / n_el, 4),
         "roofline": {"kernel": "k_decode", "bound": "hbm", "achieved": round(achieved, 2),
