@@ -19,20 +19,25 @@ namespace {
 
 // One lane per stream, 256 tokens of one slab per block.  The slab is walked
 // in tiles of CT channels: at each tile boundary the block stages the tile's
-// CDF rows as packed (start, frequency) pairs and, when C % 16 == 0, the
-// tile's symbols of its 256 tokens (coalesced 16-byte loads) in LDS.  The
-// coding loop then reads only LDS: 16 symbols per ds_read_b128, pair lookups
-// in batches of 8.  All lanes of a wave read the same pair row at the same
-// step (broadcast or distinct banks); the symbol rows have a 16-byte-padded
-// stride that spreads lanes over all banks.  Without global loads in the
-// loop, the lanes' byte stores never make it wait.
+// CDF rows as packed (start, frequency) pairs in LDS.  When C % 16 == 0 the
+// symbols of the block's 256 tokens are staged too, in tiles of SW = 64
+// channels (coalesced 16-byte loads; SW is a multiple of CT), so each
+// 128-byte line of a token row is fetched in two halves rather than in
+// 32-byte pieces.  The coding loop then reads only LDS: 16 symbols per
+// ds_read_b128, pair lookups in batches of 8.  All lanes of a wave read the
+// same pair row at the same step (broadcast or distinct banks); the symbol
+// rows have a 16-byte-padded stride that spreads lanes over all banks.
+// Without global loads in the loop, the lanes' byte stores never make it
+// wait.
+constexpr int ENC_SW = 64;  // symbol tile width (channels)
+
 template <bool VEC16, int PER>
 __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
                                                 const uint16_t *__restrict__ cdf,
                                                 uint8_t *__restrict__ slots,
                                                 uint16_t *__restrict__ stream_len, KParams p, int CT)
 {
-    // LDS: pairs [CT][A] u32 | symbols [256][CT + 16] u8 (VEC16 only)
+    // LDS: pairs [CT][A] u32 | symbols [256][SW + 16] u8 (VEC16 only)
     extern __shared__ uint32_t lds[];
     const int bps = (p.Tc + 255) / 256;
     const int64_t slab = blockIdx.x / bps;
@@ -45,7 +50,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
     const uint8_t *q = sym + (g.row0 + (active ? t : 0)) * C;
     const uint16_t *rows = cdf + slab * C * A;
     lds_u32 *const pairs = (lds_u32 *)lds;
-    const int sstride = CT + 16;
+    constexpr int sstride = ENC_SW + 16;
     lds_u8 *const stile = (lds_u8 *)(pairs + CT * A);
     const int ntiles = (C + CT - 1) / CT;
 
@@ -53,50 +58,51 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
     SlotOut out{(uint32_t *)(slots + (int64_t)blockIdx.x * p.slot_bytes * 256) + threadIdx.x, 256u};
     EncState e;
     enc_init(e);
-    // A tile's pairs and symbols arrive in registers while the previous tile
-    // is coded, and go into LDS between two barriers.  Symbol pieces: 16 bytes
-    // of a token row; CT <= 64 gives at most 4 per thread.
+    // Tiles arrive in registers while the previous ones are coded, and go
+    // into LDS between two barriers.  Symbol pieces: 16 bytes of a token row,
+    // SW / 16 = 4 per row, so 4 per thread.
     PairTile<PER> pt;
     u32x4 sv[4];
-    const int per_row = CT / 16;
-    auto load_syms = [&](int c0) {
+    constexpr int per_row = ENC_SW / 16;
+    auto load_syms = [&](int s0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int ch = (int)threadIdx.x + 256 * i;
             const int r = ch / per_row, part = ch - r * per_row;
-            const int tok = tb * 256 + r, cc = c0 + part * 16;
-            sv[i] = (ch < 256 * per_row && tok < g.nj && cc < C)
-                        ? *(const u32x4 *)(sym + (g.row0 + tok) * C + cc)
-                        : u32x4{0, 0, 0, 0};
+            const int tok = tb * 256 + r, cc = s0 + part * 16;
+            sv[i] = (tok < g.nj && cc < C) ? *(const u32x4 *)(sym + (g.row0 + tok) * C + cc)
+                                           : u32x4{0, 0, 0, 0};
         }
     };
     auto store_syms = [&]() {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int ch = (int)threadIdx.x + 256 * i;
-            if (ch < 256 * per_row) {
-                const int r = ch / per_row, part = ch - r * per_row;
-                *(lds_u32x4 *)(stile + r * sstride + part * 16) = sv[i];
-            }
+            const int r = ch / per_row, part = ch - r * per_row;
+            *(lds_u32x4 *)(stile + r * sstride + part * 16) = sv[i];
         }
     };
     pt.load(rows, 0, CT, C, A);
     if constexpr (VEC16) load_syms(0);
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
+        const int s0 = c0 - c0 % ENC_SW;  // the symbol tile holding [c0, c1)
+        const bool new_stile = c0 == s0;
         __syncthreads();  // every wave is done with the previous tile
         pt.store(pairs, CT, A);
-        if constexpr (VEC16) store_syms();
+        if constexpr (VEC16) {
+            if (new_stile) store_syms();
+        }
         __syncthreads();
-        if (it + 1 < ntiles) {
-            pt.load(rows, c0 + CT, CT, C, A);
-            if constexpr (VEC16) load_syms(c0 + CT);
+        if (it + 1 < ntiles) pt.load(rows, c0 + CT, CT, C, A);
+        if constexpr (VEC16) {
+            if (new_stile && s0 + ENC_SW < C) load_syms(s0 + ENC_SW);
         }
         if (!active) continue;
         if constexpr (VEC16) {
             const lds_u8 *my = stile + threadIdx.x * sstride;
             for (int cg = c0; cg < c1; cg += 16) {
-                const u32x4 v = *(const lds_u32x4 *)(my + (cg - c0));
+                const u32x4 v = *(const lds_u32x4 *)(my + (cg - s0));
                 const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
                 const lds_u32 *trow = pairs + (cg - c0) * A;
 #pragma unroll
@@ -283,12 +289,14 @@ __global__ void k_zero_u64(uint64_t *dst) { *dst = 0; }
 
 }  // namespace
 
-// Channels per tile: 1024 pairs (4 KB), between 16 and 64 channels (a
-// multiple of 16, so symbol tiles are whole 16-byte pieces).
+// Channels per pair tile: a power of two from 16 to 64, at most 1024 pairs
+// (4 KB) when A allows, so the coding loop's 16-symbol steps and the 64-channel
+// symbol tiles both split into whole tiles.
 static int enc_tile_channels(int A)
 {
-    const int ct = 1024 / A;
-    return ct < 16 ? 16 : (ct > 64 ? 64 : ct);
+    int ct = 16;
+    while (ct < ENC_SW && 2 * ct * A <= 1024) ct *= 2;
+    return ct;
 }
 
 hipError_t launch_zero_u64(uint64_t *dst, hipStream_t stream)
@@ -310,7 +318,7 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
     const int per = (CT * (p.A / 2) + 255) / 256;  // pairs staged per thread
 #define KVC_ENC(V, P, L)                                                                             \
     hipLaunchKernelGGL((k_encode<V, P>), grid, dim3(256), L, stream, sym, cdf, slots, stream_len, p, CT)
-    const size_t lds_syms = lds_pairs + 256 * (size_t)(CT + 16);
+    const size_t lds_syms = lds_pairs + 256 * (size_t)(ENC_SW + 16);
     if (vec16) {
         if (per <= 2) KVC_ENC(true, 2, lds_syms);
         else KVC_ENC(true, 8, lds_syms);

@@ -48,6 +48,9 @@ SMALL = {
     "A4_T257": cfg_of(1, 128, 257, 256, ((0, 1, 4),), seed=8),
     "mistral_L32_C1024_T64": kvgen.CONFIGS["c2"].scaled(n_tokens=64),
     "bins6_odd_MAX": cfg_of(2, 48, 90, 256, ((0, 2, 6),), seed=9),
+    # alphabets whose 1024 / A is not a power of two (encoder tile widths)
+    "A24_C96": cfg_of(1, 96, 80, 256, ((0, 1, 24),), seed=10),
+    "A40_and_A24_C64": cfg_of(2, 64, 120, 256, ((0, 1, 40), (1, 2, 24)), seed=11),
 }
 
 
