@@ -138,7 +138,9 @@ int kvc_quantize(const kvc_desc *desc, const uint16_t *kv, uint8_t *sym, uint16_
         return KVC_ERR_ARG;
     hipStream_t s = (hipStream_t)stream;
     const bool vec8 = (g.p.C % 8 == 0) && aligned(kv, 16) && aligned(sym, 8);
-    if (cdf && vec8 && aligned(cdf, 16) && quant_cdf_fused_ok(g.p))
+    // The fused pass runs one block per slab: with fewer slabs than the chip
+    // has compute units, two passes spread over more blocks finish sooner.
+    if (cdf && vec8 && aligned(cdf, 16) && g.p.n_slabs >= 256 && quant_cdf_fused_ok(g.p))
         return launch_status(launch_quant_cdf(kv, sym, max1, cdf, g.p, dev_status, s));
     hipError_t e = launch_quantize_rows(kv, sym, max1, g.p, dev_status, vec8, s);
     if (e == hipSuccess && cdf) e = launch_cdf(sym, cdf, g.p, s);

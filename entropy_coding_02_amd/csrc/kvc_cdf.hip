@@ -81,14 +81,24 @@ __global__ __launch_bounds__(256) void k_cdf_wide(const uint8_t *__restrict__ sy
     if (cq < C) {
         const uint8_t *col = sym + g.row0 * C + cq;
         const int cl = 4 * lane;
-        for (int t = wid; t < g.nj; t += 4) {
-            const uint32_t v = *(const uint32_t *)(col + (int64_t)t * C);
+        // 8 tokens per step, loaded before any is counted, so 8 loads are in flight
+        for (int t0 = wid; t0 < g.nj; t0 += 32) {
+            uint32_t v[8];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                uint32_t s = (v >> (8 * k)) & 0xFFu;
-                s = s < (uint32_t)A ? s : (uint32_t)(A - 1);
-                const int c = cl + k;
-                atomicAdd(&hist[c * W + (c >> 2) + (int)(s >> 1)], 1u << (16 * (s & 1u)));
+            for (int u = 0; u < 8; ++u) {
+                const int t = t0 + 4 * u;
+                v[u] = t < g.nj ? *(const uint32_t *)(col + (int64_t)t * C) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (t0 + 4 * u >= g.nj) break;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    uint32_t s = (v[u] >> (8 * k)) & 0xFFu;
+                    s = s < (uint32_t)A ? s : (uint32_t)(A - 1);
+                    const int c = cl + k;
+                    atomicAdd(&hist[c * W + (c >> 2) + (int)(s >> 1)], 1u << (16 * (s & 1u)));
+                }
             }
         }
     }

@@ -76,6 +76,16 @@ __device__ __forceinline__ uint32_t kvc_f2h(float f)
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// Two floats to a packed fp16 pair (lo in the low half), each rounded to
+// nearest even: one v_cvt_pk_f16_f32 on gfx950.
+__device__ __forceinline__ uint32_t kvc_f2h2(float lo, float hi)
+{
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+    typedef float float2_t __attribute__((ext_vector_type(2)));
+    const float2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
     for (int off = 32; off > 0; off >>= 1) {

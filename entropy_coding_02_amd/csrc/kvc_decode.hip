@@ -145,6 +145,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
                     const int cg = cb + gi * 8;
                     in.group();
                     uint32_t sw[2] = {0, 0};
+                    float ylo = 0.0f;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         if ((i & 1) == 0) dec_refill(d, in);
@@ -154,9 +155,9 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
                             const float y = lut[s] * m;
                             if constexpr (ODT == ODT_F16) {
                                 if (i & 1)
-                                    hw[gi * 4 + (i >> 1)] |= kvc_f2h(y) << 16;
+                                    hw[gi * 4 + (i >> 1)] = kvc_f2h2(ylo, y);
                                 else
-                                    hw[gi * 4 + (i >> 1)] = kvc_f2h(y);
+                                    ylo = y;
                             } else {
                                 fw[i] = y;
                             }

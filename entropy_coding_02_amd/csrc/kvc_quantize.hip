@@ -123,21 +123,41 @@ __global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__
     __syncthreads();
     const float M = (float)p.maxq[g.lk];
     const uint32_t amax = (uint32_t)A - 1u;
-    for (int t = wid; t < g.nj; t += nw) {
-        const int64_t row = g.row0 + t;
-        const uint16_t *x = kv + row * C;
-        u32x4 reg[KREG];
-        uint32_t mx = 0;
+    // Software pipeline over the wave's rows t = wid, wid + nw, ...: the next
+    // row's pieces are loaded while the current one is processed, and a
+    // row's symbol stores go out after the next row's data has arrived, so
+    // the wait for a load never also waits for stores issued just before it.
+    auto load_row = [&](int t, u32x4 *r) {
+        const uint16_t *x = kv + (g.row0 + t) * C;
 #pragma unroll
         for (int k = 0; k < KREG; ++k) {
             const int pi = lane + 64 * k;
-            reg[k] = pi < C8 ? *(const u32x4 *)(x + 8 * pi) : u32x4{0, 0, 0, 0};
+            r[k] = pi < C8 ? *(const u32x4 *)(x + 8 * pi) : u32x4{0, 0, 0, 0};
+        }
+    };
+    u32x4 cur[KREG], nxt[KREG];
+    uint32_t qb[KREG][2];  // the previous row's symbols, not yet stored
+    int64_t qrow = -1;
+    auto store_row = [&]() {
+#pragma unroll
+        for (int k = 0; k < KREG; ++k) {
+            const int pi = lane + 64 * k;
+            if (pi < C8) *(uint2 *)(sym + qrow * C + 8 * pi) = make_uint2(qb[k][0], qb[k][1]);
+        }
+    };
+    if (wid < g.nj) load_row(wid, cur);
+    for (int t = wid; t < g.nj; t += nw) {
+        const int64_t row = g.row0 + t;
+        uint32_t mx = 0;
+#pragma unroll
+        for (int k = 0; k < KREG; ++k)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t a = reg[k][i] & 0x7FFF7FFFu;
+                const uint32_t a = cur[k][i] & 0x7FFF7FFFu;
                 mx = max(mx, max(a & 0xFFFFu, a >> 16));
             }
-        }
+        if (qrow >= 0) store_row();
+        if (t + nw < g.nj) load_row(t + nw, nxt);
         mx = wave_max_u32(mx);
         const float m = kvc_h2f(mx);
         const float factor = (mx != 0) ? M / m : 0.0f;
@@ -146,19 +166,22 @@ __global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__
 #pragma unroll
         for (int k = 0; k < KREG; ++k) {
             const int pi = lane + 64 * k;
+            qb[k][0] = qb[k][1] = 0;
             if (pi >= C8) continue;
-            uint32_t b[2] = {0, 0};
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t h = (reg[k][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                const uint32_t h = (cur[k][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
                 const uint32_t q = quant1(h, factor, M);
-                b[i >> 2] |= q << (8 * (i & 3));
+                qb[k][i >> 2] |= q << (8 * (i & 3));
                 const uint32_t s = q < amax ? q : amax;  // only non-finite rows exceed A - 1
                 atomicAdd(&hist[(int)(s >> 1) * C + i * C8 + pi], 1u << (16u * (s & 1u)));
             }
-            *(uint2 *)(sym + row * C + 8 * pi) = make_uint2(b[0], b[1]);
         }
+        qrow = row;
+#pragma unroll
+        for (int k = 0; k < KREG; ++k) cur[k] = nxt[k];
     }
+    if (qrow >= 0) store_row();
     __syncthreads();
     const uint32_t K = 65536u - (uint32_t)A;
     for (int c = threadIdx.x; c < C; c += blockDim.x) {

@@ -51,6 +51,10 @@ SMALL = {
     # alphabets whose 1024 / A is not a power of two (encoder tile widths)
     "A24_C96": cfg_of(1, 96, 80, 256, ((0, 1, 24),), seed=10),
     "A40_and_A24_C64": cfg_of(2, 64, 120, 256, ((0, 1, 40), (1, 2, 24)), seed=11),
+    # 256 slabs or more: the fused quantize + CDF pass (ragged last chunk)
+    "fused_L2_C64_T16421_Tc128": cfg_of(2, 64, 16421, 128, ((0, 1, 32), (1, 2, 16)), seed=12),
+    # fused pass at A = 64: a 128 KB LDS histogram
+    "fused_70b_shape_T300": kvgen.CONFIGS["c5"].scaled(n_tokens=300),
 }
 
 
