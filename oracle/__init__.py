@@ -14,6 +14,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvc_oracle.c")
+_SRCS = [_SRC, os.path.join(_HERE, "kvc_container.c")]
 _LIB_PATH = os.path.join(_HERE, "liborc.so")
 
 ORC_OK, ORC_ERR_ARG, ORC_ERR_NONFINITE, ORC_ERR_CAPACITY, ORC_ERR_CORRUPT = 0, -1, -2, -3, -4
@@ -24,11 +25,11 @@ _lib = None
 def build(force: bool = False) -> str:
     """Compile liborc.so: gcc, -O2, no FP contraction, no fast-math."""
     hdr = os.path.join(_HERE, "kvc_oracle.h")
-    newest = max(os.path.getmtime(_SRC), os.path.getmtime(hdr))
+    newest = max([os.path.getmtime(f) for f in _SRCS] + [os.path.getmtime(hdr)])
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
         tmp = _LIB_PATH + f".tmp{os.getpid()}"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-                               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+                               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, *_SRCS, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -58,6 +59,14 @@ def _load():
         lib.orc_decode.argtypes = [I32, I32, I64, I32, I32, P, P, P, P, P]
         lib.orc_dequantize.restype = ctypes.c_int
         lib.orc_dequantize.argtypes = [I32, I32, I64, P, P, P, P, I32]
+        lib.orc_container_bytes.restype = I64
+        lib.orc_container_bytes.argtypes = [I32, I32, I64, I32, P, I64]
+        lib.orc_container_payload_offset.restype = I64
+        lib.orc_container_payload_offset.argtypes = [I32, I32, I64, I32, P]
+        lib.orc_serialize.restype = I64
+        lib.orc_serialize.argtypes = [I32, I32, I64, I32, P, P, P, P, P, I64, P, I64]
+        lib.orc_deserialize.restype = ctypes.c_int
+        lib.orc_deserialize.argtypes = [I32, I32, I64, I32, P, P, I64, P, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -187,6 +196,60 @@ def dequantize(sym: np.ndarray, max1: np.ndarray, bins: np.ndarray, fp32: bool =
     if rc != ORC_OK:
         raise OracleError("orc_dequantize", rc)
     return out
+
+
+def _bins32(bins) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(bins, dtype=np.int32).reshape(-1))
+
+
+def container_bytes(L: int, C: int, T: int, Tc: int, bins, payload_bytes: int) -> int:
+    n = _load().orc_container_bytes(L, C, T, Tc, _ptr(_bins32(bins)), payload_bytes)
+    if n < 0:
+        raise OracleError("orc_container_bytes", n)
+    return int(n)
+
+
+def container_payload_offset(L: int, C: int, T: int, Tc: int, bins) -> int:
+    n = _load().orc_container_payload_offset(L, C, T, Tc, _ptr(_bins32(bins)))
+    if n < 0:
+        raise OracleError("orc_container_payload_offset", n)
+    return int(n)
+
+
+def serialize(cdf_tab: np.ndarray, max1: np.ndarray, stream_len: np.ndarray, payload: np.ndarray,
+              bins, Tc: int) -> np.ndarray:
+    """-> the container bytes (u8)."""
+    L, _, T = max1.shape
+    C = cdf_tab.shape[3]
+    pb = int(payload.size)
+    n = container_bytes(L, C, T, Tc, bins, pb)
+    out = np.empty(n, dtype=np.uint8)
+    pay = np.ascontiguousarray(payload, dtype=np.uint8) if pb else np.zeros(1, np.uint8)
+    rc = _load().orc_serialize(L, C, T, Tc, _ptr(_bins32(bins)), _ptr(np.ascontiguousarray(cdf_tab)),
+                               _ptr(np.ascontiguousarray(max1)), _ptr(np.ascontiguousarray(stream_len)),
+                               _ptr(pay), pb, _ptr(out), n)
+    if rc < 0:
+        raise OracleError("orc_serialize", rc)
+    return out
+
+
+def deserialize(data: np.ndarray, L: int, C: int, T: int, Tc: int, bins):
+    """-> dict(cdf, max1, stream_len, slab_off, payload_bytes, payload_offset)."""
+    A = int(np.max(bins))
+    NC = n_chunks(T, Tc)
+    cdf_tab = np.empty((NC, L, 2, C, A), dtype=np.uint16)
+    max1 = np.empty((L, 2, T), dtype=np.uint16)
+    stream_len = np.empty(2 * L * T, dtype=np.uint16)
+    slab_off = np.empty(NC * L * 2 + 1, dtype=np.uint64)
+    pb = ctypes.c_int64(0)
+    data = np.ascontiguousarray(data, dtype=np.uint8)
+    rc = _load().orc_deserialize(L, C, T, Tc, _ptr(_bins32(bins)), _ptr(data), data.size,
+                                 _ptr(cdf_tab), _ptr(max1), _ptr(stream_len), _ptr(slab_off),
+                                 ctypes.addressof(pb))
+    if rc != ORC_OK:
+        raise OracleError("orc_deserialize", rc)
+    return dict(cdf=cdf_tab, max1=max1, stream_len=stream_len, slab_off=slab_off,
+                payload_bytes=int(pb.value), payload_offset=container_payload_offset(L, C, T, Tc, bins))
 
 
 def codec(kv: np.ndarray, bins: np.ndarray, Tc: int):

@@ -52,6 +52,18 @@ int orc_decode(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t A, const uin
 int orc_dequantize(int32_t L, int32_t C, int64_t T, const int32_t *bins, const uint8_t *sym,
                    const uint16_t *max1, void *out, int32_t out_fp32);
 
+/* Byte container with compact CDF tables (kvc_container.c). */
+int64_t orc_container_bytes(int32_t L, int32_t C, int64_t T, int32_t Tc, const int32_t *bins,
+                            int64_t payload_bytes);
+int64_t orc_container_payload_offset(int32_t L, int32_t C, int64_t T, int32_t Tc,
+                                     const int32_t *bins);
+int64_t orc_serialize(int32_t L, int32_t C, int64_t T, int32_t Tc, const int32_t *bins,
+                      const uint16_t *cdf, const uint16_t *max1, const uint16_t *stream_len,
+                      const uint8_t *payload, int64_t payload_bytes, uint8_t *out, int64_t out_cap);
+int orc_deserialize(int32_t L, int32_t C, int64_t T, int32_t Tc, const int32_t *bins,
+                    const uint8_t *in, int64_t in_bytes, uint16_t *cdf, uint16_t *max1,
+                    uint16_t *stream_len, uint64_t *slab_off, int64_t *payload_bytes);
+
 #ifdef __cplusplus
 }
 #endif
