@@ -19,12 +19,14 @@ LIB_PATH = os.path.join(_PKG, "libkvc.so")
 
 KVC_OK, KVC_ERR_ARG, KVC_ERR_CAPACITY, KVC_ERR_HIP = 0, -1, -2, -3
 KVC_DEV_NONFINITE, KVC_DEV_CORRUPT, KVC_DEV_PAYLOAD_OVERFLOW = 1, 2, 4
+KVC_DEV_BAD_CDF, KVC_DEV_BAD_CONTAINER = 8, 16
 KVC_F16, KVC_F32 = 0, 1
 
 EXPORTED = (
     "kvc_version", "kvc_status_string", "kvc_alphabet", "kvc_n_chunks", "kvc_n_slabs",
     "kvc_n_streams", "kvc_cdf_bytes", "kvc_scratch_bytes", "kvc_max_payload_bytes",
     "kvc_quantize", "kvc_cdf", "kvc_encode", "kvc_decode", "kvc_dequantize",
+    "kvc_container_bytes", "kvc_container_payload_offset", "kvc_serialize", "kvc_deserialize",
 )
 
 
@@ -78,6 +80,14 @@ def _load():
         lib.kvc_decode.argtypes = [D, P, I64, P, P, P, P, P, P, I32, P, P]
         lib.kvc_dequantize.restype = ctypes.c_int
         lib.kvc_dequantize.argtypes = [D, P, P, P, I32, P]
+        lib.kvc_container_bytes.restype = I64
+        lib.kvc_container_bytes.argtypes = [D, I64]
+        lib.kvc_container_payload_offset.restype = I64
+        lib.kvc_container_payload_offset.argtypes = [D]
+        lib.kvc_serialize.restype = ctypes.c_int
+        lib.kvc_serialize.argtypes = [D, P, P, P, P, P, P, I64, P, P]
+        lib.kvc_deserialize.restype = ctypes.c_int
+        lib.kvc_deserialize.argtypes = [D, P, I64, P, P, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -121,6 +131,14 @@ class Desc:
     def scratch_bytes(self): return self._q("kvc_scratch_bytes")
     @property
     def max_payload_bytes(self): return self._q("kvc_max_payload_bytes")
+    @property
+    def container_payload_offset(self): return self._q("kvc_container_payload_offset")
+
+    def container_bytes(self, payload_bytes: int) -> int:
+        v = _load().kvc_container_bytes(self.ref, payload_bytes)
+        if v < 0:
+            raise KvcError("kvc_container_bytes", int(v))
+        return int(v)
 
 
 def _ptr(t) -> Optional[int]:
@@ -184,6 +202,22 @@ def kvc_decode(desc: Desc, payload, slab_off, stream_len, cdf, max1=None, sym_ou
 def kvc_dequantize(desc: Desc, sym, max1, out, out_dtype=KVC_F16, stream=None):
     _check("kvc_dequantize", _load().kvc_dequantize(desc.ref, _ptr(sym), _ptr(max1), _ptr(out),
                                                     out_dtype, _stream(stream)))
+
+
+def kvc_serialize(desc: Desc, cdf, max1, stream_len, slab_off, payload, out, dev_status=None,
+                  stream=None, out_cap=None):
+    oc = out.numel() * out.element_size() if out_cap is None else out_cap
+    _check("kvc_serialize", _load().kvc_serialize(desc.ref, _ptr(cdf), _ptr(max1), _ptr(stream_len),
+                                                  _ptr(slab_off), _ptr(payload), _ptr(out), oc,
+                                                  _ptr(dev_status), _stream(stream)))
+
+
+def kvc_deserialize(desc: Desc, inp, cdf, max1, stream_len, slab_off, dev_status=None, stream=None,
+                    in_bytes=None):
+    nb = inp.numel() * inp.element_size() if in_bytes is None else in_bytes
+    _check("kvc_deserialize", _load().kvc_deserialize(desc.ref, _ptr(inp), nb, _ptr(cdf), _ptr(max1),
+                                                      _ptr(stream_len), _ptr(slab_off),
+                                                      _ptr(dev_status), _stream(stream)))
 
 
 # --------------------------------------------------------------- convenience

@@ -214,4 +214,58 @@ int kvc_dequantize(const kvc_desc *desc, const uint8_t *sym, const uint16_t *max
         launch_dequantize(sym, max1, out, out_dtype, g.p, false, (hipStream_t)stream));
 }
 
+int64_t kvc_container_bytes(const kvc_desc *desc, int64_t payload_bytes)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    if (payload_bytes < 0) return KVC_ERR_ARG;
+    return container_total(container_layout(g.p), payload_bytes);
+}
+
+int64_t kvc_container_payload_offset(const kvc_desc *desc)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    return rc == KVC_OK ? container_layout(g.p).pay : rc;
+}
+
+int kvc_serialize(const kvc_desc *desc, const uint16_t *cdf, const uint16_t *max1,
+                  const uint16_t *stream_len, const uint64_t *slab_off, const uint8_t *payload,
+                  uint8_t *out, int64_t out_cap, int32_t *dev_status, void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    const ContainerLayout cl = container_layout(g.p);
+    const bool empty = g.p.n_rows == 0;
+    if (!out || !aligned(out, 16) || !slab_off || !aligned(slab_off, 8) ||
+        (dev_status && !aligned(dev_status, 4)) ||
+        (!empty && (!cdf || !max1 || !stream_len || !payload || !aligned(cdf, 4) ||
+                    !aligned(max1, 4) || !aligned(stream_len, 4) || !aligned(payload, 4))))
+        return KVC_ERR_ARG;
+    if (out_cap < container_total(cl, 0)) return KVC_ERR_CAPACITY;
+    return launch_status(launch_serialize(cdf, max1, stream_len, slab_off, payload, out, out_cap,
+                                          g.p, dev_status, (hipStream_t)stream));
+}
+
+int kvc_deserialize(const kvc_desc *desc, const uint8_t *in, int64_t in_bytes, uint16_t *cdf,
+                    uint16_t *max1, uint16_t *stream_len, uint64_t *slab_off, int32_t *dev_status,
+                    void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    const ContainerLayout cl = container_layout(g.p);
+    const bool empty = g.p.n_rows == 0;
+    if (!in || !aligned(in, 16) || !slab_off || !aligned(slab_off, 8) ||
+        (dev_status && !aligned(dev_status, 4)) ||
+        (!empty && (!cdf || !max1 || !stream_len || !aligned(cdf, 4) || !aligned(max1, 4) ||
+                    !aligned(stream_len, 4))))
+        return KVC_ERR_ARG;
+    if (in_bytes < container_total(cl, 0)) return KVC_ERR_CAPACITY;
+    return launch_status(launch_deserialize(in, in_bytes, cdf, max1, stream_len, slab_off, g.p,
+                                            dev_status, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -1,0 +1,240 @@
+// kvc_container.hip - the codec's output as one byte buffer, for storage or
+// the network (the serializer entry of [CG] 2.1; to_bytes of a KV tensor in
+// [CG] 3.2), with each CDF row cut to its own layer's alphabet.
+//
+// Format, version 1 (little-endian; every section starts at a multiple of 16
+// bytes; padding bytes are zero):
+//   header   64 bytes: u32 magic 0x3143564B ("KVC1"), u32 version 1, u32 L,
+//            u32 C, u64 T, u32 Tc, u32 A, u64 payload_bytes, u64 total_bytes,
+//            16 zero bytes
+//   bins     u8 [L][2]
+//   cdf      per slab (chunk, layer, K|V) in slab order, per channel: entries
+//            1 .. b-2 of the row as u16 (b = the slab's bins).  Entry 0 is 0
+//            and, since a quantizer with b bins emits symbols up to b-2 only,
+//            entry k >= b-1 is k + 65536 - A: both are implied.
+//   max1     u16 [L][2][T]
+//   lengths  u16 [n_streams]
+//   payload  payload_bytes bytes, the section at least 16 bytes long
+// The payload section is what kvc_decode reads: whole 16-byte pieces, never
+// past the section's end.
+#include "kvc_common.h"
+#include "kvc_kernels.h"
+
+namespace {
+
+constexpr uint32_t KVC_MAGIC = 0x3143564Bu;
+
+__host__ __device__ inline int64_t r16(int64_t x) { return (x + 15) / 16 * 16; }
+
+// compact CDF entries of the (layer, K|V) pairs before lk, per channel
+__device__ inline int64_t lk_prefix(const KParams &p, int lk)
+{
+    int64_t n = 0;
+    for (int i = 0; i < lk; ++i) n += 2 * (int64_t)p.maxq[i];  // bins - 2 = 2 * MAX
+    return n;
+}
+
+// Header, bins and the padding after them.  One block of 64 threads.
+__global__ void k_ser_header(const uint64_t *__restrict__ slab_off, uint8_t *__restrict__ out,
+                             int64_t out_cap, KParams p, ContainerLayout cl, int32_t *status)
+{
+    const uint64_t pb = slab_off[p.n_slabs];
+    const int64_t total = container_total(cl, (int64_t)pb);
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        uint32_t *h = (uint32_t *)out;
+        h[0] = KVC_MAGIC;
+        h[1] = 1;
+        h[2] = (uint32_t)p.L;
+        h[3] = (uint32_t)p.C;
+        *(uint64_t *)(out + 16) = (uint64_t)p.T;
+        h[6] = (uint32_t)p.Tc;
+        h[7] = (uint32_t)p.A;
+        *(uint64_t *)(out + 32) = pb;
+        *(uint64_t *)(out + 40) = (uint64_t)total;
+        if (total > out_cap) kvc_flag(status, KVC_DEV_PAYLOAD_OVERFLOW);
+    }
+    if (tid >= 12 && tid < 16) ((uint32_t *)out)[tid] = 0;
+    for (int64_t i = cl.bins + tid; i < cl.cdf; i += blockDim.x) {
+        const int64_t lk = i - cl.bins;
+        out[i] = lk < 2 * p.L ? (uint8_t)(2 * (p.maxq[lk] + 1)) : 0;
+    }
+}
+
+// The compact CDF section: one block per slab.  Threads walk the slab's
+// compact entries (coalesced u16 stores) and check its implied ones.
+__global__ __launch_bounds__(256) void k_ser_cdf(const uint16_t *__restrict__ cdf,
+                                                 uint8_t *__restrict__ out, KParams p,
+                                                 ContainerLayout cl, int32_t *status)
+{
+    const int64_t slab = blockIdx.x;
+    const int64_t twoL = 2 * (int64_t)p.L;
+    const int64_t j = slab / twoL;
+    const int lk = (int)(slab - j * twoL);
+    const int C = p.C, A = p.A, w = 2 * p.maxq[lk];  // w = b - 2 stored entries per row
+    const uint32_t K = 65536u - (uint32_t)A;
+    const uint16_t *rows = cdf + slab * C * A;
+    uint16_t *dst = (uint16_t *)(out + cl.cdf) + j * cl.chunk_entries + (int64_t)C * lk_prefix(p, lk);
+    const int64_t n = (int64_t)C * w;
+    for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+        const int64_t c = e / w;
+        dst[e] = rows[c * A + 1 + (e - c * w)];
+    }
+    const int imp = A - w;  // entry 0 and entries w + 1 .. A - 1
+    bool bad = false;
+    for (int64_t e = threadIdx.x; e < (int64_t)C * imp; e += blockDim.x) {
+        const int64_t c = e / imp;
+        const int i = (int)(e - c * imp);
+        const int k = i == 0 ? 0 : w + i;
+        const uint32_t want = k == 0 ? 0u : (uint32_t)k + K;
+        bad |= rows[c * A + k] != want;
+    }
+    if (bad) kvc_flag(status, KVC_DEV_BAD_CDF);
+    // zero padding after the last slab's rows
+    if (slab == p.n_slabs - 1 && threadIdx.x == 0) {
+        const int64_t end = cl.cdf + 2 * (int64_t)p.NC * cl.chunk_entries;
+        for (int64_t i = end; i < cl.max1; ++i) out[i] = 0;
+    }
+}
+
+// Copy n bytes (n = *n_dev when given, else n_host) from a 4-byte aligned
+// src to the 16-byte aligned section dst, then zero the section up to
+// r16(max(n, min_len)); nothing at or past dst + cap is written.
+__global__ __launch_bounds__(256) void k_copy_section(const uint8_t *__restrict__ src,
+                                                      uint8_t *__restrict__ dst, int64_t n_host,
+                                                      const uint64_t *n_dev, int64_t min_len,
+                                                      int64_t cap)
+{
+    const int64_t n = n_dev ? (int64_t)*n_dev : n_host;
+    const int64_t end = r16(n > min_len ? n : min_len);
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 4 * w < end; w += step) {
+        const int64_t b = 4 * w;
+        uint32_t v;
+        if (b + 4 <= n) {
+            v = ((const uint32_t *)src)[w];
+        } else {
+            v = 0;
+            for (int i = 0; i < 4; ++i)
+                if (b + i < n) v |= (uint32_t)src[b + i] << (8 * i);
+        }
+        if (b + 4 <= cap) {
+            ((uint32_t *)dst)[w] = v;
+        } else {
+            for (int i = 0; i < 4; ++i)
+                if (b + i < cap) dst[b + i] = (uint8_t)(v >> (8 * i));
+        }
+    }
+}
+
+// Check the header and bins against the descriptor.  One block of 64 threads.
+__global__ void k_deser_check(const uint8_t *__restrict__ in, int64_t in_bytes, KParams p,
+                              ContainerLayout cl, int32_t *status)
+{
+    bool bad = false;
+    if (threadIdx.x == 0) {
+        const uint32_t *h = (const uint32_t *)in;
+        const uint64_t pb = *(const uint64_t *)(in + 32);
+        const uint64_t total = *(const uint64_t *)(in + 40);
+        bad = h[0] != KVC_MAGIC || h[1] != 1 || h[2] != (uint32_t)p.L || h[3] != (uint32_t)p.C ||
+              *(const uint64_t *)(in + 16) != (uint64_t)p.T || h[6] != (uint32_t)p.Tc ||
+              h[7] != (uint32_t)p.A || pb > (uint64_t)in_bytes ||
+              total != (uint64_t)container_total(cl, (int64_t)pb) || total > (uint64_t)in_bytes;
+    }
+    for (int i = threadIdx.x; i < 2 * p.L; i += blockDim.x)
+        bad |= in[cl.bins + i] != (uint8_t)(2 * (p.maxq[i] + 1));
+    if (bad) kvc_flag(status, KVC_DEV_BAD_CONTAINER);
+}
+
+// The full [NC][L][2][C][A] table from the compact rows: one block per slab,
+// a thread per table entry (coalesced u16 stores).
+__global__ __launch_bounds__(256) void k_deser_cdf(const uint8_t *__restrict__ in,
+                                                   uint16_t *__restrict__ cdf, KParams p,
+                                                   ContainerLayout cl)
+{
+    const int64_t slab = blockIdx.x;
+    const int64_t twoL = 2 * (int64_t)p.L;
+    const int64_t j = slab / twoL;
+    const int lk = (int)(slab - j * twoL);
+    const int C = p.C, A = p.A, w = 2 * p.maxq[lk];
+    const uint32_t K = 65536u - (uint32_t)A;
+    const uint16_t *src = (const uint16_t *)(in + cl.cdf) + j * cl.chunk_entries +
+                          (int64_t)C * lk_prefix(p, lk);
+    uint16_t *rows = cdf + slab * C * A;
+    for (int64_t e = threadIdx.x; e < (int64_t)C * A; e += blockDim.x) {
+        const int64_t c = e / A;
+        const int k = (int)(e - c * A);
+        const uint32_t v = k == 0 ? 0u : (k <= w ? (uint32_t)src[c * w + (k - 1)] : (uint32_t)k + K);
+        rows[e] = (uint16_t)v;
+    }
+}
+
+unsigned grid_for(int64_t items, int64_t per_block)
+{
+    int64_t g = (items + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > 65536) g = 65536;
+    return (unsigned)g;
+}
+
+}  // namespace
+
+ContainerLayout container_layout(const KParams &p)
+{
+    ContainerLayout cl;
+    cl.chunk_entries = 0;
+    for (int i = 0; i < 2 * p.L; ++i) cl.chunk_entries += (int64_t)p.C * 2 * p.maxq[i];
+    cl.bins = 64;
+    cl.cdf = r16(cl.bins + 2 * (int64_t)p.L);
+    cl.max1 = r16(cl.cdf + 2 * (int64_t)p.NC * cl.chunk_entries);
+    cl.len = r16(cl.max1 + 2 * p.n_rows);
+    cl.pay = r16(cl.len + 2 * p.n_streams);
+    return cl;
+}
+
+hipError_t launch_serialize(const uint16_t *cdf, const uint16_t *max1, const uint16_t *stream_len,
+                            const uint64_t *slab_off, const uint8_t *payload, uint8_t *out,
+                            int64_t out_cap, const KParams &p, int32_t *status, hipStream_t stream)
+{
+    const ContainerLayout cl = container_layout(p);
+    hipLaunchKernelGGL(k_ser_header, dim3(1), dim3(64), 0, stream, slab_off, out, out_cap, p, cl,
+                       status);
+    if (p.n_slabs > 0)
+        hipLaunchKernelGGL(k_ser_cdf, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, cdf, out, p,
+                           cl, status);
+    const int64_t rows_b = 2 * p.n_rows, lens_b = 2 * p.n_streams;
+    hipLaunchKernelGGL(k_copy_section, dim3(grid_for(rows_b, 1024)), dim3(256), 0, stream,
+                       (const uint8_t *)max1, out + cl.max1, rows_b, (const uint64_t *)nullptr,
+                       (int64_t)0, cl.len - cl.max1);
+    hipLaunchKernelGGL(k_copy_section, dim3(grid_for(lens_b, 1024)), dim3(256), 0, stream,
+                       (const uint8_t *)stream_len, out + cl.len, lens_b, (const uint64_t *)nullptr,
+                       (int64_t)0, cl.pay - cl.len);
+    // the payload size is known on the device only: size the grid for the capacity
+    hipLaunchKernelGGL(k_copy_section, dim3(grid_for(out_cap - cl.pay, 4096)), dim3(256), 0, stream,
+                       payload, out + cl.pay, (int64_t)0, slab_off + p.n_slabs, (int64_t)16,
+                       out_cap - cl.pay);
+    return hipGetLastError();
+}
+
+hipError_t launch_deserialize(const uint8_t *in, int64_t in_bytes, uint16_t *cdf, uint16_t *max1,
+                              uint16_t *stream_len, uint64_t *slab_off, const KParams &p,
+                              int32_t *status, hipStream_t stream)
+{
+    const ContainerLayout cl = container_layout(p);
+    hipLaunchKernelGGL(k_deser_check, dim3(1), dim3(64), 0, stream, in, in_bytes, p, cl, status);
+    if (p.n_slabs > 0)
+        hipLaunchKernelGGL(k_deser_cdf, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, in, cdf, p,
+                           cl);
+    const int64_t rows_b = 2 * p.n_rows, lens_b = 2 * p.n_streams;
+    if (rows_b > 0) {
+        hipLaunchKernelGGL(k_copy_section, dim3(grid_for(rows_b, 1024)), dim3(256), 0, stream,
+                           in + cl.max1, (uint8_t *)max1, rows_b, (const uint64_t *)nullptr,
+                           (int64_t)0, rows_b);
+        hipLaunchKernelGGL(k_copy_section, dim3(grid_for(lens_b, 1024)), dim3(256), 0, stream,
+                           in + cl.len, (uint8_t *)stream_len, lens_b, (const uint64_t *)nullptr,
+                           (int64_t)0, lens_b);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_slab_offsets(stream_len, slab_off, p, (const uint64_t *)(in + 32), status, stream);
+}

@@ -162,9 +162,13 @@ __device__ uint64_t block_excl_scan_1024(uint64_t v, uint64_t *sh, uint64_t *tot
     return incl - v;
 }
 
-__global__ __launch_bounds__(1024) void k_scan(const uint64_t *__restrict__ slab_total,
-                                               uint64_t *__restrict__ slab_off, int64_t n,
-                                               int64_t payload_cap, int32_t *status)
+// slab_total and slab_off may be the same array (each thread reads its own
+// range before the scan and rewrites it element by element after).  With
+// `expect`, a total different from *expect sets KVC_DEV_BAD_CONTAINER;
+// otherwise a total above payload_cap sets KVC_DEV_PAYLOAD_OVERFLOW.
+__global__ __launch_bounds__(1024) void k_scan(const uint64_t *slab_total, uint64_t *slab_off,
+                                               int64_t n, int64_t payload_cap,
+                                               const uint64_t *expect, int32_t *status)
 {
     __shared__ uint64_t sh[1024];
     const int64_t per = (n + 1023) / 1024;
@@ -174,12 +178,17 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *__restrict__ slab
     uint64_t total;
     uint64_t run = block_excl_scan_1024(local, sh, &total);
     for (int64_t i = b; i < e; ++i) {
+        const uint64_t v = slab_total[i];
         slab_off[i] = run;
-        run += slab_total[i];
+        run += v;
     }
     if (threadIdx.x == 0) {
         slab_off[n] = total;
-        if (total > (uint64_t)payload_cap) kvc_flag(status, KVC_DEV_PAYLOAD_OVERFLOW);
+        if (expect) {
+            if (total != *expect) kvc_flag(status, KVC_DEV_BAD_CONTAINER);
+        } else if (total > (uint64_t)payload_cap) {
+            kvc_flag(status, KVC_DEV_PAYLOAD_OVERFLOW);
+        }
     }
 }
 
@@ -330,8 +339,20 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
     hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
                        slab_total, p);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, slab_total, slab_off, p.n_slabs,
-                       payload_cap, status);
+                       payload_cap, (const uint64_t *)nullptr, status);
     hipLaunchKernelGGL(k_pack, dim3(grid.x * 4), dim3(64), 0, stream, slots, stream_len,
                        slab_off, payload, payload_cap, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_slab_offsets(const uint16_t *stream_len, uint64_t *slab_off, const KParams &p,
+                               const uint64_t *expect, int32_t *status, hipStream_t stream)
+{
+    if (p.n_slabs == 0) return launch_zero_u64(slab_off, stream);
+    // the slab totals go into slab_off itself, then are scanned in place
+    hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
+                       slab_off, p);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, slab_off, slab_off, p.n_slabs,
+                       (int64_t)0, expect, status);
     return hipGetLastError();
 }

@@ -29,3 +29,27 @@ hipError_t launch_dequantize(const uint8_t *sym, const uint16_t *max1, void *out
                              const KParams &p, bool vec, hipStream_t stream);
 
 hipError_t launch_zero_u64(uint64_t *dst, hipStream_t stream);
+
+// slab_off [n_slabs + 1] from the stream lengths (exclusive scan of the slab
+// sums); with `expect`, a total different from *expect sets KVC_DEV_BAD_CONTAINER.
+hipError_t launch_slab_offsets(const uint16_t *stream_len, uint64_t *slab_off, const KParams &p,
+                               const uint64_t *expect, int32_t *status, hipStream_t stream);
+
+// Byte container (kvc_container.hip): section offsets, from the descriptor alone.
+struct ContainerLayout {
+    int64_t bins, cdf, max1, len, pay;  // section offsets
+    int64_t chunk_entries;              // compact CDF entries of one chunk
+};
+ContainerLayout container_layout(const KParams &p);
+// total container bytes: the payload section is padded to at least 16 bytes
+__host__ __device__ inline int64_t container_total(const ContainerLayout &cl, int64_t payload_bytes)
+{
+    const int64_t n = payload_bytes < 16 ? 16 : payload_bytes;
+    return cl.pay + (n + 15) / 16 * 16;
+}
+hipError_t launch_serialize(const uint16_t *cdf, const uint16_t *max1, const uint16_t *stream_len,
+                            const uint64_t *slab_off, const uint8_t *payload, uint8_t *out,
+                            int64_t out_cap, const KParams &p, int32_t *status, hipStream_t stream);
+hipError_t launch_deserialize(const uint8_t *in, int64_t in_bytes, uint16_t *cdf, uint16_t *max1,
+                              uint16_t *stream_len, uint64_t *slab_off, const KParams &p,
+                              int32_t *status, hipStream_t stream);

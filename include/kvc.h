@@ -66,7 +66,9 @@ enum kvc_status {
 /* device-side findings, OR-ed into *dev_status */
 #define KVC_DEV_NONFINITE 1        /* a row max was Inf or NaN (kvc_quantize) */
 #define KVC_DEV_CORRUPT 2          /* a stream left its coding interval (kvc_decode) */
-#define KVC_DEV_PAYLOAD_OVERFLOW 4 /* the packed payload did not fit (kvc_encode) */
+#define KVC_DEV_PAYLOAD_OVERFLOW 4 /* the packed payload did not fit (kvc_encode, kvc_serialize) */
+#define KVC_DEV_BAD_CDF 8          /* a CDF row the container cannot carry (kvc_serialize) */
+#define KVC_DEV_BAD_CONTAINER 16   /* a container that does not match the descriptor (kvc_deserialize) */
 
 enum kvc_dtype { KVC_F16 = 0, KVC_F32 = 1 };
 
@@ -178,6 +180,59 @@ int kvc_decode(const kvc_desc *desc, const uint8_t *payload, int64_t payload_byt
  */
 int kvc_dequantize(const kvc_desc *desc, const uint8_t *sym, const uint16_t *max1, void *out,
                    int32_t out_dtype, void *stream);
+
+/*
+ * Byte container: everything kvc_decode needs, in one buffer for storage or
+ * the network (the serializer of [CG] 2.1; to_bytes of a KV tensor in [CG]
+ * 3.2).  Each CDF row is cut to its own layer's alphabet: entries 1 .. b-2 of
+ * the row are stored (b = bins of its layer and K|V); entry 0 is 0 and every
+ * entry k >= b-1 is k + 65536 - A, because a quantizer with b bins never
+ * emits a symbol above b-2.  Format, version 1 (little-endian, sections at
+ * multiples of 16 bytes, padding zero):
+ *   header   64 bytes: u32 magic 0x3143564B ("KVC1"), u32 version 1, u32 L,
+ *            u32 C, u64 T, u32 Tc, u32 A, u64 payload_bytes, u64 total_bytes,
+ *            16 zero bytes
+ *   bins     u8 [L][2]
+ *   cdf      per slab (chunk, layer, K|V), per channel: entries 1 .. b-2 (u16)
+ *   max1     u16 [L][2][T]
+ *   lengths  u16 [n_streams]
+ *   payload  the streams, the section at least 16 bytes long
+ *
+ * kvc_container_bytes          total size for a payload of payload_bytes bytes
+ * kvc_container_payload_offset offset of the payload section (a multiple of 16)
+ */
+int64_t kvc_container_bytes(const kvc_desc *desc, int64_t payload_bytes);
+int64_t kvc_container_payload_offset(const kvc_desc *desc);
+
+/*
+ * Write the container of an encoded KV cache.
+ *   cdf, max1, stream_len, slab_off, payload   as kvc_encode left them (device, read);
+ *                the payload size is slab_off[n_slabs], read on the device
+ *   out          device, 16-byte aligned, out_cap bytes (written); out_cap below
+ *                kvc_container_bytes(desc, 0) returns KVC_ERR_CAPACITY
+ * A container larger than out_cap sets KVC_DEV_PAYLOAD_OVERFLOW, and nothing is
+ * written at or past out_cap; a CDF row that is not of the form above sets
+ * KVC_DEV_BAD_CDF (its implied entries are then lost).
+ */
+int kvc_serialize(const kvc_desc *desc, const uint16_t *cdf, const uint16_t *max1,
+                  const uint16_t *stream_len, const uint64_t *slab_off, const uint8_t *payload,
+                  uint8_t *out, int64_t out_cap, int32_t *dev_status, void *stream);
+
+/*
+ * Read a container back into the buffers kvc_decode takes.
+ *   in           device, 16-byte aligned, in_bytes bytes (read, never past in_bytes)
+ *   cdf          [NC][L][2][C][A] uint16 (device, written): the full tables
+ *   max1         [L][2][T] (device, written)
+ *   stream_len   [n_streams] (device, written)
+ *   slab_off     [n_slabs + 1] (device, written): recomputed from the lengths
+ * The payload is used in place: kvc_decode(desc, in + kvc_container_payload_offset(desc),
+ * in_bytes - that offset, ...).  A header or bins different from the descriptor,
+ * or lengths that do not add up to the header's payload size, set
+ * KVC_DEV_BAD_CONTAINER.
+ */
+int kvc_deserialize(const kvc_desc *desc, const uint8_t *in, int64_t in_bytes, uint16_t *cdf,
+                    uint16_t *max1, uint16_t *stream_len, uint64_t *slab_off, int32_t *dev_status,
+                    void *stream);
 
 #ifdef __cplusplus
 }

@@ -83,3 +83,32 @@ def test_null_and_misaligned_pointers_rejected(lib):
         assert lib.kvc_decode(d.ref, 64, nb, 64, 64, 64, 64, None, 64, 0, None, None) == kvc.KVC_ERR_ARG
     assert lib.kvc_dequantize(d.ref, 64, 64, 64, 9, None) == kvc.KVC_ERR_ARG
     assert lib.kvc_status_string(kvc.KVC_ERR_CAPACITY) == b"buffer too small"
+
+
+def test_container_sizes_agree_with_the_oracle(lib):
+    import oracle
+    cases = [(c.n_layers, c.n_channels, c.n_tokens, c.chunk_tokens, c.bins()) for c in kvgen.CONFIGS.values()]
+    cases += [(3, 40, 0, 256, np.array([[32, 16], [8, 6], [256, 4]], np.int32)),
+              (1, 7, 70, 32, np.array([[16, 16]], np.int32))]
+    for L, C, T, Tc, bins in cases:
+        d = kvc.Desc(L, C, T, bins, Tc)
+        assert d.container_payload_offset == oracle.container_payload_offset(L, C, T, Tc, bins)
+        assert d.container_payload_offset % 16 == 0
+        for pb in (0, 1, 15, 16, 17, 123457):
+            assert d.container_bytes(pb) == oracle.container_bytes(L, C, T, Tc, bins, pb)
+
+
+def test_container_calls_reject_bad_arguments(lib):
+    d = kvc.Desc(1, 16, 64, [[32, 16]])
+    need = d.container_bytes(0)
+    ok = 1 << 20  # a 16-byte aligned stand-in address; nothing is launched on these paths
+    # null or misaligned container, capacity below the empty container
+    assert lib.kvc_serialize(d.ref, ok, ok, ok, ok, ok, None, need, None, None) == kvc.KVC_ERR_ARG
+    assert lib.kvc_serialize(d.ref, ok, ok, ok, ok, ok, ok + 4, need, None, None) == kvc.KVC_ERR_ARG
+    assert lib.kvc_serialize(d.ref, ok, ok, ok, ok, ok, ok, need - 1, None, None) == kvc.KVC_ERR_CAPACITY
+    assert lib.kvc_serialize(d.ref, None, ok, ok, ok, ok, ok, need, None, None) == kvc.KVC_ERR_ARG
+    assert lib.kvc_deserialize(d.ref, None, need, ok, ok, ok, ok, None, None) == kvc.KVC_ERR_ARG
+    assert lib.kvc_deserialize(d.ref, ok + 8, need, ok, ok, ok, ok, None, None) == kvc.KVC_ERR_ARG
+    assert lib.kvc_deserialize(d.ref, ok, need - 16, ok, ok, ok, ok, None, None) == kvc.KVC_ERR_CAPACITY
+    assert lib.kvc_deserialize(d.ref, ok, need, ok, ok, ok, ok + 4, None, None) == kvc.KVC_ERR_ARG
+    assert lib.kvc_container_bytes(d.ref, -1) == kvc.KVC_ERR_ARG
