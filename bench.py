@@ -120,6 +120,40 @@ def traffic_for(kernel: str, workload: str):
     return rec.get("bytes_per_launch") if ok else None
 
 
+def container_leg(kvc, d, buf, cfg, stream, steps):
+    """The byte container (kvc_serialize / kvc_deserialize) of the last step's
+    output: its size in bits per element and each call's time (HIP events on
+    the launch stream, median of `steps` calls), outside the timed step."""
+    import torch
+    pb = int(buf.slab_off[d.n_slabs].item())
+    n = d.container_bytes(pb)
+    out = torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device="cuda")
+    cdf2 = torch.empty_like(buf.cdf)
+    max2 = torch.empty_like(buf.max1)
+    len2 = torch.empty_like(buf.stream_len)
+    off2 = torch.empty_like(buf.slab_off)
+    ser, des = [], []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        kvc.kvc_serialize(d, buf.cdf, buf.max1, buf.stream_len, buf.slab_off, buf.payload, out,
+                          buf.dev_status, stream, out_cap=n)
+        e[1].record(stream)
+        kvc.kvc_deserialize(d, out, cdf2, max2, len2, off2, buf.dev_status, stream, in_bytes=n)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        ser.append(e[0].elapsed_time(e[1]))
+        des.append(e[1].elapsed_time(e[2]))
+    assert int(buf.dev_status.item()) == 0, "device status flags set by the container calls"
+    assert torch.equal(cdf2, buf.cdf) and torch.equal(off2[: d.n_slabs + 1], buf.slab_off[: d.n_slabs + 1])
+    n_el = cfg.n_elements
+    full = pb + d.cdf_bytes + 2 * (2 * d.n_layers * d.n_tokens) + 2 * d.n_streams
+    return {"bytes": n, "bits_per_elem": round(8 * n / n_el, 4),
+            "bits_per_elem_full_tables": round(8 * full / n_el, 4),
+            "serialize_ms": round(statistics.median(ser), 4),
+            "deserialize_ms": round(statistics.median(des), 4)}
+
+
 def cpu_baseline(cfg, kv_np):
     """The oracle, as it stands, over a bounded sample: whole slabs of the
     workload (all of it when it is small), single-threaded."""
@@ -130,8 +164,8 @@ def cpu_baseline(cfg, kv_np):
     bins = cfg.bins()
     n_tok = min(T, Tc)  # the first chunk of every layer
     sub = np.ascontiguousarray(kv_np[:, :, :n_tok])
-    budget_s, n_el, spent, passes = 10.0, 0, 0.0, 0
-    while spent < budget_s and passes < 8:
+    budget_s, n_el, spent, passes = 12.0, 0, 0.0, 0
+    while spent < budget_s and passes < 64:
         t0 = time.perf_counter()
         r = oracle.codec(sub, bins, Tc)
         spent += time.perf_counter() - t0
@@ -258,6 +292,7 @@ def main():
                      "traffic": traffic_for("k_decode", cfg.workload),
                      "algorithmic_bytes_per_launch": dec_bytes},
     }
+    res["container"] = container_leg(kvc, d, buf, cfg, stream, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, kv_np)
     print(json.dumps(res), flush=True)
