@@ -14,7 +14,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvc_oracle.c")
-_SRCS = [_SRC, os.path.join(_HERE, "kvc_container.c")]
+_SRCS = [_SRC, os.path.join(_HERE, "kvc_container.c"), os.path.join(_HERE, "kvc_int8.c")]
 _LIB_PATH = os.path.join(_HERE, "liborc.so")
 
 ORC_OK, ORC_ERR_ARG, ORC_ERR_NONFINITE, ORC_ERR_CAPACITY, ORC_ERR_CORRUPT = 0, -1, -2, -3, -4
@@ -67,6 +67,10 @@ def _load():
         lib.orc_serialize.argtypes = [I32, I32, I64, I32, P, P, P, P, P, I64, P, I64]
         lib.orc_deserialize.restype = ctypes.c_int
         lib.orc_deserialize.argtypes = [I32, I32, I64, I32, P, P, I64, P, P, P, P, P]
+        lib.orc_int8_quantize.restype = ctypes.c_int
+        lib.orc_int8_quantize.argtypes = [I32, I32, I64, I32, P, P, P, P]
+        lib.orc_int8_dequantize.restype = ctypes.c_int
+        lib.orc_int8_dequantize.argtypes = [I32, I32, I64, I32, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -250,6 +254,31 @@ def deserialize(data: np.ndarray, L: int, C: int, T: int, Tc: int, bins):
         raise OracleError("orc_deserialize", rc)
     return dict(cdf=cdf_tab, max1=max1, stream_len=stream_len, slab_off=slab_off,
                 payload_bytes=int(pb.value), payload_offset=container_payload_offset(L, C, T, Tc, bins))
+
+
+def int8_quantize(kv: np.ndarray, g: int):
+    """-> (q u8 [L][2][T][C], scale f32 [L][2][T][C/g], zero_point u8 [L][2][T][C/g])."""
+    L, _, T, C = kv.shape
+    q = np.empty(kv.shape, dtype=np.uint8)
+    scale = np.empty((L, 2, T, C // g), dtype=np.float32)
+    zp = np.empty((L, 2, T, C // g), dtype=np.uint8)
+    rc = _load().orc_int8_quantize(L, C, T, g, _ptr(np.ascontiguousarray(kv, dtype=np.uint16)),
+                                   _ptr(q), _ptr(scale), _ptr(zp))
+    if rc != ORC_OK:
+        raise OracleError("orc_int8_quantize", rc)
+    return q, scale, zp
+
+
+def int8_dequantize(q: np.ndarray, scale: np.ndarray, zp: np.ndarray, g: int) -> np.ndarray:
+    """-> fp16 bits (u16) [L][2][T][C]."""
+    L, _, T, C = q.shape
+    out = np.empty(q.shape, dtype=np.uint16)
+    rc = _load().orc_int8_dequantize(L, C, T, g, _ptr(np.ascontiguousarray(q)),
+                                     _ptr(np.ascontiguousarray(scale, dtype=np.float32)),
+                                     _ptr(np.ascontiguousarray(zp)), _ptr(out))
+    if rc != ORC_OK:
+        raise OracleError("orc_int8_dequantize", rc)
+    return out
 
 
 def codec(kv: np.ndarray, bins: np.ndarray, Tc: int):

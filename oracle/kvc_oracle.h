@@ -64,6 +64,12 @@ int orc_deserialize(int32_t L, int32_t C, int64_t T, int32_t Tc, const int32_t *
                     const uint8_t *in, int64_t in_bytes, uint16_t *cdf, uint16_t *max1,
                     uint16_t *stream_len, uint64_t *slab_off, int64_t *payload_bytes);
 
+/* 8-bit comparator quantizer, [KVM] 四 (kvc_int8.c): groups of g channels. */
+int orc_int8_quantize(int32_t L, int32_t C, int64_t T, int32_t g, const uint16_t *kv, uint8_t *q,
+                      float *scale, uint8_t *zp);
+int orc_int8_dequantize(int32_t L, int32_t C, int64_t T, int32_t g, const uint8_t *q,
+                        const float *scale, const uint8_t *zp, uint16_t *out);
+
 #ifdef __cplusplus
 }
 #endif
