@@ -154,6 +154,44 @@ def container_leg(kvc, d, buf, cfg, stream, steps):
             "deserialize_ms": round(statistics.median(des), 4)}
 
 
+def int8_leg(kvc, d, kvt, buf, cfg, stream, steps, container_bits):
+    """The 8-bit comparator on the same input: its size next to the codec's
+    container, and both reconstructions' relative RMS error against the fp16
+    input (the codec's from the last step's decode), outside the timed step."""
+    import torch
+    C = cfg.n_channels
+    g = 128 if C % 128 == 0 else C  # head_dim of the workloads' 8 x 128 heads
+    n_el, n_g = cfg.n_elements, cfg.n_elements // g
+    q = torch.empty(n_el, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(n_g, dtype=torch.float32, device="cuda")
+    zp = torch.empty(n_g, dtype=torch.uint8, device="cuda")
+    y8 = torch.empty(n_el, dtype=torch.float16, device="cuda")
+    qt, dt = [], []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        kvc.kvc_int8_quantize(d, g, kvt, q, sc, zp, buf.dev_status, stream)
+        e[1].record(stream)
+        kvc.kvc_int8_dequantize(d, g, q, sc, zp, y8, stream)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        qt.append(e[0].elapsed_time(e[1]))
+        dt.append(e[1].elapsed_time(e[2]))
+    x = kvt.view(torch.float16).reshape(-1).float()
+    rms = float(torch.sqrt(torch.mean(x * x)))
+
+    def rel_rmse(y):
+        dlt = y.reshape(-1)[:n_el].float() - x
+        return float(torch.sqrt(torch.mean(dlt * dlt))) / rms
+
+    bits8 = 8 + 8 * 5 / g  # u8 code per element, fp32 scale and u8 zero point per group
+    return {"group": g, "bits_per_elem": round(bits8, 4),
+            "size_ratio_vs_codec_container": round(bits8 / container_bits, 3),
+            "rel_rmse_int8": round(rel_rmse(y8), 6), "rel_rmse_codec": round(rel_rmse(buf.out), 6),
+            "quantize_ms": round(statistics.median(qt), 4),
+            "dequantize_ms": round(statistics.median(dt), 4)}
+
+
 def cpu_baseline(cfg, kv_np):
     """The oracle, as it stands, over a bounded sample: whole slabs of the
     workload (all of it when it is small), single-threaded."""
@@ -293,6 +331,8 @@ def main():
                      "algorithmic_bytes_per_launch": dec_bytes},
     }
     res["container"] = container_leg(kvc, d, buf, cfg, stream, args.steps)
+    res["int8_comparator"] = int8_leg(kvc, d, kvt, buf, cfg, stream, args.steps,
+                                      res["container"]["bits_per_elem"])
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, kv_np)
     print(json.dumps(res), flush=True)

@@ -27,6 +27,7 @@ EXPORTED = (
     "kvc_n_streams", "kvc_cdf_bytes", "kvc_scratch_bytes", "kvc_max_payload_bytes",
     "kvc_quantize", "kvc_cdf", "kvc_encode", "kvc_decode", "kvc_dequantize",
     "kvc_container_bytes", "kvc_container_payload_offset", "kvc_serialize", "kvc_deserialize",
+    "kvc_int8_quantize", "kvc_int8_dequantize",
 )
 
 
@@ -88,6 +89,10 @@ def _load():
         lib.kvc_serialize.argtypes = [D, P, P, P, P, P, P, I64, P, P]
         lib.kvc_deserialize.restype = ctypes.c_int
         lib.kvc_deserialize.argtypes = [D, P, I64, P, P, P, P, P, P]
+        lib.kvc_int8_quantize.restype = ctypes.c_int
+        lib.kvc_int8_quantize.argtypes = [D, I32, P, P, P, P, P, P]
+        lib.kvc_int8_dequantize.restype = ctypes.c_int
+        lib.kvc_int8_dequantize.argtypes = [D, I32, P, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -218,6 +223,19 @@ def kvc_deserialize(desc: Desc, inp, cdf, max1, stream_len, slab_off, dev_status
     _check("kvc_deserialize", _load().kvc_deserialize(desc.ref, _ptr(inp), nb, _ptr(cdf), _ptr(max1),
                                                       _ptr(stream_len), _ptr(slab_off),
                                                       _ptr(dev_status), _stream(stream)))
+
+
+def kvc_int8_quantize(desc: Desc, group: int, kv, q, scale, zero_point, dev_status=None,
+                      stream=None):
+    _check("kvc_int8_quantize", _load().kvc_int8_quantize(desc.ref, group, _ptr(kv), _ptr(q),
+                                                          _ptr(scale), _ptr(zero_point),
+                                                          _ptr(dev_status), _stream(stream)))
+
+
+def kvc_int8_dequantize(desc: Desc, group: int, q, scale, zero_point, out, stream=None):
+    _check("kvc_int8_dequantize", _load().kvc_int8_dequantize(desc.ref, group, _ptr(q), _ptr(scale),
+                                                              _ptr(zero_point), _ptr(out),
+                                                              _stream(stream)))
 
 
 # --------------------------------------------------------------- convenience

@@ -268,4 +268,34 @@ int kvc_deserialize(const kvc_desc *desc, const uint8_t *in, int64_t in_bytes, u
                                             dev_status, (hipStream_t)stream));
 }
 
+int kvc_int8_quantize(const kvc_desc *desc, int32_t group, const uint16_t *kv, uint8_t *q,
+                      float *scale, uint8_t *zero_point, int32_t *dev_status, void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    if (group < 1 || g.p.C % group != 0) return KVC_ERR_ARG;
+    if (g.p.n_rows == 0) return KVC_OK;
+    if (!kv || !q || !scale || !zero_point || !aligned(kv, 4) || !aligned(q, 4) ||
+        !aligned(scale, 4) || (dev_status && !aligned(dev_status, 4)))
+        return KVC_ERR_ARG;
+    const bool vec = aligned(kv, 16) && aligned(q, 8);
+    return launch_status(launch_int8_quantize(kv, q, scale, zero_point, g.p.n_rows, g.p.C, group, vec,
+                                              dev_status, (hipStream_t)stream));
+}
+
+int kvc_int8_dequantize(const kvc_desc *desc, int32_t group, const uint8_t *q, const float *scale,
+                        const uint8_t *zero_point, uint16_t *out, void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    if (group < 1 || g.p.C % group != 0) return KVC_ERR_ARG;
+    if (g.p.n_rows == 0) return KVC_OK;
+    if (!q || !scale || !zero_point || !out || !aligned(scale, 4) || !aligned(out, 4))
+        return KVC_ERR_ARG;
+    return launch_status(launch_int8_dequantize(q, scale, zero_point, out, g.p.n_rows * g.p.C, group,
+                                                (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -71,8 +71,13 @@ __device__ __forceinline__ float kvc_h2f(uint32_t bits)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
+// fp32 to fp16 bits, rounded to nearest even.  The empty asm keeps f a
+// rounded fp32 value: otherwise the compiler may fold the product feeding it
+// into one mixed-precision FMA that rounds to fp16 once, while every product
+// here is defined as rounded to fp32 first and then to fp16.
 __device__ __forceinline__ uint32_t kvc_f2h(float f)
 {
+    __asm__("" : "+v"(f));
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
@@ -80,6 +85,7 @@ __device__ __forceinline__ uint32_t kvc_f2h(float f)
 // nearest even: one v_cvt_pk_f16_f32 on gfx950.
 __device__ __forceinline__ uint32_t kvc_f2h2(float lo, float hi)
 {
+    __asm__("" : "+v"(lo), "+v"(hi));  // as in kvc_f2h
     typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
     typedef float float2_t __attribute__((ext_vector_type(2)));
     const float2_t v = {lo, hi};

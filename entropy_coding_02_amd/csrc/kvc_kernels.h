@@ -53,3 +53,10 @@ hipError_t launch_serialize(const uint16_t *cdf, const uint16_t *max1, const uin
 hipError_t launch_deserialize(const uint8_t *in, int64_t in_bytes, uint16_t *cdf, uint16_t *max1,
                               uint16_t *stream_len, uint64_t *slab_off, const KParams &p,
                               int32_t *status, hipStream_t stream);
+
+// 8-bit comparator quantizer (kvc_int8.hip).
+hipError_t launch_int8_quantize(const uint16_t *kv, uint8_t *q, float *scale, uint8_t *zp,
+                                int64_t n_rows, int C, int g, bool vec, int32_t *status,
+                                hipStream_t stream);
+hipError_t launch_int8_dequantize(const uint8_t *q, const float *scale, const uint8_t *zp,
+                                  uint16_t *out, int64_t n_el, int g, hipStream_t stream);

@@ -234,6 +234,30 @@ int kvc_deserialize(const kvc_desc *desc, const uint8_t *in, int64_t in_bytes, u
                     uint16_t *max1, uint16_t *stream_len, uint64_t *slab_off, int32_t *dev_status,
                     void *stream);
 
+/*
+ * The 8-bit comparator: the per-channel INT8 KV quantizer of the page
+ * "大模型推理的KV Cache管理：从内存碎片到前缀缓存的优化实战" (KV cache management for LLM
+ * inference), section 四, against which the codec's size and error are
+ * measured (the CacheGen page's 8-bit baseline, [CG] 1.3).  Per group of
+ * `group` contiguous channels of a row (head_dim; it must divide C), in fp32
+ * with every operation rounded on its own and round half to even:
+ *   scale = (max - min) / 255,  zero_point = clamp(round(-min / scale), 0, 255),
+ *   q = clamp(round((x - min) / scale), 0, 255),  y = fp16((q - zero_point) * scale).
+ * A constant group stores q = 0, zero_point = 0 (the printed formula divides 0
+ * by 0 there) and decodes to 0.  desc->bins and chunk_tokens are not used
+ * (but must be valid).
+ *   kv          [L][2][T][C] fp16 (device, read)
+ *   q           [L][2][T][C] uint8 (device, written)
+ *   scale       [L][2][T][C/group] fp32 (device, written)
+ *   zero_point  [L][2][T][C/group] uint8 (device, written)
+ *   out         [L][2][T][C] fp16 (device, written)
+ * Inf or NaN in a group sets KVC_DEV_NONFINITE; that group's outputs are unspecified.
+ */
+int kvc_int8_quantize(const kvc_desc *desc, int32_t group, const uint16_t *kv, uint8_t *q,
+                      float *scale, uint8_t *zero_point, int32_t *dev_status, void *stream);
+int kvc_int8_dequantize(const kvc_desc *desc, int32_t group, const uint8_t *q, const float *scale,
+                        const uint8_t *zero_point, uint16_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
