@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void k_int8_quant_groups(const uint16_t *__res
     }
 }
 
-// y = fp16((q - zero_point) * scale), 8 elements per thread when g % 8 == 0.
+// y = fp16((q - zero_point) * scale), one element per thread.
 __global__ __launch_bounds__(256) void k_int8_dequant(const uint8_t *__restrict__ q,
                                                       const float *__restrict__ scale,
                                                       const uint8_t *__restrict__ zp,
@@ -118,6 +118,32 @@ __global__ __launch_bounds__(256) void k_int8_dequant(const uint8_t *__restrict_
         const int64_t gi = e / g;
         const float d = (float)((int32_t)q[e] - (int32_t)zp[gi]);
         out[e] = (uint16_t)kvc_f2h(d * scale[gi]);
+    }
+}
+
+// The same for g % 8 == 0 and aligned buffers: 8 elements (one group) per
+// thread, an 8-byte load and a 16-byte store.
+__global__ __launch_bounds__(256) void k_int8_dequant8(const uint8_t *__restrict__ q,
+                                                       const float *__restrict__ scale,
+                                                       const uint8_t *__restrict__ zp,
+                                                       uint16_t *__restrict__ out, int64_t n8, int g8)
+{
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n8; e += step) {
+        const int64_t gi = e / g8;
+        const uint2 v = ((const uint2 *)q)[e];
+        const int32_t z = zp[gi];
+        const float s = scale[gi];
+        uint32_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = i < 2 ? v.x : v.y;
+            const int sh = 16 * (i & 1);
+            const float a = (float)((int32_t)((w >> sh) & 0xFFu) - z) * s;
+            const float b = (float)((int32_t)((w >> (sh + 8)) & 0xFFu) - z) * s;
+            h[i] = kvc_f2h2(a, b);
+        }
+        ((uint4 *)out)[e] = make_uint4(h[0], h[1], h[2], h[3]);
     }
 }
 
@@ -159,7 +185,13 @@ hipError_t launch_int8_dequantize(const uint8_t *q, const float *scale, const ui
                                   uint16_t *out, int64_t n_el, int g, hipStream_t stream)
 {
     if (n_el == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_int8_dequant, dim3(grid_cap((n_el + 255) / 256)), dim3(256), 0, stream, q,
-                       scale, zp, out, n_el, g);
+    if (g % 8 == 0 && ((uintptr_t)q & 7) == 0 && ((uintptr_t)out & 15) == 0) {
+        const int64_t n8 = n_el / 8;
+        hipLaunchKernelGGL(k_int8_dequant8, dim3(grid_cap((n8 + 255) / 256)), dim3(256), 0, stream, q,
+                           scale, zp, out, n8, g / 8);
+    } else {
+        hipLaunchKernelGGL(k_int8_dequant, dim3(grid_cap((n_el + 255) / 256)), dim3(256), 0, stream,
+                           q, scale, zp, out, n_el, g);
+    }
     return hipGetLastError();
 }
