@@ -281,6 +281,26 @@ def int8_dequantize(q: np.ndarray, scale: np.ndarray, zp: np.ndarray, g: int) ->
     return out
 
 
+def chunk_of(r: dict, j: int, T: int, Tc: int):
+    """Chunk j of an encoded tensor as a tensor of its own (T = N_j tokens):
+    its CDF slabs, its max1 rows, its stream lengths and its payload bytes,
+    cut out of codec()'s outputs ([CG] 2.3 step 3: chunks stream on their own)."""
+    L = r["max1"].shape[0]
+    nj = chunk_tokens(T, Tc, j)
+    s0, s1 = j * 2 * L, (j + 1) * 2 * L
+    lo, hi = int(r["slab_off"][s0]), int(r["slab_off"][s1])
+    return dict(cdf=np.ascontiguousarray(r["cdf"][j:j + 1]),
+                max1=np.ascontiguousarray(r["max1"][:, :, j * Tc:j * Tc + nj]),
+                stream_len=np.ascontiguousarray(r["stream_len"][j * 2 * L * Tc:j * 2 * L * Tc + 2 * L * nj]),
+                payload=np.ascontiguousarray(r["payload"][lo:hi]), n_tokens=nj)
+
+
+def serialize_chunk(r: dict, j: int, bins, T: int, Tc: int) -> np.ndarray:
+    """The container of chunk j alone (a tensor of N_j tokens)."""
+    c = chunk_of(r, j, T, Tc)
+    return serialize(c["cdf"], c["max1"], c["stream_len"], c["payload"], bins, Tc)
+
+
 def codec(kv: np.ndarray, bins: np.ndarray, Tc: int):
     """The whole hot path on the CPU: dict of every intermediate and output."""
     A = int(np.max(bins))
