@@ -27,7 +27,7 @@ EXPORTED = (
     "kvc_n_streams", "kvc_cdf_bytes", "kvc_scratch_bytes", "kvc_max_payload_bytes",
     "kvc_quantize", "kvc_cdf", "kvc_encode", "kvc_decode", "kvc_dequantize",
     "kvc_container_bytes", "kvc_container_payload_offset", "kvc_serialize", "kvc_deserialize",
-    "kvc_int8_quantize", "kvc_int8_dequantize",
+    "kvc_int8_quantize", "kvc_int8_dequantize", "kvc_serialize_chunk", "kvc_quantize_levels",
 )
 
 
@@ -89,6 +89,10 @@ def _load():
         lib.kvc_serialize.argtypes = [D, P, P, P, P, P, P, I64, P, P]
         lib.kvc_deserialize.restype = ctypes.c_int
         lib.kvc_deserialize.argtypes = [D, P, I64, P, P, P, P, P, P]
+        lib.kvc_quantize_levels.restype = ctypes.c_int
+        lib.kvc_quantize_levels.argtypes = [D, I32, P, P, P, P, P, P]
+        lib.kvc_serialize_chunk.restype = ctypes.c_int
+        lib.kvc_serialize_chunk.argtypes = [D, I64, P, P, P, P, P, P, I64, P, P]
         lib.kvc_int8_quantize.restype = ctypes.c_int
         lib.kvc_int8_quantize.argtypes = [D, I32, P, P, P, P, P, P]
         lib.kvc_int8_dequantize.restype = ctypes.c_int
@@ -183,6 +187,16 @@ def kvc_quantize(desc: Desc, kv, sym, max1, cdf=None, dev_status=None, stream=No
                                                 _ptr(dev_status), _stream(stream)))
 
 
+def kvc_quantize_levels(descs, kv, syms, max1, cdfs, dev_status=None, stream=None):
+    """descs: Desc per level; syms, cdfs: device tensors per level."""
+    n = len(descs)
+    arr = (KvcDesc * n)(*[d.c for d in descs])  # the Desc objects keep their bins alive
+    ps = (ctypes.c_void_p * n)(*[_ptr(t) for t in syms])
+    pc = (ctypes.c_void_p * n)(*[_ptr(t) for t in cdfs])
+    _check("kvc_quantize_levels", _load().kvc_quantize_levels(arr, n, _ptr(kv), ps, _ptr(max1), pc,
+                                                              _ptr(dev_status), _stream(stream)))
+
+
 def kvc_cdf(desc: Desc, sym, cdf, stream=None):
     _check("kvc_cdf", _load().kvc_cdf(desc.ref, _ptr(sym), _ptr(cdf), _stream(stream)))
 
@@ -215,6 +229,15 @@ def kvc_serialize(desc: Desc, cdf, max1, stream_len, slab_off, payload, out, dev
     _check("kvc_serialize", _load().kvc_serialize(desc.ref, _ptr(cdf), _ptr(max1), _ptr(stream_len),
                                                   _ptr(slab_off), _ptr(payload), _ptr(out), oc,
                                                   _ptr(dev_status), _stream(stream)))
+
+
+def kvc_serialize_chunk(desc: Desc, chunk: int, cdf, max1, stream_len, slab_off, payload, out,
+                        dev_status=None, stream=None, out_cap=None):
+    oc = out.numel() * out.element_size() if out_cap is None else out_cap
+    _check("kvc_serialize_chunk", _load().kvc_serialize_chunk(desc.ref, chunk, _ptr(cdf), _ptr(max1),
+                                                              _ptr(stream_len), _ptr(slab_off),
+                                                              _ptr(payload), _ptr(out), oc,
+                                                              _ptr(dev_status), _stream(stream)))
 
 
 def kvc_deserialize(desc: Desc, inp, cdf, max1, stream_len, slab_off, dev_status=None, stream=None,

@@ -147,6 +147,45 @@ int kvc_quantize(const kvc_desc *desc, const uint16_t *kv, uint8_t *sym, uint16_
     return launch_status(e);
 }
 
+int kvc_quantize_levels(const kvc_desc *levels, int32_t n_levels, const uint16_t *kv,
+                        uint8_t *const *sym, uint16_t *max1, uint16_t *const *cdf,
+                        int32_t *dev_status, void *stream)
+{
+    if (!levels || n_levels < 1 || n_levels > KVC_MAX_LEVELS || !sym || !cdf) return KVC_ERR_ARG;
+    Geometry g[KVC_MAX_LEVELS];
+    for (int l = 0; l < n_levels; ++l) {
+        int rc = make_geometry(&levels[l], g[l]);
+        if (rc != KVC_OK) return rc;
+        if (levels[l].n_layers != levels[0].n_layers || levels[l].n_channels != levels[0].n_channels ||
+            levels[l].n_tokens != levels[0].n_tokens ||
+            levels[l].chunk_tokens != levels[0].chunk_tokens)
+            return KVC_ERR_ARG;
+        if (!sym[l] || !cdf[l] || !aligned(sym[l], 4) || !aligned(cdf[l], 4)) return KVC_ERR_ARG;
+    }
+    const KParams &p = g[0].p;
+    if (p.n_rows == 0) return KVC_OK;
+    if (!kv || !max1 || !aligned(kv, 4) || !aligned(max1, 2) || (dev_status && !aligned(dev_status, 4)))
+        return KVC_ERR_ARG;
+    LevelParams lv;
+    memset(&lv, 0, sizeof(lv));
+    lv.n = n_levels;
+    bool fused = p.n_slabs >= 256 && aligned(kv, 16);
+    for (int l = 0; l < n_levels; ++l) {
+        lv.A[l] = g[l].p.A;
+        lv.sym[l] = sym[l];
+        lv.cdf[l] = cdf[l];
+        memcpy(lv.maxq[l], g[l].p.maxq, sizeof(lv.maxq[l]));
+        fused = fused && aligned(sym[l], 8) && aligned(cdf[l], 16);
+    }
+    if (fused && quant_cdf_levels_ok(p, lv))
+        return launch_status(launch_quant_cdf_levels(kv, max1, p, lv, dev_status, (hipStream_t)stream));
+    for (int l = 0; l < n_levels; ++l) {  // level by level (max1 written each time, identically)
+        int rc = kvc_quantize(&levels[l], kv, sym[l], max1, cdf[l], dev_status, stream);
+        if (rc != KVC_OK) return rc;
+    }
+    return KVC_OK;
+}
+
 int kvc_cdf(const kvc_desc *desc, const uint8_t *sym, uint16_t *cdf, void *stream)
 {
     Geometry g;
@@ -247,6 +286,30 @@ int kvc_serialize(const kvc_desc *desc, const uint16_t *cdf, const uint16_t *max
     if (out_cap < container_total(cl, 0)) return KVC_ERR_CAPACITY;
     return launch_status(launch_serialize(cdf, max1, stream_len, slab_off, payload, out, out_cap,
                                           g.p, dev_status, (hipStream_t)stream));
+}
+
+int kvc_serialize_chunk(const kvc_desc *desc, int64_t chunk, const uint16_t *cdf,
+                        const uint16_t *max1, const uint16_t *stream_len, const uint64_t *slab_off,
+                        const uint8_t *payload, uint8_t *out, int64_t out_cap, int32_t *dev_status,
+                        void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    if (chunk < 0 || chunk >= g.p.NC) return KVC_ERR_ARG;
+    kvc_desc cd = *desc;  // chunk `chunk` as a tensor of its own
+    cd.n_tokens = (chunk == g.p.NC - 1) ? g.p.last_nj : g.p.Tc;
+    Geometry gc;
+    rc = make_geometry(&cd, gc);
+    if (rc != KVC_OK) return rc;
+    if (!out || !aligned(out, 16) || !slab_off || !aligned(slab_off, 8) || !cdf || !max1 ||
+        !stream_len || !payload || !aligned(cdf, 4) || !aligned(max1, 4) || !aligned(stream_len, 4) ||
+        (dev_status && !aligned(dev_status, 4)))
+        return KVC_ERR_ARG;
+    if (out_cap < container_total(container_layout(gc.p), 0)) return KVC_ERR_CAPACITY;
+    return launch_status(launch_serialize_chunk(cdf, max1, stream_len, slab_off, payload, out,
+                                                out_cap, g.p, gc.p, chunk, dev_status,
+                                                (hipStream_t)stream));
 }
 
 int kvc_deserialize(const kvc_desc *desc, const uint8_t *in, int64_t in_bytes, uint16_t *cdf,

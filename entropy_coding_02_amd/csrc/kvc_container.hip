@@ -35,10 +35,11 @@ __device__ inline int64_t lk_prefix(const KParams &p, int lk)
 }
 
 // Header, bins and the padding after them.  One block of 64 threads.
-__global__ void k_ser_header(const uint64_t *__restrict__ slab_off, uint8_t *__restrict__ out,
-                             int64_t out_cap, KParams p, ContainerLayout cl, int32_t *status)
+__global__ void k_ser_header(const uint64_t *__restrict__ off0, const uint64_t *__restrict__ off1,
+                             uint8_t *__restrict__ out, int64_t out_cap, KParams p,
+                             ContainerLayout cl, int32_t *status)
 {
-    const uint64_t pb = slab_off[p.n_slabs];
+    const uint64_t pb = *off1 - (off0 ? *off0 : 0u);  // payload bytes
     const int64_t total = container_total(cl, (int64_t)pb);
     const int tid = threadIdx.x;
     if (tid == 0) {
@@ -97,21 +98,26 @@ __global__ __launch_bounds__(256) void k_ser_cdf(const uint16_t *__restrict__ cd
     }
 }
 
-// Copy n bytes (n = *n_dev when given, else n_host) from a 4-byte aligned
-// src to the 16-byte aligned section dst, then zero the section up to
-// r16(max(n, min_len)); nothing at or past dst + cap is written.
+// Copy n bytes from src to the 4-byte aligned dst, then zero up to
+// r16(max(n, min_len)); nothing at or past dst + cap is written.  n is
+// n_host, or *n_end - *n_begin when n_end is given (n_begin may be NULL: 0);
+// with n_begin the source starts at src + *n_begin.  A 4-byte aligned source
+// is copied by dwords, any other byte by byte.
 __global__ __launch_bounds__(256) void k_copy_section(const uint8_t *__restrict__ src,
                                                       uint8_t *__restrict__ dst, int64_t n_host,
-                                                      const uint64_t *n_dev, int64_t min_len,
-                                                      int64_t cap)
+                                                      const uint64_t *n_begin, const uint64_t *n_end,
+                                                      int64_t min_len, int64_t cap)
 {
-    const int64_t n = n_dev ? (int64_t)*n_dev : n_host;
+    const int64_t b0 = n_begin ? (int64_t)*n_begin : 0;
+    const int64_t n = n_end ? (int64_t)*n_end - b0 : n_host;
+    src += b0;
+    const bool dw = ((uintptr_t)src & 3) == 0;
     const int64_t end = r16(n > min_len ? n : min_len);
     const int64_t step = (int64_t)gridDim.x * blockDim.x;
     for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 4 * w < end; w += step) {
         const int64_t b = 4 * w;
         uint32_t v;
-        if (b + 4 <= n) {
+        if (dw && b + 4 <= n) {
             v = ((const uint32_t *)src)[w];
         } else {
             v = 0;
@@ -124,6 +130,25 @@ __global__ __launch_bounds__(256) void k_copy_section(const uint8_t *__restrict_
             for (int i = 0; i < 4; ++i)
                 if (b + i < cap) dst[b + i] = (uint8_t)(v >> (8 * i));
         }
+    }
+}
+
+// The max1 rows of chunk j: rows [lk * T + t0, + nj) of every (layer, K|V) lk,
+// packed into the section at dst (zero padded to 16 bytes).
+__global__ __launch_bounds__(256) void k_gather_max1(const uint16_t *__restrict__ max1,
+                                                     uint16_t *__restrict__ dst, int64_t T,
+                                                     int64_t t0, int64_t nj, int64_t n_lk,
+                                                     int64_t padded)
+{
+    const int64_t n = n_lk * nj;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < padded / 2; i += step) {
+        uint16_t v = 0;
+        if (i < n) {
+            const int64_t lk = i / nj;
+            v = max1[lk * T + t0 + (i - lk * nj)];
+        }
+        dst[i] = v;
     }
 }
 
@@ -197,22 +222,52 @@ hipError_t launch_serialize(const uint16_t *cdf, const uint16_t *max1, const uin
                             int64_t out_cap, const KParams &p, int32_t *status, hipStream_t stream)
 {
     const ContainerLayout cl = container_layout(p);
-    hipLaunchKernelGGL(k_ser_header, dim3(1), dim3(64), 0, stream, slab_off, out, out_cap, p, cl,
-                       status);
+    hipLaunchKernelGGL(k_ser_header, dim3(1), dim3(64), 0, stream, (const uint64_t *)nullptr,
+                       slab_off + p.n_slabs, out, out_cap, p, cl, status);
     if (p.n_slabs > 0)
         hipLaunchKernelGGL(k_ser_cdf, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, cdf, out, p,
                            cl, status);
     const int64_t rows_b = 2 * p.n_rows, lens_b = 2 * p.n_streams;
+    const uint64_t *none = nullptr;
     hipLaunchKernelGGL(k_copy_section, dim3(grid_for(rows_b, 1024)), dim3(256), 0, stream,
-                       (const uint8_t *)max1, out + cl.max1, rows_b, (const uint64_t *)nullptr,
-                       (int64_t)0, cl.len - cl.max1);
+                       (const uint8_t *)max1, out + cl.max1, rows_b, none, none, (int64_t)0,
+                       cl.len - cl.max1);
     hipLaunchKernelGGL(k_copy_section, dim3(grid_for(lens_b, 1024)), dim3(256), 0, stream,
-                       (const uint8_t *)stream_len, out + cl.len, lens_b, (const uint64_t *)nullptr,
-                       (int64_t)0, cl.pay - cl.len);
+                       (const uint8_t *)stream_len, out + cl.len, lens_b, none, none, (int64_t)0,
+                       cl.pay - cl.len);
     // the payload size is known on the device only: size the grid for the capacity
     hipLaunchKernelGGL(k_copy_section, dim3(grid_for(out_cap - cl.pay, 4096)), dim3(256), 0, stream,
-                       payload, out + cl.pay, (int64_t)0, slab_off + p.n_slabs, (int64_t)16,
+                       payload, out + cl.pay, (int64_t)0, none, slab_off + p.n_slabs, (int64_t)16,
                        out_cap - cl.pay);
+    return hipGetLastError();
+}
+
+hipError_t launch_serialize_chunk(const uint16_t *cdf, const uint16_t *max1,
+                                  const uint16_t *stream_len, const uint64_t *slab_off,
+                                  const uint8_t *payload, uint8_t *out, int64_t out_cap,
+                                  const KParams &whole, const KParams &p, int64_t j,
+                                  int32_t *status, hipStream_t stream)
+{
+    // p describes chunk j as a tensor of its own: T = N_j, one chunk, 2L slabs
+    const ContainerLayout cl = container_layout(p);
+    const int64_t twoL = 2 * (int64_t)p.L;
+    const uint64_t *off0 = slab_off + j * twoL, *off1 = slab_off + (j + 1) * twoL;
+    hipLaunchKernelGGL(k_ser_header, dim3(1), dim3(64), 0, stream, off0, off1, out, out_cap, p, cl,
+                       status);
+    if (p.n_slabs > 0)
+        hipLaunchKernelGGL(k_ser_cdf, dim3((unsigned)p.n_slabs), dim3(256), 0, stream,
+                           cdf + j * twoL * p.C * p.A, out, p, cl, status);
+    const int64_t nj = p.T, rows_padded = cl.len - cl.max1;
+    hipLaunchKernelGGL(k_gather_max1, dim3(grid_for(rows_padded / 2, 1024)), dim3(256), 0, stream,
+                       max1, (uint16_t *)(out + cl.max1), whole.T, j * (int64_t)whole.Tc, nj, twoL,
+                       rows_padded);
+    const uint64_t *none = nullptr;
+    const int64_t lens_b = 2 * p.n_streams;
+    hipLaunchKernelGGL(k_copy_section, dim3(grid_for(lens_b, 1024)), dim3(256), 0, stream,
+                       (const uint8_t *)(stream_len + j * twoL * whole.Tc), out + cl.len, lens_b, none,
+                       none, (int64_t)0, cl.pay - cl.len);
+    hipLaunchKernelGGL(k_copy_section, dim3(grid_for(out_cap - cl.pay, 4096)), dim3(256), 0, stream,
+                       payload, out + cl.pay, (int64_t)0, off0, off1, (int64_t)16, out_cap - cl.pay);
     return hipGetLastError();
 }
 
@@ -227,12 +282,11 @@ hipError_t launch_deserialize(const uint8_t *in, int64_t in_bytes, uint16_t *cdf
                            cl);
     const int64_t rows_b = 2 * p.n_rows, lens_b = 2 * p.n_streams;
     if (rows_b > 0) {
+        const uint64_t *none = nullptr;
         hipLaunchKernelGGL(k_copy_section, dim3(grid_for(rows_b, 1024)), dim3(256), 0, stream,
-                           in + cl.max1, (uint8_t *)max1, rows_b, (const uint64_t *)nullptr,
-                           (int64_t)0, rows_b);
+                           in + cl.max1, (uint8_t *)max1, rows_b, none, none, (int64_t)0, rows_b);
         hipLaunchKernelGGL(k_copy_section, dim3(grid_for(lens_b, 1024)), dim3(256), 0, stream,
-                           in + cl.len, (uint8_t *)stream_len, lens_b, (const uint64_t *)nullptr,
-                           (int64_t)0, lens_b);
+                           in + cl.len, (uint8_t *)stream_len, lens_b, none, none, (int64_t)0, lens_b);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -13,6 +13,23 @@ bool quant_cdf_fused_ok(const KParams &p);
 hipError_t launch_quant_cdf(const uint16_t *kv, uint8_t *sym, uint16_t *max1, uint16_t *cdf,
                             const KParams &p, int32_t *status, hipStream_t stream);
 
+// Quality levels (bins tables) of one tensor for the multi-level pass.
+#define KVC_MAX_LEVELS 4
+struct LevelParams {
+    int32_t n;                                       // levels
+    int32_t words;                                   // LDS words of all histograms
+    int32_t A[KVC_MAX_LEVELS];                       // alphabet of each level
+    int32_t hist[KVC_MAX_LEVELS];                    // LDS word offset of each level's histogram
+    uint8_t *sym[KVC_MAX_LEVELS];
+    uint16_t *cdf[KVC_MAX_LEVELS];
+    uint8_t maxq[KVC_MAX_LEVELS][2 * KVC_MAX_LAYERS];  // MAX per (layer, K|V) of each level
+};
+// The shape qualifies: C % 8 == 0, C <= 1024, every A % 8 == 0 and all
+// histograms fit the device's LDS per block.
+bool quant_cdf_levels_ok(const KParams &p, const LevelParams &lv);
+hipError_t launch_quant_cdf_levels(const uint16_t *kv, uint16_t *max1, const KParams &p,
+                                   LevelParams lv, int32_t *status, hipStream_t stream);
+
 hipError_t launch_cdf(const uint8_t *sym, uint16_t *cdf, const KParams &p, hipStream_t stream);
 
 hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots,
@@ -50,6 +67,11 @@ __host__ __device__ inline int64_t container_total(const ContainerLayout &cl, in
 hipError_t launch_serialize(const uint16_t *cdf, const uint16_t *max1, const uint16_t *stream_len,
                             const uint64_t *slab_off, const uint8_t *payload, uint8_t *out,
                             int64_t out_cap, const KParams &p, int32_t *status, hipStream_t stream);
+hipError_t launch_serialize_chunk(const uint16_t *cdf, const uint16_t *max1,
+                                  const uint16_t *stream_len, const uint64_t *slab_off,
+                                  const uint8_t *payload, uint8_t *out, int64_t out_cap,
+                                  const KParams &whole, const KParams &chunk, int64_t j,
+                                  int32_t *status, hipStream_t stream);
 hipError_t launch_deserialize(const uint8_t *in, int64_t in_bytes, uint16_t *cdf, uint16_t *max1,
                               uint16_t *stream_len, uint64_t *slab_off, const KParams &p,
                               int32_t *status, hipStream_t stream);

@@ -204,6 +204,90 @@ __global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__
     }
 }
 
+// Several quality levels (bins tables) of the same tensor in one pass: as
+// k_quant_cdf, but each row, read once, is quantized and counted for every
+// level (level i: its own MAX per (layer, K|V), symbols, histogram at word
+// offset lv.hist[i] of LDS and CDF rows).  The shared row max goes to max1.
+template <int KREG>
+__global__ __launch_bounds__(1024) void k_quant_cdf_levels(const uint16_t *__restrict__ kv,
+                                                           uint16_t *__restrict__ max1, KParams p,
+                                                           LevelParams lv, int32_t *status)
+{
+    extern __shared__ uint32_t hist[];
+    const int64_t slab = blockIdx.x;
+    const SlabGeom g = slab_geom(p, slab);
+    const int C = p.C, C8 = C / 8;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int i = threadIdx.x; i < lv.words; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (int t = wid; t < g.nj; t += nw) {
+        const int64_t row = g.row0 + t;
+        const uint16_t *x = kv + row * C;
+        u32x4 reg[KREG];
+        uint32_t mx = 0;
+#pragma unroll
+        for (int k = 0; k < KREG; ++k) {
+            const int pi = lane + 64 * k;
+            reg[k] = pi < C8 ? *(const u32x4 *)(x + 8 * pi) : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t a = reg[k][i] & 0x7FFF7FFFu;
+                mx = max(mx, max(a & 0xFFFFu, a >> 16));
+            }
+        }
+        mx = wave_max_u32(mx);
+        const float m = kvc_h2f(mx);
+        if (mx >= 0x7C00u && lane == 0) kvc_flag(status, KVC_DEV_NONFINITE);
+        if (lane == 0) max1[row] = (uint16_t)mx;
+#pragma unroll 1
+        for (int l = 0; l < lv.n; ++l) {
+            const float M = (float)lv.maxq[l][g.lk];
+            const float factor = (mx != 0) ? M / m : 0.0f;
+            const uint32_t amax = (uint32_t)lv.A[l] - 1u;
+            uint32_t *h = hist + lv.hist[l];
+#pragma unroll
+            for (int k = 0; k < KREG; ++k) {
+                const int pi = lane + 64 * k;
+                if (pi >= C8) continue;
+                uint32_t b[2] = {0, 0};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t hv = (reg[k][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                    const uint32_t q = quant1(hv, factor, M);
+                    b[i >> 2] |= q << (8 * (i & 3));
+                    const uint32_t s = q < amax ? q : amax;
+                    atomicAdd(&h[(int)(s >> 1) * C + i * C8 + pi], 1u << (16u * (s & 1u)));
+                }
+                *(uint2 *)(lv.sym[l] + row * C + 8 * pi) = make_uint2(b[0], b[1]);
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int l = 0; l < lv.n; ++l) {
+        const int A = lv.A[l];
+        const uint32_t K = 65536u - (uint32_t)A;
+        for (int c = threadIdx.x; c < C; c += blockDim.x) {
+            const uint32_t *h = hist + lv.hist[l] + (c & 7) * C8 + (c >> 3);
+            uint32_t *dst = (uint32_t *)(lv.cdf[l] + (slab * C + c) * A);
+            uint32_t Ck = 0;
+            for (int k = 0; k < A; k += 8) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t cnt = h[(k / 2 + e) * C];
+                    const uint32_t lo = kvc_cdf_entry((uint32_t)(k + 2 * e), Ck, K, g.rn);
+                    Ck += cnt & 0xFFFFu;
+                    const uint32_t hi = kvc_cdf_entry((uint32_t)(k + 2 * e + 1), Ck, K, g.rn);
+                    Ck += cnt >> 16;
+                    w[e] = lo | (hi << 16);
+                }
+                *(u32x4 *)(dst + k / 2) = u32x4{w[0], w[1], w[2], w[3]};
+            }
+        }
+    }
+}
+
 }  // namespace
 
 // Dynamic LDS of the fused pass, or 0 when the shape does not qualify
@@ -238,6 +322,51 @@ hipError_t launch_quant_cdf(const uint16_t *kv, uint8_t *sym, uint16_t *max1, ui
     else
         hipLaunchKernelGGL(k_quant_cdf<2>, dim3((unsigned)p.n_slabs), dim3(1024), lds, stream, kv, sym,
                            max1, cdf, p, status);
+    return hipGetLastError();
+}
+
+// LDS bytes of the multi-level pass (setting lv's histogram offsets), or 0
+// when the shape does not qualify.
+static size_t quant_cdf_levels_lds(const KParams &p, LevelParams &lv)
+{
+    if (p.C % 8 != 0 || p.C > 1024) return 0;
+    lv.words = 0;
+    for (int l = 0; l < lv.n; ++l) {
+        if (lv.A[l] % 8 != 0) return 0;
+        lv.hist[l] = lv.words;
+        lv.words += (lv.A[l] / 2) * p.C;
+    }
+    const size_t lds = sizeof(uint32_t) * (size_t)lv.words;
+    int dev = 0, lim = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return 0;
+    return lds <= (size_t)lim ? lds : 0;
+}
+
+bool quant_cdf_levels_ok(const KParams &p, const LevelParams &lv)
+{
+    LevelParams t = lv;
+    return quant_cdf_levels_lds(p, t) != 0;
+}
+
+hipError_t launch_quant_cdf_levels(const uint16_t *kv, uint16_t *max1, const KParams &p,
+                                   LevelParams lv, int32_t *status, hipStream_t stream)
+{
+    if (p.n_slabs == 0) return hipSuccess;
+    const size_t lds = quant_cdf_levels_lds(p, lv);
+    if (lds == 0) return hipErrorInvalidValue;
+    const void *fn = p.C <= 512 ? (const void *)k_quant_cdf_levels<1> : (const void *)k_quant_cdf_levels<2>;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    if (p.C <= 512)
+        hipLaunchKernelGGL(k_quant_cdf_levels<1>, dim3((unsigned)p.n_slabs), dim3(1024), lds, stream,
+                           kv, max1, p, lv, status);
+    else
+        hipLaunchKernelGGL(k_quant_cdf_levels<2>, dim3((unsigned)p.n_slabs), dim3(1024), lds, stream,
+                           kv, max1, p, lv, status);
     return hipGetLastError();
 }
 

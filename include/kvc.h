@@ -120,6 +120,22 @@ int kvc_quantize(const kvc_desc *desc, const uint16_t *kv, uint8_t *sym, uint16_
                  uint16_t *cdf, int32_t *dev_status, void *stream);
 
 /*
+ * Several quality levels of one tensor: exactly what kvc_quantize(levels[i],
+ * kv, sym[i], max1, cdf[i]) gives for each i, from one pass over kv where the
+ * shape allows (the row max is shared; each level has its own bins table,
+ * symbols and CDFs).  Each level is then encoded with kvc_encode; chunks of
+ * different levels can be sent chunk by chunk (kvc_serialize_chunk), the
+ * bandwidth adaptation that chunking serves ([CG] 2.3 step 3, [CG] 4 point 2).
+ *   levels     HOST array of n_levels descriptors (1 <= n_levels <= 4) with the same
+ *              n_layers, n_channels, n_tokens and chunk_tokens; bins may differ
+ *   sym, cdf   HOST arrays of n_levels device pointers (written), laid out as in kvc_quantize
+ *   max1       [L][2][T] (device, written once for all levels)
+ */
+int kvc_quantize_levels(const kvc_desc *levels, int32_t n_levels, const uint16_t *kv,
+                        uint8_t *const *sym, uint16_t *max1, uint16_t *const *cdf,
+                        int32_t *dev_status, void *stream);
+
+/*
  * Symbol statistics to CDFs, [CG] 2.3 step 2, per 256-token chunk (step 3).
  * For chunk j with N_j tokens, layer, K|V and channel c: n_s = count of
  * symbol s in the chunk's column, C_k = n_0 + .. + n_{k-1}, K = 65536 - A,
@@ -217,6 +233,26 @@ int64_t kvc_container_payload_offset(const kvc_desc *desc);
 int kvc_serialize(const kvc_desc *desc, const uint16_t *cdf, const uint16_t *max1,
                   const uint16_t *stream_len, const uint64_t *slab_off, const uint8_t *payload,
                   uint8_t *out, int64_t out_cap, int32_t *dev_status, void *stream);
+
+/*
+ * The container of one chunk, the streaming unit of [CG] 2.3 step 3 (chunks
+ * let a sender follow bandwidth swings, [CG] 4 point 2): chunk `chunk` of the
+ * encoded tensor `desc` describes, written as a tensor of its own, i.e.
+ * exactly what kvc_serialize writes for the descriptor `desc` with n_tokens
+ * set to the chunk's token count N_j (its header says T = N_j).  A receiver
+ * reads it with kvc_deserialize and kvc_decode under that descriptor and gets
+ * the chunk's rows [L][2][N_j][C].  Encoding one tensor at several bins
+ * tables (kvc_quantize_levels) and sending each chunk at the level the link
+ * allows is the bandwidth adaptation built on it.
+ *   cdf, max1, stream_len, slab_off, payload   of the whole tensor, as kvc_encode left them
+ *   out          device, 16-byte aligned, out_cap bytes (written); as kvc_serialize
+ * The chunk's payload size is read on the device (a difference of two slab
+ * offsets); flags as kvc_serialize.
+ */
+int kvc_serialize_chunk(const kvc_desc *desc, int64_t chunk, const uint16_t *cdf,
+                        const uint16_t *max1, const uint16_t *stream_len, const uint64_t *slab_off,
+                        const uint8_t *payload, uint8_t *out, int64_t out_cap, int32_t *dev_status,
+                        void *stream);
 
 /*
  * Read a container back into the buffers kvc_decode takes.
