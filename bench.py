@@ -192,6 +192,50 @@ def int8_leg(kvc, d, kvt, buf, cfg, stream, steps, container_bits):
             "dequantize_ms": round(statistics.median(dt), 4)}
 
 
+def levels_leg(kvc, cfg, kvt, stream, steps):
+    """Three quality levels of the same input (the workload's bins, then
+    halved twice, at least 4): one kvc_quantize_levels call against one
+    kvc_quantize per level, and each level's container size and relative RMS
+    error after encode, serialize and decode, outside the timed step."""
+    import numpy as np
+    import torch
+    L, C, T, Tc = cfg.n_layers, cfg.n_channels, cfg.n_tokens, cfg.chunk_tokens
+    b0 = cfg.bins()
+    tables = [b0, np.maximum(b0 // 2, 4), np.maximum(b0 // 4, 4)]
+    tables = [t + (t % 2) for t in tables]
+    descs = [kvc.Desc(L, C, T, t, Tc) for t in tables]
+    bufs = [kvc.alloc(d, out_dtype=kvc.KVC_F16) for d in descs]
+    one, sep = [], []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        kvc.kvc_quantize_levels(descs, kvt, [b.sym for b in bufs], bufs[0].max1, [b.cdf for b in bufs],
+                                bufs[0].dev_status, stream)
+        e[1].record(stream)
+        for d, b in zip(descs, bufs):
+            kvc.kvc_quantize(d, kvt, b.sym, b.max1, b.cdf, b.dev_status, stream)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        one.append(e[0].elapsed_time(e[1]))
+        sep.append(e[1].elapsed_time(e[2]))
+    x = kvt.view(torch.float16).reshape(-1).float()
+    rms = float(torch.sqrt(torch.mean(x * x)))
+    out = []
+    for t, d, b in zip(tables, descs, bufs):
+        kvc.kvc_encode(d, b.sym, b.cdf, b.scratch, b.stream_len, b.slab_off, b.payload, b.dev_status,
+                       stream)
+        kvc.decode(b, stream=stream)
+        torch.cuda.synchronize()
+        assert int(b.dev_status.item()) == 0, "device status flags set in the levels leg"
+        n = d.container_bytes(int(b.slab_off[d.n_slabs].item()))
+        dlt = b.out[: cfg.n_elements].float() - x
+        out.append({"bins": sorted({int(v) for v in t.reshape(-1)}, reverse=True),
+                    "container_bits_per_elem": round(8 * n / cfg.n_elements, 4),
+                    "rel_rmse": round(float(torch.sqrt(torch.mean(dlt * dlt))) / rms, 6)})
+    return {"levels": out, "one_pass_ms": round(statistics.median(one), 4),
+            "level_by_level_ms": round(statistics.median(sep), 4)}
+
+
 def cpu_baseline(cfg, kv_np):
     """The oracle, as it stands, over a bounded sample: whole slabs of the
     workload (all of it when it is small), single-threaded."""
@@ -333,6 +377,7 @@ def main():
     res["container"] = container_leg(kvc, d, buf, cfg, stream, args.steps)
     res["int8_comparator"] = int8_leg(kvc, d, kvt, buf, cfg, stream, args.steps,
                                       res["container"]["bits_per_elem"])
+    res["quality_levels"] = levels_leg(kvc, cfg, kvt, stream, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, kv_np)
     print(json.dumps(res), flush=True)

@@ -12,6 +12,15 @@
 
 namespace {
 
+__device__ __forceinline__ uint32_t quant1f(float x, float factor, float M)
+{
+    float p = x * factor;
+    p = p + M;
+    float r = __builtin_rintf(p);
+    r = r < 0.0f ? 0.0f : (r > 255.0f ? 255.0f : r);  // only non-finite rows get here
+    return (uint32_t)r;
+}
+
 __device__ __forceinline__ uint32_t quant1(uint32_t bits, float factor, float M)
 {
     float p = kvc_h2f(bits) * factor;
@@ -239,6 +248,11 @@ __global__ __launch_bounds__(1024) void k_quant_cdf_levels(const uint16_t *__res
         const float m = kvc_h2f(mx);
         if (mx >= 0x7C00u && lane == 0) kvc_flag(status, KVC_DEV_NONFINITE);
         if (lane == 0) max1[row] = (uint16_t)mx;
+        float xf[KREG][8];  // the row's values in fp32, converted once for all levels
+#pragma unroll
+        for (int k = 0; k < KREG; ++k)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xf[k][i] = kvc_h2f((reg[k][i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
 #pragma unroll 1
         for (int l = 0; l < lv.n; ++l) {
             const float M = (float)lv.maxq[l][g.lk];
@@ -252,8 +266,7 @@ __global__ __launch_bounds__(1024) void k_quant_cdf_levels(const uint16_t *__res
                 uint32_t b[2] = {0, 0};
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const uint32_t hv = (reg[k][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-                    const uint32_t q = quant1(hv, factor, M);
+                    const uint32_t q = quant1f(xf[k][i], factor, M);
                     b[i >> 2] |= q << (8 * (i & 3));
                     const uint32_t s = q < amax ? q : amax;
                     atomicAdd(&h[(int)(s >> 1) * C + i * C8 + pi], 1u << (16u * (s & 1u)));
