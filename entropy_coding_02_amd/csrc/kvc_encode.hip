@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
     const int ntiles = (C + CT - 1) / CT;
 
     // slot dword k of this lane: block region + (k * 256 + lane) dwords
-    SlotOut out{(uint32_t *)(slots + (int64_t)blockIdx.x * p.slot_bytes * 256) + threadIdx.x, 256u};
+    SlotOut out{(uint32_t *)(slots + (int64_t)blockIdx.x * p.slot_bytes * 256), threadIdx.x, 256u};
     EncState e;
     enc_init(e);
     // Tiles arrive in registers while the previous ones are coded, and go

@@ -103,18 +103,114 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restric
     }
 }
 
+// The fused passes below, for a finite row (every |x| <= m, so p lies in
+// [0, 2 MAX] up to a rounding and |p| < 2^22): p + 1.5 * 2^23 is rounded to
+// an integer, ties to even, which is rint(p); its fp32 bits are 0x4B400000 +
+// rint(p), the symbol in the low byte.  Rows holding Inf or NaN take the
+// clamped quant1 instead (they are flagged; their symbols only stay in range).
+__device__ __forceinline__ uint32_t quant_bits(float x, float factor, float M)
+{
+    float p = x * factor;
+    p = p + M;
+    return __float_as_uint(p + 12582912.0f);
+}
+
+// The low bytes of four words, b0 lowest.
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3)
+{
+    return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
+}
+
+// Row max of the wave's 64 lanes, uniform: DPP steps within quads, half
+// rows and rows, then the row broadcasts; lane 63 ends with the maximum.
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row half mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row bcast 15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row bcast 31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// max over the lane's pieces of |x| as bits (sign cleared), two halves per
+// packed 16-bit max.
+template <int KREG>
+__device__ __forceinline__ uint32_t lane_absmax(const u32x4 (&r)[KREG])
+{
+    typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 acc = {0, 0};
+#pragma unroll
+    for (int k = 0; k < KREG; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, r[k][i] & 0x7FFF7FFFu));
+    return max((uint32_t)acc.x, (uint32_t)acc.y);
+}
+
+// Histogram layout of the fused passes (C % 8 == 0, C8 = C / 8): the 16-bit
+// counter of (symbol s, channel c = 8 pi + i) is half (i & 1) of word
+// s * (C / 2) + (i >> 1) * C8 + pi.  At each step the lanes of a wave hold
+// consecutive pieces pi of one element slot i, so their atomics go to
+// consecutive words (distinct banks) whatever the symbols, and which half a
+// counter is does not depend on the data.
+__device__ __forceinline__ int hist_word(int s, int i, int pi, int C8)
+{
+    return s * 4 * C8 + (i >> 1) * C8 + pi;
+}
+
+// CDF rows of one slab from its histogram (layout above) at hist: thread j
+// takes channel 8 (j % C8) + j / C8, so the lanes of a wave read consecutive
+// words.  Rows of A entries (A % 8 == 0) go out as 16-byte stores.
+__device__ __forceinline__ void slab_cdf_rows(const uint32_t *hist, uint16_t *cdf, int64_t slab, int C,
+                                              int A, double rn)
+{
+    const int C8 = C / 8;
+    const uint32_t K = 65536u - (uint32_t)A;
+    for (int j = threadIdx.x; j < C; j += blockDim.x) {
+        const int pi = j % C8, i = j / C8;
+        const uint32_t *h = hist + hist_word(0, i, pi, C8);
+        const int sh = 16 * (i & 1);
+        uint32_t *dst = (uint32_t *)(cdf + (slab * C + 8 * pi + i) * A);
+        uint32_t Ck = 0;
+        for (int k = 0; k < A; k += 8) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = kvc_cdf_entry((uint32_t)(k + 2 * e), Ck, K, rn);
+                Ck += (h[(k + 2 * e) * 4 * C8] >> sh) & 0xFFFFu;
+                const uint32_t hi = kvc_cdf_entry((uint32_t)(k + 2 * e + 1), Ck, K, rn);
+                Ck += (h[(k + 2 * e + 1) * 4 * C8] >> sh) & 0xFFFFu;
+                w[e] = lo | (hi << 16);
+            }
+            *(u32x4 *)(dst + k / 2) = u32x4{w[0], w[1], w[2], w[3]};
+        }
+    }
+}
+
+__device__ __forceinline__ void zero_lds(uint32_t *hist, int words)  // words % 4 == 0
+{
+    for (int i = 4 * threadIdx.x; i < words; i += 4 * blockDim.x) *(u32x4 *)(hist + i) = u32x4{0, 0, 0, 0};
+}
+
+// One element of a finite row: its quantizer bits b (symbol in the low
+// byte) counted at the byte offset (b & 0xFFFFFF) * rowb + base, where base
+// already takes off the 0x400000 * rowb that the bits' 0x4B40 prefix adds.
+__device__ __forceinline__ void count_bits(lds_u8 *h8, uint32_t b, uint32_t rowb, uint32_t base, uint32_t one)
+{
+    const uint32_t off = (b & 0xFFFFFFu) * rowb + base;
+    __hip_atomic_fetch_add((lds_u32 *)(h8 + off), one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // Quantization, histograms and CDFs in one pass: one block of 1024 threads
 // per slab (chunk, layer, K|V), for C % 8 == 0 and C <= 512 * KREG.  Each
 // wave takes whole token rows: the row (8 channels per 16-byte piece, KREG
 // pieces per lane) stays in registers for the integer max, the quantizer
-// and the symbol stores, and every symbol is counted at once in an LDS
-// histogram of packed 16-bit counters.  Counter pair (channel c, symbols
-// 2h, 2h+1) is word h * C + (c & 7) * (C / 8) + (c >> 3): at each step the
-// lanes of a wave hold channels 8 apart, which this layout puts in
-// consecutive words, so their atomics hit distinct banks whatever the
-// symbols.  After the last row each thread turns one channel's counts into
-// its CDF row (kvc_cdf_entry) and writes it with 16-byte stores.  The input
-// is read once; no pass re-reads the symbols.
+// and the symbol stores, and every symbol is counted at once in the LDS
+// histogram of 16-bit counters.  After the last row the block turns the
+// counts into CDF rows (kvc_cdf_entry).  The input is read once; no pass
+// re-reads the symbols.
 template <int KREG>
 __global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__ kv,
                                                     uint8_t *__restrict__ sym,
@@ -123,15 +219,21 @@ __global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__
                                                     int32_t *status)
 {
     extern __shared__ uint32_t hist[];
+    lds_u8 *const h8 = (lds_u8 *)hist;
     const int64_t slab = blockIdx.x;
     const SlabGeom g = slab_geom(p, slab);
     const int C = p.C, A = p.A, C8 = C / 8;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    const int nwords = (A / 2) * C;
-    for (int i = threadIdx.x; i < nwords; i += blockDim.x) hist[i] = 0;
-    __syncthreads();
+    zero_lds(hist, (A / 2) * C);
     const float M = (float)p.maxq[g.lk];
     const uint32_t amax = (uint32_t)A - 1u;
+    const uint32_t rowb = ((uint32_t)C & 0x7F8u) * 2u;  // bytes from one symbol's counters to the next's
+    uint32_t base[KREG][4];
+#pragma unroll
+    for (int k = 0; k < KREG; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) base[k][j] = 4u * (uint32_t)hist_word(0, 2 * j, lane + 64 * k, C8) - 0x400000u * rowb;
+    __syncthreads();
     // Software pipeline over the wave's rows t = wid, wid + nw, ...: the next
     // row's pieces are loaded while the current one is processed, and a
     // row's symbol stores go out after the next row's data has arrived, so
@@ -157,33 +259,41 @@ __global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__
     if (wid < g.nj) load_row(wid, cur);
     for (int t = wid; t < g.nj; t += nw) {
         const int64_t row = g.row0 + t;
-        uint32_t mx = 0;
-#pragma unroll
-        for (int k = 0; k < KREG; ++k)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t a = cur[k][i] & 0x7FFF7FFFu;
-                mx = max(mx, max(a & 0xFFFFu, a >> 16));
-            }
+        uint32_t mx = lane_absmax<KREG>(cur);
         if (qrow >= 0) store_row();
         if (t + nw < g.nj) load_row(t + nw, nxt);
-        mx = wave_max_u32(mx);
+        mx = wave_max_dpp(mx);
         const float m = kvc_h2f(mx);
         const float factor = (mx != 0) ? M / m : 0.0f;
-        if (mx >= 0x7C00u && lane == 0) kvc_flag(status, KVC_DEV_NONFINITE);
         if (lane == 0) max1[row] = (uint16_t)mx;
+        if (mx < 0x7C00u) {
 #pragma unroll
-        for (int k = 0; k < KREG; ++k) {
-            const int pi = lane + 64 * k;
-            qb[k][0] = qb[k][1] = 0;
-            if (pi >= C8) continue;
+            for (int k = 0; k < KREG; ++k) {
+                const int pi = lane + 64 * k;
+                if (pi >= C8) continue;
+                uint32_t b[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t h = (cur[k][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-                const uint32_t q = quant1(h, factor, M);
-                qb[k][i >> 2] |= q << (8 * (i & 3));
-                const uint32_t s = q < amax ? q : amax;  // only non-finite rows exceed A - 1
-                atomicAdd(&hist[(int)(s >> 1) * C + i * C8 + pi], 1u << (16u * (s & 1u)));
+                for (int i = 0; i < 8; ++i) {
+                    b[i] = quant_bits(kvc_h2f((cur[k][i >> 1] >> (16 * (i & 1))) & 0xFFFFu), factor, M);
+                    count_bits(h8, b[i], rowb, base[k][i >> 1], (i & 1) ? 0x10000u : 1u);
+                }
+                qb[k][0] = pack_low_bytes(b[0], b[1], b[2], b[3]);
+                qb[k][1] = pack_low_bytes(b[4], b[5], b[6], b[7]);
+            }
+        } else {
+            if (lane == 0) kvc_flag(status, KVC_DEV_NONFINITE);
+#pragma unroll
+            for (int k = 0; k < KREG; ++k) {
+                const int pi = lane + 64 * k;
+                qb[k][0] = qb[k][1] = 0;
+                if (pi >= C8) continue;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t q = quant1((cur[k][i >> 1] >> (16 * (i & 1))) & 0xFFFFu, factor, M);
+                    qb[k][i >> 2] |= q << (8 * (i & 3));
+                    const uint32_t s = q < amax ? q : amax;
+                    atomicAdd(&hist[hist_word((int)s, i, pi, C8)], (i & 1) ? 0x10000u : 1u);
+                }
             }
         }
         qrow = row;
@@ -192,25 +302,7 @@ __global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__
     }
     if (qrow >= 0) store_row();
     __syncthreads();
-    const uint32_t K = 65536u - (uint32_t)A;
-    for (int c = threadIdx.x; c < C; c += blockDim.x) {
-        const uint32_t *h = hist + (c & 7) * C8 + (c >> 3);
-        uint32_t *dst = (uint32_t *)(cdf + (slab * C + c) * A);
-        uint32_t Ck = 0;
-        for (int k = 0; k < A; k += 8) {
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t cnt = h[(k / 2 + e) * C];
-                const uint32_t lo = kvc_cdf_entry((uint32_t)(k + 2 * e), Ck, K, g.rn);
-                Ck += cnt & 0xFFFFu;
-                const uint32_t hi = kvc_cdf_entry((uint32_t)(k + 2 * e + 1), Ck, K, g.rn);
-                Ck += cnt >> 16;
-                w[e] = lo | (hi << 16);
-            }
-            *(u32x4 *)(dst + k / 2) = u32x4{w[0], w[1], w[2], w[3]};  // A % 8 == 0
-        }
-    }
+    slab_cdf_rows(hist, cdf, slab, C, A, g.rn);
 }
 
 // Several quality levels (bins tables) of the same tensor in one pass: as
@@ -227,27 +319,22 @@ __global__ __launch_bounds__(1024) void k_quant_cdf_levels(const uint16_t *__res
     const SlabGeom g = slab_geom(p, slab);
     const int C = p.C, C8 = C / 8;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    for (int i = threadIdx.x; i < lv.words; i += blockDim.x) hist[i] = 0;
+    const uint32_t rowb = ((uint32_t)C & 0x7F8u) * 2u;
+    zero_lds(hist, lv.words);
     __syncthreads();
     for (int t = wid; t < g.nj; t += nw) {
         const int64_t row = g.row0 + t;
         const uint16_t *x = kv + row * C;
         u32x4 reg[KREG];
-        uint32_t mx = 0;
 #pragma unroll
         for (int k = 0; k < KREG; ++k) {
             const int pi = lane + 64 * k;
             reg[k] = pi < C8 ? *(const u32x4 *)(x + 8 * pi) : u32x4{0, 0, 0, 0};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t a = reg[k][i] & 0x7FFF7FFFu;
-                mx = max(mx, max(a & 0xFFFFu, a >> 16));
-            }
         }
-        mx = wave_max_u32(mx);
+        const uint32_t mx = wave_max_dpp(lane_absmax<KREG>(reg));
         const float m = kvc_h2f(mx);
-        if (mx >= 0x7C00u && lane == 0) kvc_flag(status, KVC_DEV_NONFINITE);
         if (lane == 0) max1[row] = (uint16_t)mx;
+        if (mx >= 0x7C00u && lane == 0) kvc_flag(status, KVC_DEV_NONFINITE);
         float xf[KREG][8];  // the row's values in fp32, converted once for all levels
 #pragma unroll
         for (int k = 0; k < KREG; ++k)
@@ -259,46 +346,39 @@ __global__ __launch_bounds__(1024) void k_quant_cdf_levels(const uint16_t *__res
             const float factor = (mx != 0) ? M / m : 0.0f;
             const uint32_t amax = (uint32_t)lv.A[l] - 1u;
             uint32_t *h = hist + lv.hist[l];
+            lds_u8 *const h8 = (lds_u8 *)h;
 #pragma unroll
             for (int k = 0; k < KREG; ++k) {
                 const int pi = lane + 64 * k;
                 if (pi >= C8) continue;
-                uint32_t b[2] = {0, 0};
+                uint32_t q2[2];
+                if (mx < 0x7C00u) {
+                    uint32_t b[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t q = quant1f(xf[k][i], factor, M);
-                    b[i >> 2] |= q << (8 * (i & 3));
-                    const uint32_t s = q < amax ? q : amax;
-                    atomicAdd(&h[(int)(s >> 1) * C + i * C8 + pi], 1u << (16u * (s & 1u)));
+                    for (int i = 0; i < 8; ++i) {
+                        b[i] = quant_bits(xf[k][i], factor, M);
+                        const uint32_t base = 4u * (uint32_t)hist_word(0, i, pi, C8) - 0x400000u * rowb;
+                        count_bits(h8, b[i], rowb, base, (i & 1) ? 0x10000u : 1u);
+                    }
+                    q2[0] = pack_low_bytes(b[0], b[1], b[2], b[3]);
+                    q2[1] = pack_low_bytes(b[4], b[5], b[6], b[7]);
+                } else {
+                    q2[0] = q2[1] = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t q = quant1f(xf[k][i], factor, M);
+                        q2[i >> 2] |= q << (8 * (i & 3));
+                        const uint32_t s = q < amax ? q : amax;
+                        atomicAdd(&h[hist_word((int)s, i, pi, C8)], (i & 1) ? 0x10000u : 1u);
+                    }
                 }
-                *(uint2 *)(lv.sym[l] + row * C + 8 * pi) = make_uint2(b[0], b[1]);
+                *(uint2 *)(lv.sym[l] + row * C + 8 * pi) = make_uint2(q2[0], q2[1]);
             }
         }
     }
     __syncthreads();
 #pragma unroll 1
-    for (int l = 0; l < lv.n; ++l) {
-        const int A = lv.A[l];
-        const uint32_t K = 65536u - (uint32_t)A;
-        for (int c = threadIdx.x; c < C; c += blockDim.x) {
-            const uint32_t *h = hist + lv.hist[l] + (c & 7) * C8 + (c >> 3);
-            uint32_t *dst = (uint32_t *)(lv.cdf[l] + (slab * C + c) * A);
-            uint32_t Ck = 0;
-            for (int k = 0; k < A; k += 8) {
-                uint32_t w[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t cnt = h[(k / 2 + e) * C];
-                    const uint32_t lo = kvc_cdf_entry((uint32_t)(k + 2 * e), Ck, K, g.rn);
-                    Ck += cnt & 0xFFFFu;
-                    const uint32_t hi = kvc_cdf_entry((uint32_t)(k + 2 * e + 1), Ck, K, g.rn);
-                    Ck += cnt >> 16;
-                    w[e] = lo | (hi << 16);
-                }
-                *(u32x4 *)(dst + k / 2) = u32x4{w[0], w[1], w[2], w[3]};
-            }
-        }
-    }
+    for (int l = 0; l < lv.n; ++l) slab_cdf_rows(hist + lv.hist[l], lv.cdf[l], slab, C, lv.A[l], g.rn);
 }
 
 }  // namespace

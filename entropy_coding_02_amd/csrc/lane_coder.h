@@ -20,7 +20,8 @@
 //     carry that runs past all k pending bytes sets bit 8k of pb: it belongs
 //     to bytes already written, and is added to them (a rare path);
 //   * when k reaches 6, the 4 oldest pending bytes go out as one aligned
-//     big-endian dword, so at least 2 bytes always stay pending.
+//     big-endian dword, so at least 2 bytes always stay pending (the state
+//     counts pending bits, 8k).
 // All arithmetic is 32/64-bit integer; this header is compiled both for the
 // GPU kernels and, in the tests, for the host.
 #pragma once
@@ -43,19 +44,26 @@ struct EncState {
     uint32_t lo;     // low 32 bits of the coding interval's lower end
     uint32_t range;  // interval width, >= 2^24 between symbols
     uint64_t pb;     // k pending bytes (newest lowest) + carry indicator at bit 8k
-    uint32_t k;      // pending byte count
+    uint32_t kb;     // pending bits, 8k
     uint32_t w;      // dwords already written to the stream slot
 };
 
 // A stream slot: dword-addressable memory owned by one lane; dword i of the
-// stream is at p[i * stride] (the kernels interleave the slots of a block's
-// lanes, stride = lanes per block, so lanes writing their k-th dwords at
-// about the same time fill the same cache lines).
+// stream is at base[i * stride + lane] (the kernels interleave the slots of a
+// block's lanes, stride = lanes per block, so lanes writing their k-th dwords
+// at about the same time fill the same cache lines).  base is the same for
+// the whole block and a slot region stays below 4 GiB, so an address is the
+// uniform base plus a 32-bit offset.
 struct SlotOut {
-    uint32_t *p;
+    uint32_t *base;
+    uint32_t lane;
     uint32_t stride;
-    KVC_HD uint32_t load(uint32_t i) const { return p[(uint64_t)i * stride]; }
-    KVC_HD void store(uint32_t i, uint32_t v) const { p[(uint64_t)i * stride] = v; }
+    KVC_HD uint32_t *at(uint32_t i) const
+    {
+        return (uint32_t *)((char *)base + (size_t)((i * stride + lane) * 4u));
+    }
+    KVC_HD uint32_t load(uint32_t i) const { return *at(i); }
+    KVC_HD void store(uint32_t i, uint32_t v) const { *at(i) = v; }
 };
 
 KVC_HD void enc_init(EncState &e)
@@ -63,7 +71,7 @@ KVC_HD void enc_init(EncState &e)
     e.lo = 0;
     e.range = 0xFFFFFFFFu;
     e.pb = 0;
-    e.k = 0;
+    e.kb = 0;
     e.w = 0;
 }
 
@@ -93,15 +101,17 @@ KVC_HD void enc_put(EncState &e, uint32_t st, uint32_t fr, const Out &out)
     uint64_t wide = (uint64_t)lo2 << n;
     e.pb = (e.pb << n) | (wide >> 32);
     e.lo = (uint32_t)wide;
-    e.k += n >> 3;
-    if (e.k >= 6) {
-        uint32_t sh = 8u * (e.k - 4u);
-        uint32_t word = (uint32_t)(e.pb >> sh);
-        if ((e.pb >> (sh + 32u)) != 0) enc_carry_into_written(out, e.w);
+    e.kb += n;
+    if (e.kb >= 48u) {
+        // k = 6 or 7: bytes k-1 .. k-4 go out, 16 or 24 bits stay; the carry
+        // indicator (bit 8k) is bit sh of the high dword
+        const uint32_t sh = e.kb - 32u;
+        const uint32_t word = (uint32_t)(e.pb >> sh);
+        if (((uint32_t)(e.pb >> 32) >> sh) != 0) enc_carry_into_written(out, e.w);
         out.store(e.w, kvc_bswap32(word));
         e.w += 1;
-        e.pb &= ((uint64_t)1 << sh) - 1u;
-        e.k -= 4;
+        e.pb = (uint64_t)((uint32_t)e.pb & ((1u << sh) - 1u));
+        e.kb -= 32u;
     }
 }
 
@@ -113,13 +123,13 @@ KVC_HD uint32_t enc_finish(EncState &e, const Out &out)
     uint32_t lo2 = e.lo + 0xFFFFFFu;
     e.pb += (lo2 < 0xFFFFFFu) ? 1u : 0u;
     uint32_t top = lo2 >> 24;  // the byte kept after rounding up to a multiple of 2^24
-    uint32_t kb = 8u * e.k;
+    const uint32_t kb = e.kb;
     if ((e.pb >> kb) != 0) {
         enc_carry_into_written(out, e.w);
         e.pb &= ((uint64_t)1 << kb) - 1u;
     }
     uint64_t tail = (e.pb << 8) | top;  // k + 1 bytes, oldest first
-    uint32_t nt = e.k + 1u;
+    uint32_t nt = kb / 8u + 1u;
     while (nt > 0 && (tail & 0xFFu) == 0) {
         tail >>= 8;
         nt -= 1;

@@ -15,7 +15,7 @@ int64_t hostsim_encode_stream(const uint8_t *q, int32_t C, int32_t A, const uint
 {
     EncState e;
     enc_init(e);
-    SlotOut out{(uint32_t *)slot, 1};
+    SlotOut out{(uint32_t *)slot, 0, 1};
     for (int32_t c = 0; c < C; ++c) {
         const uint16_t *row = cdf_rows + (int64_t)c * A;
         uint32_t s = q[c] < (uint32_t)A ? q[c] : (uint32_t)A - 1u;
