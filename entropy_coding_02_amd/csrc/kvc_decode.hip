@@ -20,6 +20,11 @@
 #ifndef KVC_DEC_BLOCKS_MAX_WAVES
 #define KVC_DEC_BLOCKS_MAX_WAVES 2048
 #endif
+// Launches of at most this many streams decode with a group of lanes per
+// stream (k_decode_group), for rows of 8 to 64 entries.
+#ifndef KVC_DEC_GROUP_MAX_STREAMS
+#define KVC_DEC_GROUP_MAX_STREAMS 32768
+#endif
 
 namespace {
 
@@ -192,6 +197,231 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
     if (active && bad) kvc_flag(status, KVC_DEV_CORRUPT);
 }
 
+// Sum of v over each aligned group of G lanes (G = 2, 4 or 8), in every lane
+// of the group: DPP swaps within quads, then the half-row mirror.
+template <int G>
+__device__ __forceinline__ uint32_t group_sum(uint32_t v)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
+    if constexpr (G >= 4) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+    if constexpr (G >= 8) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);  // half-row mirror
+    return v;
+}
+
+// Decoding with G lanes per stream, for launches with few streams.  A stream's
+// symbols are a chain of dependent steps, so with one lane per stream a small
+// launch leaves most of the chip idle while each step waits on its table
+// reads.  Here the G lanes of a group carry identical coder state and byte
+// feeds (each its own ring), and at each symbol lane q counts the entries of
+// its slice [q E, q E + E) of the channel's padded search row (E = P2 / G)
+// with r * cdf_k <= code.  The group's DPP sum is the number of qualifying
+// entries; for a non-decreasing row (cdf_0 = 0) the symbol is that count
+// minus one, clamped to A - 1: the largest qualifying k, as the one-lane
+// searches find it.  The slice reads do not depend on the coder state.  The
+// outputs of a stream are split over its lanes.  Block: 256 / G streams of
+// one slab; LDS as in k_decode.
+template <bool VEC, int OUT, int NSTEP, int G>
+__global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict__ payload,
+                                                      int64_t payload_bytes,
+                                                      const uint64_t *__restrict__ slab_off,
+                                                      const uint16_t *__restrict__ stream_len,
+                                                      const uint16_t *__restrict__ cdf,
+                                                      const uint16_t *__restrict__ max1,
+                                                      uint8_t *__restrict__ sym_out,
+                                                      void *__restrict__ out, KParams p,
+                                                      int32_t *status, int CT)
+{
+    extern __shared__ uint32_t lds[];
+    __shared__ uint32_t s_red[4];
+    constexpr uint32_t P2 = 1u << NSTEP;
+    constexpr int E = (int)P2 / G;  // slice entries per lane: 2, 4, 8 or 16
+    static_assert(E >= 2 && E <= 16 && (E & (E - 1)) == 0, "slices of 2 to 16 entries");
+    constexpr int SPB = 256 / G;     // streams per block
+    const int C = p.C, A = p.A;
+    float *lut = (float *)lds;
+    lds_u32 *const ring = (lds_u32 *)(lds + 256) + threadIdx.x * 17u;
+    const int n16 = (CT * (int)P2 + 1) / 2;
+    lds_u32 *const tile = (lds_u32 *)(lds + 256 + 256 * 17);
+    lds_u16 *const r16 = (lds_u16 *)tile;
+    lds_u32 *const pr = tile + n16;
+
+    const int q = (int)threadIdx.x % G;   // lane within the stream's group
+    const int sl = (int)threadIdx.x / G;  // stream within the block
+    const int bps = (p.Tc + SPB - 1) / SPB;
+    const int64_t slab = blockIdx.x / bps;
+    const int tb = (int)(blockIdx.x - slab * bps);
+    const int t = tb * SPB + sl;
+    const SlabGeom g = slab_geom(p, slab);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const bool active = t < g.nj;
+
+    // bytes of the slab's streams before this block
+    uint32_t pre = 0;
+    const int n_before = min(tb * SPB, g.nj);
+    for (int i = threadIdx.x; i < n_before; i += 256) pre += stream_len[g.sid0 + i];
+    pre = wave_sum_u32(pre);
+    if (lane == 0) s_red[wid] = pre;
+    __syncthreads();
+    pre = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    __syncthreads();
+    // exclusive scan over the block's streams: lane 0 of each group adds its length
+    const uint32_t len = active ? stream_len[g.sid0 + t] : 0u;
+    uint32_t incl = q == 0 ? len : 0u;
+    for (int off = 1; off < 64; off <<= 1) {
+        uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_red[wid] = incl;
+    if (threadIdx.x < (unsigned)A) {
+        const int M = p.maxq[g.lk];
+        lut[threadIdx.x] = (float)((int)threadIdx.x - M) / (float)M;
+    }
+    if (P2 > (uint32_t)A)
+        for (int e = threadIdx.x; e < CT * (int)P2; e += 256)
+            if ((uint32_t)(e & (P2 - 1)) >= (uint32_t)A) r16[e] = 0xFFFFu;
+    __syncthreads();
+    uint32_t wbase = 0;
+    for (int i = 0; i < wid; ++i) wbase += s_red[i];
+
+    const int64_t row = g.row0 + (active ? t : 0);
+    const uint64_t off = active ? slab_off[slab] + pre + wbase + incl - len : 0;
+    RingIn<lds_u32 *> in;
+    in.init(payload, off, len, (uint64_t)payload_bytes, ring);
+    DecState d;
+    dec_init(d, in);
+    constexpr int ODT = (OUT & OUT_F16) ? ODT_F16 : (OUT & OUT_F32) ? ODT_F32 : -1;
+    const float m = (ODT >= 0) ? kvc_h2f(max1[row]) : 0.0f;
+    uint32_t bad = 0;
+    uint8_t *so = (OUT & OUT_SYM) ? sym_out + row * C : nullptr;
+    const uint16_t *srows = cdf + slab * C * A;
+    const int ntiles = (C + CT - 1) / CT;
+    const uint32_t amax = (uint32_t)A - 1u;
+    auto decode1 = [&](int cl) -> uint32_t {
+        const lds_u16 *sp = r16 + cl * (int)P2 + q * E;
+        uint32_t e2[E / 2];
+        if constexpr (E == 2) {
+            e2[0] = *(const lds_u32 *)sp;
+        } else if constexpr (E == 4) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = *(const __attribute__((address_space(3))) u32x2 *)sp;
+            e2[0] = v.x;
+            e2[1] = v.y;
+        } else {
+#pragma unroll
+            for (int h = 0; h < E / 8; ++h) {
+                const u32x4 v = *(const lds_u32x4 *)(sp + 8 * h);
+                e2[4 * h] = v.x;
+                e2[4 * h + 1] = v.y;
+                e2[4 * h + 2] = v.z;
+                e2[4 * h + 3] = v.w;
+            }
+        }
+        const uint32_t r = d.range >> 16;
+        uint32_t n = 0;
+#pragma unroll
+        for (int i = 0; i < E; ++i) n += r * ((e2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) <= d.code ? 1u : 0u;
+        n = group_sum<G>(n);
+        const uint32_t s = min(n - 1u, amax);  // n = 0 only for a row with cdf_0 > 0
+        const uint32_t pp = pr[cl * A + s];
+        bad |= dec_advance(d, r, pp & 0xFFFFu, pp >> 16);
+        return s;
+    };
+
+    PairTile<2> pt;
+    uint32_t hw[16];
+    pt.load(srows, 0, CT, C, A);
+    for (int it = 0; it < ntiles; ++it) {
+        const int c0 = it * CT, c1 = min(C, c0 + CT);
+        __syncthreads();
+        pt.store(pr, CT, A, r16, (int)P2);
+        __syncthreads();
+        if (it + 1 < ntiles) pt.load(srows, c0 + CT, CT, C, A);
+        if (!active) continue;
+        if constexpr (VEC) {
+            // C % 16 == 0, CT % 16 == 0: blocks of 32 channels (64 fp16 bytes per
+            // row), lane q writing 64 / G bytes of each; 8-symbol groups of
+            // symbols or fp32 values by lane gi % G
+            for (int cb = c0; cb < c1; cb += 32) {
+                const int nb = min(32, c1 - cb);  // 16 or 32
+#pragma unroll
+                for (int gi = 0; gi < 4; ++gi) {
+                    if (gi * 8 >= nb) break;
+                    const int cg = cb + gi * 8;
+                    in.group();
+                    uint32_t sw[2] = {0, 0};
+                    float fw[8];
+                    float ylo = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        if ((i & 1) == 0) dec_refill(d, in);
+                        const uint32_t s = decode1(cg - c0 + i);
+                        sw[i >> 2] |= s << (8 * (i & 3));
+                        if constexpr (ODT >= 0) {
+                            const float y = lut[s] * m;
+                            if constexpr (ODT == ODT_F16) {
+                                if (i & 1)
+                                    hw[gi * 4 + (i >> 1)] = kvc_f2h2(ylo, y);
+                                else
+                                    ylo = y;
+                            } else {
+                                fw[i] = y;
+                            }
+                        }
+                    }
+                    if (q == gi % G) {
+                        if constexpr ((OUT & OUT_SYM) != 0) *(uint2 *)(so + cg) = make_uint2(sw[0], sw[1]);
+                        if constexpr (ODT == ODT_F32) {
+                            float4 *o = (float4 *)((float *)out + row * C + cg);
+                            o[0] = make_float4(fw[0], fw[1], fw[2], fw[3]);
+                            o[1] = make_float4(fw[4], fw[5], fw[6], fw[7]);
+                        }
+                    }
+                }
+                if constexpr (ODT == ODT_F16) {
+                    constexpr int NW = 16 / G;  // dwords per lane
+                    uint32_t wv[NW];
+#pragma unroll
+                    for (int k = 0; k < NW; ++k) {
+                        wv[k] = hw[k];
+#pragma unroll
+                        for (int j = 1; j < G; ++j)
+                            if (q == j) wv[k] = hw[j * NW + k];
+                    }
+                    if (q * 2 * NW < nb) {
+                        uint32_t *o = (uint32_t *)((uint16_t *)out + row * C + cb) + q * NW;
+                        if constexpr (NW == 8) {
+                            ((uint4 *)o)[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                            ((uint4 *)o)[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+                        } else if constexpr (NW == 4) {
+                            *(uint4 *)o = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                        } else {
+                            *(uint2 *)o = make_uint2(wv[0], wv[1]);
+                        }
+                    }
+                }
+            }
+        } else {
+            for (int c = c0; c < c1; ++c) {
+                if ((c & 7) == 0) in.group();
+                if ((c & 1) == 0) dec_refill(d, in);
+                const uint32_t s = decode1(c - c0);
+                if (q == c % G) {
+                    if constexpr ((OUT & OUT_SYM) != 0) so[c] = (uint8_t)s;
+                    if constexpr (ODT >= 0) {
+                        const float y = lut[s] * m;
+                        if constexpr (ODT == ODT_F16)
+                            ((uint16_t *)out)[row * C + c] = (uint16_t)kvc_f2h(y);
+                        else
+                            ((float *)out)[row * C + c] = y;
+                    }
+                }
+            }
+        }
+    }
+
+    if (active && bad && q == 0) kvc_flag(status, KVC_DEV_CORRUPT);
+}
+
 // Dequantization alone: one wavefront per row; each wave keeps the table of
 // its current (layer, K|V) in its own LDS slice.
 template <int ODT>
@@ -243,6 +473,47 @@ static size_t dec_lds_bytes(int A, int CT)
     return sizeof(uint32_t) * (256 + 256 * 17 + n16 + (size_t)CT * A);
 }
 
+// k_decode_group: 4 lanes per stream (8 for 64-entry rows, so a lane's slice is 8 entries).
+static hipError_t launch_decode_group(const uint8_t *payload, int64_t payload_bytes,
+                                      const uint64_t *slab_off, const uint16_t *stream_len,
+                                      const uint16_t *cdf, const uint16_t *max1, uint8_t *sym_out,
+                                      void *out, int mode, const KParams &p, int32_t *status, bool vec,
+                                      int CT, size_t lds, int nstep, hipStream_t stream)
+{
+    const int G = nstep == 6 ? 8 : 4;
+    const int64_t bps = (p.Tc + 256 / G - 1) / (256 / G);
+    dim3 grid((unsigned)(bps * p.n_slabs)), block(256);
+#define KVC_DECG(V, O, N, GG)                                                                        \
+    hipLaunchKernelGGL((k_decode_group<V, O, N, GG>), grid, block, lds, stream, payload, payload_bytes, \
+                       slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
+#define KVC_DECG_N(V, O)                                                                             \
+    switch (nstep) {                                                                                 \
+    case 3: KVC_DECG(V, O, 3, 4); break;                                                             \
+    case 4: KVC_DECG(V, O, 4, 4); break;                                                             \
+    case 5: KVC_DECG(V, O, 5, 4); break;                                                             \
+    default: KVC_DECG(V, O, 6, 8); break;                                                            \
+    }
+#define KVC_DECG_M(V)                                                                                \
+    switch (mode) {                                                                                  \
+    case OUT_F16: KVC_DECG_N(V, OUT_F16) break;                                                      \
+    case OUT_F32: KVC_DECG_N(V, OUT_F32) break;                                                      \
+    case OUT_SYM: KVC_DECG_N(V, OUT_SYM) break;                                                      \
+    case OUT_F16 | OUT_SYM: KVC_DECG_N(V, OUT_F16 | OUT_SYM) break;                                  \
+    case OUT_F32 | OUT_SYM: KVC_DECG_N(V, OUT_F32 | OUT_SYM) break;                                  \
+    default: break;                                                                                  \
+    }
+    (void)G;
+    if (vec) {
+        KVC_DECG_M(true)
+    } else {
+        KVC_DECG_M(false)
+    }
+#undef KVC_DECG_M
+#undef KVC_DECG_N
+#undef KVC_DECG
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const uint64_t *slab_off,
                          const uint16_t *stream_len, const uint16_t *cdf, const uint16_t *max1,
                          uint8_t *sym_out, void *out, int out_dtype, const KParams &p,
@@ -256,6 +527,9 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
     const size_t lds = dec_lds_bytes(p.A, CT);
     vec = vec && (CT % 16 == 0);
     const int nstep = (int)cdf_nstep((uint32_t)p.A);
+    if (nstep >= 3 && nstep <= 6 && p.n_streams <= KVC_DEC_GROUP_MAX_STREAMS)
+        return launch_decode_group(payload, payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out,
+                                   mode, p, status, vec, CT, lds, nstep, stream);
     // The two-level search: measured faster for rows of up to 32 entries at any
     // launch size (most so where few waves cannot hide LDS latency), slower
     // for 64-entry rows unless the launch is that small.
