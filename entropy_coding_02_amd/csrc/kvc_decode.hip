@@ -23,7 +23,11 @@
 // Launches of at most this many streams decode with a group of lanes per
 // stream (k_decode_group), for rows of 8 to 64 entries.
 #ifndef KVC_DEC_GROUP_MAX_STREAMS
-#define KVC_DEC_GROUP_MAX_STREAMS 32768
+#define KVC_DEC_GROUP_MAX_STREAMS 16384
+#endif
+// Lanes per stream there for rows of 16 or 32 entries (4 or 8; 64-entry rows use 8).
+#ifndef KVC_DEC_GROUP_LANES
+#define KVC_DEC_GROUP_LANES 4
 #endif
 
 namespace {
@@ -480,7 +484,7 @@ static hipError_t launch_decode_group(const uint8_t *payload, int64_t payload_by
                                       void *out, int mode, const KParams &p, int32_t *status, bool vec,
                                       int CT, size_t lds, int nstep, hipStream_t stream)
 {
-    const int G = nstep == 6 ? 8 : 4;
+    const int G = (nstep == 6 || (nstep >= 4 && KVC_DEC_GROUP_LANES == 8)) ? 8 : 4;
     const int64_t bps = (p.Tc + 256 / G - 1) / (256 / G);
     dim3 grid((unsigned)(bps * p.n_slabs)), block(256);
 #define KVC_DECG(V, O, N, GG)                                                                        \
@@ -489,8 +493,8 @@ static hipError_t launch_decode_group(const uint8_t *payload, int64_t payload_by
 #define KVC_DECG_N(V, O)                                                                             \
     switch (nstep) {                                                                                 \
     case 3: KVC_DECG(V, O, 3, 4); break;                                                             \
-    case 4: KVC_DECG(V, O, 4, 4); break;                                                             \
-    case 5: KVC_DECG(V, O, 5, 4); break;                                                             \
+    case 4: KVC_DECG(V, O, 4, KVC_DEC_GROUP_LANES); break;                                           \
+    case 5: KVC_DECG(V, O, 5, KVC_DEC_GROUP_LANES); break;                                           \
     default: KVC_DECG(V, O, 6, 8); break;                                                            \
     }
 #define KVC_DECG_M(V)                                                                                \

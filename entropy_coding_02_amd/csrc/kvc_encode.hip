@@ -301,10 +301,22 @@ __global__ void k_zero_u64(uint64_t *dst) { *dst = 0; }
 // Channels per pair tile: a power of two from 16 to 64, at most 1024 pairs
 // (4 KB) when A allows, so the coding loop's 16-symbol steps and the 64-channel
 // symbol tiles both split into whole tiles.
-static int enc_tile_channels(int A)
+// Launches of at most this many streams stage wider CDF tiles.
+#ifndef KVC_ENC_WIDE_MAX_STREAMS
+#define KVC_ENC_WIDE_MAX_STREAMS 32768
+#endif
+
+// Channels per tile (a power of two, 16 to ENC_SW).  With few streams a tile
+// of 16 channels is coded in less time than its successor's rows take to
+// arrive from memory, so small launches stage up to ENC_SW channels (up to 8
+// pairs per thread); large ones keep the tile at one or two pairs per thread.
+static int enc_tile_channels(int A, int64_t n_streams)
 {
     int ct = 16;
-    while (ct < ENC_SW && 2 * ct * A <= 1024) ct *= 2;
+    if (n_streams <= KVC_ENC_WIDE_MAX_STREAMS)
+        while (ct < ENC_SW && 2 * ct * (A / 2) <= 8 * 256) ct *= 2;
+    else
+        while (ct < ENC_SW && 2 * ct * A <= 1024) ct *= 2;
     return ct;
 }
 
@@ -322,7 +334,7 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
     if (p.n_slabs == 0) return launch_zero_u64(slab_off, stream);
     const int64_t bps = (p.Tc + 255) / 256;
     dim3 grid((unsigned)(bps * p.n_slabs));
-    const int CT = enc_tile_channels(p.A);
+    const int CT = enc_tile_channels(p.A, p.n_streams);
     const size_t lds_pairs = (size_t)CT * p.A * sizeof(uint32_t);
     const int per = (CT * (p.A / 2) + 255) / 256;  // pairs staged per thread
 #define KVC_ENC(V, P, L)                                                                             \

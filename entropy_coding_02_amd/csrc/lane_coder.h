@@ -278,6 +278,17 @@ struct RingIn {
         rd += 1u;
         return v;
     }
+    // next() if take, else 0 and nothing consumed.  Branch-free: the ring is
+    // read either way (without take, stream dword rd - 1 again: it is still
+    // in the ring), so no path waits for that read before the next refill.
+    KVC_HD uint32_t next_if(bool take)
+    {
+        const uint32_t v = take ? nxt : 0u;
+        const uint32_t idx = take ? rd : rd - 1u;
+        nxt = ring[idx & 15u];
+        rd = idx + 1u;
+        return v;
+    }
 };
 
 struct DecState {
@@ -316,13 +327,14 @@ KVC_HD uint32_t dec_advance(DecState &d, uint32_t r, uint32_t st, uint32_t fr)
 }
 
 // Top bb up to at least 32 valid bits: enough for the next two symbols.
+// Without a branch (In::next_if), so a wave does not stall on the byte feed.
 template <class In>
 KVC_HD void dec_refill(DecState &d, In &in)
 {
-    if (d.nb < 32u) {
-        d.bb |= (uint64_t)in.next() << (32u - d.nb);
-        d.nb += 32u;
-    }
+    const bool need = d.nb < 32u;
+    const uint32_t v = in.next_if(need);  // 0 unless need, and then 32 - nb is in [1, 32]
+    d.bb |= (uint64_t)v << ((32u - d.nb) & 63u);
+    d.nb += need ? 32u : 0u;
 }
 
 // ------------------------------------------------- per-symbol table lookups
