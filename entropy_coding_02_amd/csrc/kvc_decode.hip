@@ -218,7 +218,8 @@ __device__ __forceinline__ uint32_t group_sum(uint32_t v)
 // reads.  Here the G lanes of a group carry identical coder state and byte
 // feeds (each its own ring), and at each symbol lane q counts the entries of
 // its slice [q E, q E + E) of the channel's padded search row (E = P2 / G)
-// with r * cdf_k <= code.  The group's DPP sum is the number of qualifying
+// with r * cdf_k <= code (a prefix of the slice on a non-decreasing row, so
+// a binary search over the slice's registers).  The group's DPP sum is the number of qualifying
 // entries; for a non-decreasing row (cdf_0 = 0) the symbol is that count
 // minus one, clamped to A - 1: the largest qualifying k, as the one-lane
 // searches find it.  The slice reads do not depend on the coder state.  The
@@ -321,9 +322,11 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
             }
         }
         const uint32_t r = d.range >> 16;
-        uint32_t n = 0;
-#pragma unroll
-        for (int i = 0; i < E; ++i) n += r * ((e2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) <= d.code ? 1u : 0u;
+        // qualifying entries of the slice: none, or a prefix ending at piece_last
+        // (computed either way; the empty asm keeps it out of a branch)
+        uint32_t n = piece_last<E>(e2, r, d.code) + 1u;
+        __asm__("" : "+v"(n));
+        n = r * (e2[0] & 0xFFFFu) <= d.code ? n : 0u;
         n = group_sum<G>(n);
         const uint32_t s = min(n - 1u, amax);  // n = 0 only for a row with cdf_0 > 0
         const uint32_t pp = pr[cl * A + s];

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
                     for (int i = 0; i < 8; ++i) {
                         const int k = h * 8 + i;
                         uint32_t s = (wv[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                        s = s < (uint32_t)A ? s : (uint32_t)(A - 1);
+                        s = min(s, (uint32_t)A - 1u);
                         pv[i] = trow[k * A + s];
                     }
 #pragma unroll
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
         } else {
             for (int c = c0; c < c1; ++c) {
                 uint32_t s = q[c];
-                s = s < (uint32_t)A ? s : (uint32_t)(A - 1);
+                s = min(s, (uint32_t)A - 1u);
                 enc_pair(e, pairs[(c - c0) * A + s], out);
             }
         }

@@ -372,27 +372,62 @@ KVC_HD uint32_t cdf_search(const Row &row, uint32_t A, uint32_t r, uint32_t code
     return s < A - 1u ? s : A - 1u;
 }
 
+// Index of the last qualifying entry (r * e <= code) of a non-decreasing run
+// of E entries (E a power of two, 2 to 16) packed two per dword (entry 2j in
+// the low half of d[j]), given that entry 0 qualifies: a binary search over
+// values already in registers (log2 E compares, each halving the run with
+// selects).
+template <int E>
+KVC_HD uint32_t piece_last(const uint32_t *d, uint32_t r, uint32_t code)
+{
+    if constexpr (E == 2) {
+        return r * (d[0] >> 16) <= code ? 1u : 0u;
+    } else {
+        constexpr int H = E / 4;  // dwords in each half
+        const bool a = r * (d[H] & 0xFFFFu) <= code;  // entry E / 2
+        uint32_t h[H];
+#pragma unroll
+        for (int k = 0; k < H; ++k) h[k] = a ? d[H + k] : d[k];
+        return (a ? (uint32_t)(E / 2) : 0u) + piece_last<E / 2>(h, r, code);
+    }
+}
+
+// The same over NB values one per register (h[0] is taken to qualify).
+template <int NB>
+KVC_HD uint32_t heads_last(const uint32_t *h, uint32_t r, uint32_t code)
+{
+    if constexpr (NB == 1) {
+        return 0u;
+    } else {
+        const bool a = r * h[NB / 2] <= code;
+        uint32_t g[NB / 2];
+#pragma unroll
+        for (int k = 0; k < NB / 2; ++k) g[k] = a ? h[NB / 2 + k] : h[k];
+        return (a ? (uint32_t)(NB / 2) : 0u) + heads_last<NB / 2>(g, r, code);
+    }
+}
+
 // Two-level form of cdf_search for rows padded to 2^NSTEP = 8 * NB entries
-// (NSTEP 3 .. 6): b = how many block heads row[8], row[16], .. qualify, then
-// n = how many of row[8b + 1 .. 8b + 7] qualify, those 8 entries read as one
-// 16-byte piece (piece(b) returns entries 8b .. 8b + 7, two per dword, the
-// lower index in the low half).  On a non-decreasing padded row the
-// qualifying entries form a prefix, so 8b + n is the k binary lifting finds;
-// the count needs two dependent table reads instead of NSTEP.
+// (NSTEP 3 .. 6): b = the last block head row[8b] that qualifies (row[0] is
+// taken to), then the last qualifying entry of row[8b .. 8b + 7], those 8
+// entries read as one 16-byte piece (piece(b) returns them two per dword,
+// the lower index in the low half); both searches run over registers.  On a
+// non-decreasing padded row the qualifying entries form a prefix, so this is
+// the k binary lifting finds, with two dependent table reads instead of NSTEP.
 template <int NSTEP, class Row, class Piece>
 KVC_HD uint32_t cdf_search_blocks(const Row &row, const Piece &piece, uint32_t A, uint32_t r,
                                   uint32_t code)
 {
     static_assert(NSTEP >= 3 && NSTEP <= 6, "rows of 8 to 64 entries");
     constexpr int NB = 1 << (NSTEP - 3);
-    uint32_t b = 0;
+    uint32_t hd[NB];
+    hd[0] = 0u;  // row[0]: not compared
 #pragma unroll
-    for (int i = 1; i < NB; ++i) b += r * (uint32_t)row[8 * i] <= code ? 1u : 0u;
+    for (int i = 1; i < NB; ++i) hd[i] = (uint32_t)row[8 * i];
+    const uint32_t b = heads_last<NB>(hd, r, code);
     const kvc_u32x4 v = piece(b);
-    uint32_t n = 0;
-#pragma unroll
-    for (int i = 1; i < 8; ++i) n += r * ((v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) <= code ? 1u : 0u;
-    const uint32_t s = 8u * b + n;
+    const uint32_t dv[4] = {v[0], v[1], v[2], v[3]};
+    const uint32_t s = 8u * b + piece_last<8>(dv, r, code);
     return s < A - 1u ? s : A - 1u;
 }
 
