@@ -28,6 +28,7 @@ EXPORTED = (
     "kvc_quantize", "kvc_cdf", "kvc_encode", "kvc_decode", "kvc_dequantize",
     "kvc_container_bytes", "kvc_container_payload_offset", "kvc_serialize", "kvc_deserialize",
     "kvc_int8_quantize", "kvc_int8_dequantize", "kvc_serialize_chunk", "kvc_quantize_levels",
+    "kvc_decode_lanes",
 )
 
 
@@ -65,6 +66,8 @@ def _load():
         lib.kvc_status_string.restype = ctypes.c_char_p
         lib.kvc_status_string.argtypes = [ctypes.c_int]
         lib.kvc_alphabet.restype = I32
+        lib.kvc_decode_lanes.restype = I32
+        lib.kvc_decode_lanes.argtypes = [D]
         for n in ("kvc_n_chunks", "kvc_n_slabs", "kvc_n_streams", "kvc_cdf_bytes",
                   "kvc_scratch_bytes", "kvc_max_payload_bytes"):
             getattr(lib, n).restype = I64
@@ -134,6 +137,8 @@ class Desc:
     def n_slabs(self): return self._q("kvc_n_slabs")
     @property
     def n_streams(self): return self._q("kvc_n_streams")
+    @property
+    def decode_lanes(self): return self._q("kvc_decode_lanes")
     @property
     def cdf_bytes(self): return self._q("kvc_cdf_bytes")
     @property

@@ -105,6 +105,13 @@ int64_t kvc_n_streams(const kvc_desc *desc)
     return rc == KVC_OK ? g.p.n_streams : rc;
 }
 
+int32_t kvc_decode_lanes(const kvc_desc *desc)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    return rc == KVC_OK ? decode_lanes_per_stream(g.p) : rc;
+}
+
 int64_t kvc_cdf_bytes(const kvc_desc *desc)
 {
     Geometry g;

@@ -15,11 +15,6 @@
 #include "lane_coder.h"
 #include "pair_tile.h"
 
-// Launches of at most this many waves use the two-level table search for
-// 64-entry rows.
-#ifndef KVC_DEC_BLOCKS_MAX_WAVES
-#define KVC_DEC_BLOCKS_MAX_WAVES 2048
-#endif
 // Launches of at most this many streams decode with a group of lanes per
 // stream (k_decode_group), for rows of 8 to 64 entries.
 #ifndef KVC_DEC_GROUP_MAX_STREAMS
@@ -480,6 +475,13 @@ static size_t dec_lds_bytes(int A, int CT)
     return sizeof(uint32_t) * (256 + 256 * 17 + n16 + (size_t)CT * A);
 }
 
+int decode_lanes_per_stream(const KParams &p)
+{
+    const int nstep = (int)cdf_nstep((uint32_t)p.A);
+    if (nstep < 3 || nstep > 6 || p.n_streams > KVC_DEC_GROUP_MAX_STREAMS) return 1;
+    return (nstep == 6 || (nstep >= 4 && KVC_DEC_GROUP_LANES == 8)) ? 8 : 4;
+}
+
 // k_decode_group: 4 lanes per stream (8 for 64-entry rows, so a lane's slice is 8 entries).
 static hipError_t launch_decode_group(const uint8_t *payload, int64_t payload_bytes,
                                       const uint64_t *slab_off, const uint16_t *stream_len,
@@ -487,7 +489,7 @@ static hipError_t launch_decode_group(const uint8_t *payload, int64_t payload_by
                                       void *out, int mode, const KParams &p, int32_t *status, bool vec,
                                       int CT, size_t lds, int nstep, hipStream_t stream)
 {
-    const int G = (nstep == 6 || (nstep >= 4 && KVC_DEC_GROUP_LANES == 8)) ? 8 : 4;
+    const int G = decode_lanes_per_stream(p);
     const int64_t bps = (p.Tc + 256 / G - 1) / (256 / G);
     dim3 grid((unsigned)(bps * p.n_slabs)), block(256);
 #define KVC_DECG(V, O, N, GG)                                                                        \
@@ -534,24 +536,22 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
     const size_t lds = dec_lds_bytes(p.A, CT);
     vec = vec && (CT % 16 == 0);
     const int nstep = (int)cdf_nstep((uint32_t)p.A);
-    if (nstep >= 3 && nstep <= 6 && p.n_streams <= KVC_DEC_GROUP_MAX_STREAMS)
+    if (decode_lanes_per_stream(p) > 1)
         return launch_decode_group(payload, payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out,
                                    mode, p, status, vec, CT, lds, nstep, stream);
-    // The two-level search: measured faster for rows of up to 32 entries at any
-    // launch size (most so where few waves cannot hide LDS latency), slower
-    // for 64-entry rows unless the launch is that small.
-    const bool blk = (nstep >= 3 && nstep <= 5) ||
-                     (nstep == 6 && (int64_t)grid.x * 4 <= KVC_DEC_BLOCKS_MAX_WAVES);
+    // Rows of 8 to 64 entries take the two-level search (measured faster than
+    // binary lifting at every launch size since its searches run over
+    // registers); 4-entry and 128- or 256-entry rows binary lifting.
 #define KVC_DEC(V, O, N, B)                                                                          \
     hipLaunchKernelGGL((k_decode<V, O, N, B>), grid, block, lds, stream, payload, payload_bytes,     \
                        slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
 #define KVC_DEC_N(V, O)                                                                              \
     switch (nstep) {                                                                                 \
     case 2: KVC_DEC(V, O, 2, false); break;                                                          \
-    case 3: if (blk) KVC_DEC(V, O, 3, true); else KVC_DEC(V, O, 3, false); break;                    \
-    case 4: if (blk) KVC_DEC(V, O, 4, true); else KVC_DEC(V, O, 4, false); break;                    \
-    case 5: if (blk) KVC_DEC(V, O, 5, true); else KVC_DEC(V, O, 5, false); break;                    \
-    case 6: if (blk) KVC_DEC(V, O, 6, true); else KVC_DEC(V, O, 6, false); break;                    \
+    case 3: KVC_DEC(V, O, 3, true); break;                                                           \
+    case 4: KVC_DEC(V, O, 4, true); break;                                                           \
+    case 5: KVC_DEC(V, O, 5, true); break;                                                           \
+    case 6: KVC_DEC(V, O, 6, true); break;                                                           \
     case 7: KVC_DEC(V, O, 7, false); break;                                                          \
     default: KVC_DEC(V, O, 8, false); break;                                                         \
     }

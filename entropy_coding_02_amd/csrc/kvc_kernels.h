@@ -37,6 +37,9 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
                          uint8_t *payload, int64_t payload_cap, const KParams &p, int32_t *status,
                          bool vec16, hipStream_t stream);
 
+// Lanes per stream launch_decode uses for this shape (1, 4 or 8).
+int decode_lanes_per_stream(const KParams &p);
+
 hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const uint64_t *slab_off,
                          const uint16_t *stream_len, const uint16_t *cdf, const uint16_t *max1,
                          uint8_t *sym_out, void *out, int out_dtype, const KParams &p,

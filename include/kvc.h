@@ -98,6 +98,11 @@ int32_t kvc_alphabet(const kvc_desc *desc);
 int64_t kvc_n_chunks(const kvc_desc *desc);
 int64_t kvc_n_slabs(const kvc_desc *desc);
 int64_t kvc_n_streams(const kvc_desc *desc);
+/* Lanes per stream kvc_decode launches with for this shape: 4 (8 for rows of
+ * 33 to 64 entries) when there are at most 16384 streams and the alphabet pads
+ * to 8 to 64 entries, so that a small launch spreads each stream's search
+ * over several lanes; else 1.  Informational: the output is the same. */
+int32_t kvc_decode_lanes(const kvc_desc *desc);
 int64_t kvc_cdf_bytes(const kvc_desc *desc);
 int64_t kvc_scratch_bytes(const kvc_desc *desc);
 int64_t kvc_max_payload_bytes(const kvc_desc *desc);
@@ -180,7 +185,9 @@ int kvc_encode(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf, vo
  *   sym_out        NULL, or [L][2][T][C] uint8 (device, written): decoded symbols
  *   out            NULL, or [L][2][T][C] of out_dtype (device, written)
  * A stream inconsistent with its CDFs sets KVC_DEV_CORRUPT; C symbols are
- * still written for it.
+ * still written for it.  CDF rows are expected non-decreasing (kvc_quantize,
+ * kvc_cdf and kvc_deserialize guarantee it); on a decreasing row the symbol
+ * is some k in [0, A).
  */
 int kvc_decode(const kvc_desc *desc, const uint8_t *payload, int64_t payload_bytes,
                const uint64_t *slab_off, const uint16_t *stream_len, const uint16_t *cdf,

@@ -57,6 +57,21 @@ def test_sizes_match_layout(lib):
     assert d.n_chunks == 1 and d.n_streams == 16384 and d.cdf_bytes == 4194304
 
 
+@pytest.mark.parametrize("T,bins,lanes", [
+    (256, 32, 4),      # 16384 streams, rows of 32: four lanes per stream
+    (257, 32, 1),      # one stream more: one lane
+    (256, 64, 8),      # rows of 64: eight lanes (slices of 8 entries)
+    (256, 16, 4), (256, 6, 4),
+    (256, 4, 1),       # rows of 4: binary lifting, one lane
+    (256, 256, 1),     # rows of 256
+])
+def test_decode_lanes_rule(lib, T, bins, lanes):
+    d = kvc.Desc(32, 1024, T, np.full((32, 2), bins, np.int32))
+    assert d.decode_lanes == lanes
+    bad = kvc.Desc(1, 0, 64, [[32, 16]])
+    assert lib.kvc_decode_lanes(bad.ref) == kvc.KVC_ERR_ARG
+
+
 @pytest.mark.parametrize("bad", [
     dict(bins=[[3, 16]]), dict(bins=[[2, 16]]), dict(bins=[[258, 16]]), dict(bins=[[31, 16]]),
     dict(n_channels=0), dict(n_channels=16385), dict(chunk_tokens=0), dict(chunk_tokens=65536),

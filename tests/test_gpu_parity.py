@@ -55,6 +55,10 @@ SMALL = {
     "fused_L2_C64_T16421_Tc128": cfg_of(2, 64, 16421, 128, ((0, 1, 32), (1, 2, 16)), seed=12),
     # fused pass at A = 64: a 128 KB LDS histogram
     "fused_70b_shape_T300": kvgen.CONFIGS["c5"].scaled(n_tokens=300),
+    # more than 16384 streams: one lane per stream (the launches above with
+    # few streams decode with a group of lanes per stream), rows of 8 and 16
+    "one_lane_A8_C16_T9000": cfg_of(1, 16, 9000, 256, ((0, 1, 8),), seed=13),
+    "one_lane_A16_C24_T9000": cfg_of(1, 24, 9000, 512, ((0, 1, 16),), seed=14),
 }
 
 
