@@ -9,7 +9,8 @@
 // k_slab_sum:  per-slab sum of the stream lengths.
 // k_scan:      exclusive scan of the slab sums -> slab_off (one block).
 // k_pack:      per 64 streams, their payload offsets, then the wave copies
-//              them from their slots to the payload through an LDS window.
+//              them from their slots to the payload through an LDS window
+//              (whole slot dwords as unaligned dword stores).
 #include "kvc_common.h"
 #include "kvc_kernels.h"
 #include "lane_coder.h"
@@ -195,16 +196,17 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *slab_total, uint6
 // One wavefront per 64 consecutive streams of an encoder block (so 4 blocks
 // of 64 lanes per encoder block).  Lane i first finds stream i's payload
 // offset o (slab offset + the lengths before it).  The wave then walks its
-// streams' destination dwords in rounds of 64: it stages slot dwords
-// [64r - 1, 64r + 64) of all 64 streams in LDS (coalesced loads: the slots
-// are interleaved, lane i's k-th dword next to lane i + 1's), and writes the
-// streams one after the other, lane j taking destination dword 64r + j of
-// the stream: the funnel shift of two staged dwords, stored as one dword
-// when the destination dword lies inside [o, o + len) and byte by byte at
-// the stream's two ends, whose dwords it shares with its neighbours.  One
-// store instruction thus covers 256 contiguous bytes.  Nothing is written at
-// or past payload_cap.
-constexpr int PACK_W = 64;  // destination dwords per stream and round
+// streams' slot dwords in rounds of 64: it stages slot dwords [64r, 64r + 64)
+// of all 64 streams in LDS (coalesced loads: the slots are interleaved, lane
+// i's k-th dword next to lane i + 1's) and writes the streams one after the
+// other, lane j taking slot dword 64r + j.  A slot dword holds 4 stream bytes
+// in stream order, so every whole one goes out as one dword store at byte
+// offset o + 4j, unaligned (gfx9 global stores take any byte address and
+// write only the 4 bytes), and the last len % 4 bytes as byte stores; a
+// store instruction thus covers up to 256 contiguous payload bytes and no
+// byte of a neighbouring stream is touched.  Nothing is written at or past
+// payload_cap.
+constexpr int PACK_W = 64;  // slot dwords per stream and round
 
 __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
                                              const uint16_t *__restrict__ stream_len,
@@ -235,59 +237,47 @@ __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
         if (lane >= off) incl += v;
     }
     const uint64_t o = slab_off[slab] + pre + incl - len;
-    // destination dwords the stream touches, and its slot dwords
-    const uint32_t nd = len ? (uint32_t)(((o + len + 3u) >> 2) - (o >> 2)) : 0u;
-    const int ndw = (int)((len + 3u) >> 2);
-    const uint32_t rounds = (wave_max_u32(nd) + PACK_W - 1) / PACK_W;
+    const int ndw = (int)((len + 3u) >> 2);  // slot dwords holding the stream
+    const int ndw_max = (int)wave_max_u32((uint32_t)ndw);
+    const int rounds = (ndw_max + PACK_W - 1) / PACK_W;
     // slot dword k of stream wq * 64 + i is dword k * 256 + wq * 64 + i of the block's slots
     const uint32_t *srcw = (const uint32_t *)(slots + eb * p.slot_bytes * 256) + wq * 64;
-    const int slot_dw = (int)(p.slot_bytes / 4);
-    const int ndw_max = (int)wave_max_u32((uint32_t)ndw);
     const uint32_t olo = (uint32_t)o, ohi = (uint32_t)(o >> 32);
     const uint64_t cap = (uint64_t)payload_cap;
     // staging: lane l loads 16 bytes = dword k of streams 4m .. 4m + 3 (m = l & 15) for
-    // k = k0 + 4q + (l >> 4), q = 0 .. 16, so one wave-wide load covers 4 slot rows
+    // k = k0 + 4q + (l >> 4), q = 0 .. 15, so one wave-wide load covers 4 slot rows
     const int sg = lane >> 4, sm = lane & 15;
 
-    for (uint32_t r = 0; r < rounds; ++r) {
-        // win[i][u] = slot dword 64r - 1 + u of stream i (u = 0 .. 64; 0 before the stream)
-        const int k0 = (int)r * PACK_W - 1;
-        u32x4 v4[(PACK_W + 4) / 4];
+    for (int r = 0; r < rounds; ++r) {
+        const int k0 = r * PACK_W;
+        u32x4 v4[PACK_W / 4];
 #pragma unroll
-        for (int q = 0; q < (PACK_W + 4) / 4; ++q) {
+        for (int q = 0; q < PACK_W / 4; ++q) {
             const int k = k0 + 4 * q + sg;
-            v4[q] = (k >= 0 && k < ndw_max && k < slot_dw) ? *(const u32x4 *)(srcw + (int64_t)k * 256 + 4 * sm)
-                                                            : u32x4{0, 0, 0, 0};
+            v4[q] = k < ndw_max ? *(const u32x4 *)(srcw + (int64_t)k * 256 + 4 * sm) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int q = 0; q < (PACK_W + 4) / 4; ++q) {
+        for (int q = 0; q < PACK_W / 4; ++q) {
             const int u = 4 * q + sg;
-            if (u <= PACK_W) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) win[(4 * sm + e) * (PACK_W + 1) + u] = v4[q][e];
-            }
+            for (int e = 0; e < 4; ++e) win[(4 * sm + e) * (PACK_W + 1) + u] = v4[q][e];
         }
         __syncthreads();
+        const uint32_t j = (uint32_t)(k0 + lane);  // this lane's slot dword
         for (int i = 0; i < 64; ++i) {
-            const uint32_t nd_i = (uint32_t)__builtin_amdgcn_readlane((int)nd, i);
-            if (r * PACK_W >= nd_i) continue;
-            const uint32_t j = r * PACK_W + (uint32_t)lane;
-            if (j >= nd_i) continue;
+            const uint32_t len_i = (uint32_t)__builtin_amdgcn_readlane((int)len, i);
+            if ((uint32_t)k0 * 4u >= len_i) continue;  // uniform: stream i is done
+            if (4u * j >= len_i) continue;
             const uint64_t o_i = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ohi, i) << 32) |
                                  (uint32_t)__builtin_amdgcn_readlane((int)olo, i);
-            const uint32_t len_i = (uint32_t)__builtin_amdgcn_readlane((int)len, i);
-            const uint32_t lo = win[i * (PACK_W + 1) + lane], hi = win[i * (PACK_W + 1) + lane + 1];
-            const uint32_t a = (uint32_t)o_i & 3u;
-            // destination dword (o_i >> 2) + j holds stream bytes [4j - a, 4j - a + 4)
-            const uint32_t v = a ? (lo >> (32u - 8u * a)) | (hi << (8u * a)) : hi;
-            const uint64_t b = ((o_i >> 2) + j) * 4u;
-            if (b >= o_i && b + 4u <= o_i + len_i && b + 4u <= cap) {
-                *(uint32_t *)(payload + b) = v;
+            const uint32_t v = win[i * (PACK_W + 1) + lane];
+            const uint64_t b = o_i + 4u * j;  // stream bytes [4j, 4j + 4) go here
+            const uint32_t nb = min(len_i - 4u * j, 4u);
+            if (nb == 4u && b + 4u <= cap) {
+                __builtin_memcpy(payload + b, &v, 4);
             } else {
-                for (uint32_t q = 0; q < 4; ++q) {
-                    const uint64_t bq = b + q;
-                    if (bq >= o_i && bq < o_i + len_i && bq < cap) payload[bq] = (uint8_t)(v >> (8u * q));
-                }
+                for (uint32_t q = 0; q < nb; ++q)
+                    if (b + q < cap) payload[b + q] = (uint8_t)(v >> (8u * q));
             }
         }
         __syncthreads();
