@@ -21,18 +21,17 @@ namespace {
 // One lane per stream, 256 tokens of one slab per block.  The slab is walked
 // in tiles of CT channels: at each tile boundary the block stages the tile's
 // CDF rows as packed (start, frequency) pairs in LDS.  When C % 16 == 0 the
-// symbols of the block's 256 tokens are staged too, in tiles of SW = 64
-// channels (coalesced 16-byte loads; SW is a multiple of CT), so each
-// 128-byte line of a token row is fetched in two halves rather than in
-// 32-byte pieces.  The coding loop then reads only LDS: 16 symbols per
+// symbols of the block's 256 tokens are staged too, in tiles of SW channels
+// (coalesced 16-byte loads; SW is a multiple of CT): 64, so a 128-byte line
+// of a token row is fetched in two halves rather than in 32-byte pieces, or
+// 128 (whole lines) for launches of few streams, where the LDS it takes
+// costs no occupancy that matters.  The coding loop then reads only LDS: 16 symbols per
 // ds_read_b128, pair lookups in batches of 8.  All lanes of a wave read the
 // same pair row at the same step (broadcast or distinct banks); the symbol
 // rows have a 16-byte-padded stride that spreads lanes over all banks.
 // Without global loads in the loop, the lanes' byte stores never make it
 // wait.
-constexpr int ENC_SW = 64;  // symbol tile width (channels)
-
-template <bool VEC16, int PER>
+template <bool VEC16, int PER, int ENC_SW>
 __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
                                                 const uint16_t *__restrict__ cdf,
                                                 uint8_t *__restrict__ slots,
@@ -61,13 +60,13 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
     enc_init(e);
     // Tiles arrive in registers while the previous ones are coded, and go
     // into LDS between two barriers.  Symbol pieces: 16 bytes of a token row,
-    // SW / 16 = 4 per row, so 4 per thread.
+    // SW / 16 per row, and as many per thread (256 rows, 256 threads).
     PairTile<PER> pt;
-    u32x4 sv[4];
     constexpr int per_row = ENC_SW / 16;
+    u32x4 sv[per_row];
     auto load_syms = [&](int s0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < per_row; ++i) {
             const int ch = (int)threadIdx.x + 256 * i;
             const int r = ch / per_row, part = ch - r * per_row;
             const int tok = tb * 256 + r, cc = s0 + part * 16;
@@ -77,7 +76,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
     };
     auto store_syms = [&]() {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < per_row; ++i) {
             const int ch = (int)threadIdx.x + 256 * i;
             const int r = ch / per_row, part = ch - r * per_row;
             *(lds_u32x4 *)(stile + r * sstride + part * 16) = sv[i];
@@ -288,25 +287,27 @@ __global__ void k_zero_u64(uint64_t *dst) { *dst = 0; }
 
 }  // namespace
 
-// Channels per pair tile: a power of two from 16 to 64, at most 1024 pairs
-// (4 KB) when A allows, so the coding loop's 16-symbol steps and the 64-channel
-// symbol tiles both split into whole tiles.
-// Launches of at most this many streams stage wider CDF tiles.
+// Launches of at most this many streams stage wider CDF and symbol tiles.
 #ifndef KVC_ENC_WIDE_MAX_STREAMS
 #define KVC_ENC_WIDE_MAX_STREAMS 32768
 #endif
 
-// Channels per tile (a power of two, 16 to ENC_SW).  With few streams a tile
-// of 16 channels is coded in less time than its successor's rows take to
-// arrive from memory, so small launches stage up to ENC_SW channels (up to 8
-// pairs per thread); large ones keep the tile at one or two pairs per thread.
+// Symbol tile width: 128 channels for launches of few streams, else 64.
+static int enc_symbol_tile(int64_t n_streams) { return n_streams <= KVC_ENC_WIDE_MAX_STREAMS ? 128 : 64; }
+
+// Channels per tile (a power of two, 16 to the symbol tile width).  With few
+// streams a tile of 16 channels is coded in less time than its successor's
+// rows take to arrive from memory, so small launches stage up to 128
+// channels (up to 8 pairs per thread); large ones keep the tile at one or two
+// pairs per thread.
 static int enc_tile_channels(int A, int64_t n_streams)
 {
+    const int sw = enc_symbol_tile(n_streams);
     int ct = 16;
     if (n_streams <= KVC_ENC_WIDE_MAX_STREAMS)
-        while (ct < ENC_SW && 2 * ct * (A / 2) <= 8 * 256) ct *= 2;
+        while (ct < sw && 2 * ct * (A / 2) <= 8 * 256) ct *= 2;
     else
-        while (ct < ENC_SW && 2 * ct * A <= 1024) ct *= 2;
+        while (ct < sw && 2 * ct * A <= 1024) ct *= 2;
     return ct;
 }
 
@@ -327,16 +328,23 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
     const int CT = enc_tile_channels(p.A, p.n_streams);
     const size_t lds_pairs = (size_t)CT * p.A * sizeof(uint32_t);
     const int per = (CT * (p.A / 2) + 255) / 256;  // pairs staged per thread
-#define KVC_ENC(V, P, L)                                                                             \
-    hipLaunchKernelGGL((k_encode<V, P>), grid, dim3(256), L, stream, sym, cdf, slots, stream_len, p, CT)
-    const size_t lds_syms = lds_pairs + 256 * (size_t)(ENC_SW + 16);
-    if (vec16) {
-        if (per <= 2) KVC_ENC(true, 2, lds_syms);
-        else KVC_ENC(true, 8, lds_syms);
-    } else {
-        if (per <= 2) KVC_ENC(false, 2, lds_pairs);
-        else KVC_ENC(false, 8, lds_pairs);
+    const int sw = enc_symbol_tile(p.n_streams);
+#define KVC_ENC(V, P, S, L)                                                                          \
+    hipLaunchKernelGGL((k_encode<V, P, S>), grid, dim3(256), L, stream, sym, cdf, slots, stream_len, p, \
+                       CT)
+#define KVC_ENC_S(S)                                                                                 \
+    {                                                                                                \
+        const size_t lds_syms = lds_pairs + 256 * (size_t)(S + 16);                                  \
+        if (vec16) {                                                                                 \
+            if (per <= 2) KVC_ENC(true, 2, S, lds_syms);                                             \
+            else KVC_ENC(true, 8, S, lds_syms);                                                      \
+        } else {                                                                                     \
+            if (per <= 2) KVC_ENC(false, 2, S, lds_pairs);                                           \
+            else KVC_ENC(false, 8, S, lds_pairs);                                                    \
+        }                                                                                            \
     }
+    if (sw == 128) KVC_ENC_S(128) else KVC_ENC_S(64)
+#undef KVC_ENC_S
 #undef KVC_ENC
     hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
                        slab_total, p);
