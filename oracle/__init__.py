@@ -14,7 +14,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvc_oracle.c")
-_SRCS = [_SRC, os.path.join(_HERE, "kvc_container.c"), os.path.join(_HERE, "kvc_int8.c")]
+_SRCS = [_SRC, os.path.join(_HERE, "kvc_container.c"), os.path.join(_HERE, "kvc_int8.c"),
+         os.path.join(_HERE, "kvc_delta.c")]
 _LIB_PATH = os.path.join(_HERE, "liborc.so")
 
 ORC_OK, ORC_ERR_ARG, ORC_ERR_NONFINITE, ORC_ERR_CAPACITY, ORC_ERR_CORRUPT = 0, -1, -2, -3, -4
@@ -59,6 +60,10 @@ def _load():
         lib.orc_decode.argtypes = [I32, I32, I64, I32, I32, P, P, P, P, P]
         lib.orc_dequantize.restype = ctypes.c_int
         lib.orc_dequantize.argtypes = [I32, I32, I64, P, P, P, P, I32]
+        lib.orc_delta_forward.restype = ctypes.c_int
+        lib.orc_delta_forward.argtypes = [I32, I32, I64, I32, I32, P, P, P]
+        lib.orc_delta_inverse.restype = ctypes.c_int
+        lib.orc_delta_inverse.argtypes = [I32, I32, I64, I32, I32, P]
         lib.orc_container_bytes.restype = I64
         lib.orc_container_bytes.argtypes = [I32, I32, I64, I32, P, I64]
         lib.orc_container_payload_offset.restype = I64
@@ -254,6 +259,27 @@ def deserialize(data: np.ndarray, L: int, C: int, T: int, Tc: int, bins):
         raise OracleError("orc_deserialize", rc)
     return dict(cdf=cdf_tab, max1=max1, stream_len=stream_len, slab_off=slab_off,
                 payload_bytes=int(pb.value), payload_offset=container_payload_offset(L, C, T, Tc, bins))
+
+
+def delta_forward(kv: np.ndarray, bins: np.ndarray, Tc: int, G: int) -> np.ndarray:
+    """Token-delta transform (anchors every G chunk-relative tokens): fp16 bits [L][2][T][C]."""
+    L, _, T, C = kv.shape
+    out = np.empty(kv.shape, dtype=np.uint16)
+    rc = _load().orc_delta_forward(L, C, T, Tc, G, _ptr(np.ascontiguousarray(bins, dtype=np.int32)),
+                                   _ptr(np.ascontiguousarray(kv, dtype=np.uint16)), _ptr(out))
+    if rc != ORC_OK:
+        raise OracleError("orc_delta_forward", rc)
+    return out
+
+
+def delta_inverse(y: np.ndarray, Tc: int, G: int) -> np.ndarray:
+    """Inverse of delta_forward on a decoded fp16 tensor (a new array)."""
+    L, _, T, C = y.shape
+    out = np.array(y, dtype=np.uint16, copy=True, order="C")
+    rc = _load().orc_delta_inverse(L, C, T, Tc, G, _ptr(out))
+    if rc != ORC_OK:
+        raise OracleError("orc_delta_inverse", rc)
+    return out
 
 
 def int8_quantize(kv: np.ndarray, g: int):

@@ -65,6 +65,11 @@ int orc_deserialize(int32_t L, int32_t C, int64_t T, int32_t Tc, const int32_t *
                     uint16_t *stream_len, uint64_t *slab_off, int64_t *payload_bytes);
 
 /* 8-bit comparator quantizer, [KVM] 四 (kvc_int8.c): groups of g channels. */
+/* Token-delta coding with anchors every G chunk-relative tokens (kvc_delta.c). */
+int orc_delta_forward(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t G, const int32_t *bins,
+                      const uint16_t *kv, uint16_t *out);
+int orc_delta_inverse(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t G, uint16_t *y);
+
 int orc_int8_quantize(int32_t L, int32_t C, int64_t T, int32_t g, const uint16_t *kv, uint8_t *q,
                       float *scale, uint8_t *zp);
 int orc_int8_dequantize(int32_t L, int32_t C, int64_t T, int32_t g, const uint8_t *q,
