@@ -28,7 +28,7 @@ EXPORTED = (
     "kvc_quantize", "kvc_cdf", "kvc_encode", "kvc_decode", "kvc_dequantize",
     "kvc_container_bytes", "kvc_container_payload_offset", "kvc_serialize", "kvc_deserialize",
     "kvc_int8_quantize", "kvc_int8_dequantize", "kvc_serialize_chunk", "kvc_quantize_levels",
-    "kvc_decode_lanes",
+    "kvc_decode_lanes", "kvc_delta_forward", "kvc_delta_inverse",
 )
 
 
@@ -68,6 +68,10 @@ def _load():
         lib.kvc_alphabet.restype = I32
         lib.kvc_decode_lanes.restype = I32
         lib.kvc_decode_lanes.argtypes = [D]
+        lib.kvc_delta_forward.restype = ctypes.c_int
+        lib.kvc_delta_forward.argtypes = [D, I32, P, P, P, P]
+        lib.kvc_delta_inverse.restype = ctypes.c_int
+        lib.kvc_delta_inverse.argtypes = [D, I32, P, P]
         for n in ("kvc_n_chunks", "kvc_n_slabs", "kvc_n_streams", "kvc_cdf_bytes",
                   "kvc_scratch_bytes", "kvc_max_payload_bytes"):
             getattr(lib, n).restype = I64
@@ -264,6 +268,15 @@ def kvc_int8_dequantize(desc: Desc, group: int, q, scale, zero_point, out, strea
     _check("kvc_int8_dequantize", _load().kvc_int8_dequantize(desc.ref, group, _ptr(q), _ptr(scale),
                                                               _ptr(zero_point), _ptr(out),
                                                               _stream(stream)))
+
+
+def kvc_delta_forward(desc: Desc, anchor_tokens: int, kv, delta, dev_status=None, stream=None):
+    _check("kvc_delta_forward", _load().kvc_delta_forward(desc.ref, anchor_tokens, _ptr(kv), _ptr(delta),
+                                                          _ptr(dev_status), _stream(stream)))
+
+
+def kvc_delta_inverse(desc: Desc, anchor_tokens: int, y, stream=None):
+    _check("kvc_delta_inverse", _load().kvc_delta_inverse(desc.ref, anchor_tokens, _ptr(y), _stream(stream)))
 
 
 # --------------------------------------------------------------- convenience

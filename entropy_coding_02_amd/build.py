@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvc.so")
 SOURCES = ["kvc_abi.hip", "kvc_quantize.hip", "kvc_cdf.hip", "kvc_encode.hip", "kvc_decode.hip",
-           "kvc_container.hip", "kvc_int8.hip"]
+           "kvc_container.hip", "kvc_int8.hip", "kvc_delta.hip"]
 ARCH = os.environ.get("KVC_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -368,4 +368,31 @@ int kvc_int8_dequantize(const kvc_desc *desc, int32_t group, const uint8_t *q, c
                                                 (hipStream_t)stream));
 }
 
+int kvc_delta_forward(const kvc_desc *desc, int32_t anchor_tokens, const uint16_t *kv, uint16_t *delta,
+                      int32_t *dev_status, void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    if (anchor_tokens < 1 || anchor_tokens > 65535) return KVC_ERR_ARG;
+    if (g.p.n_rows == 0) return KVC_OK;
+    if (!kv || !delta || !aligned(kv, 2) || !aligned(delta, 2) || (dev_status && !aligned(dev_status, 4)))
+        return KVC_ERR_ARG;
+    const bool vec = g.p.C % 8 == 0 && g.p.C <= 1024 && aligned(kv, 16) && aligned(delta, 16);
+    return launch_status(launch_delta_forward(kv, delta, g.p, anchor_tokens, vec, dev_status,
+                                              (hipStream_t)stream));
+}
+
+int kvc_delta_inverse(const kvc_desc *desc, int32_t anchor_tokens, uint16_t *y, void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    if (anchor_tokens < 1 || anchor_tokens > 65535) return KVC_ERR_ARG;
+    if (g.p.n_rows == 0) return KVC_OK;
+    if (!y || !aligned(y, 2)) return KVC_ERR_ARG;
+    const bool vec = g.p.C % 8 == 0 && g.p.C <= 1024 && aligned(y, 16);
+    return launch_status(launch_delta_inverse(y, g.p, anchor_tokens, vec, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -80,6 +80,11 @@ hipError_t launch_deserialize(const uint8_t *in, int64_t in_bytes, uint16_t *cdf
                               int32_t *status, hipStream_t stream);
 
 // 8-bit comparator quantizer (kvc_int8.hip).
+// Token-delta coding (kvc_delta.hip), anchors every G chunk-relative tokens.
+hipError_t launch_delta_forward(const uint16_t *kv, uint16_t *out, const KParams &p, int G, bool vec,
+                                int32_t *status, hipStream_t stream);
+hipError_t launch_delta_inverse(uint16_t *y, const KParams &p, int G, bool vec, hipStream_t stream);
+
 hipError_t launch_int8_quantize(const uint16_t *kv, uint8_t *q, float *scale, uint8_t *zp,
                                 int64_t n_rows, int C, int g, bool vec, int32_t *status,
                                 hipStream_t stream);

@@ -278,6 +278,28 @@ int kvc_deserialize(const kvc_desc *desc, const uint8_t *in, int64_t in_bytes, u
                     void *stream);
 
 /*
+ * Token-delta coding with anchors, the step before quantization in the
+ * CacheGen write-up ([CG] 1.2 point 1: neighbouring tokens' K/V are close, so
+ * differences rather than raw values are coded; [CG] 2.3 step 1 names the
+ * anchor-based form).  Anchors are the tokens at chunk-relative positions 0,
+ * G, 2G, ... (G = anchor_tokens, 1..65535; every chunk stands alone).
+ *   kvc_delta_forward: an anchor row is kept; any other row x becomes
+ *     fp16(fp32(x) - fp32(xa_hat)), xa_hat = the codec's reconstruction of its
+ *     anchor row (desc's bins: max-abs quantization, then fp16(fp32(q - MAX) /
+ *     MAX * max1), as kvc_decode writes it).  The result goes through
+ *     kvc_quantize / kvc_encode unchanged.
+ *   kvc_delta_inverse: on the tensor kvc_decode wrote (fp16), every
+ *     non-anchor row y becomes fp16(fp32(y) + fp32(y_anchor)), in place.
+ *   kv, delta, y  [L][2][T][C] fp16 (device); kv and delta may be the same
+ *                 buffer (else they must not overlap)
+ * A row holding Inf or NaN, or a delta past the fp16 range, sets
+ * KVC_DEV_NONFINITE (kvc_delta_forward); such outputs are unspecified.
+ */
+int kvc_delta_forward(const kvc_desc *desc, int32_t anchor_tokens, const uint16_t *kv, uint16_t *delta,
+                      int32_t *dev_status, void *stream);
+int kvc_delta_inverse(const kvc_desc *desc, int32_t anchor_tokens, uint16_t *y, void *stream);
+
+/*
  * The 8-bit comparator: the per-channel INT8 KV quantizer of the page
  * "大模型推理的KV Cache管理：从内存碎片到前缀缓存的优化实战" (KV cache management for LLM
  * inference), section 四, against which the codec's size and error are
