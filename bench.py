@@ -254,6 +254,62 @@ def levels_leg(kvc, cfg, kvt, stream, steps):
             "level_by_level_ms": round(statistics.median(sep), 4)}
 
 
+def delta_leg(kvc, d, buf, cfg, kvt, stream, steps):
+    """Token-delta coding (anchors every G chunk-relative tokens) in front of
+    the codec: container size and relative RMS error after forward, encode,
+    decode and inverse, for a few anchor spacings at the workload's bins and
+    one at halved bins, next to the plain codec; forward and inverse times
+    (HIP events, median of `steps`).  Outside the timed step; reuses the
+    step's buffers."""
+    import numpy as np
+    import torch
+    n = cfg.n_elements
+    x = kvt.view(torch.float16).reshape(-1)
+    dlt = torch.empty_like(kvt)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def run(desc, G):
+        b = dataclasses.replace(buf, desc=desc)
+        if G:
+            kvc.kvc_delta_forward(desc, G, kvt, dlt, st, stream)
+        kvc.encode(b, dlt if G else kvt, stream=stream)
+        kvc.decode(b, stream=stream)
+        if G:
+            kvc.kvc_delta_inverse(desc, G, b.out, stream)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0 and int(b.dev_status.item()) == 0, "device status flags set in the delta leg"
+        nb = desc.container_bytes(int(b.slab_off[desc.n_slabs].item()))
+        return {"container_bits_per_elem": round(8 * nb / n, 4),
+                "rel_rmse": round(rel_rmse_f16(b.out[:n].view(torch.float16), x), 6)}
+
+    L = cfg.n_layers
+    b0 = cfg.bins()
+    half = np.maximum(b0 // 2, 4)
+    half = half + (half % 2)
+    d_half = kvc.Desc(L, cfg.n_channels, cfg.n_tokens, half, cfg.chunk_tokens)
+    out = {"plain": run(d, 0), "anchors": []}
+    for G, desc, tag in ((2, d, b0), (4, d, b0), (8, d, b0), (4, d_half, half)):
+        r = run(desc, G)
+        r.update(anchor_tokens=G, bins=sorted({int(v) for v in tag.reshape(-1)}, reverse=True))
+        out["anchors"].append(r)
+    fw, iv = [], []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        kvc.kvc_delta_forward(d, 4, kvt, dlt, st, stream)
+        e[1].record(stream)
+        kvc.kvc_delta_inverse(d, 4, dlt, stream)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        fw.append(e[0].elapsed_time(e[1]))
+        iv.append(e[1].elapsed_time(e[2]))
+    out["forward_ms"] = round(statistics.median(fw), 4)
+    out["inverse_ms"] = round(statistics.median(iv), 4)
+    out["forward_GBps"] = round(4 * n / (out["forward_ms"] * 1e-3) / 1e9, 1)  # 2 B in + 2 B out
+    del dlt
+    return out
+
+
 def cpu_baseline(cfg, kv_np):
     """The oracle, as it stands, over a bounded sample: whole slabs of the
     workload (all of it when it is small), single-threaded."""
@@ -397,6 +453,7 @@ def main():
     res["int8_comparator"] = int8_leg(kvc, d, kvt, buf, cfg, stream, args.steps,
                                       res["container"]["bits_per_elem"])
     res["quality_levels"] = levels_leg(kvc, cfg, kvt, stream, args.steps)
+    res["token_delta"] = delta_leg(kvc, d, buf, cfg, kvt, stream, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, kv_np)
     print(json.dumps(res), flush=True)
