@@ -15,6 +15,8 @@ typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 // Everything a kernel needs to know about the problem, passed by value.
 // Slab s = (chunk j, layer l, K|V kv) with lk = 2*l + kv; j = s / (2L).

@@ -7,7 +7,8 @@
 //     lut[q] = fp32(q - MAX) / MAX        (one IEEE division per entry)
 // in LDS, and each lane then decodes its C symbols: a binary search of the
 // channel's CDF row for the largest k with r*cdf_k <= code, the interval
-// update, byte refill, and y = lut[s] * max1 written as fp16 or fp32.
+// update, byte refill, and y = lut[s] * max1 written as fp16 or fp32 (lut[s]
+// is staged next to each (start, frequency) pair, so one read gives both).
 // Because fl(fl(q - MAX) / MAX) is exactly the table entry, the fused output
 // equals the separate dequantization bit for bit.
 #include "kvc_common.h"
@@ -34,7 +35,7 @@ enum { OUT_F16 = 1, OUT_F32 = 2, OUT_SYM = 4 };
 
 // BLK: the two-level table search (two dependent LDS reads per symbol
 // instead of NSTEP, a few more VALU operations).
-template <bool VEC, int OUT, int NSTEP, bool BLK>
+template <bool VEC, int OUT, int NSTEP, bool BLK, bool PAD = true>
 __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payload,
                                                 int64_t payload_bytes,
                                                 const uint64_t *__restrict__ slab_off,
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
                                                 uint8_t *__restrict__ sym_out, void *__restrict__ out,
                                                 KParams p, int32_t *status, int CT)
 {
-    // LDS: lut[256] f32 | ring[256][17] u32 | rows16 [CT][P2] u16 | pairs [CT][A] u32
+    // LDS: lut[256] f32 | ring[256][17] u32 | rows16 [CT][P2] u16 | (pair, lut) [CT][A] u32x2
     extern __shared__ uint32_t lds[];
     __shared__ uint32_t s_red[4];
     constexpr uint32_t P2 = 1u << NSTEP;  // search row length: A padded to a power of two
@@ -106,14 +107,22 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
     uint8_t *so = (OUT & OUT_SYM) ? sym_out + row * C : nullptr;
     const uint16_t *srows = cdf + slab * C * A;
     const int ntiles = (C + CT - 1) / CT;
-    auto decode1 = [&](int cl) -> uint32_t {
+    // search the row, then one 8-byte read: the symbol's (start, frequency) and
+    // its dequantization value lv
+    auto decode1 = [&](int cl, float &lv) -> uint32_t {
+        const uint32_t r = d.range >> 16;
+        uint32_t s;
         if constexpr (BLK) {
             const lds_u16 *rowp = r16 + cl * P2;
             auto piece = [&](uint32_t b) -> kvc_u32x4 { return *(const lds_u32x4 *)(rowp + 8u * b); };
-            return dec_symbol_blocks<NSTEP>(d, rowp, piece, pr + cl * A, (uint32_t)A, &bad);
+            s = cdf_search_blocks<NSTEP, PAD>(rowp, piece, (uint32_t)A, r, d.code);
         } else {
-            return dec_symbol<NSTEP>(d, r16 + cl * P2, pr + cl * A, (uint32_t)A, &bad);
+            s = cdf_search<NSTEP>(r16 + cl * P2, (uint32_t)A, r, d.code);
         }
+        const u32x2 e = *(const lds_u32x2 *)(pr + 2 * (cl * A + (int)s));
+        bad |= dec_advance(d, r, e.x & 0xFFFFu, e.x >> 16);
+        lv = __uint_as_float(e.y);
+        return s;
     };
 
     // the tile's rows arrive in registers while the previous tile is decoded,
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
         __syncthreads();  // all waves are done with the previous tile
-        pt.store(pr, CT, A, r16, (int)P2);
+        pt.store_with(pr, CT, A, r16, (int)P2, (const uint32_t *)lut);
         __syncthreads();
         if (it + 1 < ntiles) pt.load(srows, c0 + CT, CT, C, A);
         if (!active) continue;
@@ -153,10 +162,11 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         if ((i & 1) == 0) dec_refill(d, in);
-                        const uint32_t s = decode1(cg - c0 + i);
+                        float lv;
+                        const uint32_t s = decode1(cg - c0 + i, lv);
                         sw[i >> 2] |= s << (8 * (i & 3));
                         if constexpr (ODT >= 0) {
-                            const float y = lut[s] * m;
+                            const float y = lv * m;
                             if constexpr (ODT == ODT_F16) {
                                 if (i & 1)
                                     hw[gi * 4 + (i >> 1)] = kvc_f2h2(ylo, y);
@@ -180,10 +190,11 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
             for (int c = c0; c < c1; ++c) {
                 if ((c & 7) == 0) in.group();
                 if ((c & 1) == 0) dec_refill(d, in);
-                const uint32_t s = decode1(c - c0);
+                float lv;
+                const uint32_t s = decode1(c - c0, lv);
                 if constexpr ((OUT & OUT_SYM) != 0) so[c] = (uint8_t)s;
                 if constexpr (ODT >= 0) {
-                    const float y = lut[s] * m;
+                    const float y = lv * m;
                     if constexpr (ODT == ODT_F16)
                         ((uint16_t *)out)[row * C + c] = (uint16_t)kvc_f2h(y);
                     else
@@ -296,14 +307,13 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
     const uint16_t *srows = cdf + slab * C * A;
     const int ntiles = (C + CT - 1) / CT;
     const uint32_t amax = (uint32_t)A - 1u;
-    auto decode1 = [&](int cl) -> uint32_t {
+    auto decode1 = [&](int cl, float &lv) -> uint32_t {
         const lds_u16 *sp = r16 + cl * (int)P2 + q * E;
         uint32_t e2[E / 2];
         if constexpr (E == 2) {
             e2[0] = *(const lds_u32 *)sp;
         } else if constexpr (E == 4) {
-            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            const u32x2 v = *(const __attribute__((address_space(3))) u32x2 *)sp;
+            const u32x2 v = *(const lds_u32x2 *)sp;
             e2[0] = v.x;
             e2[1] = v.y;
         } else {
@@ -319,13 +329,14 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
         const uint32_t r = d.range >> 16;
         // qualifying entries of the slice: none, or a prefix ending at piece_last
         // (computed either way; the empty asm keeps it out of a branch)
-        uint32_t n = piece_last<E>(e2, r, d.code) + 1u;
+        uint32_t n = piece_last<E>(0u, e2, r, d.code) + 1u;
         __asm__("" : "+v"(n));
         n = r * (e2[0] & 0xFFFFu) <= d.code ? n : 0u;
         n = group_sum<G>(n);
         const uint32_t s = min(n - 1u, amax);  // n = 0 only for a row with cdf_0 > 0
-        const uint32_t pp = pr[cl * A + s];
-        bad |= dec_advance(d, r, pp & 0xFFFFu, pp >> 16);
+        const u32x2 e = *(const lds_u32x2 *)(pr + 2 * (cl * A + (int)s));
+        bad |= dec_advance(d, r, e.x & 0xFFFFu, e.x >> 16);
+        lv = __uint_as_float(e.y);
         return s;
     };
 
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
         __syncthreads();
-        pt.store(pr, CT, A, r16, (int)P2);
+        pt.store_with(pr, CT, A, r16, (int)P2, (const uint32_t *)lut);
         __syncthreads();
         if (it + 1 < ntiles) pt.load(srows, c0 + CT, CT, C, A);
         if (!active) continue;
@@ -356,10 +367,11 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         if ((i & 1) == 0) dec_refill(d, in);
-                        const uint32_t s = decode1(cg - c0 + i);
+                        float lv;
+                        const uint32_t s = decode1(cg - c0 + i, lv);
                         sw[i >> 2] |= s << (8 * (i & 3));
                         if constexpr (ODT >= 0) {
-                            const float y = lut[s] * m;
+                            const float y = lv * m;
                             if constexpr (ODT == ODT_F16) {
                                 if (i & 1)
                                     hw[gi * 4 + (i >> 1)] = kvc_f2h2(ylo, y);
@@ -406,11 +418,12 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
             for (int c = c0; c < c1; ++c) {
                 if ((c & 7) == 0) in.group();
                 if ((c & 1) == 0) dec_refill(d, in);
-                const uint32_t s = decode1(c - c0);
+                float lv;
+                const uint32_t s = decode1(c - c0, lv);
                 if (q == c % G) {
                     if constexpr ((OUT & OUT_SYM) != 0) so[c] = (uint8_t)s;
                     if constexpr (ODT >= 0) {
-                        const float y = lut[s] * m;
+                        const float y = lv * m;
                         if constexpr (ODT == ODT_F16)
                             ((uint16_t *)out)[row * C + c] = (uint16_t)kvc_f2h(y);
                         else
@@ -472,7 +485,7 @@ static size_t dec_lds_bytes(int A, int CT)
     int P2 = 1;
     while (P2 < A) P2 <<= 1;
     const size_t n16 = ((size_t)CT * P2 + 1) / 2;
-    return sizeof(uint32_t) * (256 + 256 * 17 + n16 + (size_t)CT * A);
+    return sizeof(uint32_t) * (256 + 256 * 17 + n16 + 2 * (size_t)CT * A);
 }
 
 int decode_lanes_per_stream(const KParams &p)
@@ -545,13 +558,20 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
 #define KVC_DEC(V, O, N, B)                                                                          \
     hipLaunchKernelGGL((k_decode<V, O, N, B>), grid, block, lds, stream, payload, payload_bytes,     \
                        slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
+#define KVC_DECB(V, O, N)                                                                            \
+    if (p.A == (1 << N))                                                                             \
+        hipLaunchKernelGGL((k_decode<V, O, N, true, false>), grid, block, lds, stream, payload,      \
+                           payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT); \
+    else                                                                                             \
+        hipLaunchKernelGGL((k_decode<V, O, N, true, true>), grid, block, lds, stream, payload,       \
+                           payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
 #define KVC_DEC_N(V, O)                                                                              \
     switch (nstep) {                                                                                 \
     case 2: KVC_DEC(V, O, 2, false); break;                                                          \
-    case 3: KVC_DEC(V, O, 3, true); break;                                                           \
-    case 4: KVC_DEC(V, O, 4, true); break;                                                           \
-    case 5: KVC_DEC(V, O, 5, true); break;                                                           \
-    case 6: KVC_DEC(V, O, 6, true); break;                                                           \
+    case 3: KVC_DECB(V, O, 3); break;                                                                \
+    case 4: KVC_DECB(V, O, 4); break;                                                                \
+    case 5: KVC_DECB(V, O, 5); break;                                                                \
+    case 6: KVC_DECB(V, O, 6); break;                                                                \
     case 7: KVC_DEC(V, O, 7, false); break;                                                          \
     default: KVC_DEC(V, O, 8, false); break;                                                         \
     }
@@ -571,6 +591,7 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
     }
 #undef KVC_DEC_M
 #undef KVC_DEC_N
+#undef KVC_DECB
 #undef KVC_DEC
     return hipGetLastError();
 }

@@ -374,36 +374,37 @@ KVC_HD uint32_t cdf_search(const Row &row, uint32_t A, uint32_t r, uint32_t code
 
 // Index of the last qualifying entry (r * e <= code) of a non-decreasing run
 // of E entries (E a power of two, 2 to 16) packed two per dword (entry 2j in
-// the low half of d[j]), given that entry 0 qualifies: a binary search over
-// values already in registers (log2 E compares, each halving the run with
-// selects).
+// the low half of d[j]), given that entry 0 qualifies, appended to idx: the
+// result is idx * E + that index.  A binary search over values already in
+// registers: log2 E compares, each halving the run with selects and adding
+// one bit (idx = 2 idx + bit, one add with carry).
 template <int E>
-KVC_HD uint32_t piece_last(const uint32_t *d, uint32_t r, uint32_t code)
+KVC_HD uint32_t piece_last(uint32_t idx, const uint32_t *d, uint32_t r, uint32_t code)
 {
     if constexpr (E == 2) {
-        return r * (d[0] >> 16) <= code ? 1u : 0u;
+        return 2u * idx + (r * (d[0] >> 16) <= code ? 1u : 0u);
     } else {
         constexpr int H = E / 4;  // dwords in each half
         const bool a = r * (d[H] & 0xFFFFu) <= code;  // entry E / 2
         uint32_t h[H];
 #pragma unroll
         for (int k = 0; k < H; ++k) h[k] = a ? d[H + k] : d[k];
-        return (a ? (uint32_t)(E / 2) : 0u) + piece_last<E / 2>(h, r, code);
+        return piece_last<E / 2>(2u * idx + (a ? 1u : 0u), h, r, code);
     }
 }
 
 // The same over NB values one per register (h[0] is taken to qualify).
 template <int NB>
-KVC_HD uint32_t heads_last(const uint32_t *h, uint32_t r, uint32_t code)
+KVC_HD uint32_t heads_last(uint32_t idx, const uint32_t *h, uint32_t r, uint32_t code)
 {
     if constexpr (NB == 1) {
-        return 0u;
+        return idx;
     } else {
         const bool a = r * h[NB / 2] <= code;
         uint32_t g[NB / 2];
 #pragma unroll
         for (int k = 0; k < NB / 2; ++k) g[k] = a ? h[NB / 2 + k] : h[k];
-        return (a ? (uint32_t)(NB / 2) : 0u) + heads_last<NB / 2>(g, r, code);
+        return heads_last<NB / 2>(2u * idx + (a ? 1u : 0u), g, r, code);
     }
 }
 
@@ -414,7 +415,8 @@ KVC_HD uint32_t heads_last(const uint32_t *h, uint32_t r, uint32_t code)
 // the lower index in the low half); both searches run over registers.  On a
 // non-decreasing padded row the qualifying entries form a prefix, so this is
 // the k binary lifting finds, with two dependent table reads instead of NSTEP.
-template <int NSTEP, class Row, class Piece>
+// PAD: the row has padding (A < 2^NSTEP), so the result is clamped to A - 1.
+template <int NSTEP, bool PAD, class Row, class Piece>
 KVC_HD uint32_t cdf_search_blocks(const Row &row, const Piece &piece, uint32_t A, uint32_t r,
                                   uint32_t code)
 {
@@ -424,11 +426,12 @@ KVC_HD uint32_t cdf_search_blocks(const Row &row, const Piece &piece, uint32_t A
     hd[0] = 0u;  // row[0]: not compared
 #pragma unroll
     for (int i = 1; i < NB; ++i) hd[i] = (uint32_t)row[8 * i];
-    const uint32_t b = heads_last<NB>(hd, r, code);
+    const uint32_t b = heads_last<NB>(0u, hd, r, code);
     const kvc_u32x4 v = piece(b);
     const uint32_t dv[4] = {v[0], v[1], v[2], v[3]};
-    const uint32_t s = 8u * b + piece_last<8>(dv, r, code);
-    return s < A - 1u ? s : A - 1u;
+    const uint32_t s = piece_last<8>(b, dv, r, code);
+    if constexpr (PAD) return s < A - 1u ? s : A - 1u;
+    return s;
 }
 
 // Decode one symbol: search `row` (padded cumulative frequencies), take its
@@ -447,12 +450,12 @@ KVC_HD uint32_t dec_symbol(DecState &d, const Row &row, const Pairs &pairs, uint
 }
 
 // dec_symbol with the two-level search (cdf_search_blocks).
-template <int NSTEP, class Row, class Piece, class Pairs>
+template <int NSTEP, bool PAD, class Row, class Piece, class Pairs>
 KVC_HD uint32_t dec_symbol_blocks(DecState &d, const Row &row, const Piece &piece, const Pairs &pairs,
                                   uint32_t A, uint32_t *bad)
 {
     const uint32_t r = d.range >> 16;
-    const uint32_t s = cdf_search_blocks<NSTEP>(row, piece, A, r, d.code);
+    const uint32_t s = cdf_search_blocks<NSTEP, PAD>(row, piece, A, r, d.code);
     const uint32_t p = pairs[s];
     *bad |= dec_advance(d, r, p & 0xFFFFu, p >> 16);
     return s;

@@ -31,6 +31,26 @@ struct PairTile {
             }
         }
     }
+    // The decoder's form: entry k of row cl as the 8-byte (pair, lut[k]) at
+    // dst[2 (cl A + k)], so one read gives a symbol's interval and its
+    // dequantization value; and the starts as rows of P2 uint16 (the search).
+    template <class D32, class D16, class LUT>
+    __device__ void store_with(D32 dst, int CT, int A, D16 dst16, int P2, const LUT &lut) const
+    {
+        const int npairs = CT * (A >> 1);
+#pragma unroll
+        for (int i = 0; i < kMaxPer; ++i) {
+            const int e = (int)threadIdx.x + i * 256;
+            if (e < npairs) {
+                const int cl = e / (A >> 1), k = (e - cl * (A >> 1)) * 2;
+                const uint32_t st0 = w[i] & 0xFFFFu, st1 = w[i] >> 16;
+                *(lds_u32x4 *)(dst + 4 * e) =
+                    u32x4{cdf_pair(st0, st1), lut[k], cdf_pair(st1, n2[i]), lut[k + 1]};
+                dst16[cl * P2 + k] = (uint16_t)st0;
+                dst16[cl * P2 + k + 1] = (uint16_t)st1;
+            }
+        }
+    }
     // Also writes the starts as rows of P2 uint16 (for the decoder's search).
     template <class D32, class D16 = lds_u16 *>
     __device__ void store(D32 dst, int CT, int A, D16 dst16 = nullptr, int P2 = 0) const

@@ -54,10 +54,10 @@ int hostsim_decode_stream(const uint8_t *buf, int64_t cap, int64_t off, int64_t 
         uint32_t sym;
         if (search == 1 && nstep >= 3 && nstep <= 6) {
             switch (nstep) {
-            case 3: sym = dec_symbol_blocks<3>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
-            case 4: sym = dec_symbol_blocks<4>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
-            case 5: sym = dec_symbol_blocks<5>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
-            default: sym = dec_symbol_blocks<6>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
+            case 3: sym = (uint32_t)A < (1u << 3) ? dec_symbol_blocks<3, true>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad) : dec_symbol_blocks<3, false>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
+            case 4: sym = (uint32_t)A < (1u << 4) ? dec_symbol_blocks<4, true>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad) : dec_symbol_blocks<4, false>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
+            case 5: sym = (uint32_t)A < (1u << 5) ? dec_symbol_blocks<5, true>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad) : dec_symbol_blocks<5, false>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
+            default: sym = (uint32_t)A < 64u ? dec_symbol_blocks<6, true>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad) : dec_symbol_blocks<6, false>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
             }
             q[c] = (uint8_t)sym;
             continue;
