@@ -1,14 +1,15 @@
 // kvc_encode.hip - range coding of every stream, then packing ([CG] 2.1
 // ac_enc; 2.3 step 3 for the chunking).
 //
-// k_encode:    one lane per stream (chunk, layer, K|V, token), 256 tokens of
-//              one slab per block; the lane walks its C channel symbols and
+// k_encode:    one lane per stream (chunk, layer, K|V, token), 16 or 64 streams
+//              per wave, 256 tokens of one slab per slot region; the lane
+//              walks its C channel symbols and
 //              codes each with its channel's CDF row (all lanes of a wave read
 //              the same row at the same step).  Bytes go to the lane's own
 //              scratch slot as aligned dwords; the length to stream_len.
 // k_slab_sum:  per-slab sum of the stream lengths.
 // k_scan:      exclusive scan of the slab sums -> slab_off (one block).
-// k_pack:      per 64 streams, their payload offsets, then the wave copies
+// k_pack:      per 16 or 64 streams, their payload offsets, then the wave copies
 //              them from their slots to the payload through an LDS window
 //              (whole slot dwords as unaligned dword stores).
 #include "kvc_common.h"
@@ -18,10 +19,16 @@
 
 namespace {
 
-// One lane per stream, 256 tokens of one slab per block.  The slab is walked
+// One lane per stream; the 256 tokens of a slab that share a slot region are
+// coded by 256 / (4 SPW) blocks of four waves, SPW streams per wave (the
+// other lanes only help stage tiles).  SPW = 64 keeps every lane coding;
+// launches of few streams take SPW = 16, which fills four times as many
+// SIMDs with waves whose branch to write out a finished dword is taken only
+// when one of 16 lanes, not one of 64, has one (at a bit or two per symbol
+// some lane of 64 nearly always has).  The slab is walked
 // in tiles of CT channels: at each tile boundary the block stages the tile's
 // CDF rows as packed (start, frequency) pairs in LDS.  When C % 16 == 0 the
-// symbols of the block's 256 tokens are staged too, in tiles of SW channels
+// symbols of the block's tokens are staged too, in tiles of SW channels
 // (coalesced 16-byte loads; SW is a multiple of CT): 64, so a 128-byte line
 // of a token row is fetched in two halves rather than in 32-byte pieces, or
 // 128 (whole lines) for launches of few streams, where the LDS it takes
@@ -31,21 +38,30 @@ namespace {
 // rows have a 16-byte-padded stride that spreads lanes over all banks.
 // Without global loads in the loop, the lanes' byte stores never make it
 // wait.
-template <bool VEC16, int PER, int ENC_SW>
+template <bool VEC16, int PER, int ENC_SW, int SPW>
 __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
                                                 const uint16_t *__restrict__ cdf,
                                                 uint8_t *__restrict__ slots,
                                                 uint16_t *__restrict__ stream_len, KParams p, int CT)
 {
-    // LDS: pairs [CT][A] u32 | symbols [256][SW + 16] u8 (VEC16 only)
+    static_assert(SPW == 16 || SPW == 32 || SPW == 64, "16, 32 or 64 streams per wave");
+    constexpr int SPB = 4 * SPW;   // streams (token rows) per block
+    constexpr int GB = 256 / SPB;  // blocks per 256-token slot region
+    // LDS: pairs [CT][A] u32 | symbols [SPB][SW + 16] u8 (VEC16 only)
     extern __shared__ uint32_t lds[];
     const int bps = (p.Tc + 255) / 256;
-    const int64_t slab = blockIdx.x / bps;
-    const int tb = (int)(blockIdx.x - slab * bps);
-    const int t = tb * 256 + (int)threadIdx.x;
+    const int64_t grp = blockIdx.x / GB;  // slot region: 256 tokens of one slab
+    const int sub = (int)(blockIdx.x - grp * GB);
+    const int64_t slab = grp / bps;
+    const int tb = (int)(grp - slab * bps);
     const SlabGeom g = slab_geom(p, slab);
+    const int r0 = tb * 256 + sub * SPB;  // the block's first token
+    if (r0 >= g.nj) return;               // uniform: the whole block is past the slab
+    const int lane = (int)threadIdx.x & 63;
+    const int j = ((int)threadIdx.x >> 6) * SPW + lane;  // stream within the block (lane < SPW)
+    const int t = r0 + j;
     const int C = p.C, A = p.A;
-    const bool active = t < g.nj;
+    const bool active = lane < SPW && t < g.nj;
     const int64_t sid = g.sid0 + t;
     const uint8_t *q = sym + (g.row0 + (active ? t : 0)) * C;
     const uint16_t *rows = cdf + slab * C * A;
@@ -54,29 +70,31 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
     lds_u8 *const stile = (lds_u8 *)(pairs + CT * A);
     const int ntiles = (C + CT - 1) / CT;
 
-    // slot dword k of this lane: block region + (k * 256 + lane) dwords
-    SlotOut out{(uint32_t *)(slots + (int64_t)blockIdx.x * p.slot_bytes * 256), threadIdx.x, 256u};
+    // slot dword k of this lane: region + (k * 256 + stream within the region) dwords
+    SlotOut out{(uint32_t *)(slots + grp * p.slot_bytes * 256), (uint32_t)(sub * SPB + j), 256u};
     EncState e;
     enc_init(e);
     // Tiles arrive in registers while the previous ones are coded, and go
     // into LDS between two barriers.  Symbol pieces: 16 bytes of a token row,
-    // SW / 16 per row, and as many per thread (256 rows, 256 threads).
+    // SW / 16 per row, SPB rows over 256 threads.
     PairTile<PER> pt;
     constexpr int per_row = ENC_SW / 16;
-    u32x4 sv[per_row];
+    constexpr int NP = SPB * per_row / 256;  // pieces per thread
+    static_assert(NP >= 1 && SPB * per_row == 256 * NP, "whole pieces per thread");
+    u32x4 sv[NP];
     auto load_syms = [&](int s0) {
 #pragma unroll
-        for (int i = 0; i < per_row; ++i) {
+        for (int i = 0; i < NP; ++i) {
             const int ch = (int)threadIdx.x + 256 * i;
             const int r = ch / per_row, part = ch - r * per_row;
-            const int tok = tb * 256 + r, cc = s0 + part * 16;
+            const int tok = r0 + r, cc = s0 + part * 16;
             sv[i] = (tok < g.nj && cc < C) ? *(const u32x4 *)(sym + (g.row0 + tok) * C + cc)
                                            : u32x4{0, 0, 0, 0};
         }
     };
     auto store_syms = [&]() {
 #pragma unroll
-        for (int i = 0; i < per_row; ++i) {
+        for (int i = 0; i < NP; ++i) {
             const int ch = (int)threadIdx.x + 256 * i;
             const int r = ch / per_row, part = ch - r * per_row;
             *(lds_u32x4 *)(stile + r * sstride + part * 16) = sv[i];
@@ -100,7 +118,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
         }
         if (!active) continue;
         if constexpr (VEC16) {
-            const lds_u8 *my = stile + threadIdx.x * sstride;
+            const lds_u8 *my = stile + j * sstride;
             for (int cg = c0; cg < c1; cg += 16) {
                 const u32x4 v = *(const lds_u32x4 *)(my + (cg - s0));
                 const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
@@ -192,39 +210,45 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *slab_total, uint6
     }
 }
 
-// One wavefront per 64 consecutive streams of an encoder block (so 4 blocks
-// of 64 lanes per encoder block).  Lane i first finds stream i's payload
-// offset o (slab offset + the lengths before it).  The wave then walks its
-// streams' slot dwords in rounds of 64: it stages slot dwords [64r, 64r + 64)
-// of all 64 streams in LDS (coalesced loads: the slots are interleaved, lane
-// i's k-th dword next to lane i + 1's) and writes the streams one after the
-// other, lane j taking slot dword 64r + j.  A slot dword holds 4 stream bytes
-// in stream order, so every whole one goes out as one dword store at byte
-// offset o + 4j, unaligned (gfx9 global stores take any byte address and
-// write only the 4 bytes), and the last len % 4 bytes as byte stores; a
-// store instruction thus covers up to 256 contiguous payload bytes and no
-// byte of a neighbouring stream is touched.  Nothing is written at or past
-// payload_cap.
+// One wavefront per SPW consecutive streams of a slot region (256 tokens of
+// one slab): 64, or 16 for launches of few streams, where four times as many
+// waves each walk a quarter of the streams.  Lane i < SPW first finds stream
+// i's payload offset o (slab offset + the lengths before it).  The wave then
+// walks its streams' slot dwords in rounds of 64: it stages slot dwords
+// [64r, 64r + 64) of its SPW streams in LDS (coalesced loads: the slots are
+// interleaved, stream i's k-th dword next to stream i + 1's) and writes the
+// streams one after the other, lane j taking slot dword 64r + j.  A slot
+// dword holds 4 stream bytes in stream order, so every whole one goes out as
+// one dword store at byte offset o + 4j, unaligned (gfx9 global stores take
+// any byte address and write only the 4 bytes), and the last len % 4 bytes
+// as byte stores; a store instruction thus covers up to 256 contiguous
+// payload bytes and no byte of a neighbouring stream is touched.  Nothing is
+// written at or past payload_cap.
 constexpr int PACK_W = 64;  // slot dwords per stream and round
 
+template <int SPW>
 __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
                                              const uint16_t *__restrict__ stream_len,
                                              const uint64_t *__restrict__ slab_off,
                                              uint8_t *__restrict__ payload, int64_t payload_cap,
                                              KParams p)
 {
-    __shared__ uint32_t win[64 * (PACK_W + 1)];  // [stream][PACK_W + 1] staged slot dwords
+    static_assert(SPW == 16 || SPW == 64, "16 or 64 streams per wave");
+    constexpr int WPR = 256 / SPW;  // waves per slot region
+    constexpr int PPR = SPW / 4;    // 16-byte pieces per staged slot row
+    constexpr int RPL = 64 / PPR;   // slot rows per wave-wide load
+    __shared__ uint32_t win[SPW * (PACK_W + 1)];  // [stream][PACK_W + 1] staged slot dwords
     const int bps = (p.Tc + 255) / 256;
-    const int64_t eb = blockIdx.x >> 2;  // encoder block
-    const int wq = (int)(blockIdx.x & 3u);
+    const int64_t eb = blockIdx.x / WPR;  // slot region
+    const int wq = (int)(blockIdx.x - eb * WPR);
     const int64_t slab = eb / bps;
     const int tb = (int)(eb - slab * bps);
     const SlabGeom g = slab_geom(p, slab);
     const int lane = (int)threadIdx.x;
-    const int t0 = tb * 256 + wq * 64;
+    const int t0 = tb * 256 + wq * SPW;
     if (t0 >= g.nj) return;  // the whole wave is past the slab's streams
     const int t = t0 + lane;
-    const bool active = t < g.nj;
+    const bool active = lane < SPW && t < g.nj;
 
     uint32_t pre = 0;  // bytes of the slab's streams before this wave's
     for (int i = lane; i < t0; i += 64) pre += stream_len[g.sid0 + i];
@@ -239,31 +263,31 @@ __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
     const int ndw = (int)((len + 3u) >> 2);  // slot dwords holding the stream
     const int ndw_max = (int)wave_max_u32((uint32_t)ndw);
     const int rounds = (ndw_max + PACK_W - 1) / PACK_W;
-    // slot dword k of stream wq * 64 + i is dword k * 256 + wq * 64 + i of the block's slots
-    const uint32_t *srcw = (const uint32_t *)(slots + eb * p.slot_bytes * 256) + wq * 64;
+    // slot dword k of stream wq * SPW + i is dword k * 256 + wq * SPW + i of the region's slots
+    const uint32_t *srcw = (const uint32_t *)(slots + eb * p.slot_bytes * 256) + wq * SPW;
     const uint32_t olo = (uint32_t)o, ohi = (uint32_t)(o >> 32);
     const uint64_t cap = (uint64_t)payload_cap;
-    // staging: lane l loads 16 bytes = dword k of streams 4m .. 4m + 3 (m = l & 15) for
-    // k = k0 + 4q + (l >> 4), q = 0 .. 15, so one wave-wide load covers 4 slot rows
-    const int sg = lane >> 4, sm = lane & 15;
+    // staging: lane l loads 16 bytes = dword k of streams 4m .. 4m + 3 (m = l % PPR) for
+    // k = k0 + RPL q + l / PPR, so one wave-wide load covers RPL slot rows
+    const int sg = lane / PPR, sm = lane % PPR;
 
     for (int r = 0; r < rounds; ++r) {
         const int k0 = r * PACK_W;
-        u32x4 v4[PACK_W / 4];
+        u32x4 v4[PACK_W / RPL];
 #pragma unroll
-        for (int q = 0; q < PACK_W / 4; ++q) {
-            const int k = k0 + 4 * q + sg;
+        for (int q = 0; q < PACK_W / RPL; ++q) {
+            const int k = k0 + RPL * q + sg;
             v4[q] = k < ndw_max ? *(const u32x4 *)(srcw + (int64_t)k * 256 + 4 * sm) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int q = 0; q < PACK_W / 4; ++q) {
-            const int u = 4 * q + sg;
+        for (int q = 0; q < PACK_W / RPL; ++q) {
+            const int u = RPL * q + sg;
 #pragma unroll
             for (int e = 0; e < 4; ++e) win[(4 * sm + e) * (PACK_W + 1) + u] = v4[q][e];
         }
         __syncthreads();
         const uint32_t j = (uint32_t)(k0 + lane);  // this lane's slot dword
-        for (int i = 0; i < 64; ++i) {
+        for (int i = 0; i < SPW; ++i) {
             const uint32_t len_i = (uint32_t)__builtin_amdgcn_readlane((int)len, i);
             if ((uint32_t)k0 * 4u >= len_i) continue;  // uniform: stream i is done
             if (4u * j >= len_i) continue;
@@ -291,9 +315,20 @@ __global__ void k_zero_u64(uint64_t *dst) { *dst = 0; }
 #ifndef KVC_ENC_WIDE_MAX_STREAMS
 #define KVC_ENC_WIDE_MAX_STREAMS 32768
 #endif
+// Launches of at most this many streams code 16 streams per wave, others 64.
+#ifndef KVC_ENC_SPARSE_MAX_STREAMS
+#define KVC_ENC_SPARSE_MAX_STREAMS 16384
+#endif
+// Launches of at most this many streams pack 16 streams per wave, others 64.
+#ifndef KVC_PACK_SPARSE_MAX_STREAMS
+#define KVC_PACK_SPARSE_MAX_STREAMS 16384
+#endif
 
 // Symbol tile width: 128 channels for launches of few streams, else 64.
 static int enc_symbol_tile(int64_t n_streams) { return n_streams <= KVC_ENC_WIDE_MAX_STREAMS ? 128 : 64; }
+
+// Streams coded per wave.
+static int enc_streams_per_wave(int64_t n_streams) { return n_streams <= KVC_ENC_SPARSE_MAX_STREAMS ? 16 : 64; }
 
 // Channels per tile (a power of two, 16 to the symbol tile width).  With few
 // streams a tile of 16 channels is coded in less time than its successor's
@@ -324,34 +359,44 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
 {
     if (p.n_slabs == 0) return launch_zero_u64(slab_off, stream);
     const int64_t bps = (p.Tc + 255) / 256;
-    dim3 grid((unsigned)(bps * p.n_slabs));
+    const int64_t regions = bps * p.n_slabs;  // slot regions: 256 tokens of one slab
     const int CT = enc_tile_channels(p.A, p.n_streams);
     const size_t lds_pairs = (size_t)CT * p.A * sizeof(uint32_t);
     const int per = (CT * (p.A / 2) + 255) / 256;  // pairs staged per thread
     const int sw = enc_symbol_tile(p.n_streams);
-#define KVC_ENC(V, P, S, L)                                                                          \
-    hipLaunchKernelGGL((k_encode<V, P, S>), grid, dim3(256), L, stream, sym, cdf, slots, stream_len, p, \
-                       CT)
-#define KVC_ENC_S(S)                                                                                 \
+    const int spw = enc_streams_per_wave(p.n_streams);
+    const dim3 grid((unsigned)(regions * (64 / spw)));
+#define KVC_ENC(V, P, S, W, L)                                                                       \
+    hipLaunchKernelGGL((k_encode<V, P, S, W>), grid, dim3(256), L, stream, sym, cdf, slots, stream_len, \
+                       p, CT)
+#define KVC_ENC_S(S, W)                                                                              \
     {                                                                                                \
-        const size_t lds_syms = lds_pairs + 256 * (size_t)(S + 16);                                  \
+        const size_t lds_syms = lds_pairs + 4 * W * (size_t)(S + 16);                                \
         if (vec16) {                                                                                 \
-            if (per <= 2) KVC_ENC(true, 2, S, lds_syms);                                             \
-            else KVC_ENC(true, 8, S, lds_syms);                                                      \
+            if (per <= 2) KVC_ENC(true, 2, S, W, lds_syms);                                          \
+            else KVC_ENC(true, 8, S, W, lds_syms);                                                   \
         } else {                                                                                     \
-            if (per <= 2) KVC_ENC(false, 2, S, lds_pairs);                                           \
-            else KVC_ENC(false, 8, S, lds_pairs);                                                    \
+            if (per <= 2) KVC_ENC(false, 2, S, W, lds_pairs);                                        \
+            else KVC_ENC(false, 8, S, W, lds_pairs);                                                 \
         }                                                                                            \
     }
-    if (sw == 128) KVC_ENC_S(128) else KVC_ENC_S(64)
+    if (spw == 16) {
+        if (sw == 128) KVC_ENC_S(128, 16) else KVC_ENC_S(64, 16)
+    } else {
+        if (sw == 128) KVC_ENC_S(128, 64) else KVC_ENC_S(64, 64)
+    }
 #undef KVC_ENC_S
 #undef KVC_ENC
     hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
                        slab_total, p);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, slab_total, slab_off, p.n_slabs,
                        payload_cap, (const uint64_t *)nullptr, status);
-    hipLaunchKernelGGL(k_pack, dim3(grid.x * 4), dim3(64), 0, stream, slots, stream_len,
-                       slab_off, payload, payload_cap, p);
+    if (p.n_streams <= KVC_PACK_SPARSE_MAX_STREAMS)
+        hipLaunchKernelGGL(k_pack<16>, dim3((unsigned)(regions * 16)), dim3(64), 0, stream, slots,
+                           stream_len, slab_off, payload, payload_cap, p);
+    else
+        hipLaunchKernelGGL(k_pack<64>, dim3((unsigned)(regions * 4)), dim3(64), 0, stream, slots,
+                           stream_len, slab_off, payload, payload_cap, p);
     return hipGetLastError();
 }
 
