@@ -162,22 +162,32 @@ __global__ __launch_bounds__(256) void k_slab_sum(const uint16_t *__restrict__ s
 }
 
 // Exclusive scan of 1024 per-thread values held in registers; returns the
-// thread's prefix and writes the block total to *total.
+// thread's prefix and writes the block total to *total.  Each wave scans its
+// 64 values with shuffles, wave 0 scans the 16 wave totals, and every thread
+// adds its wave's offset: three barriers.
 __device__ uint64_t block_excl_scan_1024(uint64_t v, uint64_t *sh, uint64_t *total)
 {
-    const int tid = threadIdx.x;
-    sh[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        uint64_t add = tid >= off ? sh[tid - off] : 0;
-        __syncthreads();
-        sh[tid] += add;
-        __syncthreads();
+    const int lane = (int)threadIdx.x & 63, wid = (int)threadIdx.x >> 6;
+    uint64_t incl = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint64_t o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
     }
-    uint64_t incl = sh[tid];
-    *total = sh[1023];
+    if (lane == 63) sh[wid] = incl;
     __syncthreads();
-    return incl - v;
+    if (wid == 0) {
+        uint64_t w = lane < 16 ? sh[lane] : 0u;
+        for (int off = 1; off < 16; off <<= 1) {
+            const uint64_t o = __shfl_up(w, off, 64);
+            if (lane >= off) w += o;
+        }
+        if (lane < 16) sh[16 + lane] = w;  // inclusive prefix of the wave totals
+    }
+    __syncthreads();
+    const uint64_t base = wid > 0 ? sh[16 + wid - 1] : 0u;
+    *total = sh[31];
+    __syncthreads();
+    return base + incl - v;
 }
 
 // slab_total and slab_off may be the same array (each thread reads its own
@@ -188,7 +198,7 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *slab_total, uint6
                                                int64_t n, int64_t payload_cap,
                                                const uint64_t *expect, int32_t *status)
 {
-    __shared__ uint64_t sh[1024];
+    __shared__ uint64_t sh[32];
     const int64_t per = (n + 1023) / 1024;
     const int64_t b = threadIdx.x * per, e = min(n, b + per);
     uint64_t local = 0;
