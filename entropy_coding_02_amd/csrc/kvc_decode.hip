@@ -212,10 +212,30 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
 template <int G>
 __device__ __forceinline__ uint32_t group_sum(uint32_t v)
 {
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
-    if constexpr (G >= 4) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
-    if constexpr (G >= 8) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);  // half-row mirror
+    // (every source lane exists, so bound_ctrl loses nothing and saves setting the old value)
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);  // quad [1,0,3,2]
+    if constexpr (G >= 4) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);  // quad [2,3,0,1]
+    if constexpr (G >= 8) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true);  // half-row mirror
     return v;
+}
+
+// Number of qualifying entries (r * cdf_k <= code) of an E-entry slice held two
+// per dword (lower index in the low half) whose entry 0 qualifies, on a
+// non-decreasing slice: one more than piece_last's index, by the same
+// selects, with the count's terms added rather than or-ed.
+template <int E>
+__device__ __forceinline__ uint32_t slice_count(const uint32_t *d, uint32_t r, uint32_t code)
+{
+    if constexpr (E == 2) {
+        return r * (d[0] >> 16) <= code ? 2u : 1u;
+    } else {
+        constexpr int H = E / 4;  // dwords in each half
+        const bool a = r * (d[H] & 0xFFFFu) <= code;  // entry E / 2
+        uint32_t h[H];
+#pragma unroll
+        for (int k = 0; k < H; ++k) h[k] = a ? d[H + k] : d[k];
+        return (a ? (uint32_t)(E / 2) : 0u) + slice_count<E / 2>(h, r, code);
+    }
 }
 
 // Decoding with G lanes per stream, for launches with few streams.  A stream's
@@ -231,7 +251,7 @@ __device__ __forceinline__ uint32_t group_sum(uint32_t v)
 // searches find it.  The slice reads do not depend on the coder state.  The
 // outputs of a stream are split over its lanes.  Block: 256 / G streams of
 // one slab; LDS as in k_decode.
-template <bool VEC, int OUT, int NSTEP, int G>
+template <bool VEC, int OUT, int NSTEP, int G, bool PAD>
 __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict__ payload,
                                                       int64_t payload_bytes,
                                                       const uint64_t *__restrict__ slab_off,
@@ -327,14 +347,23 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
             }
         }
         const uint32_t r = d.range >> 16;
-        // qualifying entries of the slice: none, or a prefix ending at piece_last
-        // (computed either way; the empty asm keeps it out of a branch)
-        uint32_t n = piece_last<E>(0u, e2, r, d.code) + 1u;
+        // qualifying entries of the slice: none, or a prefix of slice_count
+        // (computed either way; the empty asm keeps it out of a branch).  Lane 0's
+        // entry 0 is staged as 0 and always qualifies, so n >= 1 and, on a row
+        // without padding (n <= A), s = n - 1 needs no clamp.
+        uint32_t n = slice_count<E>(e2, r, d.code);
         __asm__("" : "+v"(n));
         n = r * (e2[0] & 0xFFFFu) <= d.code ? n : 0u;
         n = group_sum<G>(n);
-        const uint32_t s = min(n - 1u, amax);  // n = 0 only for a row with cdf_0 > 0
-        const u32x2 e = *(const lds_u32x2 *)(pr + 2 * (cl * A + (int)s));
+        u32x2 e;
+        uint32_t s;
+        if constexpr (PAD) {
+            s = min(n - 1u, amax);  // padding entries (0xFFFF) may qualify
+            e = *(const lds_u32x2 *)(pr + 2 * (cl * A + (int)s));
+        } else {
+            s = n - 1u;
+            e = *(const lds_u32x2 *)(pr + 2 * ((cl * A - 1) + (int)n));
+        }
         bad |= dec_advance(d, r, e.x & 0xFFFFu, e.x >> 16);
         lv = __uint_as_float(e.y);
         return s;
@@ -506,8 +535,12 @@ static hipError_t launch_decode_group(const uint8_t *payload, int64_t payload_by
     const int64_t bps = (p.Tc + 256 / G - 1) / (256 / G);
     dim3 grid((unsigned)(bps * p.n_slabs)), block(256);
 #define KVC_DECG(V, O, N, GG)                                                                        \
-    hipLaunchKernelGGL((k_decode_group<V, O, N, GG>), grid, block, lds, stream, payload, payload_bytes, \
-                       slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
+    if (p.A == (1 << N))                                                                             \
+        hipLaunchKernelGGL((k_decode_group<V, O, N, GG, false>), grid, block, lds, stream, payload,   \
+                           payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT); \
+    else                                                                                             \
+        hipLaunchKernelGGL((k_decode_group<V, O, N, GG, true>), grid, block, lds, stream, payload,    \
+                           payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
 #define KVC_DECG_N(V, O)                                                                             \
     switch (nstep) {                                                                                 \
     case 3: KVC_DECG(V, O, 3, 4); break;                                                             \

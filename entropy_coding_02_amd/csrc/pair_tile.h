@@ -33,7 +33,9 @@ struct PairTile {
     }
     // The decoder's form: entry k of row cl as the 8-byte (pair, lut[k]) at
     // dst[2 (cl A + k)], so one read gives a symbol's interval and its
-    // dequantization value; and the starts as rows of P2 uint16 (the search).
+    // dequantization value; and the starts as rows of P2 uint16 (the search),
+    // entry 0 written as 0, so that it qualifies as on a well-formed row
+    // (cdf_0 = 0) and every search finds a k in [0, A).
     template <class D32, class D16, class LUT>
     __device__ void store_with(D32 dst, int CT, int A, D16 dst16, int P2, const LUT &lut) const
     {
@@ -46,7 +48,7 @@ struct PairTile {
                 const uint32_t st0 = w[i] & 0xFFFFu, st1 = w[i] >> 16;
                 *(lds_u32x4 *)(dst + 4 * e) =
                     u32x4{cdf_pair(st0, st1), lut[k], cdf_pair(st1, n2[i]), lut[k + 1]};
-                dst16[cl * P2 + k] = (uint16_t)st0;
+                dst16[cl * P2 + k] = (uint16_t)(k == 0 ? 0u : st0);
                 dst16[cl * P2 + k + 1] = (uint16_t)st1;
             }
         }
