@@ -327,9 +327,9 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
     const uint16_t *srows = cdf + slab * C * A;
     const int ntiles = (C + CT - 1) / CT;
     const uint32_t amax = (uint32_t)A - 1u;
-    auto decode1 = [&](int cl, float &lv) -> uint32_t {
+    // this lane's slice of the search row of tile channel cl
+    auto load_slice = [&](int cl, uint32_t(&e2)[E / 2]) {
         const lds_u16 *sp = r16 + cl * (int)P2 + q * E;
-        uint32_t e2[E / 2];
         if constexpr (E == 2) {
             e2[0] = *(const lds_u32 *)sp;
         } else if constexpr (E == 4) {
@@ -346,6 +346,8 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
                 e2[4 * h + 3] = v.w;
             }
         }
+    };
+    auto decode1 = [&](int cl, const uint32_t(&e2)[E / 2], float &lv) -> uint32_t {
         const uint32_t r = d.range >> 16;
         // qualifying entries of the slice: none, or a prefix of slice_count
         // (computed either way; the empty asm keeps it out of a branch).  Lane 0's
@@ -371,6 +373,13 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
 
     PairTile<2> pt;
     uint32_t hw[16];
+    // slices of 8 consecutive channels, loaded one such group ahead of their
+    // decoding (the groups of a tile alternate between the two buffers)
+    uint32_t sa[8][E / 2], sb[8][E / 2];
+    auto load_group = [&](int cl0, uint32_t(&buf)[8][E / 2]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) load_slice(cl0 + i, buf[i]);
+    };
     pt.load(srows, 0, CT, C, A);
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
@@ -382,13 +391,21 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
         if constexpr (VEC) {
             // C % 16 == 0, CT % 16 == 0: blocks of 32 channels (64 fp16 bytes per
             // row), lane q writing 64 / G bytes of each; 8-symbol groups of
-            // symbols or fp32 values by lane gi % G
+            // symbols or fp32 values by lane gi % G.  A block has an even number
+            // of groups, so group gi of every block decodes from buffer gi % 2.
+            load_group(0, sa);
             for (int cb = c0; cb < c1; cb += 32) {
                 const int nb = min(32, c1 - cb);  // 16 or 32
 #pragma unroll
                 for (int gi = 0; gi < 4; ++gi) {
                     if (gi * 8 >= nb) break;
                     const int cg = cb + gi * 8;
+                    uint32_t(&cur)[8][E / 2] = (gi & 1) ? sb : sa;
+                    // the next group of the tile (the last group reloads itself, so the
+                    // loads need no branch); the barrier keeps them ahead of this
+                    // group's decoding
+                    load_group(min(cg + 8, c1 - 8) - c0, (gi & 1) ? sa : sb);
+                    __asm__ volatile("" ::: "memory");
                     in.group();
                     uint32_t sw[2] = {0, 0};
                     float fw[8];
@@ -397,7 +414,7 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
                     for (int i = 0; i < 8; ++i) {
                         if ((i & 1) == 0) dec_refill(d, in);
                         float lv;
-                        const uint32_t s = decode1(cg - c0 + i, lv);
+                        const uint32_t s = decode1(cg - c0 + i, cur[i], lv);
                         sw[i >> 2] |= s << (8 * (i & 3));
                         if constexpr (ODT >= 0) {
                             const float y = lv * m;
@@ -448,7 +465,9 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
                 if ((c & 7) == 0) in.group();
                 if ((c & 1) == 0) dec_refill(d, in);
                 float lv;
-                const uint32_t s = decode1(c - c0, lv);
+                uint32_t e2[E / 2];
+                load_slice(c - c0, e2);
+                const uint32_t s = decode1(c - c0, e2, lv);
                 if (q == c % G) {
                     if constexpr ((OUT & OUT_SYM) != 0) so[c] = (uint8_t)s;
                     if constexpr (ODT >= 0) {
