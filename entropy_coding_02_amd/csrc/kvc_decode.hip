@@ -207,34 +207,37 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
     if (active && bad) kvc_flag(status, KVC_DEV_CORRUPT);
 }
 
-// Sum of v over each aligned group of G lanes (G = 2, 4 or 8), in every lane
-// of the group: DPP swaps within quads, then the half-row mirror.
+// Maximum of v over each aligned group of G lanes (G = 2, 4 or 8), in every
+// lane of the group: DPP swaps within quads, then the half-row mirror (every
+// source lane exists, so bound_ctrl loses nothing and saves setting the old
+// value).
 template <int G>
-__device__ __forceinline__ uint32_t group_sum(uint32_t v)
+__device__ __forceinline__ uint32_t group_max(uint32_t v)
 {
-    // (every source lane exists, so bound_ctrl loses nothing and saves setting the old value)
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);  // quad [1,0,3,2]
-    if constexpr (G >= 4) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);  // quad [2,3,0,1]
-    if constexpr (G >= 8) v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true);  // half-row mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));
+    if constexpr (G >= 4) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));
+    if constexpr (G >= 8) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true));
     return v;
 }
 
-// Number of qualifying entries (r * cdf_k <= code) of an E-entry slice held two
-// per dword (lower index in the low half) whose entry 0 qualifies, on a
-// non-decreasing slice: one more than piece_last's index, by the same
-// selects, with the count's terms added rather than or-ed.
+// The last key of k[0, E) with r * (key >> 16) <= code, k[0] taken to
+// qualify (the qualifying keys a prefix); its index in idx.
 template <int E>
-__device__ __forceinline__ uint32_t slice_count(const uint32_t *d, uint32_t r, uint32_t code)
+__device__ __forceinline__ uint32_t slice_last_key(const uint32_t *k, uint32_t r, uint32_t code,
+                                                   uint32_t &idx)
 {
-    if constexpr (E == 2) {
-        return r * (d[0] >> 16) <= code ? 2u : 1u;
+    if constexpr (E == 1) {
+        idx = 0;
+        return k[0];
     } else {
-        constexpr int H = E / 4;  // dwords in each half
-        const bool a = r * (d[H] & 0xFFFFu) <= code;  // entry E / 2
-        uint32_t h[H];
+        const bool a = r * (k[E / 2] >> 16) <= code;
+        uint32_t h[E / 2];
 #pragma unroll
-        for (int k = 0; k < H; ++k) h[k] = a ? d[H + k] : d[k];
-        return (a ? (uint32_t)(E / 2) : 0u) + slice_count<E / 2>(h, r, code);
+        for (int i = 0; i < E / 2; ++i) h[i] = a ? k[E / 2 + i] : k[i];
+        uint32_t sub;
+        const uint32_t v = slice_last_key<E / 2>(h, r, code, sub);
+        idx = (a ? (uint32_t)(E / 2) : 0u) + sub;
+        return v;
     }
 }
 
@@ -242,15 +245,19 @@ __device__ __forceinline__ uint32_t slice_count(const uint32_t *d, uint32_t r, u
 // symbols are a chain of dependent steps, so with one lane per stream a small
 // launch leaves most of the chip idle while each step waits on its table
 // reads.  Here the G lanes of a group carry identical coder state and byte
-// feeds (each its own ring), and at each symbol lane q counts the entries of
-// its slice [q E, q E + E) of the channel's padded search row (E = P2 / G)
-// with r * cdf_k <= code (a prefix of the slice on a non-decreasing row, so
-// a binary search over the slice's registers).  The group's DPP sum is the number of qualifying
-// entries; for a non-decreasing row (cdf_0 = 0) the symbol is that count
-// minus one, clamped to A - 1: the largest qualifying k, as the one-lane
-// searches find it.  The slice reads do not depend on the coder state.  The
-// outputs of a stream are split over its lanes.  Block: 256 / G streams of
-// one slab; LDS as in k_decode.
+// feeds (each its own ring).  A tile's CDF rows are staged as rows of P2 keys
+// start << 16 | frequency (PairTile::store_keys: entries past A repeat entry
+// A - 1, entry 0's start is 0), and at each symbol lane q searches its slice
+// [q E, q E + E) of the channel's row (E = P2 / G) over registers for the
+// last key with r * start <= code (a prefix of the slice on a non-decreasing
+// row).  On such a row the keys grow with the index, so the maximum over the
+// group of the lanes' keys (a lane whose first key does not qualify offers
+// 0) is the key of the largest qualifying k, the symbol the one-lane
+// searches find: its interval comes out of the search itself, with no table
+// read after it, and the symbol, needed only for the output, is the maximum
+// of the lanes' q E + index.  The slice reads do not depend on the coder
+// state and are issued a group of 8 channels ahead.  The outputs of a stream
+// are split over its lanes.  Block: 256 / G streams of one slab.
 template <bool VEC, int OUT, int NSTEP, int G, bool PAD>
 __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict__ payload,
                                                       int64_t payload_bytes,
@@ -271,10 +278,9 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
     const int C = p.C, A = p.A;
     float *lut = (float *)lds;
     lds_u32 *const ring = (lds_u32 *)(lds + 256) + threadIdx.x * 17u;
-    const int n16 = (CT * (int)P2 + 1) / 2;
     lds_u32 *const tile = (lds_u32 *)(lds + 256 + 256 * 17);
-    lds_u16 *const r16 = (lds_u16 *)tile;
-    lds_u32 *const pr = tile + n16;
+    lds_u32 *const keys = tile;  // [CT][P2] keys start << 16 | frequency
+    constexpr int SW = E;        // dwords of a lane's slice
 
     const int q = (int)threadIdx.x % G;   // lane within the stream's group
     const int sl = (int)threadIdx.x / G;  // stream within the block
@@ -307,9 +313,6 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
         const int M = p.maxq[g.lk];
         lut[threadIdx.x] = (float)((int)threadIdx.x - M) / (float)M;
     }
-    if (P2 > (uint32_t)A)
-        for (int e = threadIdx.x; e < CT * (int)P2; e += 256)
-            if ((uint32_t)(e & (P2 - 1)) >= (uint32_t)A) r16[e] = 0xFFFFu;
     __syncthreads();
     uint32_t wbase = 0;
     for (int i = 0; i < wid; ++i) wbase += s_red[i];
@@ -327,56 +330,51 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
     const uint16_t *srows = cdf + slab * C * A;
     const int ntiles = (C + CT - 1) / CT;
     const uint32_t amax = (uint32_t)A - 1u;
-    // this lane's slice of the search row of tile channel cl
-    auto load_slice = [&](int cl, uint32_t(&e2)[E / 2]) {
-        const lds_u16 *sp = r16 + cl * (int)P2 + q * E;
+    // this lane's slice of the key row of tile channel cl: keys [q E, q E + E)
+    auto load_slice = [&](int cl, uint32_t(&ks)[SW]) {
+        const lds_u32 *sp = keys + cl * (int)P2 + q * E;
         if constexpr (E == 2) {
-            e2[0] = *(const lds_u32 *)sp;
-        } else if constexpr (E == 4) {
             const u32x2 v = *(const lds_u32x2 *)sp;
-            e2[0] = v.x;
-            e2[1] = v.y;
+            ks[0] = v.x;
+            ks[1] = v.y;
         } else {
 #pragma unroll
-            for (int h = 0; h < E / 8; ++h) {
-                const u32x4 v = *(const lds_u32x4 *)(sp + 8 * h);
-                e2[4 * h] = v.x;
-                e2[4 * h + 1] = v.y;
-                e2[4 * h + 2] = v.z;
-                e2[4 * h + 3] = v.w;
+            for (int h = 0; h < E / 4; ++h) {
+                const u32x4 v = *(const lds_u32x4 *)(sp + 4 * h);
+                ks[4 * h] = v.x;
+                ks[4 * h + 1] = v.y;
+                ks[4 * h + 2] = v.z;
+                ks[4 * h + 3] = v.w;
             }
         }
     };
-    auto decode1 = [&](int cl, const uint32_t(&e2)[E / 2], float &lv) -> uint32_t {
+    // The slice's last qualifying key (r * start <= code; a prefix of a slice
+    // whose key 0 qualifies) by binary search over registers, its index in
+    // ki.  Keys of qualifying entries grow with the index, so the group's
+    // maximum over lanes whose key 0 qualifies is the key of the symbol: its
+    // interval is known without a table read that waits on the search.  The
+    // symbol itself (for the output) is the maximum of the lanes' q E + ki.
+    auto decode1 = [&](int cl, const uint32_t(&ks)[SW], float &lv) -> uint32_t {
         const uint32_t r = d.range >> 16;
-        // qualifying entries of the slice: none, or a prefix of slice_count
-        // (computed either way; the empty asm keeps it out of a branch).  Lane 0's
-        // entry 0 is staged as 0 and always qualifies, so n >= 1 and, on a row
-        // without padding (n <= A), s = n - 1 needs no clamp.
-        uint32_t n = slice_count<E>(e2, r, d.code);
-        __asm__("" : "+v"(n));
-        n = r * (e2[0] & 0xFFFFu) <= d.code ? n : 0u;
-        n = group_sum<G>(n);
-        u32x2 e;
-        uint32_t s;
-        if constexpr (PAD) {
-            s = min(n - 1u, amax);  // padding entries (0xFFFF) may qualify
-            e = *(const lds_u32x2 *)(pr + 2 * (cl * A + (int)s));
-        } else {
-            s = n - 1u;
-            e = *(const lds_u32x2 *)(pr + 2 * ((cl * A - 1) + (int)n));
-        }
-        bad |= dec_advance(d, r, e.x & 0xFFFFu, e.x >> 16);
-        lv = __uint_as_float(e.y);
+        uint32_t ki;
+        uint32_t key = slice_last_key<E>(ks, r, d.code, ki);
+        __asm__("" : "+v"(key), "+v"(ki));
+        const bool q0 = r * (ks[0] >> 16) <= d.code;  // lane 0: start 0, always
+        key = q0 ? key : 0u;
+        uint32_t s = q0 ? (uint32_t)(q * E) + ki : 0u;
+        key = group_max<G>(key);
+        s = group_max<G>(s);
+        if constexpr (PAD) s = min(s, amax);  // padding repeats entry A - 1
+        bad |= dec_advance(d, r, key >> 16, key & 0xFFFFu);
+        lv = lut[s];
         return s;
     };
-
     PairTile<2> pt;
     uint32_t hw[16];
     // slices of 8 consecutive channels, loaded one such group ahead of their
     // decoding (the groups of a tile alternate between the two buffers)
-    uint32_t sa[8][E / 2], sb[8][E / 2];
-    auto load_group = [&](int cl0, uint32_t(&buf)[8][E / 2]) {
+    uint32_t sa[8][SW], sb[8][SW];
+    auto load_group = [&](int cl0, uint32_t(&buf)[8][SW]) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) load_slice(cl0 + i, buf[i]);
     };
@@ -384,7 +382,7 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
         __syncthreads();
-        pt.store_with(pr, CT, A, r16, (int)P2, (const uint32_t *)lut);
+        pt.store_keys(keys, CT, A, (int)P2);
         __syncthreads();
         if (it + 1 < ntiles) pt.load(srows, c0 + CT, CT, C, A);
         if (!active) continue;
@@ -400,7 +398,7 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
                 for (int gi = 0; gi < 4; ++gi) {
                     if (gi * 8 >= nb) break;
                     const int cg = cb + gi * 8;
-                    uint32_t(&cur)[8][E / 2] = (gi & 1) ? sb : sa;
+                    uint32_t(&cur)[8][SW] = (gi & 1) ? sb : sa;
                     // the next group of the tile (the last group reloads itself, so the
                     // loads need no branch); the barrier keeps them ahead of this
                     // group's decoding
@@ -465,7 +463,7 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
                 if ((c & 7) == 0) in.group();
                 if ((c & 1) == 0) dec_refill(d, in);
                 float lv;
-                uint32_t e2[E / 2];
+                uint32_t e2[SW];
                 load_slice(c - c0, e2);
                 const uint32_t s = decode1(c - c0, e2, lv);
                 if (q == c % G) {

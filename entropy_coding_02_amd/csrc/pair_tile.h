@@ -53,6 +53,28 @@ struct PairTile {
             }
         }
     }
+    // The group decoder's form: row cl as P2 keys start << 16 | frequency (a
+    // pair with its halves swapped, so that on a non-decreasing row the keys
+    // grow with k), entry 0's start taken as 0 (as on a well-formed row), and
+    // entries [A, P2) repeating entry A - 1.
+    template <class D32>
+    __device__ void store_keys(D32 dst, int CT, int A, int P2) const
+    {
+        const int npairs = CT * (A >> 1);
+#pragma unroll
+        for (int i = 0; i < kMaxPer; ++i) {
+            const int e = (int)threadIdx.x + i * 256;
+            if (e < npairs) {
+                const int cl = e / (A >> 1), k = (e - cl * (A >> 1)) * 2;
+                const uint32_t st0 = k == 0 ? 0u : (w[i] & 0xFFFFu), st1 = w[i] >> 16;
+                const uint32_t p0 = cdf_pair(st0, st1), p1 = cdf_pair(st1, n2[i]);
+                const uint32_t k0 = (p0 << 16) | (p0 >> 16), k1 = (p1 << 16) | (p1 >> 16);
+                *(lds_u32x2 *)(dst + cl * P2 + k) = u32x2{k0, k1};
+                if (k + 2 == A)
+                    for (int kk = A; kk < P2; ++kk) dst[cl * P2 + kk] = k1;
+            }
+        }
+    }
     // Also writes the starts as rows of P2 uint16 (for the decoder's search).
     template <class D32, class D16 = lds_u16 *>
     __device__ void store(D32 dst, int CT, int A, D16 dst16 = nullptr, int P2 = 0) const
