@@ -58,14 +58,16 @@ __global__ __launch_bounds__(256) void k_cdf(const uint8_t *__restrict__ sym,
 
 // Wide variant for C % 4 == 0 and A <= 64: a block covers 256 channels of a
 // slab (4 consecutive channels per lane, so a wave reads 256 contiguous
-// symbol bytes of a token with one dword load per lane); wave w takes the
-// tokens t = w (mod 4).  Counters are 16-bit halves of LDS words, word
+// symbol bytes of a token with one dword load per lane); wave w of the NW
+// takes the tokens t = w (mod NW): 4, or 16 on launches of few slabs, where
+// the 16 waves each walk a quarter of the tokens.  Counters are 16-bit halves of LDS words, word
 // (c, s) at c*W + (c >> 2) + s/2 with W = A/2 + 1: at each of a lane's four
 // steps the lanes' channels are 4 apart, and the (c >> 2) skew makes the word
 // stride between lanes odd, so equal symbols fall in distinct banks.  Each
 // thread then turns one channel's counts into its CDF row.
-__global__ __launch_bounds__(256) void k_cdf_wide(const uint8_t *__restrict__ sym,
-                                                  uint16_t *__restrict__ cdf, KParams p)
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_cdf_wide(const uint8_t *__restrict__ sym,
+                                                      uint16_t *__restrict__ cdf, KParams p)
 {
     extern __shared__ uint32_t hist[];
     const int A = p.A, W = A / 2 + 1, C = p.C;
@@ -75,23 +77,23 @@ __global__ __launch_bounds__(256) void k_cdf_wide(const uint8_t *__restrict__ sy
     const int c0 = (int)(blockIdx.x - slab * ntile) * 256;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int nwords = 256 * W + 64;
-    for (int i = threadIdx.x; i < nwords; i += 256) hist[i] = 0;
+    for (int i = threadIdx.x; i < nwords; i += 64 * NW) hist[i] = 0;
     __syncthreads();
     const int cq = c0 + 4 * lane;  // this lane's first channel
     if (cq < C) {
         const uint8_t *col = sym + g.row0 * C + cq;
         const int cl = 4 * lane;
         // 8 tokens per step, loaded before any is counted, so 8 loads are in flight
-        for (int t0 = wid; t0 < g.nj; t0 += 32) {
+        for (int t0 = wid; t0 < g.nj; t0 += 8 * NW) {
             uint32_t v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int t = t0 + 4 * u;
+                const int t = t0 + NW * u;
                 v[u] = t < g.nj ? *(const uint32_t *)(col + (int64_t)t * C) : 0u;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                if (t0 + 4 * u >= g.nj) break;
+                if (t0 + NW * u >= g.nj) break;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     uint32_t s = (v[u] >> (8 * k)) & 0xFFu;
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void k_cdf_wide(const uint8_t *__restrict__ sy
     }
     __syncthreads();
     const int c = c0 + (int)threadIdx.x;
-    if (c < C) {
+    if (threadIdx.x < 256 && c < C) {
         const int cl = (int)threadIdx.x;
         const uint32_t *h = hist + cl * W + (cl >> 2);
         const uint32_t K = 65536u - (uint32_t)A;
@@ -123,13 +125,21 @@ __global__ __launch_bounds__(256) void k_cdf_wide(const uint8_t *__restrict__ sy
 
 }  // namespace
 
+// Launches of at most this many 256-channel tiles take 16 waves per block.
+#ifndef KVC_CDF_WIDE_TALL_MAX_BLOCKS
+#define KVC_CDF_WIDE_TALL_MAX_BLOCKS 1024
+#endif
+
 hipError_t launch_cdf(const uint8_t *sym, uint16_t *cdf, const KParams &p, hipStream_t stream)
 {
     if (p.n_slabs == 0) return hipSuccess;
     if (p.C % 4 == 0 && p.A <= 64 && ((uintptr_t)sym & 3) == 0 && ((uintptr_t)cdf & 3) == 0) {
         const size_t lds = sizeof(uint32_t) * (256 * (size_t)(p.A / 2 + 1) + 64);
         dim3 grid((unsigned)(((p.C + 255) / 256) * p.n_slabs));
-        hipLaunchKernelGGL(k_cdf_wide, grid, dim3(256), lds, stream, sym, cdf, p);
+        if (grid.x <= KVC_CDF_WIDE_TALL_MAX_BLOCKS)
+            hipLaunchKernelGGL(k_cdf_wide<16>, grid, dim3(1024), lds, stream, sym, cdf, p);
+        else
+            hipLaunchKernelGGL(k_cdf_wide<4>, grid, dim3(256), lds, stream, sym, cdf, p);
         return hipGetLastError();
     }
     const int CT = p.A <= 128 ? 64 : 32;
