@@ -30,6 +30,37 @@ __device__ __forceinline__ uint32_t quant1(uint32_t bits, float factor, float M)
     return (uint32_t)r;
 }
 
+// For a finite row (every |x| <= m, so p lies in
+// [0, 2 MAX] up to a rounding and |p| < 2^22): p + 1.5 * 2^23 is rounded to
+// an integer, ties to even, which is rint(p); its fp32 bits are 0x4B400000 +
+// rint(p), the symbol in the low byte.  Rows holding Inf or NaN take the
+// clamped quant1 instead (they are flagged; their symbols only stay in range).
+__device__ __forceinline__ uint32_t quant_bits(float x, float factor, float M)
+{
+    float p = x * factor;
+    p = p + M;
+    return __float_as_uint(p + 12582912.0f);
+}
+
+// The low bytes of four words, b0 lowest.
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3)
+{
+    return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
+}
+
+// Row max of the wave's 64 lanes, uniform: DPP steps within quads, half
+// rows and rows, then the row broadcasts; lane 63 ends with the maximum.
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row half mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row bcast 15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row bcast 31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // VEC = fp16 elements per lane access: 8 (16-byte loads, C % 8 == 0 and
 // 16-byte aligned buffers) or 1 (any C).
 template <int VEC>
@@ -73,7 +104,7 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restric
         } else {
             for (int c = lane; c < C; c += 64) mx = max(mx, (uint32_t)(x[c] & 0x7FFFu));
         }
-        mx = wave_max_u32(mx);
+        mx = (VEC == 8) ? wave_max_dpp(mx) : wave_max_u32(mx);
         const int32_t lk = (int32_t)(row / p.T);
         const float M = (float)p.maxq[lk];
         const float m = kvc_h2f(mx);
@@ -81,13 +112,23 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restric
         if (mx >= 0x7C00u && lane == 0) kvc_flag(status, KVC_DEV_NONFINITE);
         if (lane == 0) max1[row] = (uint16_t)mx;
         if constexpr (VEC == 8) {
+            const bool finite = mx < 0x7C00u;
             auto put = [&](int c, const u32x4 &v) {
                 uint32_t b[2] = {0, 0};
+                if (finite) {
+                    uint32_t w[8];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t q0 = quant1(v[i] & 0xFFFFu, factor, M);
-                    const uint32_t q1 = quant1(v[i] >> 16, factor, M);
-                    b[i >> 1] |= (q0 | (q1 << 8)) << ((i & 1) * 16);
+                    for (int i = 0; i < 8; ++i)
+                        w[i] = quant_bits(kvc_h2f((v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu), factor, M);
+                    b[0] = pack_low_bytes(w[0], w[1], w[2], w[3]);
+                    b[1] = pack_low_bytes(w[4], w[5], w[6], w[7]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t q0 = quant1(v[i] & 0xFFFFu, factor, M);
+                        const uint32_t q1 = quant1(v[i] >> 16, factor, M);
+                        b[i >> 1] |= (q0 | (q1 << 8)) << ((i & 1) * 16);
+                    }
                 }
                 *(uint2 *)(q + c) = make_uint2(b[0], b[1]);
             };
@@ -101,37 +142,6 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restric
             for (int c = lane; c < C; c += 64) q[c] = (uint8_t)quant1(x[c], factor, M);
         }
     }
-}
-
-// The fused passes below, for a finite row (every |x| <= m, so p lies in
-// [0, 2 MAX] up to a rounding and |p| < 2^22): p + 1.5 * 2^23 is rounded to
-// an integer, ties to even, which is rint(p); its fp32 bits are 0x4B400000 +
-// rint(p), the symbol in the low byte.  Rows holding Inf or NaN take the
-// clamped quant1 instead (they are flagged; their symbols only stay in range).
-__device__ __forceinline__ uint32_t quant_bits(float x, float factor, float M)
-{
-    float p = x * factor;
-    p = p + M;
-    return __float_as_uint(p + 12582912.0f);
-}
-
-// The low bytes of four words, b0 lowest.
-__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3)
-{
-    return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
-}
-
-// Row max of the wave's 64 lanes, uniform: DPP steps within quads, half
-// rows and rows, then the row broadcasts; lane 63 ends with the maximum.
-__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v)
-{
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row half mirror
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row bcast 15
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row bcast 31
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // max over the lane's pieces of |x| as bits (sign cleared), two halves per
