@@ -103,6 +103,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return v;
 }
 
+// The dispatcher hands workgroups to the 8 XCDs (each with its own L2) in
+// turn, so block b runs on XCD b % 8.  xcd_block renumbers a grid of nb
+// blocks so that consecutive numbers run on one XCD (a bijection of
+// [0, nb); the last nb % 8 keep their numbers): blocks of one slab, which
+// stage the same CDF rows, then read them through one L2 instead of up to
+// eight.  Which XCD runs a block changes nothing but where its reads hit.
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb)
+{
+#ifdef KVC_NO_XCD_REMAP
+    return b;
+#endif
+    const int64_t per = nb >> 3;
+    if (b >= (per << 3)) return b;
+    return (b & 7) * per + (b >> 3);
+}
+
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
 {
     for (int off = 32; off > 0; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, 64);

@@ -285,8 +285,9 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
     const int q = (int)threadIdx.x % G;   // lane within the stream's group
     const int sl = (int)threadIdx.x / G;  // stream within the block
     const int bps = (p.Tc + SPB - 1) / SPB;
-    const int64_t slab = blockIdx.x / bps;
-    const int tb = (int)(blockIdx.x - slab * bps);
+    const int64_t bl = xcd_block(blockIdx.x, gridDim.x);  // the slab's blocks share an XCD
+    const int64_t slab = bl / bps;
+    const int tb = (int)(bl - slab * bps);
     const int t = tb * SPB + sl;
     const SlabGeom g = slab_geom(p, slab);
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;

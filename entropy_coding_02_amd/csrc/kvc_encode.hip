@@ -50,8 +50,9 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
     // LDS: pairs [CT][A] u32 | symbols [SPB][SW + 16] u8 (VEC16 only)
     extern __shared__ uint32_t lds[];
     const int bps = (p.Tc + 255) / 256;
-    const int64_t grp = blockIdx.x / GB;  // slot region: 256 tokens of one slab
-    const int sub = (int)(blockIdx.x - grp * GB);
+    const int64_t bl = xcd_block(blockIdx.x, gridDim.x);  // a slab's blocks share an XCD
+    const int64_t grp = bl / GB;  // slot region: 256 tokens of one slab
+    const int sub = (int)(bl - grp * GB);
     const int64_t slab = grp / bps;
     const int tb = (int)(grp - slab * bps);
     const SlabGeom g = slab_geom(p, slab);
