@@ -109,7 +109,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 // [0, nb); the last nb % 8 keep their numbers): blocks of one slab, which
 // stage the same CDF rows, then read them through one L2 instead of up to
 // eight.  Which XCD runs a block changes nothing but where its reads hit.
-__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb)
+__host__ __device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb)
 {
 #ifdef KVC_NO_XCD_REMAP
     return b;

@@ -5,9 +5,13 @@
 #include <string.h>
 #include <vector>
 
+#include "../../entropy_coding_02_amd/csrc/kvc_common.h"
 #include "../../entropy_coding_02_amd/csrc/lane_coder.h"
 
 extern "C" {
+
+// The kernels' XCD-aware block renumbering (kvc_common.h).
+int64_t hostsim_xcd_block(int64_t b, int64_t nb) { return xcd_block(b, nb); }
 
 // Encode one stream into `slot` (>= round_up(2C+16, 16) bytes); returns its length.
 int64_t hostsim_encode_stream(const uint8_t *q, int32_t C, int32_t A, const uint16_t *cdf_rows,

@@ -18,14 +18,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "hostsim", "hostsim.hip")
 LIB = os.path.join(HERE, "hostsim", "libhostsim.so")
 HDR = os.path.join(os.path.dirname(HERE), "entropy_coding_02_amd", "csrc", "lane_coder.h")
+COMMON = os.path.join(os.path.dirname(HERE), "entropy_coding_02_amd", "csrc", "kvc_common.h")
 
 
 @pytest.fixture(scope="module")
 def hs():
-    newest = max(os.path.getmtime(SRC), os.path.getmtime(HDR))
+    newest = max(os.path.getmtime(SRC), os.path.getmtime(HDR), os.path.getmtime(COMMON))
     if not os.path.exists(LIB) or os.path.getmtime(LIB) < newest:
         tmp = LIB + f".tmp{os.getpid()}"
         subprocess.check_call(["/opt/rocm/bin/hipcc", "-std=c++17", "-O2", "--offload-arch=gfx950",
+                               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                                "-fPIC", "-shared", "-o", tmp, SRC])
         os.replace(tmp, LIB)
     lib = ctypes.CDLL(LIB)
@@ -35,6 +37,8 @@ def hs():
     lib.hostsim_decode_stream.restype = ctypes.c_int
     lib.hostsim_decode_stream.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32]
+    lib.hostsim_xcd_block.restype = ctypes.c_int64
+    lib.hostsim_xcd_block.argtypes = [ctypes.c_int64, ctypes.c_int64]
     return lib
 
 
@@ -141,3 +145,15 @@ def test_corrupt_streams_match_oracle_flag(hs, search):
             q_o, bad_o = oracle.decode_stream(data, rows)
             q_h, bad_h = h_decode(hs, buf, 0, len(data), rows, search=search)
             assert bad_o == bad_h and np.array_equal(q_o, q_h)
+
+
+def test_xcd_block_renumbering_is_a_bijection(hs):
+    """The kernels' XCD-aware block numbering covers every block exactly once
+    and gives the blocks of one XCD (b % 8) consecutive numbers."""
+    for nb in list(range(0, 70)) + [255, 256, 257, 1024, 4099, 16384]:
+        got = [hs.hostsim_xcd_block(b, nb) for b in range(nb)]
+        assert sorted(got) == list(range(nb)), nb
+        per = nb // 8
+        for x in range(8):
+            mine = sorted(got[b] for b in range(x, 8 * per, 8))
+            assert mine == list(range(x * per, (x + 1) * per)), (nb, x)
