@@ -35,9 +35,13 @@ __device__ __forceinline__ uint32_t quant1(uint32_t bits, float factor, float M)
 // an integer, ties to even, which is rint(p); its fp32 bits are 0x4B400000 +
 // rint(p), the symbol in the low byte.  Rows holding Inf or NaN take the
 // clamped quant1 instead (they are flagged; their symbols only stay in range).
+// The product is written as fma(x, factor, 0): one rounding of the exact
+// product, the same value as x * factor (a zero's sign aside, which the
+// + MAX that follows erases), and with x converted from fp16 the compiler
+// folds the conversion into one v_fma_mix_f32.
 __device__ __forceinline__ uint32_t quant_bits(float x, float factor, float M)
 {
-    float p = x * factor;
+    float p = __builtin_fmaf(x, factor, 0.0f);
     p = p + M;
     return __float_as_uint(p + 12582912.0f);
 }
