@@ -91,8 +91,9 @@ const char *kvc_status_string(int status);
  *   kvc_alphabet          A = max over layers and K|V of bins ([CG] 2.3 step 2
  *                         sizes the CDF by the largest bins value)
  *   kvc_scratch_bytes     device scratch kvc_encode needs: a slot of
- *                         round_up(2C+16, 16) bytes for each of the 256 lanes of
- *                         every slab's ceil(chunk_tokens/256) blocks, plus 8 bytes per slab
+ *                         round_up(2C+16, 16) bytes for each of the 256 token
+ *                         rows of every slab's ceil(chunk_tokens/256) slot
+ *                         regions, plus 8 bytes per slab
  *   kvc_max_payload_bytes an upper bound of the payload: n_streams * (2C+1) */
 int32_t kvc_alphabet(const kvc_desc *desc);
 int64_t kvc_n_chunks(const kvc_desc *desc);
