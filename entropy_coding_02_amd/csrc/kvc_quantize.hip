@@ -248,10 +248,12 @@ __global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__
 #pragma unroll
         for (int j = 0; j < 4; ++j) base[k][j] = 4u * (uint32_t)hist_word(0, 2 * j, lane + 64 * k, C8) - 0x400000u * rowb;
     __syncthreads();
-    // Software pipeline over the wave's rows t = wid, wid + nw, ...: the next
-    // row's pieces are loaded while the current one is processed, and a
-    // row's symbol stores go out after the next row's data has arrived, so
-    // the wait for a load never also waits for stores issued just before it.
+    // Software pipeline over the wave's rows t = wid, wid + nw, ...: the rows
+    // two steps ahead are loaded while the current one is processed (three
+    // buffers, in turn, so no registers are copied), so a wave keeps two rows
+    // of loads in flight; and a row's symbol stores go out after the next
+    // row's data has arrived, so the wait for a load never also waits for
+    // stores issued just before it.
     auto load_row = [&](int t, u32x4 *r) {
         const uint16_t *x = kv + (g.row0 + t) * C;
 #pragma unroll
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__
             r[k] = pi < C8 ? *(const u32x4 *)(x + 8 * pi) : u32x4{0, 0, 0, 0};
         }
     };
-    u32x4 cur[KREG], nxt[KREG];
+    u32x4 ba[KREG], bb[KREG], bc[KREG];
     uint32_t qb[KREG][2];  // the previous row's symbols, not yet stored
     int64_t qrow = -1;
     auto store_row = [&]() {
@@ -270,12 +272,12 @@ __global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__
             if (pi < C8) *(uint2 *)(sym + qrow * C + 8 * pi) = make_uint2(qb[k][0], qb[k][1]);
         }
     };
-    if (wid < g.nj) load_row(wid, cur);
-    for (int t = wid; t < g.nj; t += nw) {
+    // row t from cur; the loads of row t + 2 nw into pf
+    auto step = [&](int t, const u32x4(&cur)[KREG], u32x4(&pf)[KREG]) {
         const int64_t row = g.row0 + t;
         uint32_t mx = lane_absmax<KREG>(cur);
         if (qrow >= 0) store_row();
-        if (t + nw < g.nj) load_row(t + nw, nxt);
+        if (t + 2 * nw < g.nj) load_row(t + 2 * nw, pf);
         mx = wave_max_dpp(mx);
         const float m = kvc_h2f(mx);
         const float factor = (mx != 0) ? M / m : 0.0f;
@@ -311,8 +313,15 @@ __global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__
             }
         }
         qrow = row;
-#pragma unroll
-        for (int k = 0; k < KREG; ++k) cur[k] = nxt[k];
+    };
+    if (wid < g.nj) load_row(wid, ba);
+    if (wid + nw < g.nj) load_row(wid + nw, bb);
+    for (int t = wid; t < g.nj; t += 3 * nw) {
+        step(t, ba, bc);
+        if (t + nw >= g.nj) break;
+        step(t + nw, bb, ba);
+        if (t + 2 * nw >= g.nj) break;
+        step(t + 2 * nw, bc, bb);
     }
     if (qrow >= 0) store_row();
     __syncthreads();
