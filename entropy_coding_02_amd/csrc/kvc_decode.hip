@@ -119,7 +119,8 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
         } else {
             s = cdf_search<NSTEP>(r16 + cl * P2, (uint32_t)A, r, d.code);
         }
-        const u32x2 e = *(const lds_u32x2 *)(pr + 2 * (cl * A + (int)s));
+        const lds_u32 *prow = pr + 2 * cl * A;  // uniform: the address is one shift-add of s
+        const u32x2 e = *(const lds_u32x2 *)(prow + 2 * s);
         bad |= dec_advance(d, r, e.x & 0xFFFFu, e.x >> 16);
         lv = __uint_as_float(e.y);
         return s;
