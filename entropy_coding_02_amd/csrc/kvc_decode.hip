@@ -11,6 +11,9 @@
 // is staged next to each (start, frequency) pair, so one read gives both).
 // Because fl(fl(q - MAX) / MAX) is exactly the table entry, the fused output
 // equals the separate dequantization bit for bit.
+//
+// k_decode_group: launches of few streams, G lanes per stream splitting each
+// symbol's search over rows of (start, frequency) keys (comment at the kernel).
 #include "kvc_common.h"
 #include "kvc_kernels.h"
 #include "lane_coder.h"

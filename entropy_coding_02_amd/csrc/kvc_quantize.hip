@@ -6,7 +6,8 @@
 // max of (bits & 0x7FFF): exact, and it detects Inf/NaN (>= 0x7C00) for free.
 // The quantizer runs in fp32 with one rounding per operation (the library is
 // built with -ffp-contract=off): factor = MAX / m by IEEE division,
-// p = x * factor, p = p + MAX, q = rint(p) (round half to even).
+// p = x * factor, p = p + MAX, q = rint(p) (round half to even).  (The fast
+// paths write the product as fma(x, factor, 0), the same single rounding.)
 #include "kvc_common.h"
 #include "kvc_kernels.h"
 
