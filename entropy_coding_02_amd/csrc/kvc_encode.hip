@@ -318,6 +318,270 @@ __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
     }
 }
 
+// One stream coded by a quad of lanes (lane_coder.h, "one stream coded by G
+// lanes"), for launches of few streams: 64 streams per block, 16 per wave,
+// a slot region's 256 tokens over four blocks.  C splits into 4 blocks of B
+// = C / 4 channels (C % (4 CT) == 0, B % CTB == 0, B % 16 == 0).
+//  A. Every lane follows its stream's range chain over all C channels, in
+//     tiles of CT channels staged as k_encode stages them (pairs, and the 64
+//     streams' symbols), recording the range at its own block's start and the
+//     shift totals at every block boundary.
+//  B. Lane q codes channels [q B, q B + B) with the full coder from low = 0,
+//     its shifted-out bytes going straight to their stream positions in the
+//     stream's slot (contiguous here, one unaligned dword store per flush).
+//     Tiles of CTB channels of all four blocks are staged at once: four pair
+//     tiles, and the symbols of 64 streams x 4 blocks.
+//  C. After a barrier, lane 0 of the quad adds the blocks' lows and the final
+//     0xFFFFFF and trims: the stream's bytes and length are those of k_encode.
+// Slots: stream j of slot region grp at slots + (grp * 256 + j) * slot_bytes.
+template <int PER>
+__global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict__ sym,
+                                                      const uint16_t *__restrict__ cdf,
+                                                      uint8_t *__restrict__ slots,
+                                                      uint16_t *__restrict__ stream_len, KParams p, int CT,
+                                                      int CTB)
+{
+    constexpr int SPB = 64;      // streams per block
+    constexpr int GB = 4;        // blocks per slot region
+    constexpr int SW = 128;      // phase A symbol tile width (channels)
+    constexpr int sstride = SW + 16;
+    extern __shared__ uint32_t lds[];
+    const int bps = (p.Tc + 255) / 256;
+    const int64_t bl = xcd_block(blockIdx.x, gridDim.x);  // a slab's blocks share an XCD
+    const int64_t grp = bl / GB;
+    const int sub = (int)(bl - grp * GB);
+    const int64_t slab = grp / bps;
+    const int tb = (int)(grp - slab * bps);
+    const SlabGeom g = slab_geom(p, slab);
+    const int r0 = tb * 256 + sub * SPB;  // the block's first token
+    if (r0 >= g.nj) return;               // uniform
+    const int lane = (int)threadIdx.x & 63, wid = (int)threadIdx.x >> 6;
+    const int qd = lane & 3;                  // this lane's block of channels
+    const int jj = wid * 16 + (lane >> 2);    // stream within the block
+    const int t = r0 + jj;
+    const bool active = t < g.nj;
+    const int C = p.C, A = p.A, B = C / 4;
+    const uint16_t *rows = cdf + slab * C * A;
+    const int64_t row = g.row0 + (active ? t : 0);
+    uint8_t *const myslot = slots + ((int64_t)grp * 256 + sub * SPB + jj) * p.slot_bytes;
+
+    // ---- A: the range chain
+    lds_u32 *const pairs = (lds_u32 *)lds;
+    lds_u8 *const stile = (lds_u8 *)(pairs + CT * A);
+    constexpr int NP = SPB * (SW / 16) / 256;  // symbol pieces per thread
+    u32x4 sv[NP];
+    auto load_syms = [&](int s0) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int ch = (int)threadIdx.x + 256 * i;
+            const int r = ch / (SW / 16), part = ch - r * (SW / 16);
+            const int tok = r0 + r, cc = s0 + part * 16;
+            sv[i] = (tok < g.nj && cc < C) ? *(const u32x4 *)(sym + (g.row0 + tok) * C + cc)
+                                           : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto store_syms = [&]() {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int ch = (int)threadIdx.x + 256 * i;
+            const int r = ch / (SW / 16), part = ch - r * (SW / 16);
+            *(lds_u32x4 *)(stile + r * sstride + part * 16) = sv[i];
+        }
+    };
+    uint32_t range = 0xFFFFFFFFu, S = 0, rq = 0, S1 = 0, S2 = 0, S3 = 0;
+    {
+        PairTile<PER> pt;
+        pt.load(rows, 0, CT, C, A);
+        load_syms(0);
+        const int ntiles = C / CT;
+        for (int it = 0; it < ntiles; ++it) {
+            const int c0 = it * CT;
+            const int s0 = c0 - c0 % SW;
+            const bool new_stile = c0 == s0;
+            __syncthreads();
+            pt.store(pairs, CT, A);
+            if (new_stile) store_syms();
+            __syncthreads();
+            if (it + 1 < ntiles) pt.load(rows, c0 + CT, CT, C, A);
+            if (new_stile && s0 + SW < C) load_syms(s0 + SW);
+            // block boundaries fall on tile starts
+            if (c0 == B) S1 = S;
+            if (c0 == 2 * B) S2 = S;
+            if (c0 == 3 * B) S3 = S;
+            rq = c0 == qd * B ? range : rq;
+            if (!active) continue;
+            const lds_u8 *my = stile + jj * sstride;
+            for (int cg = c0; cg < c0 + CT; cg += 16) {
+                const u32x4 v = *(const lds_u32x4 *)(my + (cg - s0));
+                const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+                const lds_u32 *trow = pairs + (cg - c0) * A;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t pv[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int k = h * 8 + i;
+                        uint32_t sy = (wv[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+                        sy = min(sy, (uint32_t)A - 1u);
+                        pv[i] = trow[k * A + sy];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) S += enc_range_step(range, pv[i] >> 16);
+                }
+            }
+        }
+    }
+    const uint32_t SC = S;
+
+    // ---- B: each lane codes its block
+    lds_u32 *const pairsB = (lds_u32 *)lds;                    // [4][CTB][A]
+    lds_u8 *const symB = (lds_u8 *)(pairsB + 4 * CTB * A);    // [64 x 4 rows][CTB + 16]
+    const int bstride = CTB + 16;
+    const int npB = SPB * 4 * (CTB / 16);  // 16-byte symbol pieces per tile (<= 512)
+    u32x4 svB[2];
+    auto load_symsB = [&](int j0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ch = (int)threadIdx.x + 256 * i;
+            svB[i] = u32x4{0, 0, 0, 0};
+            if (ch < npB) {
+                const int r = ch / (CTB / 16), part = ch - r * (CTB / 16);  // r = stream * 4 + block
+                const int tok = r0 + (r >> 2), cc = (r & 3) * B + j0 + part * 16;
+                if (tok < g.nj) svB[i] = *(const u32x4 *)(sym + (g.row0 + tok) * C + cc);
+            }
+        }
+    };
+    auto store_symsB = [&]() {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ch = (int)threadIdx.x + 256 * i;
+            if (ch < npB) {
+                const int r = ch / (CTB / 16), part = ch - r * (CTB / 16);
+                *(lds_u32x4 *)(symB + r * bstride + part * 16) = svB[i];
+            }
+        }
+    };
+    EncState e;
+    enc_init(e);
+    e.range = rq;
+    const uint32_t Sg = qd == 0 ? 0u : qd == 1 ? S1 : qd == 2 ? S2 : S3;
+    const SplitOut out{myslot, Sg / 8u};
+    {
+        PairTile<2> pb[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) pb[b].load(rows, b * B, CTB, C, A);
+        load_symsB(0);
+        for (int j0 = 0; j0 < B; j0 += CTB) {
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < 4; ++b) pb[b].store(pairsB + b * CTB * A, CTB, A);
+            store_symsB();
+            __syncthreads();
+            if (j0 + CTB < B) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) pb[b].load(rows, b * B + j0 + CTB, CTB, C, A);
+                load_symsB(j0 + CTB);
+            }
+            if (!active) continue;
+            const lds_u8 *my = symB + (jj * 4 + qd) * bstride;
+            const lds_u32 *ptab = pairsB + qd * CTB * A;
+            for (int cg = 0; cg < CTB; cg += 16) {
+                const u32x4 v = *(const lds_u32x4 *)(my + cg);
+                const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+                const lds_u32 *trow = ptab + cg * A;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t pv[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int k = h * 8 + i;
+                        uint32_t sy = (wv[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+                        sy = min(sy, (uint32_t)A - 1u);
+                        pv[i] = trow[k * A + sy];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) enc_pair(e, pv[i], out);
+                }
+            }
+        }
+    }
+    if (active) {
+        enc_block_end(e, out);
+        if (qd == 3)
+            for (uint32_t b = 0; b < 4u; ++b) *out.byte(SC / 8u + b) = (uint8_t)(e.lo >> (24u - 8u * b));
+    }
+    // ---- C: the lows added, 0xFFFFFF added, the tail trimmed (lane 0 of the quad)
+    const int qbase = lane & ~3;
+    const uint32_t lo0 = (uint32_t)__shfl((int)e.lo, qbase, 64);
+    const uint32_t lo1 = (uint32_t)__shfl((int)e.lo, qbase + 1, 64);
+    const uint32_t lo2 = (uint32_t)__shfl((int)e.lo, qbase + 2, 64);
+    __syncthreads();  // every block's bytes are in the slot
+    if (active && qd == 0) {
+        split_add(out, S1 / 8u, lo0, 4);
+        split_add(out, S2 / 8u, lo1, 4);
+        split_add(out, S3 / 8u, lo2, 4);
+        const uint32_t nt = SC / 8u + 4u;
+        split_add(out, nt - 3u, 0xFFFFFFu, 3);
+        stream_len[g.sid0 + t] = (uint16_t)split_trim(out, nt - 3u);
+    }
+}
+
+// k_pack for slots holding each stream contiguously (k_encode_split): a wave
+// per 16 streams of a slot region finds their payload offsets as k_pack does,
+// then copies them one after the other, lane j taking the stream's dword j
+// (aligned loads) and storing it at its byte offset (unaligned dword stores;
+// the last len % 4 bytes as byte stores).  Nothing is written at or past
+// payload_cap.
+__global__ __launch_bounds__(64) void k_pack_flat(const uint8_t *__restrict__ slots,
+                                                  const uint16_t *__restrict__ stream_len,
+                                                  const uint64_t *__restrict__ slab_off,
+                                                  uint8_t *__restrict__ payload, int64_t payload_cap,
+                                                  KParams p)
+{
+    constexpr int SPW = 16, WPR = 256 / SPW;
+    const int bps = (p.Tc + 255) / 256;
+    const int64_t eb = blockIdx.x / WPR;  // slot region
+    const int wq = (int)(blockIdx.x - eb * WPR);
+    const int64_t slab = eb / bps;
+    const int tb = (int)(eb - slab * bps);
+    const SlabGeom g = slab_geom(p, slab);
+    const int lane = (int)threadIdx.x;
+    const int t0 = tb * 256 + wq * SPW;
+    if (t0 >= g.nj) return;
+    const int t = t0 + lane;
+    const bool active = lane < SPW && t < g.nj;
+    uint32_t pre = 0;
+    for (int i = lane; i < t0; i += 64) pre += stream_len[g.sid0 + i];
+    pre = wave_sum_u32(pre);
+    const uint32_t len = active ? stream_len[g.sid0 + t] : 0u;
+    uint32_t incl = len;
+    for (int off = 1; off < 64; off <<= 1) {
+        uint32_t v = (uint32_t)__shfl_up((int)incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    const uint64_t o = slab_off[slab] + pre + incl - len;
+    const uint32_t olo = (uint32_t)o, ohi = (uint32_t)(o >> 32);
+    const uint64_t cap = (uint64_t)payload_cap;
+    const uint8_t *src0 = slots + ((int64_t)eb * 256 + wq * SPW) * p.slot_bytes;
+    for (int i = 0; i < SPW; ++i) {
+        const uint32_t len_i = (uint32_t)__builtin_amdgcn_readlane((int)len, i);
+        const uint64_t o_i = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ohi, i) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)olo, i);
+        const uint32_t *src = (const uint32_t *)(src0 + (int64_t)i * p.slot_bytes);
+        for (uint32_t j = (uint32_t)lane; 4u * j < len_i; j += 64u) {
+            const uint32_t v = src[j];
+            const uint64_t b = o_i + 4u * j;
+            const uint32_t nb = min(len_i - 4u * j, 4u);
+            if (nb == 4u && b + 4u <= cap) {
+                __builtin_memcpy(payload + b, &v, 4);
+            } else {
+                for (uint32_t q = 0; q < nb; ++q)
+                    if (b + q < cap) payload[b + q] = (uint8_t)(v >> (8u * q));
+            }
+        }
+    }
+}
+
 __global__ void k_zero_u64(uint64_t *dst) { *dst = 0; }
 
 }  // namespace
@@ -340,6 +604,16 @@ static int enc_symbol_tile(int64_t n_streams) { return n_streams <= KVC_ENC_WIDE
 
 // Streams coded per wave.
 static int enc_streams_per_wave(int64_t n_streams) { return n_streams <= KVC_ENC_SPARSE_MAX_STREAMS ? 16 : 64; }
+
+// Launches of at most this many streams code each stream with a quad of lanes
+// (k_encode_split) where the shape allows it.
+#ifndef KVC_ENC_SPLIT_MAX_STREAMS
+#define KVC_ENC_SPLIT_MAX_STREAMS 16384
+#endif
+
+// Phase-B tile width of k_encode_split: 32 channels, or 16 for 64-entry rows
+// (the four pair tiles of a step fit 512 pairs per tile).
+static int enc_split_tile(int A) { return A <= 32 ? 32 : 16; }
 
 // Channels per tile (a power of two, 16 to the symbol tile width).  With few
 // streams a tile of 16 channels is coded in less time than its successor's
@@ -377,6 +651,27 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
     const int sw = enc_symbol_tile(p.n_streams);
     const int spw = enc_streams_per_wave(p.n_streams);
     const dim3 grid((unsigned)(regions * (64 / spw)));
+    const int ctb = enc_split_tile(p.A);
+    if (vec16 && p.n_streams <= KVC_ENC_SPLIT_MAX_STREAMS && p.A <= 64 && p.C % (4 * CT) == 0 &&
+        (p.C / 4) % ctb == 0) {
+        const size_t lds_a = lds_pairs + 64 * (size_t)(128 + 16);
+        const size_t lds_b = 4 * (size_t)ctb * p.A * sizeof(uint32_t) + 256 * (size_t)(ctb + 16);
+        const size_t lds = lds_a > lds_b ? lds_a : lds_b;
+        const dim3 sgrid((unsigned)(regions * 4));
+        if (per <= 2)
+            hipLaunchKernelGGL((k_encode_split<2>), sgrid, dim3(256), lds, stream, sym, cdf, slots,
+                               stream_len, p, CT, ctb);
+        else
+            hipLaunchKernelGGL((k_encode_split<8>), sgrid, dim3(256), lds, stream, sym, cdf, slots,
+                               stream_len, p, CT, ctb);
+        hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
+                           slab_total, p);
+        hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, slab_total, slab_off, p.n_slabs,
+                           payload_cap, (const uint64_t *)nullptr, status);
+        hipLaunchKernelGGL(k_pack_flat, dim3((unsigned)(regions * 16)), dim3(64), 0, stream, slots,
+                           stream_len, slab_off, payload, payload_cap, p);
+        return hipGetLastError();
+    }
 #define KVC_ENC(V, P, S, W, L)                                                                       \
     hipLaunchKernelGGL((k_encode<V, P, S, W>), grid, dim3(256), L, stream, sym, cdf, slots, stream_len, \
                        p, CT)

@@ -148,6 +148,100 @@ KVC_HD uint32_t enc_finish(EncState &e, const Out &out)
     return 0;
 }
 
+// ------------------------------------------- one stream coded by G lanes
+//
+// The interval arithmetic splits: the range never depends on low, and low is
+// a sum.  With r_i = range_i >> 16, S_i the bits shifted out before symbol i
+// (S_0 = 0) and S at the end, the coder's final low is
+//     X = sum_i r_i * cdf_{s_i} * 2^(S - S_i)
+// (each term is added, then shifted with everything after it).  Cut the
+// symbols into consecutive blocks.  Block g coded alone, from low = 0 and the
+// range the whole chain has at its start, gives P_g = sum over its symbols of
+// r_i * cdf_{s_i} * 2^(E_g - S_i) (E_g = S at its end) as (E_g - S_g)/8
+// shifted-out bytes followed by its 4-byte low, and X = sum_g P_g * 2^(S - E_g).
+// In stream byte positions P_g starts at S_g / 8, so consecutive blocks
+// overlap only where P_g's low meets P_{g+1}'s first 4 bytes.  The stream is
+// the first S/8 + 1 bytes of X + 0xFFFFFF written in S/8 + 4 bytes, trailing
+// zeros removed: what enc_finish writes.
+//
+// Hence G lanes can code one stream: each follows the range chain over the
+// whole stream (no low, no bytes: a few operations a symbol), then codes its
+// own block with the full coder, writing its shifted-out bytes straight to
+// their stream positions; a last step adds every block's low (and the
+// 0xFFFFFF) at its position, the carry running into the bytes before it,
+// and trims.
+
+// One range-chain step: the interval width after a symbol of frequency fr,
+// renormalised; returns the bits shifted.
+KVC_HD uint32_t enc_range_step(uint32_t &range, uint32_t fr)
+{
+    range = (range >> 16) * fr;
+    const uint32_t n = kvc_renorm_bits(range);
+    range <<= n;
+    return n;
+}
+
+// A stream slot holding the stream's bytes contiguously, viewed from one
+// block whose first byte is at stream position off.  load/store move the
+// block's dword i (its bytes 4i .. 4i + 3, the first in the low byte, as
+// SlotOut does) as one unaligned 4-byte access.
+struct SplitOut {
+    uint8_t *base;
+    uint32_t off;
+    KVC_HD uint8_t *byte(uint32_t pos) const { return base + pos; }
+    KVC_HD uint32_t load(uint32_t i) const
+    {
+        uint32_t v;
+        __builtin_memcpy(&v, base + off + 4u * i, 4);
+        return v;
+    }
+    KVC_HD void store(uint32_t i, uint32_t v) const { __builtin_memcpy(base + off + 4u * i, &v, 4); }
+};
+
+// End of a block: resolve a carry past the pending bytes, then write them
+// after the block's dwords.  Returns the number of pending bytes; the low
+// stays in e.lo.
+template <class Out>
+KVC_HD uint32_t enc_block_end(EncState &e, const Out &out)
+{
+    const uint32_t kb = e.kb;  // < 48
+    if ((e.pb >> kb) != 0) {
+        enc_carry_into_written(out, e.w);
+        e.pb &= ((uint64_t)1 << kb) - 1u;
+    }
+    const uint32_t k = kb >> 3;
+    for (uint32_t i = 0; i < k; ++i) *out.byte(out.off + 4u * e.w + i) = (uint8_t)(e.pb >> (8u * (k - 1u - i)));
+    return k;
+}
+
+// Add the nb-byte (<= 4) big-endian value v at stream positions [pos, pos + nb)
+// of the stream f addresses (f.off unused), the carry running into the bytes
+// before pos.
+KVC_HD void split_add(const SplitOut &f, uint32_t pos, uint32_t v, uint32_t nb)
+{
+    uint32_t carry = 0;
+    for (uint32_t b = nb; b-- > 0;) {
+        uint8_t *q = f.byte(pos + b);
+        const uint32_t t = (uint32_t)*q + ((v >> (8u * (nb - 1u - b))) & 0xFFu) + carry;
+        *q = (uint8_t)t;
+        carry = t >> 8;
+    }
+    for (uint32_t q = pos; carry != 0 && q-- > 0;) {
+        uint8_t *c = f.byte(q);
+        const uint32_t t = (uint32_t)*c + 1u;
+        *c = (uint8_t)t;
+        carry = t >> 8;
+    }
+}
+
+// Stream length once every byte of positions [0, n) is in place: n without
+// its trailing zero bytes.
+KVC_HD uint32_t split_trim(const SplitOut &f, uint32_t n)
+{
+    while (n > 0 && *f.byte(n - 1u) == 0) --n;
+    return n;
+}
+
 // ----------------------------------------------------------------- decoder
 
 // Funnel shift: bits [sh, sh + 32) of the 64-bit value hi:lo (sh < 32).

@@ -29,6 +29,53 @@ int64_t hostsim_encode_stream(const uint8_t *q, int32_t C, int32_t A, const uint
     return enc_finish(e, out);
 }
 
+// Encode one stream the way the split encoder kernel does with G lanes
+// (lane_coder.h, "one stream coded by G lanes"): the range chain over the
+// whole stream, then each block of ceil(C/G) channels coded alone with its
+// bytes written at their stream positions, then the blocks' lows and
+// 0xFFFFFF added and the tail trimmed.  Same slot and result as
+// hostsim_encode_stream.
+int64_t hostsim_encode_stream_split(const uint8_t *q, int32_t C, int32_t A, const uint16_t *cdf_rows,
+                                    uint8_t *slot, int32_t G)
+{
+    auto pair_of = [&](int32_t c) {
+        const uint16_t *row = cdf_rows + (int64_t)c * A;
+        const uint32_t s = q[c] < (uint32_t)A ? q[c] : (uint32_t)A - 1u;
+        return cdf_pair(row[s], s + 1 < (uint32_t)A ? row[s + 1] : 65536u);
+    };
+    const int32_t B = (C + G - 1) / G;
+    std::vector<uint32_t> r0(G), s0(G + 1);
+    uint32_t range = 0xFFFFFFFFu, S = 0;
+    for (int32_t c = 0; c < C; ++c) {
+        if (c % B == 0) {
+            r0[c / B] = range;
+            s0[c / B] = S;
+        }
+        S += enc_range_step(range, pair_of(c) >> 16);
+    }
+    for (int32_t g = (C + B - 1) / B; g < G; ++g) {  // blocks past the last channel
+        r0[g] = range;
+        s0[g] = S;
+    }
+    s0[G] = S;
+    const SplitOut f{slot, 0};
+    std::vector<uint32_t> lo(G);
+    for (int32_t g = 0; g < G; ++g) {
+        EncState e;
+        enc_init(e);
+        e.range = r0[g];
+        const SplitOut out{slot, s0[g] / 8u};
+        for (int32_t c = g * B; c < C && c < (g + 1) * B; ++c) enc_pair(e, pair_of(c), out);
+        enc_block_end(e, out);
+        lo[g] = e.lo;
+    }
+    for (uint32_t b = 0; b < 4u; ++b) *f.byte(S / 8u + b) = (uint8_t)(lo[G - 1] >> (24u - 8u * b));
+    for (int32_t g = 0; g + 1 < G; ++g) split_add(f, s0[g + 1] / 8u, lo[g], 4);
+    const uint32_t nt = S / 8u + 4u;
+    split_add(f, nt - 3u, 0xFFFFFFu, 3);
+    return split_trim(f, nt - 3u);
+}
+
 // Decode the stream at [off, off+len) of a buffer of `cap` bytes (a multiple
 // of 4, at least 4); returns the corrupt flag.
 // search 0: binary lifting; 1: the two-level search where the padded row has

@@ -55,6 +55,11 @@ SMALL = {
     "fused_L2_C64_T16421_Tc128": cfg_of(2, 64, 16421, 128, ((0, 1, 32), (1, 2, 16)), seed=12),
     # fused pass at A = 64: a 128 KB LDS histogram
     "fused_70b_shape_T300": kvgen.CONFIGS["c5"].scaled(n_tokens=300),
+    # a quad of lanes per stream in the encoder (k_encode_split: at most 16384
+    # streams, C a multiple of 4 CDF tiles): padded rows, 64-entry rows, a
+    # ragged chunk
+    "split_A24_C512_T200_Tc128": cfg_of(2, 512, 200, 128, ((0, 1, 24), (1, 2, 16)), seed=15),
+    "split_A64_C256_T300": cfg_of(2, 256, 300, 256, ((0, 1, 64), (1, 2, 32)), seed=16),
     # more than 16384 streams: one lane per stream (the launches above with
     # few streams decode with a group of lanes per stream), rows of 8 and 16
     "one_lane_A8_C16_T9000": cfg_of(1, 16, 9000, 256, ((0, 1, 8),), seed=13),

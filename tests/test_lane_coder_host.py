@@ -37,6 +37,8 @@ def hs():
     lib.hostsim_decode_stream.restype = ctypes.c_int
     lib.hostsim_decode_stream.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32]
+    lib.hostsim_encode_stream_split.restype = ctypes.c_int64
+    lib.hostsim_encode_stream_split.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32]
     lib.hostsim_xcd_block.restype = ctypes.c_int64
     lib.hostsim_xcd_block.argtypes = [ctypes.c_int64, ctypes.c_int64]
     return lib
@@ -62,10 +64,23 @@ def h_decode(lib, buf, off, length, rows, cap=None, search=0):
     return q, bool(bad)
 
 
+def h_encode_split(lib, q, rows, G):
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+    C, A = rows.shape
+    slot = np.full((2 * C + 16 + 15) // 16 * 16, 0xAB, dtype=np.uint8)
+    n = lib.hostsim_encode_stream_split(q.ctypes.data, C, A, rows.ctypes.data, slot.ctypes.data, G)
+    return slot[:n].tobytes()
+
+
 def check(lib, q, rows):
+    """The lane coder, and the split coder with 2, 3, 4 and 8 lanes, against the oracle."""
     want = oracle.encode_stream(np.asarray(q, np.uint8), rows)
     got = h_encode(lib, q, rows)
     assert got == want, (len(got), len(want))
+    for G in (2, 3, 4, 8):
+        got = h_encode_split(lib, q, rows, G)
+        assert got == want, (G, len(got), len(want))
     return want
 
 
