@@ -318,33 +318,70 @@ __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
     }
 }
 
+// A chunk of k_encode_split's pair table in registers: chunk m < NA is
+// channels [m CH, m CH + CH); chunk NA + m is channels [b B + m CQ, b B +
+// m CQ + CQ) of the four blocks b (local channel lc is block lc / CQ).
+template <int PERC>
+struct ChunkPairs {
+    uint32_t w[PERC], n2[PERC];
+
+    __device__ void load(const uint16_t *rows, int m, int NA, int CH, int CQ, int B, int A)
+    {
+        const int half = A >> 1, npairs = CH * half;
+#pragma unroll
+        for (int i = 0; i < PERC; ++i) {
+            const int e = (int)threadIdx.x + 256 * i;
+            w[i] = 0;
+            n2[i] = 65536u;
+            if (e < npairs) {
+                const int cl = e / half, k = (e - cl * half) * 2;
+                const int ch = m < NA ? m * CH + cl : (cl / CQ) * B + (m - NA) * CQ + cl % CQ;
+                const uint16_t *row = rows + (int64_t)ch * A;
+                w[i] = *(const uint32_t *)(row + k);
+                if (k + 2 < A) n2[i] = row[k + 2];
+            }
+        }
+    }
+    __device__ void store(lds_u32 *ptab, int CH, int A) const
+    {
+        const int npairs = CH * (A >> 1);
+#pragma unroll
+        for (int i = 0; i < PERC; ++i) {
+            const int e = (int)threadIdx.x + 256 * i;
+            if (e < npairs) {
+                const uint32_t st0 = w[i] & 0xFFFFu, st1 = w[i] >> 16;
+                ptab[2 * e] = cdf_pair(st0, st1);
+                ptab[2 * e + 1] = cdf_pair(st1, n2[i]);
+            }
+        }
+    }
+};
+
 // One stream coded by a quad of lanes (lane_coder.h, "one stream coded by G
 // lanes"), for launches of few streams: 64 streams per block, 16 per wave,
 // a slot region's 256 tokens over four blocks.  C splits into 4 blocks of B
-// = C / 4 channels (C % (4 CT) == 0, B % CTB == 0, B % 16 == 0).
-//  A. Every lane follows its stream's range chain over all C channels, in
-//     tiles of CT channels staged as k_encode stages them (pairs, and the 64
-//     streams' symbols), recording the range at its own block's start and the
-//     shift totals at every block boundary.
+// = C / 4 channels.  The block stages the symbols of all its 64 streams in
+// LDS once, and the CDF pairs in chunks of CH channels (64 KB or less), so
+// each phase waits on memory C / CH times, not once per small tile.
+//  A. Every lane follows its stream's range chain over all C channels,
+//     recording the range at its own block's start and the shift totals at
+//     every block boundary.
 //  B. Lane q codes channels [q B, q B + B) with the full coder from low = 0,
 //     its shifted-out bytes going straight to their stream positions in the
 //     stream's slot (contiguous here, one unaligned dword store per flush).
-//     Tiles of CTB channels of all four blocks are staged at once: four pair
-//     tiles, and the symbols of 64 streams x 4 blocks.
+//     A chunk holds CH / 4 channels of each of the four blocks.
 //  C. After a barrier, lane 0 of the quad adds the blocks' lows and the final
 //     0xFFFFFF and trims: the stream's bytes and length are those of k_encode.
 // Slots: stream j of slot region grp at slots + (grp * 256 + j) * slot_bytes.
-template <int PER>
+// Needs C % CH == 0, CH % 64 == 0, CH * A / 2 <= 256 * PERC.
+template <int PERC>
 __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict__ sym,
                                                       const uint16_t *__restrict__ cdf,
                                                       uint8_t *__restrict__ slots,
-                                                      uint16_t *__restrict__ stream_len, KParams p, int CT,
-                                                      int CTB)
+                                                      uint16_t *__restrict__ stream_len, KParams p, int CH)
 {
-    constexpr int SPB = 64;      // streams per block
-    constexpr int GB = 4;        // blocks per slot region
-    constexpr int SW = 128;      // phase A symbol tile width (channels)
-    constexpr int sstride = SW + 16;
+    constexpr int SPB = 64;  // streams per block
+    constexpr int GB = 4;    // blocks per slot region
     extern __shared__ uint32_t lds[];
     const int bps = (p.Tc + 255) / 256;
     const int64_t bl = xcd_block(blockIdx.x, gridDim.x);  // a slab's blocks share an XCD
@@ -356,154 +393,100 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
     const int r0 = tb * 256 + sub * SPB;  // the block's first token
     if (r0 >= g.nj) return;               // uniform
     const int lane = (int)threadIdx.x & 63, wid = (int)threadIdx.x >> 6;
-    const int qd = lane & 3;                  // this lane's block of channels
-    const int jj = wid * 16 + (lane >> 2);    // stream within the block
+    const int qd = lane & 3;                // this lane's block of channels
+    const int jj = wid * 16 + (lane >> 2);  // stream within the block
     const int t = r0 + jj;
     const bool active = t < g.nj;
-    const int C = p.C, A = p.A, B = C / 4;
+    const int C = p.C, A = p.A, B = C / 4, CQ = CH / 4;
     const uint16_t *rows = cdf + slab * C * A;
-    const int64_t row = g.row0 + (active ? t : 0);
     uint8_t *const myslot = slots + ((int64_t)grp * 256 + sub * SPB + jj) * p.slot_bytes;
+    const int sst = C + 16;  // symbol row stride (bytes)
+    lds_u8 *const stab = (lds_u8 *)lds;                        // [64][C + 16] symbols
+    lds_u32 *const ptab = (lds_u32 *)lds + 16 * sst;           // [CH][A] (start, frequency) pairs
+
+    // chunks of CH channels of pairs, each loaded into registers one chunk
+    // ahead of its use and stored to the table between two barriers
+    const int NA = C / CH, NM = 2 * NA;
+    ChunkPairs<PERC> cp;
+    // the symbols of the block's 64 streams, 16-byte pieces, 16 per thread in
+    // flight, with the first pair chunk
+    {
+        const int per_row = C / 16, npieces = SPB * per_row;
+        cp.load(rows, 0, NA, CH, CQ, B, A);
+        for (int base = 0; base < npieces; base += 256 * 16) {
+            u32x4 v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int ch = base + (int)threadIdx.x + 256 * i;
+                const int r = ch / per_row, part = ch - r * per_row;
+                v[i] = (ch < npieces && r0 + r < g.nj)
+                           ? *(const u32x4 *)(sym + (g.row0 + r0 + r) * C + part * 16)
+                           : u32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int ch = base + (int)threadIdx.x + 256 * i;
+                const int r = ch / per_row, part = ch - r * per_row;
+                if (ch < npieces) *(lds_u32x4 *)(stab + r * sst + part * 16) = v[i];
+            }
+        }
+    }
+    // 16 symbols of this lane's stream from channel c (c % 16 == 0) and their pairs from
+    // table row lc0, in batches of 8
+    const lds_u8 *my = stab + jj * sst;
+    auto pairs16 = [&](int c, int lc0, auto &&use) {
+        const u32x4 v = *(const lds_u32x4 *)(my + c);
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+        const lds_u32 *trow = ptab + lc0 * A;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t pv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int k = h * 8 + i;
+                uint32_t sy = (wv[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+                sy = min(sy, (uint32_t)A - 1u);
+                pv[i] = trow[k * A + sy];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) use(pv[i]);
+        }
+    };
 
     // ---- A: the range chain
-    lds_u32 *const pairs = (lds_u32 *)lds;
-    lds_u8 *const stile = (lds_u8 *)(pairs + CT * A);
-    constexpr int NP = SPB * (SW / 16) / 256;  // symbol pieces per thread
-    u32x4 sv[NP];
-    auto load_syms = [&](int s0) {
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int ch = (int)threadIdx.x + 256 * i;
-            const int r = ch / (SW / 16), part = ch - r * (SW / 16);
-            const int tok = r0 + r, cc = s0 + part * 16;
-            sv[i] = (tok < g.nj && cc < C) ? *(const u32x4 *)(sym + (g.row0 + tok) * C + cc)
-                                           : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto store_syms = [&]() {
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int ch = (int)threadIdx.x + 256 * i;
-            const int r = ch / (SW / 16), part = ch - r * (SW / 16);
-            *(lds_u32x4 *)(stile + r * sstride + part * 16) = sv[i];
-        }
-    };
     uint32_t range = 0xFFFFFFFFu, S = 0, rq = 0, S1 = 0, S2 = 0, S3 = 0;
-    {
-        PairTile<PER> pt;
-        pt.load(rows, 0, CT, C, A);
-        load_syms(0);
-        const int ntiles = C / CT;
-        for (int it = 0; it < ntiles; ++it) {
-            const int c0 = it * CT;
-            const int s0 = c0 - c0 % SW;
-            const bool new_stile = c0 == s0;
-            __syncthreads();
-            pt.store(pairs, CT, A);
-            if (new_stile) store_syms();
-            __syncthreads();
-            if (it + 1 < ntiles) pt.load(rows, c0 + CT, CT, C, A);
-            if (new_stile && s0 + SW < C) load_syms(s0 + SW);
-            // block boundaries fall on tile starts
-            if (c0 == B) S1 = S;
-            if (c0 == 2 * B) S2 = S;
-            if (c0 == 3 * B) S3 = S;
-            rq = c0 == qd * B ? range : rq;
-            if (!active) continue;
-            const lds_u8 *my = stile + jj * sstride;
-            for (int cg = c0; cg < c0 + CT; cg += 16) {
-                const u32x4 v = *(const lds_u32x4 *)(my + (cg - s0));
-                const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-                const lds_u32 *trow = pairs + (cg - c0) * A;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    uint32_t pv[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int k = h * 8 + i;
-                        uint32_t sy = (wv[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                        sy = min(sy, (uint32_t)A - 1u);
-                        pv[i] = trow[k * A + sy];
-                    }
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) S += enc_range_step(range, pv[i] >> 16);
-                }
-            }
+    for (int c0 = 0; c0 < C; c0 += CH) {
+        const int m = c0 / CH;
+        __syncthreads();  // every wave is done with the previous chunk
+        cp.store(ptab, CH, A);
+        __syncthreads();
+        if (m + 1 < NM) cp.load(rows, m + 1, NA, CH, CQ, B, A);
+        for (int cg = c0; cg < c0 + CH; cg += 16) {
+            // block boundaries fall on multiples of 16 channels
+            if (cg == B) S1 = S;
+            if (cg == 2 * B) S2 = S;
+            if (cg == 3 * B) S3 = S;
+            rq = cg == qd * B ? range : rq;
+            if (active) pairs16(cg, cg - c0, [&](uint32_t pr) { S += enc_range_step(range, pr >> 16); });
         }
     }
     const uint32_t SC = S;
 
     // ---- B: each lane codes its block
-    lds_u32 *const pairsB = (lds_u32 *)lds;                    // [4][CTB][A]
-    lds_u8 *const symB = (lds_u8 *)(pairsB + 4 * CTB * A);    // [64 x 4 rows][CTB + 16]
-    const int bstride = CTB + 16;
-    const int npB = SPB * 4 * (CTB / 16);  // 16-byte symbol pieces per tile (<= 512)
-    u32x4 svB[2];
-    auto load_symsB = [&](int j0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int ch = (int)threadIdx.x + 256 * i;
-            svB[i] = u32x4{0, 0, 0, 0};
-            if (ch < npB) {
-                const int r = ch / (CTB / 16), part = ch - r * (CTB / 16);  // r = stream * 4 + block
-                const int tok = r0 + (r >> 2), cc = (r & 3) * B + j0 + part * 16;
-                if (tok < g.nj) svB[i] = *(const u32x4 *)(sym + (g.row0 + tok) * C + cc);
-            }
-        }
-    };
-    auto store_symsB = [&]() {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int ch = (int)threadIdx.x + 256 * i;
-            if (ch < npB) {
-                const int r = ch / (CTB / 16), part = ch - r * (CTB / 16);
-                *(lds_u32x4 *)(symB + r * bstride + part * 16) = svB[i];
-            }
-        }
-    };
     EncState e;
     enc_init(e);
     e.range = rq;
     const uint32_t Sg = qd == 0 ? 0u : qd == 1 ? S1 : qd == 2 ? S2 : S3;
     const SplitOut out{myslot, Sg / 8u};
-    {
-        PairTile<2> pb[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) pb[b].load(rows, b * B, CTB, C, A);
-        load_symsB(0);
-        for (int j0 = 0; j0 < B; j0 += CTB) {
-            __syncthreads();
-#pragma unroll
-            for (int b = 0; b < 4; ++b) pb[b].store(pairsB + b * CTB * A, CTB, A);
-            store_symsB();
-            __syncthreads();
-            if (j0 + CTB < B) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) pb[b].load(rows, b * B + j0 + CTB, CTB, C, A);
-                load_symsB(j0 + CTB);
-            }
-            if (!active) continue;
-            const lds_u8 *my = symB + (jj * 4 + qd) * bstride;
-            const lds_u32 *ptab = pairsB + qd * CTB * A;
-            for (int cg = 0; cg < CTB; cg += 16) {
-                const u32x4 v = *(const lds_u32x4 *)(my + cg);
-                const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-                const lds_u32 *trow = ptab + cg * A;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    uint32_t pv[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int k = h * 8 + i;
-                        uint32_t sy = (wv[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                        sy = min(sy, (uint32_t)A - 1u);
-                        pv[i] = trow[k * A + sy];
-                    }
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) enc_pair(e, pv[i], out);
-                }
-            }
-        }
+    for (int j0 = 0; j0 < B; j0 += CQ) {
+        const int m = NA + j0 / CQ;
+        __syncthreads();
+        cp.store(ptab, CH, A);
+        __syncthreads();
+        if (m + 1 < NM) cp.load(rows, m + 1, NA, CH, CQ, B, A);
+        if (!active) continue;
+        for (int cg = 0; cg < CQ; cg += 16)
+            pairs16(qd * B + j0 + cg, qd * CQ + cg, [&](uint32_t pr) { enc_pair(e, pr, out); });
     }
     if (active) {
         enc_block_end(e, out);
@@ -528,9 +511,10 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
 
 // k_pack for slots holding each stream contiguously (k_encode_split): a wave
 // per 16 streams of a slot region finds their payload offsets as k_pack does,
-// then copies them one after the other, lane j taking the stream's dword j
-// (aligned loads) and storing it at its byte offset (unaligned dword stores;
-// the last len % 4 bytes as byte stores).  Nothing is written at or past
+// then copies them in rounds of 64 dwords: lane j first loads dword j of all
+// 16 streams (aligned loads, all in flight at once), then stores them one
+// stream after the other at their byte offsets (unaligned dword stores; the
+// last len % 4 bytes as byte stores).  Nothing is written at or past
 // payload_cap.
 __global__ __launch_bounds__(64) void k_pack_flat(const uint8_t *__restrict__ slots,
                                                   const uint16_t *__restrict__ stream_len,
@@ -563,20 +547,29 @@ __global__ __launch_bounds__(64) void k_pack_flat(const uint8_t *__restrict__ sl
     const uint32_t olo = (uint32_t)o, ohi = (uint32_t)(o >> 32);
     const uint64_t cap = (uint64_t)payload_cap;
     const uint8_t *src0 = slots + ((int64_t)eb * 256 + wq * SPW) * p.slot_bytes;
-    for (int i = 0; i < SPW; ++i) {
-        const uint32_t len_i = (uint32_t)__builtin_amdgcn_readlane((int)len, i);
-        const uint64_t o_i = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ohi, i) << 32) |
-                             (uint32_t)__builtin_amdgcn_readlane((int)olo, i);
-        const uint32_t *src = (const uint32_t *)(src0 + (int64_t)i * p.slot_bytes);
-        for (uint32_t j = (uint32_t)lane; 4u * j < len_i; j += 64u) {
-            const uint32_t v = src[j];
+    const int ndw_max = (int)((wave_max_u32(len) + 3u) >> 2);
+    // rounds of 64 dwords: each lane loads dword 64r + lane of all SPW streams first
+    for (int k0 = 0; k0 < ndw_max; k0 += 64) {
+        const uint32_t j = (uint32_t)(k0 + lane);
+        uint32_t v[SPW];
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const uint32_t len_i = (uint32_t)__builtin_amdgcn_readlane((int)len, i);
+            v[i] = 4u * j < len_i ? ((const uint32_t *)(src0 + (int64_t)i * p.slot_bytes))[j] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const uint32_t len_i = (uint32_t)__builtin_amdgcn_readlane((int)len, i);
+            if (4u * j >= len_i) continue;
+            const uint64_t o_i = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ohi, i) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readlane((int)olo, i);
             const uint64_t b = o_i + 4u * j;
             const uint32_t nb = min(len_i - 4u * j, 4u);
             if (nb == 4u && b + 4u <= cap) {
-                __builtin_memcpy(payload + b, &v, 4);
+                __builtin_memcpy(payload + b, &v[i], 4);
             } else {
                 for (uint32_t q = 0; q < nb; ++q)
-                    if (b + q < cap) payload[b + q] = (uint8_t)(v >> (8u * q));
+                    if (b + q < cap) payload[b + q] = (uint8_t)(v[i] >> (8u * q));
             }
         }
     }
@@ -611,9 +604,25 @@ static int enc_streams_per_wave(int64_t n_streams) { return n_streams <= KVC_ENC
 #define KVC_ENC_SPLIT_MAX_STREAMS 16384
 #endif
 
-// Phase-B tile width of k_encode_split: 32 channels, or 16 for 64-entry rows
-// (the four pair tiles of a step fit 512 pairs per tile).
-static int enc_split_tile(int A) { return A <= 32 ? 32 : 16; }
+// k_encode_split's pair chunk (channels) and dynamic LDS for this shape, or
+// 0 when the shape does not take it: C % 64 == 0, A <= 64, a power-of-two
+// chunk of at least 64 channels dividing C with at most 32 KB of pairs, and
+// the 64 streams' symbols plus one chunk within the device's LDS per block.
+static int enc_split_chunk(const KParams &p, size_t *lds)
+{
+    if (p.C % 64 != 0 || p.A > 64) return 0;
+    int ch = 64;
+    while (2 * ch <= p.C / 2 && 2 * ch * p.A * 4 <= 32768 && p.C % (2 * ch) == 0) ch *= 2;
+    if (p.C % ch != 0 || ch * p.A * 4 > 32768) return 0;
+    const size_t bytes = 64 * (size_t)(p.C + 16) + (size_t)ch * p.A * sizeof(uint32_t);
+    int dev = 0, lim = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        bytes > (size_t)lim)
+        return 0;
+    *lds = bytes;
+    return ch;
+}
 
 // Channels per tile (a power of two, 16 to the symbol tile width).  With few
 // streams a tile of 16 channels is coded in less time than its successor's
@@ -651,19 +660,17 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
     const int sw = enc_symbol_tile(p.n_streams);
     const int spw = enc_streams_per_wave(p.n_streams);
     const dim3 grid((unsigned)(regions * (64 / spw)));
-    const int ctb = enc_split_tile(p.A);
-    if (vec16 && p.n_streams <= KVC_ENC_SPLIT_MAX_STREAMS && p.A <= 64 && p.C % (4 * CT) == 0 &&
-        (p.C / 4) % ctb == 0) {
-        const size_t lds_a = lds_pairs + 64 * (size_t)(128 + 16);
-        const size_t lds_b = 4 * (size_t)ctb * p.A * sizeof(uint32_t) + 256 * (size_t)(ctb + 16);
-        const size_t lds = lds_a > lds_b ? lds_a : lds_b;
-        const dim3 sgrid((unsigned)(regions * 4));
-        if (per <= 2)
-            hipLaunchKernelGGL((k_encode_split<2>), sgrid, dim3(256), lds, stream, sym, cdf, slots,
-                               stream_len, p, CT, ctb);
-        else
-            hipLaunchKernelGGL((k_encode_split<8>), sgrid, dim3(256), lds, stream, sym, cdf, slots,
-                               stream_len, p, CT, ctb);
+    size_t lds_split = 0;
+    const int ch = (vec16 && p.n_streams <= KVC_ENC_SPLIT_MAX_STREAMS) ? enc_split_chunk(p, &lds_split) : 0;
+    if (ch > 0) {
+        const void *fn = (const void *)k_encode_split<16>;
+        if (lds_split > 65536) {
+            const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)lds_split);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL((k_encode_split<16>), dim3((unsigned)(regions * 4)), dim3(256), lds_split, stream,
+                           sym, cdf, slots, stream_len, p, ch);
         hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
                            slab_total, p);
         hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, slab_total, slab_off, p.n_slabs,
