@@ -52,7 +52,9 @@ KERNEL_SOURCES = {
     "k_decode": [CSRC + "kvc_decode.hip", CSRC + "lane_coder.h", CSRC + "pair_tile.h"] + COMMON,
     "k_decode_group": [CSRC + "kvc_decode.hip", CSRC + "lane_coder.h", CSRC + "pair_tile.h"] + COMMON,
     "k_encode": [CSRC + "kvc_encode.hip", CSRC + "lane_coder.h", CSRC + "pair_tile.h"] + COMMON,
+    "k_encode_split": [CSRC + "kvc_encode.hip", CSRC + "lane_coder.h", CSRC + "pair_tile.h"] + COMMON,
     "k_pack": [CSRC + "kvc_encode.hip"] + COMMON,
+    "k_pack_flat": [CSRC + "kvc_encode.hip"] + COMMON,
     "k_quant_cdf": [CSRC + "kvc_quantize.hip"] + COMMON,
 }
 COPY_BYTES = 256 << 20
