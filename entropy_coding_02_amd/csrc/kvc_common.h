@@ -125,6 +125,12 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
     return v;
 }
 
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v)
+{
+    for (int off = 32; off > 0; off >>= 1) v += (uint64_t)__shfl_xor((unsigned long long)v, off, 64);
+    return v;
+}
+
 __device__ __forceinline__ void kvc_flag(int32_t *status, int32_t bit)
 {
     if (status) atomicOr(status, bit);

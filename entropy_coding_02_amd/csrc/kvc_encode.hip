@@ -383,6 +383,7 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
     constexpr int SPB = 64;  // streams per block
     constexpr int GB = 4;    // blocks per slot region
     extern __shared__ uint32_t lds[];
+    __shared__ uint32_t s_tot[4];
     const int bps = (p.Tc + 255) / 256;
     const int64_t bl = xcd_block(blockIdx.x, gridDim.x);  // a slab's blocks share an XCD
     const int64_t grp = bl / GB;
@@ -391,7 +392,14 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
     const int tb = (int)(grp - slab * bps);
     const SlabGeom g = slab_geom(p, slab);
     const int r0 = tb * 256 + sub * SPB;  // the block's first token
-    if (r0 >= g.nj) return;               // uniform
+    // the block's payload bytes go to the last 4 bytes of its first stream's
+    // slot, which no stream reaches (at most 2C + 4 of round_up(2C + 16, 16))
+    uint32_t *const btot =
+        (uint32_t *)(slots + ((int64_t)grp * 256 + sub * SPB + 1) * p.slot_bytes - 4);
+    if (r0 >= g.nj) {  // uniform
+        if (threadIdx.x == 0) *btot = 0;
+        return;
+    }
     const int lane = (int)threadIdx.x & 63, wid = (int)threadIdx.x >> 6;
     const int qd = lane & 3;                // this lane's block of channels
     const int jj = wid * 16 + (lane >> 2);  // stream within the block
@@ -499,14 +507,20 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
     const uint32_t lo1 = (uint32_t)__shfl((int)e.lo, qbase + 1, 64);
     const uint32_t lo2 = (uint32_t)__shfl((int)e.lo, qbase + 2, 64);
     __syncthreads();  // every block's bytes are in the slot
+    uint32_t len = 0;
     if (active && qd == 0) {
         split_add(out, S1 / 8u, lo0, 4);
         split_add(out, S2 / 8u, lo1, 4);
         split_add(out, S3 / 8u, lo2, 4);
         const uint32_t nt = SC / 8u + 4u;
         split_add(out, nt - 3u, 0xFFFFFFu, 3);
-        stream_len[g.sid0 + t] = (uint16_t)split_trim(out, nt - 3u);
+        len = split_trim(out, nt - 3u);
+        stream_len[g.sid0 + t] = (uint16_t)len;
     }
+    len = wave_sum_u32(len);
+    if (lane == 0) s_tot[wid] = len;
+    __syncthreads();
+    if (threadIdx.x == 0) *btot = s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
 }
 
 // k_pack for slots holding each stream contiguously (k_encode_split): a wave
@@ -516,11 +530,12 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
 // stream after the other at their byte offsets (unaligned dword stores; the
 // last len % 4 bytes as byte stores).  Nothing is written at or past
 // payload_cap.
+template <bool FUSED>
 __global__ __launch_bounds__(64) void k_pack_flat(const uint8_t *__restrict__ slots,
                                                   const uint16_t *__restrict__ stream_len,
-                                                  const uint64_t *__restrict__ slab_off,
+                                                  uint64_t *__restrict__ slab_off,
                                                   uint8_t *__restrict__ payload, int64_t payload_cap,
-                                                  KParams p)
+                                                  KParams p, int32_t *status)
 {
     constexpr int SPW = 16, WPR = 256 / SPW;
     const int bps = (p.Tc + 255) / 256;
@@ -543,7 +558,31 @@ __global__ __launch_bounds__(64) void k_pack_flat(const uint8_t *__restrict__ sl
         uint32_t v = (uint32_t)__shfl_up((int)incl, off, 64);
         if (lane >= off) incl += v;
     }
-    const uint64_t o = slab_off[slab] + pre + incl - len;
+    uint64_t base;  // the slab's first payload byte
+    if constexpr (FUSED) {
+        // the totals k_encode_split left per encoder block (4 per slot region, in
+        // payload order): those of earlier slabs; the wave of block 0 also writes
+        // the grand total and checks it against the capacity
+        auto btot = [&](int64_t b) {
+            return (uint64_t) * (const uint32_t *)(slots + ((b >> 2) * 256 + (b & 3) * 64 + 1) * p.slot_bytes - 4);
+        };
+        uint64_t acc = 0;
+        for (int64_t b = lane; b < slab * bps * 4; b += 64) acc += btot(b);
+        base = wave_sum_u64(acc);
+        if (tb == 0 && wq == 0 && lane == 0) slab_off[slab] = base;
+        if (blockIdx.x == 0) {
+            uint64_t all = 0;
+            for (int64_t b = lane; b < p.n_slabs * bps * 4; b += 64) all += btot(b);
+            all = wave_sum_u64(all);
+            if (lane == 0) {
+                slab_off[p.n_slabs] = all;
+                if (all > (uint64_t)payload_cap) kvc_flag(status, KVC_DEV_PAYLOAD_OVERFLOW);
+            }
+        }
+    } else {
+        base = slab_off[slab];
+    }
+    const uint64_t o = base + pre + incl - len;
     const uint32_t olo = (uint32_t)o, ohi = (uint32_t)(o >> 32);
     const uint64_t cap = (uint64_t)payload_cap;
     const uint8_t *src0 = slots + ((int64_t)eb * 256 + wq * SPW) * p.slot_bytes;
@@ -602,6 +641,13 @@ static int enc_streams_per_wave(int64_t n_streams) { return n_streams <= KVC_ENC
 // (k_encode_split) where the shape allows it.
 #ifndef KVC_ENC_SPLIT_MAX_STREAMS
 #define KVC_ENC_SPLIT_MAX_STREAMS 16384
+#endif
+
+// Split launches of at most this many encoder blocks take their slab offsets
+// from k_pack_flat (each pack wave sums the block totals before its slab)
+// instead of k_slab_sum and k_scan.
+#ifndef KVC_PACK_FUSED_MAX_BLOCKS
+#define KVC_PACK_FUSED_MAX_BLOCKS 1024
 #endif
 
 // k_encode_split's pair chunk (channels) and dynamic LDS for this shape, or
@@ -671,12 +717,18 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
         }
         hipLaunchKernelGGL((k_encode_split<16>), dim3((unsigned)(regions * 4)), dim3(256), lds_split, stream,
                            sym, cdf, slots, stream_len, p, ch);
-        hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
-                           slab_total, p);
-        hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, slab_total, slab_off, p.n_slabs,
-                           payload_cap, (const uint64_t *)nullptr, status);
-        hipLaunchKernelGGL(k_pack_flat, dim3((unsigned)(regions * 16)), dim3(64), 0, stream, slots,
-                           stream_len, slab_off, payload, payload_cap, p);
+        if (regions * 4 <= KVC_PACK_FUSED_MAX_BLOCKS) {
+            // the slab offsets come out of the pack itself, from the encoder's block totals
+            hipLaunchKernelGGL(k_pack_flat<true>, dim3((unsigned)(regions * 16)), dim3(64), 0, stream, slots,
+                               stream_len, slab_off, payload, payload_cap, p, status);
+        } else {
+            hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
+                               slab_total, p);
+            hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, slab_total, slab_off, p.n_slabs,
+                               payload_cap, (const uint64_t *)nullptr, status);
+            hipLaunchKernelGGL(k_pack_flat<false>, dim3((unsigned)(regions * 16)), dim3(64), 0, stream, slots,
+                               stream_len, slab_off, payload, payload_cap, p, status);
+        }
         return hipGetLastError();
     }
 #define KVC_ENC(V, P, S, W, L)                                                                       \

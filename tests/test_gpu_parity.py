@@ -170,10 +170,12 @@ def test_corrupt_payload_flagged_and_bounded():
     assert np.array_equal(got, want)
 
 
-def test_payload_overflow_flagged_and_cap_respected():
-    say("[gpu] payload capacity")
+@pytest.mark.parametrize("name", ["ragged_L3_C40_T300_Tc128", "split_A24_C512_T200_Tc128"])
+def test_payload_overflow_flagged_and_cap_respected(name):
+    """One-lane and split encoders (the latter takes its slab offsets from the pack)."""
+    say(f"[gpu] payload capacity {name}")
     import torch
-    cfg = SMALL["ragged_L3_C40_T300_Tc128"]
+    cfg = SMALL[name]
     kv, _ = kvgen.generate(cfg)
     d = kvc.Desc(cfg.n_layers, cfg.n_channels, cfg.n_tokens, cfg.bins(), cfg.chunk_tokens)
     buf = kvc.alloc(d)
