@@ -318,40 +318,58 @@ __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
     }
 }
 
-// A chunk of k_encode_split's pair table in registers: chunk m < NA is
-// channels [m CH, m CH + CH); chunk NA + m is channels [b B + m CQ, b B +
-// m CQ + CQ) of the four blocks b (local channel lc is block lc / CQ).
+// floor(x / d) as a multiply-high, with m = 0xFFFFFFFF / d + 1 (d >= 2):
+// m = 2^32 / d + eps with 0 <= eps < 1, so x m / 2^32 exceeds x / d by less
+// than x / 2^32, which is below 1 / d when x d < 2^32 -- too little to
+// carry x / d (whose fraction is at most (d - 1) / d) past an integer.
+__device__ __forceinline__ uint32_t div_by_mulhi(uint32_t x, uint32_t m) { return __umulhi(x, m); }
+
+// A chunk of k_encode_split's pair table in registers.  With A even a CDF
+// row is A / 2 dwords, each one (start, next start) pair, so pair e of a
+// chunk is a dword of the table: chunk m < NA is dwords [m P, m P + P) (P =
+// CH A / 2, channels [m CH, m CH + CH)); chunk NA + m is four runs of Q = P
+// / 4 dwords, run b starting at channel b B + m CQ (local channel lc is block
+// lc / CQ).  A thread's pairs are e = threadIdx.x + 256 i; bit i of last
+// marks a pair that ends its row (its successor start is 65536), the same
+// for every chunk.
 template <int PERC>
 struct ChunkPairs {
-    uint32_t w[PERC], n2[PERC];
+    uint32_t w[PERC], nx[PERC];
 
-    __device__ void load(const uint16_t *rows, int m, int NA, int CH, int CQ, int B, int A)
+    // Every load is issued (pairs past the chunk read its first dword, and
+    // a row's last pair reads its own start again), so none waits on a branch.
+    __device__ void load(const uint32_t *rows, int m, int NA, int P, int B2, uint32_t last)
     {
-        const int half = A >> 1, npairs = CH * half;
+        const int Q = P >> 2;
 #pragma unroll
         for (int i = 0; i < PERC; ++i) {
             const int e = (int)threadIdx.x + 256 * i;
-            w[i] = 0;
-            n2[i] = 65536u;
-            if (e < npairs) {
-                const int cl = e / half, k = (e - cl * half) * 2;
-                const int ch = m < NA ? m * CH + cl : (cl / CQ) * B + (m - NA) * CQ + cl % CQ;
-                const uint16_t *row = rows + (int64_t)ch * A;
-                w[i] = *(const uint32_t *)(row + k);
-                if (k + 2 < A) n2[i] = row[k + 2];
+            int d;
+            if (m < NA) {
+                d = m * P + e;
+            } else {
+                const int b = (e >= Q) + (e >= 2 * Q) + (e >= 3 * Q);
+                d = b * B2 + (m - NA) * Q + (e - b * Q);
             }
+            d = e < P ? d : (m < NA ? m * P : (m - NA) * Q);
+            w[i] = rows[d];
+            nx[i] = ((const uint16_t *)rows)[2 * d + (((last >> i) & 1u) ? 0 : 2)];
         }
     }
-    __device__ void store(lds_u32 *ptab, int CH, int A) const
+    __device__ void store(lds_u32 *ptab, int P, uint32_t last) const
     {
-        const int npairs = CH * (A >> 1);
 #pragma unroll
         for (int i = 0; i < PERC; ++i) {
             const int e = (int)threadIdx.x + 256 * i;
-            if (e < npairs) {
-                const uint32_t st0 = w[i] & 0xFFFFu, st1 = w[i] >> 16;
+            if (e < P) {
+                // the loaded values are used from here only: nothing may be
+                // computed from them (and so wait for them) at the load
+                uint32_t wv = w[i], nv = nx[i];
+                __asm__ volatile("" : "+v"(wv), "+v"(nv));
+                const uint32_t st0 = wv & 0xFFFFu, st1 = wv >> 16;
+                const uint32_t n2 = ((last >> i) & 1u) ? 65536u : nv;
                 ptab[2 * e] = cdf_pair(st0, st1);
-                ptab[2 * e + 1] = cdf_pair(st1, n2[i]);
+                ptab[2 * e + 1] = cdf_pair(st1, n2);
             }
         }
     }
@@ -373,7 +391,7 @@ struct ChunkPairs {
 //  C. After a barrier, lane 0 of the quad adds the blocks' lows and the final
 //     0xFFFFFF and trims: the stream's bytes and length are those of k_encode.
 // Slots: stream j of slot region grp at slots + (grp * 256 + j) * slot_bytes.
-// Needs C % CH == 0, CH % 64 == 0, CH * A / 2 <= 256 * PERC.
+// Needs A even, C % CH == 0, CH % 64 == 0, CH * A / 2 <= 256 * PERC.
 template <int PERC>
 __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict__ sym,
                                                       const uint16_t *__restrict__ cdf,
@@ -405,8 +423,9 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
     const int jj = wid * 16 + (lane >> 2);  // stream within the block
     const int t = r0 + jj;
     const bool active = t < g.nj;
-    const int C = p.C, A = p.A, B = C / 4, CQ = CH / 4;
-    const uint16_t *rows = cdf + slab * C * A;
+    const int C = p.C, A = p.A, B = C / 4, CQ = CH / 4, half = A / 2;
+    const uint32_t *rows = (const uint32_t *)(cdf + slab * C * A);  // A even: rows of A / 2 dwords
+    const int P = CH * half, B2 = B * half;                           // pairs per chunk, per block
     uint8_t *const myslot = slots + ((int64_t)grp * 256 + sub * SPB + jj) * p.slot_bytes;
     const int sst = C + 16;  // symbol row stride (bytes)
     lds_u8 *const stab = (lds_u8 *)lds;                        // [64][C + 16] symbols
@@ -415,70 +434,106 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
     // chunks of CH channels of pairs, each loaded into registers one chunk
     // ahead of its use and stored to the table between two barriers
     const int NA = C / CH, NM = 2 * NA;
+    uint32_t last = 0;  // pair e = threadIdx.x + 256 i ends its row: (e + 1) % half == 0
+    {
+        const int step = 256 % half;
+        int rem = ((int)threadIdx.x + 1) % half;
+#pragma unroll
+        for (int i = 0; i < PERC; ++i) {
+            last |= (rem == 0 ? 1u : 0u) << i;
+            rem += step;
+            rem -= rem >= half ? half : 0;
+        }
+    }
     ChunkPairs<PERC> cp;
     // the symbols of the block's 64 streams, 16-byte pieces, 16 per thread in
     // flight, with the first pair chunk
     {
+        // the block's rows are contiguous in sym: piece k is bytes [16 k, 16 k
+        // + 16) from its first row, row k / per_row of the table
         const int per_row = C / 16, npieces = SPB * per_row;
-        cp.load(rows, 0, NA, CH, CQ, B, A);
+        const int nvalid = (g.nj - r0 < SPB ? g.nj - r0 : SPB) * per_row;
+        const uint32_t mrow = 0xFFFFFFFFu / (uint32_t)per_row + 1u;  // npieces * per_row < 2^32
+        const uint8_t *src = sym + (g.row0 + r0) * C;
+        cp.load(rows, 0, NA, P, B2, last);
         for (int base = 0; base < npieces; base += 256 * 16) {
             u32x4 v[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int ch = base + (int)threadIdx.x + 256 * i;
-                const int r = ch / per_row, part = ch - r * per_row;
-                v[i] = (ch < npieces && r0 + r < g.nj)
-                           ? *(const u32x4 *)(sym + (g.row0 + r0 + r) * C + part * 16)
-                           : u32x4{0, 0, 0, 0};
+                const int k = base + (int)threadIdx.x + 256 * i;
+                v[i] = k < nvalid ? *(const u32x4 *)(src + (int64_t)k * 16) : u32x4{0, 0, 0, 0};
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int ch = base + (int)threadIdx.x + 256 * i;
-                const int r = ch / per_row, part = ch - r * per_row;
-                if (ch < npieces) *(lds_u32x4 *)(stab + r * sst + part * 16) = v[i];
+                const int k = base + (int)threadIdx.x + 256 * i;
+                const int r = (int)div_by_mulhi((uint32_t)k, mrow);
+                if (k < npieces) *(lds_u32x4 *)(stab + k * 16 + r * 16) = v[i];
             }
         }
     }
-    // 16 symbols of this lane's stream from channel c (c % 16 == 0) and their pairs from
-    // table row lc0, in batches of 8
+    // This lane's symbols [c, c + n) (c, n multiples of 16) and their pairs
+    // from table rows t0 .., 8 at a time: the next 8 lookups (and the
+    // symbols two groups of 16 ahead) are in flight while `use` runs on the
+    // current 8, so the coder waits on LDS only at a run's start.  grp(g) runs before the
+    // symbols [c + g, c + g + 16) are used.
     const lds_u8 *my = stab + jj * sst;
-    auto pairs16 = [&](int c, int lc0, auto &&use) {
-        const u32x4 v = *(const lds_u32x4 *)(my + c);
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-        const lds_u32 *trow = ptab + lc0 * A;
+    const uint32_t amax = (uint32_t)A - 1u;
+    auto look8 = [&](uint32_t lo, uint32_t hi, const lds_u32 *t, uint32_t(&pv)[8]) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint32_t pv[8];
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t sy = min(((i < 4 ? lo : hi) >> (8 * (i & 3))) & 0xFFu, amax);
+            pv[i] = t[i * A + sy];
+        }
+    };
+    auto run_pairs = [&](int c, int n, int t0, auto &&grp, auto &&use) {
+        const lds_u32 *trow = ptab + t0 * A;
+        u32x4 s0 = *(const lds_u32x4 *)(my + c);
+        u32x4 s1 = *(const lds_u32x4 *)(my + c + (16 < n ? 16 : 0));
+        uint32_t pa[8], pb[8];
+        look8(s0.x, s0.y, trow, pa);
+        for (int g = 0; g < n; g += 16) {
+            // groups past the run read its last group again
+            const int gn = g + 16 < n ? g + 16 : g, gnn = g + 32 < n ? g + 32 : n - 16;
+            const u32x4 s2 = *(const lds_u32x4 *)(my + c + gnn);
+            look8(s0.z, s0.w, trow + (g + 8) * A, pb);
+            // the lookups above are issued before any use of pa[] below
+            __asm__ volatile("" : "+v"(pa[0])::"memory");
+            grp(g);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int k = h * 8 + i;
-                uint32_t sy = (wv[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                sy = min(sy, (uint32_t)A - 1u);
-                pv[i] = trow[k * A + sy];
-            }
+            for (int i = 0; i < 8; ++i) use(pa[i]);
+            look8(s1.x, s1.y, trow + gn * A, pa);
+            __asm__ volatile("" : "+v"(pb[0])::"memory");
 #pragma unroll
-            for (int i = 0; i < 8; ++i) use(pv[i]);
+            for (int i = 0; i < 8; ++i) use(pb[i]);
+            s0 = s1;
+            s1 = s2;
         }
     };
 
-    // ---- A: the range chain
-    uint32_t range = 0xFFFFFFFFu, S = 0, rq = 0, S1 = 0, S2 = 0, S3 = 0;
-    for (int c0 = 0; c0 < C; c0 += CH) {
-        const int m = c0 / CH;
+    // ---- A: the range chain up to the last block's start (the last block's
+    // own chain runs inside its coder in B)
+    const int CA = 3 * B, NAA = (CA + CH - 1) / CH;  // channels, chunks
+    uint32_t range = 0xFFFFFFFFu, S = 0, rq = 0, S1 = 0, S2 = 0;
+    for (int m = 0; m < NAA; ++m) {
+        const int c0 = m * CH;
         __syncthreads();  // every wave is done with the previous chunk
-        cp.store(ptab, CH, A);
+        cp.store(ptab, P, last);
         __syncthreads();
-        if (m + 1 < NM) cp.load(rows, m + 1, NA, CH, CQ, B, A);
-        for (int cg = c0; cg < c0 + CH; cg += 16) {
-            // block boundaries fall on multiples of 16 channels
-            if (cg == B) S1 = S;
-            if (cg == 2 * B) S2 = S;
-            if (cg == 3 * B) S3 = S;
-            rq = cg == qd * B ? range : rq;
-            if (active) pairs16(cg, cg - c0, [&](uint32_t pr) { S += enc_range_step(range, pr >> 16); });
-        }
+        cp.load(rows, m + 1 < NAA ? m + 1 : NA, NA, P, B2, last);
+        if (active)
+            run_pairs(
+                c0, CA - c0 < CH ? CA - c0 : CH, 0,
+                [&](int g) {
+                    // block boundaries fall on multiples of 16 channels
+                    const int cg = c0 + g;
+                    if (cg == B) S1 = S;
+                    if (cg == 2 * B) S2 = S;
+                    rq = cg == qd * B ? range : rq;
+                },
+                [&](uint32_t pr) { S += enc_range_step(range, pr >> 16); });
     }
-    const uint32_t SC = S;
+    const uint32_t S3 = S;
+    rq = qd == 3 ? range : rq;
 
     // ---- B: each lane codes its block
     EncState e;
@@ -486,16 +541,19 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
     e.range = rq;
     const uint32_t Sg = qd == 0 ? 0u : qd == 1 ? S1 : qd == 2 ? S2 : S3;
     const SplitOut out{myslot, Sg / 8u};
-    for (int j0 = 0; j0 < B; j0 += CQ) {
-        const int m = NA + j0 / CQ;
+    for (int m = NA; m < NM; ++m) {
+        const int j0 = (m - NA) * CQ;
         __syncthreads();
-        cp.store(ptab, CH, A);
+        cp.store(ptab, P, last);
         __syncthreads();
-        if (m + 1 < NM) cp.load(rows, m + 1, NA, CH, CQ, B, A);
-        if (!active) continue;
-        for (int cg = 0; cg < CQ; cg += 16)
-            pairs16(qd * B + j0 + cg, qd * CQ + cg, [&](uint32_t pr) { enc_pair(e, pr, out); });
+        if (m + 1 < NM) cp.load(rows, m + 1, NA, P, B2, last);
+        if (active)
+            run_pairs(qd * B + j0, CQ, qd * CQ, [](int) {}, [&](uint32_t pr) { enc_pair(e, pr, out); });
     }
+    // the bits shifted out of the whole stream: those before the last block
+    // and those the last block's coder shifted (its written dwords and
+    // pending bits)
+    const uint32_t SC = (uint32_t)__shfl((int)(Sg + 32u * e.w + e.kb), (lane & ~3) + 3, 64);
     if (active) {
         enc_block_end(e, out);
         if (qd == 3)
@@ -656,7 +714,7 @@ static int enc_streams_per_wave(int64_t n_streams) { return n_streams <= KVC_ENC
 // the 64 streams' symbols plus one chunk within the device's LDS per block.
 static int enc_split_chunk(const KParams &p, size_t *lds)
 {
-    if (p.C % 64 != 0 || p.A > 64) return 0;
+    if (p.C % 64 != 0 || p.A > 64 || p.A % 2 != 0) return 0;
     int ch = 64;
     while (2 * ch <= p.C / 2 && 2 * ch * p.A * 4 <= 32768 && p.C % (2 * ch) == 0) ch *= 2;
     if (p.C % ch != 0 || ch * p.A * 4 > 32768) return 0;
