@@ -318,11 +318,35 @@ __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
     }
 }
 
+// SplitOut for a lane of k_encode_split's phase B: the per-symbol dword
+// store is a raw buffer store over the block's 64 slots, and a store that must
+// not happen gets an offset past the buffer's range, which the hardware
+// drops (no write, no fault), so no lane mask has to be set up for it.
+struct SplitOutBuf : SplitOut {
+    __amdgpu_buffer_rsrc_t rsrc;  // the block's slots, uniform
+    uint32_t lbase;               // this lane's slot within them (bytes)
+    __device__ void store_if(bool p, uint32_t i, uint32_t v) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(v, rsrc, p ? lbase + off + 4u * i : 0x80000000u, 0, 0);
+    }
+    __device__ bool any(bool p) const { return __ballot(p) != 0; }
+    // out of line, so the common path is one uniform branch over the call
+    __device__ __noinline__ void carry(bool p, uint32_t w) const
+    {
+        if (p) enc_carry_into_written(*this, w);
+    }
+};
+
 // floor(x / d) as a multiply-high, with m = 0xFFFFFFFF / d + 1 (d >= 2):
 // m = 2^32 / d + eps with 0 <= eps < 1, so x m / 2^32 exceeds x / d by less
 // than x / 2^32, which is below 1 / d when x d < 2^32 -- too little to
 // carry x / d (whose fraction is at most (d - 1) / d) past an integer.
 __device__ __forceinline__ uint32_t div_by_mulhi(uint32_t x, uint32_t m) { return __umulhi(x, m); }
+
+// In B the four lanes of a quad read rows of four blocks a multiple of 32
+// dwords apart, which would put equal symbols in one LDS bank: the table's
+// four runs are set this many dwords apart.
+#define KVC_SPLIT_SKEW 8
 
 // A chunk of k_encode_split's pair table in registers.  With A even a CDF
 // row is A / 2 dwords, each one (start, next start) pair, so pair e of a
@@ -356,20 +380,23 @@ struct ChunkPairs {
             nx[i] = ((const uint16_t *)rows)[2 * d + (((last >> i) & 1u) ? 0 : 2)];
         }
     }
-    __device__ void store(lds_u32 *ptab, int P, uint32_t last) const
+    // run b of the chunk goes b * skew dwords further on
+    __device__ void store(lds_u32 *ptab, int P, uint32_t last, int skew) const
     {
+        const int Q = P >> 2;
 #pragma unroll
         for (int i = 0; i < PERC; ++i) {
             const int e = (int)threadIdx.x + 256 * i;
             if (e < P) {
+                lds_u32 *const dst = ptab + ((e >= Q) + (e >= 2 * Q) + (e >= 3 * Q)) * skew;
                 // the loaded values are used from here only: nothing may be
                 // computed from them (and so wait for them) at the load
                 uint32_t wv = w[i], nv = nx[i];
                 __asm__ volatile("" : "+v"(wv), "+v"(nv));
                 const uint32_t st0 = wv & 0xFFFFu, st1 = wv >> 16;
                 const uint32_t n2 = ((last >> i) & 1u) ? 65536u : nv;
-                ptab[2 * e] = cdf_pair(st0, st1);
-                ptab[2 * e + 1] = cdf_pair(st1, n2);
+                dst[2 * e] = cdf_pair(st0, st1);
+                dst[2 * e + 1] = cdf_pair(st1, n2);
             }
         }
     }
@@ -472,7 +499,7 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
         }
     }
     // This lane's symbols [c, c + n) (c, n multiples of 16) and their pairs
-    // from table rows t0 .., 8 at a time: the next 8 lookups (and the
+    // from the table rows at trow, 8 at a time: the next 8 lookups (and the
     // symbols two groups of 16 ahead) are in flight while `use` runs on the
     // current 8, so the coder waits on LDS only at a run's start.  grp(g) runs before the
     // symbols [c + g, c + g + 16) are used.
@@ -485,8 +512,7 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
             pv[i] = t[i * A + sy];
         }
     };
-    auto run_pairs = [&](int c, int n, int t0, auto &&grp, auto &&use) {
-        const lds_u32 *trow = ptab + t0 * A;
+    auto run_pairs = [&](int c, int n, const lds_u32 *trow, auto &&grp, auto &&use) {
         u32x4 s0 = *(const lds_u32x4 *)(my + c);
         u32x4 s1 = *(const lds_u32x4 *)(my + c + (16 < n ? 16 : 0));
         uint32_t pa[8], pb[8];
@@ -517,12 +543,12 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
     for (int m = 0; m < NAA; ++m) {
         const int c0 = m * CH;
         __syncthreads();  // every wave is done with the previous chunk
-        cp.store(ptab, P, last);
+        cp.store(ptab, P, last, 0);
         __syncthreads();
         cp.load(rows, m + 1 < NAA ? m + 1 : NA, NA, P, B2, last);
         if (active)
             run_pairs(
-                c0, CA - c0 < CH ? CA - c0 : CH, 0,
+                c0, CA - c0 < CH ? CA - c0 : CH, ptab,
                 [&](int g) {
                     // block boundaries fall on multiples of 16 channels
                     const int cg = c0 + g;
@@ -540,15 +566,19 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
     enc_init(e);
     e.range = rq;
     const uint32_t Sg = qd == 0 ? 0u : qd == 1 ? S1 : qd == 2 ? S2 : S3;
-    const SplitOut out{myslot, Sg / 8u};
+    uint8_t *const bslots = slots + ((int64_t)grp * 256 + sub * SPB) * p.slot_bytes;
+    const SplitOutBuf out{{myslot, Sg / 8u},
+                          __builtin_amdgcn_make_buffer_rsrc(bslots, (short)0, (int)(SPB * p.slot_bytes), 0x00020000),
+                          (uint32_t)(jj * p.slot_bytes)};
     for (int m = NA; m < NM; ++m) {
         const int j0 = (m - NA) * CQ;
         __syncthreads();
-        cp.store(ptab, P, last);
+        cp.store(ptab, P, last, KVC_SPLIT_SKEW);
         __syncthreads();
         if (m + 1 < NM) cp.load(rows, m + 1, NA, P, B2, last);
         if (active)
-            run_pairs(qd * B + j0, CQ, qd * CQ, [](int) {}, [&](uint32_t pr) { enc_pair(e, pr, out); });
+            run_pairs(qd * B + j0, CQ, ptab + qd * (CQ * A + KVC_SPLIT_SKEW), [](int) {},
+                      [&](uint32_t pr) { enc_pair_nb(e, pr, out); });
     }
     // the bits shifted out of the whole stream: those before the last block
     // and those the last block's coder shifted (its written dwords and
@@ -718,7 +748,7 @@ static int enc_split_chunk(const KParams &p, size_t *lds)
     int ch = 64;
     while (2 * ch <= p.C / 2 && 2 * ch * p.A * 4 <= 32768 && p.C % (2 * ch) == 0) ch *= 2;
     if (p.C % ch != 0 || ch * p.A * 4 > 32768) return 0;
-    const size_t bytes = 64 * (size_t)(p.C + 16) + (size_t)ch * p.A * sizeof(uint32_t);
+    const size_t bytes = 64 * (size_t)(p.C + 16) + ((size_t)ch * p.A + 3 * KVC_SPLIT_SKEW) * sizeof(uint32_t);
     int dev = 0, lim = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||

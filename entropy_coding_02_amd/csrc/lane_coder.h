@@ -196,6 +196,15 @@ struct SplitOut {
         return v;
     }
     KVC_HD void store(uint32_t i, uint32_t v) const { __builtin_memcpy(base + off + 4u * i, &v, 4); }
+    KVC_HD void store_if(bool p, uint32_t i, uint32_t v) const
+    {
+        if (p) store(i, v);
+    }
+    KVC_HD bool any(bool p) const { return p; }
+    KVC_HD void carry(bool p, uint32_t w) const
+    {
+        if (p) enc_carry_into_written(*this, w);
+    }
 };
 
 // End of a block: resolve a carry past the pending bytes, then write them
@@ -448,6 +457,43 @@ template <class Out>
 KVC_HD void enc_pair(EncState &e, uint32_t p, const Out &out)
 {
     enc_put(e, p & 0xFFFFu, p >> 16, out);
+}
+
+// enc_put with no branch that depends on the lane: the flush is computed on
+// every symbol and selected, the dword goes out through out.store_if(flush,
+// ...), and only a carry past the pending bytes (when out.any() sees one in
+// any lane) takes a branch, to out.carry().  Same state, same bytes as enc_put.  Where lanes
+// run in lockstep this trades a few selects for the two masked blocks
+// enc_put's flush needs on nearly every symbol.
+template <class Out>
+KVC_HD void enc_put_nb(EncState &e, uint32_t st, uint32_t fr, const Out &out)
+{
+    const uint32_t r = e.range >> 16;
+    const uint32_t add = r * st;
+    const uint32_t lo2 = e.lo + add;
+    uint64_t pb = e.pb + ((lo2 < add) ? 1u : 0u);
+    e.range = r * fr;
+    const uint32_t n = kvc_renorm_bits(e.range);
+    e.range <<= n;
+    const uint64_t wide = (uint64_t)lo2 << n;
+    pb = (pb << n) | (wide >> 32);
+    e.lo = (uint32_t)wide;
+    const uint32_t kb = e.kb + n;
+    // k = 6 or 7 pending bytes: bytes k-1 .. k-4 go out (see enc_put)
+    const bool fl = kb >= 48u;
+    const uint32_t sh = (kb - 32u) & 31u;  // 16 or 24 when fl
+    const bool ci = fl && (((uint32_t)(pb >> 32) >> sh) != 0);
+    if (__builtin_expect(out.any(ci), 0)) out.carry(ci, e.w);
+    out.store_if(fl, e.w, kvc_bswap32((uint32_t)(pb >> sh)));
+    e.w += fl ? 1u : 0u;
+    e.pb = fl ? (uint64_t)((uint32_t)pb & ((1u << sh) - 1u)) : pb;
+    e.kb = fl ? kb - 32u : kb;
+}
+
+template <class Out>
+KVC_HD void enc_pair_nb(EncState &e, uint32_t p, const Out &out)
+{
+    enc_put_nb(e, p & 0xFFFFu, p >> 16, out);
 }
 
 // Largest k in [0, A) with r * row[k] <= code, where `row` holds the A

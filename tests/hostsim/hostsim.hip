@@ -65,7 +65,7 @@ int64_t hostsim_encode_stream_split(const uint8_t *q, int32_t C, int32_t A, cons
         enc_init(e);
         e.range = r0[g];
         const SplitOut out{slot, s0[g] / 8u};
-        for (int32_t c = g * B; c < C && c < (g + 1) * B; ++c) enc_pair(e, pair_of(c), out);
+        for (int32_t c = g * B; c < C && c < (g + 1) * B; ++c) enc_pair_nb(e, pair_of(c), out);
         enc_block_end(e, out);
         lo[g] = e.lo;
     }
