@@ -9,7 +9,9 @@ What fixes these functions here, apart from the oracle itself:
   * exact rational rounding away from ties (brute force with Fractions);
   * the reconstruction error bound max|x|/(2*MAX), exhaustively over fp16,
     plus the fp32 rounding slack derived in the test below;
-  * fp16 output equal to numpy's RNE conversion of the fp32 output.
+  * fp16 output equal to numpy's RNE conversion of the fp32 output;
+  * the page's own quantize and dequantize expressions, evaluated by torch on
+    CPU float32 tensors, agree bit for bit (operation order pins).
 """
 from fractions import Fraction
 
@@ -187,17 +189,91 @@ def test_nonfinite_and_bad_bins_rejected():
             quant_rows(row, nb)
 
 
-def test_fp32_torch_expression_agrees():
-    """Supplementary consistency check (not a pin): the same closed form in
-    torch fp32 CPU ops, one rounding per op, gives identical symbols."""
+def _edge_maxes():
+    """fp16 row maxima: subnormals (smallest, largest), the smallest normal,
+    1.0, values with long mantissas, 65504, and a spread of random finite ones."""
+    fixed = [0x0001, 0x0003, 0x02AB, 0x03FF, 0x0400, 0x0401, 0x1E66, 0x3BFF, 0x3C00, 0x3C01,
+             0x4247, 0x4E00, 0x57FF, 0x6AAA, 0x7800, 0x7BFE, 0x7BFF]
+    rng = np.random.default_rng(1234)
+    rand = rng.integers(1, 0x7C00, 200)
+    return np.array(fixed + list(rand), dtype=np.uint16)
+
+
+DEQ_BINS = [4, 6, 16, 32, 64, 256]
+
+
+@pytest.mark.parametrize("nbins", DEQ_BINS)
+def test_dequantize_page_code_pin(nbins):
+    """Pin of the dequantizer's operation order: the write-up's decoder
+    ("2.4 Decoder pipeline", step 2) undoes the offset (integer subtraction of
+    C = bins//2 - 1), converts to float and divides by C, then multiplies by
+    the stored maxima.  That expression, evaluated by torch on CPU float32
+    tensors (each operation rounded on its own), must equal the oracle bit for
+    bit for every symbol q in [0, 2*MAX] and every row maximum in the sweep,
+    in fp32 and after RNE to fp16.  The sweep is chosen so that the two
+    plausible reorderings, (q-MAX)*m/MAX and (q-MAX)*(m/MAX), disagree with
+    the page's order somewhere (asserted, so the pin is known to catch them)."""
+    torch = pytest.importorskip("torch")
+    MAX = nbins // 2 - 1
+    maxes = _edge_maxes()
+    R, Q = maxes.size, 2 * MAX + 1
+    q = np.ascontiguousarray(np.broadcast_to(np.arange(Q, dtype=np.uint8)[None, :], (R, Q)))
+    sym = np.ascontiguousarray(np.broadcast_to(q[None, None], (1, 2, R, Q)))
+    mx = np.ascontiguousarray(np.broadcast_to(maxes[None, None], (1, 2, R)))
+    bins = np.array([[nbins, nbins]], dtype=np.int32)
+    want32 = oracle.dequantize(sym, mx, bins, fp32=True)[0, 0]
+    want16 = oracle.dequantize(sym, mx, bins, fp32=False)[0, 0]
+
+    # the page's expression, groups along the first axis as its [:, None, None] broadcast
+    t = torch.from_numpy(q.astype(np.int64))[None]                      # [1, R, Q] integer indices
+    maxt = torch.from_numpy(maxes.view(np.float16).astype(np.float32))[None, :, None]  # [1, R, 1]
+    Ct = (torch.tensor([nbins], dtype=torch.int64) // 2 - 1)[:, None, None]
+    y = t - Ct
+    y = y.float() / Ct
+    y = y * maxt
+    got32 = y[0].numpy()
+    assert got32.dtype == np.float32
+    assert np.array_equal(got32.view(np.uint32), want32.view(np.uint32))
+    got16 = y[0].half().numpy().view(np.uint16)
+    assert np.array_equal(got16, want16)
+
+    # the sweep tells the page's order from the two reorderings
+    d = (t - Ct).float()
+    Mf = Ct.float()
+    alt1 = (d * maxt / Mf)[0].numpy()
+    alt2 = (d * (maxt / Mf))[0].numpy()
+    if MAX & (MAX - 1):  # dividing by a power of two is exact: then every order agrees
+        assert not np.array_equal(alt1.view(np.uint32), want32.view(np.uint32))
+        assert not np.array_equal(alt2.view(np.uint32), want32.view(np.uint32))
+
+
+def test_quantize_page_code_pin():
+    """Pin of the quantizer's operation order: the write-up's encoder
+    ("2.3 Encoder pipeline", step 1) computes MAX = bins//2 - 1 per group, the
+    group's max |x|, factor = MAX / max1, then round(x * factor + MAX).  That
+    expression, evaluated by torch on CPU float32 tensors (each operation
+    rounded on its own; torch.round is half-to-even), must give the oracle's
+    symbols bit for bit.  Rows span 2^-24 .. 65504 in scale, include
+    subnormal-only rows and rows whose max is 65504.  A reordered factor,
+    round((x * MAX) / max1 + MAX), is asserted to differ on this data."""
     torch = pytest.importorskip("torch")
     rng = np.random.default_rng(11)
     x = (rng.standard_normal((2, 2, 50, 128)) * np.exp2(rng.uniform(-10, 8, (2, 2, 50, 1)))).astype(np.float32)
+    x[0, 0, 0] = rng.standard_normal(128) * 2.0**-20          # subnormal fp16 values only
+    x[0, 1, 1, :3] = [65504, -65504, 1.0]                     # the largest finite max
+    x[1, 0, 2] = np.clip(rng.standard_normal(128) * 30000, -65504, 65504)
     bits = f16(x)
     bins = np.array([[32, 16], [64, 4]], dtype=np.int32)
     sym, _ = oracle.quantize(bits, bins)
-    xt = torch.from_numpy(as_f32(bits))
-    M = torch.from_numpy((bins // 2 - 1).astype(np.float32))[:, :, None, None]
-    m = xt.abs().amax(dim=-1, keepdim=True)
-    q = torch.round(xt * (M / m) + M).to(torch.uint8).numpy()
-    assert np.array_equal(q, sym)
+    L = bins.shape[0]
+    groups = torch.from_numpy(as_f32(bits)).reshape(L * 2, 50, 128)   # one group per (layer, K|V)
+    bt = torch.from_numpy(bins.reshape(-1).astype(np.int64))
+    MAXt = (bt // 2 - 1)[:, None, None]
+    max1 = torch.amax(torch.abs(groups), dim=-1, keepdim=True)
+    factor = MAXt / max1
+    xq = torch.round(groups * factor + MAXt)
+    assert xq.dtype == torch.float32
+    got = xq.to(torch.uint8).numpy().reshape(sym.shape)
+    assert np.array_equal(got, sym)
+    alt = torch.round((groups * MAXt) / max1 + MAXt).to(torch.uint8).numpy().reshape(sym.shape)
+    assert not np.array_equal(alt, sym)
