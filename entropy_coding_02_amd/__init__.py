@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libkvc.so")
 
 KVC_OK, KVC_ERR_ARG, KVC_ERR_CAPACITY, KVC_ERR_HIP = 0, -1, -2, -3
 KVC_DEV_NONFINITE, KVC_DEV_CORRUPT, KVC_DEV_PAYLOAD_OVERFLOW = 1, 2, 4
-KVC_DEV_BAD_CDF, KVC_DEV_BAD_CONTAINER = 8, 16
+KVC_DEV_BAD_CDF, KVC_DEV_BAD_CONTAINER, KVC_DEV_BAD_SYMBOL = 8, 16, 32
 KVC_F16, KVC_F32 = 0, 1
 
 EXPORTED = (
@@ -81,7 +81,7 @@ def _load():
         lib.kvc_quantize.restype = ctypes.c_int
         lib.kvc_quantize.argtypes = [D, P, P, P, P, P, P]
         lib.kvc_cdf.restype = ctypes.c_int
-        lib.kvc_cdf.argtypes = [D, P, P, P]
+        lib.kvc_cdf.argtypes = [D, P, P, P, P]
         lib.kvc_encode.restype = ctypes.c_int
         lib.kvc_encode.argtypes = [D, P, P, P, I64, P, P, P, I64, P, P]
         lib.kvc_decode.restype = ctypes.c_int
@@ -206,8 +206,8 @@ def kvc_quantize_levels(descs, kv, syms, max1, cdfs, dev_status=None, stream=Non
                                                               _ptr(dev_status), _stream(stream)))
 
 
-def kvc_cdf(desc: Desc, sym, cdf, stream=None):
-    _check("kvc_cdf", _load().kvc_cdf(desc.ref, _ptr(sym), _ptr(cdf), _stream(stream)))
+def kvc_cdf(desc: Desc, sym, cdf, dev_status=None, stream=None):
+    _check("kvc_cdf", _load().kvc_cdf(desc.ref, _ptr(sym), _ptr(cdf), _ptr(dev_status), _stream(stream)))
 
 
 def kvc_encode(desc: Desc, sym, cdf, scratch, stream_len, slab_off, payload, dev_status=None,
@@ -326,7 +326,7 @@ def encode(buf: Buffers, kv, fused_cdf: bool = True, stream=None):
     d = buf.desc
     kvc_quantize(d, kv, buf.sym, buf.max1, buf.cdf if fused_cdf else None, buf.dev_status, stream)
     if not fused_cdf:
-        kvc_cdf(d, buf.sym, buf.cdf, stream)
+        kvc_cdf(d, buf.sym, buf.cdf, buf.dev_status, stream)
     kvc_encode(d, buf.sym, buf.cdf, buf.scratch, buf.stream_len, buf.slab_off, buf.payload,
                buf.dev_status, stream)
 

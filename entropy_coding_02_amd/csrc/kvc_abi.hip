@@ -150,7 +150,7 @@ int kvc_quantize(const kvc_desc *desc, const uint16_t *kv, uint8_t *sym, uint16_
     if (cdf && vec8 && aligned(cdf, 16) && g.p.n_slabs >= 256 && quant_cdf_fused_ok(g.p))
         return launch_status(launch_quant_cdf(kv, sym, max1, cdf, g.p, dev_status, s));
     hipError_t e = launch_quantize_rows(kv, sym, max1, g.p, dev_status, vec8, s);
-    if (e == hipSuccess && cdf) e = launch_cdf(sym, cdf, g.p, s);
+    if (e == hipSuccess && cdf) e = launch_cdf(sym, cdf, g.p, dev_status, s);
     return launch_status(e);
 }
 
@@ -193,14 +193,16 @@ int kvc_quantize_levels(const kvc_desc *levels, int32_t n_levels, const uint16_t
     return KVC_OK;
 }
 
-int kvc_cdf(const kvc_desc *desc, const uint8_t *sym, uint16_t *cdf, void *stream)
+int kvc_cdf(const kvc_desc *desc, const uint8_t *sym, uint16_t *cdf, int32_t *dev_status,
+            void *stream)
 {
     Geometry g;
     int rc = make_geometry(desc, g);
     if (rc != KVC_OK) return rc;
     if (g.p.n_rows == 0) return KVC_OK;
-    if (!sym || !cdf || !aligned(sym, 4) || !aligned(cdf, 4)) return KVC_ERR_ARG;
-    return launch_status(launch_cdf(sym, cdf, g.p, (hipStream_t)stream));
+    if (!sym || !cdf || !aligned(sym, 4) || !aligned(cdf, 4) || (dev_status && !aligned(dev_status, 4)))
+        return KVC_ERR_ARG;
+    return launch_status(launch_cdf(sym, cdf, g.p, dev_status, (hipStream_t)stream));
 }
 
 int kvc_encode(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf, void *scratch,

@@ -14,7 +14,8 @@
 namespace {
 
 __global__ __launch_bounds__(256) void k_cdf(const uint8_t *__restrict__ sym,
-                                             uint16_t *__restrict__ cdf, KParams p, int CT)
+                                             uint16_t *__restrict__ cdf, KParams p, int CT,
+                                             int32_t *status)
 {
     extern __shared__ uint32_t hist[];
     const int A = p.A, stride = A + 1, C = p.C;
@@ -27,15 +28,18 @@ __global__ __launch_bounds__(256) void k_cdf(const uint8_t *__restrict__ sym,
 
     for (int i = threadIdx.x; i < CT * stride; i += blockDim.x) hist[i] = 0;
     __syncthreads();
+    uint32_t bad = 0;
     if (c < C) {
         const uint8_t *col = sym + g.row0 * C + c;
         uint32_t *h = hist + cl * stride;
         for (int t = tg; t < g.nj; t += tstep) {
             uint32_t v = col[(int64_t)t * C];
+            bad |= v >= (uint32_t)A ? 1u : 0u;
             v = v < (uint32_t)A ? v : (uint32_t)(A - 1);
             atomicAdd(&h[v], 1u);
         }
     }
+    if (bad) kvc_flag(status, KVC_DEV_BAD_SYMBOL);
     __syncthreads();
     if (tg == 0 && c < C) {
         uint32_t *h = hist + cl * stride;
@@ -67,7 +71,8 @@ __global__ __launch_bounds__(256) void k_cdf(const uint8_t *__restrict__ sym,
 // thread then turns one channel's counts into its CDF row.
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void k_cdf_wide(const uint8_t *__restrict__ sym,
-                                                      uint16_t *__restrict__ cdf, KParams p)
+                                                      uint16_t *__restrict__ cdf, KParams p,
+                                                      int32_t *status)
 {
     extern __shared__ uint32_t hist[];
     const int A = p.A, W = A / 2 + 1, C = p.C;
@@ -80,6 +85,7 @@ __global__ __launch_bounds__(64 * NW) void k_cdf_wide(const uint8_t *__restrict_
     for (int i = threadIdx.x; i < nwords; i += 64 * NW) hist[i] = 0;
     __syncthreads();
     const int cq = c0 + 4 * lane;  // this lane's first channel
+    uint32_t bad = 0;
     if (cq < C) {
         const uint8_t *col = sym + g.row0 * C + cq;
         const int cl = 4 * lane;
@@ -91,6 +97,8 @@ __global__ __launch_bounds__(64 * NW) void k_cdf_wide(const uint8_t *__restrict_
                 const int t = t0 + NW * u;
                 v[u] = t < g.nj ? *(const uint32_t *)(col + (int64_t)t * C) : 0u;
             }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) bad |= kvc_bytes_ge(v[u], (uint32_t)A);  // missing tokens read 0
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (t0 + NW * u >= g.nj) break;
@@ -104,6 +112,7 @@ __global__ __launch_bounds__(64 * NW) void k_cdf_wide(const uint8_t *__restrict_
             }
         }
     }
+    if (bad) kvc_flag(status, KVC_DEV_BAD_SYMBOL);
     __syncthreads();
     const int c = c0 + (int)threadIdx.x;
     if (threadIdx.x < 256 && c < C) {
@@ -126,25 +135,24 @@ __global__ __launch_bounds__(64 * NW) void k_cdf_wide(const uint8_t *__restrict_
 }  // namespace
 
 // Launches of at most this many 256-channel tiles take 16 waves per block.
-#ifndef KVC_CDF_WIDE_TALL_MAX_BLOCKS
-#define KVC_CDF_WIDE_TALL_MAX_BLOCKS 1024
-#endif
+constexpr int64_t KVC_CDF_WIDE_TALL_MAX_BLOCKS = 1024;
 
-hipError_t launch_cdf(const uint8_t *sym, uint16_t *cdf, const KParams &p, hipStream_t stream)
+hipError_t launch_cdf(const uint8_t *sym, uint16_t *cdf, const KParams &p, int32_t *status,
+                      hipStream_t stream)
 {
     if (p.n_slabs == 0) return hipSuccess;
     if (p.C % 4 == 0 && p.A <= 64 && ((uintptr_t)sym & 3) == 0 && ((uintptr_t)cdf & 3) == 0) {
         const size_t lds = sizeof(uint32_t) * (256 * (size_t)(p.A / 2 + 1) + 64);
         dim3 grid((unsigned)(((p.C + 255) / 256) * p.n_slabs));
         if (grid.x <= KVC_CDF_WIDE_TALL_MAX_BLOCKS)
-            hipLaunchKernelGGL(k_cdf_wide<16>, grid, dim3(1024), lds, stream, sym, cdf, p);
+            hipLaunchKernelGGL(k_cdf_wide<16>, grid, dim3(1024), lds, stream, sym, cdf, p, status);
         else
-            hipLaunchKernelGGL(k_cdf_wide<4>, grid, dim3(256), lds, stream, sym, cdf, p);
+            hipLaunchKernelGGL(k_cdf_wide<4>, grid, dim3(256), lds, stream, sym, cdf, p, status);
         return hipGetLastError();
     }
     const int CT = p.A <= 128 ? 64 : 32;
     const size_t lds = (size_t)CT * (p.A + 1) * sizeof(uint32_t);
     dim3 grid((unsigned)(((p.C + CT - 1) / CT) * p.n_slabs));
-    hipLaunchKernelGGL(k_cdf, grid, dim3(256), lds, stream, sym, cdf, p, CT);
+    hipLaunchKernelGGL(k_cdf, grid, dim3(256), lds, stream, sym, cdf, p, CT, status);
     return hipGetLastError();
 }

@@ -94,6 +94,19 @@ __device__ __forceinline__ uint32_t kvc_f2h2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
 }
 
+// Nonzero when some byte of w is >= A (4 <= A <= 256), without unpacking the
+// bytes: for A <= 128 a byte b is >= A when its top bit is set or its low
+// seven bits plus 128 - A carry into bit 7; for A > 128 when its top bit is
+// set and its low seven bits plus 256 - A carry into bit 7.  The sums stay
+// below 256, so no carry crosses into the next byte.
+__host__ __device__ __forceinline__ uint32_t kvc_bytes_ge(uint32_t w, uint32_t A)
+{
+    if (A >= 256u) return 0u;
+    const uint32_t lo = w & 0x7F7F7F7Fu;
+    if (A <= 128u) return ((lo + (128u - A) * 0x01010101u) | w) & 0x80808080u;
+    return ((lo + (256u - A) * 0x01010101u) & w) & 0x80808080u;
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
     for (int off = 32; off > 0; off >>= 1) {
@@ -111,9 +124,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 // eight.  Which XCD runs a block changes nothing but where its reads hit.
 __host__ __device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nb)
 {
-#ifdef KVC_NO_XCD_REMAP
-    return b;
-#endif
     const int64_t per = nb >> 3;
     if (b >= (per << 3)) return b;
     return (b & 7) * per + (b >> 3);

@@ -21,13 +21,9 @@
 
 // Launches of at most this many streams decode with a group of lanes per
 // stream (k_decode_group), for rows of 8 to 64 entries.
-#ifndef KVC_DEC_GROUP_MAX_STREAMS
-#define KVC_DEC_GROUP_MAX_STREAMS 16384
-#endif
+constexpr int64_t KVC_DEC_GROUP_MAX_STREAMS = 16384;
 // Lanes per stream there for rows of 16 or 32 entries (4 or 8; 64-entry rows use 8).
-#ifndef KVC_DEC_GROUP_LANES
-#define KVC_DEC_GROUP_LANES 4
-#endif
+constexpr int64_t KVC_DEC_GROUP_LANES = 4;
 
 namespace {
 

@@ -42,7 +42,8 @@ template <bool VEC16, int PER, int ENC_SW, int SPW>
 __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
                                                 const uint16_t *__restrict__ cdf,
                                                 uint8_t *__restrict__ slots,
-                                                uint16_t *__restrict__ stream_len, KParams p, int CT)
+                                                uint16_t *__restrict__ stream_len, KParams p, int CT,
+                                                int32_t *status)
 {
     static_assert(SPW == 16 || SPW == 32 || SPW == 64, "16, 32 or 64 streams per wave");
     constexpr int SPB = 4 * SPW;   // streams (token rows) per block
@@ -83,6 +84,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
     constexpr int NP = SPB * per_row / 256;  // pieces per thread
     static_assert(NP >= 1 && SPB * per_row == 256 * NP, "whole pieces per thread");
     u32x4 sv[NP];
+    uint32_t badsym = 0;  // some staged symbol byte is >= A
     auto load_syms = [&](int s0) {
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
@@ -92,6 +94,10 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
             sv[i] = (tok < g.nj && cc < C) ? *(const u32x4 *)(sym + (g.row0 + tok) * C + cc)
                                            : u32x4{0, 0, 0, 0};
         }
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+            badsym |= kvc_bytes_ge(sv[i].x, (uint32_t)A) | kvc_bytes_ge(sv[i].y, (uint32_t)A) |
+                      kvc_bytes_ge(sv[i].z, (uint32_t)A) | kvc_bytes_ge(sv[i].w, (uint32_t)A);
     };
     auto store_syms = [&]() {
 #pragma unroll
@@ -141,12 +147,14 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
         } else {
             for (int c = c0; c < c1; ++c) {
                 uint32_t s = q[c];
+                badsym |= s >= (uint32_t)A ? 1u : 0u;
                 s = min(s, (uint32_t)A - 1u);
                 enc_pair(e, pairs[(c - c0) * A + s], out);
             }
         }
     }
     if (active) stream_len[sid] = (uint16_t)enc_finish(e, out);
+    if (badsym) kvc_flag(status, KVC_DEV_BAD_SYMBOL);
 }
 
 __global__ __launch_bounds__(256) void k_slab_sum(const uint16_t *__restrict__ stream_len,
@@ -423,7 +431,8 @@ template <int PERC>
 __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict__ sym,
                                                       const uint16_t *__restrict__ cdf,
                                                       uint8_t *__restrict__ slots,
-                                                      uint16_t *__restrict__ stream_len, KParams p, int CH)
+                                                      uint16_t *__restrict__ stream_len, KParams p, int CH,
+                                                      int32_t *status)
 {
     constexpr int SPB = 64;  // streams per block
     constexpr int GB = 4;    // blocks per slot region
@@ -475,6 +484,7 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
     ChunkPairs<PERC> cp;
     // the symbols of the block's 64 streams, 16-byte pieces, 16 per thread in
     // flight, with the first pair chunk
+    uint32_t badsym = 0;  // some staged symbol byte is >= A
     {
         // the block's rows are contiguous in sym: piece k is bytes [16 k, 16 k
         // + 16) from its first row, row k / per_row of the table
@@ -496,6 +506,11 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
                 const int r = (int)div_by_mulhi((uint32_t)k, mrow);
                 if (k < npieces) *(lds_u32x4 *)(stab + k * 16 + r * 16) = v[i];
             }
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                badsym |= kvc_bytes_ge(v[i].x, (uint32_t)A) |
+                          kvc_bytes_ge(v[i].y, (uint32_t)A) | kvc_bytes_ge(v[i].z, (uint32_t)A) |
+                          kvc_bytes_ge(v[i].w, (uint32_t)A);
         }
     }
     // This lane's symbols [c, c + n) (c, n multiples of 16) and their pairs
@@ -609,6 +624,7 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
     if (lane == 0) s_tot[wid] = len;
     __syncthreads();
     if (threadIdx.x == 0) *btot = s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
+    if (badsym) kvc_flag(status, KVC_DEV_BAD_SYMBOL);
 }
 
 // k_pack for slots holding each stream contiguously (k_encode_split): a wave
@@ -707,17 +723,11 @@ __global__ void k_zero_u64(uint64_t *dst) { *dst = 0; }
 }  // namespace
 
 // Launches of at most this many streams stage wider CDF and symbol tiles.
-#ifndef KVC_ENC_WIDE_MAX_STREAMS
-#define KVC_ENC_WIDE_MAX_STREAMS 32768
-#endif
+constexpr int64_t KVC_ENC_WIDE_MAX_STREAMS = 32768;
 // Launches of at most this many streams code 16 streams per wave, others 64.
-#ifndef KVC_ENC_SPARSE_MAX_STREAMS
-#define KVC_ENC_SPARSE_MAX_STREAMS 16384
-#endif
+constexpr int64_t KVC_ENC_SPARSE_MAX_STREAMS = 16384;
 // Launches of at most this many streams pack 16 streams per wave, others 64.
-#ifndef KVC_PACK_SPARSE_MAX_STREAMS
-#define KVC_PACK_SPARSE_MAX_STREAMS 16384
-#endif
+constexpr int64_t KVC_PACK_SPARSE_MAX_STREAMS = 16384;
 
 // Symbol tile width: 128 channels for launches of few streams, else 64.
 static int enc_symbol_tile(int64_t n_streams) { return n_streams <= KVC_ENC_WIDE_MAX_STREAMS ? 128 : 64; }
@@ -727,16 +737,12 @@ static int enc_streams_per_wave(int64_t n_streams) { return n_streams <= KVC_ENC
 
 // Launches of at most this many streams code each stream with a quad of lanes
 // (k_encode_split) where the shape allows it.
-#ifndef KVC_ENC_SPLIT_MAX_STREAMS
-#define KVC_ENC_SPLIT_MAX_STREAMS 16384
-#endif
+constexpr int64_t KVC_ENC_SPLIT_MAX_STREAMS = 16384;
 
 // Split launches of at most this many encoder blocks take their slab offsets
 // from k_pack_flat (each pack wave sums the block totals before its slab)
 // instead of k_slab_sum and k_scan.
-#ifndef KVC_PACK_FUSED_MAX_BLOCKS
-#define KVC_PACK_FUSED_MAX_BLOCKS 1024
-#endif
+constexpr int64_t KVC_PACK_FUSED_MAX_BLOCKS = 1024;
 
 // k_encode_split's pair chunk (channels) and dynamic LDS for this shape, or
 // 0 when the shape does not take it: C % 64 == 0, A <= 64, a power-of-two
@@ -804,7 +810,7 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
             if (e != hipSuccess) return e;
         }
         hipLaunchKernelGGL((k_encode_split<16>), dim3((unsigned)(regions * 4)), dim3(256), lds_split, stream,
-                           sym, cdf, slots, stream_len, p, ch);
+                           sym, cdf, slots, stream_len, p, ch, status);
         if (regions * 4 <= KVC_PACK_FUSED_MAX_BLOCKS) {
             // the slab offsets come out of the pack itself, from the encoder's block totals
             hipLaunchKernelGGL(k_pack_flat<true>, dim3((unsigned)(regions * 16)), dim3(64), 0, stream, slots,
@@ -821,7 +827,7 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
     }
 #define KVC_ENC(V, P, S, W, L)                                                                       \
     hipLaunchKernelGGL((k_encode<V, P, S, W>), grid, dim3(256), L, stream, sym, cdf, slots, stream_len, \
-                       p, CT)
+                       p, CT, status)
 #define KVC_ENC_S(S, W)                                                                              \
     {                                                                                                \
         const size_t lds_syms = lds_pairs + 4 * W * (size_t)(S + 16);                                \

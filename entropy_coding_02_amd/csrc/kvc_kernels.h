@@ -30,7 +30,8 @@ bool quant_cdf_levels_ok(const KParams &p, const LevelParams &lv);
 hipError_t launch_quant_cdf_levels(const uint16_t *kv, uint16_t *max1, const KParams &p,
                                    LevelParams lv, int32_t *status, hipStream_t stream);
 
-hipError_t launch_cdf(const uint8_t *sym, uint16_t *cdf, const KParams &p, hipStream_t stream);
+hipError_t launch_cdf(const uint8_t *sym, uint16_t *cdf, const KParams &p, int32_t *status,
+                      hipStream_t stream);
 
 hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots,
                          uint64_t *slab_total, uint16_t *stream_len, uint64_t *slab_off,

@@ -69,6 +69,7 @@ enum kvc_status {
 #define KVC_DEV_PAYLOAD_OVERFLOW 4 /* the packed payload did not fit (kvc_encode, kvc_serialize) */
 #define KVC_DEV_BAD_CDF 8          /* a CDF row the container cannot carry (kvc_serialize) */
 #define KVC_DEV_BAD_CONTAINER 16   /* a container that does not match the descriptor (kvc_deserialize) */
+#define KVC_DEV_BAD_SYMBOL 32      /* a symbol >= A, outside every CDF row (kvc_cdf, kvc_encode) */
 
 enum kvc_dtype { KVC_F16 = 0, KVC_F32 = 1 };
 
@@ -146,10 +147,14 @@ int kvc_quantize_levels(const kvc_desc *levels, int32_t n_levels, const uint16_t
  * For chunk j with N_j tokens, layer, K|V and channel c: n_s = count of
  * symbol s in the chunk's column, C_k = n_0 + .. + n_{k-1}, K = 65536 - A,
  *   cdf_k = k + floor(C_k * K / N_j),  k = 0..A-1     (every frequency >= 1)
- *   sym  [L][2][T][C] uint8 (device, read; values >= A are counted as A-1)
- *   cdf  [NC][L][2][C][A] uint16 (device, written)
+ *   sym         [L][2][T][C] uint8 (device, read)
+ *   cdf         [NC][L][2][C][A] uint16 (device, written)
+ *   dev_status  device int32 (or NULL): a symbol >= A sets KVC_DEV_BAD_SYMBOL,
+ *               and the CDFs of its slab are then unspecified (the kernels
+ *               stay inside their buffers)
  */
-int kvc_cdf(const kvc_desc *desc, const uint8_t *sym, uint16_t *cdf, void *stream);
+int kvc_cdf(const kvc_desc *desc, const uint8_t *sym, uint16_t *cdf, int32_t *dev_status,
+            void *stream);
 
 /*
  * Range coding of every stream and packing, [CG] 2.1 (ac_enc) and 1.2 point 3.
@@ -165,6 +170,8 @@ int kvc_cdf(const kvc_desc *desc, const uint8_t *sym, uint16_t *cdf, void *strea
  *   slab_off    [n_slabs + 1] uint64 (device, written; slab_off[n_slabs] = payload size)
  *   payload     payload_cap bytes (device, written); if the payload is larger,
  *               KVC_DEV_PAYLOAD_OVERFLOW is set and only bytes below the cap are written
+ * A symbol >= A sets KVC_DEV_BAD_SYMBOL; the streams of its slab are then
+ * unspecified (it has no CDF interval to be coded with).
  */
 int kvc_encode(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf, void *scratch,
                int64_t scratch_bytes, uint16_t *stream_len, uint64_t *slab_off, uint8_t *payload,

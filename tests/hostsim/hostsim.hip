@@ -13,6 +13,9 @@ extern "C" {
 // The kernels' XCD-aware block renumbering (kvc_common.h).
 int64_t hostsim_xcd_block(int64_t b, int64_t nb) { return xcd_block(b, nb); }
 
+// The kernels' packed test for symbol bytes >= A (kvc_common.h).
+uint32_t hostsim_bytes_ge(uint32_t w, uint32_t A) { return kvc_bytes_ge(w, A); }
+
 // Encode one stream into `slot` (>= round_up(2C+16, 16) bytes); returns its length.
 int64_t hostsim_encode_stream(const uint8_t *q, int32_t C, int32_t A, const uint16_t *cdf_rows,
                               uint8_t *slot)

@@ -97,6 +97,10 @@ def test_null_and_misaligned_pointers_rejected(lib):
     for nb in (0, 2, 4, 10, 12, 18):
         assert lib.kvc_decode(d.ref, 64, nb, 64, 64, 64, 64, None, 64, 0, None, None) == kvc.KVC_ERR_ARG
     assert lib.kvc_dequantize(d.ref, 64, 64, 64, 9, None) == kvc.KVC_ERR_ARG
+    # kvc_cdf: null symbols, misaligned CDF or status
+    assert lib.kvc_cdf(d.ref, None, 64, None, None) == kvc.KVC_ERR_ARG
+    assert lib.kvc_cdf(d.ref, 64, 66, None, None) == kvc.KVC_ERR_ARG
+    assert lib.kvc_cdf(d.ref, 64, 64, 66, None) == kvc.KVC_ERR_ARG
     assert lib.kvc_status_string(kvc.KVC_ERR_CAPACITY) == b"buffer too small"
 
 

@@ -41,6 +41,8 @@ def hs():
     lib.hostsim_encode_stream_split.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32]
     lib.hostsim_xcd_block.restype = ctypes.c_int64
     lib.hostsim_xcd_block.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    lib.hostsim_bytes_ge.restype = ctypes.c_uint32
+    lib.hostsim_bytes_ge.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
     return lib
 
 
@@ -172,3 +174,30 @@ def test_xcd_block_renumbering_is_a_bijection(hs):
         for x in range(8):
             mine = sorted(got[b] for b in range(x, 8 * per, 8))
             assert mine == list(range(x * per, (x + 1) * per)), (nb, x)
+
+
+def test_bytes_ge_exhaustive(hs):
+    """The kernels' packed check for symbol bytes >= A (what raises
+    KVC_DEV_BAD_SYMBOL in the CDF and encoder kernels): for every even A in
+    [4, 256] and every byte value in every byte position (the other bytes
+    0 or A - 1, the largest valid symbol), bit 7 of exactly the bytes >= A is
+    set; plus random dwords against a byte-by-byte comparison."""
+    rng = np.random.default_rng(5)
+    rand = rng.integers(0, 2**32, 400, dtype=np.uint64)
+    for A in range(4, 257, 2):
+        for fill in (0, A - 1):
+            for pos in range(4):
+                for b in range(256):
+                    w = 0
+                    for k in range(4):
+                        w |= (b if k == pos else fill) << (8 * k)
+                    got = hs.hostsim_bytes_ge(w, A)
+                    want = (0x80 << (8 * pos)) if b >= A else 0
+                    assert got == want, (A, fill, pos, b, hex(got))
+        for w in rand:
+            w = int(w)
+            want = 0
+            for k in range(4):
+                if ((w >> (8 * k)) & 0xFF) >= A:
+                    want |= 0x80 << (8 * k)
+            assert hs.hostsim_bytes_ge(w, A) == want, (A, hex(w))
