@@ -25,6 +25,9 @@ constexpr int64_t KVC_DEC_GROUP_MAX_STREAMS = 16384;
 // Lanes per stream there for rows of 16 or 32 entries (4 or 8; 64-entry rows use 8).
 constexpr int64_t KVC_DEC_GROUP_LANES = 4;
 
+// Record dwords per channel of k_decode_mode: ModeRec and the block heads.
+#define DEC_MODE_RS(NSTEP) ((NSTEP) <= 5 ? 8 : 12)
+
 namespace {
 
 enum { ODT_F16 = 0, ODT_F32 = 1 };
@@ -195,6 +198,208 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
                 if constexpr ((OUT & OUT_SYM) != 0) so[c] = (uint8_t)s;
                 if constexpr (ODT >= 0) {
                     const float y = lv * m;
+                    if constexpr (ODT == ODT_F16)
+                        ((uint16_t *)out)[row * C + c] = (uint16_t)kvc_f2h(y);
+                    else
+                        ((float *)out)[row * C + c] = y;
+                }
+            }
+        }
+    }
+
+    if (active && bad) kvc_flag(status, KVC_DEV_CORRUPT);
+}
+
+// Mode-first decoding, one lane per stream (256 tokens of one slab per
+// block), for rows of 8 to 64 entries.  Each tile's CDF rows are staged as
+// k_decode stages them, plus a record per channel (PairTile::store_mode): the
+// row's one symbol of frequency above 65536 - KVC_MODE_SPAN, if it has one,
+// with its start, frequency and dequantization value, and the row's block
+// heads.  All 64 lanes of a wave decode the same channel at each step, so
+// the record is one broadcast read.  When the row has such a symbol, every
+// lane first tries it: one multiply-add, one multiply and two compares, and
+// if all lanes land inside its interval with no renormalisation due, that is
+// the symbol (the row's only qualifying one on a non-decreasing row).  In
+// most chunks of long contexts most channels hardly vary, so most symbols
+// end there.  Otherwise the wave takes the exact two-level search with the
+// heads from the record.  Renormalisation takes its bits from a 32-bit window
+// at the stream's byte position (WinIn): no bit buffer to count or top up.
+// The output is k_decode's.
+template <bool VEC, int OUT, int NSTEP, bool PAD>
+__global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__ payload,
+                                                     int64_t payload_bytes,
+                                                     const uint64_t *__restrict__ slab_off,
+                                                     const uint16_t *__restrict__ stream_len,
+                                                     const uint16_t *__restrict__ cdf,
+                                                     const uint16_t *__restrict__ max1,
+                                                     uint8_t *__restrict__ sym_out, void *__restrict__ out,
+                                                     KParams p, int32_t *status, int CT)
+{
+    // LDS: lut[256] f32 | ring[256][17] u32 | rec[2][CT][RS] u32 | rows16 [CT][P2] u16 |
+    //      (pair, lut) [CT][A] u32x2
+    extern __shared__ uint32_t lds[];
+    __shared__ uint32_t s_red[4];
+    constexpr uint32_t P2 = 1u << NSTEP;
+    constexpr int NB = 1 << (NSTEP - 3);
+    constexpr int RS = DEC_MODE_RS(NSTEP);
+    const int C = p.C, A = p.A;
+    float *lut = (float *)lds;
+    lds_u32 *const ring = (lds_u32 *)(lds + 256) + threadIdx.x * 17u;
+    lds_u32 *const recs = (lds_u32 *)(lds + 256 + 256 * 17);
+    lds_u32 *const tile = recs + 2 * CT * RS;
+    const int n16 = (CT * (int)P2 + 1) / 2;
+    lds_u16 *const r16 = (lds_u16 *)tile;
+    lds_u32 *const pr = tile + n16;
+
+    const int bps = (p.Tc + 255) / 256;
+    const int64_t slab = blockIdx.x / bps;
+    const int tb = (int)(blockIdx.x - slab * bps);
+    const int t = tb * 256 + (int)threadIdx.x;
+    const SlabGeom g = slab_geom(p, slab);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const bool active = t < g.nj;
+
+    // bytes of the slab's streams before this block (only when chunk_tokens > 256)
+    uint32_t pre = 0;
+    const int n_before = min(tb * 256, g.nj);
+    for (int i = threadIdx.x; i < n_before; i += 256) pre += stream_len[g.sid0 + i];
+    pre = wave_sum_u32(pre);
+    if (lane == 0) s_red[wid] = pre;
+    __syncthreads();
+    pre = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    __syncthreads();
+    // exclusive scan of this block's lengths
+    const uint32_t len = active ? stream_len[g.sid0 + t] : 0u;
+    uint32_t incl = len;
+    for (int off = 1; off < 64; off <<= 1) {
+        uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_red[wid] = incl;
+    if (threadIdx.x < (unsigned)A) {
+        const int M = p.maxq[g.lk];
+        lut[threadIdx.x] = (float)((int)threadIdx.x - M) / (float)M;
+    }
+    // padding of the search rows and of the record heads (never rewritten by
+    // the tile stores), and both record buffers' kind words
+    if (P2 > (uint32_t)A)
+        for (int e = threadIdx.x; e < CT * (int)P2; e += 256)
+            if ((uint32_t)(e & (P2 - 1)) >= (uint32_t)A) r16[e] = 0xFFFFu;
+    for (int i = threadIdx.x; i < 2 * CT; i += 256) {
+        recs[i * RS] = 0u;
+        for (int b = 1; b < NB; ++b)
+            if (8 * b >= A) recs[i * RS + 3 + b] = 0xFFFFu;
+    }
+    __syncthreads();
+    uint32_t wbase = 0;
+    for (int i = 0; i < wid; ++i) wbase += s_red[i];
+
+    const int64_t row = g.row0 + (active ? t : 0);
+    const uint64_t off = active ? slab_off[slab] + pre + wbase + incl - len : 0;
+    WinIn<lds_u32 *> in;
+    uint32_t code = in.init(payload, off, len, (uint64_t)payload_bytes, ring);
+    uint32_t range = 0xFFFFFFFFu;
+    constexpr int ODT = (OUT & OUT_F16) ? ODT_F16 : (OUT & OUT_F32) ? ODT_F32 : -1;
+    constexpr int PER = 2;  // pairs staged per thread: CT * A / 2 / 256
+    const float m = (ODT >= 0) ? kvc_h2f(max1[row]) : 0.0f;
+    uint32_t bad = 0;
+    uint8_t *so = (OUT & OUT_SYM) ? sym_out + row * C : nullptr;
+    const uint16_t *srows = cdf + slab * C * A;
+    const int ntiles = (C + CT - 1) / CT;
+    const lds_u32 *rec = recs;
+    // one symbol of tile channel cl; lvb receives its dequantization value
+    auto decode1 = [&](int cl, uint32_t &lvb) -> uint32_t {
+        const lds_u32 *rc = rec + cl * RS;
+        const u32x4 ra = *(const lds_u32x4 *)rc;
+        const u32x4 rb = *(const lds_u32x4 *)(rc + 4);
+        uint32_t hd[NB];
+        hd[0] = 0u;
+        if constexpr (NB >= 2) hd[1] = rb.x;
+        if constexpr (NB >= 4) {
+            hd[2] = rb.y;
+            hd[3] = rb.z;
+        }
+        if constexpr (NB >= 8) {
+            const u32x4 rd = *(const lds_u32x4 *)(rc + 8);
+            hd[4] = rb.w;
+            hd[5] = rd.x;
+            hd[6] = rd.y;
+            hd[7] = rd.z;
+        }
+        const ModeRec mr{(uint32_t)__builtin_amdgcn_readfirstlane((int)ra.x), (int32_t)ra.y, ra.z, ra.w};
+        const lds_u16 *rowp = r16 + cl * P2;
+        auto piece = [&](uint32_t b) -> kvc_u32x4 { return *(const lds_u32x4 *)(rowp + 8u * b); };
+        const lds_u32 *prow = pr + 2 * cl * A;  // uniform: the entry address is one shift-add of s
+        auto ent = [&](uint32_t s) -> kvc_u32x2 { return *(const lds_u32x2 *)(prow + 2 * s); };
+        uint32_t fast;
+        return dec_symbol_mode<NSTEP, PAD>(code, range, in, mr, hd, piece, ent, (uint32_t)A, &bad, &fast,
+                                           &lvb);
+    };
+
+    PairTile<PER> pt;
+    uint32_t hw[16];
+    auto put_f16 = [&](int cb, int nb) {
+        uint4 *o = (uint4 *)((uint16_t *)out + row * C + cb);
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+            if (gi * 8 < nb) o[gi] = make_uint4(hw[4 * gi], hw[4 * gi + 1], hw[4 * gi + 2], hw[4 * gi + 3]);
+    };
+    pt.load(srows, 0, CT, C, A);
+    for (int it = 0; it < ntiles; ++it) {
+        const int c0 = it * CT, c1 = min(C, c0 + CT);
+        lds_u32 *const rnow = recs + (it & 1) * CT * RS;
+        __syncthreads();  // all waves are done with the previous tile
+        pt.store_mode(pr, CT, A, r16, (int)P2, (const uint32_t *)lut, rnow, recs + ((it + 1) & 1) * CT * RS,
+                      RS);
+        __syncthreads();
+        rec = rnow;
+        if (it + 1 < ntiles) pt.load(srows, c0 + CT, CT, C, A);
+        if (!active) continue;
+        if constexpr (VEC) {
+            for (int cb = c0; cb < c1; cb += 32) {
+                const int nb = min(32, c1 - cb);  // 16 or 32
+                float fw[8];
+#pragma unroll
+                for (int gi = 0; gi < 4; ++gi) {
+                    if (gi * 8 >= nb) break;
+                    const int cg = cb + gi * 8;
+                    in.group();
+                    uint32_t sw[2] = {0, 0};
+                    float ylo = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        uint32_t lvb;
+                        const uint32_t s = decode1(cg - c0 + i, lvb);
+                        sw[i >> 2] |= s << (8 * (i & 3));
+                        if constexpr (ODT >= 0) {
+                            const float y = __uint_as_float(lvb) * m;
+                            if constexpr (ODT == ODT_F16) {
+                                if (i & 1)
+                                    hw[gi * 4 + (i >> 1)] = kvc_f2h2(ylo, y);
+                                else
+                                    ylo = y;
+                            } else {
+                                fw[i] = y;
+                            }
+                        }
+                    }
+                    if constexpr ((OUT & OUT_SYM) != 0) *(uint2 *)(so + cg) = make_uint2(sw[0], sw[1]);
+                    if constexpr (ODT == ODT_F32) {
+                        float4 *o = (float4 *)((float *)out + row * C + cg);
+                        o[0] = make_float4(fw[0], fw[1], fw[2], fw[3]);
+                        o[1] = make_float4(fw[4], fw[5], fw[6], fw[7]);
+                    }
+                }
+                if constexpr (ODT == ODT_F16) put_f16(cb, nb);
+            }
+        } else {
+            for (int c = c0; c < c1; ++c) {
+                if ((c & 7) == 0) in.group();
+                uint32_t lvb;
+                const uint32_t s = decode1(c - c0, lvb);
+                if constexpr ((OUT & OUT_SYM) != 0) so[c] = (uint8_t)s;
+                if constexpr (ODT >= 0) {
+                    const float y = __uint_as_float(lvb) * m;
                     if constexpr (ODT == ODT_F16)
                         ((uint16_t *)out)[row * C + c] = (uint16_t)kvc_f2h(y);
                     else
@@ -535,6 +740,12 @@ static size_t dec_lds_bytes(int A, int CT)
     return sizeof(uint32_t) * (256 + 256 * 17 + n16 + 2 * (size_t)CT * A);
 }
 
+// k_decode_mode: as dec_lds_bytes plus two buffers of CT records.
+static size_t dec_mode_lds_bytes(int A, int CT, int nstep)
+{
+    return dec_lds_bytes(A, CT) + sizeof(uint32_t) * 2 * (size_t)CT * DEC_MODE_RS(nstep);
+}
+
 int decode_lanes_per_stream(const KParams &p)
 {
     const int nstep = (int)cdf_nstep((uint32_t)p.A);
@@ -603,18 +814,20 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
     if (decode_lanes_per_stream(p) > 1)
         return launch_decode_group(payload, payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out,
                                    mode, p, status, vec, CT, lds, nstep, stream);
-    // Rows of 8 to 64 entries take the two-level search (measured faster than
-    // binary lifting at every launch size since its searches run over
-    // registers); 4-entry and 128- or 256-entry rows binary lifting.
+    // Rows of 8 to 64 entries take the mode-first decoder (its exact path is
+    // the two-level search, measured faster than binary lifting at every
+    // launch size since its searches run over registers); 4-entry and 128-
+    // or 256-entry rows binary lifting.
+    const size_t lds_mode = dec_mode_lds_bytes(p.A, CT, nstep);
 #define KVC_DEC(V, O, N, B)                                                                          \
     hipLaunchKernelGGL((k_decode<V, O, N, B>), grid, block, lds, stream, payload, payload_bytes,     \
                        slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
 #define KVC_DECB(V, O, N)                                                                            \
     if (p.A == (1 << N))                                                                             \
-        hipLaunchKernelGGL((k_decode<V, O, N, true, false>), grid, block, lds, stream, payload,      \
+        hipLaunchKernelGGL((k_decode_mode<V, O, N, false>), grid, block, lds_mode, stream, payload,  \
                            payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT); \
     else                                                                                             \
-        hipLaunchKernelGGL((k_decode<V, O, N, true, true>), grid, block, lds, stream, payload,       \
+        hipLaunchKernelGGL((k_decode_mode<V, O, N, true>), grid, block, lds_mode, stream, payload,   \
                            payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
 #define KVC_DEC_N(V, O)                                                                              \
     switch (nstep) {                                                                                 \

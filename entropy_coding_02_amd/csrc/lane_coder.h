@@ -32,8 +32,20 @@
 #define KVC_HD __host__ __device__ __forceinline__
 
 typedef uint32_t kvc_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t kvc_u32x2 __attribute__((ext_vector_type(2)));
 
 KVC_HD uint32_t kvc_bswap32(uint32_t v) { return __builtin_bswap32(v); }
+
+// a * b for a, b < 2^24 (one full-rate 24-bit multiply on the GPU, where a
+// 32-bit multiply whose operands the compiler cannot bound is quarter rate).
+KVC_HD uint32_t kvc_umul24(uint32_t a, uint32_t b)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __umul24(a, b);
+#else
+    return (a & 0xFFFFFFu) * (b & 0xFFFFFFu);
+#endif
+}
 
 // Shift count (bits) that brings range back to >= 2^24; range must be >= 2^8.
 KVC_HD uint32_t kvc_renorm_bits(uint32_t range) { return (uint32_t)__builtin_clz(range) & 24u; }
@@ -540,7 +552,7 @@ KVC_HD uint32_t heads_last(uint32_t idx, const uint32_t *h, uint32_t r, uint32_t
     if constexpr (NB == 1) {
         return idx;
     } else {
-        const bool a = r * h[NB / 2] <= code;
+        const bool a = kvc_umul24(r, h[NB / 2]) <= code;
         uint32_t g[NB / 2];
 #pragma unroll
         for (int k = 0; k < NB / 2; ++k) g[k] = a ? h[NB / 2 + k] : h[k];
@@ -607,4 +619,207 @@ KVC_HD uint32_t cdf_nstep(uint32_t A)
     uint32_t n = 0;
     while ((1u << n) < A) ++n;
     return n;
+}
+
+// ------------------------------------ decoder fed by a byte-position window
+//
+// Renormalisation shifts code left by n = 0, 8 or 16 bits (a whole number of
+// bytes) and brings in the next n stream bits.  WinIn keeps posb, the stream
+// position (in bits, a multiple of 8) of the first bit not yet in code, and
+// hands out the 32 stream bits from there as one window: ring dwords
+// posb/32 and posb/32 + 1 funnel-shifted by posb mod 32.  Narrowing and
+// renormalising are then code = the high half of ((code - r*st) : window)
+// << n and posb += n: no bit buffer to count and top up per symbol.
+//
+// The ring holds 16 stream dwords per lane (dword j at slot j mod 16) and a
+// 17th slot with a copy of slot 0, so a window read at slot 15 needs no
+// wrap.  Feeding is RingIn's: a 16-byte piece (4 stream dwords) is fetched
+// one group of 8 symbols before it is committed.  At a group start, after
+// the commit, w - posb/32 >= 6 holds: the group consumes at most 16 bytes
+// (4 dwords) and a window needs 2 dwords, and a piece is asked for whenever
+// w - posb/32 <= 10, so the next group starts with at least 6 again.  A
+// commit overwrites the slots of dwords w - 16 .. w - 13, none of which is
+// still needed (w - posb/32 <= 10 when the piece was asked for).
+template <class Ring>
+struct WinIn {
+    const uint8_t *p;  // base + a0
+    Ring ring;         // this lane's 17 ring slots
+    uint32_t len;      // stream length in bytes
+    int32_t lim16;     // largest offset from p at which a 16-byte piece may be loaded (>= -12)
+    uint32_t sh;       // (start & 3) * 8
+    uint32_t w;        // stream dwords committed: [0, w), a multiple of 4
+    uint32_t posb;     // stream bit position of the next bit not yet in code
+    uint32_t last;     // raw dword w: the low part of stream dword w
+    kvc_u32x4 st;      // the piece in flight: raw dwords w+1 .. w+4, moved back by `back` bytes
+    uint32_t back;     // how far the piece was moved back (0 unless near the buffer end)
+    uint32_t want;     // a piece is in flight
+
+    KVC_HD void issue()
+    {
+        const int32_t off = 4 * (int32_t)(w + 1u);
+        const int32_t at = off < lim16 ? off : lim16;
+        __builtin_memcpy(&st, p + at, 16);
+        back = (uint32_t)(off - at);
+    }
+    // Stream dwords w .. w+3, big-endian, zero past the stream, into the ring.
+    KVC_HD void commit()
+    {
+        kvc_u32x4 r = st;
+        if (!kvc_all(back == 0u)) {
+            const uint32_t d = back >> 2;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t i = (uint32_t)k + d;
+                r[k] = i == 1u ? st[1] : i == 2u ? st[2] : i == 3u ? st[3] : (i == 0u ? st[0] : 0u);
+            }
+        }
+        uint32_t v[4];
+        v[0] = kvc_bswap32(kvc_alignbit(r[0], last, sh));
+        v[1] = kvc_bswap32(kvc_alignbit(r[1], r[0], sh));
+        v[2] = kvc_bswap32(kvc_alignbit(r[2], r[1], sh));
+        v[3] = kvc_bswap32(kvc_alignbit(r[3], r[2], sh));
+        if (!kvc_all(4u * w + 16u <= len)) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t pos = 4u * (w + (uint32_t)k);
+                const uint32_t keep = len > pos ? len - pos : 0u;
+                v[k] = keep >= 4u ? v[k] : (keep == 0u ? 0u : v[k] & ~(0xFFFFFFFFu >> (8u * keep)));
+            }
+        }
+        const uint32_t b = w & 12u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ring[b + (uint32_t)k] = v[k];
+        if (b == 0u) ring[16] = v[0];
+        last = r[3];
+        w += 4u;
+    }
+    // Returns the first 4 stream bytes (the decoder's initial code).
+    KVC_HD uint32_t init(const uint8_t *base, uint64_t start, uint64_t length, uint64_t capacity, Ring rg)
+    {
+        uint64_t a0 = start & ~(uint64_t)3;
+        sh = (uint32_t)(start & 3u) * 8u;
+        len = (uint32_t)length;
+        if (a0 + 4u > capacity) {  // only an empty stream at the very end of the buffer
+            a0 = capacity - 4u;
+            len = 0;
+        }
+        p = base + a0;
+        const uint64_t room = capacity - 16u;  // the last piece starts here
+        lim16 = a0 > room ? -(int32_t)(a0 - room) : (room - a0 > 0x7FFFFFF0u ? 0x7FFFFFF0 : (int32_t)(room - a0));
+        ring = rg;
+        w = 0;
+        last = *(const uint32_t *)p;
+        issue();
+        commit();
+        issue();
+        commit();  // stream dwords 0..7 in the ring
+        issue();   // stream dwords 8..11 in flight
+        want = 1;
+        posb = 32;
+        return ring[0];
+    }
+    // Once per group of 8 symbols.
+    KVC_HD void group()
+    {
+        if (want) commit();
+        want = w - (posb >> 5) <= 10u ? 1u : 0u;
+        if (want) issue();
+    }
+    // The 32 stream bits from posb on.
+    KVC_HD uint32_t window() const
+    {
+        const uint32_t j = (posb >> 5) & 15u;
+        const uint64_t two = ((uint64_t)ring[j] << 32) | ring[j + 1u];
+        return (uint32_t)((two << (posb & 31u)) >> 32);
+    }
+};
+
+// code - r * st as r * (-st) + code (a 24-bit signed multiply-add on the GPU:
+// r < 2^16 and -st >= -65535 both fit 24 signed bits).
+KVC_HD uint32_t kvc_mad_nst(uint32_t r, int32_t nst, uint32_t code)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return (uint32_t)__mul24((int)r, nst) + code;
+#else
+    return (uint32_t)((int64_t)r * nst) + code;
+#endif
+}
+
+// Narrow to the interval [st, st + fr) found for r = range >> 16 and
+// renormalise from the window.  Returns 1 if code left the interval.
+template <class In>
+KVC_HD uint32_t dec_step_win(uint32_t &code, uint32_t &range, In &in, uint32_t r, uint32_t st,
+                             uint32_t fr)
+{
+    const uint32_t win = in.window();
+    const uint32_t c2 = code - r * st;
+    const uint32_t rn = r * fr;
+    const uint32_t bad = c2 >= rn ? 1u : 0u;
+    const uint32_t n = kvc_renorm_bits(rn);
+    range = rn << n;
+    code = (uint32_t)(((((uint64_t)c2) << 32) | win) << n >> 32);
+    in.posb += n;
+    return bad;
+}
+
+// A CDF row's mode record for the mode-first decoder: the row's one symbol
+// whose frequency exceeds 65536 - KVC_MODE_SPAN (there is at most one), or
+// none.  Rows of chunks where a channel's symbol hardly varies (most rows of
+// the larger workloads) have one; for them every lane of a wave first tries
+// that symbol: one multiply-add and one multiply, and a check that every
+// lane's code lies in its interval with no renormalisation due.  Any other
+// case takes the exact search.
+#define KVC_MODE_SPAN 1024u
+struct ModeRec {
+    uint32_t kind_md;  // 1 | md << 8 when the row has such a symbol md, else 0
+    int32_t nst;       // -(start of md)
+    uint32_t fr;       // frequency of md
+    uint32_t lv;       // dequantization value of md (fp32 bits)
+};
+
+// The two-level search of cdf_search_blocks with its NB block heads given
+// (hd[0] = 0; the heads are row[8b], uniform over a wave in the kernels).
+template <int NSTEP, bool PAD, class Piece>
+KVC_HD uint32_t cdf_search_heads(const uint32_t *hd, const Piece &piece, uint32_t A, uint32_t r,
+                                 uint32_t code)
+{
+    static_assert(NSTEP >= 3 && NSTEP <= 6, "rows of 8 to 64 entries");
+    constexpr int NB = 1 << (NSTEP - 3);
+    const uint32_t b = heads_last<NB>(0u, hd, r, code);
+    const kvc_u32x4 v = piece(b);
+    const uint32_t dv[4] = {v[0], v[1], v[2], v[3]};
+    const uint32_t s = piece_last<8>(b, dv, r, code);
+    if constexpr (PAD) return s < A - 1u ? s : A - 1u;
+    return s;
+}
+
+// One symbol of the mode-first decoder: the mode record's symbol when every
+// lane lands in its interval without renormalising (*fast = 1), else the
+// exact two-level search (heads hd, pieces of the padded row); ent(s) gives
+// symbol s's (start | frequency << 16) pair and its dequantization value
+// (fp32 bits), and *lv receives the chosen symbol's.  Returns the symbol;
+// *bad |= 1 when the stream left its interval.
+template <int NSTEP, bool PAD, class Piece, class Ent, class In>
+KVC_HD uint32_t dec_symbol_mode(uint32_t &code, uint32_t &range, In &in, const ModeRec &m,
+                                const uint32_t *hd, const Piece &piece, const Ent &ent, uint32_t A,
+                                uint32_t *bad, uint32_t *fast, uint32_t *lv)
+{
+    const uint32_t r = range >> 16;
+    if (m.kind_md & 1u) {
+        const uint32_t d = kvc_mad_nst(r, m.nst, code);
+        const uint32_t rn = kvc_umul24(r, m.fr);
+        if (kvc_all(d < rn && rn >= (1u << 24))) {
+            code = d;
+            range = rn;
+            *fast = 1;
+            *lv = m.lv;
+            return m.kind_md >> 8;
+        }
+    }
+    *fast = 0;
+    const uint32_t s = cdf_search_heads<NSTEP, PAD>(hd, piece, A, r, code);
+    const kvc_u32x2 e = ent(s);
+    *bad |= dec_step_win(code, range, in, r, e[0] & 0xFFFFu, e[0] >> 16);
+    *lv = e[1];
+    return s;
 }

@@ -82,20 +82,25 @@ int64_t hostsim_encode_stream_split(const uint8_t *q, int32_t C, int32_t A, cons
 // Decode the stream at [off, off+len) of a buffer of `cap` bytes (a multiple
 // of 4, at least 4); returns the corrupt flag.
 // search 0: binary lifting; 1: the two-level search where the padded row has
-// 8 to 64 entries (binary lifting otherwise).
-int hostsim_decode_stream(const uint8_t *buf, int64_t cap, int64_t off, int64_t len, int32_t C,
-                          int32_t A, const uint16_t *cdf_rows, uint8_t *q, int32_t search)
+// 8 to 64 entries (binary lifting otherwise); 2: the mode-first decoder with
+// the window feed there (fast_count, if not NULL, counts its fast symbols).
+int hostsim_decode_stream_n(const uint8_t *buf, int64_t cap, int64_t off, int64_t len, int32_t C,
+                            int32_t A, const uint16_t *cdf_rows, uint8_t *q, int32_t search,
+                            int64_t *fast_count)
 {
-    uint32_t ring[16];
+    uint32_t ring[16], ring2[17];
     RingIn<uint32_t *> in;
     in.init(buf, (uint64_t)off, (uint64_t)len, (uint64_t)cap, ring);
     DecState d;
     dec_init(d, in);
+    WinIn<uint32_t *> win;  // the mode-first decoder's feed (search 2)
+    uint32_t wcode = win.init(buf, (uint64_t)off, (uint64_t)len, (uint64_t)cap, ring2), wrange = 0xFFFFFFFFu;
     uint32_t bad = 0, nstep = cdf_nstep((uint32_t)A), P2 = 1u << nstep;
     std::vector<uint16_t> padded(P2);
     std::vector<uint32_t> pairs(A);
     for (int32_t c = 0; c < C; ++c) {
         if ((c & 7) == 0) in.group();
+        if ((c & 7) == 0) win.group();
         if ((c & 1) == 0) dec_refill(d, in);
         const uint16_t *row = cdf_rows + (int64_t)c * A;
         for (uint32_t k = 0; k < P2; ++k) padded[k] = k < (uint32_t)A ? row[k] : 0xFFFFu;
@@ -106,6 +111,30 @@ int hostsim_decode_stream(const uint8_t *buf, int64_t cap, int64_t off, int64_t 
             return v;
         };
         uint32_t sym;
+        if (search == 2 && nstep >= 3 && nstep <= 6) {
+            // the mode-first decoder (lane_coder.h dec_symbol_mode), its record
+            // and block heads built from the row as the kernel's staging does
+            ModeRec m{0u, 0, 0u, 0u};
+            for (int32_t k = 0; k < A; ++k) {
+                const uint32_t pr = pairs[k];
+                if ((pr >> 16) > 65536u - KVC_MODE_SPAN)
+                    m = ModeRec{1u | ((uint32_t)k << 8), -(int32_t)(pr & 0xFFFFu), pr >> 16, 0u};
+            }
+            uint32_t hd[8] = {0u};
+            for (uint32_t b = 1; b < (P2 >> 3); ++b) hd[b] = padded[8 * b];
+            uint32_t fast = 0;
+            auto pa = [&](uint32_t k) { return kvc_u32x2{pairs[k], 0u}; };
+            uint32_t lvv = 0;
+            switch (nstep) {
+            case 3: sym = (uint32_t)A < 8u ? dec_symbol_mode<3, true>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv) : dec_symbol_mode<3, false>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv); break;
+            case 4: sym = (uint32_t)A < 16u ? dec_symbol_mode<4, true>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv) : dec_symbol_mode<4, false>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv); break;
+            case 5: sym = (uint32_t)A < 32u ? dec_symbol_mode<5, true>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv) : dec_symbol_mode<5, false>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv); break;
+            default: sym = (uint32_t)A < 64u ? dec_symbol_mode<6, true>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv) : dec_symbol_mode<6, false>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv); break;
+            }
+            q[c] = (uint8_t)sym;
+            if (fast_count) *fast_count += fast;
+            continue;
+        }
         if (search == 1 && nstep >= 3 && nstep <= 6) {
             switch (nstep) {
             case 3: sym = (uint32_t)A < (1u << 3) ? dec_symbol_blocks<3, true>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad) : dec_symbol_blocks<3, false>(d, padded.data(), piece, pairs.data(), (uint32_t)A, &bad); break;
@@ -129,6 +158,12 @@ int hostsim_decode_stream(const uint8_t *buf, int64_t cap, int64_t off, int64_t 
         q[c] = (uint8_t)sym;
     }
     return (int)bad;
+}
+
+int hostsim_decode_stream(const uint8_t *buf, int64_t cap, int64_t off, int64_t len, int32_t C,
+                          int32_t A, const uint16_t *cdf_rows, uint8_t *q, int32_t search)
+{
+    return hostsim_decode_stream_n(buf, cap, off, len, C, A, cdf_rows, q, search, nullptr);
 }
 
 }  // extern "C"

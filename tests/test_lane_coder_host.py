@@ -41,6 +41,9 @@ def hs():
     lib.hostsim_encode_stream_split.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32]
     lib.hostsim_xcd_block.restype = ctypes.c_int64
     lib.hostsim_xcd_block.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    lib.hostsim_decode_stream_n.restype = ctypes.c_int
+    lib.hostsim_decode_stream_n.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32, P]
     lib.hostsim_bytes_ge.restype = ctypes.c_uint32
     lib.hostsim_bytes_ge.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
     return lib
@@ -98,7 +101,7 @@ def test_random_and_skewed_streams(hs):
         q = rng.integers(0, A, C).astype(np.uint8)
         data = check(hs, q, rows)
         buf = np.frombuffer(data + bytes(max(16, (len(data) + 4) // 4 * 4) - len(data)), np.uint8).copy()
-        for search in (0, 1):
+        for search in (0, 1, 2):
             got, bad = h_decode(hs, buf, 0, len(data), rows, search=search)
             assert not bad and np.array_equal(got, q), (trial, search)
 
@@ -125,7 +128,7 @@ def test_zero_tail_trim_reaches_written_dwords(hs):
     check(hs, np.zeros(400, np.uint8), rows)  # empty stream
 
 
-@pytest.mark.parametrize("search", [0, 1])
+@pytest.mark.parametrize("search", [0, 1, 2])
 def test_decode_every_alignment_up_to_buffer_end(hs, search):
     """Streams at every byte alignment; the buffer ends right after the last
     stream (rounded up to whole dwords, the padding filled with junk that
@@ -152,7 +155,7 @@ def test_decode_every_alignment_up_to_buffer_end(hs, search):
             off += len(s)
 
 
-@pytest.mark.parametrize("search", [0, 1])
+@pytest.mark.parametrize("search", [0, 1, 2])
 def test_corrupt_streams_match_oracle_flag(hs, search):
     for rows in (np.tile(cdf_from_counts([5, 20, 5, 1]), (64, 1)),
                  np.tile(np.array([0] + list(range(65504, 65535)), np.uint16), (64, 1))):  # f=1 tail
@@ -201,3 +204,38 @@ def test_bytes_ge_exhaustive(hs):
                 if ((w >> (8 * k)) & 0xFF) >= A:
                     want |= 0x80 << (8 * k)
             assert hs.hostsim_bytes_ge(w, A) == want, (A, hex(w))
+
+
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
+def test_mode_first_decoder_on_kv_streams(hs, name):
+    """The mode-first decoder (search 2: the mode record's symbol tried first,
+    the exact two-level search otherwise, bits from the byte-position window)
+    decodes every stream of a KV-shaped slab set back to the oracle's
+    symbols, streams packed back to back at their payload offsets, and takes
+    its fast path for most symbols of these workloads."""
+    import kvgen
+    cfg = kvgen.CONFIGS[name].scaled(n_layers=4, n_tokens=300, layer_bins=((0, 2, int(kvgen.CONFIGS[name].bins().max())), (2, 4, 16)))
+    kv, _ = kvgen.generate(cfg)
+    bins, Tc = cfg.bins(), cfg.chunk_tokens
+    r = oracle.codec(kv, bins, Tc)
+    L, T, C, A = cfg.n_layers, cfg.n_tokens, cfg.n_channels, r["A"]
+    pay = r["payload"]
+    buf = np.concatenate([pay, np.full((-pay.size) % 4 + 16, 0xA5, np.uint8)])
+    fast = ctypes.c_int64(0)
+    sid, total = 0, 0
+    for j in range((T + Tc - 1) // Tc):
+        nj = min(Tc, T - j * Tc)
+        for lk in range(2 * L):
+            rows = np.ascontiguousarray(r["cdf"][j, lk // 2, lk % 2])
+            off = int(r["slab_off"][j * 2 * L + lk])
+            for t in range(nj):
+                n = int(r["stream_len"][sid])
+                q = np.empty(C, np.uint8)
+                bad = hs.hostsim_decode_stream_n(buf.ctypes.data, pay.size + (-pay.size) % 4, off, n, C, A,
+                                                 rows.ctypes.data, q.ctypes.data, 2, ctypes.byref(fast))
+                assert bad == 0
+                assert np.array_equal(q, r["sym"][lk // 2, lk % 2, j * Tc + t]), (j, lk, t)
+                off += n
+                sid += 1
+                total += C
+    assert fast.value > 0.3 * total, (fast.value, total)
