@@ -27,6 +27,13 @@ constexpr int64_t KVC_DEC_GROUP_LANES = 4;
 
 // Record dwords per channel of k_decode_mode: ModeRec and the block heads.
 #define DEC_MODE_RS(NSTEP) ((NSTEP) <= 5 ? 8 : 12)
+// Output block of k_decode_mode (channels whose fp16 outputs are stored
+// together): 64 (a whole 128-byte line per lane) for rows of up to 32 entries.
+#define DEC_MODE_OB(NSTEP) ((NSTEP) <= 5 ? 64 : 32)
+// Pairs each thread stages per tile: the tile's CT * A / 2 over 256 threads
+// (CT = dec_mode_tile_channels: 64 channels up to rows of 32 entries, so at
+// most 4; 16 channels of 64-entry rows, 2).
+#define DEC_MODE_PER(NSTEP) ((NSTEP) <= 5 ? 4 : 2)
 
 namespace {
 
@@ -225,7 +232,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
 // heads from the record.  Renormalisation takes its bits from a 32-bit window
 // at the stream's byte position (WinIn): no bit buffer to count or top up.
 // The output is k_decode's.
-template <bool VEC, int OUT, int NSTEP, bool PAD>
+template <bool VEC, int OUT, int NSTEP, bool PAD, int OB>
 __global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__ payload,
                                                      int64_t payload_bytes,
                                                      const uint64_t *__restrict__ slab_off,
@@ -281,12 +288,12 @@ __global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__
         lut[threadIdx.x] = (float)((int)threadIdx.x - M) / (float)M;
     }
     // padding of the search rows and of the record heads (never rewritten by
-    // the tile stores), and both record buffers' kind words
+    // the tile stores), and both record buffers' frequency words
     if (P2 > (uint32_t)A)
         for (int e = threadIdx.x; e < CT * (int)P2; e += 256)
             if ((uint32_t)(e & (P2 - 1)) >= (uint32_t)A) r16[e] = 0xFFFFu;
     for (int i = threadIdx.x; i < 2 * CT; i += 256) {
-        recs[i * RS] = 0u;
+        recs[i * RS + 2] = 0u;
         for (int b = 1; b < NB; ++b)
             if (8 * b >= A) recs[i * RS + 3 + b] = 0xFFFFu;
     }
@@ -300,18 +307,30 @@ __global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__
     uint32_t code = in.init(payload, off, len, (uint64_t)payload_bytes, ring);
     uint32_t range = 0xFFFFFFFFu;
     constexpr int ODT = (OUT & OUT_F16) ? ODT_F16 : (OUT & OUT_F32) ? ODT_F32 : -1;
-    constexpr int PER = 2;  // pairs staged per thread: CT * A / 2 / 256
+    constexpr int PER = DEC_MODE_PER(NSTEP);  // pairs staged per thread: CT * A / 2 / 256
     const float m = (ODT >= 0) ? kvc_h2f(max1[row]) : 0.0f;
     uint32_t bad = 0;
     uint8_t *so = (OUT & OUT_SYM) ? sym_out + row * C : nullptr;
     const uint16_t *srows = cdf + slab * C * A;
     const int ntiles = (C + CT - 1) / CT;
     const lds_u32 *rec = recs;
-    // one symbol of tile channel cl; lvb receives its dequantization value
-    auto decode1 = [&](int cl, uint32_t &lvb) -> uint32_t {
+    // the record of tile channel cl (a broadcast read: every lane the same
+    // address), loaded one symbol ahead of its use
+    struct Rec {
+        u32x4 a, b, c;
+    };
+    auto load_rec = [&](int cl) -> Rec {
         const lds_u32 *rc = rec + cl * RS;
-        const u32x4 ra = *(const lds_u32x4 *)rc;
-        const u32x4 rb = *(const lds_u32x4 *)(rc + 4);
+        Rec q;
+        q.a = *(const lds_u32x4 *)rc;
+        q.b = *(const lds_u32x4 *)(rc + 4);
+        if constexpr (NB >= 8) q.c = *(const lds_u32x4 *)(rc + 8);
+        return q;
+    };
+    // one symbol of tile channel cl with its record rq; lvb receives its
+    // dequantization value
+    auto decode1 = [&](int cl, const Rec &rq, uint32_t &lvb) -> uint32_t {
+        const u32x4 ra = rq.a, rb = rq.b;
         uint32_t hd[NB];
         hd[0] = 0u;
         if constexpr (NB >= 2) hd[1] = rb.x;
@@ -320,13 +339,12 @@ __global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__
             hd[3] = rb.z;
         }
         if constexpr (NB >= 8) {
-            const u32x4 rd = *(const lds_u32x4 *)(rc + 8);
             hd[4] = rb.w;
-            hd[5] = rd.x;
-            hd[6] = rd.y;
-            hd[7] = rd.z;
+            hd[5] = rq.c.x;
+            hd[6] = rq.c.y;
+            hd[7] = rq.c.z;
         }
-        const ModeRec mr{(uint32_t)__builtin_amdgcn_readfirstlane((int)ra.x), (int32_t)ra.y, ra.z, ra.w};
+        const ModeRec mr{ra.x, (int32_t)ra.y, ra.z, ra.w};
         const lds_u16 *rowp = r16 + cl * P2;
         auto piece = [&](uint32_t b) -> kvc_u32x4 { return *(const lds_u32x4 *)(rowp + 8u * b); };
         const lds_u32 *prow = pr + 2 * cl * A;  // uniform: the entry address is one shift-add of s
@@ -337,13 +355,18 @@ __global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__
     };
 
     PairTile<PER> pt;
-    uint32_t hw[16];
+    uint32_t hw[OB / 2];
     auto put_f16 = [&](int cb, int nb) {
         uint4 *o = (uint4 *)((uint16_t *)out + row * C + cb);
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi)
+        for (int gi = 0; gi < OB / 8; ++gi)
             if (gi * 8 < nb) o[gi] = make_uint4(hw[4 * gi], hw[4 * gi + 1], hw[4 * gi + 2], hw[4 * gi + 3]);
     };
+    // The fp16 output of a tile's last 32-channel block is stored after the
+    // next tile is staged: the staging waits for the next tile's CDF rows,
+    // and vector memory operations complete in order, so stores issued just
+    // before it would make every wave wait for their acknowledgement.
+    int pend_cb = 0, pend_nb = 0;
     pt.load(srows, 0, CT, C, A);
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
@@ -353,23 +376,30 @@ __global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__
                       RS);
         __syncthreads();
         rec = rnow;
+        if constexpr (VEC && ODT == ODT_F16) {
+            if (pend_nb) put_f16(pend_cb, pend_nb);
+            pend_nb = 0;
+        }
         if (it + 1 < ntiles) pt.load(srows, c0 + CT, CT, C, A);
         if (!active) continue;
         if constexpr (VEC) {
-            for (int cb = c0; cb < c1; cb += 32) {
-                const int nb = min(32, c1 - cb);  // 16 or 32
+            for (int cb = c0; cb < c1; cb += OB) {
+                const int nb = min(OB, c1 - cb);  // a multiple of 16
                 float fw[8];
 #pragma unroll
-                for (int gi = 0; gi < 4; ++gi) {
+                for (int gi = 0; gi < OB / 8; ++gi) {
                     if (gi * 8 >= nb) break;
                     const int cg = cb + gi * 8;
                     in.group();
                     uint32_t sw[2] = {0, 0};
                     float ylo = 0.0f;
+                    Rec rq = load_rec(cg - c0);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
+                        const Rec rn = load_rec(cg - c0 + (i < 7 ? i + 1 : i));
                         uint32_t lvb;
-                        const uint32_t s = decode1(cg - c0 + i, lvb);
+                        const uint32_t s = decode1(cg - c0 + i, rq, lvb);
+                        rq = rn;
                         sw[i >> 2] |= s << (8 * (i & 3));
                         if constexpr (ODT >= 0) {
                             const float y = __uint_as_float(lvb) * m;
@@ -390,13 +420,20 @@ __global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__
                         o[1] = make_float4(fw[4], fw[5], fw[6], fw[7]);
                     }
                 }
-                if constexpr (ODT == ODT_F16) put_f16(cb, nb);
+                if constexpr (ODT == ODT_F16) {
+                    if (cb + OB < c1) {
+                        put_f16(cb, nb);
+                    } else {
+                        pend_cb = cb;
+                        pend_nb = nb;
+                    }
+                }
             }
         } else {
             for (int c = c0; c < c1; ++c) {
                 if ((c & 7) == 0) in.group();
                 uint32_t lvb;
-                const uint32_t s = decode1(c - c0, lvb);
+                const uint32_t s = decode1(c - c0, load_rec(c - c0), lvb);
                 if constexpr ((OUT & OUT_SYM) != 0) so[c] = (uint8_t)s;
                 if constexpr (ODT >= 0) {
                     const float y = __uint_as_float(lvb) * m;
@@ -409,6 +446,9 @@ __global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__
         }
     }
 
+    if constexpr (VEC && ODT == ODT_F16) {
+        if (pend_nb) put_f16(pend_cb, pend_nb);
+    }
     if (active && bad) kvc_flag(status, KVC_DEV_CORRUPT);
 }
 
@@ -740,6 +780,15 @@ static size_t dec_lds_bytes(int A, int CT)
     return sizeof(uint32_t) * (256 + 256 * 17 + n16 + 2 * (size_t)CT * A);
 }
 
+// k_decode_mode's tile: as k_decode's, but at least its output block (64
+// channels for rows of up to 32 entries, whose fp16 outputs are stored as
+// whole 128-byte lines).
+static int dec_mode_tile_channels(int nstep)
+{
+    const int ct = 1024 >> nstep;
+    return DEC_MODE_OB(nstep) == 64 && ct < 64 ? 64 : ct;
+}
+
 // k_decode_mode: as dec_lds_bytes plus two buffers of CT records.
 static size_t dec_mode_lds_bytes(int A, int CT, int nstep)
 {
@@ -818,17 +867,23 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
     // the two-level search, measured faster than binary lifting at every
     // launch size since its searches run over registers); 4-entry and 128-
     // or 256-entry rows binary lifting.
-    const size_t lds_mode = dec_mode_lds_bytes(p.A, CT, nstep);
+    const int CT_mode = dec_mode_tile_channels(nstep);
+    const size_t lds_mode = dec_mode_lds_bytes(p.A, CT_mode, nstep);
+    // the staging covers DEC_MODE_PER(nstep) pairs per thread: never launch a
+    // tile it would stage only in part
+    if (nstep >= 3 && nstep <= 6 && CT_mode * (p.A / 2) > 256 * DEC_MODE_PER(nstep)) return hipErrorInvalidValue;
 #define KVC_DEC(V, O, N, B)                                                                          \
     hipLaunchKernelGGL((k_decode<V, O, N, B>), grid, block, lds, stream, payload, payload_bytes,     \
                        slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
 #define KVC_DECB(V, O, N)                                                                            \
     if (p.A == (1 << N))                                                                             \
-        hipLaunchKernelGGL((k_decode_mode<V, O, N, false>), grid, block, lds_mode, stream, payload,  \
-                           payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT); \
+        hipLaunchKernelGGL((k_decode_mode<V, O, N, false, DEC_MODE_OB(N)>), grid, block, lds_mode, stream, \
+                           payload, payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p,  \
+                           status, CT_mode);                                                          \
     else                                                                                             \
-        hipLaunchKernelGGL((k_decode_mode<V, O, N, true>), grid, block, lds_mode, stream, payload,   \
-                           payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
+        hipLaunchKernelGGL((k_decode_mode<V, O, N, true, DEC_MODE_OB(N)>), grid, block, lds_mode, stream, \
+                           payload, payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p,  \
+                           status, CT_mode)
 #define KVC_DEC_N(V, O)                                                                              \
     switch (nstep) {                                                                                 \
     case 2: KVC_DEC(V, O, 2, false); break;                                                          \

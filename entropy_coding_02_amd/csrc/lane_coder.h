@@ -279,7 +279,7 @@ KVC_HD uint32_t kvc_alignbit(uint32_t hi, uint32_t lo, uint32_t sh)
 KVC_HD bool kvc_all(bool c)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    return __all(c);
+    return __builtin_amdgcn_ballot_w64(c) == __builtin_amdgcn_read_exec();
 #else
     return c;
 #endif
@@ -634,7 +634,8 @@ KVC_HD uint32_t cdf_nstep(uint32_t A)
 // The ring holds 16 stream dwords per lane (dword j at slot j mod 16) and a
 // 17th slot with a copy of slot 0, so a window read at slot 15 needs no
 // wrap.  Feeding is RingIn's: a 16-byte piece (4 stream dwords) is fetched
-// one group of 8 symbols before it is committed.  At a group start, after
+// one group of 8 symbols before it is committed; pieces past the stream's
+// end are written as zeros without a load.  At a group start, after
 // the commit, w - posb/32 >= 6 holds: the group consumes at most 16 bytes
 // (4 dwords) and a window needs 2 dwords, and a piece is asked for whenever
 // w - posb/32 <= 10, so the next group starts with at least 6 again.  A
@@ -713,17 +714,33 @@ struct WinIn {
         commit();
         issue();
         commit();  // stream dwords 0..7 in the ring
-        issue();   // stream dwords 8..11 in flight
-        want = 1;
+        want = 4u * w < len ? 1u : 0u;
+        if (want) issue();  // stream dwords 8..11 in flight
+        else zeros();       // a stream of at most 32 bytes is all in the ring
         posb = 32;
         return ring[0];
     }
-    // Once per group of 8 symbols.
+    // Stream dwords w .. w+3 when all of them lie past the stream: zeros,
+    // written without a load.
+    KVC_HD void zeros()
+    {
+        const uint32_t b = w & 12u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ring[b + (uint32_t)k] = 0u;
+        if (b == 0u) ring[16] = 0u;
+        w += 4u;
+    }
+    // Once per group of 8 symbols.  Pieces wholly past the stream are not
+    // fetched: the ring gets zeros instead, so a lane whose stream is all in
+    // the ring issues no more loads (and waits for none), which is most lanes
+    // where a stream takes a few dozen bytes.
     KVC_HD void group()
     {
         if (want) commit();
-        want = w - (posb >> 5) <= 10u ? 1u : 0u;
+        const bool need = w - (posb >> 5) <= 10u;
+        want = need && 4u * w < len ? 1u : 0u;
         if (want) issue();
+        else if (need) zeros();
     }
     // The 32 stream bits from posb on.
     KVC_HD uint32_t window() const
@@ -767,14 +784,15 @@ KVC_HD uint32_t dec_step_win(uint32_t &code, uint32_t &range, In &in, uint32_t r
 // none.  Rows of chunks where a channel's symbol hardly varies (most rows of
 // the larger workloads) have one; for them every lane of a wave first tries
 // that symbol: one multiply-add and one multiply, and a check that every
-// lane's code lies in its interval with no renormalisation due.  Any other
-// case takes the exact search.
+// lane's code lies in its interval with no renormalisation due.  A row
+// without one has frequency 0 in its record, so the check fails for every
+// lane and the exact search runs (no separate branch on the kind).
 #define KVC_MODE_SPAN 1024u
 struct ModeRec {
-    uint32_t kind_md;  // 1 | md << 8 when the row has such a symbol md, else 0
-    int32_t nst;       // -(start of md)
-    uint32_t fr;       // frequency of md
-    uint32_t lv;       // dequantization value of md (fp32 bits)
+    uint32_t md;   // the symbol
+    int32_t nst;   // -(start of md)
+    uint32_t fr;   // frequency of md, or 0 when the row has no such symbol
+    uint32_t lv;   // dequantization value of md (fp32 bits)
 };
 
 // The two-level search of cdf_search_blocks with its NB block heads given
@@ -805,7 +823,7 @@ KVC_HD uint32_t dec_symbol_mode(uint32_t &code, uint32_t &range, In &in, const M
                                 uint32_t *bad, uint32_t *fast, uint32_t *lv)
 {
     const uint32_t r = range >> 16;
-    if (m.kind_md & 1u) {
+    {
         const uint32_t d = kvc_mad_nst(r, m.nst, code);
         const uint32_t rn = kvc_umul24(r, m.fr);
         if (kvc_all(d < rn && rn >= (1u << 24))) {
@@ -813,7 +831,7 @@ KVC_HD uint32_t dec_symbol_mode(uint32_t &code, uint32_t &range, In &in, const M
             range = rn;
             *fast = 1;
             *lv = m.lv;
-            return m.kind_md >> 8;
+            return m.md;
         }
     }
     *fast = 0;

@@ -58,10 +58,10 @@ struct PairTile {
     // (dwords 0-3), then the block heads row[8b], b >= 1, as dwords 3 + b.
     // A head is written by the thread holding entry 8b; the ModeRec only by
     // a thread holding an entry whose frequency exceeds 65536 - KVC_MODE_SPAN
-    // (a row has at most one), so a row without one keeps the zero kind word
-    // the staging of the tile before wrote: records alternate between two
-    // buffers, and each staging clears the kind words of the other one
-    // (rec_clear), which every wave finished reading before this staging.
+    // (a row has at most one), so a row without one keeps the zero frequency
+    // word the staging of the tile before wrote: records alternate between
+    // two buffers, and each staging clears the frequency words of the other
+    // one (rec_clear), which every wave finished reading before this staging.
     template <class D32, class D16, class LUT>
     __device__ void store_mode(D32 dst, int CT, int A, D16 dst16, int P2, const LUT &lut, D32 rec,
                                D32 rec_clear, int RS) const
@@ -79,12 +79,12 @@ struct PairTile {
                 *(lds_u32 *)(dst16 + cl * P2 + k) = (k == 0 ? 0u : st0) | (st1 << 16);
                 if ((k & 7) == 0 && k > 0) rec[cl * RS + 3 + (k >> 3)] = st0;
                 if ((p0 >> 16) > 65536u - KVC_MODE_SPAN)
-                    *(lds_u32x4 *)(rec + cl * RS) = u32x4{1u | ((uint32_t)k << 8), 0u - st0, p0 >> 16, l0};
+                    *(lds_u32x4 *)(rec + cl * RS) = u32x4{(uint32_t)k, 0u - st0, p0 >> 16, l0};
                 if ((p1 >> 16) > 65536u - KVC_MODE_SPAN)
-                    *(lds_u32x4 *)(rec + cl * RS) = u32x4{1u | ((uint32_t)(k + 1) << 8), 0u - st1, p1 >> 16, l1};
+                    *(lds_u32x4 *)(rec + cl * RS) = u32x4{(uint32_t)(k + 1), 0u - st1, p1 >> 16, l1};
             }
         }
-        if ((int)threadIdx.x < CT) rec_clear[(int)threadIdx.x * RS] = 0u;
+        if ((int)threadIdx.x < CT) rec_clear[(int)threadIdx.x * RS + 2] = 0u;
     }
     // The group decoder's form: row cl as P2 keys start << 16 | frequency (a
     // pair with its halves swapped, so that on a non-decreasing row the keys

@@ -118,7 +118,7 @@ int hostsim_decode_stream_n(const uint8_t *buf, int64_t cap, int64_t off, int64_
             for (int32_t k = 0; k < A; ++k) {
                 const uint32_t pr = pairs[k];
                 if ((pr >> 16) > 65536u - KVC_MODE_SPAN)
-                    m = ModeRec{1u | ((uint32_t)k << 8), -(int32_t)(pr & 0xFFFFu), pr >> 16, 0u};
+                    m = ModeRec{(uint32_t)k, -(int32_t)(pr & 0xFFFFu), pr >> 16, 0u};
             }
             uint32_t hd[8] = {0u};
             for (uint32_t b = 1; b < (P2 >> 3); ++b) hd[b] = padded[8 * b];

@@ -63,6 +63,12 @@ SMALL = {
     # few streams decode with a group of lanes per stream), rows of 8 and 16
     "one_lane_A8_C16_T9000": cfg_of(1, 16, 9000, 256, ((0, 1, 8),), seed=13),
     "one_lane_A16_C24_T9000": cfg_of(1, 24, 9000, 512, ((0, 1, 16),), seed=14),
+    # the mode-first decoder's tiles: 64-entry rows (16-channel tiles), padded
+    # 64-entry rows, 32-entry rows with a last tile of 8 channels (no 16-byte
+    # path), and near-constant channels that take its fast path
+    "one_lane_A64_C80_T9000": cfg_of(1, 80, 9000, 256, ((0, 1, 64),), seed=17, innov="t3", of=0.05, om=50),
+    "one_lane_A40_C96_T9000": cfg_of(1, 96, 9000, 256, ((0, 1, 40),), seed=18),
+    "one_lane_A32_C200_T9000": cfg_of(1, 200, 9000, 256, ((0, 1, 32),), seed=19, lo=0.05, hi=8.0, of=0.02, om=20),
 }
 
 
