@@ -27,13 +27,10 @@ constexpr int64_t KVC_DEC_GROUP_LANES = 4;
 
 // Record dwords per channel of k_decode_mode: ModeRec and the block heads.
 #define DEC_MODE_RS(NSTEP) ((NSTEP) <= 5 ? 8 : 12)
-// Output block of k_decode_mode (channels whose fp16 outputs are stored
-// together): 64 (a whole 128-byte line per lane) for rows of up to 32 entries.
-#define DEC_MODE_OB(NSTEP) ((NSTEP) <= 5 ? 64 : 32)
-// Pairs each thread stages per tile: the tile's CT * A / 2 over 256 threads
-// (CT = dec_mode_tile_channels: 64 channels up to rows of 32 entries, so at
-// most 4; 16 channels of 64-entry rows, 2).
-#define DEC_MODE_PER(NSTEP) ((NSTEP) <= 5 ? 4 : 2)
+// Pairs each thread stages per tile of k_decode_mode: the tile's CT * A / 2
+// pairs over 256 threads (CT = dec_mode_tile_channels: CT * P2 = 1024, and
+// 32 channels of 64-entry rows).
+#define DEC_MODE_PER(NSTEP) ((NSTEP) == 6 ? 4 : 2)
 
 namespace {
 
@@ -219,38 +216,46 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
 
 // Mode-first decoding, one lane per stream (256 tokens of one slab per
 // block), for rows of 8 to 64 entries.  Each tile's CDF rows are staged as
-// k_decode stages them, plus a record per channel (PairTile::store_mode): the
-// row's one symbol of frequency above 65536 - KVC_MODE_SPAN, if it has one,
-// with its start, frequency and dequantization value, and the row's block
-// heads.  All 64 lanes of a wave decode the same channel at each step, so
-// the record is one broadcast read.  When the row has such a symbol, every
-// lane first tries it: one multiply-add, one multiply and two compares, and
-// if all lanes land inside its interval with no renormalisation due, that is
-// the symbol (the row's only qualifying one on a non-decreasing row).  In
-// most chunks of long contexts most channels hardly vary, so most symbols
-// end there.  Otherwise the wave takes the exact two-level search with the
-// heads from the record.  Renormalisation takes its bits from a 32-bit window
-// at the stream's byte position (WinIn): no bit buffer to count or top up.
-// The output is k_decode's.
-template <bool VEC, int OUT, int NSTEP, bool PAD, int OB>
-__global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__ payload,
-                                                     int64_t payload_bytes,
-                                                     const uint64_t *__restrict__ slab_off,
-                                                     const uint16_t *__restrict__ stream_len,
-                                                     const uint16_t *__restrict__ cdf,
-                                                     const uint16_t *__restrict__ max1,
-                                                     uint8_t *__restrict__ sym_out, void *__restrict__ out,
-                                                     KParams p, int32_t *status, int CT)
+// (start, frequency) pairs and search rows, plus a record per channel
+// (PairTile::store_mode): the row's one symbol of frequency above
+// 65536 - KVC_MODE_SPAN, if it has one, with its start, frequency and
+// dequantization value, and the row's block heads.  All 64 lanes of a wave
+// decode the same channel at each step, so the record is one broadcast read.
+// Every lane first tries the record's symbol: one multiply-add, one multiply
+// and a compare, and if all lanes land inside its interval with no
+// renormalisation due, that is the symbol (the row's only qualifying one on a
+// non-decreasing row).  In most chunks of long contexts most channels hardly
+// vary, so most symbols end there.  Otherwise the wave takes the exact
+// two-level search with the heads from the record.  Renormalisation takes
+// its bits from a 32-bit window at the stream's byte position (WinIn): no bit
+// buffer to count or top up.
+//
+// Output: a lane writes its own token row.  The fp16 values of two 32-channel
+// halves are collected in registers (the older half moved down as the next
+// one starts) and stored as one 128-byte line, which keeps the HBM writes of
+// ~250K concurrently written rows efficient.  Vector memory operations
+// complete in order, so a load issued after a store cannot be waited for
+// before the store is acknowledged: each half's first byte-feed load is
+// issued before its stores, and the next tile's CDF rows are requested
+// before them as well.
+template <bool VEC, int OUT, int NSTEP, bool PAD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 ? 4 : 3))) void k_decode_mode(
+    const uint8_t *__restrict__ payload, int64_t payload_bytes, const uint64_t *__restrict__ slab_off,
+    const uint16_t *__restrict__ stream_len, const uint16_t *__restrict__ cdf,
+    const uint16_t *__restrict__ max1, uint8_t *__restrict__ sym_out, void *__restrict__ out, KParams p,
+    int32_t *status, int CT)
 {
     // LDS: lut[256] f32 | ring[256][17] u32 | rec[2][CT][RS] u32 | rows16 [CT][P2] u16 |
-    //      (pair, lut) [CT][A] u32x2
+    //      pairs [CT][A] u32
     extern __shared__ uint32_t lds[];
     __shared__ uint32_t s_red[4];
     constexpr uint32_t P2 = 1u << NSTEP;
     constexpr int NB = 1 << (NSTEP - 3);
     constexpr int RS = DEC_MODE_RS(NSTEP);
+    constexpr int PER = DEC_MODE_PER(NSTEP);  // pairs staged per thread: CT * A / 2 / 256
     const int C = p.C, A = p.A;
     float *lut = (float *)lds;
+    const lds_u32 *const lutw = (const lds_u32 *)lds;
     lds_u32 *const ring = (lds_u32 *)(lds + 256) + threadIdx.x * 17u;
     lds_u32 *const recs = (lds_u32 *)(lds + 256 + 256 * 17);
     lds_u32 *const tile = recs + 2 * CT * RS;
@@ -307,90 +312,90 @@ __global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__
     uint32_t code = in.init(payload, off, len, (uint64_t)payload_bytes, ring);
     uint32_t range = 0xFFFFFFFFu;
     constexpr int ODT = (OUT & OUT_F16) ? ODT_F16 : (OUT & OUT_F32) ? ODT_F32 : -1;
-    constexpr int PER = DEC_MODE_PER(NSTEP);  // pairs staged per thread: CT * A / 2 / 256
     const float m = (ODT >= 0) ? kvc_h2f(max1[row]) : 0.0f;
     uint32_t bad = 0;
     uint8_t *so = (OUT & OUT_SYM) ? sym_out + row * C : nullptr;
     const uint16_t *srows = cdf + slab * C * A;
     const int ntiles = (C + CT - 1) / CT;
     const lds_u32 *rec = recs;
-    // the record of tile channel cl (a broadcast read: every lane the same
-    // address), loaded one symbol ahead of its use
-    struct Rec {
-        u32x4 a, b, c;
-    };
-    auto load_rec = [&](int cl) -> Rec {
+    // the mode part of tile channel cl's record (a broadcast read: every lane
+    // the same address), loaded one symbol ahead of its use
+    using Rec = u32x4;
+    auto load_rec = [&](int cl) -> Rec { return *(const lds_u32x4 *)(rec + cl * RS); };
+    // one symbol of tile channel cl with its record's mode part ra; lvb
+    // receives its dequantization value
+    auto decode1 = [&](int cl, const Rec &ra, uint32_t &lvb) -> uint32_t {
         const lds_u32 *rc = rec + cl * RS;
-        Rec q;
-        q.a = *(const lds_u32x4 *)rc;
-        q.b = *(const lds_u32x4 *)(rc + 4);
-        if constexpr (NB >= 8) q.c = *(const lds_u32x4 *)(rc + 8);
-        return q;
-    };
-    // one symbol of tile channel cl with its record rq; lvb receives its
-    // dequantization value
-    auto decode1 = [&](int cl, const Rec &rq, uint32_t &lvb) -> uint32_t {
-        const u32x4 ra = rq.a, rb = rq.b;
-        uint32_t hd[NB];
-        hd[0] = 0u;
-        if constexpr (NB >= 2) hd[1] = rb.x;
-        if constexpr (NB >= 4) {
-            hd[2] = rb.y;
-            hd[3] = rb.z;
-        }
-        if constexpr (NB >= 8) {
-            hd[4] = rb.w;
-            hd[5] = rq.c.x;
-            hd[6] = rq.c.y;
-            hd[7] = rq.c.z;
-        }
+        auto heads = [&](uint32_t *hd) {  // the exact path's block heads
+            hd[0] = 0u;
+            if constexpr (NB >= 2) {
+                const u32x4 rb = *(const lds_u32x4 *)(rc + 4);
+                hd[1] = rb.x;
+                if constexpr (NB >= 4) {
+                    hd[2] = rb.y;
+                    hd[3] = rb.z;
+                }
+                if constexpr (NB >= 8) {
+                    const u32x4 rd = *(const lds_u32x4 *)(rc + 8);
+                    hd[4] = rb.w;
+                    hd[5] = rd.x;
+                    hd[6] = rd.y;
+                    hd[7] = rd.z;
+                }
+            }
+        };
         const ModeRec mr{ra.x, (int32_t)ra.y, ra.z, ra.w};
         const lds_u16 *rowp = r16 + cl * P2;
         auto piece = [&](uint32_t b) -> kvc_u32x4 { return *(const lds_u32x4 *)(rowp + 8u * b); };
-        const lds_u32 *prow = pr + 2 * cl * A;  // uniform: the entry address is one shift-add of s
-        auto ent = [&](uint32_t s) -> kvc_u32x2 { return *(const lds_u32x2 *)(prow + 2 * s); };
+        const lds_u32 *prow = pr + cl * A;  // uniform: the pair address is one shift-add of s
+        auto ent = [&](uint32_t s) -> kvc_u32x2 { return kvc_u32x2{prow[s], lutw[s]}; };
         uint32_t fast;
-        return dec_symbol_mode<NSTEP, PAD>(code, range, in, mr, hd, piece, ent, (uint32_t)A, &bad, &fast,
+        return dec_symbol_mode<NSTEP, PAD>(code, range, in, mr, heads, piece, ent, (uint32_t)A, &bad, &fast,
                                            &lvb);
     };
 
     PairTile<PER> pt;
-    uint32_t hw[OB / 2];
-    auto put_f16 = [&](int cb, int nb) {
-        uint4 *o = (uint4 *)((uint16_t *)out + row * C + cb);
+    // fp16 output: hw[0..15] the previous 32-channel half, hw[16..31] the
+    // current one; a 64-channel pair of halves goes out as one line per lane
+    uint32_t hw[32];
+    auto put_pair = [&](int cs, int nch) {  // channels [cs, cs + nch) from hw[0 ..]
+        uint4 *o = (uint4 *)((uint16_t *)out + row * C + cs);
 #pragma unroll
-        for (int gi = 0; gi < OB / 8; ++gi)
-            if (gi * 8 < nb) o[gi] = make_uint4(hw[4 * gi], hw[4 * gi + 1], hw[4 * gi + 2], hw[4 * gi + 3]);
+        for (int q = 0; q < 8; ++q)
+            if (q * 8 < nch) o[q] = make_uint4(hw[4 * q], hw[4 * q + 1], hw[4 * q + 2], hw[4 * q + 3]);
     };
-    // The fp16 output of a tile's last 32-channel block is stored after the
-    // next tile is staged: the staging waits for the next tile's CDF rows,
-    // and vector memory operations complete in order, so stores issued just
-    // before it would make every wave wait for their acknowledgement.
-    int pend_cb = 0, pend_nb = 0;
+    auto put_half = [&](int cs, int nch) {  // channels [cs, cs + nch) from hw[16 ..]
+        uint4 *o = (uint4 *)((uint16_t *)out + row * C + cs);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (q * 8 < nch) o[q] = make_uint4(hw[16 + 4 * q], hw[17 + 4 * q], hw[18 + 4 * q], hw[19 + 4 * q]);
+    };
     pt.load(srows, 0, CT, C, A);
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
         lds_u32 *const rnow = recs + (it & 1) * CT * RS;
         __syncthreads();  // all waves are done with the previous tile
-        pt.store_mode(pr, CT, A, r16, (int)P2, (const uint32_t *)lut, rnow, recs + ((it + 1) & 1) * CT * RS,
-                      RS);
+        pt.store_mode(pr, CT, A, r16, (int)P2, (const uint32_t *)lut, rnow, recs + ((it + 1) & 1) * CT * RS, RS);
         __syncthreads();
         rec = rnow;
-        if constexpr (VEC && ODT == ODT_F16) {
-            if (pend_nb) put_f16(pend_cb, pend_nb);
-            pend_nb = 0;
-        }
         if (it + 1 < ntiles) pt.load(srows, c0 + CT, CT, C, A);
         if (!active) continue;
         if constexpr (VEC) {
-            for (int cb = c0; cb < c1; cb += OB) {
-                const int nb = min(OB, c1 - cb);  // a multiple of 16
+            // halves of 32 channels (CT is a multiple of 32; C of 16)
+            for (int cb = c0; cb < c1; cb += 32) {
+                const int nb = min(32, c1 - cb);  // 16 or 32
+                in.group();                       // before the stores below
+                if constexpr (ODT == ODT_F16) {
+                    if ((cb & 63) == 0 && cb >= 64) put_pair(cb - 64, 64);
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) hw[q] = hw[16 + q];
+                }
                 float fw[8];
 #pragma unroll
-                for (int gi = 0; gi < OB / 8; ++gi) {
+                for (int gi = 0; gi < 4; ++gi) {
                     if (gi * 8 >= nb) break;
                     const int cg = cb + gi * 8;
-                    in.group();
+                    if (gi) in.group();
                     uint32_t sw[2] = {0, 0};
                     float ylo = 0.0f;
                     Rec rq = load_rec(cg - c0);
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__
                             const float y = __uint_as_float(lvb) * m;
                             if constexpr (ODT == ODT_F16) {
                                 if (i & 1)
-                                    hw[gi * 4 + (i >> 1)] = kvc_f2h2(ylo, y);
+                                    hw[16 + gi * 4 + (i >> 1)] = kvc_f2h2(ylo, y);
                                 else
                                     ylo = y;
                             } else {
@@ -418,14 +423,6 @@ __global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__
                         float4 *o = (float4 *)((float *)out + row * C + cg);
                         o[0] = make_float4(fw[0], fw[1], fw[2], fw[3]);
                         o[1] = make_float4(fw[4], fw[5], fw[6], fw[7]);
-                    }
-                }
-                if constexpr (ODT == ODT_F16) {
-                    if (cb + OB < c1) {
-                        put_f16(cb, nb);
-                    } else {
-                        pend_cb = cb;
-                        pend_nb = nb;
                     }
                 }
             }
@@ -445,9 +442,15 @@ __global__ __launch_bounds__(256) void k_decode_mode(const uint8_t *__restrict__
             }
         }
     }
-
+    // the row's last half or pair of halves
     if constexpr (VEC && ODT == ODT_F16) {
-        if (pend_nb) put_f16(pend_cb, pend_nb);
+        if (active && C > 0) {
+            const int hl = (C - 1) >> 5;  // index of the last half
+            if (hl & 1)
+                put_pair(32 * (hl - 1), C - 32 * (hl - 1));
+            else
+                put_half(32 * hl, C - 32 * hl);
+        }
     }
     if (active && bad) kvc_flag(status, KVC_DEV_CORRUPT);
 }
@@ -780,19 +783,21 @@ static size_t dec_lds_bytes(int A, int CT)
     return sizeof(uint32_t) * (256 + 256 * 17 + n16 + 2 * (size_t)CT * A);
 }
 
-// k_decode_mode's tile: as k_decode's, but at least its output block (64
-// channels for rows of up to 32 entries, whose fp16 outputs are stored as
-// whole 128-byte lines).
+// k_decode_mode's tile: as k_decode's (CT * P2 = 1024), but at least one
+// 32-channel half of its output.
 static int dec_mode_tile_channels(int nstep)
 {
     const int ct = 1024 >> nstep;
-    return DEC_MODE_OB(nstep) == 64 && ct < 64 ? 64 : ct;
+    return ct < 32 ? 32 : ct;
 }
 
-// k_decode_mode: as dec_lds_bytes plus two buffers of CT records.
+// k_decode_mode: the table, the rings, two buffers of CT records, the search
+// rows and the (start, frequency) pairs.
 static size_t dec_mode_lds_bytes(int A, int CT, int nstep)
 {
-    return dec_lds_bytes(A, CT) + sizeof(uint32_t) * 2 * (size_t)CT * DEC_MODE_RS(nstep);
+    const size_t P2 = (size_t)1 << nstep;
+    const size_t n16 = ((size_t)CT * P2 + 1) / 2;
+    return sizeof(uint32_t) * (256 + 256 * 17 + 2 * (size_t)CT * DEC_MODE_RS(nstep) + n16 + (size_t)CT * A);
 }
 
 int decode_lanes_per_stream(const KParams &p)
@@ -877,11 +882,11 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
                        slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
 #define KVC_DECB(V, O, N)                                                                            \
     if (p.A == (1 << N))                                                                             \
-        hipLaunchKernelGGL((k_decode_mode<V, O, N, false, DEC_MODE_OB(N)>), grid, block, lds_mode, stream, \
+        hipLaunchKernelGGL((k_decode_mode<V, O, N, false>), grid, block, lds_mode, stream, \
                            payload, payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p,  \
                            status, CT_mode);                                                          \
     else                                                                                             \
-        hipLaunchKernelGGL((k_decode_mode<V, O, N, true, DEC_MODE_OB(N)>), grid, block, lds_mode, stream, \
+        hipLaunchKernelGGL((k_decode_mode<V, O, N, true>), grid, block, lds_mode, stream, \
                            payload, payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p,  \
                            status, CT_mode)
 #define KVC_DEC_N(V, O)                                                                              \

@@ -813,13 +813,14 @@ KVC_HD uint32_t cdf_search_heads(const uint32_t *hd, const Piece &piece, uint32_
 
 // One symbol of the mode-first decoder: the mode record's symbol when every
 // lane lands in its interval without renormalising (*fast = 1), else the
-// exact two-level search (heads hd, pieces of the padded row); ent(s) gives
+// exact two-level search, with the block heads heads(hd) loads (only then:
+// the fast path needs none) and pieces of the padded row; ent(s) gives
 // symbol s's (start | frequency << 16) pair and its dequantization value
 // (fp32 bits), and *lv receives the chosen symbol's.  Returns the symbol;
 // *bad |= 1 when the stream left its interval.
-template <int NSTEP, bool PAD, class Piece, class Ent, class In>
+template <int NSTEP, bool PAD, class Heads, class Piece, class Ent, class In>
 KVC_HD uint32_t dec_symbol_mode(uint32_t &code, uint32_t &range, In &in, const ModeRec &m,
-                                const uint32_t *hd, const Piece &piece, const Ent &ent, uint32_t A,
+                                const Heads &heads, const Piece &piece, const Ent &ent, uint32_t A,
                                 uint32_t *bad, uint32_t *fast, uint32_t *lv)
 {
     const uint32_t r = range >> 16;
@@ -835,6 +836,9 @@ KVC_HD uint32_t dec_symbol_mode(uint32_t &code, uint32_t &range, In &in, const M
         }
     }
     *fast = 0;
+    constexpr int NB = 1 << (NSTEP - 3);
+    uint32_t hd[NB];
+    heads(hd);
     const uint32_t s = cdf_search_heads<NSTEP, PAD>(hd, piece, A, r, code);
     const kvc_u32x2 e = ent(s);
     *bad |= dec_step_win(code, range, in, r, e[0] & 0xFFFFu, e[0] >> 16);

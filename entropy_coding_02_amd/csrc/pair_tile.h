@@ -53,15 +53,18 @@ struct PairTile {
             }
         }
     }
-    // The mode-first decoder's form: store_with's (pair, lut) entries and
-    // search rows, plus a record of RS dwords per channel in rec: ModeRec
-    // (dwords 0-3), then the block heads row[8b], b >= 1, as dwords 3 + b.
-    // A head is written by the thread holding entry 8b; the ModeRec only by
-    // a thread holding an entry whose frequency exceeds 65536 - KVC_MODE_SPAN
-    // (a row has at most one), so a row without one keeps the zero frequency
-    // word the staging of the tile before wrote: records alternate between
-    // two buffers, and each staging clears the frequency words of the other
-    // one (rec_clear), which every wave finished reading before this staging.
+    // The mode-first decoder's form: the (start, frequency) pairs, entry k of
+    // row cl at dst[cl A + k] (its dequantization value is read from the
+    // slab's table), the starts as rows of P2 uint16 (the search; entry 0
+    // written as 0, as in store_with), and a record of RS dwords per channel
+    // in rec: ModeRec (dwords 0-3), then the block heads row[8b], b >= 1, as
+    // dwords 3 + b.  A head is written by the thread holding entry 8b; the
+    // ModeRec only by a thread holding an entry whose frequency exceeds
+    // 65536 - KVC_MODE_SPAN (a row has at most one), so a row without one
+    // keeps the zero frequency word the staging of the tile before wrote:
+    // records alternate between two buffers, and each staging clears the
+    // frequency words of the other one (rec_clear), which every wave finished
+    // reading before this staging.
     template <class D32, class D16, class LUT>
     __device__ void store_mode(D32 dst, int CT, int A, D16 dst16, int P2, const LUT &lut, D32 rec,
                                D32 rec_clear, int RS) const
@@ -74,14 +77,13 @@ struct PairTile {
                 const int cl = e / (A >> 1), k = (e - cl * (A >> 1)) * 2;
                 const uint32_t st0 = w[i] & 0xFFFFu, st1 = w[i] >> 16;
                 const uint32_t p0 = cdf_pair(st0, st1), p1 = cdf_pair(st1, n2[i]);
-                const uint32_t l0 = lut[k], l1 = lut[k + 1];
-                *(lds_u32x4 *)(dst + 4 * e) = u32x4{p0, l0, p1, l1};
+                *(lds_u32x2 *)(dst + 2 * e) = u32x2{p0, p1};
                 *(lds_u32 *)(dst16 + cl * P2 + k) = (k == 0 ? 0u : st0) | (st1 << 16);
                 if ((k & 7) == 0 && k > 0) rec[cl * RS + 3 + (k >> 3)] = st0;
                 if ((p0 >> 16) > 65536u - KVC_MODE_SPAN)
-                    *(lds_u32x4 *)(rec + cl * RS) = u32x4{(uint32_t)k, 0u - st0, p0 >> 16, l0};
+                    *(lds_u32x4 *)(rec + cl * RS) = u32x4{(uint32_t)k, 0u - st0, p0 >> 16, lut[k]};
                 if ((p1 >> 16) > 65536u - KVC_MODE_SPAN)
-                    *(lds_u32x4 *)(rec + cl * RS) = u32x4{(uint32_t)(k + 1), 0u - st1, p1 >> 16, l1};
+                    *(lds_u32x4 *)(rec + cl * RS) = u32x4{(uint32_t)(k + 1), 0u - st1, p1 >> 16, lut[k + 1]};
             }
         }
         if ((int)threadIdx.x < CT) rec_clear[(int)threadIdx.x * RS + 2] = 0u;

@@ -120,8 +120,10 @@ int hostsim_decode_stream_n(const uint8_t *buf, int64_t cap, int64_t off, int64_
                 if ((pr >> 16) > 65536u - KVC_MODE_SPAN)
                     m = ModeRec{(uint32_t)k, -(int32_t)(pr & 0xFFFFu), pr >> 16, 0u};
             }
-            uint32_t hd[8] = {0u};
-            for (uint32_t b = 1; b < (P2 >> 3); ++b) hd[b] = padded[8 * b];
+            auto hd = [&](uint32_t *h) {
+                h[0] = 0u;
+                for (uint32_t b = 1; b < (P2 >> 3); ++b) h[b] = padded[8 * b];
+            };
             uint32_t fast = 0;
             auto pa = [&](uint32_t k) { return kvc_u32x2{pairs[k], 0u}; };
             uint32_t lvv = 0;
