@@ -28,8 +28,9 @@ EXPORTED = (
     "kvc_quantize", "kvc_cdf", "kvc_encode", "kvc_decode", "kvc_dequantize",
     "kvc_container_bytes", "kvc_container_payload_offset", "kvc_serialize", "kvc_deserialize",
     "kvc_int8_quantize", "kvc_int8_dequantize", "kvc_serialize_chunk", "kvc_quantize_levels",
-    "kvc_decode_lanes", "kvc_delta_forward", "kvc_delta_inverse",
+    "kvc_decode_lanes", "kvc_delta_forward", "kvc_delta_inverse", "kvc_encode_noalloc",
 )
+KVC_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class KvcDesc(ctypes.Structure):
@@ -84,6 +85,8 @@ def _load():
         lib.kvc_cdf.argtypes = [D, P, P, P, P]
         lib.kvc_encode.restype = ctypes.c_int
         lib.kvc_encode.argtypes = [D, P, P, P, I64, P, P, P, I64, P, P]
+        lib.kvc_encode_noalloc.restype = ctypes.c_int
+        lib.kvc_encode_noalloc.argtypes = [D, P, P, P, P, P, I64, P, P]
         lib.kvc_decode.restype = ctypes.c_int
         lib.kvc_decode.argtypes = [D, P, I64, P, P, P, P, P, P, I32, P, P]
         lib.kvc_dequantize.restype = ctypes.c_int
@@ -217,6 +220,14 @@ def kvc_encode(desc: Desc, sym, cdf, scratch, stream_len, slab_off, payload, dev
     _check("kvc_encode", _load().kvc_encode(desc.ref, _ptr(sym), _ptr(cdf), _ptr(scratch), sb,
                                             _ptr(stream_len), _ptr(slab_off), _ptr(payload), pc,
                                             _ptr(dev_status), _stream(stream)))
+
+
+def kvc_encode_noalloc(desc: Desc, sym, cdf, stream_len, slab_off, payload, dev_status=None, stream=None,
+                       payload_cap=None):
+    pc = payload.numel() * payload.element_size() if payload_cap is None else payload_cap
+    _check("kvc_encode_noalloc", _load().kvc_encode_noalloc(desc.ref, _ptr(sym), _ptr(cdf), _ptr(stream_len),
+                                                            _ptr(slab_off), _ptr(payload), pc,
+                                                            _ptr(dev_status), _stream(stream)))
 
 
 def kvc_decode(desc: Desc, payload, slab_off, stream_len, cdf, max1=None, sym_out=None, out=None,

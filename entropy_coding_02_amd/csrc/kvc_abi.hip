@@ -2,8 +2,16 @@
 // the host, then asynchronous launches on the caller's stream.
 #include <string.h>
 
+#include <mutex>
+
 #include "kvc_common.h"
 #include "kvc_kernels.h"
+
+// Encoder workspace of kvc_encode_noalloc: one array per GPU the library runs
+// on, held until the process ends, shared by every call on that GPU.  In host
+// code its name is only a stand-in; its device address comes from
+// hipGetSymbolAddress (per device, kept in noalloc_base below).
+static __device__ __align__(256) uint8_t scratch[KVC_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -57,6 +65,25 @@ int make_geometry(const kvc_desc *d, Geometry &g)
 }
 
 bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+// Device address of `scratch` on the current device: looked up with
+// hipGetSymbolAddress on the first call on each device (with that device
+// current) and kept; NULL if the lookup fails.
+constexpr int kMaxDevices = 64;
+void *noalloc_base()
+{
+    static std::mutex mu;
+    static void *base[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!base[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        base[dev] = ptr;
+    }
+    return base[dev];
+}
 
 int launch_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
 
@@ -226,6 +253,20 @@ int kvc_encode(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf, vo
     const bool vec16 = (g.p.C % 16 == 0) && aligned(sym, 16);
     return launch_status(launch_encode(sym, cdf, slots, slab_total, stream_len, slab_off, payload,
                                        payload_cap, g.p, dev_status, vec16, s));
+}
+
+int kvc_encode_noalloc(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf,
+                       uint16_t *stream_len, uint64_t *slab_off, uint8_t *payload, int64_t payload_cap,
+                       int32_t *dev_status, void *stream)
+{
+    Geometry g;
+    int rc = make_geometry(desc, g);
+    if (rc != KVC_OK) return rc;
+    if (g.scratch > (int64_t)KVC_NOALLOC_SCRATCH_BYTES) return KVC_ERR_CAPACITY;
+    void *const base = noalloc_base();
+    if (!base) return KVC_ERR_HIP;
+    return kvc_encode(desc, sym, cdf, base, (int64_t)KVC_NOALLOC_SCRATCH_BYTES, stream_len, slab_off,
+                      payload, payload_cap, dev_status, stream);
 }
 
 int kvc_decode(const kvc_desc *desc, const uint8_t *payload, int64_t payload_bytes,

@@ -178,6 +178,24 @@ int kvc_encode(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf, vo
                int64_t payload_cap, int32_t *dev_status, void *stream);
 
 /*
+ * kvc_encode without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that forbid
+ * allocation).  Same arguments, outputs and flags as kvc_encode, minus
+ * scratch/scratch_bytes: the workspace is a device array inside the library,
+ * KVC_NOALLOC_SCRATCH_BYTES long, one per GPU (held until the process ends;
+ * its address is looked up on the first call on each device).  The call
+ * allocates nothing.  A shape whose kvc_scratch_bytes exceeds that size
+ * returns KVC_ERR_CAPACITY and launches nothing (e.g. one 256-token chunk of
+ * 32 layers x 1024 channels fits; 8K tokens do not).  Every call on a GPU
+ * uses that GPU's one array: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ */
+#define KVC_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kvc_encode_noalloc(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf,
+                       uint16_t *stream_len, uint64_t *slab_off, uint8_t *payload, int64_t payload_cap,
+                       int32_t *dev_status, void *stream);
+
+/*
  * Parallel decode with fused dequantization, [CG] 2.4 steps 1-2.
  * Per stream: code = first 4 bytes (big-endian), range = 2^32-1; per channel
  * r = range >> 16, s = the largest k with r*cdf_k <= code, code -= r*cdf_s,
