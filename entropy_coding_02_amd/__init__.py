@@ -106,7 +106,7 @@ def _load():
         lib.kvc_int8_quantize.restype = ctypes.c_int
         lib.kvc_int8_quantize.argtypes = [D, I32, P, P, P, P, P, P]
         lib.kvc_int8_dequantize.restype = ctypes.c_int
-        lib.kvc_int8_dequantize.argtypes = [D, I32, P, P, P, P, P]
+        lib.kvc_int8_dequantize.argtypes = [D, I32, P, P, P, P, I32, P]
         _lib = lib
     return _lib
 
@@ -275,9 +275,9 @@ def kvc_int8_quantize(desc: Desc, group: int, kv, q, scale, zero_point, dev_stat
                                                           _ptr(dev_status), _stream(stream)))
 
 
-def kvc_int8_dequantize(desc: Desc, group: int, q, scale, zero_point, out, stream=None):
+def kvc_int8_dequantize(desc: Desc, group: int, q, scale, zero_point, out, out_dtype=KVC_F16, stream=None):
     _check("kvc_int8_dequantize", _load().kvc_int8_dequantize(desc.ref, group, _ptr(q), _ptr(scale),
-                                                              _ptr(zero_point), _ptr(out),
+                                                              _ptr(zero_point), _ptr(out), out_dtype,
                                                               _stream(stream)))
 
 

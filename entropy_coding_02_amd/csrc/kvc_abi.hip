@@ -398,17 +398,17 @@ int kvc_int8_quantize(const kvc_desc *desc, int32_t group, const uint16_t *kv, u
 }
 
 int kvc_int8_dequantize(const kvc_desc *desc, int32_t group, const uint8_t *q, const float *scale,
-                        const uint8_t *zero_point, uint16_t *out, void *stream)
+                        const uint8_t *zero_point, void *out, int32_t out_dtype, void *stream)
 {
     Geometry g;
     int rc = make_geometry(desc, g);
     if (rc != KVC_OK) return rc;
-    if (group < 1 || g.p.C % group != 0) return KVC_ERR_ARG;
+    if (group < 1 || g.p.C % group != 0 || (out_dtype != KVC_F16 && out_dtype != KVC_F32)) return KVC_ERR_ARG;
     if (g.p.n_rows == 0) return KVC_OK;
     if (!q || !scale || !zero_point || !out || !aligned(scale, 4) || !aligned(out, 4))
         return KVC_ERR_ARG;
-    return launch_status(launch_int8_dequantize(q, scale, zero_point, out, g.p.n_rows * g.p.C, group,
-                                                (hipStream_t)stream));
+    return launch_status(launch_int8_dequantize(q, scale, zero_point, out, out_dtype == KVC_F32,
+                                                g.p.n_rows * g.p.C, group, (hipStream_t)stream));
 }
 
 int kvc_delta_forward(const kvc_desc *desc, int32_t anchor_tokens, const uint16_t *kv, uint16_t *delta,

@@ -5,11 +5,14 @@
 //
 // Anchors are the tokens at chunk-relative positions 0, G, 2G, ... (G =
 // anchor_tokens), so every chunk stands alone.  Forward: an anchor row is
-// kept; another row x becomes d = fp16(fp32(x) - fp32(xa_hat)), where xa_hat
-// is the codec's reconstruction of its anchor row (the group max-abs
+// kept; another row x becomes d = fp16(sat(fp32(x) - fp32(xa_hat))), where
+// xa_hat is the codec's reconstruction of its anchor row (the group max-abs
 // quantizer at the layer's bins, dequantized to fp16: the values a decoder
 // holds).  Inverse, on the decoded fp16 tensor y: every non-anchor row
-// becomes fp16(fp32(y) + fp32(y_anchor)).  Both are HBM-bound streaming
+// becomes fp16(sat(fp32(y) + fp32(y_anchor))).  sat() clamps to the finite
+// fp16 range [-65504, 65504] (a difference of two finite fp16 values can
+// reach twice that; the clamp is a coding error like any other), so only a
+// non-finite input raises KVC_DEV_NONFINITE.  Both are HBM-bound streaming
 // passes: one wave per anchor group, the anchor row (reconstructed once) in
 // registers.
 #include "kvc_common.h"
@@ -35,8 +38,14 @@ __device__ __forceinline__ uint32_t recon1(uint32_t bits, float factor, float M,
     return kvc_f2h(u * m);
 }
 
-__device__ __forceinline__ uint32_t dsub(uint32_t x, uint32_t a) { return kvc_f2h(kvc_h2f(x) - kvc_h2f(a)); }
-__device__ __forceinline__ uint32_t dadd(uint32_t y, uint32_t a) { return kvc_f2h(kvc_h2f(y) + kvc_h2f(a)); }
+__device__ __forceinline__ float dsat(float v) { return __builtin_fminf(__builtin_fmaxf(v, -65504.0f), 65504.0f); }
+__device__ __forceinline__ uint32_t dsub(uint32_t x, uint32_t a) { return kvc_f2h(dsat(kvc_h2f(x) - kvc_h2f(a))); }
+__device__ __forceinline__ uint32_t dadd(uint32_t y, uint32_t a) { return kvc_f2h(dsat(kvc_h2f(y) + kvc_h2f(a))); }
+// Inf or NaN in either half of a packed pair.
+__device__ __forceinline__ bool nonfinite2(uint32_t x)
+{
+    return (x & 0x7C00u) == 0x7C00u || (x & 0x7C000000u) == 0x7C000000u;
+}
 
 struct Groups {
     int64_t per_lk;  // groups per (layer, K|V)
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(256) void k_delta_fwd(const uint16_t *kv, uint16_t 
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t lo = dsub(x[i] & 0xFFFFu, ah[k][i] & 0xFFFFu);
                     const uint32_t hi = dsub(x[i] >> 16, ah[k][i] >> 16);
-                    bad |= (lo & 0x7C00u) == 0x7C00u || (hi & 0x7C00u) == 0x7C00u;
+                    bad |= nonfinite2(x[i]);
                     d[i] = lo | (hi << 16);
                 }
                 *(u32x4 *)(out + row * C + 8 * pi) = d;
@@ -208,9 +217,9 @@ __global__ __launch_bounds__(64) void k_delta_fwd_any(const uint16_t *kv, uint16
         for (int r = 1; r < nrows; ++r) {
             const int64_t row = row0 + r;
             for (int c = lane; c < C; c += 64) {
-                const uint32_t d = dsub(kv[row * C + c], xa[c]);
-                bad |= (d & 0x7C00u) == 0x7C00u;
-                out[row * C + c] = (uint16_t)d;
+                const uint32_t x = kv[row * C + c];
+                bad |= nonfinite2(x);
+                out[row * C + c] = (uint16_t)dsub(x, xa[c]);
             }
         }
         if (bad) kvc_flag(status, KVC_DEV_NONFINITE);

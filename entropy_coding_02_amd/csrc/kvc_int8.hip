@@ -107,26 +107,33 @@ __global__ __launch_bounds__(256) void k_int8_quant_groups(const uint16_t *__res
     }
 }
 
-// y = fp16((q - zero_point) * scale), one element per thread.
+// y = (q - zero_point) * scale, as fp32 (F32) or rounded to fp16, one
+// element per thread.
+template <bool F32>
 __global__ __launch_bounds__(256) void k_int8_dequant(const uint8_t *__restrict__ q,
                                                       const float *__restrict__ scale,
                                                       const uint8_t *__restrict__ zp,
-                                                      uint16_t *__restrict__ out, int64_t n_el, int g)
+                                                      void *__restrict__ out, int64_t n_el, int g)
 {
     const int64_t step = (int64_t)gridDim.x * blockDim.x;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n_el; e += step) {
         const int64_t gi = e / g;
         const float d = (float)((int32_t)q[e] - (int32_t)zp[gi]);
-        out[e] = (uint16_t)kvc_f2h(d * scale[gi]);
+        const float y = d * scale[gi];
+        if constexpr (F32)
+            ((float *)out)[e] = y;
+        else
+            ((uint16_t *)out)[e] = (uint16_t)kvc_f2h(y);
     }
 }
 
 // The same for g % 8 == 0 and aligned buffers: 8 elements (one group) per
-// thread, an 8-byte load and a 16-byte store.
+// thread, an 8-byte load and one 16-byte (fp16) or two (fp32) stores.
+template <bool F32>
 __global__ __launch_bounds__(256) void k_int8_dequant8(const uint8_t *__restrict__ q,
                                                        const float *__restrict__ scale,
                                                        const uint8_t *__restrict__ zp,
-                                                       uint16_t *__restrict__ out, int64_t n8, int g8)
+                                                       void *__restrict__ out, int64_t n8, int g8)
 {
     const int64_t step = (int64_t)gridDim.x * blockDim.x;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n8; e += step) {
@@ -134,16 +141,19 @@ __global__ __launch_bounds__(256) void k_int8_dequant8(const uint8_t *__restrict
         const uint2 v = ((const uint2 *)q)[e];
         const int32_t z = zp[gi];
         const float s = scale[gi];
-        uint32_t h[4];
+        float y[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t w = i < 2 ? v.x : v.y;
-            const int sh = 16 * (i & 1);
-            const float a = (float)((int32_t)((w >> sh) & 0xFFu) - z) * s;
-            const float b = (float)((int32_t)((w >> (sh + 8)) & 0xFFu) - z) * s;
-            h[i] = kvc_f2h2(a, b);
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t w = i < 4 ? v.x : v.y;
+            y[i] = (float)((int32_t)((w >> (8 * (i & 3))) & 0xFFu) - z) * s;
         }
-        ((uint4 *)out)[e] = make_uint4(h[0], h[1], h[2], h[3]);
+        if constexpr (F32) {
+            ((float4 *)out)[2 * e] = make_float4(y[0], y[1], y[2], y[3]);
+            ((float4 *)out)[2 * e + 1] = make_float4(y[4], y[5], y[6], y[7]);
+        } else {
+            ((uint4 *)out)[e] = make_uint4(kvc_f2h2(y[0], y[1]), kvc_f2h2(y[2], y[3]), kvc_f2h2(y[4], y[5]),
+                                           kvc_f2h2(y[6], y[7]));
+        }
     }
 }
 
@@ -181,17 +191,23 @@ hipError_t launch_int8_quantize(const uint16_t *kv, uint8_t *q, float *scale, ui
     return hipGetLastError();
 }
 
-hipError_t launch_int8_dequantize(const uint8_t *q, const float *scale, const uint8_t *zp,
-                                  uint16_t *out, int64_t n_el, int g, hipStream_t stream)
+hipError_t launch_int8_dequantize(const uint8_t *q, const float *scale, const uint8_t *zp, void *out,
+                                  bool f32, int64_t n_el, int g, hipStream_t stream)
 {
     if (n_el == 0) return hipSuccess;
     if (g % 8 == 0 && ((uintptr_t)q & 7) == 0 && ((uintptr_t)out & 15) == 0) {
         const int64_t n8 = n_el / 8;
-        hipLaunchKernelGGL(k_int8_dequant8, dim3(grid_cap((n8 + 255) / 256)), dim3(256), 0, stream, q,
-                           scale, zp, out, n8, g / 8);
+        const dim3 grid(grid_cap((n8 + 255) / 256)), block(256);
+        if (f32)
+            hipLaunchKernelGGL(k_int8_dequant8<true>, grid, block, 0, stream, q, scale, zp, out, n8, g / 8);
+        else
+            hipLaunchKernelGGL(k_int8_dequant8<false>, grid, block, 0, stream, q, scale, zp, out, n8, g / 8);
     } else {
-        hipLaunchKernelGGL(k_int8_dequant, dim3(grid_cap((n_el + 255) / 256)), dim3(256), 0, stream,
-                           q, scale, zp, out, n_el, g);
+        const dim3 grid(grid_cap((n_el + 255) / 256)), block(256);
+        if (f32)
+            hipLaunchKernelGGL(k_int8_dequant<true>, grid, block, 0, stream, q, scale, zp, out, n_el, g);
+        else
+            hipLaunchKernelGGL(k_int8_dequant<false>, grid, block, 0, stream, q, scale, zp, out, n_el, g);
     }
     return hipGetLastError();
 }

@@ -89,5 +89,5 @@ hipError_t launch_delta_inverse(uint16_t *y, const KParams &p, int G, bool vec, 
 hipError_t launch_int8_quantize(const uint16_t *kv, uint8_t *q, float *scale, uint8_t *zp,
                                 int64_t n_rows, int C, int g, bool vec, int32_t *status,
                                 hipStream_t stream);
-hipError_t launch_int8_dequantize(const uint8_t *q, const float *scale, const uint8_t *zp,
-                                  uint16_t *out, int64_t n_el, int g, hipStream_t stream);
+hipError_t launch_int8_dequantize(const uint8_t *q, const float *scale, const uint8_t *zp, void *out,
+                                  bool f32, int64_t n_el, int g, hipStream_t stream);

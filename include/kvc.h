@@ -310,16 +310,19 @@ int kvc_deserialize(const kvc_desc *desc, const uint8_t *in, int64_t in_bytes, u
  * anchor-based form).  Anchors are the tokens at chunk-relative positions 0,
  * G, 2G, ... (G = anchor_tokens, 1..65535; every chunk stands alone).
  *   kvc_delta_forward: an anchor row is kept; any other row x becomes
- *     fp16(fp32(x) - fp32(xa_hat)), xa_hat = the codec's reconstruction of its
+ *     fp16(sat(fp32(x) - fp32(xa_hat))), xa_hat = the codec's reconstruction of its
  *     anchor row (desc's bins: max-abs quantization, then fp16(fp32(q - MAX) /
  *     MAX * max1), as kvc_decode writes it).  The result goes through
  *     kvc_quantize / kvc_encode unchanged.
  *   kvc_delta_inverse: on the tensor kvc_decode wrote (fp16), every
- *     non-anchor row y becomes fp16(fp32(y) + fp32(y_anchor)), in place.
+ *     non-anchor row y becomes fp16(sat(fp32(y) + fp32(y_anchor))), in place.
+ *   sat() clamps to [-65504, 65504]: a delta between two finite fp16 values can
+ *     pass the fp16 range, and is then coded as +-65504 (an error of at most
+ *     |delta| - 65504 on that element, counted like any coding error).
  *   kv, delta, y  [L][2][T][C] fp16 (device); kv and delta may be the same
  *                 buffer (else they must not overlap)
- * A row holding Inf or NaN, or a delta past the fp16 range, sets
- * KVC_DEV_NONFINITE (kvc_delta_forward); such outputs are unspecified.
+ * A row holding Inf or NaN sets KVC_DEV_NONFINITE (kvc_delta_forward); such
+ * outputs are unspecified.
  */
 int kvc_delta_forward(const kvc_desc *desc, int32_t anchor_tokens, const uint16_t *kv, uint16_t *delta,
                       int32_t *dev_status, void *stream);
@@ -333,7 +336,9 @@ int kvc_delta_inverse(const kvc_desc *desc, int32_t anchor_tokens, uint16_t *y, 
  * `group` contiguous channels of a row (head_dim; it must divide C), in fp32
  * with every operation rounded on its own and round half to even:
  *   scale = (max - min) / 255,  zero_point = clamp(round(-min / scale), 0, 255),
- *   q = clamp(round((x - min) / scale), 0, 255),  y = fp16((q - zero_point) * scale).
+ *   q = clamp(round((x - min) / scale), 0, 255),  y = (q - zero_point) * scale,
+ * y written as fp32 (the page's dequantizer returns float32) or rounded to
+ * fp16 (out_dtype; where |y| passes 65504 the fp16 value is Inf).
  * A constant group stores q = 0, zero_point = 0 (the printed formula divides 0
  * by 0 there) and decodes to 0.  desc->bins and chunk_tokens are not used
  * (but must be valid).
@@ -341,13 +346,13 @@ int kvc_delta_inverse(const kvc_desc *desc, int32_t anchor_tokens, uint16_t *y, 
  *   q           [L][2][T][C] uint8 (device, written)
  *   scale       [L][2][T][C/group] fp32 (device, written)
  *   zero_point  [L][2][T][C/group] uint8 (device, written)
- *   out         [L][2][T][C] fp16 (device, written)
+ *   out         [L][2][T][C] of out_dtype (device, written)
  * Inf or NaN in a group sets KVC_DEV_NONFINITE; that group's outputs are unspecified.
  */
 int kvc_int8_quantize(const kvc_desc *desc, int32_t group, const uint16_t *kv, uint8_t *q,
                       float *scale, uint8_t *zero_point, int32_t *dev_status, void *stream);
 int kvc_int8_dequantize(const kvc_desc *desc, int32_t group, const uint8_t *q, const float *scale,
-                        const uint8_t *zero_point, uint16_t *out, void *stream);
+                        const uint8_t *zero_point, void *out, int32_t out_dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -75,7 +75,7 @@ def _load():
         lib.orc_int8_quantize.restype = ctypes.c_int
         lib.orc_int8_quantize.argtypes = [I32, I32, I64, I32, P, P, P, P]
         lib.orc_int8_dequantize.restype = ctypes.c_int
-        lib.orc_int8_dequantize.argtypes = [I32, I32, I64, I32, P, P, P, P]
+        lib.orc_int8_dequantize.argtypes = [I32, I32, I64, I32, P, P, P, P, I32]
         _lib = lib
     return _lib
 
@@ -295,13 +295,13 @@ def int8_quantize(kv: np.ndarray, g: int):
     return q, scale, zp
 
 
-def int8_dequantize(q: np.ndarray, scale: np.ndarray, zp: np.ndarray, g: int) -> np.ndarray:
-    """-> fp16 bits (u16) [L][2][T][C]."""
+def int8_dequantize(q: np.ndarray, scale: np.ndarray, zp: np.ndarray, g: int, fp32: bool = False) -> np.ndarray:
+    """-> fp16 bits (u16) [L][2][T][C], or float32 when fp32."""
     L, _, T, C = q.shape
-    out = np.empty(q.shape, dtype=np.uint16)
+    out = np.empty(q.shape, dtype=np.float32 if fp32 else np.uint16)
     rc = _load().orc_int8_dequantize(L, C, T, g, _ptr(np.ascontiguousarray(q)),
                                      _ptr(np.ascontiguousarray(scale, dtype=np.float32)),
-                                     _ptr(np.ascontiguousarray(zp)), _ptr(out))
+                                     _ptr(np.ascontiguousarray(zp)), _ptr(out), 1 if fp32 else 0)
     if rc != ORC_OK:
         raise OracleError("orc_int8_dequantize", rc)
     return out

@@ -17,10 +17,14 @@
  *     values a decoder holds, so an anchor's error does not carry into its
  *     tokens;
  *   - forward: an anchor row is kept; any other row becomes
- *       d = fp16(fp32(x) - fp32(xa_hat))     (fp32 subtraction, then fp16)
+ *       d = fp16(sat(fp32(x) - fp32(xa_hat)))  (fp32 subtraction, then fp16)
  *     and the delta tensor goes through the unchanged codec;
  *   - inverse, on the decoded fp16 tensor y (whose anchor rows are xa_hat):
- *       x_hat = fp16(fp32(y) + fp32(y_anchor)) for every non-anchor row.
+ *       x_hat = fp16(sat(fp32(y) + fp32(y_anchor))) for every non-anchor row;
+ *   - sat() clamps to [-65504, 65504], the finite fp16 range: a delta of two
+ *     finite fp16 values can reach twice that, and a clamped delta is a
+ *     coding error like any other (the inverse then lands at most
+ *     |delta| - 65504 away); only a non-finite input is an error.
  */
 #include <math.h>
 #include <stdint.h>
@@ -28,6 +32,8 @@
 #include <string.h>
 
 #include "kvc_oracle.h"
+
+static float sat(float v) { return v > 65504.0f ? 65504.0f : (v < -65504.0f ? -65504.0f : v); }
 
 static int64_t anchor_of(int64_t t, int32_t Tc, int32_t G)
 {
@@ -78,12 +84,12 @@ int orc_delta_forward(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t G, co
                     continue;
                 }
                 for (int32_t c = 0; c < C; ++c) {
-                    float diff = orc_half_to_float(x[c]) - orc_half_to_float(xa[c]);
-                    d[c] = orc_float_to_half(diff);
-                    if ((d[c] & 0x7C00u) == 0x7C00u) { /* Inf/NaN input, or a delta past fp16 */
+                    const float xv = orc_half_to_float(x[c]);
+                    if (!isfinite(xv)) {
                         rc = ORC_ERR_NONFINITE;
                         break;
                     }
+                    d[c] = orc_float_to_half(sat(xv - orc_half_to_float(xa[c])));
                 }
                 if (rc != ORC_OK) break;
             }
@@ -104,7 +110,7 @@ int orc_delta_inverse(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t G, ui
             const uint16_t *ya = y + (base + a) * C; /* anchors are never rewritten */
             uint16_t *yt = y + (base + t) * C;
             for (int32_t c = 0; c < C; ++c)
-                yt[c] = orc_float_to_half(orc_half_to_float(yt[c]) + orc_half_to_float(ya[c]));
+                yt[c] = orc_float_to_half(sat(orc_half_to_float(yt[c]) + orc_half_to_float(ya[c])));
         }
     }
     return ORC_OK;

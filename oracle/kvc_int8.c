@@ -17,7 +17,11 @@
  *   scale      = (mx - mn) / 255
  *   zero_point = clamp(round(-mn / scale), 0, 255)          (u8)
  *   q          = clamp(round((x - mn) / scale), 0, 255)     (u8)
- *   y          = (q - zero_point) * scale, rounded to fp16
+ *   y          = (q - zero_point) * scale
+ * The page's dequantizer returns that product as float32 (it converts q and
+ * the zero point with .float() and multiplies by the float scale), so fp32 is
+ * the output that follows it; an fp16 output is the fp32 value rounded to
+ * nearest even (and overflows to Inf where |y| passes 65504).
  * A constant group has scale 0, where the printed formula divides 0 by 0:
  * here it stores q = 0, zero_point = 0 and decodes to 0.
  */
@@ -67,7 +71,7 @@ int orc_int8_quantize(int32_t L, int32_t C, int64_t T, int32_t g, const uint16_t
 }
 
 int orc_int8_dequantize(int32_t L, int32_t C, int64_t T, int32_t g, const uint8_t *q,
-                        const float *scale, const uint8_t *zp, uint16_t *out)
+                        const float *scale, const uint8_t *zp, void *out, int32_t out_fp32)
 {
     if (L < 1 || C < 1 || T < 0 || g < 1 || C % g != 0) return ORC_ERR_ARG;
     const int64_t n_rows = 2 * (int64_t)L * T;
@@ -77,7 +81,10 @@ int orc_int8_dequantize(int32_t L, int32_t C, int64_t T, int32_t g, const uint8_
             const int64_t gi = row * G + c / g;
             const float d = (float)((int32_t)q[row * C + c] - (int32_t)zp[gi]);
             const float y = d * scale[gi];
-            out[row * C + c] = orc_float_to_half(y);
+            if (out_fp32)
+                ((float *)out)[row * C + c] = y;
+            else
+                ((uint16_t *)out)[row * C + c] = orc_float_to_half(y);
         }
     }
     return ORC_OK;

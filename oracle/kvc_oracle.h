@@ -73,7 +73,7 @@ int orc_delta_inverse(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t G, ui
 int orc_int8_quantize(int32_t L, int32_t C, int64_t T, int32_t g, const uint16_t *kv, uint8_t *q,
                       float *scale, uint8_t *zp);
 int orc_int8_dequantize(int32_t L, int32_t C, int64_t T, int32_t g, const uint8_t *q,
-                        const float *scale, const uint8_t *zp, uint16_t *out);
+                        const float *scale, const uint8_t *zp, void *out, int32_t out_fp32);
 
 #ifdef __cplusplus
 }

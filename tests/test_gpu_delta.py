@@ -85,15 +85,35 @@ def test_whole_chain_through_the_codec():
 
 
 @pytest.mark.parametrize("C", [8, 12])
-def test_overflow_flagged(C):
+def test_saturation_and_nonfinite(C):
+    """Deltas past the fp16 range saturate (bit-exact against the oracle, status
+    clear), on both kernel paths (C = 8: 16-byte rows; C = 12: a thread per
+    element); the inverse saturates its sums; Inf in a delta row is flagged."""
     import torch
+    from test_oracle_delta import saturation_example
+    say(f"[gpu] delta saturation C={C}")
+    base, bins = saturation_example()
     kv = np.zeros((1, 2, 2, C), np.uint16)
-    kv[0, 0, 0, 0] = np.float16(-65504.0).view(np.uint16)
-    kv[0, 0, 1, 0] = np.float16(65504.0).view(np.uint16)
-    d = kvc.Desc(1, C, 2, np.array([[6, 6]], np.int32), 2)
+    kv[..., :4] = base
+    kv[..., 4:8] = base[..., ::-1]
+    d = kvc.Desc(1, C, 2, bins, 2)
+    want = oracle.delta_forward(kv, bins, 2, 2)
     x = _dev(kv)
+    out = torch.empty_like(x)
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
-    kvc.kvc_delta_forward(d, 2, x, torch.empty_like(x), st)
+    kvc.kvc_delta_forward(d, 2, x, out, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), want)
+    z = np.zeros((1, 2, 2, C), np.uint16)
+    z[0, :, 0, :4] = np.array([65504.0, -65504.0, 65504.0, 1.0], np.float16).view(np.uint16)
+    z[0, :, 1, :4] = np.array([32.0, -32.0, -1.0, 1.0], np.float16).view(np.uint16)
+    y = _dev(z)
+    kvc.kvc_delta_inverse(d, 2, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), oracle.delta_inverse(z, 2, 2))
+    kv[0, 1, 1, C - 1] = np.float16(np.inf).view(np.uint16)
+    kvc.kvc_delta_forward(d, 2, _dev(kv), out, st)
     torch.cuda.synchronize()
     assert int(st.item()) & kvc.KVC_DEV_NONFINITE
 

@@ -39,26 +39,30 @@ def _run(kv_np, g):
     sc = torch.empty(max(n_g, 1), dtype=torch.float32, device="cuda")
     zp = torch.empty(max(n_g, 1), dtype=torch.uint8, device="cuda")
     out = torch.empty(max(n_el, 1), dtype=torch.int16, device="cuda")
+    out32 = torch.empty(max(n_el, 1), dtype=torch.float32, device="cuda")
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
     kvc.kvc_int8_quantize(d, g, kv, q, sc, zp, st)
     kvc.kvc_int8_dequantize(d, g, q, sc, zp, out)
+    kvc.kvc_int8_dequantize(d, g, q, sc, zp, out32, kvc.KVC_F32)
     torch.cuda.synchronize()
     return (q[:n_el].cpu().numpy().reshape(L, 2, T, C), sc[:n_g].cpu().numpy().reshape(L, 2, T, C // g),
             zp[:n_g].cpu().numpy().reshape(L, 2, T, C // g),
-            out[:n_el].cpu().numpy().view(np.uint16).reshape(L, 2, T, C), int(st.item()))
+            out[:n_el].cpu().numpy().view(np.uint16).reshape(L, 2, T, C), int(st.item()),
+            out32[:n_el].cpu().numpy().reshape(L, 2, T, C))
 
 
 @pytest.mark.parametrize("name,cfg,g", CASES, ids=[c[0] for c in CASES])
 def test_int8_bit_exact(name, cfg, g):
     say(f"[gpu] int8 {name}")
     kv_np, _ = kvgen.generate(cfg)
-    q, sc, zp, out, st = _run(kv_np, g)
+    q, sc, zp, out, st, out32 = _run(kv_np, g)
     oq, osc, ozp = oracle.int8_quantize(kv_np, g)
     assert st == 0
     assert np.array_equal(q, oq)
     assert np.array_equal(sc.view(np.uint32), osc.view(np.uint32))
     assert np.array_equal(zp, ozp)
     assert np.array_equal(out, oracle.int8_dequantize(oq, osc, ozp, g))
+    assert np.array_equal(out32.view(np.uint32), oracle.int8_dequantize(oq, osc, ozp, g, fp32=True).view(np.uint32))
 
 
 @pytest.mark.parametrize("g", [16, 12])
@@ -72,17 +76,20 @@ def test_int8_edge_values(g):
     kv[1, 0, 5, :g] = -0.0       # one negative-zero group
     kv[1, 1, 7, :g] = [65504.0, -65504.0] * (g // 2)
     kv_np = kv.view(np.uint16)
-    q, sc, zp, out, st = _run(kv_np, g)
+    q, sc, zp, out, st, out32 = _run(kv_np, g)
     oq, osc, ozp = oracle.int8_quantize(kv_np, g)
     assert st == 0
     assert np.array_equal(q, oq) and np.array_equal(zp, ozp)
     assert np.array_equal(sc.view(np.uint32), osc.view(np.uint32))
     assert np.array_equal(out, oracle.int8_dequantize(oq, osc, ozp, g))
+    want32 = oracle.int8_dequantize(oq, osc, ozp, g, fp32=True)
+    assert np.array_equal(out32.view(np.uint32), want32.view(np.uint32))
+    assert np.isfinite(out32).all()  # the +-65504 group: finite in fp32
 
 
 def test_int8_nonfinite_flagged():
     kv = np.zeros((1, 2, 4, 64), np.uint16)
     kv[0, 1, 2, 17] = 0x7E00  # NaN
     for g in (16, 64):
-        *_, st = _run(kv, g)
+        *_, st, _ = _run(kv, g)
         assert st & kvc.KVC_DEV_NONFINITE

@@ -113,12 +113,47 @@ def test_codec_error_is_the_delta_step_only(G):
         assert np.mean((y - x)[:, :, na] ** 2) < 0.5 * np.mean((plain - x)[:, :, na] ** 2)
 
 
-def test_rejects_bad_arguments_and_overflow():
+def test_rejects_bad_arguments_and_nonfinite():
     kv, bins = _hand_example()
     with pytest.raises(oracle.OracleError):
         oracle.delta_forward(kv, bins, 5, 0)
-    big = np.zeros((1, 2, 2, 4), np.uint16)
-    big[0, 0, 0] = f16([-65504.0, 0, 0, 0])  # anchor, on the grid (its own max)
-    big[0, 0, 1] = f16([65504.0, 0, 0, 0])   # delta 131008: past fp16
-    with pytest.raises(oracle.OracleError):
-        oracle.delta_forward(big, np.array([[6, 6]], np.int32), 2, 2)
+    for t in (0, 1):  # Inf in an anchor row, then in a delta row
+        bad = np.zeros((1, 2, 2, 4), np.uint16)
+        bad[0, 1, t, 2] = f16([np.inf])[0]
+        with pytest.raises(oracle.OracleError):
+            oracle.delta_forward(bad, np.array([[6, 6]], np.int32), 2, 2)
+
+
+def saturation_example():
+    """L = 1, T = 2, C = 4, G = 2, bins 6 (MAX = 2): the anchor row
+    [-65504, 65504, 0, 32752] is on the quantizer grid (max1 = 65504, codes
+    0, 4, 2, 3), so its reconstruction is itself; the token row
+    [16, -16, 0, -32752] has differences 65520, -65520, 0, -65504, whose
+    fp16 roundings without the clamp would be +Inf, -Inf (65520 is half way to
+    the next power of two and rounds up), and which saturate to +-65504."""
+    kv = np.zeros((1, 2, 2, 4), np.uint16)
+    kv[0, 0, 0] = f16([-65504.0, 65504.0, 0.0, 32752.0])
+    kv[0, 0, 1] = f16([16.0, -16.0, 0.0, -32752.0])
+    kv[0, 1, 0] = f16([1.0, 2.0, 3.0, 4.0])
+    kv[0, 1, 1] = f16([1.0, 2.0, 3.0, 4.0])
+    return kv, np.array([[6, 6]], np.int32)
+
+
+def test_saturating_delta_pin():
+    kv, bins = saturation_example()
+    d = oracle.delta_forward(kv, bins, 2, 2)
+    assert np.array_equal(d[0, 0, 0], kv[0, 0, 0])
+    assert np.array_equal(d[0, 0, 1], f16([65504.0, -65504.0, 0.0, -65504.0]))
+    # the V half: anchor [1, 2, 3, 4] at max1 4, codes rint(x / 2 + 2) -> [2, 3, 4, 4]
+    # (2.5 rounds to even), reconstruction [0, 2, 4, 4], so the deltas are [1, 0, -1, 0]
+    assert np.array_equal(d[0, 1, 1], f16([1.0, 0.0, -1.0, 0.0]))
+    # the inverse on these deltas taken as decoded: anchor + clamped delta; the first two
+    # elements come back 16 away from the input (the clamp's error), the last exactly
+    y = oracle.delta_inverse(d, 2, 2)
+    assert np.array_equal(y[0, 0, 1], f16([0.0, 0.0, 0.0, -32752.0]))
+    # a sum past the fp16 range saturates too: 65504 + 32 would round to Inf
+    z = np.zeros((1, 2, 2, 4), np.uint16)
+    z[0, 0, 0] = f16([65504.0, -65504.0, 65504.0, 1.0])
+    z[0, 0, 1] = f16([32.0, -32.0, -1.0, 1.0])
+    w = oracle.delta_inverse(z, 2, 2)
+    assert np.array_equal(w[0, 0, 1], f16([65504.0, -65504.0, 65504.0, 2.0]))

@@ -1,7 +1,8 @@
 """Pins of the oracle's 8-bit comparator quantizer (oracle/kvc_int8.c):
 exact rational values of the printed formulas away from rounding ties, the
 special points (group min and max, clamped zero points, constant groups),
-the reconstruction error bound, and exact dequantized values."""
+the reconstruction error bound, exact dequantized values, and the page's
+own dequantize expression evaluated by torch in float32 (bit for bit)."""
 from fractions import Fraction
 
 import numpy as np
@@ -117,3 +118,29 @@ def test_exact_ties_round_to_even():
     assert scale[0, 0, 0, 0] == np.float32(s)
     assert zp[0, 0, 0, 0] == 2  # 2.5 -> 2
     assert q[0, 0, 0, :8].tolist() == [0, 255, 0, 2, 16, 2, 3, 254]  # 0.5->0, 2.5->2, 16.5->16, 1.5->2, 254.5->254
+
+
+def test_dequantize_page_code_pin_fp32():
+    """The page's dequantize_key ([KVM] 四): q and the zero point converted
+    with .float(), subtracted, times the float scale.  Evaluated by torch on
+    CPU float32 tensors it must equal the oracle's fp32 output bit for bit;
+    the fp16 output is that value rounded to nearest even.  Includes groups
+    spanning +-65504 (the 70B workload's saturated channels), where the fp32
+    result stays finite and the fp16 one overflows."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    g = 16
+    groups = [rng.standard_normal(g) * rng.uniform(0.01, 3000) for _ in range(300)]
+    groups += [[65504.0, -65504.0] * (g // 2), [65504.0] + [-3.0] * (g - 1)]
+    kv, _ = _as_kv(groups, g)
+    q, scale, zp = oracle.int8_quantize(kv, g)
+    y32 = oracle.int8_dequantize(q, scale, zp, g, fp32=True)
+    y16 = oracle.int8_dequantize(q, scale, zp, g)
+    qt = torch.from_numpy(q.astype(np.uint8))
+    zt = torch.from_numpy(np.repeat(zp, g, axis=-1).astype(np.uint8))
+    st = torch.from_numpy(np.repeat(scale, g, axis=-1))
+    page = (qt.float() - zt.float()) * st
+    assert page.dtype == torch.float32
+    assert np.array_equal(page.numpy().view(np.uint32), y32.view(np.uint32))
+    assert np.array_equal(page.half().numpy().view(np.uint16), y16)
+    assert np.isfinite(y32).all() and not np.isfinite(y16.view(np.float16)).all()
