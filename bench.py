@@ -254,7 +254,7 @@ def levels_leg(kvc, cfg, kvt, stream, steps):
         one.append(e[0].elapsed_time(e[1]))
         sep.append(e[1].elapsed_time(e[2]))
     x = kvt.view(torch.float16).reshape(-1)
-    out = []
+    out, level_bytes = [], []
     for t, d, b in zip(tables, descs, bufs):
         kvc.kvc_encode(d, b.sym, b.cdf, b.scratch, b.stream_len, b.slab_off, b.payload, b.dev_status,
                        stream)
@@ -262,11 +262,67 @@ def levels_leg(kvc, cfg, kvt, stream, steps):
         torch.cuda.synchronize()
         assert int(b.dev_status.item()) == 0, "device status flags set in the levels leg"
         n = d.container_bytes(int(b.slab_off[d.n_slabs].item()))
+        level_bytes.append(n)
         out.append({"bins": sorted({int(v) for v in t.reshape(-1)}, reverse=True),
                     "container_bits_per_elem": round(8 * n / cfg.n_elements, 4),
                     "rel_rmse": round(rel_rmse_f16(b.out[: cfg.n_elements], x), 6)})
-    return {"levels": out, "one_pass_ms": round(statistics.median(one), 4),
-            "level_by_level_ms": round(statistics.median(sep), 4)}
+    res = {"levels": out, "one_pass_ms": round(statistics.median(one), 4),
+           "level_by_level_ms": round(statistics.median(sep), 4)}
+    res["streaming"] = streaming_leg(kvc, cfg, descs, bufs, max(level_bytes), steps)
+    return res
+
+
+def streaming_leg(kvc, cfg, descs, bufs, max_level_bytes, steps):
+    """kvc_stream_encode over the quality levels: chunk j at the level of a
+    fixed schedule (runs of 16 chunks cycling 0, 1, 2, 1), each chunk's
+    container copied to page-locked host memory at its exact size.  Wall
+    time of the whole call with the copies on a second stream (overlapped)
+    and on the compute stream (serial), next to one plain device-to-host
+    copy of the same number of bytes.  Outside the timed step."""
+    import numpy as np
+    import torch
+    nc = descs[0].n_chunks
+    cycle = [0, 1, 2, 1]
+    sched = np.array([cycle[(j // 16) % 4] for j in range(nc)], np.int32)
+    work = torch.empty(kvc.kvc_stream_work_bytes(descs, 0), dtype=torch.uint8, device="cuda")
+    host = torch.empty(int(max_level_bytes * 1.05) + nc * 4096, dtype=torch.uint8).pin_memory()
+    sizes = torch.zeros(nc, dtype=torch.int64).pin_memory()
+    st = bufs[0].dev_status
+    cs, xs = torch.cuda.Stream(), torch.cuda.Stream()
+    syms, cdfs, max1 = [b.sym for b in bufs], [b.cdf for b in bufs], bufs[0].max1
+
+    def run(two):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        kvc.kvc_stream_encode(descs, sched, syms, cdfs, max1, work, host, sizes, st, cs, xs if two else cs)
+        return (time.perf_counter() - t0) * 1e3
+
+    run(True)  # warm-up
+    if int(st.item()):
+        raise RuntimeError(f"streaming leg: device status {int(st.item()):#x}")
+    reps = max(1, min(steps, 3))
+    ov = statistics.median([run(True) for _ in range(reps)])
+    se = statistics.median([run(False) for _ in range(reps)])
+    total = int(sizes.sum().item())
+    dev = torch.empty(total, dtype=torch.uint8, device="cuda")
+    cp = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        host[:total].copy_(dev, non_blocking=True)
+        torch.cuda.synchronize()
+        cp.append((time.perf_counter() - t0) * 1e3)
+    d2h = statistics.median(cp)
+    in_bytes = 2 * cfg.n_elements
+    del work, dev
+    return {"chunks": nc, "schedule": "runs of 16 chunks at levels 0, 1, 2, 1, ...",
+            "chunks_per_level": [int((sched == i).sum()) for i in range(len(descs))],
+            "container_bytes": total, "bits_per_elem": round(8 * total / cfg.n_elements, 4),
+            "overlapped_ms": round(ov, 3), "serial_ms": round(se, 3),
+            "overlap_speedup": round(se / ov, 3), "d2h_only_ms": round(d2h, 3),
+            "d2h_GBps": round(total / (d2h * 1e-3) / 1e9, 2),
+            "overlapped_input_GBps": round(in_bytes / (ov * 1e-3) / 1e9, 2),
+            "timing": "wall clock of kvc_stream_encode (it returns with every container in host memory)"}
 
 
 def delta_leg(kvc, d, buf, cfg, kvt, stream, steps):
@@ -534,6 +590,7 @@ def main():
         res["int8_comparator"] = int8_leg(kvc, d, kvt, buf, cfg, stream, args.steps,
                                           res["container"]["bits_per_elem"])
         res["quality_levels"] = levels_leg(kvc, cfg, kvt, stream, args.steps)
+        res["streaming"] = res["quality_levels"].pop("streaming")
         res["token_delta"] = delta_leg(kvc, d, buf, cfg, kvt, stream, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, kv_np)

@@ -29,6 +29,7 @@ EXPORTED = (
     "kvc_container_bytes", "kvc_container_payload_offset", "kvc_serialize", "kvc_deserialize",
     "kvc_int8_quantize", "kvc_int8_dequantize", "kvc_serialize_chunk", "kvc_quantize_levels",
     "kvc_decode_lanes", "kvc_delta_forward", "kvc_delta_inverse", "kvc_encode_noalloc",
+    "kvc_stream_work_bytes", "kvc_stream_encode",
 )
 KVC_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -42,6 +43,11 @@ class KvcDesc(ctypes.Structure):
         ("reserved", ctypes.c_int32),
         ("bins", ctypes.POINTER(ctypes.c_int32)),
     ]
+
+
+# void on_chunk(void *user, int64_t chunk, int32_t level, const uint8_t *container, int64_t n_bytes)
+CHUNK_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                            ctypes.c_int64)
 
 
 class KvcError(RuntimeError):
@@ -107,6 +113,11 @@ def _load():
         lib.kvc_int8_quantize.argtypes = [D, I32, P, P, P, P, P, P]
         lib.kvc_int8_dequantize.restype = ctypes.c_int
         lib.kvc_int8_dequantize.argtypes = [D, I32, P, P, P, P, I32, P]
+        lib.kvc_stream_work_bytes.restype = I64
+        lib.kvc_stream_work_bytes.argtypes = [D, I32, I32]
+        lib.kvc_stream_encode.restype = ctypes.c_int
+        lib.kvc_stream_encode.argtypes = [D, I32, P, P, P, P, I32, P, I64, P, I64, P, P, P, P,
+                                          CHUNK_FN, P]
         _lib = lib
     return _lib
 
@@ -258,6 +269,51 @@ def kvc_serialize_chunk(desc: Desc, chunk: int, cdf, max1, stream_len, slab_off,
                                                               _ptr(stream_len), _ptr(slab_off),
                                                               _ptr(payload), _ptr(out), oc,
                                                               _ptr(dev_status), _stream(stream)))
+
+
+def kvc_stream_work_bytes(descs, chunks_per_unit: int = 0) -> int:
+    n = len(descs)
+    arr = (KvcDesc * n)(*[d.c for d in descs])
+    v = int(_load().kvc_stream_work_bytes(arr, n, chunks_per_unit))
+    if v < 0:
+        raise KvcError("kvc_stream_work_bytes", v)
+    return v
+
+
+def _host_ptr(t) -> int:
+    if t.is_cuda or not t.is_pinned() or not t.is_contiguous():
+        raise ValueError("kvc: page-locked contiguous host tensors only (torch pin_memory)")
+    return t.data_ptr()
+
+
+def kvc_stream_encode(descs, chunk_level, syms, cdfs, max1, work, host_out, chunk_bytes, dev_status=None,
+                      compute_stream=None, copy_stream=None, chunks_per_unit: int = 0, on_chunk=None,
+                      work_bytes=None, host_cap=None):
+    """descs: Desc per level; chunk_level: host int32 [NC]; syms, cdfs: device
+    tensors per level; work: device buffer; host_out (uint8) and chunk_bytes
+    (int64 [NC]): pinned host tensors; on_chunk(chunk, level, memoryview) or
+    None.  Returns once every container is in host_out."""
+    import torch
+    n = len(descs)
+    arr = (KvcDesc * n)(*[d.c for d in descs])
+    ps = (ctypes.c_void_p * n)(*[_ptr(t) for t in syms])
+    pc = (ctypes.c_void_p * n)(*[_ptr(t) for t in cdfs])
+    lv = np.ascontiguousarray(np.asarray(chunk_level, dtype=np.int32))
+    wb = work.numel() * work.element_size() if work_bytes is None else work_bytes
+    hc = host_out.numel() * host_out.element_size() if host_cap is None else host_cap
+    if chunk_bytes.dtype != torch.int64:
+        raise ValueError("kvc: chunk_bytes must be int64")
+    if on_chunk is None:
+        cb = ctypes.cast(None, CHUNK_FN)
+    else:
+        def _cb(_user, chunk, level, ptr, nbytes):
+            on_chunk(int(chunk), int(level), (ctypes.c_uint8 * nbytes).from_address(ptr))
+        cb = CHUNK_FN(_cb)
+    cs = _stream(compute_stream)
+    xs = cs if copy_stream is None else _stream(copy_stream)
+    _check("kvc_stream_encode", _load().kvc_stream_encode(
+        arr, n, lv.ctypes.data, ps, pc, _ptr(max1), chunks_per_unit, _ptr(work), wb, _host_ptr(host_out), hc,
+        _host_ptr(chunk_bytes), _ptr(dev_status), cs, xs, cb, None))
 
 
 def kvc_deserialize(desc: Desc, inp, cdf, max1, stream_len, slab_off, dev_status=None, stream=None,

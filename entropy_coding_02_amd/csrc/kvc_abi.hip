@@ -2,7 +2,9 @@
 // the host, then asynchronous launches on the caller's stream.
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "kvc_common.h"
 #include "kvc_kernels.h"
@@ -45,6 +47,7 @@ int make_geometry(const kvc_desc *d, Geometry &g)
     p.A = A;
     p.Tc = d->chunk_tokens;
     p.T = d->n_tokens;
+    p.Ts = p.T;
     int64_t NC = (p.T + p.Tc - 1) / p.Tc;
     if (NC > INT32_MAX) return KVC_ERR_ARG;
     p.NC = (int32_t)NC;
@@ -83,6 +86,69 @@ void *noalloc_base()
         base[dev] = ptr;
     }
     return base[dev];
+}
+
+// Device workspace of the streaming encoder for units of up to U chunks
+// (sizes are the largest over the levels); every section 256-byte aligned.
+struct StreamLayout {
+    int32_t U;                                   // chunks per unit
+    int64_t len, off, pay, sizes, staging, total;  // section offsets; scratch at 0
+    int64_t pay_cap, chunk_cap;                  // unit payload, staging bytes per chunk
+};
+
+// Check the level descriptors (as kvc_quantize_levels) and lay out the workspace.
+int stream_layout(const kvc_desc *levels, int32_t n_levels, int32_t chunks_per_unit, Geometry *g,
+                  StreamLayout &sl)
+{
+    if (!levels || n_levels < 1 || n_levels > KVC_MAX_LEVELS || chunks_per_unit < 0) return KVC_ERR_ARG;
+    for (int l = 0; l < n_levels; ++l) {
+        int rc = make_geometry(&levels[l], g[l]);
+        if (rc != KVC_OK) return rc;
+        if (levels[l].n_layers != levels[0].n_layers || levels[l].n_channels != levels[0].n_channels ||
+            levels[l].n_tokens != levels[0].n_tokens || levels[l].chunk_tokens != levels[0].chunk_tokens)
+            return KVC_ERR_ARG;
+    }
+    const KParams &P = g[0].p;
+    const int64_t per_chunk = 2 * (int64_t)P.L * P.Tc;  // streams of a full chunk
+    int64_t U = chunks_per_unit ? chunks_per_unit : (((int64_t)1 << 17) + per_chunk - 1) / per_chunk;
+    U = std::max<int64_t>(1, std::min<int64_t>(U, P.NC));
+    sl.U = (int32_t)U;
+    int64_t scratch = 0, n_streams = 0, n_slabs = 0, chunk_cap = 0;
+    for (int l = 0; l < n_levels; ++l) {
+        kvc_desc du = levels[l], dc = levels[l];
+        du.n_tokens = std::min<int64_t>(U * P.Tc, P.T);
+        dc.n_tokens = std::min<int64_t>(P.Tc, P.T);
+        Geometry gu, gc;
+        int rc = make_geometry(&du, gu);
+        if (rc == KVC_OK) rc = make_geometry(&dc, gc);
+        if (rc != KVC_OK) return rc;
+        scratch = std::max(scratch, gu.scratch);
+        n_streams = gu.p.n_streams;
+        n_slabs = gu.p.n_slabs;
+        const int64_t chunk_pay = gc.p.n_streams * (2 * (int64_t)P.C + 1);
+        chunk_cap = std::max(chunk_cap, round_up(container_total(container_layout(gc.p), chunk_pay), 256));
+    }
+    sl.pay_cap = n_streams * (2 * (int64_t)P.C + 1);
+    sl.chunk_cap = chunk_cap;
+    sl.len = round_up(scratch, 256);
+    sl.off = sl.len + round_up(2 * n_streams, 256);
+    sl.pay = sl.off + round_up(8 * (n_slabs + 1), 256);
+    sl.sizes = sl.pay + round_up(sl.pay_cap, 256);
+    sl.staging = sl.sizes + round_up(8 * U, 256);
+    sl.total = sl.staging + 2 * U * chunk_cap;
+    return KVC_OK;
+}
+
+// Page-locked host memory (a hipHostMalloc allocation).
+bool host_pinned(const void *ptr)
+{
+    hipPointerAttribute_t a;
+    const hipError_t e = hipPointerGetAttributes(&a, ptr);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // a pageable pointer is not an error of the caller's streams
+        return false;
+    }
+    return a.type == hipMemoryTypeHost;
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
@@ -357,9 +423,152 @@ int kvc_serialize_chunk(const kvc_desc *desc, int64_t chunk, const uint16_t *cdf
         (dev_status && !aligned(dev_status, 4)))
         return KVC_ERR_ARG;
     if (out_cap < container_total(container_layout(gc.p), 0)) return KVC_ERR_CAPACITY;
-    return launch_status(launch_serialize_chunk(cdf, max1, stream_len, slab_off, payload, out,
-                                                out_cap, g.p, gc.p, chunk, dev_status,
-                                                (hipStream_t)stream));
+    const int64_t twoL = 2 * (int64_t)g.p.L;
+    const ChunkSrc src{cdf + chunk * twoL * g.p.C * g.p.A, max1, g.p.T, chunk * (int64_t)g.p.Tc,
+                       stream_len + chunk * twoL * g.p.Tc, slab_off + chunk * twoL, payload};
+    return launch_status(launch_serialize_chunk(src, out, out_cap, gc.p, dev_status, (hipStream_t)stream));
+}
+
+int64_t kvc_stream_work_bytes(const kvc_desc *levels, int32_t n_levels, int32_t chunks_per_unit)
+{
+    Geometry g[KVC_MAX_LEVELS];
+    StreamLayout sl;
+    const int rc = stream_layout(levels, n_levels, chunks_per_unit, g, sl);
+    return rc == KVC_OK ? sl.total : rc;
+}
+
+int kvc_stream_encode(const kvc_desc *levels, int32_t n_levels, const int32_t *chunk_level,
+                      const uint8_t *const *sym, const uint16_t *const *cdf, const uint16_t *max1,
+                      int32_t chunks_per_unit, void *work, int64_t work_bytes, uint8_t *host_out,
+                      int64_t host_cap, int64_t *chunk_bytes, int32_t *dev_status, void *compute_stream,
+                      void *copy_stream, kvc_chunk_fn on_chunk, void *user)
+{
+    Geometry g[KVC_MAX_LEVELS];
+    StreamLayout sl;
+    int rc = stream_layout(levels, n_levels, chunks_per_unit, g, sl);
+    if (rc != KVC_OK) return rc;
+    const KParams &P = g[0].p;
+    if (P.NC == 0) return KVC_OK;
+    if (!chunk_level || !sym || !cdf || !max1 || !aligned(max1, 4) || !work || !aligned(work, 256) ||
+        !host_out || host_cap < 0 || !chunk_bytes || !aligned(chunk_bytes, 8) ||
+        (dev_status && !aligned(dev_status, 4)))
+        return KVC_ERR_ARG;
+    for (int l = 0; l < n_levels; ++l)
+        if (!sym[l] || !cdf[l] || !aligned(sym[l], 4) || !aligned(cdf[l], 4)) return KVC_ERR_ARG;
+    for (int64_t j = 0; j < P.NC; ++j)
+        if (chunk_level[j] < 0 || chunk_level[j] >= n_levels) return KVC_ERR_ARG;
+    if (!host_pinned(host_out) || !host_pinned(chunk_bytes)) return KVC_ERR_ARG;
+    if (work_bytes < sl.total) return KVC_ERR_CAPACITY;
+
+    // units: runs of at most U consecutive chunks of one level
+    struct Unit { int64_t ja, jb; int32_t level; };
+    std::vector<Unit> units;
+    for (int64_t j = 0; j < P.NC;) {
+        int64_t jb = j + 1;
+        while (jb < P.NC && jb - j < sl.U && chunk_level[jb] == chunk_level[j]) ++jb;
+        units.push_back({j, jb, chunk_level[j]});
+        j = jb;
+    }
+    const int64_t n_units = (int64_t)units.size();
+    const int64_t twoL = 2 * (int64_t)P.L;
+    uint8_t *const wk = (uint8_t *)work;
+    uint16_t *const len_u = (uint16_t *)(wk + sl.len);
+    uint64_t *const off_u = (uint64_t *)(wk + sl.off);
+    uint8_t *const pay_u = wk + sl.pay;
+    uint64_t *const sizes_u = (uint64_t *)(wk + sl.sizes);
+    const hipStream_t cs = (hipStream_t)compute_stream, xs = (hipStream_t)copy_stream;
+    auto staging = [&](int64_t u) { return wk + sl.staging + (u & 1) * sl.U * sl.chunk_cap; };
+
+    // serialized[h]: staging half h written and its sizes in chunk_bytes (compute
+    // stream); copied[h]: the copies out of half h done (copy stream)
+    hipEvent_t serialized[2] = {}, copied[2] = {};
+    for (int h = 0; h < 2 && rc == KVC_OK; ++h)
+        if (hipEventCreateWithFlags(&serialized[h], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&copied[h], hipEventDisableTiming) != hipSuccess)
+            rc = KVC_ERR_HIP;
+    std::vector<int64_t> host_off(P.NC, 0);
+    int64_t cursor = 0;
+
+    // Encode unit u and write its containers into staging half u % 2.
+    auto enqueue = [&](int64_t u) -> int {
+        const Unit &un = units[u];
+        const int l = un.level;
+        const KParams &pl = g[l].p;
+        kvc_desc du = levels[l];
+        du.n_tokens = std::min<int64_t>(un.jb * P.Tc, P.T) - un.ja * P.Tc;
+        Geometry gu;
+        if (make_geometry(&du, gu) != KVC_OK) return KVC_ERR_ARG;
+        gu.p.Ts = P.T;  // the unit's rows sit in the whole tensor's row blocks
+        const uint8_t *sym_u = sym[l] + un.ja * P.Tc * P.C;
+        const uint16_t *cdf_u = cdf[l] + un.ja * twoL * P.C * pl.A;
+        uint8_t *slots = wk;
+        uint64_t *slab_total = (uint64_t *)(wk + gu.slot_area);
+        const bool vec16 = (P.C % 16 == 0) && aligned(sym_u, 16);
+        hipError_t e = launch_encode(sym_u, cdf_u, slots, slab_total, len_u, off_u, pay_u, sl.pay_cap, gu.p,
+                                     dev_status, vec16, cs);
+        // staging half u % 2 is free once the copies of unit u - 2 are done
+        if (e == hipSuccess && u >= 2) e = hipStreamWaitEvent(cs, copied[u & 1], 0);
+        uint8_t *const st = staging(u);
+        for (int64_t j = un.ja; j < un.jb && e == hipSuccess; ++j) {
+            const int64_t k = j - un.ja;
+            kvc_desc dc = levels[l];
+            dc.n_tokens = std::min<int64_t>((j + 1) * P.Tc, P.T) - j * P.Tc;
+            Geometry gc;
+            if (make_geometry(&dc, gc) != KVC_OK) return KVC_ERR_ARG;
+            const ChunkSrc src{cdf[l] + j * twoL * P.C * pl.A, max1, P.T, j * (int64_t)P.Tc,
+                               len_u + k * twoL * P.Tc, off_u + k * twoL, pay_u};
+            e = launch_serialize_chunk(src, st + k * sl.chunk_cap, sl.chunk_cap, gc.p, dev_status, cs);
+        }
+        const int n = (int)(un.jb - un.ja);
+        if (e == hipSuccess) e = launch_container_totals(st, sl.chunk_cap, n, sizes_u, cs);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(chunk_bytes + un.ja, sizes_u, 8 * (size_t)n, hipMemcpyDeviceToHost, cs);
+        if (e == hipSuccess) e = hipEventRecord(serialized[u & 1], cs);
+        return launch_status(e);
+    };
+    // Copy unit u's containers to host_out at their exact sizes.
+    auto copy_out = [&](int64_t u) -> int {
+        const Unit &un = units[u];
+        if (hipEventSynchronize(serialized[u & 1]) != hipSuccess) return KVC_ERR_HIP;
+        const uint8_t *const st = staging(u);
+        for (int64_t j = un.ja; j < un.jb; ++j) {
+            const int64_t n = chunk_bytes[j];
+            if (n <= 0 || n > sl.chunk_cap) return KVC_ERR_HIP;  // not a container this call wrote
+            if (n > host_cap - cursor) return KVC_ERR_CAPACITY;
+            if (hipMemcpyAsync(host_out + cursor, st + (j - un.ja) * sl.chunk_cap, (size_t)n,
+                               hipMemcpyDeviceToHost, xs) != hipSuccess)
+                return KVC_ERR_HIP;
+            host_off[j] = cursor;
+            cursor += n;
+        }
+        return launch_status(hipEventRecord(copied[u & 1], xs));
+    };
+    // Hand unit u's containers to the caller once their copies are done.
+    auto deliver = [&](int64_t u) -> int {
+        if (!on_chunk) return KVC_OK;
+        if (hipEventSynchronize(copied[u & 1]) != hipSuccess) return KVC_ERR_HIP;
+        const Unit &un = units[u];
+        for (int64_t j = un.ja; j < un.jb; ++j) on_chunk(user, j, un.level, host_out + host_off[j], chunk_bytes[j]);
+        return KVC_OK;
+    };
+    // Unit u is encoded while unit u - 1 is copied; the callbacks of unit u - 2
+    // run after both are queued.
+    for (int64_t u = 0; u < n_units && rc == KVC_OK; ++u) {
+        rc = enqueue(u);
+        if (rc == KVC_OK && u >= 1) rc = copy_out(u - 1);
+        if (rc == KVC_OK && u >= 2) rc = deliver(u - 2);
+    }
+    if (rc == KVC_OK) rc = copy_out(n_units - 1);
+    if (rc == KVC_OK && n_units >= 2) rc = deliver(n_units - 2);
+    if (rc == KVC_OK) rc = deliver(n_units - 1);
+    // drain both streams before the events go (also after an error)
+    const hipError_t e1 = hipStreamSynchronize(cs), e2 = hipStreamSynchronize(xs);
+    if (rc == KVC_OK && (e1 != hipSuccess || e2 != hipSuccess)) rc = KVC_ERR_HIP;
+    for (int h = 0; h < 2; ++h) {
+        if (serialized[h]) (void)hipEventDestroy(serialized[h]);
+        if (copied[h]) (void)hipEventDestroy(copied[h]);
+    }
+    return rc;
 }
 
 int kvc_deserialize(const kvc_desc *desc, const uint8_t *in, int64_t in_bytes, uint16_t *cdf,

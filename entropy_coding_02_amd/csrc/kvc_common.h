@@ -22,6 +22,8 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 // Slab s = (chunk j, layer l, K|V kv) with lk = 2*l + kv; j = s / (2L).
 struct KParams {
     int64_t T;          // tokens
+    int64_t Ts;         // token stride of the (layer, K|V) row blocks in kv and sym: T, or the
+                        // whole tensor's T when a run of its chunks is encoded as a tensor
     int64_t n_rows;     // 2 * L * T
     int64_t n_slabs;    // NC * 2L
     int64_t n_streams;  // 2 * L * T
@@ -35,7 +37,7 @@ struct KParams {
 };
 
 struct SlabGeom {
-    int64_t row0;    // row index of the slab's first token: lk*T + j*Tc
+    int64_t row0;    // row index of the slab's first token: lk*Ts + j*Tc
     int64_t sid0;    // stream id of the slab's first token
     int32_t nj;      // tokens in the slab
     int32_t lk;      // 2*l + kv
@@ -50,7 +52,7 @@ __device__ __forceinline__ SlabGeom slab_geom(const KParams &p, int64_t s)
     g.lk = (int32_t)(s - j * twoL);
     g.nj = (j == p.NC - 1) ? p.last_nj : p.Tc;
     g.rn = (j == p.NC - 1) ? p.rn_last : p.rn_full;
-    g.row0 = (int64_t)g.lk * p.T + j * p.Tc;
+    g.row0 = (int64_t)g.lk * p.Ts + j * p.Tc;
     g.sid0 = j * twoL * p.Tc + (int64_t)g.lk * g.nj;
     return g;
 }

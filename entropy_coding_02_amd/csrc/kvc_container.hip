@@ -202,6 +202,14 @@ unsigned grid_for(int64_t items, int64_t per_block)
     return (unsigned)g;
 }
 
+// The total_bytes field of n containers laid stride bytes apart, into dst[n].
+__global__ void k_container_totals(const uint8_t *__restrict__ base, int64_t stride, int n,
+                                   uint64_t *__restrict__ dst)
+{
+    const int k = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (k < n) dst[k] = *(const uint64_t *)(base + (int64_t)k * stride + 40);
+}
+
 }  // namespace
 
 ContainerLayout container_layout(const KParams &p)
@@ -242,32 +250,28 @@ hipError_t launch_serialize(const uint16_t *cdf, const uint16_t *max1, const uin
     return hipGetLastError();
 }
 
-hipError_t launch_serialize_chunk(const uint16_t *cdf, const uint16_t *max1,
-                                  const uint16_t *stream_len, const uint64_t *slab_off,
-                                  const uint8_t *payload, uint8_t *out, int64_t out_cap,
-                                  const KParams &whole, const KParams &p, int64_t j,
+hipError_t launch_serialize_chunk(const ChunkSrc &src, uint8_t *out, int64_t out_cap, const KParams &p,
                                   int32_t *status, hipStream_t stream)
 {
-    // p describes chunk j as a tensor of its own: T = N_j, one chunk, 2L slabs
+    // p describes the chunk as a tensor of its own: T = N_j, one chunk, 2L slabs
     const ContainerLayout cl = container_layout(p);
     const int64_t twoL = 2 * (int64_t)p.L;
-    const uint64_t *off0 = slab_off + j * twoL, *off1 = slab_off + (j + 1) * twoL;
+    const uint64_t *off0 = src.off, *off1 = src.off + twoL;
     hipLaunchKernelGGL(k_ser_header, dim3(1), dim3(64), 0, stream, off0, off1, out, out_cap, p, cl,
                        status);
     if (p.n_slabs > 0)
-        hipLaunchKernelGGL(k_ser_cdf, dim3((unsigned)p.n_slabs), dim3(256), 0, stream,
-                           cdf + j * twoL * p.C * p.A, out, p, cl, status);
+        hipLaunchKernelGGL(k_ser_cdf, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, src.cdf, out, p, cl,
+                           status);
     const int64_t nj = p.T, rows_padded = cl.len - cl.max1;
     hipLaunchKernelGGL(k_gather_max1, dim3(grid_for(rows_padded / 2, 1024)), dim3(256), 0, stream,
-                       max1, (uint16_t *)(out + cl.max1), whole.T, j * (int64_t)whole.Tc, nj, twoL,
-                       rows_padded);
+                       src.max1, (uint16_t *)(out + cl.max1), src.max1_T, src.t0, nj, twoL, rows_padded);
     const uint64_t *none = nullptr;
     const int64_t lens_b = 2 * p.n_streams;
     hipLaunchKernelGGL(k_copy_section, dim3(grid_for(lens_b, 1024)), dim3(256), 0, stream,
-                       (const uint8_t *)(stream_len + j * twoL * whole.Tc), out + cl.len, lens_b, none,
-                       none, (int64_t)0, cl.pay - cl.len);
+                       (const uint8_t *)src.stream_len, out + cl.len, lens_b, none, none, (int64_t)0,
+                       cl.pay - cl.len);
     hipLaunchKernelGGL(k_copy_section, dim3(grid_for(out_cap - cl.pay, 4096)), dim3(256), 0, stream,
-                       payload, out + cl.pay, (int64_t)0, off0, off1, (int64_t)16, out_cap - cl.pay);
+                       src.payload, out + cl.pay, (int64_t)0, off0, off1, (int64_t)16, out_cap - cl.pay);
     return hipGetLastError();
 }
 
@@ -291,4 +295,13 @@ hipError_t launch_deserialize(const uint8_t *in, int64_t in_bytes, uint16_t *cdf
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_slab_offsets(stream_len, slab_off, p, (const uint64_t *)(in + 32), status, stream);
+}
+
+hipError_t launch_container_totals(const uint8_t *base, int64_t stride, int n, uint64_t *dst,
+                                   hipStream_t stream)
+{
+    if (n > 0)
+        hipLaunchKernelGGL(k_container_totals, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, base,
+                           stride, n, dst);
+    return hipGetLastError();
 }

@@ -288,6 +288,53 @@ int kvc_serialize_chunk(const kvc_desc *desc, int64_t chunk, const uint16_t *cdf
                         void *stream);
 
 /*
+ * Streaming encoder: compute, compress and transmit at the same time ([CG]
+ * 4 point 2), chunk by chunk ([CG] 2.3 step 3).  Chunk j is sent at quality
+ * level chunk_level[j] (the sender's schedule, e.g. from the link's measured
+ * bandwidth): its container is exactly what kvc_serialize_chunk writes for
+ * levels[chunk_level[j]], chunk j (so kvc_deserialize + kvc_decode read it).
+ * Chunks go in units of at most `chunks_per_unit` consecutive chunks of one
+ * level: on compute_stream a unit is encoded (kvc_encode's kernels, on the
+ * unit's rows of sym in place) and its chunk containers are written into one
+ * half of a device staging area; on copy_stream the containers of the unit
+ * before are copied to host_out meanwhile, each at its exact size.  The host
+ * thread reads each unit's container sizes once its staging is written, to
+ * issue those copies, so the call returns only when every container is in
+ * host_out (both streams synchronised).
+ *   levels       HOST array of n_levels descriptors (1..4), as kvc_quantize_levels:
+ *                same n_layers, n_channels, n_tokens, chunk_tokens; bins may differ
+ *   chunk_level  HOST int32 [NC], each in [0, n_levels)
+ *   sym, cdf     HOST arrays of n_levels device pointers: each level's symbols
+ *                [L][2][T][C] and CDFs [NC][L][2][C][A_level] (kvc_quantize_levels)
+ *   max1         [L][2][T] fp16 bits (device)
+ *   chunks_per_unit  1.. , or 0: enough chunks for about 2^17 streams per unit
+ *                (whole-chip encoder launches), at most NC
+ *   work         device, 256-byte aligned, work_bytes >= kvc_stream_work_bytes(levels,
+ *                n_levels, chunks_per_unit): encoder scratch, one unit's lengths,
+ *                offsets and payload, and the two staging halves
+ *   host_out     page-locked host memory (hipHostMalloc), host_cap bytes: the
+ *                containers of chunks 0, 1, ... back to back (chunk j at the sum of
+ *                chunk_bytes[0..j))
+ *   chunk_bytes  page-locked host int64 [NC] (written): each container's size
+ *   compute_stream, copy_stream  HIP streams (equal priority); the same stream
+ *                twice runs every step in order, without overlap
+ *   on_chunk     NULL, or called on this thread for each chunk in order once its
+ *                container is in host_out: (user, chunk, level, bytes, n_bytes)
+ * Returns KVC_ERR_CAPACITY when the containers outgrow host_cap (the chunks
+ * copied so far stay valid; no copy passes host_cap), KVC_ERR_HIP on a failed
+ * launch or copy.  Device flags as kvc_encode and kvc_serialize_chunk.  The
+ * call creates four HIP events for its duration and allocates no memory.
+ */
+typedef void (*kvc_chunk_fn)(void *user, int64_t chunk, int32_t level, const uint8_t *container,
+                             int64_t n_bytes);
+int64_t kvc_stream_work_bytes(const kvc_desc *levels, int32_t n_levels, int32_t chunks_per_unit);
+int kvc_stream_encode(const kvc_desc *levels, int32_t n_levels, const int32_t *chunk_level,
+                      const uint8_t *const *sym, const uint16_t *const *cdf, const uint16_t *max1,
+                      int32_t chunks_per_unit, void *work, int64_t work_bytes, uint8_t *host_out,
+                      int64_t host_cap, int64_t *chunk_bytes, int32_t *dev_status, void *compute_stream,
+                      void *copy_stream, kvc_chunk_fn on_chunk, void *user);
+
+/*
  * Read a container back into the buffers kvc_decode takes.
  *   in           device, 16-byte aligned, in_bytes bytes (read, never past in_bytes)
  *   cdf          [NC][L][2][C][A] uint16 (device, written): the full tables

@@ -131,3 +131,44 @@ def test_container_calls_reject_bad_arguments(lib):
     assert lib.kvc_deserialize(d.ref, ok, need - 16, ok, ok, ok, ok, None, None) == kvc.KVC_ERR_CAPACITY
     assert lib.kvc_deserialize(d.ref, ok, need, ok, ok, ok, ok + 4, None, None) == kvc.KVC_ERR_ARG
     assert lib.kvc_container_bytes(d.ref, -1) == kvc.KVC_ERR_ARG
+
+
+def test_stream_work_bytes_and_argument_checks(lib):
+    """kvc_stream_work_bytes: the automatic unit is about 2^17 streams (at
+    most NC chunks), the workspace grows with the unit, mismatched levels are
+    refused; kvc_stream_encode refuses null arguments and out-of-range levels
+    before any HIP call."""
+    L, C, T, Tc = 2, 64, 1000, 64  # 16 chunks of 256 streams
+    a, b = kvc.Desc(L, C, T, [[32, 16], [16, 8]], Tc), kvc.Desc(L, C, T, [[8, 8], [4, 4]], Tc)
+    w = [kvc.kvc_stream_work_bytes([a, b], u) for u in range(1, 17)]
+    assert all(x < y for x, y in zip(w, w[1:]))
+    assert kvc.kvc_stream_work_bytes([a, b], 0) == w[-1]      # 2^17 streams > 16 chunks: all of them
+    assert kvc.kvc_stream_work_bytes([a, b], 99) == w[-1]     # capped at NC
+    assert kvc.kvc_stream_work_bytes([a], 4) <= kvc.kvc_stream_work_bytes([a, b], 4)
+    big = kvc.Desc(32, 1024, 80000, np.full((32, 2), 32, np.int32), 256)  # 16384 streams a chunk
+    assert kvc.kvc_stream_work_bytes([big], 0) == kvc.kvc_stream_work_bytes([big], 8)
+    for bad in ([a, kvc.Desc(L, C, T + 1, [[32, 16], [16, 8]], Tc)], [a, kvc.Desc(L, 32, T, [[32, 16], [16, 8]], Tc)]):
+        with pytest.raises(kvc.KvcError):
+            kvc.kvc_stream_work_bytes(bad, 1)
+    arr = (kvc.KvcDesc * 2)(a.c, b.c)
+    assert lib.kvc_stream_work_bytes(arr, 0, 1) == kvc.KVC_ERR_ARG
+    assert lib.kvc_stream_work_bytes(arr, 5, 1) == kvc.KVC_ERR_ARG
+    assert lib.kvc_stream_work_bytes(arr, 2, -1) == kvc.KVC_ERR_ARG
+    ok = 1 << 20
+    ptrs = (ctypes.c_void_p * 2)(ok, ok)
+    levels = np.zeros(16, np.int32)
+    none_fn = ctypes.cast(None, kvc.CHUNK_FN)
+
+    def call(level_ptr, syms=ptrs, max1=ok, work=ok, host=ok, sizes=ok):
+        return lib.kvc_stream_encode(arr, 2, level_ptr, syms, ptrs, max1, 1, work, 1 << 40, host, 1 << 30,
+                                     sizes, None, None, None, none_fn, None)
+    assert call(None) == kvc.KVC_ERR_ARG
+    assert call(levels.ctypes.data, max1=None) == kvc.KVC_ERR_ARG
+    assert call(levels.ctypes.data, work=ok + 16) == kvc.KVC_ERR_ARG   # not 256-byte aligned
+    assert call(levels.ctypes.data, host=None) == kvc.KVC_ERR_ARG
+    assert call(levels.ctypes.data, sizes=ok + 4) == kvc.KVC_ERR_ARG
+    assert call(levels.ctypes.data, syms=(ctypes.c_void_p * 2)(ok, None)) == kvc.KVC_ERR_ARG
+    for lv in (-1, 2):
+        bad = levels.copy()
+        bad[7] = lv
+        assert call(bad.ctypes.data) == kvc.KVC_ERR_ARG
