@@ -49,15 +49,15 @@ def _load():
         lib.orc_quantize.restype = ctypes.c_int
         lib.orc_quantize.argtypes = [I32, I32, I64, P, P, P, P]
         lib.orc_cdf.restype = ctypes.c_int
-        lib.orc_cdf.argtypes = [I32, I32, I64, I32, I32, P, P]
+        lib.orc_cdf.argtypes = [I32, I32, I64, I32, I32, I32, P, P]
         lib.orc_encode_stream.restype = I64
         lib.orc_encode_stream.argtypes = [P, I32, I32, P, P, I64]
         lib.orc_decode_stream.restype = ctypes.c_int
         lib.orc_decode_stream.argtypes = [P, I64, I32, I32, P, P]
         lib.orc_encode.restype = I64
-        lib.orc_encode.argtypes = [I32, I32, I64, I32, I32, P, P, P, P, P, I64]
+        lib.orc_encode.argtypes = [I32, I32, I64, I32, I32, I32, P, P, P, P, P, I64]
         lib.orc_decode.restype = ctypes.c_int
-        lib.orc_decode.argtypes = [I32, I32, I64, I32, I32, P, P, P, P, P]
+        lib.orc_decode.argtypes = [I32, I32, I64, I32, I32, I32, P, P, P, P, P]
         lib.orc_dequantize.restype = ctypes.c_int
         lib.orc_dequantize.argtypes = [I32, I32, I64, P, P, P, P, I32]
         lib.orc_delta_forward.restype = ctypes.c_int
@@ -65,13 +65,13 @@ def _load():
         lib.orc_delta_inverse.restype = ctypes.c_int
         lib.orc_delta_inverse.argtypes = [I32, I32, I64, I32, I32, P]
         lib.orc_container_bytes.restype = I64
-        lib.orc_container_bytes.argtypes = [I32, I32, I64, I32, P, I64]
+        lib.orc_container_bytes.argtypes = [I32, I32, I64, I32, I32, P, I64]
         lib.orc_container_payload_offset.restype = I64
-        lib.orc_container_payload_offset.argtypes = [I32, I32, I64, I32, P]
+        lib.orc_container_payload_offset.argtypes = [I32, I32, I64, I32, I32, P]
         lib.orc_serialize.restype = I64
-        lib.orc_serialize.argtypes = [I32, I32, I64, I32, P, P, P, P, P, I64, P, I64]
+        lib.orc_serialize.argtypes = [I32, I32, I64, I32, I32, P, P, P, P, P, I64, P, I64]
         lib.orc_deserialize.restype = ctypes.c_int
-        lib.orc_deserialize.argtypes = [I32, I32, I64, I32, P, P, I64, P, P, P, P, P]
+        lib.orc_deserialize.argtypes = [I32, I32, I64, I32, I32, P, P, I64, P, P, P, P, P]
         lib.orc_int8_quantize.restype = ctypes.c_int
         lib.orc_int8_quantize.argtypes = [I32, I32, I64, I32, P, P, P, P]
         lib.orc_int8_dequantize.restype = ctypes.c_int
@@ -112,6 +112,14 @@ def chunk_tokens(T: int, Tc: int, j: int) -> int:
     return min(Tc, T - j * Tc)
 
 
+def tables_of(T: int, Tc: int, tab_chunks: int = 1) -> tuple[int, int]:
+    """(chunks per CDF table as stored, number of tables per (layer, K|V)):
+    tab_chunks taken as at most NC (1 when there are no chunks)."""
+    NC = n_chunks(T, Tc)
+    S = min(tab_chunks, NC) if NC else 1
+    return S, -(-NC // S)
+
+
 # ----------------------------------------------------------------- steps
 
 def quantize(kv: np.ndarray, bins: np.ndarray):
@@ -128,12 +136,13 @@ def quantize(kv: np.ndarray, bins: np.ndarray):
     return sym, max1
 
 
-def cdf(sym: np.ndarray, Tc: int, A: int) -> np.ndarray:
-    """sym u8 [L][2][T][C] -> cdf u16 [NC][L][2][C][A]."""
+def cdf(sym: np.ndarray, Tc: int, A: int, tab_chunks: int = 1) -> np.ndarray:
+    """sym u8 [L][2][T][C] -> cdf u16 [NG][L][2][C][A], one table per
+    tab_chunks chunks (1: per chunk)."""
     L, _, T, C = sym.shape
     sym = np.ascontiguousarray(sym, dtype=np.uint8)
-    out = np.empty((n_chunks(T, Tc), L, 2, C, A), dtype=np.uint16)
-    rc = _load().orc_cdf(L, C, T, Tc, A, _ptr(sym), _ptr(out))
+    out = np.empty((tables_of(T, Tc, tab_chunks)[1], L, 2, C, A), dtype=np.uint16)
+    rc = _load().orc_cdf(L, C, T, Tc, tab_chunks, A, _ptr(sym), _ptr(out))
     if rc != ORC_OK:
         raise OracleError("orc_cdf", rc)
     return out
@@ -163,7 +172,8 @@ def decode_stream(data: bytes, cdf_rows: np.ndarray):
     return q, bool(bad)
 
 
-def encode(sym: np.ndarray, cdf_tab: np.ndarray, Tc: int, A: int, payload_cap: int | None = None):
+def encode(sym: np.ndarray, cdf_tab: np.ndarray, Tc: int, A: int, payload_cap: int | None = None,
+           tab_chunks: int = 1):
     """-> (stream_len u16 [n_streams], slab_off u64 [n_slabs+1], payload u8)."""
     L, _, T, C = sym.shape
     NC = n_chunks(T, Tc)
@@ -174,7 +184,7 @@ def encode(sym: np.ndarray, cdf_tab: np.ndarray, Tc: int, A: int, payload_cap: i
     stream_len = np.zeros(n_streams, dtype=np.uint16)
     slab_off = np.zeros(n_slabs + 1, dtype=np.uint64)
     payload = np.zeros(max(payload_cap, 1), dtype=np.uint8)
-    n = _load().orc_encode(L, C, T, Tc, A, _ptr(np.ascontiguousarray(sym)),
+    n = _load().orc_encode(L, C, T, Tc, tab_chunks, A, _ptr(np.ascontiguousarray(sym)),
                            _ptr(np.ascontiguousarray(cdf_tab)), _ptr(stream_len), _ptr(slab_off),
                            _ptr(payload), payload_cap)
     if n < 0:
@@ -183,11 +193,11 @@ def encode(sym: np.ndarray, cdf_tab: np.ndarray, Tc: int, A: int, payload_cap: i
 
 
 def decode(payload: np.ndarray, slab_off: np.ndarray, stream_len: np.ndarray, cdf_tab: np.ndarray,
-           L: int, C: int, T: int, Tc: int, A: int):
+           L: int, C: int, T: int, Tc: int, A: int, tab_chunks: int = 1):
     """-> (sym u8 [L][2][T][C], corrupt flag)."""
     sym = np.empty((L, 2, T, C), dtype=np.uint8)
     pay = np.concatenate([np.ascontiguousarray(payload, dtype=np.uint8), np.zeros(1, np.uint8)])
-    rc = _load().orc_decode(L, C, T, Tc, A, _ptr(pay), _ptr(np.ascontiguousarray(slab_off)),
+    rc = _load().orc_decode(L, C, T, Tc, tab_chunks, A, _ptr(pay), _ptr(np.ascontiguousarray(slab_off)),
                             _ptr(np.ascontiguousarray(stream_len)),
                             _ptr(np.ascontiguousarray(cdf_tab)), _ptr(sym))
     if rc not in (ORC_OK, ORC_ERR_CORRUPT):
@@ -211,30 +221,30 @@ def _bins32(bins) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(bins, dtype=np.int32).reshape(-1))
 
 
-def container_bytes(L: int, C: int, T: int, Tc: int, bins, payload_bytes: int) -> int:
-    n = _load().orc_container_bytes(L, C, T, Tc, _ptr(_bins32(bins)), payload_bytes)
+def container_bytes(L: int, C: int, T: int, Tc: int, bins, payload_bytes: int, tab_chunks: int = 1) -> int:
+    n = _load().orc_container_bytes(L, C, T, Tc, tab_chunks, _ptr(_bins32(bins)), payload_bytes)
     if n < 0:
         raise OracleError("orc_container_bytes", n)
     return int(n)
 
 
-def container_payload_offset(L: int, C: int, T: int, Tc: int, bins) -> int:
-    n = _load().orc_container_payload_offset(L, C, T, Tc, _ptr(_bins32(bins)))
+def container_payload_offset(L: int, C: int, T: int, Tc: int, bins, tab_chunks: int = 1) -> int:
+    n = _load().orc_container_payload_offset(L, C, T, Tc, tab_chunks, _ptr(_bins32(bins)))
     if n < 0:
         raise OracleError("orc_container_payload_offset", n)
     return int(n)
 
 
 def serialize(cdf_tab: np.ndarray, max1: np.ndarray, stream_len: np.ndarray, payload: np.ndarray,
-              bins, Tc: int) -> np.ndarray:
+              bins, Tc: int, tab_chunks: int = 1) -> np.ndarray:
     """-> the container bytes (u8)."""
     L, _, T = max1.shape
     C = cdf_tab.shape[3]
     pb = int(payload.size)
-    n = container_bytes(L, C, T, Tc, bins, pb)
+    n = container_bytes(L, C, T, Tc, bins, pb, tab_chunks)
     out = np.empty(n, dtype=np.uint8)
     pay = np.ascontiguousarray(payload, dtype=np.uint8) if pb else np.zeros(1, np.uint8)
-    rc = _load().orc_serialize(L, C, T, Tc, _ptr(_bins32(bins)), _ptr(np.ascontiguousarray(cdf_tab)),
+    rc = _load().orc_serialize(L, C, T, Tc, tab_chunks, _ptr(_bins32(bins)), _ptr(np.ascontiguousarray(cdf_tab)),
                                _ptr(np.ascontiguousarray(max1)), _ptr(np.ascontiguousarray(stream_len)),
                                _ptr(pay), pb, _ptr(out), n)
     if rc < 0:
@@ -242,23 +252,24 @@ def serialize(cdf_tab: np.ndarray, max1: np.ndarray, stream_len: np.ndarray, pay
     return out
 
 
-def deserialize(data: np.ndarray, L: int, C: int, T: int, Tc: int, bins):
+def deserialize(data: np.ndarray, L: int, C: int, T: int, Tc: int, bins, tab_chunks: int = 1):
     """-> dict(cdf, max1, stream_len, slab_off, payload_bytes, payload_offset)."""
     A = int(np.max(bins))
     NC = n_chunks(T, Tc)
-    cdf_tab = np.empty((NC, L, 2, C, A), dtype=np.uint16)
+    cdf_tab = np.empty((tables_of(T, Tc, tab_chunks)[1], L, 2, C, A), dtype=np.uint16)
     max1 = np.empty((L, 2, T), dtype=np.uint16)
     stream_len = np.empty(2 * L * T, dtype=np.uint16)
     slab_off = np.empty(NC * L * 2 + 1, dtype=np.uint64)
     pb = ctypes.c_int64(0)
     data = np.ascontiguousarray(data, dtype=np.uint8)
-    rc = _load().orc_deserialize(L, C, T, Tc, _ptr(_bins32(bins)), _ptr(data), data.size,
+    rc = _load().orc_deserialize(L, C, T, Tc, tab_chunks, _ptr(_bins32(bins)), _ptr(data), data.size,
                                  _ptr(cdf_tab), _ptr(max1), _ptr(stream_len), _ptr(slab_off),
                                  ctypes.addressof(pb))
     if rc != ORC_OK:
         raise OracleError("orc_deserialize", rc)
     return dict(cdf=cdf_tab, max1=max1, stream_len=stream_len, slab_off=slab_off,
-                payload_bytes=int(pb.value), payload_offset=container_payload_offset(L, C, T, Tc, bins))
+                payload_bytes=int(pb.value),
+                payload_offset=container_payload_offset(L, C, T, Tc, bins, tab_chunks))
 
 
 def delta_forward(kv: np.ndarray, bins: np.ndarray, Tc: int, G: int) -> np.ndarray:
@@ -307,34 +318,36 @@ def int8_dequantize(q: np.ndarray, scale: np.ndarray, zp: np.ndarray, g: int, fp
     return out
 
 
-def chunk_of(r: dict, j: int, T: int, Tc: int):
+def chunk_of(r: dict, j: int, T: int, Tc: int, tab_chunks: int = 1):
     """Chunk j of an encoded tensor as a tensor of its own (T = N_j tokens):
-    its CDF slabs, its max1 rows, its stream lengths and its payload bytes,
-    cut out of codec()'s outputs ([CG] 2.3 step 3: chunks stream on their own)."""
+    the CDF tables it was coded with (its own, or its group's when tables are
+    shared), its max1 rows, its stream lengths and its payload bytes, cut out
+    of codec()'s outputs ([CG] 2.3 step 3: chunks stream on their own)."""
     L = r["max1"].shape[0]
     nj = chunk_tokens(T, Tc, j)
+    g = j // tables_of(T, Tc, tab_chunks)[0]
     s0, s1 = j * 2 * L, (j + 1) * 2 * L
     lo, hi = int(r["slab_off"][s0]), int(r["slab_off"][s1])
-    return dict(cdf=np.ascontiguousarray(r["cdf"][j:j + 1]),
+    return dict(cdf=np.ascontiguousarray(r["cdf"][g:g + 1]),
                 max1=np.ascontiguousarray(r["max1"][:, :, j * Tc:j * Tc + nj]),
                 stream_len=np.ascontiguousarray(r["stream_len"][j * 2 * L * Tc:j * 2 * L * Tc + 2 * L * nj]),
                 payload=np.ascontiguousarray(r["payload"][lo:hi]), n_tokens=nj)
 
 
-def serialize_chunk(r: dict, j: int, bins, T: int, Tc: int) -> np.ndarray:
-    """The container of chunk j alone (a tensor of N_j tokens)."""
-    c = chunk_of(r, j, T, Tc)
+def serialize_chunk(r: dict, j: int, bins, T: int, Tc: int, tab_chunks: int = 1) -> np.ndarray:
+    """The container of chunk j alone (a tensor of N_j tokens, one table)."""
+    c = chunk_of(r, j, T, Tc, tab_chunks)
     return serialize(c["cdf"], c["max1"], c["stream_len"], c["payload"], bins, Tc)
 
 
-def codec(kv: np.ndarray, bins: np.ndarray, Tc: int):
+def codec(kv: np.ndarray, bins: np.ndarray, Tc: int, tab_chunks: int = 1):
     """The whole hot path on the CPU: dict of every intermediate and output."""
     A = int(np.max(bins))
     sym, max1 = quantize(kv, bins)
-    cdf_tab = cdf(sym, Tc, A)
-    stream_len, slab_off, payload = encode(sym, cdf_tab, Tc, A)
+    cdf_tab = cdf(sym, Tc, A, tab_chunks)
+    stream_len, slab_off, payload = encode(sym, cdf_tab, Tc, A, tab_chunks=tab_chunks)
     L, _, T, C = kv.shape
-    dsym, bad = decode(payload, slab_off, stream_len, cdf_tab, L, C, T, Tc, A)
+    dsym, bad = decode(payload, slab_off, stream_len, cdf_tab, L, C, T, Tc, A, tab_chunks)
     out16 = dequantize(dsym, max1, bins, fp32=False)
     return dict(A=A, sym=sym, max1=max1, cdf=cdf_tab, stream_len=stream_len, slab_off=slab_off,
                 payload=payload, dec_sym=dsym, corrupt=bad, out_f16=out16)

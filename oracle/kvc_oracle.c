@@ -117,29 +117,42 @@ int orc_quantize(int32_t L, int32_t C, int64_t T, const int32_t *bins, const uin
 /* ------------------------------------------------------------ a4 + a5: CDF */
 
 /*
- * Per chunk j (tokens [j*Tc, min(j*Tc+Tc, T))), layer, K|V and channel c:
- *   n_s   = number of chunk tokens whose symbol in channel c is s, s in [0, A)
+ * Per table, layer, K|V and channel c.  A table serves S consecutive chunks
+ * (S = tab_chunks, taken as at most NC): table g covers tokens
+ * [g*S*Tc, min((g+1)*S*Tc, T)), N_g of them.  S = 1 is the page's reading,
+ * one table per chunk ([CG] 2.3 steps 2-3); S > 1 shares one table between
+ * the chunks of a group, which the page's per-chunk tables leave open.
+ *   n_s   = number of the table's tokens whose symbol in channel c is s, s in [0, A)
  *   C_k   = n_0 + ... + n_{k-1}
- *   cdf_k = k + floor(C_k * (65536 - A) / N_j),   k = 0..A  (cdf_A = 65536)
+ *   cdf_k = k + floor(C_k * (65536 - A) / N_g),   k = 0..A  (cdf_A = 65536)
  * Every symbol keeps a frequency cdf_{s+1} - cdf_s >= 1.
  */
-int orc_cdf(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t A, const uint8_t *sym,
-            uint16_t *cdf)
+static int64_t eff_tab_chunks(int64_t T, int32_t Tc, int32_t tab_chunks)
 {
-    if (L < 1 || C < 1 || T < 0 || Tc < 1 || Tc > 65535 || A < 2 || A > 256) return ORC_ERR_ARG;
-    int64_t NC = (T + Tc - 1) / Tc;
+    const int64_t NC = (T + Tc - 1) / Tc;
+    return tab_chunks < NC ? tab_chunks : (NC > 0 ? NC : 1);
+}
+
+int orc_cdf(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t tab_chunks, int32_t A,
+            const uint8_t *sym, uint16_t *cdf)
+{
+    if (L < 1 || C < 1 || T < 0 || Tc < 1 || Tc > 65535 || tab_chunks < 1 || A < 2 || A > 256)
+        return ORC_ERR_ARG;
+    const int64_t S = eff_tab_chunks(T, Tc, tab_chunks);
+    const int64_t span = S * Tc; /* tokens of a full table */
+    const int64_t NG = (T + span - 1) / span;
     uint64_t *n = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)A);
     if (!n) return ORC_ERR_ARG;
     const uint64_t K = 65536u - (uint64_t)A;
-    for (int64_t j = 0; j < NC; ++j) {
-        int64_t t0 = j * Tc;
-        int64_t Nj = (T - t0 < Tc) ? (T - t0) : Tc;
+    for (int64_t g = 0; g < NG; ++g) {
+        int64_t t0 = g * span;
+        int64_t Ng = (T - t0 < span) ? (T - t0) : span;
         for (int32_t l = 0; l < L; ++l) {
             for (int kvi = 0; kvi < 2; ++kvi) {
-                int64_t slab = (j * L + l) * 2 + kvi;
+                int64_t tab = (g * L + l) * 2 + kvi;
                 for (int32_t c = 0; c < C; ++c) {
                     memset(n, 0, sizeof(uint64_t) * (size_t)A);
-                    for (int64_t t = t0; t < t0 + Nj; ++t) {
+                    for (int64_t t = t0; t < t0 + Ng; ++t) {
                         uint8_t s = sym[(((int64_t)l * 2 + kvi) * T + t) * C + c];
                         if (s >= A) {
                             free(n);
@@ -147,10 +160,10 @@ int orc_cdf(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t A, const uint8_
                         }
                         n[s] += 1;
                     }
-                    uint16_t *row = cdf + (slab * C + c) * A;
+                    uint16_t *row = cdf + (tab * C + c) * A;
                     uint64_t Ck = 0;
                     for (int32_t k = 0; k < A; ++k) {
-                        row[k] = (uint16_t)((uint64_t)k + (Ck * K) / (uint64_t)Nj);
+                        row[k] = (uint16_t)((uint64_t)k + (Ck * K) / (uint64_t)Ng);
                         Ck += n[k];
                     }
                 }
@@ -309,16 +322,19 @@ static int64_t chunk_tokens_of(int64_t T, int32_t Tc, int64_t j)
 
 /*
  * Streams in (chunk, layer, K|V, token) order; stream (j, l, kv, t) codes the
- * symbols of token j*Tc+t of (l, kv) with the CDF rows of slab (j, l, kv).
+ * symbols of token j*Tc+t of (l, kv) with the CDF rows of table
+ * (floor(j / S), l, kv), S = chunks per table (orc_cdf).
  * slab_off[s] = bytes of all streams of the slabs before slab s.  Returns the
  * payload size, or a negative error (ORC_ERR_CAPACITY if it exceeds the cap).
  */
-int64_t orc_encode(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t A, const uint8_t *sym,
-                   const uint16_t *cdf, uint16_t *stream_len, uint64_t *slab_off, uint8_t *payload,
-                   int64_t payload_cap)
+int64_t orc_encode(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t tab_chunks, int32_t A,
+                   const uint8_t *sym, const uint16_t *cdf, uint16_t *stream_len, uint64_t *slab_off,
+                   uint8_t *payload, int64_t payload_cap)
 {
-    if (L < 1 || C < 1 || T < 0 || Tc < 1 || Tc > 65535 || A < 2 || A > 256) return ORC_ERR_ARG;
+    if (L < 1 || C < 1 || T < 0 || Tc < 1 || Tc > 65535 || tab_chunks < 1 || A < 2 || A > 256)
+        return ORC_ERR_ARG;
     int64_t NC = (T + Tc - 1) / Tc;
+    const int64_t S = eff_tab_chunks(T, Tc, tab_chunks);
     int64_t tmpcap = 2 * (int64_t)C + 8;
     uint8_t *tmp = (uint8_t *)malloc((size_t)tmpcap);
     if (!tmp) return ORC_ERR_ARG;
@@ -329,7 +345,8 @@ int64_t orc_encode(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t A, const
         for (int32_t l = 0; l < L; ++l) {
             for (int kvi = 0; kvi < 2; ++kvi, ++slab) {
                 slab_off[slab] = (uint64_t)off;
-                const uint16_t *rows = cdf + slab * C * (int64_t)A;
+                const int64_t tab = (j / S) * 2 * L + (int64_t)l * 2 + kvi;
+                const uint16_t *rows = cdf + tab * C * (int64_t)A;
                 for (int64_t t = 0; t < Nj; ++t, ++sid) {
                     const uint8_t *q = sym + (((int64_t)l * 2 + kvi) * T + j * Tc + t) * C;
                     int64_t n = orc_encode_stream(q, C, A, rows, tmp, tmpcap);
@@ -354,19 +371,22 @@ int64_t orc_encode(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t A, const
 
 /* Decode every stream back to symbols [L][2][T][C].  Returns ORC_OK, or
  * ORC_ERR_CORRUPT if any stream was inconsistent. */
-int orc_decode(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t A, const uint8_t *payload,
-               const uint64_t *slab_off, const uint16_t *stream_len, const uint16_t *cdf,
-               uint8_t *sym)
+int orc_decode(int32_t L, int32_t C, int64_t T, int32_t Tc, int32_t tab_chunks, int32_t A,
+               const uint8_t *payload, const uint64_t *slab_off, const uint16_t *stream_len,
+               const uint16_t *cdf, uint8_t *sym)
 {
-    if (L < 1 || C < 1 || T < 0 || Tc < 1 || Tc > 65535 || A < 2 || A > 256) return ORC_ERR_ARG;
+    if (L < 1 || C < 1 || T < 0 || Tc < 1 || Tc > 65535 || tab_chunks < 1 || A < 2 || A > 256)
+        return ORC_ERR_ARG;
     int64_t NC = (T + Tc - 1) / Tc;
+    const int64_t S = eff_tab_chunks(T, Tc, tab_chunks);
     int64_t sid = 0, slab = 0;
     int corrupt = 0;
     for (int64_t j = 0; j < NC; ++j) {
         int64_t Nj = chunk_tokens_of(T, Tc, j);
         for (int32_t l = 0; l < L; ++l) {
             for (int kvi = 0; kvi < 2; ++kvi, ++slab) {
-                const uint16_t *rows = cdf + slab * C * (int64_t)A;
+                const int64_t tab = (j / S) * 2 * L + (int64_t)l * 2 + kvi;
+                const uint16_t *rows = cdf + tab * C * (int64_t)A;
                 uint64_t off = slab_off[slab];
                 for (int64_t t = 0; t < Nj; ++t, ++sid) {
                     uint8_t *q = sym + (((int64_t)l * 2 + kvi) * T + j * Tc + t) * C;

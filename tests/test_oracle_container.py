@@ -16,15 +16,19 @@ def r16(x):
     return (x + 15) // 16 * 16
 
 
-def test_hand_built_container_of_a_tiny_case():
-    # L=1, C=2, T=3, Tc=2 -> chunks of 2 and 1 tokens; bins K=6, V=4 -> A=6, K=65530
+@pytest.mark.parametrize("S", [1, 2, 7])
+def test_hand_built_container_of_a_tiny_case(S):
+    # L=1, C=2, T=3, Tc=2 -> chunks of 2 and 1 tokens; bins K=6, V=4 -> A=6, K=65530.
+    # S chunks per CDF table: 1 -> two tables; 2, or 7 (stored as 2 = NC) -> one table
     L, C, T, Tc = 1, 2, 3, 2
     bins = np.array([[6, 4]], np.int32)
     A, Kc = 6, 65536 - 6
     NC = 2
-    cdf = np.zeros((NC, L, 2, C, A), np.uint16)
+    S_stored = min(S, NC)
+    NG = -(-NC // S_stored)
+    cdf = np.zeros((NG, L, 2, C, A), np.uint16)
     inner = {}
-    for j in range(NC):
+    for j in range(NG):
         for kv in range(2):
             b = int(bins[0, kv])
             for c in range(C):
@@ -37,36 +41,41 @@ def test_hand_built_container_of_a_tiny_case():
     stream_len = np.array([2, 1, 0, 2, 0, 0], np.uint16)
     payload = np.frombuffer(b"\x11\x22\x33\x44\x55", np.uint8)
 
-    got = oracle.serialize(cdf, max1, stream_len, payload, bins, Tc)
+    got = oracle.serialize(cdf, max1, stream_len, payload, bins, Tc, tab_chunks=S)
 
     # offsets by hand: header 64, bins at 64 (2 bytes), CDF at 80:
-    # per chunk 2 channels x (6-2) + 2 channels x (4-2) = 12 entries = 24 bytes, 2 chunks = 48
-    o_cdf, o_max1, o_len, o_pay = 80, 128, 144, 160
+    # per table 2 channels x (6-2) + 2 channels x (4-2) = 12 entries = 24 bytes
+    o_cdf = 80
+    o_max1 = r16(o_cdf + 24 * NG)
+    o_len = o_max1 + 16  # 6 max1 values = 12 bytes, padded
+    o_pay = o_len + 16
     total = o_pay + 16
     want = bytearray(total)
-    struct.pack_into("<IIIIQIIQQ", want, 0, 0x3143564B, 1, L, C, T, Tc, A, payload.size, total)
+    struct.pack_into("<IIIIQIIQQI", want, 0, 0x3143564B, 1, L, C, T, Tc, A, payload.size, total, S_stored)
     want[64:66] = bytes([6, 4])
     p = o_cdf
-    for j in range(NC):
+    for j in range(NG):
         for kv in range(2):
             for c in range(C):
                 for v in inner[(j, kv, c)]:
                     struct.pack_into("<H", want, p, v)
                     p += 2
-    assert p == 128
+    assert p == o_cdf + 24 * NG
     for i, v in enumerate(max1.reshape(-1)):
         struct.pack_into("<H", want, o_max1 + 2 * i, int(v))
     for i, v in enumerate(stream_len):
         struct.pack_into("<H", want, o_len + 2 * i, int(v))
     want[o_pay:o_pay + 5] = payload.tobytes()
     assert got.tobytes() == bytes(want)
-    assert oracle.container_payload_offset(L, C, T, Tc, bins) == o_pay
-    assert oracle.container_bytes(L, C, T, Tc, bins, 5) == total
+    assert oracle.container_payload_offset(L, C, T, Tc, bins, S) == o_pay
+    assert oracle.container_bytes(L, C, T, Tc, bins, 5, S) == total
 
-    back = oracle.deserialize(got, L, C, T, Tc, bins)
+    back = oracle.deserialize(got, L, C, T, Tc, bins, S)
     assert np.array_equal(back["cdf"], cdf)
     assert np.array_equal(back["max1"], max1)
     assert np.array_equal(back["stream_len"], stream_len)
+    with pytest.raises(oracle.OracleError):  # the header's S must match the reader's
+        oracle.deserialize(got, L, C, T, Tc, bins, 1 if S_stored == 2 else 2)
     assert back["slab_off"].tolist() == [0, 3, 5, 5, 5]
     assert back["payload_bytes"] == 5
 
