@@ -325,6 +325,69 @@ def streaming_leg(kvc, cfg, descs, bufs, max_level_bytes, steps):
             "timing": "wall clock of kvc_stream_encode (it returns with every container in host memory)"}
 
 
+def entropy_bound_bits(sym, L, T, C, A, span):
+    """Sum over CDF tables (spans of `span` tokens) and channels of N_g * H,
+    H the empirical entropy of the channel's symbols over the table's tokens:
+    the least payload a coder with one static model per table can reach, in
+    bits.  GPU bincount per (layer, K|V) row block."""
+    import math
+    import torch
+    ng = -(-T // span)
+    rows = sym[: 2 * L * T * C].view(2 * L, T, C)
+    grp = torch.arange(T, device=sym.device) // span
+    base = (grp[:, None] * C + torch.arange(C, device=sym.device)[None, :]) * A
+    nlogn = 0.0
+    for lk in range(2 * L):
+        cnt = torch.bincount((base + rows[lk].long()).view(-1), minlength=ng * C * A).double()
+        nz = cnt[cnt > 0]
+        nlogn += float((nz * torch.log2(nz)).sum())
+    sizes = [min(span, T - g * span) for g in range(ng)]
+    return 2 * L * C * sum(n * math.log2(n) for n in sizes) - nlogn
+
+
+def cdf_sharing_leg(kvc, cfg, kvt, buf, stream):
+    """CDF tables shared by N consecutive chunks (N = 1: the page's per-chunk
+    tables; 4; all: one table per (layer, K|V, channel)): container, payload
+    and table bits per element, the payload against the entropy bound of the
+    same tables, and the stage times of one run each (HIP events).  Outside
+    the timed step; reuses the step's buffers (N = 1 has the most tables)."""
+    import torch
+    L, C, T, Tc = cfg.n_layers, cfg.n_channels, cfg.n_tokens, cfg.chunk_tokens
+    bins = cfg.bins()
+    n = cfg.n_elements
+    per_table = 2 * C * int((bins - 2).sum())  # compact bytes of one table of every (layer, K|V)
+    out = []
+    for label, N in (("1", 1), ("4", 4), ("all", 1 << 30)):
+        d = kvc.Desc(L, C, T, bins, Tc, cdf_chunks=N)
+        b = dataclasses.replace(buf, desc=d)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        kvc.kvc_quantize(d, kvt, b.sym, b.max1, b.cdf, b.dev_status, stream)
+        e[1].record(stream)
+        kvc.kvc_encode(d, b.sym, b.cdf, b.scratch, b.stream_len, b.slab_off, b.payload, b.dev_status, stream)
+        e[2].record(stream)
+        kvc.decode(b, stream=stream)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        if int(b.dev_status.item()):
+            raise RuntimeError(f"CDF sharing leg: device status {int(b.dev_status.item()):#x} at N = {label}")
+        pay = int(b.slab_off[d.n_slabs].item())
+        s_eff = min(N, d.n_chunks) if d.n_chunks else 1  # chunks per table as stored
+        ng = -(-d.n_chunks // s_eff)
+        assert d.cdf_bytes == ng * 2 * L * C * d.alphabet * 2
+        bound = entropy_bound_bits(b.sym, L, T, C, d.alphabet, max(min(s_eff * Tc, T), 1))
+        out.append({"chunks_per_table": label, "tables_per_layer_kv": ng,
+                    "container_bits_per_elem": round(8 * d.container_bytes(pay) / n, 4),
+                    "payload_bits_per_elem": round(8 * pay / n, 4),
+                    "table_bits_per_elem": round(8 * ng * per_table / n, 4),
+                    "entropy_bound_bits_per_elem": round(bound / n, 4),
+                    "payload_over_bound": round(8 * pay / bound, 4) if bound > 0 else None,
+                    "quantize_cdf_ms": round(e[0].elapsed_time(e[1]), 4),
+                    "encode_ms": round(e[1].elapsed_time(e[2]), 4),
+                    "decode_ms": round(e[2].elapsed_time(e[3]), 4)})
+    return {"tables": out, "timing": "one run each, HIP events; quantize_cdf includes the tables"}
+
+
 def delta_leg(kvc, d, buf, cfg, kvt, stream, steps):
     """Token-delta coding (anchors every G chunk-relative tokens) in front of
     the codec: container size and relative RMS error after forward, encode,
@@ -592,6 +655,7 @@ def main():
         res["quality_levels"] = levels_leg(kvc, cfg, kvt, stream, args.steps)
         res["streaming"] = res["quality_levels"].pop("streaming")
         res["token_delta"] = delta_leg(kvc, d, buf, cfg, kvt, stream, args.steps)
+        res["cdf_sharing"] = cdf_sharing_leg(kvc, cfg, kvt, buf, stream)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, kv_np)
     print(json.dumps(res), flush=True)

@@ -40,7 +40,7 @@ class KvcDesc(ctypes.Structure):
         ("n_channels", ctypes.c_int32),
         ("n_tokens", ctypes.c_int64),
         ("chunk_tokens", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("cdf_chunks", ctypes.c_int32),
         ("bins", ctypes.POINTER(ctypes.c_int32)),
     ]
 
@@ -130,12 +130,13 @@ class Desc:
     """A kvc_desc plus the host bins array it points to."""
 
     def __init__(self, n_layers: int, n_channels: int, n_tokens: int, bins,
-                 chunk_tokens: int = 256):
+                 chunk_tokens: int = 256, cdf_chunks: int = 0):
+        """cdf_chunks: chunks sharing one CDF table (0 or 1: a table per chunk)."""
         self.bins = np.ascontiguousarray(np.asarray(bins, dtype=np.int32).reshape(n_layers, 2))
-        self.c = KvcDesc(n_layers, n_channels, n_tokens, chunk_tokens, 0,
+        self.c = KvcDesc(n_layers, n_channels, n_tokens, chunk_tokens, cdf_chunks,
                          self.bins.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
         self.n_layers, self.n_channels, self.n_tokens = n_layers, n_channels, n_tokens
-        self.chunk_tokens = chunk_tokens
+        self.chunk_tokens, self.cdf_chunks = chunk_tokens, cdf_chunks
 
     @property
     def ref(self):

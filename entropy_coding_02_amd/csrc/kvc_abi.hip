@@ -32,7 +32,7 @@ int make_geometry(const kvc_desc *d, Geometry &g)
     if (d->n_layers < 1 || d->n_layers > KVC_MAX_LAYERS) return KVC_ERR_ARG;
     if (d->n_channels < 1 || d->n_channels > 16384) return KVC_ERR_ARG;
     if (d->n_tokens < 0 || d->n_tokens > ((int64_t)1 << 40)) return KVC_ERR_ARG;
-    if (d->chunk_tokens < 1 || d->chunk_tokens > 65535 || d->reserved != 0) return KVC_ERR_ARG;
+    if (d->chunk_tokens < 1 || d->chunk_tokens > 65535 || d->cdf_chunks < 0) return KVC_ERR_ARG;
     memset(&g, 0, sizeof(g));
     KParams &p = g.p;
     int A = 0;
@@ -51,6 +51,10 @@ int make_geometry(const kvc_desc *d, Geometry &g)
     int64_t NC = (p.T + p.Tc - 1) / p.Tc;
     if (NC > INT32_MAX) return KVC_ERR_ARG;
     p.NC = (int32_t)NC;
+    p.S = (int32_t)(d->cdf_chunks <= 1 ? 1 : std::min<int64_t>(d->cdf_chunks, std::max<int64_t>(NC, 1)));
+    p.NG = (int32_t)((NC + p.S - 1) / p.S);
+    p.j0 = 0;
+    if (std::min<int64_t>((int64_t)p.S * p.Tc, p.T) > KVC_MAX_TABLE_TOKENS) return KVC_ERR_ARG;
     p.last_nj = NC ? (int32_t)(p.T - (NC - 1) * p.Tc) : 0;
     p.rn_full = 1.0 / (double)p.Tc;
     p.rn_last = p.last_nj ? 1.0 / (double)p.last_nj : 0.0;
@@ -68,6 +72,28 @@ int make_geometry(const kvc_desc *d, Geometry &g)
 }
 
 bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+// The tensor as the CDF producers see it: its tables as chunks of S * Tc
+// tokens, one table each (the tables are the per-chunk CDFs of that coarser
+// chunking; quantization is per row and does not see chunks).
+KParams table_params(const KParams &p)
+{
+    KParams t = p;
+    t.Tc = p.S * p.Tc;  // <= KVC_MAX_TABLE_TOKENS when S > 1 (make_geometry)
+    if (p.S > 1 && t.Tc > p.T) t.Tc = (int32_t)std::max<int64_t>(p.T, 1);
+    t.NC = p.NG;
+    t.S = 1;
+    t.NG = p.NG;
+    t.last_nj = p.NG ? (int32_t)(p.T - (int64_t)(p.NG - 1) * t.Tc) : 0;
+    t.rn_full = 1.0 / (double)t.Tc;
+    t.rn_last = t.last_nj ? 1.0 / (double)t.last_nj : 0.0;
+    t.n_slabs = (int64_t)p.NG * 2 * p.L;
+    return t;
+}
+
+// Whether the CDF kernels with 16-bit counters (the fused quantize + CDF pass,
+// k_cdf_wide) can count a table of these params.
+bool short_tables(const KParams &t) { return t.Tc <= 65535; }
 
 // Device address of `scratch` on the current device: looked up with
 // hipGetSymbolAddress on the first call on each device (with that device
@@ -209,7 +235,7 @@ int64_t kvc_cdf_bytes(const kvc_desc *desc)
 {
     Geometry g;
     int rc = make_geometry(desc, g);
-    return rc == KVC_OK ? g.p.n_slabs * g.p.C * g.p.A * 2 : rc;
+    return rc == KVC_OK ? (int64_t)g.p.NG * 2 * g.p.L * g.p.C * g.p.A * 2 : rc;
 }
 
 int64_t kvc_scratch_bytes(const kvc_desc *desc)
@@ -238,12 +264,13 @@ int kvc_quantize(const kvc_desc *desc, const uint16_t *kv, uint8_t *sym, uint16_
         return KVC_ERR_ARG;
     hipStream_t s = (hipStream_t)stream;
     const bool vec8 = (g.p.C % 8 == 0) && aligned(kv, 16) && aligned(sym, 8);
-    // The fused pass runs one block per slab: with fewer slabs than the chip
+    const KParams t = table_params(g.p);
+    // The fused pass runs one block per table: with fewer tables than the chip
     // has compute units, two passes spread over more blocks finish sooner.
-    if (cdf && vec8 && aligned(cdf, 16) && g.p.n_slabs >= 256 && quant_cdf_fused_ok(g.p))
-        return launch_status(launch_quant_cdf(kv, sym, max1, cdf, g.p, dev_status, s));
+    if (cdf && vec8 && aligned(cdf, 16) && t.n_slabs >= 256 && short_tables(t) && quant_cdf_fused_ok(t))
+        return launch_status(launch_quant_cdf(kv, sym, max1, cdf, t, dev_status, s));
     hipError_t e = launch_quantize_rows(kv, sym, max1, g.p, dev_status, vec8, s);
-    if (e == hipSuccess && cdf) e = launch_cdf(sym, cdf, g.p, dev_status, s);
+    if (e == hipSuccess && cdf) e = launch_cdf(sym, cdf, t, dev_status, s);
     return launch_status(e);
 }
 
@@ -262,15 +289,16 @@ int kvc_quantize_levels(const kvc_desc *levels, int32_t n_levels, const uint16_t
             return KVC_ERR_ARG;
         if (!sym[l] || !cdf[l] || !aligned(sym[l], 4) || !aligned(cdf[l], 4)) return KVC_ERR_ARG;
     }
-    const KParams &p = g[0].p;
+    const KParams p = table_params(g[0].p);
     if (p.n_rows == 0) return KVC_OK;
     if (!kv || !max1 || !aligned(kv, 4) || !aligned(max1, 2) || (dev_status && !aligned(dev_status, 4)))
         return KVC_ERR_ARG;
     LevelParams lv;
     memset(&lv, 0, sizeof(lv));
     lv.n = n_levels;
-    bool fused = p.n_slabs >= 256 && aligned(kv, 16);
+    bool fused = p.n_slabs >= 256 && short_tables(p) && aligned(kv, 16);
     for (int l = 0; l < n_levels; ++l) {
+        fused = fused && g[l].p.S == g[0].p.S;  // one table geometry for every level
         lv.A[l] = g[l].p.A;
         lv.sym[l] = sym[l];
         lv.cdf[l] = cdf[l];
@@ -295,7 +323,7 @@ int kvc_cdf(const kvc_desc *desc, const uint8_t *sym, uint16_t *cdf, int32_t *de
     if (g.p.n_rows == 0) return KVC_OK;
     if (!sym || !cdf || !aligned(sym, 4) || !aligned(cdf, 4) || (dev_status && !aligned(dev_status, 4)))
         return KVC_ERR_ARG;
-    return launch_status(launch_cdf(sym, cdf, g.p, dev_status, (hipStream_t)stream));
+    return launch_status(launch_cdf(sym, cdf, table_params(g.p), dev_status, (hipStream_t)stream));
 }
 
 int kvc_encode(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf, void *scratch,
@@ -424,7 +452,7 @@ int kvc_serialize_chunk(const kvc_desc *desc, int64_t chunk, const uint16_t *cdf
         return KVC_ERR_ARG;
     if (out_cap < container_total(container_layout(gc.p), 0)) return KVC_ERR_CAPACITY;
     const int64_t twoL = 2 * (int64_t)g.p.L;
-    const ChunkSrc src{cdf + chunk * twoL * g.p.C * g.p.A, max1, g.p.T, chunk * (int64_t)g.p.Tc,
+    const ChunkSrc src{cdf + (chunk / g.p.S) * twoL * g.p.C * g.p.A, max1, g.p.T, chunk * (int64_t)g.p.Tc,
                        stream_len + chunk * twoL * g.p.Tc, slab_off + chunk * twoL, payload};
     return launch_status(launch_serialize_chunk(src, out, out_cap, gc.p, dev_status, (hipStream_t)stream));
 }
@@ -498,9 +526,12 @@ int kvc_stream_encode(const kvc_desc *levels, int32_t n_levels, const int32_t *c
         du.n_tokens = std::min<int64_t>(un.jb * P.Tc, P.T) - un.ja * P.Tc;
         Geometry gu;
         if (make_geometry(&du, gu) != KVC_OK) return KVC_ERR_ARG;
-        gu.p.Ts = P.T;  // the unit's rows sit in the whole tensor's row blocks
+        gu.p.Ts = P.T;     // the unit's rows sit in the whole tensor's row blocks,
+        gu.p.S = pl.S;     // and its chunks read the whole tensor's tables
+        gu.p.NG = pl.NG;
+        gu.p.j0 = un.ja;
         const uint8_t *sym_u = sym[l] + un.ja * P.Tc * P.C;
-        const uint16_t *cdf_u = cdf[l] + un.ja * twoL * P.C * pl.A;
+        const uint16_t *cdf_u = cdf[l];
         uint8_t *slots = wk;
         uint64_t *slab_total = (uint64_t *)(wk + gu.slot_area);
         const bool vec16 = (P.C % 16 == 0) && aligned(sym_u, 16);
@@ -515,7 +546,7 @@ int kvc_stream_encode(const kvc_desc *levels, int32_t n_levels, const int32_t *c
             dc.n_tokens = std::min<int64_t>((j + 1) * P.Tc, P.T) - j * P.Tc;
             Geometry gc;
             if (make_geometry(&dc, gc) != KVC_OK) return KVC_ERR_ARG;
-            const ChunkSrc src{cdf[l] + j * twoL * P.C * pl.A, max1, P.T, j * (int64_t)P.Tc,
+            const ChunkSrc src{cdf[l] + (j / pl.S) * twoL * P.C * pl.A, max1, P.T, j * (int64_t)P.Tc,
                                len_u + k * twoL * P.Tc, off_u + k * twoL, pay_u};
             e = launch_serialize_chunk(src, st + k * sl.chunk_cap, sl.chunk_cap, gc.p, dev_status, cs);
         }

@@ -141,7 +141,8 @@ hipError_t launch_cdf(const uint8_t *sym, uint16_t *cdf, const KParams &p, int32
                       hipStream_t stream)
 {
     if (p.n_slabs == 0) return hipSuccess;
-    if (p.C % 4 == 0 && p.A <= 64 && ((uintptr_t)sym & 3) == 0 && ((uintptr_t)cdf & 3) == 0) {
+    // k_cdf_wide counts in 16-bit halves: tables of at most 65535 tokens
+    if (p.Tc <= 65535 && p.C % 4 == 0 && p.A <= 64 && ((uintptr_t)sym & 3) == 0 && ((uintptr_t)cdf & 3) == 0) {
         const size_t lds = sizeof(uint32_t) * (256 * (size_t)(p.A / 2 + 1) + 64);
         dim3 grid((unsigned)(((p.C + 255) / 256) * p.n_slabs));
         if (grid.x <= KVC_CDF_WIDE_TALL_MAX_BLOCKS)

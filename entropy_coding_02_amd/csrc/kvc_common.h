@@ -20,6 +20,7 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 // Everything a kernel needs to know about the problem, passed by value.
 // Slab s = (chunk j, layer l, K|V kv) with lk = 2*l + kv; j = s / (2L).
+// CDF table (g, l, kv) serves the slabs of chunks j with floor(j / S) = g.
 struct KParams {
     int64_t T;          // tokens
     int64_t Ts;         // token stride of the (layer, K|V) row blocks in kv and sym: T, or the
@@ -30,6 +31,10 @@ struct KParams {
     int64_t slot_bytes; // encoder scratch bytes per stream
     int32_t L, C, A, Tc;
     int32_t NC;         // chunks
+    int32_t S;          // chunks per CDF table (1: a table per chunk)
+    int32_t NG;         // CDF tables per (layer, K|V): ceil(NC / S)
+    int64_t j0;         // chunk index of chunk 0 within the tensor whose tables the kernels
+                        // read (0; else the first chunk of a run encoded as a tensor)
     int32_t last_nj;    // tokens of the last chunk
     double rn_full;     // 1 / Tc, rounded to double
     double rn_last;     // 1 / last_nj, rounded to double (0 if there are no tokens)
@@ -39,6 +44,7 @@ struct KParams {
 struct SlabGeom {
     int64_t row0;    // row index of the slab's first token: lk*Ts + j*Tc
     int64_t sid0;    // stream id of the slab's first token
+    int64_t tab;     // CDF table of the slab: floor((j + j0) / S) * 2L + lk
     int32_t nj;      // tokens in the slab
     int32_t lk;      // 2*l + kv
     double rn;       // 1 / nj, rounded to double
@@ -54,21 +60,25 @@ __device__ __forceinline__ SlabGeom slab_geom(const KParams &p, int64_t s)
     g.rn = (j == p.NC - 1) ? p.rn_last : p.rn_full;
     g.row0 = (int64_t)g.lk * p.Ts + j * p.Tc;
     g.sid0 = j * twoL * p.Tc + (int64_t)g.lk * g.nj;
+    g.tab = (p.S == 1 ? j + p.j0 : (j + p.j0) / p.S) * twoL + g.lk;
     return g;
 }
 
 // CDF entry k of a row whose counts below k sum to Ck, over N tokens, with
 // K = 65536 - A:  k + floor(Ck * K / N), rn = 1/N rounded to double.
-// Exact: x = Ck * K < 2^32 and N < 2^16, so x * rn is x/N within a relative
-// 2^-52 (under 2^-36 absolutely).  If x/N is an integer m the biased
-// product lands in (m, m + 2^-17); otherwise x/N is at least 1/N >= 2^-16
-// away from both neighbouring integers, and the product plus 2^-18 stays
-// strictly between them.  The integer part is the floor.
+// Exact for N <= 2^21: x = Ck * K < 2^37 is exact in fp64, and x * rn is x/N
+// within a relative 2^-52 (x/N <= K < 2^16: under 2^-36 absolutely).  If x/N
+// is an integer m the biased product lands in (m, m + 2^-21); otherwise x/N
+// is at least 1/N >= 2^-21 away from both neighbouring integers, and the
+// product plus 2^-22 stays strictly between them.  The integer part is the floor.
 __device__ __forceinline__ uint32_t kvc_cdf_entry(uint32_t k, uint32_t Ck, uint32_t K, double rn)
 {
-    const double q = (double)(Ck * K) * rn;
-    return k + (uint32_t)(q + 0x1p-18);
+    const double q = (double)((uint64_t)Ck * K) * rn;
+    return k + (uint32_t)(q + 0x1p-22);
 }
+
+// Largest number of tokens one CDF table may count (kvc_cdf_entry's bound).
+constexpr int64_t KVC_MAX_TABLE_TOKENS = (int64_t)1 << 21;
 
 __device__ __forceinline__ float kvc_h2f(uint32_t bits)
 {

@@ -6,12 +6,13 @@
 // bytes; padding bytes are zero):
 //   header   64 bytes: u32 magic 0x3143564B ("KVC1"), u32 version 1, u32 L,
 //            u32 C, u64 T, u32 Tc, u32 A, u64 payload_bytes, u64 total_bytes,
-//            16 zero bytes
+//            u32 S (chunks per CDF table), 12 zero bytes
 //   bins     u8 [L][2]
-//   cdf      per slab (chunk, layer, K|V) in slab order, per channel: entries
-//            1 .. b-2 of the row as u16 (b = the slab's bins).  Entry 0 is 0
-//            and, since a quantizer with b bins emits symbols up to b-2 only,
-//            entry k >= b-1 is k + 65536 - A: both are implied.
+//   cdf      per table (group of S chunks, layer, K|V) in that order, per
+//            channel: entries 1 .. b-2 of the row as u16 (b = the layer's
+//            bins).  Entry 0 is 0 and, since a quantizer with b bins emits
+//            symbols up to b-2 only, entry k >= b-1 is k + 65536 - A: both
+//            are implied.
 //   max1     u16 [L][2][T]
 //   lengths  u16 [n_streams]
 //   payload  payload_bytes bytes, the section at least 16 bytes long
@@ -53,22 +54,23 @@ __global__ void k_ser_header(const uint64_t *__restrict__ off0, const uint64_t *
         h[7] = (uint32_t)p.A;
         *(uint64_t *)(out + 32) = pb;
         *(uint64_t *)(out + 40) = (uint64_t)total;
+        h[12] = (uint32_t)p.S;
         if (total > out_cap) kvc_flag(status, KVC_DEV_PAYLOAD_OVERFLOW);
     }
-    if (tid >= 12 && tid < 16) ((uint32_t *)out)[tid] = 0;
+    if (tid >= 13 && tid < 16) ((uint32_t *)out)[tid] = 0;
     for (int64_t i = cl.bins + tid; i < cl.cdf; i += blockDim.x) {
         const int64_t lk = i - cl.bins;
         out[i] = lk < 2 * p.L ? (uint8_t)(2 * (p.maxq[lk] + 1)) : 0;
     }
 }
 
-// The compact CDF section: one block per slab.  Threads walk the slab's
-// compact entries (coalesced u16 stores) and check its implied ones.
+// The compact CDF section: one block per table (g, l, kv).  Threads walk the
+// table's compact entries (coalesced u16 stores) and check its implied ones.
 __global__ __launch_bounds__(256) void k_ser_cdf(const uint16_t *__restrict__ cdf,
                                                  uint8_t *__restrict__ out, KParams p,
                                                  ContainerLayout cl, int32_t *status)
 {
-    const int64_t slab = blockIdx.x;
+    const int64_t slab = blockIdx.x;  // table index g * 2L + lk
     const int64_t twoL = 2 * (int64_t)p.L;
     const int64_t j = slab / twoL;
     const int lk = (int)(slab - j * twoL);
@@ -91,9 +93,9 @@ __global__ __launch_bounds__(256) void k_ser_cdf(const uint16_t *__restrict__ cd
         bad |= rows[c * A + k] != want;
     }
     if (bad) kvc_flag(status, KVC_DEV_BAD_CDF);
-    // zero padding after the last slab's rows
-    if (slab == p.n_slabs - 1 && threadIdx.x == 0) {
-        const int64_t end = cl.cdf + 2 * (int64_t)p.NC * cl.chunk_entries;
+    // zero padding after the last table's rows
+    if (slab == (int64_t)p.NG * twoL - 1 && threadIdx.x == 0) {
+        const int64_t end = cl.cdf + 2 * (int64_t)p.NG * cl.chunk_entries;
         for (int64_t i = end; i < cl.max1; ++i) out[i] = 0;
     }
 }
@@ -163,7 +165,7 @@ __global__ void k_deser_check(const uint8_t *__restrict__ in, int64_t in_bytes, 
         const uint64_t total = *(const uint64_t *)(in + 40);
         bad = h[0] != KVC_MAGIC || h[1] != 1 || h[2] != (uint32_t)p.L || h[3] != (uint32_t)p.C ||
               *(const uint64_t *)(in + 16) != (uint64_t)p.T || h[6] != (uint32_t)p.Tc ||
-              h[7] != (uint32_t)p.A || pb > (uint64_t)in_bytes ||
+              h[7] != (uint32_t)p.A || h[12] != (uint32_t)p.S || pb > (uint64_t)in_bytes ||
               total != (uint64_t)container_total(cl, (int64_t)pb) || total > (uint64_t)in_bytes;
     }
     for (int i = threadIdx.x; i < 2 * p.L; i += blockDim.x)
@@ -171,8 +173,8 @@ __global__ void k_deser_check(const uint8_t *__restrict__ in, int64_t in_bytes, 
     if (bad) kvc_flag(status, KVC_DEV_BAD_CONTAINER);
 }
 
-// The full [NC][L][2][C][A] table from the compact rows: one block per slab,
-// a thread per table entry (coalesced u16 stores).
+// The full [NG][L][2][C][A] tables from the compact rows: one block per
+// table, a thread per table entry (coalesced u16 stores).
 __global__ __launch_bounds__(256) void k_deser_cdf(const uint8_t *__restrict__ in,
                                                    uint16_t *__restrict__ cdf, KParams p,
                                                    ContainerLayout cl)
@@ -219,7 +221,7 @@ ContainerLayout container_layout(const KParams &p)
     for (int i = 0; i < 2 * p.L; ++i) cl.chunk_entries += (int64_t)p.C * 2 * p.maxq[i];
     cl.bins = 64;
     cl.cdf = r16(cl.bins + 2 * (int64_t)p.L);
-    cl.max1 = r16(cl.cdf + 2 * (int64_t)p.NC * cl.chunk_entries);
+    cl.max1 = r16(cl.cdf + 2 * (int64_t)p.NG * cl.chunk_entries);
     cl.len = r16(cl.max1 + 2 * p.n_rows);
     cl.pay = r16(cl.len + 2 * p.n_streams);
     return cl;
@@ -232,9 +234,10 @@ hipError_t launch_serialize(const uint16_t *cdf, const uint16_t *max1, const uin
     const ContainerLayout cl = container_layout(p);
     hipLaunchKernelGGL(k_ser_header, dim3(1), dim3(64), 0, stream, (const uint64_t *)nullptr,
                        slab_off + p.n_slabs, out, out_cap, p, cl, status);
-    if (p.n_slabs > 0)
-        hipLaunchKernelGGL(k_ser_cdf, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, cdf, out, p,
-                           cl, status);
+    const int64_t n_tables = (int64_t)p.NG * 2 * p.L;
+    if (n_tables > 0)
+        hipLaunchKernelGGL(k_ser_cdf, dim3((unsigned)n_tables), dim3(256), 0, stream, cdf, out, p, cl,
+                           status);
     const int64_t rows_b = 2 * p.n_rows, lens_b = 2 * p.n_streams;
     const uint64_t *none = nullptr;
     hipLaunchKernelGGL(k_copy_section, dim3(grid_for(rows_b, 1024)), dim3(256), 0, stream,
@@ -253,7 +256,8 @@ hipError_t launch_serialize(const uint16_t *cdf, const uint16_t *max1, const uin
 hipError_t launch_serialize_chunk(const ChunkSrc &src, uint8_t *out, int64_t out_cap, const KParams &p,
                                   int32_t *status, hipStream_t stream)
 {
-    // p describes the chunk as a tensor of its own: T = N_j, one chunk, 2L slabs
+    // p describes the chunk as a tensor of its own: T = N_j, one chunk, 2L slabs,
+    // one table per slab (S = 1)
     const ContainerLayout cl = container_layout(p);
     const int64_t twoL = 2 * (int64_t)p.L;
     const uint64_t *off0 = src.off, *off1 = src.off + twoL;
@@ -281,9 +285,9 @@ hipError_t launch_deserialize(const uint8_t *in, int64_t in_bytes, uint16_t *cdf
 {
     const ContainerLayout cl = container_layout(p);
     hipLaunchKernelGGL(k_deser_check, dim3(1), dim3(64), 0, stream, in, in_bytes, p, cl, status);
-    if (p.n_slabs > 0)
-        hipLaunchKernelGGL(k_deser_cdf, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, in, cdf, p,
-                           cl);
+    const int64_t n_tables = (int64_t)p.NG * 2 * p.L;
+    if (n_tables > 0)
+        hipLaunchKernelGGL(k_deser_cdf, dim3((unsigned)n_tables), dim3(256), 0, stream, in, cdf, p, cl);
     const int64_t rows_b = 2 * p.n_rows, lens_b = 2 * p.n_streams;
     if (rows_b > 0) {
         const uint64_t *none = nullptr;

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ payl
     const float m = (ODT >= 0) ? kvc_h2f(max1[row]) : 0.0f;
     uint32_t bad = 0;
     uint8_t *so = (OUT & OUT_SYM) ? sym_out + row * C : nullptr;
-    const uint16_t *srows = cdf + slab * C * A;
+    const uint16_t *srows = cdf + g.tab * C * A;
     const int ntiles = (C + CT - 1) / CT;
     // search the row, then one 8-byte read: the symbol's (start, frequency) and
     // its dequantization value lv
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     const float m = (ODT >= 0) ? kvc_h2f(max1[row]) : 0.0f;
     uint32_t bad = 0;
     uint8_t *so = (OUT & OUT_SYM) ? sym_out + row * C : nullptr;
-    const uint16_t *srows = cdf + slab * C * A;
+    const uint16_t *srows = cdf + g.tab * C * A;
     const int ntiles = (C + CT - 1) / CT;
     const lds_u32 *rec = recs;
     // the mode part of tile channel cl's record (a broadcast read: every lane
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(256) void k_decode_group(const uint8_t *__restrict_
     const float m = (ODT >= 0) ? kvc_h2f(max1[row]) : 0.0f;
     uint32_t bad = 0;
     uint8_t *so = (OUT & OUT_SYM) ? sym_out + row * C : nullptr;
-    const uint16_t *srows = cdf + slab * C * A;
+    const uint16_t *srows = cdf + g.tab * C * A;
     const int ntiles = (C + CT - 1) / CT;
     const uint32_t amax = (uint32_t)A - 1u;
     // this lane's slice of the key row of tile channel cl: keys [q E, q E + E)

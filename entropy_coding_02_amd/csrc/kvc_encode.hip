@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
     const bool active = lane < SPW && t < g.nj;
     const int64_t sid = g.sid0 + t;
     const uint8_t *q = sym + (g.row0 + (active ? t : 0)) * C;
-    const uint16_t *rows = cdf + slab * C * A;
+    const uint16_t *rows = cdf + g.tab * C * A;
     lds_u32 *const pairs = (lds_u32 *)lds;
     constexpr int sstride = ENC_SW + 16;
     lds_u8 *const stile = (lds_u8 *)(pairs + CT * A);
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(256) void k_encode_split(const uint8_t *__restrict_
     const int t = r0 + jj;
     const bool active = t < g.nj;
     const int C = p.C, A = p.A, B = C / 4, CQ = CH / 4, half = A / 2;
-    const uint32_t *rows = (const uint32_t *)(cdf + slab * C * A);  // A even: rows of A / 2 dwords
+    const uint32_t *rows = (const uint32_t *)(cdf + g.tab * C * A);  // A even: rows of A / 2 dwords
     const int P = CH * half, B2 = B * half;                           // pairs per chunk, per block
     uint8_t *const myslot = slots + ((int64_t)grp * 256 + sub * SPB + jj) * p.slot_bytes;
     const int sst = C + 16;  // symbol row stride (bytes)

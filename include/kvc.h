@@ -19,8 +19,10 @@
  *                                   of [CG] 3.2 with C = kv_heads * head_dim
  *   sym          [L][2][T][C]      uint8 symbols, in [0, bins-2]
  *   max1         [L][2][T]         fp16 bits: max |x| of each (layer, K|V, token) row
- *   cdf          [NC][L][2][C][A]  uint16 cumulative frequencies out of 65536;
- *                                   cdf[0] = 0, cdf[A] = 65536 is implicit
+ *   cdf          [NG][L][2][C][A]  uint16 cumulative frequencies out of 65536;
+ *                                   cdf[0] = 0, cdf[A] = 65536 is implicit; one table
+ *                                   per S consecutive chunks (S = 1: per chunk),
+ *                                   NG = ceil(NC / S)
  *   stream_len   [n_streams]       uint16 byte length of each stream
  *   slab_off     [n_slabs + 1]     uint64 payload offset of each slab's first stream
  *   payload      bytes of all streams back to back
@@ -28,7 +30,7 @@
  * layer l, K|V), slabs in (j, l, kv) order, n_slabs = 2*L*NC, and one stream
  * per (chunk, layer, K|V, token) in that order, n_streams = 2*L*T.  Stream
  * (j, l, kv, t) codes the C symbols of token j*chunk_tokens + t of (l, kv),
- * channel 0 first, with the CDF rows of slab (j, l, kv).
+ * channel 0 first, with the CDF rows of table (floor(j / S), l, kv).
  *
  * Conventions:
  *   - The caller allocates every buffer.  The library allocates no memory and
@@ -78,7 +80,11 @@ typedef struct kvc_desc {
     int32_t n_channels;   /* C = kv_heads * head_dim, 1..16384 */
     int64_t n_tokens;     /* T >= 0 */
     int32_t chunk_tokens; /* tokens per chunk, 1..65535 ([CG] 2.3 step 3 uses 256) */
-    int32_t reserved;     /* must be 0 */
+    int32_t cdf_chunks;   /* S, chunks sharing one CDF table: 0 or 1 = a table per chunk
+                             (the page's reading); S > 1 = groups of S consecutive chunks;
+                             S >= NC = one table per (layer, K|V, channel).  Taken as at
+                             most NC; a table may count at most 2^21 tokens
+                             (min(S * chunk_tokens, T) <= 2^21) */
     const int32_t *bins;  /* HOST [L][2] (K, V) bin counts, even, 4..256 ([CG] 2.2) */
 } kvc_desc;
 

@@ -15,11 +15,12 @@ def say(msg: str):
 
 
 def run_gpu(kv_np: np.ndarray, bins: np.ndarray, Tc: int, fused: bool = True,
-            out_dtype: int = kvc.KVC_F16, exact_payload: bool = False, keep_device=False):
+            out_dtype: int = kvc.KVC_F16, exact_payload: bool = False, keep_device=False,
+            cdf_chunks: int = 0):
     """kv_np: uint16 fp16 bits [L][2][T][C].  Returns a dict of numpy arrays."""
     import torch
     L, _, T, C = kv_np.shape
-    d = kvc.Desc(L, C, T, bins, Tc)
+    d = kvc.Desc(L, C, T, bins, Tc, cdf_chunks=cdf_chunks)
     buf = kvc.alloc(d, out_dtype=out_dtype, with_dec_sym=True)
     kv = torch.from_numpy(kv_np.view(np.int16)).cuda() if kv_np.size else torch.empty(1, dtype=torch.int16, device="cuda")
     kvc.encode(buf, kv, fused_cdf=fused)
@@ -45,7 +46,7 @@ def run_gpu(kv_np: np.ndarray, bins: np.ndarray, Tc: int, fused: bool = True,
         desc=d, A=d.alphabet, enc_status=enc_status, dec_status=dec_status,
         sym=buf.sym[:n_el].cpu().numpy().reshape(L, 2, T, C),
         max1=buf.max1[: L * 2 * T].cpu().numpy().view(np.uint16).reshape(L, 2, T),
-        cdf=buf.cdf[: d.cdf_bytes // 2].cpu().numpy().view(np.uint16).reshape(d.n_chunks, L, 2, C, d.alphabet),
+        cdf=buf.cdf[: d.cdf_bytes // 2].cpu().numpy().view(np.uint16).reshape(-1, L, 2, C, d.alphabet),
         stream_len=buf.stream_len[: d.n_streams].cpu().numpy().view(np.uint16),
         slab_off=slab_off,
         payload=buf.payload[:total].cpu().numpy(),

@@ -110,11 +110,15 @@ def test_container_sizes_agree_with_the_oracle(lib):
     cases += [(3, 40, 0, 256, np.array([[32, 16], [8, 6], [256, 4]], np.int32)),
               (1, 7, 70, 32, np.array([[16, 16]], np.int32))]
     for L, C, T, Tc, bins in cases:
-        d = kvc.Desc(L, C, T, bins, Tc)
-        assert d.container_payload_offset == oracle.container_payload_offset(L, C, T, Tc, bins)
-        assert d.container_payload_offset % 16 == 0
-        for pb in (0, 1, 15, 16, 17, 123457):
-            assert d.container_bytes(pb) == oracle.container_bytes(L, C, T, Tc, bins, pb)
+        for S in (0, 1, 4, 1 << 30):  # a table per chunk (0 and 1), per 4 chunks, per tensor
+            d = kvc.Desc(L, C, T, bins, Tc, cdf_chunks=S)
+            So = max(S, 1)
+            assert d.container_payload_offset == oracle.container_payload_offset(L, C, T, Tc, bins, So)
+            assert d.container_payload_offset % 16 == 0
+            for pb in (0, 1, 15, 16, 17, 123457):
+                assert d.container_bytes(pb) == oracle.container_bytes(L, C, T, Tc, bins, pb, So)
+            NG = oracle.tables_of(T, Tc, So)[1]
+            assert d.cdf_bytes == NG * 2 * L * C * int(np.max(bins)) * 2
 
 
 def test_container_calls_reject_bad_arguments(lib):
@@ -172,3 +176,15 @@ def test_stream_work_bytes_and_argument_checks(lib):
         bad = levels.copy()
         bad[7] = lv
         assert call(bad.ctypes.data) == kvc.KVC_ERR_ARG
+
+
+def test_shared_table_limits(lib):
+    """cdf_chunks < 0 is refused; a table may count at most 2^21 tokens."""
+    b = np.full((1, 2), 16, np.int32)
+    assert kvc.Desc(1, 8, 100, b, 10, cdf_chunks=-1).c and \
+        lib.kvc_cdf_bytes(kvc.Desc(1, 8, 100, b, 10, cdf_chunks=-1).ref) == kvc.KVC_ERR_ARG
+    T = (1 << 21) + 256
+    assert lib.kvc_cdf_bytes(kvc.Desc(1, 8, T, b, 256, cdf_chunks=1 << 20).ref) == kvc.KVC_ERR_ARG
+    ok = kvc.Desc(1, 8, T, b, 256, cdf_chunks=(1 << 21) // 256)  # exactly 2^21 tokens per table
+    assert ok.cdf_bytes == 2 * 2 * 8 * 16 * 2
+    assert lib.kvc_cdf_bytes(kvc.Desc(1, 8, 1 << 21, b, 256, cdf_chunks=1 << 30).ref) > 0
