@@ -19,7 +19,9 @@ from typing import List, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libkvgen.so")
+# KVC_SANITIZE=1: a copy built with AddressSanitizer and UndefinedBehaviorSanitizer (clang).
+SANITIZE = os.environ.get("KVC_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_HERE, "libkvgen_san.so" if SANITIZE else "libkvgen.so")
 
 
 @dataclass(frozen=True)
@@ -112,7 +114,11 @@ def build(force: bool = False) -> str:
     src = os.path.join(_HERE, "kvgen.c")
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
         tmp = _LIB_PATH + f".tmp{os.getpid()}"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+        cc = ["gcc"]
+        if SANITIZE:
+            cc = ["/opt/rocm/llvm/bin/clang", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer", "-g", "-shared-libsan"]
+        subprocess.check_call([*cc, "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
                                "-ffp-contract=off", "-o", tmp, src, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH

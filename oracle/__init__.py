@@ -16,7 +16,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvc_oracle.c")
 _SRCS = [_SRC, os.path.join(_HERE, "kvc_container.c"), os.path.join(_HERE, "kvc_int8.c"),
          os.path.join(_HERE, "kvc_delta.c")]
-_LIB_PATH = os.path.join(_HERE, "liborc.so")
+# KVC_SANITIZE=1 builds and loads a copy compiled with AddressSanitizer and
+# UndefinedBehaviorSanitizer (clang, whose runtime the process must preload).
+SANITIZE = os.environ.get("KVC_SANITIZE") == "1"
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+             "-g", "-shared-libsan"]
+_LIB_PATH = os.path.join(_HERE, "liborc_san.so" if SANITIZE else "liborc.so")
 
 ORC_OK, ORC_ERR_ARG, ORC_ERR_NONFINITE, ORC_ERR_CAPACITY, ORC_ERR_CORRUPT = 0, -1, -2, -3, -4
 
@@ -29,7 +34,8 @@ def build(force: bool = False) -> str:
     newest = max([os.path.getmtime(f) for f in _SRCS] + [os.path.getmtime(hdr)])
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
         tmp = _LIB_PATH + f".tmp{os.getpid()}"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+        cc = ["/opt/rocm/llvm/bin/clang", *SAN_FLAGS] if SANITIZE else ["gcc"]
+        subprocess.check_call([*cc, "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
                                "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, *_SRCS, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH

@@ -16,7 +16,8 @@ from test_oracle_coder import _straddling_sequence, cdf_from_counts
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "hostsim", "hostsim.hip")
-LIB = os.path.join(HERE, "hostsim", "libhostsim.so")
+SANITIZE = os.environ.get("KVC_SANITIZE") == "1"  # host code with AddressSanitizer + UBSan
+LIB = os.path.join(HERE, "hostsim", "libhostsim_san.so" if SANITIZE else "libhostsim.so")
 HDR = os.path.join(os.path.dirname(HERE), "entropy_coding_02_amd", "csrc", "lane_coder.h")
 COMMON = os.path.join(os.path.dirname(HERE), "entropy_coding_02_amd", "csrc", "kvc_common.h")
 
@@ -26,8 +27,13 @@ def hs():
     newest = max(os.path.getmtime(SRC), os.path.getmtime(HDR), os.path.getmtime(COMMON))
     if not os.path.exists(LIB) or os.path.getmtime(LIB) < newest:
         tmp = LIB + f".tmp{os.getpid()}"
+        san = []
+        if SANITIZE:  # the host side only: each sanitizer flag goes to the host compilation
+            san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g",
+                   "-shared-libsan"]
         subprocess.check_call(["/opt/rocm/bin/hipcc", "-std=c++17", "-O2", "--offload-arch=gfx950",
-                               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *san,
                                "-fPIC", "-shared", "-o", tmp, SRC])
         os.replace(tmp, LIB)
     lib = ctypes.CDLL(LIB)
