@@ -49,9 +49,9 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also launch one elementwise kernel that reads and writes 256 MiB "
                          "(the reference for scaling the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
-                         "WRITE_SIZE) of a --calibrate-copy run into profiles/traffic.json")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("READ_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files of a --calibrate-copy "
+                         "run (READ_COUNTERS, then WRITE_COUNTERS) into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -61,6 +61,12 @@ COMMON = [CSRC + "kvc_common.h"]
 KERNEL_SOURCES = {
     "k_decode": [CSRC + "kvc_decode.hip", CSRC + "lane_coder.h", CSRC + "pair_tile.h"] + COMMON,
     "k_decode_group": [CSRC + "kvc_decode.hip", CSRC + "lane_coder.h", CSRC + "pair_tile.h"] + COMMON,
+    "k_decode_mode": [CSRC + "kvc_decode.hip", CSRC + "lane_coder.h", CSRC + "pair_tile.h"] + COMMON,
+    "k_quant_cdf_levels": [CSRC + "kvc_quantize.hip"] + COMMON,
+    "k_quantize_rows": [CSRC + "kvc_quantize.hip"] + COMMON,
+    "k_cdf_wide": [CSRC + "kvc_cdf.hip"] + COMMON,
+    "k_slab_sum": [CSRC + "kvc_encode.hip"] + COMMON,
+    "k_scan": [CSRC + "kvc_encode.hip"] + COMMON,
     "k_encode": [CSRC + "kvc_encode.hip", CSRC + "lane_coder.h", CSRC + "pair_tile.h"] + COMMON,
     "k_encode_split": [CSRC + "kvc_encode.hip", CSRC + "lane_coder.h", CSRC + "pair_tile.h"] + COMMON,
     "k_pack": [CSRC + "kvc_encode.hip"] + COMMON,
@@ -86,32 +92,67 @@ def kernel_key(name: str):
     return base.strip() if base.strip() in KERNEL_SOURCES else None
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, workload: str):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each hot kernel, scaled by
-    what the same counters read for the COPY_BYTES copy kernel, into
-    profiles/traffic.json."""
+READ_COUNTERS = ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
+                 "TCC_EA0_RDREQ_128B_sum"]
+WRITE_COUNTERS = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_RDREQ_DRAM_sum",
+                  "TCC_EA0_WRREQ_DRAM_sum"]
+
+
+def summarize_pmc(read_csv: str, write_csv: str, workload: str):
+    """HBM bytes per dispatch of each hot kernel from two rocprofv3 --pmc runs
+    of the L2-to-memory request counters (READ_COUNTERS, then WRITE_COUNTERS):
+    reads weighted by request size (32 / 64 / 128 bytes), writes as 32- and
+    64-byte requests, and the share of requests that went to DRAM.  The
+    --calibrate-copy kernel (COPY_BYTES read and written) gives the scale that
+    turns the weighted counts into bytes (it should be about 1).  Medians over
+    dispatches, into profiles/traffic.json."""
     import csv
 
-    def per_kernel(path, counter):
+    def per_kernel(path, names):
         vals = {}
         for r in csv.DictReader(open(path)):
-            if r.get("Counter_Name") != counter:
+            if r.get("Counter_Name") not in names:
                 continue
             key = kernel_key(r["Kernel_Name"])
             if key:
-                vals.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
-        return {k: sorted(v)[len(v) // 2] for k, v in vals.items()}  # median dispatch
+                d = vals.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return vals
 
-    f = per_kernel(fetch_csv, "FETCH_SIZE")
-    w = per_kernel(write_csv, "WRITE_SIZE")
-    rf, rw = COPY_BYTES / f["copy"], COPY_BYTES / w["copy"]
+    def med(xs):
+        xs = sorted(xs)
+        return xs[len(xs) // 2]
+
+    rd, wr = per_kernel(read_csv, READ_COUNTERS), per_kernel(write_csv, WRITE_COUNTERS)
+
+    def read_bytes(c):
+        return 32 * c["TCC_EA0_RDREQ_32B_sum"] + 64 * c["TCC_EA0_RDREQ_64B_sum"] + 128 * c["TCC_EA0_RDREQ_128B_sum"]
+
+    def write_bytes(c):
+        n64 = c["TCC_EA0_WRREQ_64B_sum"]
+        return 32 * (c["TCC_EA0_WRREQ_sum"] - n64) + 64 * n64
+
+    rf = COPY_BYTES / med([read_bytes(c) for c in rd["copy"].values()])
+    rw = COPY_BYTES / med([write_bytes(c) for c in wr["copy"].values()])
     path = os.path.join(ROOT, "profiles", "traffic.json")
     db = json.load(open(path)) if os.path.exists(path) else {}
-    for k in sorted(set(f) & set(w) - {"copy"}):
+    for k in sorted(set(rd) & set(wr) - {"copy"}):
+        r_b = med([read_bytes(c) for c in rd[k].values()])
+        w_b = med([write_bytes(c) for c in wr[k].values()])
+        req = med([c["TCC_EA0_RDREQ_sum"] for c in rd[k].values()])
+        unsized = req - med([c["TCC_EA0_RDREQ_32B_sum"] + c["TCC_EA0_RDREQ_64B_sum"] + c["TCC_EA0_RDREQ_128B_sum"]
+                             for c in rd[k].values()])
+        dram = med([c["TCC_EA0_RDREQ_DRAM_sum"] for c in wr[k].values()])
+        wdram = med([c["TCC_EA0_WRREQ_DRAM_sum"] for c in wr[k].values()])
+        wreq = med([c["TCC_EA0_WRREQ_sum"] for c in wr[k].values()])
         db[f"{k}/{workload}"] = {
-            "bytes_per_launch": round(f[k] * rf + w[k] * rw),
-            "fetch_bytes_raw": f[k], "write_bytes_raw": w[k],
-            "copy_scale_fetch": rf, "copy_scale_write": rw,
+            "bytes_per_launch": round(r_b * rf + w_b * rw),
+            "read_bytes": round(r_b * rf), "write_bytes": round(w_b * rw),
+            "read_requests": req, "read_requests_of_no_size_counter": unsized,
+            "read_dram_share": round(dram / req, 4) if req else None,
+            "write_dram_share": round(wdram / wreq, 4) if wreq else None,
+            "copy_scale_read": rf, "copy_scale_write": rw,
+            "counters": READ_COUNTERS + WRITE_COUNTERS,
             "sources": KERNEL_SOURCES[k], "source_sha256": sources_sha256(KERNEL_SOURCES[k]),
         }
         print(k, json.dumps(db[f"{k}/{workload}"]))
@@ -525,7 +566,7 @@ def main():
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this codec is measured on one GPU; --gpus must be 1 "
-                                   "(sharding across GPUs is described in DESIGN.md, not run)"}))
+                                   "(the path is not sharded across GPUs)"}))
         sys.exit(2)
     import numpy as np
     import torch
@@ -612,7 +653,10 @@ def main():
                   "frac_hbm": round(alg[k] / (ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)} for k in alg}
     # the decode stage is one decode launch: its duration is the stage's
     dec_bytes = alg["decode_dequant"]
-    dec_kernel = "k_decode_group" if d.decode_lanes > 1 else "k_decode"  # the launch kvc_decode makes
+    # the launch kvc_decode makes: several lanes per stream on small launches, else one lane per
+    # stream with the mode-first search for rows of 5 to 64 entries, binary lifting otherwise
+    dec_kernel = ("k_decode_group" if d.decode_lanes > 1 else
+                  "k_decode_mode" if 4 < d.alphabet <= 64 else "k_decode")
     achieved = dec_bytes / (d_avg * 1e-3) / 1e9
     res = {
         "metric": METRIC,
