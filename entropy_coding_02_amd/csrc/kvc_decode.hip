@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     int32_t *status, int CT)
 {
     // LDS: lut[256] f32 | ring[256][17] u32 | rec[2][CT][RS] u32 | rows16 [CT][P2] u16 |
-    //      pairs [CT][A] u32
+    //      pairs [CT][A] u32 | output staging [4 waves][16 rows][36] u32
     extern __shared__ uint32_t lds[];
     __shared__ uint32_t s_red[4];
     constexpr uint32_t P2 = 1u << NSTEP;
@@ -262,6 +262,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     const int n16 = (CT * (int)P2 + 1) / 2;
     lds_u16 *const r16 = (lds_u16 *)tile;
     lds_u32 *const pr = tile + n16;
+    lds_u32 *const xs = pr + CT * A;  // output staging: per wave 16 rows of 36 dwords
 
     const int bps = (p.Tc + 255) / 256;
     const int64_t slab = blockIdx.x / bps;
@@ -356,20 +357,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
 
     PairTile<PER> pt;
     // fp16 output: hw[0..15] the previous 32-channel half, hw[16..31] the
-    // current one; a 64-channel pair of halves goes out as one line per lane
+    // current one.  A pair of halves (128 bytes of each of the wave's 64 rows)
+    // goes out through the wave's LDS slice, 16 rows at a time: those rows'
+    // lanes write their pieces to LDS, then every lane stores one 16-byte piece,
+    // 8 lanes per row, so each store writes 8 whole 128-byte lines (stored
+    // straight from the lanes, one instruction would touch 64 lines, one L2
+    // request each).  Every lane of the wave takes part, so lanes past the
+    // slab's end decode too (an empty stream) and only rows before it are stored.
     uint32_t hw[32];
-    auto put_pair = [&](int cs, int nch) {  // channels [cs, cs + nch) from hw[0 ..]
-        uint4 *o = (uint4 *)((uint16_t *)out + row * C + cs);
+    const int wid_u = __builtin_amdgcn_readfirstlane(wid);  // uniform: the slice and rows live in SGPRs
+    lds_u32 *const xw = xs + wid_u * 576;
+    const int nact = __builtin_popcountll(__builtin_amdgcn_ballot_w64(active));  // active lanes: a prefix
+    uint16_t *const wout = (uint16_t *)out + (g.row0 + (int64_t)tb * 256 + wid_u * 64) * C;  // the wave's first row
+    auto put_rows = [&](auto piece, int npc, int cs, int nch) {  // pieces piece(q), q < npc; channels [cs, cs + nch)
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            if (q * 8 < nch) o[q] = make_uint4(hw[4 * q], hw[4 * q + 1], hw[4 * q + 2], hw[4 * q + 3]);
+        for (int pass = 0; pass < 4; ++pass) {
+            if ((lane >> 4) == pass) {
+                lds_u32 *const d = xw + (lane & 15) * 36;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (q < npc) *(lds_u32x4 *)(d + 4 * q) = piece(q);
+            }
+            __asm__ volatile("" ::: "memory");  // a wave's LDS operations run in order: the reads see the writes
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int r = 8 * k + (lane >> 3), pc = lane & 7;
+                const u32x4 v = *(const lds_u32x4 *)(xw + r * 36 + 4 * pc);
+                const int wr = 16 * pass + r;
+                if (wr < nact && pc * 8 < nch)
+                    *(uint4 *)(wout + (uint32_t)(wr * C + cs + 8 * pc)) = make_uint4(v.x, v.y, v.z, v.w);
+            }
+            __asm__ volatile("" ::: "memory");  // the slice is read before the next pass writes it
+        }
+    };
+    auto put_pair = [&](int cs, int nch) {  // channels [cs, cs + nch) from hw[0 ..]
+        put_rows([&](int q) { return u32x4{hw[4 * q], hw[4 * q + 1], hw[4 * q + 2], hw[4 * q + 3]}; }, 8, cs, nch);
     };
     auto put_half = [&](int cs, int nch) {  // channels [cs, cs + nch) from hw[16 ..]
-        uint4 *o = (uint4 *)((uint16_t *)out + row * C + cs);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (q * 8 < nch) o[q] = make_uint4(hw[16 + 4 * q], hw[17 + 4 * q], hw[18 + 4 * q], hw[19 + 4 * q]);
+        put_rows([&](int q) { return u32x4{hw[16 + 4 * q], hw[17 + 4 * q], hw[18 + 4 * q], hw[19 + 4 * q]}; }, 4,
+                 cs, nch);
     };
+    const bool wave_on = nact > 0;
     pt.load(srows, 0, CT, C, A);
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
@@ -379,7 +407,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
         __syncthreads();
         rec = rnow;
         if (it + 1 < ntiles) pt.load(srows, c0 + CT, CT, C, A);
-        if (!active) continue;
+        if (!wave_on) continue;
         if constexpr (VEC) {
             // halves of 32 channels (CT is a multiple of 32; C of 16)
             for (int cb = c0; cb < c1; cb += 32) {
@@ -418,11 +446,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
                             }
                         }
                     }
-                    if constexpr ((OUT & OUT_SYM) != 0) *(uint2 *)(so + cg) = make_uint2(sw[0], sw[1]);
+                    if constexpr ((OUT & OUT_SYM) != 0)
+                        if (active) *(uint2 *)(so + cg) = make_uint2(sw[0], sw[1]);
                     if constexpr (ODT == ODT_F32) {
-                        float4 *o = (float4 *)((float *)out + row * C + cg);
-                        o[0] = make_float4(fw[0], fw[1], fw[2], fw[3]);
-                        o[1] = make_float4(fw[4], fw[5], fw[6], fw[7]);
+                        if (active) {
+                            float4 *o = (float4 *)((float *)out + row * C + cg);
+                            o[0] = make_float4(fw[0], fw[1], fw[2], fw[3]);
+                            o[1] = make_float4(fw[4], fw[5], fw[6], fw[7]);
+                        }
                     }
                 }
             }
@@ -431,6 +462,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
                 if ((c & 7) == 0) in.group();
                 uint32_t lvb;
                 const uint32_t s = decode1(c - c0, load_rec(c - c0), lvb);
+                if (!active) continue;
                 if constexpr ((OUT & OUT_SYM) != 0) so[c] = (uint8_t)s;
                 if constexpr (ODT >= 0) {
                     const float y = __uint_as_float(lvb) * m;
@@ -444,7 +476,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     }
     // the row's last half or pair of halves
     if constexpr (VEC && ODT == ODT_F16) {
-        if (active && C > 0) {
+        if (wave_on && C > 0) {
             const int hl = (C - 1) >> 5;  // index of the last half
             if (hl & 1)
                 put_pair(32 * (hl - 1), C - 32 * (hl - 1));
@@ -797,7 +829,8 @@ static size_t dec_mode_lds_bytes(int A, int CT, int nstep)
 {
     const size_t P2 = (size_t)1 << nstep;
     const size_t n16 = ((size_t)CT * P2 + 1) / 2;
-    return sizeof(uint32_t) * (256 + 256 * 17 + 2 * (size_t)CT * DEC_MODE_RS(nstep) + n16 + (size_t)CT * A);
+    return sizeof(uint32_t) * (256 + 256 * 17 + 2 * (size_t)CT * DEC_MODE_RS(nstep) + n16 + (size_t)CT * A +
+                               4 * 576);
 }
 
 int decode_lanes_per_stream(const KParams &p)
