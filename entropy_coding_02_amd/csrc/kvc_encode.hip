@@ -235,8 +235,11 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *slab_total, uint6
 // i's payload offset o (slab offset + the lengths before it).  The wave then
 // walks its streams' slot dwords in rounds of 64: it stages slot dwords
 // [64r, 64r + 64) of its SPW streams in LDS (coalesced loads: the slots are
-// interleaved, stream i's k-th dword next to stream i + 1's) and writes the
-// streams one after the other, lane j taking slot dword 64r + j.  A slot
+// interleaved, stream i's k-th dword next to stream i + 1's), then writes the
+// round's (stream, dword) pairs enumerated flat over the lanes (a prefix of
+// the streams' dword counts, each lane finding its stream by a binary search
+// of it), so a round takes about sum(dwords) / 64 store passes rather than
+// one pass per stream: most streams hold a few dwords.  A slot
 // dword holds 4 stream bytes in stream order, so every whole one goes out as
 // one dword store at byte offset o + 4j, unaligned (gfx9 global stores take
 // any byte address and write only the 4 bytes), and the last len % 4 bytes
@@ -257,6 +260,8 @@ __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
     constexpr int PPR = SPW / 4;    // 16-byte pieces per staged slot row
     constexpr int RPL = 64 / PPR;   // slot rows per wave-wide load
     __shared__ uint32_t win[SPW * (PACK_W + 1)];  // [stream][PACK_W + 1] staged slot dwords
+    __shared__ uint32_t pfx[SPW];                 // the round's flat start of each stream
+    __shared__ uint32_t s_len[SPW], s_olo[SPW], s_ohi[SPW];  // each stream's length and payload offset
     const int bps = (p.Tc + 255) / 256;
     const int64_t eb = blockIdx.x / WPR;  // slot region
     const int wq = (int)(blockIdx.x - eb * WPR);
@@ -304,15 +309,56 @@ __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
 #pragma unroll
             for (int e = 0; e < 4; ++e) win[(4 * sm + e) * (PACK_W + 1) + u] = v4[q][e];
         }
+        // the round's (stream, slot dword) pairs, enumerated flat over the lanes:
+        // stream i has n_i = clamp(ndw_i - k0, 0, PACK_W) of them, from flat index P_i on
+        const uint32_t n_me = active ? (uint32_t)min(max(ndw - k0, 0), PACK_W) : 0u;
+        uint32_t pin = n_me;  // inclusive prefix of n over the wave's streams
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t v = (uint32_t)__shfl_up((int)pin, off, 64);
+            if (lane >= off) pin += v;
+        }
+        if (lane < SPW) {
+            pfx[lane] = pin - n_me;
+            s_len[lane] = len;
+            s_olo[lane] = olo;
+            s_ohi[lane] = ohi;
+        }
+        const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)pin, 63);
         __syncthreads();
-        const uint32_t j = (uint32_t)(k0 + lane);  // this lane's slot dword
-        for (int i = 0; i < SPW; ++i) {
-            const uint32_t len_i = (uint32_t)__builtin_amdgcn_readlane((int)len, i);
-            if ((uint32_t)k0 * 4u >= len_i) continue;  // uniform: stream i is done
-            if (4u * j >= len_i) continue;
-            const uint64_t o_i = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ohi, i) << 32) |
-                                 (uint32_t)__builtin_amdgcn_readlane((int)olo, i);
-            const uint32_t v = win[i * (PACK_W + 1) + lane];
+        if (total >= 16u * SPW) {
+            // long streams (16 dwords or more on average in this round): one
+            // stream at a time, lane j taking its slot dword k0 + j, fills the
+            // lanes about as well with no search
+            const uint32_t j = (uint32_t)(k0 + lane);
+            for (int i = 0; i < SPW; ++i) {
+                const uint32_t len_i = s_len[i];
+                if ((uint32_t)k0 * 4u >= len_i) continue;  // uniform: stream i is done
+                if (4u * j >= len_i) continue;
+                const uint64_t o_i = ((uint64_t)s_ohi[i] << 32) | s_olo[i];
+                const uint32_t v = win[i * (PACK_W + 1) + lane];
+                const uint64_t b = o_i + 4u * j;
+                const uint32_t nb = min(len_i - 4u * j, 4u);
+                if (nb == 4u && b + 4u <= cap) {
+                    __builtin_memcpy(payload + b, &v, 4);
+                } else {
+                    for (uint32_t q = 0; q < nb; ++q)
+                        if (b + q < cap) payload[b + q] = (uint8_t)(v >> (8u * q));
+                }
+            }
+            __syncthreads();
+            continue;
+        }
+        for (uint32_t f = (uint32_t)lane; f < total; f += 64u) {
+            // stream i: the last with P_i <= f (P non-decreasing; streams of no dwords share a P)
+            uint32_t i = 0;
+#pragma unroll
+            for (uint32_t b = SPW / 2; b >= 1; b >>= 1)
+                if (pfx[i + b] <= f) i += b;
+            const uint32_t jr = f - pfx[i];  // slot dword within the round
+            const uint32_t j = (uint32_t)k0 + jr;
+            const uint32_t len_i = s_len[i];  // (from LDS: a lane-to-lane read would see 0 from lanes
+            const uint64_t o_i = ((uint64_t)s_ohi[i] << 32) | s_olo[i];  //  already out of this loop)
+            const uint32_t v = win[i * (PACK_W + 1) + jr];
             const uint64_t b = o_i + 4u * j;  // stream bytes [4j, 4j + 4) go here
             const uint32_t nb = min(len_i - 4u * j, 4u);
             if (nb == 4u && b + 4u <= cap) {
