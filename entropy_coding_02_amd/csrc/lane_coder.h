@@ -753,14 +753,15 @@ struct WinIn {
 
 // code - r * st as r * (-st) + code (a 24-bit signed multiply-add on the GPU:
 // r < 2^16 and -st >= -65535 both fit 24 signed bits).
-KVC_HD uint32_t kvc_mad_nst(uint32_t r, int32_t nst, uint32_t code)
+KVC_HD uint32_t kvc_mul_nst(uint32_t r, int32_t nst)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    return (uint32_t)__mul24((int)r, nst) + code;
+    return (uint32_t)__mul24((int)r, nst);
 #else
-    return (uint32_t)((int64_t)r * nst) + code;
+    return (uint32_t)((int64_t)r * nst);
 #endif
 }
+KVC_HD uint32_t kvc_mad_nst(uint32_t r, int32_t nst, uint32_t code) { return kvc_mul_nst(r, nst) + code; }
 
 // Narrow to the interval [st, st + fr) found for r = range >> 16 and
 // renormalise from the window.  Returns 1 if code left the interval.
@@ -824,18 +825,20 @@ KVC_HD uint32_t dec_symbol_mode(uint32_t &code, uint32_t &range, In &in, const M
                                 uint32_t *bad, uint32_t *fast, uint32_t *lv)
 {
     const uint32_t r = range >> 16;
-    {
-        const uint32_t d = kvc_mad_nst(r, m.nst, code);
-        const uint32_t rn = kvc_umul24(r, m.fr);
-        if (kvc_all(d < rn && rn >= (1u << 24))) {
-            code = d;
-            range = rn;
-            *fast = 1;
-            *lv = m.lv;
-            return m.md;
-        }
-    }
+    // The mode's step is taken into code and range at once, so the state
+    // needs no copies on the common path; the exact path gets the code back
+    // by subtracting the same product (exact modulo 2^32, whatever the
+    // record's start word holds) and recomputes both.
+    const uint32_t d = kvc_mad_nst(r, m.nst, code);
+    const uint32_t rn = kvc_umul24(r, m.fr);
+    const bool hit = d < rn && rn >= (1u << 24);
+    code = d;
+    range = rn;
+    *lv = m.lv;
+    *fast = 1;
+    if (kvc_all(hit)) return m.md;
     *fast = 0;
+    code = d - kvc_mul_nst(r, m.nst);
     constexpr int NB = 1 << (NSTEP - 3);
     uint32_t hd[NB];
     heads(hd);
