@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     uint32_t range = 0xFFFFFFFFu;
     constexpr int ODT = (OUT & OUT_F16) ? ODT_F16 : (OUT & OUT_F32) ? ODT_F32 : -1;
     const float m = (ODT >= 0) ? kvc_h2f(max1[row]) : 0.0f;
-    uint32_t bad = 0;
+    BadMask bad;
     uint8_t *so = (OUT & OUT_SYM) ? sym_out + row * C : nullptr;
     const uint16_t *srows = cdf + g.tab * C * A;
     const int ntiles = (C + CT - 1) / CT;
@@ -325,8 +325,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     auto load_rec = [&](int cl) -> Rec { return *(const lds_u32x4 *)(rec + cl * RS); };
     // one symbol of tile channel cl with its record's mode part ra; lvb
     // receives its dequantization value
-    auto decode1 = [&](int cl, const Rec &ra, uint32_t &lvb) -> uint32_t {
-        const lds_u32 *rc = rec + cl * RS;
+    auto decode1 = [&](int cl, const lds_u32 *rc, const Rec &ra, uint32_t &lvb) -> uint32_t {  // rc: cl's record
         auto heads = [&](uint32_t *hd) {  // the exact path's block heads
             hd[0] = 0u;
             if constexpr (NB >= 2) {
@@ -351,7 +350,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
         const lds_u32 *prow = pr + cl * A;  // uniform: the pair address is one shift-add of s
         auto ent = [&](uint32_t s) -> kvc_u32x2 { return kvc_u32x2{prow[s], lutw[s]}; };
         uint32_t fast;
-        return dec_symbol_mode<NSTEP, PAD>(code, range, in, mr, heads, piece, ent, (uint32_t)A, &bad, &fast,
+        return dec_symbol_mode<NSTEP, PAD>(code, range, in, mr, heads, piece, ent, (uint32_t)A, bad, &fast,
                                            &lvb);
     };
 
@@ -426,12 +425,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
                     if (gi) in.group();
                     uint32_t sw[2] = {0, 0};
                     float ylo = 0.0f;
-                    Rec rq = load_rec(cg - c0);
+                    // the group's records from one address held in a VGPR (their
+                    // offsets are immediates), not rebuilt from a scalar per read
+                    const lds_u32 *rg = rec + (cg - c0) * RS;
+                    __asm__("" : "+v"(rg));
+                    Rec rq = *(const lds_u32x4 *)rg;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const Rec rn = load_rec(cg - c0 + (i < 7 ? i + 1 : i));
+                        const Rec rn = *(const lds_u32x4 *)(rg + (i < 7 ? i + 1 : i) * RS);
                         uint32_t lvb;
-                        const uint32_t s = decode1(cg - c0 + i, rq, lvb);
+                        const uint32_t s = decode1(cg - c0 + i, rg + i * RS, rq, lvb);
                         rq = rn;
                         sw[i >> 2] |= s << (8 * (i & 3));
                         if constexpr (ODT >= 0) {
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
             for (int c = c0; c < c1; ++c) {
                 if ((c & 7) == 0) in.group();
                 uint32_t lvb;
-                const uint32_t s = decode1(c - c0, load_rec(c - c0), lvb);
+                const uint32_t s = decode1(c - c0, rec + (c - c0) * RS, load_rec(c - c0), lvb);
                 if (!active) continue;
                 if constexpr ((OUT & OUT_SYM) != 0) so[c] = (uint8_t)s;
                 if constexpr (ODT >= 0) {
@@ -484,7 +487,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
                 put_half(32 * hl, C - 32 * hl);
         }
     }
-    if (active && bad) kvc_flag(status, KVC_DEV_CORRUPT);
+    if (active && bad.mine()) kvc_flag(status, KVC_DEV_CORRUPT);
 }
 
 // Maximum of v over each aligned group of G lanes (G = 2, 4 or 8), in every

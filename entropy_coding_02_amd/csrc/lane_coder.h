@@ -812,17 +812,36 @@ KVC_HD uint32_t cdf_search_heads(const uint32_t *hd, const Piece &piece, uint32_
     return s;
 }
 
+// Flags of streams that left their interval, as dec_symbol_mode collects
+// them: one lane's flag (BadFlag), or on the GPU a whole wave's as a lane
+// mask (BadMask: one compare into a scalar register pair per check, no
+// per-lane select and or).
+struct BadFlag {
+    uint32_t f = 0;
+    KVC_HD void add(bool b) { f |= b ? 1u : 0u; }
+};
+struct BadMask {
+    uint64_t m = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+    __device__ void add(bool b) { m |= __builtin_amdgcn_ballot_w64(b); }
+    __device__ bool mine() const { return ((m >> __lane_id()) & 1u) != 0u; }
+#else
+    void add(bool b) { m |= b ? 1u : 0u; }
+    bool mine() const { return m != 0u; }
+#endif
+};
+
 // One symbol of the mode-first decoder: the mode record's symbol when every
 // lane lands in its interval without renormalising (*fast = 1), else the
 // exact two-level search, with the block heads heads(hd) loads (only then:
 // the fast path needs none) and pieces of the padded row; ent(s) gives
 // symbol s's (start | frequency << 16) pair and its dequantization value
 // (fp32 bits), and *lv receives the chosen symbol's.  Returns the symbol;
-// *bad |= 1 when the stream left its interval.
-template <int NSTEP, bool PAD, class Heads, class Piece, class Ent, class In>
+// bad.add(true) when the stream left its interval.
+template <int NSTEP, bool PAD, class Heads, class Piece, class Ent, class In, class Bad>
 KVC_HD uint32_t dec_symbol_mode(uint32_t &code, uint32_t &range, In &in, const ModeRec &m,
                                 const Heads &heads, const Piece &piece, const Ent &ent, uint32_t A,
-                                uint32_t *bad, uint32_t *fast, uint32_t *lv)
+                                Bad &bad, uint32_t *fast, uint32_t *lv)
 {
     const uint32_t r = range >> 16;
     // The mode's step is taken into code and range at once, so the state
@@ -844,7 +863,7 @@ KVC_HD uint32_t dec_symbol_mode(uint32_t &code, uint32_t &range, In &in, const M
     heads(hd);
     const uint32_t s = cdf_search_heads<NSTEP, PAD>(hd, piece, A, r, code);
     const kvc_u32x2 e = ent(s);
-    *bad |= dec_step_win(code, range, in, r, e[0] & 0xFFFFu, e[0] >> 16);
+    bad.add(dec_step_win(code, range, in, r, e[0] & 0xFFFFu, e[0] >> 16) != 0u);
     *lv = e[1];
     return s;
 }

@@ -96,6 +96,7 @@ int hostsim_decode_stream_n(const uint8_t *buf, int64_t cap, int64_t off, int64_
     WinIn<uint32_t *> win;  // the mode-first decoder's feed (search 2)
     uint32_t wcode = win.init(buf, (uint64_t)off, (uint64_t)len, (uint64_t)cap, ring2), wrange = 0xFFFFFFFFu;
     uint32_t bad = 0, nstep = cdf_nstep((uint32_t)A), P2 = 1u << nstep;
+    BadFlag wbad;  // the mode-first decoder's flag
     std::vector<uint16_t> padded(P2);
     std::vector<uint32_t> pairs(A);
     for (int32_t c = 0; c < C; ++c) {
@@ -128,10 +129,10 @@ int hostsim_decode_stream_n(const uint8_t *buf, int64_t cap, int64_t off, int64_
             auto pa = [&](uint32_t k) { return kvc_u32x2{pairs[k], 0u}; };
             uint32_t lvv = 0;
             switch (nstep) {
-            case 3: sym = (uint32_t)A < 8u ? dec_symbol_mode<3, true>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv) : dec_symbol_mode<3, false>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv); break;
-            case 4: sym = (uint32_t)A < 16u ? dec_symbol_mode<4, true>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv) : dec_symbol_mode<4, false>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv); break;
-            case 5: sym = (uint32_t)A < 32u ? dec_symbol_mode<5, true>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv) : dec_symbol_mode<5, false>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv); break;
-            default: sym = (uint32_t)A < 64u ? dec_symbol_mode<6, true>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv) : dec_symbol_mode<6, false>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, &bad, &fast, &lvv); break;
+            case 3: sym = (uint32_t)A < 8u ? dec_symbol_mode<3, true>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, wbad, &fast, &lvv) : dec_symbol_mode<3, false>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, wbad, &fast, &lvv); break;
+            case 4: sym = (uint32_t)A < 16u ? dec_symbol_mode<4, true>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, wbad, &fast, &lvv) : dec_symbol_mode<4, false>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, wbad, &fast, &lvv); break;
+            case 5: sym = (uint32_t)A < 32u ? dec_symbol_mode<5, true>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, wbad, &fast, &lvv) : dec_symbol_mode<5, false>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, wbad, &fast, &lvv); break;
+            default: sym = (uint32_t)A < 64u ? dec_symbol_mode<6, true>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, wbad, &fast, &lvv) : dec_symbol_mode<6, false>(wcode, wrange, win, m, hd, piece, pa, (uint32_t)A, wbad, &fast, &lvv); break;
             }
             q[c] = (uint8_t)sym;
             if (fast_count) *fast_count += fast;
@@ -159,7 +160,7 @@ int hostsim_decode_stream_n(const uint8_t *buf, int64_t cap, int64_t off, int64_
         }
         q[c] = (uint8_t)sym;
     }
-    return (int)bad;
+    return (int)(bad | wbad.f);
 }
 
 int hostsim_decode_stream(const uint8_t *buf, int64_t cap, int64_t off, int64_t len, int32_t C,

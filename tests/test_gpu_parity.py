@@ -151,10 +151,12 @@ def test_nonfinite_flagged():
     assert int(buf.dev_status.item()) & kvc.KVC_DEV_NONFINITE
 
 
-def test_corrupt_payload_flagged_and_bounded():
-    say("[gpu] corrupt payload")
+@pytest.mark.parametrize("name", ["ragged_L3_C40_T300_Tc128", "one_lane_A32_C200_T9000"])
+def test_corrupt_payload_flagged_and_bounded(name):
+    """Group decoder, then the one-lane mode-first decoder (a wave-wide flag mask)."""
+    say(f"[gpu] corrupt payload {name}")
     import torch
-    cfg = SMALL["ragged_L3_C40_T300_Tc128"]
+    cfg = SMALL[name]
     kv, _ = kvgen.generate(cfg)
     d = kvc.Desc(cfg.n_layers, cfg.n_channels, cfg.n_tokens, cfg.bins(), cfg.chunk_tokens)
     buf = kvc.alloc(d, with_dec_sym=True)
