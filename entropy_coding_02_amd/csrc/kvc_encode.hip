@@ -38,7 +38,13 @@ namespace {
 // rows have a 16-byte-padded stride that spreads lanes over all banks.
 // Without global loads in the loop, the lanes' byte stores never make it
 // wait.
-template <bool VEC16, int PER, int ENC_SW, int SPW>
+//
+// PRE4 (staged symbols, A a power of two up to 64): a byte is out of range
+// when it has a bit at or above log2 A, one and-or per 16 staged bytes; the
+// bytes are then staged as 4 * (s & (A - 1)), the byte offset of the pair
+// within its row, so each lookup address is one byte-select add, and an
+// out-of-range byte (flagged) still reads inside its row.
+template <bool VEC16, int PER, int ENC_SW, int SPW, bool PRE4 = false>
 __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
                                                 const uint16_t *__restrict__ cdf,
                                                 uint8_t *__restrict__ slots,
@@ -94,10 +100,19 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
             sv[i] = (tok < g.nj && cc < C) ? *(const u32x4 *)(sym + (g.row0 + tok) * C + cc)
                                            : u32x4{0, 0, 0, 0};
         }
+        if constexpr (PRE4) {
+            const uint32_t hi = (0x100u - (uint32_t)A) * 0x01010101u, lo = ((uint32_t)A - 1u) * 0x01010101u;
 #pragma unroll
-        for (int i = 0; i < NP; ++i)
-            badsym |= kvc_bytes_ge(sv[i].x, (uint32_t)A) | kvc_bytes_ge(sv[i].y, (uint32_t)A) |
-                      kvc_bytes_ge(sv[i].z, (uint32_t)A) | kvc_bytes_ge(sv[i].w, (uint32_t)A);
+            for (int i = 0; i < NP; ++i) {
+                badsym |= (sv[i].x | sv[i].y | sv[i].z | sv[i].w) & hi;
+                sv[i] = u32x4{(sv[i].x & lo) << 2, (sv[i].y & lo) << 2, (sv[i].z & lo) << 2, (sv[i].w & lo) << 2};
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NP; ++i)
+                badsym |= kvc_bytes_ge(sv[i].x, (uint32_t)A) | kvc_bytes_ge(sv[i].y, (uint32_t)A) |
+                          kvc_bytes_ge(sv[i].z, (uint32_t)A) | kvc_bytes_ge(sv[i].w, (uint32_t)A);
+        }
     };
     auto store_syms = [&]() {
 #pragma unroll
@@ -136,9 +151,11 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         const int k = h * 8 + i;
-                        uint32_t s = (wv[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                        s = min(s, (uint32_t)A - 1u);
-                        pv[i] = trow[k * A + s];
+                        const uint32_t b = (wv[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+                        if constexpr (PRE4)  // b = 4 * symbol, a byte offset in row k
+                            pv[i] = *(const lds_u32 *)((const lds_u8 *)(trow + k * A) + b);
+                        else
+                            pv[i] = trow[k * A + min(b, (uint32_t)A - 1u)];
                     }
 #pragma unroll
                     for (int i = 0; i < 8; ++i) enc_pair(e, pv[i], out);
@@ -874,10 +891,17 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
 #define KVC_ENC(V, P, S, W, L)                                                                       \
     hipLaunchKernelGGL((k_encode<V, P, S, W>), grid, dim3(256), L, stream, sym, cdf, slots, stream_len, \
                        p, CT, status)
+#define KVC_ENC4(P, S, W, L)                                                                         \
+    hipLaunchKernelGGL((k_encode<true, P, S, W, true>), grid, dim3(256), L, stream, sym, cdf, slots,    \
+                       stream_len, p, CT, status)
+    const bool pre4 = (p.A & (p.A - 1)) == 0 && p.A <= 64;  // symbols staged as pair byte offsets
 #define KVC_ENC_S(S, W)                                                                              \
     {                                                                                                \
         const size_t lds_syms = lds_pairs + 4 * W * (size_t)(S + 16);                                \
-        if (vec16) {                                                                                 \
+        if (vec16 && pre4) {                                                                         \
+            if (per <= 2) KVC_ENC4(2, S, W, lds_syms);                                               \
+            else KVC_ENC4(8, S, W, lds_syms);                                                        \
+        } else if (vec16) {                                                                          \
             if (per <= 2) KVC_ENC(true, 2, S, W, lds_syms);                                          \
             else KVC_ENC(true, 8, S, W, lds_syms);                                                   \
         } else {                                                                                     \
@@ -891,6 +915,7 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
         if (sw == 128) KVC_ENC_S(128, 64) else KVC_ENC_S(64, 64)
     }
 #undef KVC_ENC_S
+#undef KVC_ENC4
 #undef KVC_ENC
     hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
                        slab_total, p);

@@ -203,12 +203,15 @@ def test_payload_overflow_flagged_and_cap_respected(name):
 
 
 @pytest.mark.parametrize("name", ["C24_T100", "ragged_L3_C40_T300_Tc128", "split_A24_C512_T200_Tc128",
-                                  "mistral_L32_C1024_T64"])
+                                  "mistral_L32_C1024_T64", "one_lane_A8_C16_T9000", "one_lane_A64_C80_T9000",
+                                  "one_lane_A40_C96_T9000"])
 def test_bad_symbol_flagged(name):
     """A symbol >= A (no CDF interval) sets KVC_DEV_BAD_SYMBOL in kvc_cdf and in
-    kvc_encode (one-lane, split and scalar-staging encoders, narrow and wide
-    CDF kernels); the same symbols at A - 1 (valid for the row, whatever the
-    layer's bins) set nothing, and kvc_cdf's rows then equal the oracle's."""
+    kvc_encode (one-lane, split and scalar-staging encoders; the one-lane
+    encoder's staged symbols both as pair offsets, A a power of two, and
+    clamped, A = 40; narrow and wide CDF kernels); the same symbols at A - 1
+    (valid for the row, whatever the layer's bins) set nothing, and kvc_cdf's
+    rows then equal the oracle's."""
     import torch
     cfg = SMALL[name]
     kv, _ = kvgen.generate(cfg)
