@@ -35,6 +35,17 @@ constexpr int64_t KVC_DEC_GROUP_LANES = 4;
 namespace {
 
 enum { ODT_F16 = 0, ODT_F32 = 1 };
+
+// A lane's 17 byte-ring slots for WinIn in k_decode_mode, slot i at
+// p[(16 - i) * 256] (p: the lane's slot 16): the block's 256 lanes keep slot i
+// side by side, so a wave's reads of any mix of slots fall in distinct banks,
+// and slot i + 1 lies just below slot i, so one two-dword read (lower address
+// first) returns (slot i + 1, slot i): the window's 64 bits already in
+// register order.
+struct LaneRing {
+    lds_u32 *p;
+    __device__ lds_u32 &operator[](uint32_t i) const { return p[(16u - i) * 256u]; }
+};
 // what k_decode writes: a compile-time set, so every store in the symbol loop
 // is unconditional and the loads of the byte feed never wait for them
 enum { OUT_F16 = 1, OUT_F32 = 2, OUT_SYM = 4 };
@@ -245,7 +256,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     const uint16_t *__restrict__ max1, uint8_t *__restrict__ sym_out, void *__restrict__ out, KParams p,
     int32_t *status, int CT)
 {
-    // LDS: lut[256] f32 | ring[256][17] u32 | rec[2][CT][RS] u32 | rows16 [CT][P2] u16 |
+    // LDS: lut[256] f32 | ring[17][256] u32 | rec[2][CT][RS] u32 | rows16 [CT][P2] u16 |
     //      pairs [CT][A] u32 | output staging [4 waves][16 rows][36] u32
     extern __shared__ uint32_t lds[];
     __shared__ uint32_t s_red[4];
@@ -256,7 +267,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     const int C = p.C, A = p.A;
     float *lut = (float *)lds;
     const lds_u32 *const lutw = (const lds_u32 *)lds;
-    lds_u32 *const ring = (lds_u32 *)(lds + 256) + threadIdx.x * 17u;
+    const LaneRing ring{(lds_u32 *)(lds + 256) + threadIdx.x};  // slot i at [(16 - i) * 256]
     lds_u32 *const recs = (lds_u32 *)(lds + 256 + 256 * 17);
     lds_u32 *const tile = recs + 2 * CT * RS;
     const int n16 = (CT * (int)P2 + 1) / 2;
@@ -309,7 +320,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
 
     const int64_t row = g.row0 + (active ? t : 0);
     const uint64_t off = active ? slab_off[slab] + pre + wbase + incl - len : 0;
-    WinIn<lds_u32 *> in;
+    WinIn<LaneRing> in;
     uint32_t code = in.init(payload, off, len, (uint64_t)payload_bytes, ring);
     uint32_t range = 0xFFFFFFFFu;
     constexpr int ODT = (OUT & OUT_F16) ? ODT_F16 : (OUT & OUT_F32) ? ODT_F32 : -1;
