@@ -452,9 +452,9 @@ int kvc_serialize_chunk(const kvc_desc *desc, int64_t chunk, const uint16_t *cdf
         return KVC_ERR_ARG;
     if (out_cap < container_total(container_layout(gc.p), 0)) return KVC_ERR_CAPACITY;
     const int64_t twoL = 2 * (int64_t)g.p.L;
-    const ChunkSrc src{cdf + (chunk / g.p.S) * twoL * g.p.C * g.p.A, max1, g.p.T, chunk * (int64_t)g.p.Tc,
-                       stream_len + chunk * twoL * g.p.Tc, slab_off + chunk * twoL, payload};
-    return launch_status(launch_serialize_chunk(src, out, out_cap, gc.p, dev_status, (hipStream_t)stream));
+    const ChunkRun run{cdf, g.p.S, twoL * g.p.C * g.p.A, max1, g.p.T, g.p.Tc, chunk,
+                       stream_len + chunk * twoL * g.p.Tc, slab_off + chunk * twoL, payload, 1};
+    return launch_status(launch_serialize_chunks(run, out, out_cap, gc.p, dev_status, (hipStream_t)stream));
 }
 
 int64_t kvc_stream_work_bytes(const kvc_desc *levels, int32_t n_levels, int32_t chunks_per_unit)
@@ -540,15 +540,18 @@ int kvc_stream_encode(const kvc_desc *levels, int32_t n_levels, const int32_t *c
         // staging half u % 2 is free once the copies of unit u - 2 are done
         if (e == hipSuccess && u >= 2) e = hipStreamWaitEvent(cs, copied[u & 1], 0);
         uint8_t *const st = staging(u);
-        for (int64_t j = un.ja; j < un.jb && e == hipSuccess; ++j) {
-            const int64_t k = j - un.ja;
+        // the unit's full chunks in one set of launches, a shorter last chunk in its own
+        const int64_t jfull = std::min<int64_t>(un.jb, P.T / P.Tc);
+        for (int64_t ja = un.ja; ja < un.jb && e == hipSuccess;) {
+            const int64_t jb = ja < jfull ? jfull : ja + 1, k = ja - un.ja;
             kvc_desc dc = levels[l];
-            dc.n_tokens = std::min<int64_t>((j + 1) * P.Tc, P.T) - j * P.Tc;
+            dc.n_tokens = std::min<int64_t>((ja + 1) * P.Tc, P.T) - ja * P.Tc;
             Geometry gc;
             if (make_geometry(&dc, gc) != KVC_OK) return KVC_ERR_ARG;
-            const ChunkSrc src{cdf[l] + (j / pl.S) * twoL * P.C * pl.A, max1, P.T, j * (int64_t)P.Tc,
-                               len_u + k * twoL * P.Tc, off_u + k * twoL, pay_u};
-            e = launch_serialize_chunk(src, st + k * sl.chunk_cap, sl.chunk_cap, gc.p, dev_status, cs);
+            const ChunkRun run{cdf[l], pl.S, twoL * P.C * pl.A, max1, P.T, P.Tc, ja, len_u + k * twoL * P.Tc,
+                               off_u + k * twoL, pay_u, jb - ja};
+            e = launch_serialize_chunks(run, st + k * sl.chunk_cap, sl.chunk_cap, gc.p, dev_status, cs);
+            ja = jb;
         }
         const int n = (int)(un.jb - un.ja);
         if (e == hipSuccess) e = launch_container_totals(st, sl.chunk_cap, n, sizes_u, cs);

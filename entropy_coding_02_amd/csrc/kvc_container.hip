@@ -21,6 +21,8 @@
 #include "kvc_common.h"
 #include "kvc_kernels.h"
 
+#include <algorithm>
+
 namespace {
 
 constexpr uint32_t KVC_MAGIC = 0x3143564Bu;
@@ -35,11 +37,17 @@ __device__ inline int64_t lk_prefix(const KParams &p, int lk)
     return n;
 }
 
-// Header, bins and the padding after them.  One block of 64 threads.
+// Header, bins and the padding after them.  One block of 64 threads per
+// container; container y of a run (blockIdx.y) takes its offsets off_stride
+// further on and is written out_stride bytes further on.
 __global__ void k_ser_header(const uint64_t *__restrict__ off0, const uint64_t *__restrict__ off1,
                              uint8_t *__restrict__ out, int64_t out_cap, KParams p,
-                             ContainerLayout cl, int32_t *status)
+                             ContainerLayout cl, int32_t *status, int64_t off_stride, int64_t out_stride)
 {
+    const int64_t y = blockIdx.y;
+    if (off0) off0 += y * off_stride;
+    off1 += y * off_stride;
+    out += y * out_stride;
     const uint64_t pb = *off1 - (off0 ? *off0 : 0u);  // payload bytes
     const int64_t total = container_total(cl, (int64_t)pb);
     const int tid = threadIdx.x;
@@ -66,10 +74,16 @@ __global__ void k_ser_header(const uint64_t *__restrict__ off0, const uint64_t *
 
 // The compact CDF section: one block per table (g, l, kv).  Threads walk the
 // table's compact entries (coalesced u16 stores) and check its implied ones.
+// Container y of a run (blockIdx.y, chunk j0 + y of a tensor whose table
+// groups of S chunks lie table_stride entries apart) is written out_stride
+// bytes further on.
 __global__ __launch_bounds__(256) void k_ser_cdf(const uint16_t *__restrict__ cdf,
                                                  uint8_t *__restrict__ out, KParams p,
-                                                 ContainerLayout cl, int32_t *status)
+                                                 ContainerLayout cl, int32_t *status, int64_t j0,
+                                                 int32_t S, int64_t table_stride, int64_t out_stride)
 {
+    cdf += (j0 + (int64_t)blockIdx.y) / S * table_stride;
+    out += (int64_t)blockIdx.y * out_stride;
     const int64_t slab = blockIdx.x;  // table index g * 2L + lk
     const int64_t twoL = 2 * (int64_t)p.L;
     const int64_t j = slab / twoL;
@@ -104,12 +118,19 @@ __global__ __launch_bounds__(256) void k_ser_cdf(const uint16_t *__restrict__ cd
 // r16(max(n, min_len)); nothing at or past dst + cap is written.  n is
 // n_host, or *n_end - *n_begin when n_end is given (n_begin may be NULL: 0);
 // with n_begin the source starts at src + *n_begin.  A 4-byte aligned source
-// is copied by dwords, any other byte by byte.
+// is copied by dwords, any other byte by byte.  Copy y of a run (blockIdx.y)
+// moves src, dst and the offset pointers by y times their strides.
 __global__ __launch_bounds__(256) void k_copy_section(const uint8_t *__restrict__ src,
                                                       uint8_t *__restrict__ dst, int64_t n_host,
                                                       const uint64_t *n_begin, const uint64_t *n_end,
-                                                      int64_t min_len, int64_t cap)
+                                                      int64_t min_len, int64_t cap, int64_t src_stride,
+                                                      int64_t dst_stride, int64_t off_stride)
 {
+    const int64_t y = blockIdx.y;
+    src += y * src_stride;
+    dst += y * dst_stride;
+    if (n_begin) n_begin += y * off_stride;
+    if (n_end) n_end += y * off_stride;
     const int64_t b0 = n_begin ? (int64_t)*n_begin : 0;
     const int64_t n = n_end ? (int64_t)*n_end - b0 : n_host;
     src += b0;
@@ -136,12 +157,16 @@ __global__ __launch_bounds__(256) void k_copy_section(const uint8_t *__restrict_
 }
 
 // The max1 rows of chunk j: rows [lk * T + t0, + nj) of every (layer, K|V) lk,
-// packed into the section at dst (zero padded to 16 bytes).
+// packed into the section at dst (zero padded to 16 bytes).  Chunk y of a run
+// (blockIdx.y) starts t0_stride tokens later and is written dst_stride
+// elements further on.
 __global__ __launch_bounds__(256) void k_gather_max1(const uint16_t *__restrict__ max1,
                                                      uint16_t *__restrict__ dst, int64_t T,
                                                      int64_t t0, int64_t nj, int64_t n_lk,
-                                                     int64_t padded)
+                                                     int64_t padded, int64_t t0_stride, int64_t dst_stride)
 {
+    t0 += (int64_t)blockIdx.y * t0_stride;
+    dst += (int64_t)blockIdx.y * dst_stride;
     const int64_t n = n_lk * nj;
     const int64_t step = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < padded / 2; i += step) {
@@ -232,50 +257,56 @@ hipError_t launch_serialize(const uint16_t *cdf, const uint16_t *max1, const uin
                             int64_t out_cap, const KParams &p, int32_t *status, hipStream_t stream)
 {
     const ContainerLayout cl = container_layout(p);
+    const int64_t z = 0;
     hipLaunchKernelGGL(k_ser_header, dim3(1), dim3(64), 0, stream, (const uint64_t *)nullptr,
-                       slab_off + p.n_slabs, out, out_cap, p, cl, status);
+                       slab_off + p.n_slabs, out, out_cap, p, cl, status, z, z);
     const int64_t n_tables = (int64_t)p.NG * 2 * p.L;
     if (n_tables > 0)
         hipLaunchKernelGGL(k_ser_cdf, dim3((unsigned)n_tables), dim3(256), 0, stream, cdf, out, p, cl,
-                           status);
+                           status, z, 1, z, z);
     const int64_t rows_b = 2 * p.n_rows, lens_b = 2 * p.n_streams;
     const uint64_t *none = nullptr;
     hipLaunchKernelGGL(k_copy_section, dim3(grid_for(rows_b, 1024)), dim3(256), 0, stream,
-                       (const uint8_t *)max1, out + cl.max1, rows_b, none, none, (int64_t)0,
-                       cl.len - cl.max1);
+                       (const uint8_t *)max1, out + cl.max1, rows_b, none, none, z, cl.len - cl.max1, z, z, z);
     hipLaunchKernelGGL(k_copy_section, dim3(grid_for(lens_b, 1024)), dim3(256), 0, stream,
-                       (const uint8_t *)stream_len, out + cl.len, lens_b, none, none, (int64_t)0,
-                       cl.pay - cl.len);
+                       (const uint8_t *)stream_len, out + cl.len, lens_b, none, none, z, cl.pay - cl.len, z, z,
+                       z);
     // the payload size is known on the device only: size the grid for the capacity
     hipLaunchKernelGGL(k_copy_section, dim3(grid_for(out_cap - cl.pay, 4096)), dim3(256), 0, stream,
-                       payload, out + cl.pay, (int64_t)0, none, slab_off + p.n_slabs, (int64_t)16,
-                       out_cap - cl.pay);
+                       payload, out + cl.pay, z, none, slab_off + p.n_slabs, (int64_t)16, out_cap - cl.pay,
+                       z, z, z);
     return hipGetLastError();
 }
 
-hipError_t launch_serialize_chunk(const ChunkSrc &src, uint8_t *out, int64_t out_cap, const KParams &p,
-                                  int32_t *status, hipStream_t stream)
+hipError_t launch_serialize_chunks(const ChunkRun &run, uint8_t *out, int64_t out_stride, const KParams &p,
+                                   int32_t *status, hipStream_t stream)
 {
-    // p describes the chunk as a tensor of its own: T = N_j, one chunk, 2L slabs,
-    // one table per slab (S = 1)
+    // p describes one chunk of the run as a tensor of its own: T = N_j, one
+    // chunk, 2L slabs, one table per slab (S = 1)
+    if (run.n <= 0) return hipSuccess;
     const ContainerLayout cl = container_layout(p);
-    const int64_t twoL = 2 * (int64_t)p.L;
-    const uint64_t *off0 = src.off, *off1 = src.off + twoL;
-    hipLaunchKernelGGL(k_ser_header, dim3(1), dim3(64), 0, stream, off0, off1, out, out_cap, p, cl,
-                       status);
+    const int64_t twoL = 2 * (int64_t)p.L, out_cap = out_stride;
+    const unsigned n = (unsigned)run.n;
+    const uint64_t *off0 = run.off, *off1 = run.off + twoL;
+    hipLaunchKernelGGL(k_ser_header, dim3(1, n), dim3(64), 0, stream, off0, off1, out, out_cap, p, cl, status,
+                       twoL, out_stride);
     if (p.n_slabs > 0)
-        hipLaunchKernelGGL(k_ser_cdf, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, src.cdf, out, p, cl,
-                           status);
+        hipLaunchKernelGGL(k_ser_cdf, dim3((unsigned)p.n_slabs, n), dim3(256), 0, stream, run.cdf, out, p, cl,
+                           status, run.j0, run.S, run.table_stride, out_stride);
     const int64_t nj = p.T, rows_padded = cl.len - cl.max1;
-    hipLaunchKernelGGL(k_gather_max1, dim3(grid_for(rows_padded / 2, 1024)), dim3(256), 0, stream,
-                       src.max1, (uint16_t *)(out + cl.max1), src.max1_T, src.t0, nj, twoL, rows_padded);
+    hipLaunchKernelGGL(k_gather_max1, dim3(grid_for(rows_padded / 2, 1024), n), dim3(256), 0, stream,
+                       run.max1, (uint16_t *)(out + cl.max1), run.max1_T, run.j0 * run.Tc, nj, twoL, rows_padded,
+                       run.Tc, out_stride / 2);
     const uint64_t *none = nullptr;
-    const int64_t lens_b = 2 * p.n_streams;
-    hipLaunchKernelGGL(k_copy_section, dim3(grid_for(lens_b, 1024)), dim3(256), 0, stream,
-                       (const uint8_t *)src.stream_len, out + cl.len, lens_b, none, none, (int64_t)0,
-                       cl.pay - cl.len);
-    hipLaunchKernelGGL(k_copy_section, dim3(grid_for(out_cap - cl.pay, 4096)), dim3(256), 0, stream,
-                       src.payload, out + cl.pay, (int64_t)0, off0, off1, (int64_t)16, out_cap - cl.pay);
+    const int64_t lens_b = 2 * p.n_streams, z = 0;
+    hipLaunchKernelGGL(k_copy_section, dim3(grid_for(lens_b, 1024), n), dim3(256), 0, stream,
+                       (const uint8_t *)run.stream_len, out + cl.len, lens_b, none, none, z, cl.pay - cl.len,
+                       lens_b, out_stride, z);
+    // a grid-stride copy: enough blocks per chunk to keep the copies wide,
+    // not one per 4 KB of the capacity
+    const unsigned gp = std::min<unsigned>(grid_for(out_cap - cl.pay, 4096), 256u);
+    hipLaunchKernelGGL(k_copy_section, dim3(gp, n), dim3(256), 0, stream, run.payload, out + cl.pay, z, off0,
+                       off1, (int64_t)16, out_cap - cl.pay, z, out_stride, twoL);
     return hipGetLastError();
 }
 
@@ -291,10 +322,11 @@ hipError_t launch_deserialize(const uint8_t *in, int64_t in_bytes, uint16_t *cdf
     const int64_t rows_b = 2 * p.n_rows, lens_b = 2 * p.n_streams;
     if (rows_b > 0) {
         const uint64_t *none = nullptr;
+        const int64_t z = 0;
         hipLaunchKernelGGL(k_copy_section, dim3(grid_for(rows_b, 1024)), dim3(256), 0, stream,
-                           in + cl.max1, (uint8_t *)max1, rows_b, none, none, (int64_t)0, rows_b);
+                           in + cl.max1, (uint8_t *)max1, rows_b, none, none, z, rows_b, z, z, z);
         hipLaunchKernelGGL(k_copy_section, dim3(grid_for(lens_b, 1024)), dim3(256), 0, stream,
-                           in + cl.len, (uint8_t *)stream_len, lens_b, none, none, (int64_t)0, lens_b);
+                           in + cl.len, (uint8_t *)stream_len, lens_b, none, none, z, lens_b, z, z, z);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

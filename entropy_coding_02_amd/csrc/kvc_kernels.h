@@ -71,25 +71,30 @@ __host__ __device__ inline int64_t container_total(const ContainerLayout &cl, in
 hipError_t launch_serialize(const uint16_t *cdf, const uint16_t *max1, const uint16_t *stream_len,
                             const uint64_t *slab_off, const uint8_t *payload, uint8_t *out,
                             int64_t out_cap, const KParams &p, int32_t *status, hipStream_t stream);
-// What one chunk's container is made of: its 2L slabs of CDF rows, the max1
-// rows of its tokens (rows of max1_T tokens, the chunk's first at token t0),
-// its 2L*N_j stream lengths, the 2L+1 slab offsets around it and the payload
-// they index.
-struct ChunkSrc {
-    const uint16_t *cdf;
-    const uint16_t *max1;
-    int64_t max1_T, t0;
-    const uint16_t *stream_len;
-    const uint64_t *off;
-    const uint8_t *payload;
-};
 // The total_bytes header field of n containers laid stride bytes apart from
 // base (16-byte aligned), into dst[n] (device).
 hipError_t launch_container_totals(const uint8_t *base, int64_t stride, int n, uint64_t *dst,
                                    hipStream_t stream);
-// `chunk` describes the chunk as a tensor of its own (T = N_j).
-hipError_t launch_serialize_chunk(const ChunkSrc &src, uint8_t *out, int64_t out_cap, const KParams &chunk,
-                                  int32_t *status, hipStream_t stream);
+// n consecutive chunks j0 .. j0 + n - 1 of one shape (each with p.T tokens):
+// the whole tensor's tables (groups of S chunks, table_stride entries apart),
+// its max1 rows (max1_T tokens each, chunk j starting at token j * Tc), and
+// chunk j0's stream lengths and 2L + 1 slab offsets, chunk j0 + k's following
+// k * 2L * p.T lengths and k * 2L offsets further on, all indexing payload.
+struct ChunkRun {
+    const uint16_t *cdf;
+    int32_t S;
+    int64_t table_stride;
+    const uint16_t *max1;
+    int64_t max1_T, Tc, j0;
+    const uint16_t *stream_len;
+    const uint64_t *off;
+    const uint8_t *payload;
+    int64_t n;
+};
+// The containers of a run, container k at out + k * out_stride (each at most
+// out_stride bytes); `chunk` describes one chunk as a tensor of its own.
+hipError_t launch_serialize_chunks(const ChunkRun &run, uint8_t *out, int64_t out_stride,
+                                   const KParams &chunk, int32_t *status, hipStream_t stream);
 hipError_t launch_deserialize(const uint8_t *in, int64_t in_bytes, uint16_t *cdf, uint16_t *max1,
                               uint16_t *stream_len, uint64_t *slab_off, const KParams &p,
                               int32_t *status, hipStream_t stream);
