@@ -311,6 +311,10 @@ __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
     // staging: lane l loads 16 bytes = dword k of streams 4m .. 4m + 3 (m = l % PPR) for
     // k = k0 + RPL q + l / PPR, so one wave-wide load covers RPL slot rows
     const int sg = lane / PPR, sm = lane % PPR;
+    // a load covers streams 4 sm .. 4 sm + 3: only their longest needs slot row k
+    int ndw4 = max(ndw, __shfl_xor(ndw, 1, 64));
+    ndw4 = max(ndw4, __shfl_xor(ndw4, 2, 64));
+    const int ndw_grp = __shfl(ndw4, 4 * sm, 64);
 
     for (int r = 0; r < rounds; ++r) {
         const int k0 = r * PACK_W;
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
 #pragma unroll
         for (int q = 0; q < PACK_W / RPL; ++q) {
             const int k = k0 + RPL * q + sg;
-            v4[q] = k < ndw_max ? *(const u32x4 *)(srcw + (int64_t)k * 256 + 4 * sm) : u32x4{0, 0, 0, 0};
+            v4[q] = k < ndw_grp ? *(const u32x4 *)(srcw + (int64_t)k * 256 + 4 * sm) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int q = 0; q < PACK_W / RPL; ++q) {
