@@ -275,9 +275,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     lds_u32 *const pr = tile + n16;
     lds_u32 *const xs = pr + CT * A;  // output staging: per wave 16 rows of 36 dwords
 
+    // blocks in memory order: consecutive blocks take consecutive chunks of one
+    // (layer, K|V), whose output rows lie back to back, not the 2L slabs of one
+    // chunk, which lie a whole (layer, K|V) apart: the rows written at the same
+    // time then share DRAM pages
     const int bps = (p.Tc + 255) / 256;
-    const int64_t slab = blockIdx.x / bps;
-    const int tb = (int)(blockIdx.x - slab * bps);
+    const int64_t sb = blockIdx.x / bps;
+    const int tb = (int)(blockIdx.x - sb * bps);
+    const int64_t slab = (sb % p.NC) * (2 * (int64_t)p.L) + sb / p.NC;
     const int t = tb * 256 + (int)threadIdx.x;
     const SlabGeom g = slab_geom(p, slab);
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;

@@ -13,6 +13,15 @@
 
 namespace {
 
+// Slab of fused-pass block b, numbered so that blocks that run at the same
+// time read neighbouring memory: consecutive blocks take consecutive chunks
+// of one (layer, K|V), whose rows lie back to back, instead of the 2L slabs
+// of one chunk, which lie a whole (layer, K|V) apart (one block per slab).
+__device__ inline int64_t slab_in_memory_order(const KParams &p, int64_t b)
+{
+    return (b % p.NC) * (2 * (int64_t)p.L) + b / p.NC;
+}
+
 __device__ __forceinline__ uint32_t quant1f(float x, float factor, float M)
 {
     float p = x * factor;
@@ -235,7 +244,7 @@ __global__ __launch_bounds__(1024) void k_quant_cdf(const uint16_t *__restrict__
 {
     extern __shared__ uint32_t hist[];
     lds_u8 *const h8 = (lds_u8 *)hist;
-    const int64_t slab = blockIdx.x;
+    const int64_t slab = slab_in_memory_order(p, blockIdx.x);
     const SlabGeom g = slab_geom(p, slab);
     const int C = p.C, A = p.A, C8 = C / 8;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -339,7 +348,7 @@ __global__ __launch_bounds__(1024) void k_quant_cdf_levels(const uint16_t *__res
                                                            LevelParams lv, int32_t *status)
 {
     extern __shared__ uint32_t hist[];
-    const int64_t slab = blockIdx.x;
+    const int64_t slab = slab_in_memory_order(p, blockIdx.x);
     const SlabGeom g = slab_geom(p, slab);
     const int C = p.C, C8 = C / 8;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
