@@ -263,7 +263,10 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *slab_total, uint6
 // as byte stores; a store instruction thus covers up to 256 contiguous
 // payload bytes and no byte of a neighbouring stream is touched.  Nothing is
 // written at or past payload_cap.
-constexpr int PACK_W = 64;  // slot dwords per stream and round
+// slot dwords per stream and round: 32 keeps the window small enough for
+// about twice the waves per CU of 64 (the copy is latency-bound), and covers
+// most streams of the larger workloads in one round
+constexpr int PACK_W = 32;
 
 template <int SPW>
 __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
@@ -348,13 +351,13 @@ __global__ __launch_bounds__(64) void k_pack(const uint8_t *__restrict__ slots,
         __syncthreads();
         if (total >= 16u * SPW) {
             // long streams (16 dwords or more on average in this round): one
-            // stream at a time, lane j taking its slot dword k0 + j, fills the
-            // lanes about as well with no search
+            // stream at a time, lane j < PACK_W taking its slot dword k0 + j,
+            // with no search
             const uint32_t j = (uint32_t)(k0 + lane);
             for (int i = 0; i < SPW; ++i) {
                 const uint32_t len_i = s_len[i];
                 if ((uint32_t)k0 * 4u >= len_i) continue;  // uniform: stream i is done
-                if (4u * j >= len_i) continue;
+                if (lane >= PACK_W || 4u * j >= len_i) continue;
                 const uint64_t o_i = ((uint64_t)s_ohi[i] << 32) | s_olo[i];
                 const uint32_t v = win[i * (PACK_W + 1) + lane];
                 const uint64_t b = o_i + 4u * j;
