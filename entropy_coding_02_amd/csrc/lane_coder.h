@@ -633,14 +633,16 @@ KVC_HD uint32_t cdf_nstep(uint32_t A)
 //
 // The ring holds 16 stream dwords per lane (dword j at slot j mod 16) and a
 // 17th slot with a copy of slot 0, so a window read at slot 15 needs no
-// wrap.  Feeding is RingIn's: a 16-byte piece (4 stream dwords) is fetched
-// one group of 8 symbols before it is committed; pieces past the stream's
-// end are written as zeros without a load.  At a group start, after
-// the commit, w - posb/32 >= 6 holds: the group consumes at most 16 bytes
-// (4 dwords) and a window needs 2 dwords, and a piece is asked for whenever
-// w - posb/32 <= 10, so the next group starts with at least 6 again.  A
-// commit overwrites the slots of dwords w - 16 .. w - 13, none of which is
-// still needed (w - posb/32 <= 10 when the piece was asked for).
+// wrap.  The ring starts full (stream dwords 0..15), so a stream of up to 64
+// bytes needs no further loads.  Feeding is RingIn's: a 16-byte piece (4
+// stream dwords) is fetched one group of 8 symbols before it is committed;
+// pieces past the stream's end are written as zeros without a load.  At a
+// group start, after the commit, w - posb/32 >= 6 holds: the group consumes
+// at most 16 bytes (4 dwords) and a window needs 2 dwords, and a piece is
+// asked for whenever w - posb/32 <= 10, so the next group starts with at
+// least 6 again.  A commit overwrites the slots of dwords w - 16 .. w - 13,
+// none of which is still needed (w - posb/32 <= 10 when the piece was asked
+// for).
 template <class Ring>
 struct WinIn {
     const uint8_t *p;  // base + a0
@@ -708,15 +710,32 @@ struct WinIn {
         const uint64_t room = capacity - 16u;  // the last piece starts here
         lim16 = a0 > room ? -(int32_t)(a0 - room) : (room - a0 > 0x7FFFFFF0u ? 0x7FFFFFF0 : (int32_t)(room - a0));
         ring = rg;
-        w = 0;
         last = *(const uint32_t *)p;
-        issue();
-        commit();
-        issue();
-        commit();  // stream dwords 0..7 in the ring
-        want = 4u * w < len ? 1u : 0u;
-        if (want) issue();  // stream dwords 8..11 in flight
-        else zeros();       // a stream of at most 32 bytes is all in the ring
+        // the whole ring, stream dwords 0..15, from four pieces requested
+        // together (a piece wholly past the stream is not fetched: commit
+        // zeroes every byte past the stream); nothing is in flight after it
+        kvc_u32x4 pc[4];
+        uint32_t bk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            w = 4u * (uint32_t)k;
+            if (k < 2 || 4u * w < len) {
+                issue();
+            } else {
+                st = kvc_u32x4{0u, 0u, 0u, 0u};
+                back = 0u;
+            }
+            pc[k] = st;
+            bk[k] = back;
+        }
+        w = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            st = pc[k];
+            back = bk[k];
+            commit();
+        }
+        want = 0;
         posb = 32;
         return ring[0];
     }
