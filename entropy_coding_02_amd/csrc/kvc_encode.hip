@@ -792,15 +792,19 @@ __global__ void k_zero_u64(uint64_t *dst) { *dst = 0; }
 
 }  // namespace
 
-// Launches of at most this many streams stage wider CDF and symbol tiles.
+// Launches of at most this many streams stage wider CDF tiles.
 constexpr int64_t KVC_ENC_WIDE_MAX_STREAMS = 32768;
 // Launches of at most this many streams code 16 streams per wave, others 64.
 constexpr int64_t KVC_ENC_SPARSE_MAX_STREAMS = 16384;
 // Launches of at most this many streams pack 16 streams per wave, others 64.
 constexpr int64_t KVC_PACK_SPARSE_MAX_STREAMS = 16384;
 
-// Symbol tile width: 128 channels for launches of few streams, else 64.
-static int enc_symbol_tile(int64_t n_streams) { return n_streams <= KVC_ENC_WIDE_MAX_STREAMS ? 128 : 64; }
+// Symbol tile width: 128 channels, the whole 128-byte line of each token row
+// of 1024 channels, so every line of the symbols is read from memory once.
+// (64-channel tiles read each line twice, its halves a tile apart with the
+// first copy gone from L2 in between: 16.4 GB read for 9.8 GB of symbols and
+// tables at the 34B 80K shape, against 9.8 GB now.)
+constexpr int ENC_SYMBOL_TILE = 128;
 
 // Streams coded per wave.
 static int enc_streams_per_wave(int64_t n_streams) { return n_streams <= KVC_ENC_SPARSE_MAX_STREAMS ? 16 : 64; }
@@ -841,7 +845,7 @@ static int enc_split_chunk(const KParams &p, size_t *lds)
 // pairs per thread.
 static int enc_tile_channels(int A, int64_t n_streams)
 {
-    const int sw = enc_symbol_tile(n_streams);
+    const int sw = ENC_SYMBOL_TILE;
     int ct = 16;
     if (n_streams <= KVC_ENC_WIDE_MAX_STREAMS)
         while (ct < sw && 2 * ct * (A / 2) <= 8 * 256) ct *= 2;
@@ -867,7 +871,6 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
     const int CT = enc_tile_channels(p.A, p.n_streams);
     const size_t lds_pairs = (size_t)CT * p.A * sizeof(uint32_t);
     const int per = (CT * (p.A / 2) + 255) / 256;  // pairs staged per thread
-    const int sw = enc_symbol_tile(p.n_streams);
     const int spw = enc_streams_per_wave(p.n_streams);
     const dim3 grid((unsigned)(regions * (64 / spw)));
     size_t lds_split = 0;
@@ -916,11 +919,10 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
             else KVC_ENC(false, 8, S, W, lds_pairs);                                                 \
         }                                                                                            \
     }
-    if (spw == 16) {
-        if (sw == 128) KVC_ENC_S(128, 16) else KVC_ENC_S(64, 16)
-    } else {
-        if (sw == 128) KVC_ENC_S(128, 64) else KVC_ENC_S(64, 64)
-    }
+    if (spw == 16)
+        KVC_ENC_S(ENC_SYMBOL_TILE, 16)
+    else
+        KVC_ENC_S(ENC_SYMBOL_TILE, 64)
 #undef KVC_ENC_S
 #undef KVC_ENC4
 #undef KVC_ENC
