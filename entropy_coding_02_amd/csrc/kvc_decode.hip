@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     const uint8_t *__restrict__ payload, int64_t payload_bytes, const uint64_t *__restrict__ slab_off,
     const uint16_t *__restrict__ stream_len, const uint16_t *__restrict__ cdf,
     const uint16_t *__restrict__ max1, uint8_t *__restrict__ sym_out, void *__restrict__ out, KParams p,
-    int32_t *status, int CT)
+    int32_t *status, int CT, int A_st, int64_t sb0, int guard)
 {
     // LDS: lut[256] f32 | ring[17][256] u32 | rec[2][CT][RS] u32 | rows16 [CT][P2] u16 |
     //      pairs [CT][A] u32 | output staging [4 waves][16 rows][36] u32
@@ -264,7 +264,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     constexpr int NB = 1 << (NSTEP - 3);
     constexpr int RS = DEC_MODE_RS(NSTEP);
     constexpr int PER = DEC_MODE_PER(NSTEP);  // pairs staged per thread: CT * A / 2 / 256
-    const int C = p.C, A = p.A;
+    // A: the entries staged and searched per row; AR: the table's row length
+    // (A < AR only on a launch over slabs whose symbols all lie below A - 1)
+    const int C = p.C, A = A_st, AR = p.A;
+    // the guard launch (after launches with A < AR) decodes only when one of
+    // them found a stream inconsistent with its tables
+    if (guard && (__atomic_load_n(status, __ATOMIC_RELAXED) & KVC_DEV_CORRUPT) == 0) return;
     float *lut = (float *)lds;
     const lds_u32 *const lutw = (const lds_u32 *)lds;
     const LaneRing ring{(lds_u32 *)(lds + 256) + threadIdx.x};  // slot i at [(16 - i) * 256]
@@ -280,8 +285,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     // chunk, which lie a whole (layer, K|V) apart: the rows written at the same
     // time then share DRAM pages
     const int bps = (p.Tc + 255) / 256;
-    const int64_t sb = blockIdx.x / bps;
-    const int tb = (int)(blockIdx.x - sb * bps);
+    const int64_t sbl = blockIdx.x / bps;  // slab of the launch's range
+    const int tb = (int)(blockIdx.x - sbl * bps);
+    const int64_t sb = sb0 + sbl;
     const int64_t slab = (sb % p.NC) * (2 * (int64_t)p.L) + sb / p.NC;
     const int t = tb * 256 + (int)threadIdx.x;
     const SlabGeom g = slab_geom(p, slab);
@@ -332,7 +338,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
     const float m = (ODT >= 0) ? kvc_h2f(max1[row]) : 0.0f;
     BadMask bad;
     uint8_t *so = (OUT & OUT_SYM) ? sym_out + row * C : nullptr;
-    const uint16_t *srows = cdf + g.tab * C * A;
+    const uint16_t *srows = cdf + g.tab * C * AR;
     const int ntiles = (C + CT - 1) / CT;
     const lds_u32 *rec = recs;
     // the mode part of tile channel cl's record (a broadcast read: every lane
@@ -413,7 +419,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
                  cs, nch);
     };
     const bool wave_on = nact > 0;
-    pt.load(srows, 0, CT, C, A);
+    pt.load(srows, 0, CT, C, A, AR);
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
         lds_u32 *const rnow = recs + (it & 1) * CT * RS;
@@ -421,7 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTEP <= 5 
         pt.store_mode(pr, CT, A, r16, (int)P2, (const uint32_t *)lut, rnow, recs + ((it + 1) & 1) * CT * RS, RS);
         __syncthreads();
         rec = rnow;
-        if (it + 1 < ntiles) pt.load(srows, c0 + CT, CT, C, A);
+        if (it + 1 < ntiles) pt.load(srows, c0 + CT, CT, C, A, AR);
         if (!wave_on) continue;
         if constexpr (VEC) {
             // halves of 32 channels (CT is a multiple of 32; C of 16)
@@ -904,6 +910,46 @@ static hipError_t launch_decode_group(const uint8_t *payload, int64_t payload_by
     return hipGetLastError();
 }
 
+// KVC_DEC_N(V, O) over the output modes and vector forms (kvc_decode rejects
+// a call with nothing to write)
+#define KVC_DEC_DISPATCH                                                                             \
+    {                                                                                                \
+        if (vec) {                                                                                   \
+            switch (mode) {                                                                          \
+            case OUT_F16: KVC_DEC_N(true, OUT_F16) break;                                            \
+            case OUT_F32: KVC_DEC_N(true, OUT_F32) break;                                            \
+            case OUT_SYM: KVC_DEC_N(true, OUT_SYM) break;                                            \
+            case OUT_F16 | OUT_SYM: KVC_DEC_N(true, OUT_F16 | OUT_SYM) break;                        \
+            case OUT_F32 | OUT_SYM: KVC_DEC_N(true, OUT_F32 | OUT_SYM) break;                        \
+            default: break;                                                                          \
+            }                                                                                        \
+        } else {                                                                                     \
+            switch (mode) {                                                                          \
+            case OUT_F16: KVC_DEC_N(false, OUT_F16) break;                                           \
+            case OUT_F32: KVC_DEC_N(false, OUT_F32) break;                                           \
+            case OUT_SYM: KVC_DEC_N(false, OUT_SYM) break;                                           \
+            case OUT_F16 | OUT_SYM: KVC_DEC_N(false, OUT_F16 | OUT_SYM) break;                       \
+            case OUT_F32 | OUT_SYM: KVC_DEC_N(false, OUT_F32 | OUT_SYM) break;                       \
+            default: break;                                                                          \
+            }                                                                                        \
+        }                                                                                            \
+    }
+
+// Runs of (layer, K|V) pairs decoded with a shallower search than the
+// table's rows need take at least this many blocks (four times what the chip
+// holds at once), else they search whole rows with their neighbours.
+constexpr int64_t KVC_DEC_RUN_MIN_BLOCKS = 4096;
+
+// Search depth of the mode-first decoder for (layer, K|V) lk: that of its
+// bins, at least nmin and at most the table's (nstep).
+static int dec_run_nstep(const KParams &p, int lk, int nstep, int nmin)
+{
+    const int bins = 2 * ((int)p.maxq[lk] + 1);
+    int n = (int)cdf_nstep((uint32_t)bins);
+    if (n < nmin) n = nmin;
+    return n < nstep ? n : nstep;
+}
+
 hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const uint64_t *slab_off,
                          const uint16_t *stream_len, const uint16_t *cdf, const uint16_t *max1,
                          uint8_t *sym_out, void *out, int out_dtype, const KParams &p,
@@ -924,53 +970,97 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
     // the two-level search, measured faster than binary lifting at every
     // launch size since its searches run over registers); 4-entry and 128-
     // or 256-entry rows binary lifting.
-    const int CT_mode = dec_mode_tile_channels(nstep);
-    const size_t lds_mode = dec_mode_lds_bytes(p.A, CT_mode, nstep);
-    // the staging covers DEC_MODE_PER(nstep) pairs per thread: never launch a
-    // tile it would stage only in part
-    if (nstep >= 3 && nstep <= 6 && CT_mode * (p.A / 2) > 256 * DEC_MODE_PER(nstep)) return hipErrorInvalidValue;
-#define KVC_DEC(V, O, N, B)                                                                          \
-    hipLaunchKernelGGL((k_decode<V, O, N, B>), grid, block, lds, stream, payload, payload_bytes,     \
-                       slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
+    if (nstep >= 3 && nstep <= 6) {
+        // One launch per run of consecutive (layer, K|V) pairs whose symbols
+        // need the same search depth: a run of layers with fewer bins than the
+        // table's rows stages and searches only the first 2^n entries of each
+        // row (n = its depth), every symbol of theirs lying below entry 2^n - 1
+        // (symbols of b bins run to b - 2), with fewer levels, wider tiles and,
+        // below 64 entries, more waves per SIMD.  In memory order block sb
+        // takes (layer, K|V) sb / NC, so a run's blocks are one range of sb.
+        //
+        // Such a run decodes as the full search does until a search lands
+        // past its staged entries, which only a stream inconsistent with its
+        // tables can make happen, and the step that does flags the stream
+        // (its code lies past the last staged interval).  So when any run was
+        // cut short, a guard launch of the full search over every slab follows;
+        // its blocks return at once unless a stream was flagged, and otherwise
+        // decode everything again, so that the outputs are always the full
+        // search's.
+        // (Without a status word nothing could tell the guard, so then every
+        // run searches whole rows.)  Launches on one stream run one after the
+        // other, so a run of fewer than KVC_DEC_RUN_MIN_BLOCKS blocks, which
+        // could not fill the chip for long, searches whole rows too and joins
+        // its neighbours that do.
+        const int LK = 2 * p.L;
+        const int nmin = status ? 3 : nstep;  // the shallowest depth a run may take
+        int run_n[2 * KVC_MAX_LAYERS];  // each (layer, K|V)'s depth
+        for (int lk = 0; lk < LK;) {
+            const int n = dec_run_nstep(p, lk, nstep, nmin);
+            int lk1 = lk + 1;
+            while (lk1 < LK && dec_run_nstep(p, lk1, nstep, nmin) == n) ++lk1;
+            const bool small = bps * (int64_t)(lk1 - lk) * p.NC < KVC_DEC_RUN_MIN_BLOCKS;
+            for (int k = lk; k < lk1; ++k) run_n[k] = small ? nstep : n;
+            lk = lk1;
+        }
+        bool cut = false;
+        for (int lk0 = 0; lk0 <= LK;) {
+            const bool guard_pass = lk0 == LK;  // after the runs: the guard launch
+            if (guard_pass && !cut) break;
+            const int n0 = guard_pass ? nstep : run_n[lk0];
+            int lk1 = guard_pass ? LK + 1 : lk0 + 1;
+            while (lk1 < LK && run_n[lk1] == n0) ++lk1;
+            const int A_st = n0 < nstep ? (1 << n0) : p.A;  // entries staged per row
+            const bool pad = A_st != (1 << n0);
+            cut = cut || A_st < p.A;
+            const int CT_mode = dec_mode_tile_channels(n0);
+            const size_t lds_mode = dec_mode_lds_bytes(A_st, CT_mode, n0);
+            // the staging covers DEC_MODE_PER(n) pairs per thread: never launch a
+            // tile it would stage only in part
+            if (CT_mode * (A_st / 2) > 256 * DEC_MODE_PER(n0)) return hipErrorInvalidValue;
+            const int64_t nlk = guard_pass ? LK : lk1 - lk0;
+            const dim3 grid_run((unsigned)(bps * nlk * p.NC));
+            const int64_t sb0 = guard_pass ? 0 : (int64_t)lk0 * p.NC;
+            const int guard = guard_pass ? 1 : 0;
+#define KVC_DECM(V, O, N, PD)                                                                        \
+    hipLaunchKernelGGL((k_decode_mode<V, O, N, PD>), grid_run, block, lds_mode, stream, payload, \
+                       payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT_mode, \
+                       A_st, sb0, guard)
 #define KVC_DECB(V, O, N)                                                                            \
-    if (p.A == (1 << N))                                                                             \
-        hipLaunchKernelGGL((k_decode_mode<V, O, N, false>), grid, block, lds_mode, stream, \
-                           payload, payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p,  \
-                           status, CT_mode);                                                          \
-    else                                                                                             \
-        hipLaunchKernelGGL((k_decode_mode<V, O, N, true>), grid, block, lds_mode, stream, \
-                           payload, payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p,  \
-                           status, CT_mode)
+    if (pad) KVC_DECM(V, O, N, true);                                                                \
+    else KVC_DECM(V, O, N, false)
 #define KVC_DEC_N(V, O)                                                                              \
-    switch (nstep) {                                                                                 \
-    case 2: KVC_DEC(V, O, 2, false); break;                                                          \
+    switch (n0) {                                                                                    \
     case 3: KVC_DECB(V, O, 3); break;                                                                \
     case 4: KVC_DECB(V, O, 4); break;                                                                \
     case 5: KVC_DECB(V, O, 5); break;                                                                \
-    case 6: KVC_DECB(V, O, 6); break;                                                                \
+    default: KVC_DECB(V, O, 6); break;                                                               \
+    }
+            KVC_DEC_DISPATCH
+#undef KVC_DEC_N
+#undef KVC_DECB
+#undef KVC_DECM
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            lk0 = lk1;
+        }
+        return hipSuccess;
+    }
+#define KVC_DEC(V, O, N, B)                                                                          \
+    hipLaunchKernelGGL((k_decode<V, O, N, B>), grid, block, lds, stream, payload, payload_bytes,     \
+                       slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT)
+#define KVC_DEC_N(V, O)                                                                              \
+    switch (nstep) {                                                                                 \
+    case 2: KVC_DEC(V, O, 2, false); break;                                                          \
     case 7: KVC_DEC(V, O, 7, false); break;                                                          \
     default: KVC_DEC(V, O, 8, false); break;                                                         \
     }
-#define KVC_DEC_M(V)                                                                                 \
-    switch (mode) {                                                                                  \
-    case OUT_F16: KVC_DEC_N(V, OUT_F16) break;                                                       \
-    case OUT_F32: KVC_DEC_N(V, OUT_F32) break;                                                       \
-    case OUT_SYM: KVC_DEC_N(V, OUT_SYM) break;                                                       \
-    case OUT_F16 | OUT_SYM: KVC_DEC_N(V, OUT_F16 | OUT_SYM) break;                                   \
-    case OUT_F32 | OUT_SYM: KVC_DEC_N(V, OUT_F32 | OUT_SYM) break;                                   \
-    default: break; /* nothing to write: rejected by kvc_decode */                                  \
-    }
-    if (vec) {
-        KVC_DEC_M(true)
-    } else {
-        KVC_DEC_M(false)
-    }
-#undef KVC_DEC_M
+    KVC_DEC_DISPATCH
 #undef KVC_DEC_N
-#undef KVC_DECB
 #undef KVC_DEC
     return hipGetLastError();
 }
+#undef KVC_DEC_DISPATCH
 
 hipError_t launch_dequantize(const uint8_t *sym, const uint16_t *max1, void *out, int out_dtype,
                              const KParams &p, bool vec, hipStream_t stream)

@@ -8,13 +8,16 @@
 // Stage CDF rows [c0, c0+CT) of a slab as packed (start, frequency) pairs.
 // Thread i handles the entry pairs (2j, 2j+1) with index i, i+256, ...: one
 // 4-byte load of cdf[2j], cdf[2j+1] plus cdf[2j+2] for the second frequency
-// (A is even, so rows and pairs are 4-byte aligned).
+// (A is even, so rows and pairs are 4-byte aligned).  load() stages the first
+// A entries of rows AR entries long (AR >= A, even; AR = A when omitted): the
+// last staged entry's frequency then comes from the row's entry A.
 template <int kMaxPer>  // pairs per thread: CT * A / 2 / 256 rounded up
 struct PairTile {
     uint32_t w[kMaxPer], n2[kMaxPer];
 
-    __device__ void load(const uint16_t *rows, int c0, int CT, int C, int A)
+    __device__ void load(const uint16_t *rows, int c0, int CT, int C, int A, int AR = 0)
     {
+        if (AR < A) AR = A;
         const int npairs = CT * (A >> 1);
 #pragma unroll
         for (int i = 0; i < kMaxPer; ++i) {
@@ -24,9 +27,9 @@ struct PairTile {
             if (e < npairs) {
                 const int cl = e / (A >> 1), k = (e - cl * (A >> 1)) * 2;
                 if (c0 + cl < C) {
-                    const uint16_t *row = rows + (int64_t)(c0 + cl) * A;
+                    const uint16_t *row = rows + (int64_t)(c0 + cl) * AR;
                     w[i] = *(const uint32_t *)(row + k);
-                    if (k + 2 < A) n2[i] = row[k + 2];
+                    if (k + 2 < AR) n2[i] = row[k + 2];
                 }
             }
         }

@@ -69,6 +69,14 @@ SMALL = {
     "one_lane_A64_C80_T9000": cfg_of(1, 80, 9000, 256, ((0, 1, 64),), seed=17, innov="t3", of=0.05, om=50),
     "one_lane_A40_C96_T9000": cfg_of(1, 96, 9000, 256, ((0, 1, 40),), seed=18),
     "one_lane_A32_C200_T9000": cfg_of(1, 200, 9000, 256, ((0, 1, 32),), seed=19, lo=0.05, hi=8.0, of=0.02, om=20),
+    # layers with fewer bins than the table's rows: the mode-first decoder
+    # takes a run of them with at least 4096 slabs in a launch of its own that
+    # searches only the first 16 entries of each row (16-token chunks give
+    # 2048 slabs per layer and K|V); shorter runs search whole rows
+    "one_lane_A32_A16_C16_T32768_Tc16": cfg_of(2, 16, 32768, 16, ((0, 1, 32), (1, 2, 16)), seed=20),
+    "one_lane_A32_A16_C64_T9000": cfg_of(2, 64, 9000, 256, ((0, 1, 32), (1, 2, 16)), seed=23),
+    "one_lane_A64_A32_A16_C48_T6000": cfg_of(3, 48, 6000, 256, ((0, 1, 64), (1, 2, 32), (2, 3, 16)), seed=21,
+                                             innov="t3", of=0.05, om=50),
 }
 
 
@@ -123,6 +131,15 @@ def test_edge_values():
         compare_full("edge_values", kv, bins, 16, out_dtype=odt)
 
 
+def test_one_lane_runs_of_kv_bins():
+    """K and V of a layer with different bins (32 | 16, then 16 | 32): the
+    mode-first decoder's launches split where the search depth changes (the
+    16-entry run of 4096 slabs between two whole-row ones)."""
+    cfg = cfg_of(2, 16, 32768, 16, ((0, 2, 32),), seed=22)
+    kv, _ = kvgen.generate(cfg)
+    compare_full("one_lane_kv_bins", kv, np.array([[32, 16], [16, 32]], np.int32), cfg.chunk_tokens)
+
+
 def test_empty_input():
     say("[gpu] empty input")
     import torch
@@ -151,9 +168,13 @@ def test_nonfinite_flagged():
     assert int(buf.dev_status.item()) & kvc.KVC_DEV_NONFINITE
 
 
-@pytest.mark.parametrize("name", ["ragged_L3_C40_T300_Tc128", "one_lane_A32_C200_T9000"])
+@pytest.mark.parametrize("name", ["ragged_L3_C40_T300_Tc128", "one_lane_A32_C200_T9000",
+                                  "one_lane_A32_A16_C16_T32768_Tc16"])
 def test_corrupt_payload_flagged_and_bounded(name):
-    """Group decoder, then the one-lane mode-first decoder (a wave-wide flag mask)."""
+    """Group decoder, then the one-lane mode-first decoder (a wave-wide flag
+    mask), then the latter on layers whose launches search only the first 16
+    entries of each row: a code past them flags the stream, and the guard
+    launch decodes every stream again over whole rows."""
     say(f"[gpu] corrupt payload {name}")
     import torch
     cfg = SMALL[name]
