@@ -104,19 +104,32 @@ def summarize_pmc(read_csv: str, write_csv: str, workload: str):
     reads weighted by request size (32 / 64 / 128 bytes), writes as 32- and
     64-byte requests, and the share of requests that went to DRAM.  The
     --calibrate-copy kernel (COPY_BYTES read and written) gives the scale that
-    turns the weighted counts into bytes (it should be about 1).  Medians over
-    dispatches, into profiles/traffic.json."""
+    turns the weighted counts into bytes (it should be about 1).  A call is a
+    run of consecutive dispatches of one kernel (kvc_decode launches the
+    mode-first decoder once per run of layers with equal search depth, then
+    a guard launch): their counts are summed.  Medians over calls, into
+    profiles/traffic.json."""
     import csv
 
     def per_kernel(path, names):
-        vals = {}
+        disp = {}  # dispatch id -> (kernel key, {counter: value})
         for r in csv.DictReader(open(path)):
             if r.get("Counter_Name") not in names:
                 continue
-            key = kernel_key(r["Kernel_Name"])
-            if key:
-                d = vals.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})
-                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            did = int(r["Dispatch_Id"])
+            key, d = disp.setdefault(did, (kernel_key(r["Kernel_Name"]), {}))
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        vals, prev, call = {}, None, None
+        for did in sorted(disp):
+            key, d = disp[did]
+            if key is None:
+                prev = None
+                continue
+            if key != prev:
+                call = vals.setdefault(key, {}).setdefault(did, {})
+            for c, v in d.items():
+                call[c] = call.get(c, 0.0) + v
+            prev = key
         return vals
 
     def med(xs):
@@ -651,10 +664,11 @@ def main():
     stages = {k: {"ms": round(ms[k], 4), "algorithmic_bytes": alg[k],
                   "GBps": round(alg[k] / (ms[k] * 1e-3) / 1e9, 1),
                   "frac_hbm": round(alg[k] / (ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)} for k in alg}
-    # the decode stage is one decode launch: its duration is the stage's
+    # the decode stage is one kvc_decode call: its duration is the stage's
     dec_bytes = alg["decode_dequant"]
-    # the launch kvc_decode makes: several lanes per stream on small launches, else one lane per
-    # stream with the mode-first search for rows of 5 to 64 entries, binary lifting otherwise
+    # the kernel kvc_decode launches: several lanes per stream on small launches, else one lane
+    # per stream with the mode-first search for rows of 5 to 64 entries (once per run of layers
+    # with equal search depth, then a guard launch), binary lifting otherwise
     dec_kernel = ("k_decode_group" if d.decode_lanes > 1 else
                   "k_decode_mode" if 4 < d.alphabet <= 64 else "k_decode")
     achieved = dec_bytes / (d_avg * 1e-3) / 1e9
