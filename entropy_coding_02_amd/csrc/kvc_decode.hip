@@ -14,6 +14,8 @@
 //
 // k_decode_group: launches of few streams, G lanes per stream splitting each
 // symbol's search over rows of (start, frequency) keys (comment at the kernel).
+#include <mutex>
+
 #include "kvc_common.h"
 #include "kvc_kernels.h"
 #include "lane_coder.h"
@@ -935,6 +937,39 @@ static hipError_t launch_decode_group(const uint8_t *payload, int64_t payload_by
         }                                                                                            \
     }
 
+// Streams on which launch_decode runs the mode-first decoder's runs after the
+// first one, concurrently with it, and the events that fork them from the
+// caller's stream and join them back before the guard launch: made on first
+// use on each device, at the default priority.  g_run_mu is held from the fork
+// to the join, so that calls from several host threads do not interleave
+// their records and waits on the shared events.
+constexpr int kRunStreams = 3;
+constexpr int kRunDevices = 64;
+struct RunStreams {
+    hipStream_t s[kRunStreams];
+    hipEvent_t fork, join[kRunStreams];
+};
+static std::mutex g_run_mu;
+static RunStreams *g_runs[kRunDevices];
+
+// The current device's streams (g_run_mu held), or NULL if they cannot be made
+// (the runs then go one after the other on the caller's stream).
+static RunStreams *run_streams()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kRunDevices) return nullptr;
+    if (!g_runs[dev]) {
+        RunStreams r{};
+        bool ok = hipEventCreateWithFlags(&r.fork, hipEventDisableTiming) == hipSuccess;
+        for (int i = 0; ok && i < kRunStreams; ++i)
+            ok = hipStreamCreateWithFlags(&r.s[i], hipStreamNonBlocking) == hipSuccess &&
+                 hipEventCreateWithFlags(&r.join[i], hipEventDisableTiming) == hipSuccess;
+        if (!ok) return nullptr;
+        g_runs[dev] = new RunStreams(r);
+    }
+    return g_runs[dev];
+}
+
 // Runs of (layer, K|V) pairs decoded with a shallower search than the
 // table's rows need take at least this many blocks (four times what the chip
 // holds at once), else they search whole rows with their neighbours.
@@ -1003,13 +1038,39 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
             for (int k = lk; k < lk1; ++k) run_n[k] = small ? nstep : n;
             lk = lk1;
         }
+        int n_runs = 0;
+        for (int lk = 0; lk < LK; ++lk) n_runs += lk == 0 || run_n[lk] != run_n[lk - 1];
+        // The runs after the first go on streams of their own, concurrently
+        // with it (each run's last, partly filled wave of blocks then overlaps
+        // another run's), joined back before the guard.
+        std::unique_lock<std::mutex> run_lock(g_run_mu, std::defer_lock);
+        RunStreams *rs = nullptr;
+        if (n_runs > 1) {
+            run_lock.lock();
+            rs = run_streams();
+            if (rs && hipEventRecord(rs->fork, stream) != hipSuccess) return hipErrorLaunchFailure;
+        }
         bool cut = false;
+        int run = 0;
         for (int lk0 = 0; lk0 <= LK;) {
             const bool guard_pass = lk0 == LK;  // after the runs: the guard launch
+            if (guard_pass && rs) {
+                for (int i = 0; i < kRunStreams && i < n_runs - 1; ++i)
+                    if (hipEventRecord(rs->join[i], rs->s[i]) != hipSuccess ||
+                        hipStreamWaitEvent(stream, rs->join[i], 0) != hipSuccess)
+                        return hipErrorLaunchFailure;
+            }
             if (guard_pass && !cut) break;
             const int n0 = guard_pass ? nstep : run_n[lk0];
             int lk1 = guard_pass ? LK + 1 : lk0 + 1;
             while (lk1 < LK && run_n[lk1] == n0) ++lk1;
+            hipStream_t st = stream;  // this launch's stream
+            if (rs && !guard_pass && run > 0) {
+                st = rs->s[(run - 1) % kRunStreams];
+                if (run <= kRunStreams && hipStreamWaitEvent(st, rs->fork, 0) != hipSuccess)
+                    return hipErrorLaunchFailure;
+            }
+            run += guard_pass ? 0 : 1;
             const int A_st = n0 < nstep ? (1 << n0) : p.A;  // entries staged per row
             const bool pad = A_st != (1 << n0);
             cut = cut || A_st < p.A;
@@ -1023,7 +1084,7 @@ hipError_t launch_decode(const uint8_t *payload, int64_t payload_bytes, const ui
             const int64_t sb0 = guard_pass ? 0 : (int64_t)lk0 * p.NC;
             const int guard = guard_pass ? 1 : 0;
 #define KVC_DECM(V, O, N, PD)                                                                        \
-    hipLaunchKernelGGL((k_decode_mode<V, O, N, PD>), grid_run, block, lds_mode, stream, payload, \
+    hipLaunchKernelGGL((k_decode_mode<V, O, N, PD>), grid_run, block, lds_mode, st, payload,     \
                        payload_bytes, slab_off, stream_len, cdf, max1, sym_out, out, p, status, CT_mode, \
                        A_st, sb0, guard)
 #define KVC_DECB(V, O, N)                                                                            \
