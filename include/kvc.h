@@ -220,6 +220,16 @@ int kvc_encode_noalloc(const kvc_desc *desc, const uint8_t *sym, const uint16_t 
  * still written for it.  CDF rows are expected non-decreasing (kvc_quantize,
  * kvc_cdf and kvc_deserialize guarantee it); on a decreasing row the symbol
  * is some k in [0, A).
+ * Launches: all on `stream`, except that when layers have fewer bins than A
+ * (and dev_status is not NULL) the decode is launched once per run of layers
+ * with equal search depth and the runs after the first go on up to three
+ * streams the library owns (one set per device, made on first use, default
+ * priority), forked from `stream` by an event and joined back into it before
+ * a last guard launch on `stream`: all of the call's work is ordered after
+ * the work already on `stream`, and later work on `stream` after it (in a
+ * captured graph, a fork and a join).  Calls from several host threads take
+ * turns on those streams; calls on one device that overlap in time still
+ * race on their outputs as usual.
  */
 int kvc_decode(const kvc_desc *desc, const uint8_t *payload, int64_t payload_bytes,
                const uint64_t *slab_off, const uint16_t *stream_len, const uint16_t *cdf,
