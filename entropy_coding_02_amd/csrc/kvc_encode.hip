@@ -220,6 +220,9 @@ __device__ uint64_t block_excl_scan_1024(uint64_t v, uint64_t *sh, uint64_t *tot
 // range before the scan and rewrites it element by element after).  With
 // `expect`, a total different from *expect sets KVC_DEV_BAD_CONTAINER;
 // otherwise a total above payload_cap sets KVC_DEV_PAYLOAD_OVERFLOW.
+// Totals per thread k_scan keeps in registers (launches of up to 32768 slabs).
+constexpr int SCAN_REG = 32;
+
 __global__ __launch_bounds__(1024) void k_scan(const uint64_t *slab_total, uint64_t *slab_off,
                                                int64_t n, int64_t payload_cap,
                                                const uint64_t *expect, int32_t *status)
@@ -227,14 +230,33 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *slab_total, uint6
     __shared__ uint64_t sh[32];
     const int64_t per = (n + 1023) / 1024;
     const int64_t b = threadIdx.x * per, e = min(n, b + per);
-    uint64_t local = 0;
-    for (int64_t i = b; i < e; ++i) local += slab_total[i];
     uint64_t total;
-    uint64_t run = block_excl_scan_1024(local, sh, &total);
-    for (int64_t i = b; i < e; ++i) {
-        const uint64_t v = slab_total[i];
-        slab_off[i] = run;
-        run += v;
+    if (per <= SCAN_REG) {
+        // the thread's totals all requested at once and kept in registers for
+        // the second pass (a loop waits for each load in turn)
+        uint64_t v[SCAN_REG];
+        uint64_t local = 0;
+#pragma unroll
+        for (int k = 0; k < SCAN_REG; ++k) {
+            v[k] = b + k < e ? slab_total[b + k] : 0u;
+            local += v[k];
+        }
+        uint64_t run = block_excl_scan_1024(local, sh, &total);
+#pragma unroll
+        for (int k = 0; k < SCAN_REG; ++k)
+            if (b + k < e) {
+                slab_off[b + k] = run;
+                run += v[k];
+            }
+    } else {
+        uint64_t local = 0;
+        for (int64_t i = b; i < e; ++i) local += slab_total[i];
+        uint64_t run = block_excl_scan_1024(local, sh, &total);
+        for (int64_t i = b; i < e; ++i) {
+            const uint64_t v = slab_total[i];
+            slab_off[i] = run;
+            run += v;
+        }
     }
     if (threadIdx.x == 0) {
         slab_off[n] = total;
