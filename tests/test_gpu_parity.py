@@ -140,6 +140,36 @@ def test_one_lane_runs_of_kv_bins():
     compare_full("one_lane_kv_bins", kv, np.array([[32, 16], [16, 32]], np.int32), cfg.chunk_tokens)
 
 
+def test_one_lane_runs_without_status():
+    """kvc_decode with no status word cannot tell a guard launch about a
+    stream that left the staged rows, so it searches whole rows in one
+    launch: the same symbols and values as the oracle, as with a status word
+    (runs per search depth and the guard)."""
+    import torch
+    cfg = SMALL["one_lane_A32_A16_C16_T32768_Tc16"]
+    say("[gpu] one-lane runs, decode without a status word")
+    kv, _ = kvgen.generate(cfg)
+    bins, Tc = cfg.bins(), cfg.chunk_tokens
+    L, _, T, C = kv.shape
+    d = kvc.Desc(L, C, T, bins, Tc)
+    buf = kvc.alloc(d, out_dtype=kvc.KVC_F16, with_dec_sym=True)
+    kvc.encode(buf, torch.from_numpy(kv.view(np.int16)).cuda())
+    torch.cuda.synchronize()
+    assert int(buf.dev_status.item()) == 0
+    r = oracle.codec(kv, bins, Tc)
+    n = kv.size
+    for status in (None, buf.dev_status):
+        buf.dec_sym.fill_(0xAB)
+        buf.out.fill_(0)
+        kvc.kvc_decode(d, buf.payload, buf.slab_off, buf.stream_len, buf.cdf, buf.max1, buf.dec_sym, buf.out,
+                       kvc.KVC_F16, status)
+        torch.cuda.synchronize()
+        assert int(buf.dev_status.item()) == 0
+        assert np.array_equal(buf.dec_sym[:n].cpu().numpy().reshape(kv.shape), r["sym"])
+        got16 = buf.out[:n].cpu().view(torch.int16).numpy().view(np.uint16).reshape(kv.shape)
+        assert np.array_equal(got16, r["out_f16"])
+
+
 def test_empty_input():
     say("[gpu] empty input")
     import torch
