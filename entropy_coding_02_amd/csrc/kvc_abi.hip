@@ -118,7 +118,7 @@ void *noalloc_base()
 // (sizes are the largest over the levels); every section 256-byte aligned.
 struct StreamLayout {
     int32_t U;                                   // chunks per unit
-    int64_t len, off, pay, sizes, staging, total;  // section offsets; scratch at 0
+    int64_t len, off, pay, sizes, staging, packed, total;  // section offsets; scratch at 0
     int64_t pay_cap, chunk_cap;                  // unit payload, staging bytes per chunk
 };
 
@@ -136,7 +136,17 @@ int stream_layout(const kvc_desc *levels, int32_t n_levels, int32_t chunks_per_u
     }
     const KParams &P = g[0].p;
     const int64_t per_chunk = 2 * (int64_t)P.L * P.Tc;  // streams of a full chunk
-    int64_t U = chunks_per_unit ? chunks_per_unit : (((int64_t)1 << 17) + per_chunk - 1) / per_chunk;
+    // automatic unit: enough chunks for about 2^17 streams (an encoder launch
+    // that fills the chip), and about sqrt(2 NC) of them: each unit costs some
+    // tens of microseconds of host waiting and idle gaps, while the first
+    // unit's encode and the last one's copy are not overlapped
+    int64_t U = chunks_per_unit;
+    if (!U) {
+        const int64_t by_streams = (((int64_t)1 << 17) + per_chunk - 1) / per_chunk;
+        int64_t by_count = 1;
+        while ((by_count + 1) * (by_count + 1) <= 2 * (int64_t)P.NC) ++by_count;
+        U = std::max(by_streams, by_count);
+    }
     U = std::max<int64_t>(1, std::min<int64_t>(U, P.NC));
     sl.U = (int32_t)U;
     int64_t scratch = 0, n_streams = 0, n_slabs = 0, chunk_cap = 0;
@@ -161,7 +171,8 @@ int stream_layout(const kvc_desc *levels, int32_t n_levels, int32_t chunks_per_u
     sl.pay = sl.off + round_up(8 * (n_slabs + 1), 256);
     sl.sizes = sl.pay + round_up(sl.pay_cap, 256);
     sl.staging = sl.sizes + round_up(8 * U, 256);
-    sl.total = sl.staging + 2 * U * chunk_cap;
+    sl.packed = sl.staging + 2 * U * chunk_cap;
+    sl.total = sl.packed + 2 * U * chunk_cap;
     return KVC_OK;
 }
 
@@ -506,9 +517,11 @@ int kvc_stream_encode(const kvc_desc *levels, int32_t n_levels, const int32_t *c
     uint64_t *const sizes_u = (uint64_t *)(wk + sl.sizes);
     const hipStream_t cs = (hipStream_t)compute_stream, xs = (hipStream_t)copy_stream;
     auto staging = [&](int64_t u) { return wk + sl.staging + (u & 1) * sl.U * sl.chunk_cap; };
+    auto packed = [&](int64_t u) { return wk + sl.packed + (u & 1) * sl.U * sl.chunk_cap; };
 
-    // serialized[h]: staging half h written and its sizes in chunk_bytes (compute
-    // stream); copied[h]: the copies out of half h done (copy stream)
+    // serialized[h]: unit containers packed into half h and their sizes in
+    // chunk_bytes (compute stream); copied[h]: the copy out of half h done
+    // (copy stream)
     hipEvent_t serialized[2] = {}, copied[2] = {};
     for (int h = 0; h < 2 && rc == KVC_OK; ++h)
         if (hipEventCreateWithFlags(&serialized[h], hipEventDisableTiming) != hipSuccess ||
@@ -537,8 +550,6 @@ int kvc_stream_encode(const kvc_desc *levels, int32_t n_levels, const int32_t *c
         const bool vec16 = (P.C % 16 == 0) && aligned(sym_u, 16);
         hipError_t e = launch_encode(sym_u, cdf_u, slots, slab_total, len_u, off_u, pay_u, sl.pay_cap, gu.p,
                                      dev_status, vec16, cs);
-        // staging half u % 2 is free once the copies of unit u - 2 are done
-        if (e == hipSuccess && u >= 2) e = hipStreamWaitEvent(cs, copied[u & 1], 0);
         uint8_t *const st = staging(u);
         // the unit's full chunks in one set of launches, a shorter last chunk in its own
         const int64_t jfull = std::min<int64_t>(un.jb, P.T / P.Tc);
@@ -555,26 +566,32 @@ int kvc_stream_encode(const kvc_desc *levels, int32_t n_levels, const int32_t *c
         }
         const int n = (int)(un.jb - un.ja);
         if (e == hipSuccess) e = launch_container_totals(st, sl.chunk_cap, n, sizes_u, cs);
+        // packed half u % 2 is free once the copy of unit u - 2 is done; the
+        // containers then go into it back to back, for one copy per unit
+        if (e == hipSuccess && u >= 2) e = hipStreamWaitEvent(cs, copied[u & 1], 0);
+        if (e == hipSuccess) e = launch_pack_containers(st, sl.chunk_cap, sizes_u, n, packed(u), cs);
         if (e == hipSuccess)
             e = hipMemcpyAsync(chunk_bytes + un.ja, sizes_u, 8 * (size_t)n, hipMemcpyDeviceToHost, cs);
         if (e == hipSuccess) e = hipEventRecord(serialized[u & 1], cs);
         return launch_status(e);
     };
-    // Copy unit u's containers to host_out at their exact sizes.
+    // Copy unit u's containers, back to back at their exact sizes, to host_out
+    // in one copy (a copy costs several microseconds beyond its bytes).
     auto copy_out = [&](int64_t u) -> int {
         const Unit &un = units[u];
         if (hipEventSynchronize(serialized[u & 1]) != hipSuccess) return KVC_ERR_HIP;
-        const uint8_t *const st = staging(u);
+        int64_t total = 0;
         for (int64_t j = un.ja; j < un.jb; ++j) {
             const int64_t n = chunk_bytes[j];
-            if (n <= 0 || n > sl.chunk_cap) return KVC_ERR_HIP;  // not a container this call wrote
-            if (n > host_cap - cursor) return KVC_ERR_CAPACITY;
-            if (hipMemcpyAsync(host_out + cursor, st + (j - un.ja) * sl.chunk_cap, (size_t)n,
-                               hipMemcpyDeviceToHost, xs) != hipSuccess)
-                return KVC_ERR_HIP;
-            host_off[j] = cursor;
-            cursor += n;
+            // not a container this call wrote (a container's total is a multiple of 16)
+            if (n <= 0 || n > sl.chunk_cap || n % 16 != 0) return KVC_ERR_HIP;
+            if (n > host_cap - cursor - total) return KVC_ERR_CAPACITY;
+            host_off[j] = cursor + total;
+            total += n;
         }
+        if (hipMemcpyAsync(host_out + cursor, packed(u), (size_t)total, hipMemcpyDeviceToHost, xs) != hipSuccess)
+            return KVC_ERR_HIP;
+        cursor += total;
         return launch_status(hipEventRecord(copied[u & 1], xs));
     };
     // Hand unit u's containers to the caller once their copies are done.

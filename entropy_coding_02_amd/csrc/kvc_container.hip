@@ -237,6 +237,32 @@ __global__ void k_container_totals(const uint8_t *__restrict__ base, int64_t str
     if (k < n) dst[k] = *(const uint64_t *)(base + (int64_t)k * stride + 40);
 }
 
+// The n containers of a unit, container k at src + k * stride (stride a
+// multiple of 16) with its total in sizes[k], moved back to back into dst
+// (container k at the sum of the totals before it), so that one copy takes the
+// whole unit off the device.  A total is taken rounded up to 16 and at most
+// stride, so nothing is read or written past the slots whatever sizes holds
+// (the host checks the totals before it copies).  Block (x, k) moves 16-byte
+// pieces x, x + gridDim.x, ... of container k.
+__global__ void k_pack_containers(const uint8_t *__restrict__ src, int64_t stride,
+                                  const uint64_t *__restrict__ sizes, int n, uint8_t *__restrict__ dst)
+{
+    const int k = (int)blockIdx.y;
+    if (k >= n) return;
+    auto len_of = [&](int i) -> int64_t {
+        const uint64_t v = sizes[i];
+        const uint64_t r = v > (uint64_t)stride ? (uint64_t)stride : (v + 15u) & ~(uint64_t)15u;
+        return (int64_t)r;
+    };
+    int64_t off = 0;
+    for (int i = 0; i < k; ++i) off += len_of(i);
+    const int64_t n16 = len_of(k) / 16;
+    const u32x4 *s4 = (const u32x4 *)(src + (int64_t)k * stride);
+    u32x4 *d4 = (u32x4 *)(dst + off);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+        d4[i] = s4[i];
+}
+
 }  // namespace
 
 ContainerLayout container_layout(const KParams &p)
@@ -331,6 +357,15 @@ hipError_t launch_deserialize(const uint8_t *in, int64_t in_bytes, uint16_t *cdf
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_slab_offsets(stream_len, slab_off, p, (const uint64_t *)(in + 32), status, stream);
+}
+
+hipError_t launch_pack_containers(const uint8_t *src, int64_t stride, const uint64_t *sizes, int n,
+                                  uint8_t *dst, hipStream_t stream)
+{
+    if (n > 0)
+        hipLaunchKernelGGL(k_pack_containers, dim3(64, (unsigned)n), dim3(256), 0, stream, src, stride, sizes, n,
+                           dst);
+    return hipGetLastError();
 }
 
 hipError_t launch_container_totals(const uint8_t *base, int64_t stride, int n, uint64_t *dst,

@@ -75,6 +75,11 @@ hipError_t launch_serialize(const uint16_t *cdf, const uint16_t *max1, const uin
 // base (16-byte aligned), into dst[n] (device).
 hipError_t launch_container_totals(const uint8_t *base, int64_t stride, int n, uint64_t *dst,
                                    hipStream_t stream);
+// n containers stride bytes apart from src (stride a multiple of 16), totals
+// in sizes (device), moved back to back into dst (16-byte aligned, at least
+// n * stride bytes): container k at the sum of the totals before it.
+hipError_t launch_pack_containers(const uint8_t *src, int64_t stride, const uint64_t *sizes, int n,
+                                  uint8_t *dst, hipStream_t stream);
 // n consecutive chunks j0 .. j0 + n - 1 of one shape (each with p.T tokens):
 // the whole tensor's tables (groups of S chunks, table_stride entries apart),
 // its max1 rows (max1_T tokens each, chunk j starting at token j * Tc), and

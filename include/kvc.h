@@ -311,23 +311,24 @@ int kvc_serialize_chunk(const kvc_desc *desc, int64_t chunk, const uint16_t *cdf
  * levels[chunk_level[j]], chunk j (so kvc_deserialize + kvc_decode read it).
  * Chunks go in units of at most `chunks_per_unit` consecutive chunks of one
  * level: on compute_stream a unit is encoded (kvc_encode's kernels, on the
- * unit's rows of sym in place) and its chunk containers are written into one
- * half of a device staging area; on copy_stream the containers of the unit
- * before are copied to host_out meanwhile, each at its exact size.  The host
- * thread reads each unit's container sizes once its staging is written, to
- * issue those copies, so the call returns only when every container is in
- * host_out (both streams synchronised).
+ * unit's rows of sym in place) and its chunk containers are written into a
+ * staging area, then moved back to back into one half of a device area; on
+ * copy_stream the unit before is copied to host_out meanwhile, in one copy of
+ * its containers at their exact sizes.  The host thread reads each unit's
+ * container sizes once they are written, to issue that copy, so the call
+ * returns only when every container is in host_out (both streams
+ * synchronised).
  *   levels       HOST array of n_levels descriptors (1..4), as kvc_quantize_levels:
  *                same n_layers, n_channels, n_tokens, chunk_tokens; bins may differ
  *   chunk_level  HOST int32 [NC], each in [0, n_levels)
  *   sym, cdf     HOST arrays of n_levels device pointers: each level's symbols
  *                [L][2][T][C] and CDFs [NC][L][2][C][A_level] (kvc_quantize_levels)
  *   max1         [L][2][T] fp16 bits (device)
- *   chunks_per_unit  1.. , or 0: enough chunks for about 2^17 streams per unit
- *                (whole-chip encoder launches), at most NC
+ *   chunks_per_unit  1.. , or 0: the larger of about sqrt(2 NC) chunks and enough
+ *                chunks for about 2^17 streams (whole-chip encoder launches), at most NC
  *   work         device, 256-byte aligned, work_bytes >= kvc_stream_work_bytes(levels,
  *                n_levels, chunks_per_unit): encoder scratch, one unit's lengths,
- *                offsets and payload, and the two staging halves
+ *                offsets and payload, and two staging and two packed halves
  *   host_out     page-locked host memory (hipHostMalloc), host_cap bytes: the
  *                containers of chunks 0, 1, ... back to back (chunk j at the sum of
  *                chunk_bytes[0..j))

@@ -138,10 +138,11 @@ def test_container_calls_reject_bad_arguments(lib):
 
 
 def test_stream_work_bytes_and_argument_checks(lib):
-    """kvc_stream_work_bytes: the automatic unit is about 2^17 streams (at
-    most NC chunks), the workspace grows with the unit, mismatched levels are
-    refused; kvc_stream_encode refuses null arguments and out-of-range levels
-    before any HIP call."""
+    """kvc_stream_work_bytes: the automatic unit is the larger of about
+    sqrt(2 NC) chunks and about 2^17 streams (at most NC chunks), the
+    workspace grows with the unit, mismatched levels are refused;
+    kvc_stream_encode refuses null arguments and out-of-range levels before
+    any HIP call."""
     L, C, T, Tc = 2, 64, 1000, 64  # 16 chunks of 256 streams
     a, b = kvc.Desc(L, C, T, [[32, 16], [16, 8]], Tc), kvc.Desc(L, C, T, [[8, 8], [4, 4]], Tc)
     w = [kvc.kvc_stream_work_bytes([a, b], u) for u in range(1, 17)]
@@ -149,8 +150,10 @@ def test_stream_work_bytes_and_argument_checks(lib):
     assert kvc.kvc_stream_work_bytes([a, b], 0) == w[-1]      # 2^17 streams > 16 chunks: all of them
     assert kvc.kvc_stream_work_bytes([a, b], 99) == w[-1]     # capped at NC
     assert kvc.kvc_stream_work_bytes([a], 4) <= kvc.kvc_stream_work_bytes([a, b], 4)
-    big = kvc.Desc(32, 1024, 80000, np.full((32, 2), 32, np.int32), 256)  # 16384 streams a chunk
-    assert kvc.kvc_stream_work_bytes([big], 0) == kvc.kvc_stream_work_bytes([big], 8)
+    big = kvc.Desc(32, 1024, 80000, np.full((32, 2), 32, np.int32), 256)  # 16384 streams a chunk, 313 chunks
+    assert kvc.kvc_stream_work_bytes([big], 0) == kvc.kvc_stream_work_bytes([big], 25)  # floor(sqrt(626))
+    mid = kvc.Desc(32, 1024, 8192, np.full((32, 2), 32, np.int32), 256)  # 32 chunks: 2^17 streams = 8 of them
+    assert kvc.kvc_stream_work_bytes([mid], 0) == kvc.kvc_stream_work_bytes([mid], 8)
     for bad in ([a, kvc.Desc(L, C, T + 1, [[32, 16], [16, 8]], Tc)], [a, kvc.Desc(L, 32, T, [[32, 16], [16, 8]], Tc)]):
         with pytest.raises(kvc.KvcError):
             kvc.kvc_stream_work_bytes(bad, 1)
