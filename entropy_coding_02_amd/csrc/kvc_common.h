@@ -6,6 +6,12 @@
 
 #include "../../include/kvc.h"
 
+// Status bit a kvc_encode launch that stages only the first entries of each
+// CDF row sets on meeting a symbol past them; the guard launch that follows
+// then encodes everything again over whole rows, and k_scan clears the bit,
+// so no call leaves it set.
+#define KVC_DEV_INTERNAL_REDO (1 << 30)
+
 #define KVC_MAX_LAYERS 256
 
 // Pointers into LDS.  Typed with the LDS address space so the compiler emits

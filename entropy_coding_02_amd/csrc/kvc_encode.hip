@@ -44,13 +44,21 @@ namespace {
 // bytes are then staged as 4 * (s & (A - 1)), the byte offset of the pair
 // within its row, so each lookup address is one byte-select add, and an
 // out-of-range byte (flagged) still reads inside its row.
+//
+// A launch covers the slabs of (layer, K|V) pairs lk0 .. lk0 + nlk - 1 (of
+// every chunk, in slab order) and stages the first A_st entries of each CDF
+// row (A_st < A only where every symbol of those layers lies below A_st - 1):
+// a symbol at or past A_st then sets KVC_DEV_INTERNAL_REDO, not
+// KVC_DEV_BAD_SYMBOL.  A guard launch (guard != 0) returns unless that bit is
+// set.
 template <bool VEC16, int PER, int ENC_SW, int SPW, bool PRE4 = false>
 __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
                                                 const uint16_t *__restrict__ cdf,
                                                 uint8_t *__restrict__ slots,
                                                 uint16_t *__restrict__ stream_len, KParams p, int CT,
-                                                int32_t *status)
+                                                int32_t *status, int A_st, int lk0, int nlk, int guard)
 {
+    if (guard && (__atomic_load_n(status, __ATOMIC_RELAXED) & KVC_DEV_INTERNAL_REDO) == 0) return;
     static_assert(SPW == 16 || SPW == 32 || SPW == 64, "16, 32 or 64 streams per wave");
     constexpr int SPB = 4 * SPW;   // streams (token rows) per block
     constexpr int GB = 256 / SPB;  // blocks per 256-token slot region
@@ -58,21 +66,23 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
     extern __shared__ uint32_t lds[];
     const int bps = (p.Tc + 255) / 256;
     const int64_t bl = xcd_block(blockIdx.x, gridDim.x);  // a slab's blocks share an XCD
-    const int64_t grp = bl / GB;  // slot region: 256 tokens of one slab
-    const int sub = (int)(bl - grp * GB);
-    const int64_t slab = grp / bps;
-    const int tb = (int)(grp - slab * bps);
+    const int64_t grl = bl / GB;  // 256 tokens of one of the launch's slabs
+    const int sub = (int)(bl - grl * GB);
+    const int64_t ql = grl / bps;  // the launch's slab ql: chunk ql / nlk, (layer, K|V) lk0 + ql % nlk
+    const int tb = (int)(grl - ql * bps);
+    const int64_t slab = (ql / nlk) * (2 * (int64_t)p.L) + lk0 + ql % nlk;
+    const int64_t grp = slab * bps + tb;  // slot region
     const SlabGeom g = slab_geom(p, slab);
     const int r0 = tb * 256 + sub * SPB;  // the block's first token
     if (r0 >= g.nj) return;               // uniform: the whole block is past the slab
     const int lane = (int)threadIdx.x & 63;
     const int j = ((int)threadIdx.x >> 6) * SPW + lane;  // stream within the block (lane < SPW)
     const int t = r0 + j;
-    const int C = p.C, A = p.A;
+    const int C = p.C, A = A_st, AR = p.A;  // staged entries per row; the table's row length
     const bool active = lane < SPW && t < g.nj;
     const int64_t sid = g.sid0 + t;
     const uint8_t *q = sym + (g.row0 + (active ? t : 0)) * C;
-    const uint16_t *rows = cdf + g.tab * C * A;
+    const uint16_t *rows = cdf + g.tab * C * AR;
     lds_u32 *const pairs = (lds_u32 *)lds;
     constexpr int sstride = ENC_SW + 16;
     lds_u8 *const stile = (lds_u8 *)(pairs + CT * A);
@@ -122,7 +132,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
             *(lds_u32x4 *)(stile + r * sstride + part * 16) = sv[i];
         }
     };
-    pt.load(rows, 0, CT, C, A);
+    pt.load(rows, 0, CT, C, A, AR);
     if constexpr (VEC16) load_syms(0);
     for (int it = 0; it < ntiles; ++it) {
         const int c0 = it * CT, c1 = min(C, c0 + CT);
@@ -134,7 +144,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
             if (new_stile) store_syms();
         }
         __syncthreads();
-        if (it + 1 < ntiles) pt.load(rows, c0 + CT, CT, C, A);
+        if (it + 1 < ntiles) pt.load(rows, c0 + CT, CT, C, A, AR);
         if constexpr (VEC16) {
             if (new_stile && s0 + ENC_SW < C) load_syms(s0 + ENC_SW);
         }
@@ -171,7 +181,7 @@ __global__ __launch_bounds__(256) void k_encode(const uint8_t *__restrict__ sym,
         }
     }
     if (active) stream_len[sid] = (uint16_t)enc_finish(e, out);
-    if (badsym) kvc_flag(status, KVC_DEV_BAD_SYMBOL);
+    if (badsym) kvc_flag(status, A < AR ? KVC_DEV_INTERNAL_REDO : KVC_DEV_BAD_SYMBOL);
 }
 
 __global__ __launch_bounds__(256) void k_slab_sum(const uint16_t *__restrict__ stream_len,
@@ -259,6 +269,8 @@ __global__ __launch_bounds__(1024) void k_scan(const uint64_t *slab_total, uint6
         }
     }
     if (threadIdx.x == 0) {
+        // the encoder's guard launch has run: its redo bit is done with
+        if (status) atomicAnd(status, ~(int32_t)KVC_DEV_INTERNAL_REDO);
         slab_off[n] = total;
         if (expect) {
             if (total != *expect) kvc_flag(status, KVC_DEV_BAD_CONTAINER);
@@ -821,6 +833,21 @@ constexpr int64_t KVC_ENC_SPARSE_MAX_STREAMS = 16384;
 // Launches of at most this many streams pack 16 streams per wave, others 64.
 constexpr int64_t KVC_PACK_SPARSE_MAX_STREAMS = 16384;
 
+// Runs of (layer, K|V) pairs encoded with only the first entries of each CDF
+// row staged take at least this many blocks, else they stage whole rows.
+constexpr int64_t KVC_ENC_RUN_MIN_BLOCKS = 4096;
+
+// Depth n (rows staged to 2^n entries) for (layer, K|V) lk: that of its bins,
+// at least 3 and at most the table's (nfull); nfull when may_cut is false.
+static int enc_run_nstep(const KParams &p, int lk, int nfull, bool may_cut)
+{
+    if (!may_cut) return nfull;
+    const int bins = 2 * ((int)p.maxq[lk] + 1);
+    int n = (int)cdf_nstep((uint32_t)bins);
+    if (n < 3) n = 3;
+    return n < nfull ? n : nfull;
+}
+
 // Symbol tile width: 128 channels, the whole 128-byte line of each token row
 // of 1024 channels, so every line of the symbols is read from memory once.
 // (64-channel tiles read each line twice, its halves a tile apart with the
@@ -890,11 +917,7 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
     if (p.n_slabs == 0) return launch_zero_u64(slab_off, stream);
     const int64_t bps = (p.Tc + 255) / 256;
     const int64_t regions = bps * p.n_slabs;  // slot regions: 256 tokens of one slab
-    const int CT = enc_tile_channels(p.A, p.n_streams);
-    const size_t lds_pairs = (size_t)CT * p.A * sizeof(uint32_t);
-    const int per = (CT * (p.A / 2) + 255) / 256;  // pairs staged per thread
     const int spw = enc_streams_per_wave(p.n_streams);
-    const dim3 grid((unsigned)(regions * (64 / spw)));
     size_t lds_split = 0;
     const int ch = (vec16 && p.n_streams <= KVC_ENC_SPLIT_MAX_STREAMS) ? enc_split_chunk(p, &lds_split) : 0;
     if (ch > 0) {
@@ -920,13 +943,47 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
         }
         return hipGetLastError();
     }
+    // One launch per run of (layer, K|V) pairs whose symbols fit the same
+    // power-of-two prefix of the CDF rows, as in the decoder: a run of layers
+    // with fewer bins than the table's rows stages only the first 2^n entries
+    // of each row (symbols of b bins run to b - 2), so that its tiles hold more
+    // channels in the same LDS and fewer barriers pass per symbol.  A symbol at
+    // or past the staged entries sets the redo bit; a guard launch over whole
+    // rows follows any cut run and encodes everything again when the bit is set
+    // (k_scan clears it).  Without a status word, or for runs of fewer than
+    // KVC_ENC_RUN_MIN_BLOCKS blocks, whole rows.
+    const int LK = 2 * p.L;
+    const int nfull = (int)cdf_nstep((uint32_t)p.A);
+    int run_n[2 * KVC_MAX_LAYERS];  // each (layer, K|V)'s depth
+    for (int lk = 0; lk < LK;) {
+        const int n = enc_run_nstep(p, lk, nfull, status != nullptr);
+        int lk1 = lk + 1;
+        while (lk1 < LK && enc_run_nstep(p, lk1, nfull, status != nullptr) == n) ++lk1;
+        const bool small = (int64_t)(lk1 - lk) * p.NC * bps * (64 / spw) < KVC_ENC_RUN_MIN_BLOCKS;
+        for (int k = lk; k < lk1; ++k) run_n[k] = small ? nfull : n;
+        lk = lk1;
+    }
+    bool cut = false;
+    for (int lk0 = 0; lk0 <= LK;) {
+        const bool guard_pass = lk0 == LK;  // after the runs: the guard launch
+        if (guard_pass && !cut) break;
+        const int n0 = guard_pass ? nfull : run_n[lk0];
+        int lk1 = guard_pass ? LK + 1 : lk0 + 1;
+        while (lk1 < LK && run_n[lk1] == n0) ++lk1;
+        const int A_st = n0 < nfull ? (1 << n0) : p.A;  // entries staged per row
+        cut = cut || A_st < p.A;
+        const int nlk = guard_pass ? LK : lk1 - lk0, lkb = guard_pass ? 0 : lk0, guard = guard_pass ? 1 : 0;
+        const int CT = enc_tile_channels(A_st, p.n_streams);
+        const size_t lds_pairs = (size_t)CT * A_st * sizeof(uint32_t);
+        const int per = (CT * (A_st / 2) + 255) / 256;  // pairs staged per thread
+        const dim3 grid((unsigned)(bps * (int64_t)nlk * p.NC * (64 / spw)));
+        const bool pre4 = (A_st & (A_st - 1)) == 0 && A_st <= 64;  // symbols staged as pair byte offsets
 #define KVC_ENC(V, P, S, W, L)                                                                       \
     hipLaunchKernelGGL((k_encode<V, P, S, W>), grid, dim3(256), L, stream, sym, cdf, slots, stream_len, \
-                       p, CT, status)
+                       p, CT, status, A_st, lkb, nlk, guard)
 #define KVC_ENC4(P, S, W, L)                                                                         \
     hipLaunchKernelGGL((k_encode<true, P, S, W, true>), grid, dim3(256), L, stream, sym, cdf, slots,    \
-                       stream_len, p, CT, status)
-    const bool pre4 = (p.A & (p.A - 1)) == 0 && p.A <= 64;  // symbols staged as pair byte offsets
+                       stream_len, p, CT, status, A_st, lkb, nlk, guard)
 #define KVC_ENC_S(S, W)                                                                              \
     {                                                                                                \
         const size_t lds_syms = lds_pairs + 4 * W * (size_t)(S + 16);                                \
@@ -941,13 +998,17 @@ hipError_t launch_encode(const uint8_t *sym, const uint16_t *cdf, uint8_t *slots
             else KVC_ENC(false, 8, S, W, lds_pairs);                                                 \
         }                                                                                            \
     }
-    if (spw == 16)
-        KVC_ENC_S(ENC_SYMBOL_TILE, 16)
-    else
-        KVC_ENC_S(ENC_SYMBOL_TILE, 64)
+        if (spw == 16)
+            KVC_ENC_S(ENC_SYMBOL_TILE, 16)
+        else
+            KVC_ENC_S(ENC_SYMBOL_TILE, 64)
 #undef KVC_ENC_S
 #undef KVC_ENC4
 #undef KVC_ENC
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        lk0 = lk1;
+    }
     hipLaunchKernelGGL(k_slab_sum, dim3((unsigned)p.n_slabs), dim3(256), 0, stream, stream_len,
                        slab_total, p);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, slab_total, slab_off, p.n_slabs,

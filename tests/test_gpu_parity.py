@@ -292,6 +292,41 @@ def test_bad_symbol_flagged(name):
         assert int(buf.dev_status.item()) & kvc.KVC_DEV_BAD_SYMBOL == want_flag
 
 
+def test_one_lane_encoder_runs_redo():
+    """Layers with fewer bins than the table's rows are encoded with only the
+    first 2^n entries of each row staged.  A symbol of such a layer past them
+    but below A (legal in its table, though no quantizer of its bins makes
+    it) sends the call to its guard launch over whole rows: payload bit for
+    bit as the oracle's, and no status bit left; a symbol >= A ends with
+    exactly KVC_DEV_BAD_SYMBOL."""
+    import torch
+    cfg = SMALL["one_lane_A32_A16_C16_T32768_Tc16"]
+    kv, _ = kvgen.generate(cfg)
+    bins, Tc = cfg.bins(), cfg.chunk_tokens
+    d = kvc.Desc(cfg.n_layers, cfg.n_channels, cfg.n_tokens, bins, Tc)
+    A = d.alphabet
+    sym, _ = oracle.quantize(kv, bins)
+    L, _, T, C = sym.shape
+    for value, want in ((20, 0), (A + 8, kvc.KVC_DEV_BAD_SYMBOL)):
+        say(f"[gpu] encoder runs: layer {L - 1} symbol {value} (A={A})")
+        s2 = sym.copy()
+        s2[L - 1, 0, T // 3, 5] = value   # layer of 16 bins: staged rows of 16 entries
+        s2[L - 1, 1, T - 1, C - 1] = value
+        tab = oracle.cdf(np.minimum(s2, A - 1), Tc, A)
+        buf = kvc.alloc(d)
+        buf.dev_status.zero_()
+        kvc.kvc_encode(d, torch.from_numpy(s2).cuda(), torch.from_numpy(tab.ravel().view(np.int16)).cuda(),
+                       buf.scratch, buf.stream_len, buf.slab_off, buf.payload, buf.dev_status)
+        torch.cuda.synchronize()
+        assert int(buf.dev_status.item()) == want
+        if not want:
+            wl, wo, wp = oracle.encode(s2, tab, Tc, A)
+            assert np.array_equal(buf.stream_len[: d.n_streams].cpu().numpy().view(np.uint16), wl)
+            assert np.array_equal(buf.slab_off[: d.n_slabs + 1].cpu().numpy().view(np.uint64), wo)
+            n = int(wo[-1])
+            assert np.array_equal(buf.payload[:n].cpu().numpy(), wp[:n])
+
+
 def test_deterministic():
     cfg = SMALL["mistral_L32_C1024_T64"]
     kv, _ = kvgen.generate(cfg)
