@@ -34,7 +34,9 @@
  *
  * Conventions:
  *   - The caller allocates every buffer.  The library allocates no memory and
- *     keeps no state between calls; calls are re-entrant.
+ *     keeps no state between calls, except the streams and events kvc_decode
+ *     makes on first use on a device (kept until the process ends); calls are
+ *     re-entrant.
  *   - Every compute call is asynchronous on `stream` (a hipStream_t; NULL is
  *     the default stream).  Outputs are valid once the stream is synchronised.
  *   - Errors the host can see return a negative kvc_status at once and launch
@@ -72,6 +74,8 @@ enum kvc_status {
 #define KVC_DEV_BAD_CDF 8          /* a CDF row the container cannot carry (kvc_serialize) */
 #define KVC_DEV_BAD_CONTAINER 16   /* a container that does not match the descriptor (kvc_deserialize) */
 #define KVC_DEV_BAD_SYMBOL 32      /* a symbol >= A, outside every CDF row (kvc_cdf, kvc_encode) */
+/* Bit 30 is used within a kvc_encode call (set and cleared on its stream); no
+ * call leaves it set. */
 
 enum kvc_dtype { KVC_F16 = 0, KVC_F32 = 1 };
 
@@ -178,6 +182,11 @@ int kvc_cdf(const kvc_desc *desc, const uint8_t *sym, uint16_t *cdf, int32_t *de
  *               KVC_DEV_PAYLOAD_OVERFLOW is set and only bytes below the cap are written
  * A symbol >= A sets KVC_DEV_BAD_SYMBOL; the streams of its slab are then
  * unspecified (it has no CDF interval to be coded with).
+ * Launches (all on `stream`): when layers have fewer bins than A and
+ * dev_status is not NULL, the coder is launched once per run of layers whose
+ * symbols fit the same power-of-two prefix of the CDF rows, staging only that
+ * prefix; a symbol past it (legal in its row) makes a last guard launch code
+ * every stream again over whole rows, so the output never depends on it.
  */
 int kvc_encode(const kvc_desc *desc, const uint8_t *sym, const uint16_t *cdf, void *scratch,
                int64_t scratch_bytes, uint16_t *stream_len, uint64_t *slab_off, uint8_t *payload,
